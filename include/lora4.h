@@ -1,0 +1,194 @@
+/*
+ * lora4.h - C ABI of liblora4: the unmerged-LoRA linear layer over a frozen
+ * 4-bit base, forward and backward, for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (terminology of "Quantized weights, full precision: The
+ * math behind 75% cheaper fine-tuning", section "Terminology": X input
+ * activations, Y output split into Y^base and Y^LoRA, W base weights, A and B
+ * the down and up LoRA matrices; shapes of "Training LLMs on a Budget: LoRA,
+ * QLoRA, and LoftQ", section 2 "The math": W is [d_out, d_in], A is
+ * [r, d_in], B is [d_out, r]). With tokens as rows, M tokens, K = d_in,
+ * N = d_out and s = alpha / r:
+ *
+ *   forward : Z = X A^T                      [M, r]
+ *             Y = X deq(W)^T + s Z B^T       [M, N]   (= Y^base + Y^LoRA)
+ *   backward: dZ = s dY B                    [M, r]
+ *             dX = dY deq(W) + dZ A          [M, K]
+ *             dA = dZ^T X                    [r, K]
+ *             dB = s dY^T Z                  [N, r]
+ *
+ * There is no dW: the base is frozen (Crusoe post, "Backward pass and
+ * optimizer step in training"). deq(W) is formed in registers/LDS inside
+ * the kernels and is never written to device memory (same post, "Forward
+ * pass in training"; "Training LLMs on a Budget", section 3 "The setup").
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller. Tensors are
+ *    dense, row-major and contiguous. bf16 values are passed as uint16_t bit
+ *    patterns. 16-byte alignment is required for every tensor pointer.
+ *  - stream is a hipStream_t passed as void* (NULL = the null stream). Every
+ *    call is asynchronous on that stream; nothing synchronizes the device.
+ *    Pointers are borrowed until the stream work completes.
+ *  - Outputs are overwritten, never accumulated.
+ *  - Arguments are validated on the host before any HIP call; a negative
+ *    status is returned and nothing is launched. Launch failures return
+ *    LORA4_ERR_HIP. No C++ exception crosses this boundary.
+ *  - The library allocates no device memory. Scratch space comes from the
+ *    caller's workspace, sized by lora4_workspace_bytes().
+ *  - Calls are re-entrant; two calls that share output or workspace buffers
+ *    on different streams race.
+ */
+#ifndef LORA4_H
+#define LORA4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage formats of the frozen base.
+ *  LORA4_NF4    : NF4 codes, one fp32 absmax scale per 64 consecutive
+ *                 K-elements of a row ("Training LLMs on a Budget",
+ *                 section 3, tricks 1 and 2).
+ *  LORA4_NF4_DQ : NF4 codes whose per-64 scales are themselves stored as
+ *                 E4M3 (OCP E4M3FN) codes with one fp32 second-level scale per
+ *                 256 consecutive first-level scales (same section, trick 2,
+ *                 double quantization).
+ *  LORA4_MXFP4  : E2M1 codes with one E8M0 scale per 32 consecutive
+ *                 K-elements ("Fine-Tuning 4-Bit Models", section "Case 2").
+ */
+typedef enum {
+  LORA4_NF4 = 1,
+  LORA4_NF4_DQ = 2,
+  LORA4_MXFP4 = 3
+} lora4_format;
+
+typedef enum {
+  LORA4_OK = 0,
+  LORA4_ERR_NULL = -1,          /* a required pointer is NULL                    */
+  LORA4_ERR_SHAPE = -2,         /* a size is out of range or inconsistent        */
+  LORA4_ERR_ALIGN = -3,         /* a tensor pointer is not 16-byte aligned       */
+  LORA4_ERR_FORMAT = -4,        /* unknown format, or block does not match it    */
+  LORA4_ERR_WORKSPACE = -5,     /* workspace NULL or smaller than required       */
+  LORA4_ERR_HIP = -6,           /* a HIP call or kernel launch failed            */
+  LORA4_ERR_UNIMPLEMENTED = -7  /* valid request this build does not support     */
+} lora4_status;
+
+/* The frozen 4-bit base W, logically [N = d_out, K = d_in] per group.
+ *  format, block : LORA4_NF4 / LORA4_NF4_DQ with block 64, LORA4_MXFP4 with 32.
+ *  N, K          : rows and columns of one group; K % block == 0, K >= block.
+ *  groups        : 1 for a plain linear; E for E experts stored back to back.
+ *  codes         : uint8 [groups][N][K/2]; byte j of a row holds element 2j
+ *                  in its low nibble and element 2j+1 in its high nibble.
+ *  scales        : NF4    : float [groups][N][K/64]
+ *                  NF4_DQ : uint8 E4M3 codes [groups][N][K/64]
+ *                  MXFP4  : uint8 E8M0 codes [groups][N][K/32] (value 2^(E-127))
+ *  scales2       : NF4_DQ only: float [groups][ceil(N*K/64 / 256)], the
+ *                  second-level scale of each run of 256 consecutive
+ *                  first-level scales of one group (row-major order); the
+ *                  rebuilt scale is fp32(E4M3(code) * scales2). NULL otherwise.
+ * The dequantized element is bf16(fp32(q[code] * scale)) for NF4 (q the
+ * 16-level NF4 codebook) and bf16(e2m1(code) * 2^(E-127)) for MXFP4.
+ */
+typedef struct lora4_W {
+  int32_t format;
+  int32_t block;
+  int64_t N;
+  int64_t K;
+  int64_t groups;
+  const uint8_t *codes;
+  const void *scales;
+  const float *scales2;
+} lora4_W;
+
+/* Workspace (bytes) that lora4_forward (which = 0) or lora4_backward
+ * (which = 1) needs for this W, M tokens and rank r. Returns 0 for invalid
+ * arguments. A caller may size once for the largest M and reuse it. */
+size_t lora4_workspace_bytes(int which, const lora4_W *W, int64_t M, int32_t r);
+
+/* Forward: Y = X deq(W)^T + s (X A^T) B^T.
+ *  X      : bf16 [M, K]                      (input activations)
+ *  A      : bf16 [groups][r, K]              (down projection)
+ *  B      : bf16 [groups][N, r]              (up projection)
+ *  r      : LoRA rank, 1 <= r <= 256
+ *  s      : LoRA scale alpha / r (any finite float)
+ *  group_offsets : groups == 1: NULL. Otherwise a DEVICE int64 array of
+ *           groups+1 non-decreasing row offsets, [0] == 0, [groups] == M;
+ *           rows offsets[e]..offsets[e+1]-1 of X and Y belong to expert e
+ *           (rows are pre-sorted by expert; routing and gating are outside).
+ *  Y      : bf16 [M, N] output, rounded once from the fp32 sum.
+ *  Z      : bf16 [M, r] output Z = X A^T kept for the backward; may be NULL.
+ *  Y_base, Y_lora : optional bf16 [M, N] outputs of the two terms; may be NULL.
+ *  workspace, workspace_bytes : device scratch, >= lora4_workspace_bytes(0,...).
+ * M may be 0: nothing is launched, and X, Y may then be NULL. */
+lora4_status lora4_forward(const lora4_W *W, const uint16_t *X, int64_t M,
+                           const uint16_t *A, const uint16_t *B, int32_t r, float s,
+                           const int64_t *group_offsets,
+                           uint16_t *Y, uint16_t *Z, uint16_t *Y_base, uint16_t *Y_lora,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Backward: dX = dY deq(W) + dZ A, dA = dZ^T X, dB = s dY^T Z, dZ = s dY B.
+ *  X, A, B, r, s, group_offsets : as for lora4_forward.
+ *  dY     : bf16 [M, N] upstream gradient.
+ *  Z      : bf16 [M, r] from lora4_forward, or NULL to recompute X A^T.
+ *  dX     : bf16 [M, K] output.
+ *  dA     : bf16 [groups][r, K] output (zero for an expert with no rows).
+ *  dB     : bf16 [groups][N, r] output (zero for an expert with no rows).
+ *  workspace, workspace_bytes : device scratch, >= lora4_workspace_bytes(1,...).
+ * M may be 0: then dA and dB are set to zero, and X, dY, dX may be NULL. */
+lora4_status lora4_backward(const lora4_W *W, const uint16_t *X, const uint16_t *dY, int64_t M,
+                            const uint16_t *A, const uint16_t *B, int32_t r, float s,
+                            const int64_t *group_offsets, const uint16_t *Z,
+                            uint16_t *dX, uint16_t *dA, uint16_t *dB,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* Quantize a bf16 base W [N, K] (K % 64 == 0) to NF4 with per-64 fp32 absmax
+ * scales ("Training LLMs on a Budget", section 3, tricks 1 and 2): code = the
+ * NF4 level nearest to fp32(w / absmax), ties to the lower level; an
+ * all-zero block encodes as the zero level.
+ *  double_quant == 0: codes uint8 [N][K/2], scales float [N][K/64], scales2 unused.
+ *  double_quant != 0: codes as above; scales receives uint8 E4M3 codes
+ *    [N][K/64] of scale / group max (nearest, ties to even); scales2 receives
+ *    float [ceil(N*K/64/256)] group maxima (a group's code is 0 if its max is 0).
+ * Codes are always chosen with the exact fp32 scale. */
+lora4_status quant_pack_nf4(const uint16_t *W_bf16, int64_t N, int64_t K, int32_t double_quant,
+                            uint8_t *codes, void *scales, float *scales2, void *stream);
+
+/* Quantize a bf16 base W [N, K] (K % 32 == 0) to MXFP4 ("Fine-Tuning 4-Bit
+ * Models", section "Case 2"): per 32-element block the E8M0 code
+ * E = clamp(floor(log2 amax) - 2, -127, 127) + 127 (E = 0 for an all-zero
+ * block), and each element's E2M1 code is the nearest value to w * 2^-(E-127),
+ * ties to the even code, saturating at +-6, sign copied from w.
+ *  codes : uint8 [N][K/2]; scales_e8m0 : uint8 [N][K/32]. */
+lora4_status quant_pack_mxfp4(const uint16_t *W_bf16, int64_t N, int64_t K,
+                              uint8_t *codes, uint8_t *scales_e8m0, void *stream);
+
+/* A static, human-readable name for a status code. */
+const char *lora4_status_string(lora4_status status);
+
+/* ---- Kernel timing (profiling aid) ------------------------------------------
+ * When enabled, every kernel the library launches is bracketed by two HIP
+ * events recorded on the caller's stream. lora4_timing_collect() waits for
+ * the recorded events, sums the elapsed time per kernel name and clears the
+ * record. Timing adds two event records per launch; it is off by default. */
+typedef struct lora4_kernel_time {
+  char name[48];
+  int64_t launches;
+  double total_ms;
+} lora4_kernel_time;
+
+lora4_status lora4_timing_enable(int on);
+/* Writes up to max entries; returns the number of distinct kernels (may
+ * exceed max), or a negative status. */
+int lora4_timing_collect(lora4_kernel_time *out, int max);
+
+/* Library version string. */
+const char *lora4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA4_H */

@@ -1,0 +1,241 @@
+"""Python binding of liblora4 (include/lora4.h): the unmerged-LoRA linear over
+a frozen 4-bit base (NF4, NF4 with double-quantized scales, MXFP4) on MI355X.
+
+This module only marshals arguments: it takes device pointers and the current
+stream from torch tensors and calls the C ABI through ctypes. Every step of the
+computation runs in the library's HIP kernels. If the library is not built,
+every call raises; there is no fallback.
+
+Low-level functions carry the ABI's names and signatures (pointers as ints):
+``lora4_forward``, ``lora4_backward``, ``lora4_workspace_bytes``,
+``quant_pack_nf4``, ``quant_pack_mxfp4``. The torch-level helpers ``pack_nf4``,
+``pack_mxfp4``, ``forward`` and ``backward`` allocate outputs with torch and call
+them.
+"""
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblora4.so")
+
+LORA4_NF4, LORA4_NF4_DQ, LORA4_MXFP4 = 1, 2, 3
+FORMATS = {"nf4": LORA4_NF4, "nf4_dq": LORA4_NF4_DQ, "mxfp4": LORA4_MXFP4}
+BLOCK = {LORA4_NF4: 64, LORA4_NF4_DQ: 64, LORA4_MXFP4: 32}
+
+EXPORTS = ["lora4_forward", "lora4_backward", "lora4_workspace_bytes", "quant_pack_nf4",
+           "quant_pack_mxfp4", "lora4_status_string", "lora4_timing_enable", "lora4_timing_collect",
+           "lora4_version"]
+
+
+class Lora4Error(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({status_string(status)})")
+
+
+class lora4_W(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("block", ctypes.c_int32), ("N", ctypes.c_int64),
+                ("K", ctypes.c_int64), ("groups", ctypes.c_int64), ("codes", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("scales2", ctypes.c_void_p)]
+
+
+class lora4_kernel_time(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded liblora4 (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m lora_fine_tuning_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+        Wp = ctypes.POINTER(lora4_W)
+        L.lora4_forward.argtypes = [Wp, vp, i64, vp, vp, i32, f32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.lora4_forward.restype = ctypes.c_int
+        L.lora4_backward.argtypes = [Wp, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.lora4_backward.restype = ctypes.c_int
+        L.lora4_workspace_bytes.argtypes = [ctypes.c_int, Wp, i64, i32]
+        L.lora4_workspace_bytes.restype = sz
+        L.quant_pack_nf4.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp]
+        L.quant_pack_nf4.restype = ctypes.c_int
+        L.quant_pack_mxfp4.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.quant_pack_mxfp4.restype = ctypes.c_int
+        L.lora4_status_string.argtypes = [ctypes.c_int]
+        L.lora4_status_string.restype = ctypes.c_char_p
+        L.lora4_timing_enable.argtypes = [ctypes.c_int]
+        L.lora4_timing_enable.restype = ctypes.c_int
+        L.lora4_timing_collect.argtypes = [ctypes.POINTER(lora4_kernel_time), ctypes.c_int]
+        L.lora4_timing_collect.restype = ctypes.c_int
+        L.lora4_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status):
+    return lib().lora4_status_string(int(status)).decode()
+
+
+def _check(status, what):
+    if status != 0:
+        raise Lora4Error(status, what)
+
+
+# ---------------------------------------------------------------------------
+# ABI-named calls (pointers as ints; stream as an int handle or None)
+# ---------------------------------------------------------------------------
+
+def lora4_workspace_bytes(which, W, M, r):
+    return lib().lora4_workspace_bytes(which, ctypes.byref(W), M, r)
+
+
+def lora4_forward(W, X, M, A, B, r, s, group_offsets, Y, Z, Y_base, Y_lora, workspace, workspace_bytes,
+                  stream):
+    return lib().lora4_forward(ctypes.byref(W), X, M, A, B, r, s, group_offsets, Y, Z, Y_base, Y_lora,
+                               workspace, workspace_bytes, stream)
+
+
+def lora4_backward(W, X, dY, M, A, B, r, s, group_offsets, Z, dX, dA, dB, workspace, workspace_bytes,
+                   stream):
+    return lib().lora4_backward(ctypes.byref(W), X, dY, M, A, B, r, s, group_offsets, Z, dX, dA, dB,
+                                workspace, workspace_bytes, stream)
+
+
+def quant_pack_nf4(W_bf16, N, K, double_quant, codes, scales, scales2, stream):
+    return lib().quant_pack_nf4(W_bf16, N, K, double_quant, codes, scales, scales2, stream)
+
+
+def quant_pack_mxfp4(W_bf16, N, K, codes, scales_e8m0, stream):
+    return lib().quant_pack_mxfp4(W_bf16, N, K, codes, scales_e8m0, stream)
+
+
+def timing_enable(on=True):
+    _check(lib().lora4_timing_enable(1 if on else 0), "lora4_timing_enable")
+
+
+def timing_collect():
+    """{kernel name: (launches, total_ms)} since the last collect."""
+    buf = (lora4_kernel_time * 64)()
+    n = lib().lora4_timing_collect(buf, 64)
+    if n < 0:
+        raise Lora4Error(n, "lora4_timing_collect")
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(min(n, 64))}
+
+
+def version():
+    return lib().lora4_version().decode()
+
+
+# ---------------------------------------------------------------------------
+# torch-level helpers (allocation + marshalling)
+# ---------------------------------------------------------------------------
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+@dataclass
+class PackedBase:
+    """A frozen 4-bit base on the device, [groups][N][K] logically."""
+    fmt: int
+    N: int
+    K: int
+    groups: int
+    codes: "object"            # torch uint8 [groups, N, K/2]
+    scales: "object"           # float32 or uint8 [groups, N, K/block]
+    scales2: Optional["object"] = None
+
+    def abi(self):
+        return lora4_W(self.fmt, BLOCK[self.fmt], self.N, self.K, self.groups, _ptr(self.codes),
+                       _ptr(self.scales), _ptr(self.scales2))
+
+
+def pack_nf4(W, double_quant=False):
+    """Quantize bf16 W ([N, K] or [E, N, K], on the GPU) to NF4 on the GPU."""
+    import torch
+    Ws = W if W.dim() == 3 else W.unsqueeze(0)
+    E, N, K = Ws.shape
+    dev = W.device
+    codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device=dev)
+    if double_quant:
+        scales = torch.empty((E, N, K // 64), dtype=torch.uint8, device=dev)
+        ng = -(-(N * K // 64) // 256)
+        scales2 = torch.empty((E, ng), dtype=torch.float32, device=dev)
+    else:
+        scales = torch.empty((E, N, K // 64), dtype=torch.float32, device=dev)
+        scales2 = None
+    for e in range(E):
+        st = quant_pack_nf4(_ptr(Ws[e]), N, K, 1 if double_quant else 0, _ptr(codes[e]), _ptr(scales[e]),
+                            _ptr(scales2[e]) if double_quant else None, _stream())
+        _check(st, "quant_pack_nf4")
+    return PackedBase(LORA4_NF4_DQ if double_quant else LORA4_NF4, N, K, E, codes, scales, scales2)
+
+
+def pack_mxfp4(W):
+    """Quantize bf16 W ([N, K] or [E, N, K], on the GPU) to MXFP4 on the GPU."""
+    import torch
+    Ws = W if W.dim() == 3 else W.unsqueeze(0)
+    E, N, K = Ws.shape
+    dev = W.device
+    codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((E, N, K // 32), dtype=torch.uint8, device=dev)
+    for e in range(E):
+        _check(quant_pack_mxfp4(_ptr(Ws[e]), N, K, _ptr(codes[e]), _ptr(scales[e]), _stream()),
+               "quant_pack_mxfp4")
+    return PackedBase(LORA4_MXFP4, N, K, E, codes, scales, None)
+
+
+def workspace_for(which, base, M, r):
+    import torch
+    n = lora4_workspace_bytes(which, base.abi(), M, r)
+    if n == 0:
+        raise ValueError("invalid arguments for lora4_workspace_bytes")
+    return torch.empty((n,), dtype=torch.uint8, device=base.codes.device)
+
+
+def forward(base, X, A, B, s, group_offsets=None, want_z=True, want_parts=False, workspace=None):
+    """Y (and Z, Y_base, Y_lora) for bf16 X [M, K], A [(E,) r, K], B [(E,) N, r]."""
+    import torch
+    M = X.shape[0]
+    r = A.shape[-2]
+    dev = X.device
+    Y = torch.empty((M, base.N), dtype=torch.bfloat16, device=dev)
+    Z = torch.empty((M, r), dtype=torch.bfloat16, device=dev) if want_z else None
+    Yb = torch.empty_like(Y) if want_parts else None
+    Yl = torch.empty_like(Y) if want_parts else None
+    W = base.abi()
+    if workspace is None:
+        workspace = workspace_for(0, base, M, r)
+    st = lora4_forward(W, _ptr(X), M, _ptr(A), _ptr(B), r, float(s), _ptr(group_offsets), _ptr(Y), _ptr(Z),
+                       _ptr(Yb), _ptr(Yl), _ptr(workspace), workspace.numel(), _stream())
+    _check(st, "lora4_forward")
+    return {"Y": Y, "Z": Z, "Y_base": Yb, "Y_lora": Yl}
+
+
+def backward(base, X, dY, A, B, s, Z=None, group_offsets=None, workspace=None):
+    """dX, dA, dB for bf16 inputs (Z from forward, or None to recompute)."""
+    import torch
+    M = X.shape[0]
+    r = A.shape[-2]
+    dX = torch.empty((M, base.K), dtype=torch.bfloat16, device=X.device)
+    dA = torch.empty_like(A)
+    dB = torch.empty_like(B)
+    W = base.abi()
+    if workspace is None:
+        workspace = workspace_for(1, base, M, r)
+    st = lora4_backward(W, _ptr(X), _ptr(dY), M, _ptr(A), _ptr(B), r, float(s), _ptr(group_offsets), _ptr(Z),
+                        _ptr(dX), _ptr(dA), _ptr(dB), _ptr(workspace), workspace.numel(), _stream())
+    _check(st, "lora4_backward")
+    return {"dX": dX, "dA": dA, "dB": dB}

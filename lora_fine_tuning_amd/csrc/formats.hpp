@@ -1,0 +1,138 @@
+// The 4-bit storage formats of the frozen base and their device decoders.
+//
+// NF4 ("Training LLMs on a Budget: LoRA, QLoRA, and LoftQ", section 3, trick
+// 1): 16 levels at normal quantiles, normalised to [-1, 1], applied per block
+// of 64 consecutive K-elements with an fp32 absmax scale (trick 2). The
+// dequantized element is bf16(fp32(q[code] * scale)): one fp32 product, one
+// round-to-nearest-even.
+//
+// NF4 double quantization (same section, trick 2): the per-64 scales are
+// stored as OCP E4M3FN codes with one fp32 second-level scale per 256
+// consecutive first-level scales; the rebuilt scale is
+// fp32(E4M3(code) * scale2).
+//
+// MXFP4 ("Fine-Tuning 4-Bit Models", section "Case 2"): E2M1 codes with one
+// E8M0 scale 2^(E-127) per 32 consecutive K-elements. gfx950's
+// v_cvt_scalef32_pk_bf16_fp4 converts two codes and the scale to two bf16
+// values; it agrees bit for bit with the exact product rounded to bf16 for
+// all 16 x 16 code pairs and all finite scales (checked on the device).
+//
+// Packing (all formats): byte j of a row holds element 2j in its low nibble
+// and element 2j+1 in its high nibble.
+#pragma once
+
+#include "common.hpp"
+
+namespace lora4 {
+
+enum Fmt : int { FMT_BF16 = 0, FMT_NF4 = 1, FMT_NF4_DQ = 2, FMT_MXFP4 = 3 };
+
+// The NF4 levels (ascending) and the 15 decision thresholds of the encoder.
+// thr[i] is the largest fp32 value not above the exact midpoint of levels i
+// and i+1, so "x > thr[i]" holds exactly when x is strictly nearer level
+// i+1: counting exceeded thresholds gives the nearest level, ties to the
+// lower one. Both tables are built on the host (lora4_abi.cpp).
+struct Nf4Table {
+  float q[16];
+  float thr[15];
+};
+
+// E4M3FN code -> float (exact). 0x7F / 0xFF are NaN.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  uint32_t s = (c >> 7) & 1u, e = (c >> 3) & 15u, m = c & 7u;
+  float mag;
+  if ((c & 0x7Fu) == 0x7Fu) {
+    mag = __builtin_nanf("");
+  } else if (e == 0) {
+    mag = (float)m * 0x1p-9f;
+  } else {
+    mag = __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20));
+  }
+  return s ? -mag : mag;
+}
+
+// E8M0 code -> the fp32 scale operand of v_cvt_scalef32_pk_bf16_fp4:
+// 2^(E-127); E = 0 is the fp32 subnormal 2^-127; E = 255 is NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t E) {
+  uint32_t bits = (E == 0u) ? 0x00400000u : (E == 255u ? 0x7FC00000u : (E << 23));
+  return __builtin_bit_cast(float, bits);
+}
+
+// Dequantize 32 consecutive NF4 elements (16 code bytes) sharing one scale
+// into 16 words of bf16 pairs (element 2j in the low half of word j).
+// qlds: the 16 fp32 levels in LDS (each lane reads its own level; the 16
+// entries sit in 16 different banks, so the reads never conflict).
+__device__ __forceinline__ void dequant32_nf4(u32x4_t codes, float scale, const float *qlds,
+                                              uint32_t out[16]) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t w = codes[d];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t lo = (w >> (8 * p)) & 15u;
+      uint32_t hi = (w >> (8 * p + 4)) & 15u;
+      float a = qlds[lo] * scale;
+      float b = qlds[hi] * scale;
+      out[4 * d + p] = pack_bf16x2(a, b);
+    }
+  }
+}
+
+// Dequantize 32 consecutive MXFP4 elements (16 code bytes) sharing one E8M0
+// scale into 16 words of bf16 pairs.
+__device__ __forceinline__ void dequant32_mxfp4(u32x4_t codes, float scale, uint32_t out[16]) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t w = codes[d];
+    out[4 * d + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+    out[4 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+    out[4 * d + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+    out[4 * d + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+  }
+}
+
+// A packed base W as the kernels see it (one group; the kernels add the
+// group offsets).
+struct PackedW {
+  const uint8_t *codes;   // [groups][N][K/2]
+  const void *scales;     // fp32 (NF4), e4m3 u8 (NF4_DQ), e8m0 u8 (MXFP4)
+  const float *scales2;   // NF4_DQ second level, [groups][ceil(N*K/64/256)]
+  int64_t N, K;
+  int64_t g_codes;        // bytes per group
+  int64_t g_scales;       // scale entries per group
+  int64_t g_scales2;      // second-level entries per group
+};
+
+// Scale of the block holding (row n, element k) of group g, as the fp32
+// operand the dequantizer needs (the E8M0 operand for MXFP4).
+template <int FMT>
+__device__ __forceinline__ float block_scale(const PackedW &w, int g, int64_t n, int64_t k) {
+  if constexpr (FMT == FMT_NF4) {
+    const float *s = reinterpret_cast<const float *>(w.scales) + g * w.g_scales;
+    return s[n * (w.K >> 6) + (k >> 6)];
+  } else if constexpr (FMT == FMT_NF4_DQ) {
+    const uint8_t *s = reinterpret_cast<const uint8_t *>(w.scales) + g * w.g_scales;
+    int64_t idx = n * (w.K >> 6) + (k >> 6);
+    float c2 = w.scales2[g * w.g_scales2 + (idx >> 8)];
+    return e4m3_to_f32(s[idx]) * c2;
+  } else {
+    const uint8_t *s = reinterpret_cast<const uint8_t *>(w.scales) + g * w.g_scales;
+    return e8m0_to_f32(s[n * (w.K >> 5) + (k >> 5)]);
+  }
+}
+
+// Dequantize elements k .. k+31 of row n (k a multiple of 32) into 16 words.
+template <int FMT>
+__device__ __forceinline__ void dequant_row32(const PackedW &w, int g, int64_t n, int64_t k,
+                                              const float *qlds, uint32_t out[16]) {
+  const uint8_t *src = w.codes + g * w.g_codes + n * (w.K >> 1) + (k >> 1);
+  u32x4_t codes = ldg_b128_cached(src);
+  float sc = block_scale<FMT>(w, g, n, k);
+  if constexpr (FMT == FMT_MXFP4) {
+    dequant32_mxfp4(codes, sc, out);
+  } else {
+    dequant32_nf4(codes, sc, qlds, out);
+  }
+}
+
+}  // namespace lora4

@@ -1,0 +1,659 @@
+// Tiled bf16 MFMA GEMMs for the LoRA linear, with in-register dequant of the
+// 4-bit base. Three operand forms cover every product of the layer:
+//
+//  NT : C[M, Nc] = A[M, R] . B[Nc, R]^T  (both operands contiguous along R)
+//       forward  Y = X deq(W)^T (+ s Z B^T as a tail) ; Z = X A^T
+//  NN : C[M, Nc] = A[M, R] . B[R, Nc]    (B contiguous along Nc)
+//       dgrad    dX = dY deq(W) (+ dZ A as a tail)    ; dZ = dY B
+//  TN : C[P, Q]  = U[Mr, P]^T . V[Mr, Q] (reduction over rows, split)
+//       dA = dZ^T X ; dB^T = Z^T dY
+//
+// Every product accumulates in fp32 on v_mfma_f32_16x16x32_bf16. A workgroup
+// is 256 threads (4 waves of 64) arranged WAVES_M x WAVES_N, each wave owning
+// a (BM/WAVES_M) x (BN/WAVES_N) block of 16 x 16 MFMA tiles. The reduction
+// advances 64 at a time: global loads for step s+1 are issued before the
+// MFMAs of step s run, so memory latency overlaps compute.
+//
+// The 4-bit base is read as packed nibbles (16 bytes = 32 elements per
+// thread and step), dequantized in registers to bf16 and written to LDS; the
+// bf16 copy of W exists only there, one tile at a time. For NN the tile is
+// stored as it lies in memory (rows = reduction index) and the MFMA operand
+// is fetched with the transposing read ds_read_b64_tr_b16, so dgrad
+// dequantizes along the same axis as its scale blocks.
+#pragma once
+
+#include "formats.hpp"
+
+namespace lora4 {
+
+constexpr int BK = 64;          // reduction step
+constexpr int THREADS = 256;
+constexpr int APAD = 8;         // bf16 padding per LDS row of K-contiguous tiles
+constexpr int CPAD = 16;        // bf16 padding per LDS row of column-contiguous tiles
+
+// --------------------------------------------------------------------------
+// Operand descriptions
+// --------------------------------------------------------------------------
+
+// bf16 matrix, row-major with leading dimension ld (elements); per-group
+// element offset gstride (0 when the operand is shared by all groups).
+struct Mat {
+  const uint16_t *p;
+  int64_t ld;
+  int64_t gstride;
+};
+
+struct GemmOut {
+  uint16_t *C;        // bf16 output (or nullptr)
+  int64_t ldc;
+  float *part;        // fp32 split partials [split][rows][cols] (or nullptr)
+  int64_t part_stride;// elements between splits
+  float alpha;        // scale applied before rounding (bf16 output only)
+};
+
+struct NtParams {
+  Mat A;              // [M, R] rows indexed absolutely (shared across groups)
+  Mat B;              // FMT_BF16: [Nc, R] per group
+  PackedW W;          // packed base (FMT != BF16)
+  int64_t R;          // main reduction length
+  Mat A2;             // tail A [M, r2] (absolute rows)
+  Mat B2;             // tail B [Nc, r2] per group
+  int r2;             // tail reduction length (0: no tail)
+  int64_t M, Nc;
+  const int64_t *offsets;
+  int groups;
+  int64_t Rsplit;     // reduction elements per split (multiple of 64); splits = gridDim.z
+  GemmOut out;
+  Nf4Table tab;
+};
+
+struct NnParams {
+  Mat A;              // [M, R]
+  Mat B;              // FMT_BF16: [R, Nc] per group
+  PackedW W;          // packed base [R = N rows][Nc = K cols]
+  int64_t R;
+  Mat A2;             // tail A [M, r2]
+  Mat B2;             // tail B [r2, Nc] per group
+  int r2;
+  int64_t M, Nc;
+  const int64_t *offsets;
+  int groups;
+  int64_t Rsplit;
+  GemmOut out;
+  Nf4Table tab;
+};
+
+struct TnParams {
+  Mat U;              // [Mrows, P] (absolute rows)
+  Mat V;              // [Mrows, Q]
+  int64_t P, Q, M;
+  const int64_t *offsets;
+  int groups;
+  int splits;         // row splits per group (gridDim.z == splits)
+  float *part;        // [splits][groups][P][Q]
+};
+
+// --------------------------------------------------------------------------
+// Tile loaders
+// --------------------------------------------------------------------------
+
+// Loads a rows x 64 bf16 slab (reduction contiguous) into registers:
+// each thread holds NCH 16-byte chunks. Chunk c of thread t is
+// idx = t + 256 c: row idx / 8, columns 8 (idx % 8) .. +7.
+template <int ROWS>
+struct SlabRegs {
+  static constexpr int NCH = ROWS * 8 / THREADS > 0 ? ROWS * 8 / THREADS : 1;
+  u32x4_t v[NCH];
+};
+
+template <int ROWS>
+__device__ __forceinline__ void load_slab(SlabRegs<ROWS> &r, const uint16_t *base, int64_t ld,
+                                          int64_t row0, int64_t row_end, int64_t k0, int64_t kend,
+                                          bool vec_ok) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int c = 0; c < SlabRegs<ROWS>::NCH; ++c) {
+    int idx = t + THREADS * c;
+    int row = idx >> 3;
+    int col = (idx & 7) * 8;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (idx < ROWS * 8) {
+      int64_t gr = row0 + row;
+      int64_t gk = k0 + col;
+      if (gr < row_end && gk < kend) {
+        const uint16_t *src = base + gr * ld + gk;
+        if (vec_ok && gk + 8 <= kend) {
+          v = ldg_b128_cached(src);
+        } else {
+          uint32_t w[4] = {0u, 0u, 0u, 0u};
+          for (int j = 0; j < 8; ++j) {
+            if (gk + j < kend) w[j >> 1] |= (uint32_t)src[j] << (16 * (j & 1));
+          }
+          v = u32x4_t{w[0], w[1], w[2], w[3]};
+        }
+      }
+    }
+    r.v[c] = v;
+  }
+}
+
+template <int ROWS>
+__device__ __forceinline__ void store_slab(const SlabRegs<ROWS> &r, uint16_t *lds) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int c = 0; c < SlabRegs<ROWS>::NCH; ++c) {
+    int idx = t + THREADS * c;
+    if (idx < ROWS * 8) {
+      int row = idx >> 3;
+      int col = (idx & 7) * 8;
+      lds_write_b128(lds + row * (BK + APAD) + col, r.v[c]);
+    }
+  }
+}
+
+// Packed slab: ROWS x 64 elements of W (NT: rows = output n, 64 along K).
+// Task c of thread t: idx = t + 256 c covers row idx / 2, half idx % 2
+// (32 elements). Holds the raw codes and the scale until the LDS store.
+template <int ROWS>
+struct PackedSlabRegs {
+  static constexpr int NT = ROWS * 2 / THREADS > 0 ? ROWS * 2 / THREADS : 1;
+  u32x4_t codes[NT];
+  float scale[NT];
+};
+
+// --------------------------------------------------------------------------
+// NT kernel
+// --------------------------------------------------------------------------
+
+template <int FMT, int BM, int BN, int WAVES_M>
+__global__ __launch_bounds__(THREADS) void k_gemm_nt(NtParams p) {
+  constexpr int WAVES_N = 4 / WAVES_M;
+  constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  constexpr int FM = WTM / 16, FN = WTN / 16;
+  static_assert(FM >= 1 && FN >= 1, "wave tile too small");
+
+  __shared__ __attribute__((aligned(16))) uint16_t As[BM * (BK + APAD)];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * (BK + APAD)];
+  __shared__ float qlds[16];
+
+  const RowTile rt = map_row_tile(blockIdx.y, BM, p.offsets, p.groups, p.M);
+  if (rt.group < 0) return;
+  const int g = rt.group;
+  const int64_t row0 = rt.row0, row_end = rt.row_end;
+  const int64_t col0 = (int64_t)blockIdx.x * BN;
+  const int split = blockIdx.z;
+
+  if (threadIdx.x < 16) qlds[threadIdx.x] = p.tab.q[threadIdx.x];
+
+  // reduction ranges: main [rb, re) of R, then the tail [0, r2) (last split only)
+  const int64_t rb = (int64_t)split * p.Rsplit;
+  const int64_t re = rb + p.Rsplit < p.R ? rb + p.Rsplit : p.R;
+  const int main_steps = re > rb ? (int)((re - rb + BK - 1) / BK) : 0;
+  const bool has_tail = p.r2 > 0 && split == (int)gridDim.z - 1;
+  const int tail_steps = has_tail ? (p.r2 + BK - 1) / BK : 0;
+  const int steps = main_steps + tail_steps;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm0 = (wave % WAVES_M) * WTM, wn0 = (wave / WAVES_M) * WTN;
+
+  f32x4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const bool a_vec = (p.A.ld % 8) == 0;
+  const bool a2_vec = (p.A2.ld % 8) == 0;
+  const bool b_vec = (p.B.ld % 8) == 0;
+  const bool b2_vec = (p.B2.ld % 8) == 0;
+  const uint16_t *Bg = p.B.p ? p.B.p + g * p.B.gstride : nullptr;
+  const uint16_t *B2g = p.B2.p ? p.B2.p + g * p.B2.gstride : nullptr;
+
+  SlabRegs<BM> ra;
+  SlabRegs<BN> rb_bf;
+  PackedSlabRegs<BN> rb_pk;
+
+  auto issue = [&](int s) {
+    if (s < main_steps) {
+      const int64_t k0 = rb + (int64_t)s * BK;
+      load_slab<BM>(ra, p.A.p, p.A.ld, row0, row_end, k0, re, a_vec);
+      if constexpr (FMT == FMT_BF16) {
+        load_slab<BN>(rb_bf, Bg, p.B.ld, col0, p.Nc, k0, re, b_vec);
+      } else {
+#pragma unroll
+        for (int c = 0; c < PackedSlabRegs<BN>::NT; ++c) {
+          int idx = threadIdx.x + THREADS * c;
+          int row = idx >> 1, half = idx & 1;
+          int64_t n = col0 + row, k = k0 + half * 32;
+          u32x4_t cz = {0u, 0u, 0u, 0u};
+          float sc = 0.f;
+          if (idx < BN * 2 && n < p.Nc && k < re) {
+            const uint8_t *src = p.W.codes + g * p.W.g_codes + n * (p.W.K >> 1) + (k >> 1);
+            cz = ldg_b128_cached(src);
+            sc = block_scale<FMT>(p.W, g, n, k);
+          }
+          rb_pk.codes[c] = cz;
+          rb_pk.scale[c] = sc;
+        }
+      }
+    } else {
+      const int64_t k0 = (int64_t)(s - main_steps) * BK;
+      load_slab<BM>(ra, p.A2.p, p.A2.ld, row0, row_end, k0, p.r2, a2_vec);
+      load_slab<BN>(rb_bf, B2g, p.B2.ld, col0, p.Nc, k0, p.r2, b2_vec);
+    }
+  };
+
+  auto commit = [&](int s) {
+    store_slab<BM>(ra, As);
+    if (FMT == FMT_BF16 || s >= main_steps) {
+      store_slab<BN>(rb_bf, Bs);
+    } else {
+#pragma unroll
+      for (int c = 0; c < PackedSlabRegs<BN>::NT; ++c) {
+        int idx = threadIdx.x + THREADS * c;
+        if (idx < BN * 2) {
+          int row = idx >> 1, half = idx & 1;
+          uint32_t w[16];
+          if constexpr (FMT == FMT_MXFP4) {
+            dequant32_mxfp4(rb_pk.codes[c], rb_pk.scale[c], w);
+          } else if constexpr (FMT != FMT_BF16) {
+            dequant32_nf4(rb_pk.codes[c], rb_pk.scale[c], qlds, w);
+          }
+          uint16_t *dst = Bs + row * (BK + APAD) + half * 32;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            lds_write_b128(dst + 8 * q, u32x4_t{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]});
+        }
+      }
+    }
+  };
+
+  __syncthreads();  // qlds visible
+  if (steps > 0) issue(0);
+  for (int s = 0; s < steps; ++s) {
+    commit(s);
+    __syncthreads();
+    if (s + 1 < steps) issue(s + 1);
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 32) {
+      u32x4_t af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = lds_read_b128(As + (wm0 + i * 16 + (lane & 15)) * (BK + APAD) + kk + (lane >> 4) * 8);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = lds_read_b128(Bs + (wn0 + j * 16 + (lane & 15)) * (BK + APAD) + kk + (lane >> 4) * 8);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma_16x16x32(af[i], bfr[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+
+  // epilogue: lane holds C[4*(lane/16) + e][lane % 16] of each 16x16 tile
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t col = col0 + wn0 + j * 16 + (lane & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t row = row0 + wm0 + i * 16 + (lane >> 4) * 4 + e;
+        if (row < row_end && col < p.Nc) {
+          if (p.out.part) {
+            p.out.part[split * p.out.part_stride + row * p.Nc + col] = acc[i][j][e];
+          } else {
+            p.out.C[row * p.out.ldc + col] = to_bf16(acc[i][j][e] * p.out.alpha);
+          }
+        }
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// NN kernel
+// --------------------------------------------------------------------------
+
+// Column slab: 64 rows (reduction) x COLS bf16, columns contiguous. Chunk c
+// of thread t: idx = t + 256 c, row idx / (COLS/8), columns 8 (idx % (COLS/8)).
+template <int COLS>
+struct ColSlabRegs {
+  static constexpr int CPR = COLS / 8;                       // chunks per row
+  static constexpr int NCH = (BK * CPR + THREADS - 1) / THREADS;
+  u32x4_t v[NCH];
+};
+
+template <int COLS>
+__device__ __forceinline__ void load_colslab(ColSlabRegs<COLS> &r, const uint16_t *base, int64_t ld,
+                                             int64_t r0, int64_t rend, int64_t c0, int64_t cend,
+                                             bool vec_ok) {
+  constexpr int CPR = ColSlabRegs<COLS>::CPR;
+#pragma unroll
+  for (int c = 0; c < ColSlabRegs<COLS>::NCH; ++c) {
+    int idx = threadIdx.x + THREADS * c;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (idx < BK * CPR) {
+      int row = idx / CPR;
+      int col = (idx % CPR) * 8;
+      int64_t gr = r0 + row, gc = c0 + col;
+      if (gr < rend && gc < cend) {
+        const uint16_t *src = base + gr * ld + gc;
+        if (vec_ok && gc + 8 <= cend) {
+          v = ldg_b128_cached(src);
+        } else {
+          uint32_t w[4] = {0u, 0u, 0u, 0u};
+          for (int j = 0; j < 8; ++j) {
+            if (gc + j < cend) w[j >> 1] |= (uint32_t)src[j] << (16 * (j & 1));
+          }
+          v = u32x4_t{w[0], w[1], w[2], w[3]};
+        }
+      }
+    }
+    r.v[c] = v;
+  }
+}
+
+template <int COLS>
+__device__ __forceinline__ void store_colslab(const ColSlabRegs<COLS> &r, uint16_t *lds) {
+  constexpr int CPR = ColSlabRegs<COLS>::CPR;
+#pragma unroll
+  for (int c = 0; c < ColSlabRegs<COLS>::NCH; ++c) {
+    int idx = threadIdx.x + THREADS * c;
+    if (idx < BK * CPR) {
+      int row = idx / CPR;
+      int col = (idx % CPR) * 8;
+      lds_write_b128(lds + row * (COLS + CPAD) + col, r.v[c]);
+    }
+  }
+}
+
+// Packed column slab: 64 rows x COLS elements of W, 32-element tasks.
+template <int COLS>
+struct PackedColSlabRegs {
+  static constexpr int TPR = COLS / 32;                       // tasks per row
+  static constexpr int NT = (BK * TPR + THREADS - 1) / THREADS;
+  u32x4_t codes[NT];
+  float scale[NT];
+};
+
+// Operand fetch for a column-contiguous LDS tile (rows = reduction): the
+// 16 x 32 block (columns c0..c0+15, reduction rows k0..k0+31 of the tile)
+// as the MFMA B operand (or the A operand of a transposed product).
+__device__ __forceinline__ u32x4_t frag_tr(const uint16_t *lds, int ldr, int k0, int c0, int lane) {
+  const int grp = lane >> 4, j = lane & 15;
+  const uint16_t *p = lds + (k0 + grp * 8 + (j >> 2)) * ldr + c0 + (j & 3) * 4;
+  u32x2_t lo = lds_read_tr16(p);
+  u32x2_t hi = lds_read_tr16(p + 4 * ldr);
+  return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+}
+
+template <int FMT, int BM, int BN, int WAVES_M>
+__global__ __launch_bounds__(THREADS) void k_gemm_nn(NnParams p) {
+  constexpr int WAVES_N = 4 / WAVES_M;
+  constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  constexpr int FM = WTM / 16, FN = WTN / 16;
+  static_assert(FM >= 1 && FN >= 1, "wave tile too small");
+  static_assert(BN % 32 == 0 || FMT == FMT_BF16, "packed tiles need BN % 32 == 0");
+
+  __shared__ __attribute__((aligned(16))) uint16_t As[BM * (BK + APAD)];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[BK * (BN + CPAD)];
+  __shared__ float qlds[16];
+
+  const RowTile rt = map_row_tile(blockIdx.y, BM, p.offsets, p.groups, p.M);
+  if (rt.group < 0) return;
+  const int g = rt.group;
+  const int64_t row0 = rt.row0, row_end = rt.row_end;
+  const int64_t col0 = (int64_t)blockIdx.x * BN;
+  const int split = blockIdx.z;
+
+  if (threadIdx.x < 16) qlds[threadIdx.x] = p.tab.q[threadIdx.x];
+
+  const int64_t rb = (int64_t)split * p.Rsplit;
+  const int64_t re = rb + p.Rsplit < p.R ? rb + p.Rsplit : p.R;
+  const int main_steps = re > rb ? (int)((re - rb + BK - 1) / BK) : 0;
+  const bool has_tail = p.r2 > 0 && split == (int)gridDim.z - 1;
+  const int tail_steps = has_tail ? (p.r2 + BK - 1) / BK : 0;
+  const int steps = main_steps + tail_steps;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm0 = (wave % WAVES_M) * WTM, wn0 = (wave / WAVES_M) * WTN;
+
+  f32x4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const bool a_vec = (p.A.ld % 8) == 0;
+  const bool a2_vec = (p.A2.ld % 8) == 0;
+  const bool b_vec = (p.B.ld % 8) == 0;
+  const bool b2_vec = (p.B2.ld % 8) == 0;
+  const uint16_t *Bg = p.B.p ? p.B.p + g * p.B.gstride : nullptr;
+  const uint16_t *B2g = p.B2.p ? p.B2.p + g * p.B2.gstride : nullptr;
+
+  SlabRegs<BM> ra;
+  ColSlabRegs<BN> rb_bf;
+  PackedColSlabRegs<BN> rb_pk;
+
+  auto issue = [&](int s) {
+    if (s < main_steps) {
+      const int64_t k0 = rb + (int64_t)s * BK;
+      load_slab<BM>(ra, p.A.p, p.A.ld, row0, row_end, k0, re, a_vec);
+      if constexpr (FMT == FMT_BF16) {
+        load_colslab<BN>(rb_bf, Bg, p.B.ld, k0, re, col0, p.Nc, b_vec);
+      } else {
+        constexpr int TPR = PackedColSlabRegs<BN>::TPR;
+#pragma unroll
+        for (int c = 0; c < PackedColSlabRegs<BN>::NT; ++c) {
+          int idx = threadIdx.x + THREADS * c;
+          int row = idx / TPR, part = idx % TPR;
+          int64_t n = k0 + row, k = col0 + part * 32;
+          u32x4_t cz = {0u, 0u, 0u, 0u};
+          float sc = 0.f;
+          if (idx < BK * TPR && n < re && k < p.Nc) {
+            const uint8_t *src = p.W.codes + g * p.W.g_codes + n * (p.W.K >> 1) + (k >> 1);
+            cz = ldg_b128_cached(src);
+            sc = block_scale<FMT>(p.W, g, n, k);
+          }
+          rb_pk.codes[c] = cz;
+          rb_pk.scale[c] = sc;
+        }
+      }
+    } else {
+      const int64_t k0 = (int64_t)(s - main_steps) * BK;
+      load_slab<BM>(ra, p.A2.p, p.A2.ld, row0, row_end, k0, p.r2, a2_vec);
+      load_colslab<BN>(rb_bf, B2g, p.B2.ld, k0, p.r2, col0, p.Nc, b2_vec);
+    }
+  };
+
+  auto commit = [&](int s) {
+    store_slab<BM>(ra, As);
+    if (FMT == FMT_BF16 || s >= main_steps) {
+      store_colslab<BN>(rb_bf, Bs);
+    } else {
+      constexpr int TPR = PackedColSlabRegs<BN>::TPR;
+#pragma unroll
+      for (int c = 0; c < PackedColSlabRegs<BN>::NT; ++c) {
+        int idx = threadIdx.x + THREADS * c;
+        if (idx < BK * TPR) {
+          int row = idx / TPR, part = idx % TPR;
+          uint32_t w[16];
+          if constexpr (FMT == FMT_MXFP4) {
+            dequant32_mxfp4(rb_pk.codes[c], rb_pk.scale[c], w);
+          } else if constexpr (FMT != FMT_BF16) {
+            dequant32_nf4(rb_pk.codes[c], rb_pk.scale[c], qlds, w);
+          }
+          uint16_t *dst = Bs + row * (BN + CPAD) + part * 32;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            lds_write_b128(dst + 8 * q, u32x4_t{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]});
+        }
+      }
+    }
+  };
+
+  __syncthreads();
+  if (steps > 0) issue(0);
+  for (int s = 0; s < steps; ++s) {
+    commit(s);
+    __syncthreads();
+    if (s + 1 < steps) issue(s + 1);
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 32) {
+      u32x4_t af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = lds_read_b128(As + (wm0 + i * 16 + (lane & 15)) * (BK + APAD) + kk + (lane >> 4) * 8);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[j] = frag_tr(Bs, BN + CPAD, kk, wn0 + j * 16, lane);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma_16x16x32(af[i], bfr[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t col = col0 + wn0 + j * 16 + (lane & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t row = row0 + wm0 + i * 16 + (lane >> 4) * 4 + e;
+        if (row < row_end && col < p.Nc) {
+          if (p.out.part) {
+            p.out.part[split * p.out.part_stride + row * p.Nc + col] = acc[i][j][e];
+          } else {
+            p.out.C[row * p.out.ldc + col] = to_bf16(acc[i][j][e] * p.out.alpha);
+          }
+        }
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// TN kernel: partial[split][g][P][Q] = sum over the split's rows of U^T V
+// --------------------------------------------------------------------------
+
+template <int BP, int BQ, int WAVES_P>
+__global__ __launch_bounds__(THREADS) void k_gemm_tn(TnParams p) {
+  constexpr int WAVES_Q = 4 / WAVES_P;
+  constexpr int WTP = BP / WAVES_P, WTQ = BQ / WAVES_Q;
+  constexpr int FM = WTP / 16, FN = WTQ / 16;
+  static_assert(FM >= 1 && FN >= 1, "wave tile too small");
+
+  __shared__ __attribute__((aligned(16))) uint16_t Us[BK * (BP + CPAD)];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[BK * (BQ + CPAD)];
+
+  const int64_t p0 = (int64_t)blockIdx.x * BP;  // note: x runs over P tiles
+  const int64_t q0 = (int64_t)blockIdx.y * BQ;
+  const int split = blockIdx.z % p.splits;
+  const int g = blockIdx.z / p.splits;
+
+  int64_t ga = 0, gb = p.M;
+  if (p.offsets) {
+    ga = p.offsets[g];
+    gb = p.offsets[g + 1];
+  }
+  const int64_t rows = gb - ga;
+  const int64_t per = ((rows + p.splits - 1) / p.splits + BK - 1) / BK * BK;
+  const int64_t m0 = ga + (int64_t)split * per;
+  const int64_t m1 = m0 + per < gb ? m0 + per : gb;
+  const int steps = m1 > m0 ? (int)((m1 - m0 + BK - 1) / BK) : 0;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wp0 = (wave % WAVES_P) * WTP, wq0 = (wave / WAVES_P) * WTQ;
+
+  f32x4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const bool u_vec = (p.U.ld % 8) == 0;
+  const bool v_vec = (p.V.ld % 8) == 0;
+  ColSlabRegs<BP> ru;
+  ColSlabRegs<BQ> rv;
+
+  auto issue = [&](int s) {
+    const int64_t r0 = m0 + (int64_t)s * BK;
+    load_colslab<BP>(ru, p.U.p, p.U.ld, r0, m1, p0, p.P, u_vec);
+    load_colslab<BQ>(rv, p.V.p, p.V.ld, r0, m1, q0, p.Q, v_vec);
+  };
+
+  if (steps > 0) issue(0);
+  for (int s = 0; s < steps; ++s) {
+    store_colslab<BP>(ru, Us);
+    store_colslab<BQ>(rv, Vs);
+    __syncthreads();
+    if (s + 1 < steps) issue(s + 1);
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 32) {
+      u32x4_t af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = frag_tr(Us, BP + CPAD, kk, wp0 + i * 16, lane);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[j] = frag_tr(Vs, BQ + CPAD, kk, wq0 + j * 16, lane);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma_16x16x32(af[i], bfr[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+
+  float *out = p.part + ((int64_t)split * p.groups + g) * p.P * p.Q;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t q = q0 + wq0 + j * 16 + (lane & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t pp = p0 + wp0 + i * 16 + (lane >> 4) * 4 + e;
+        if (pp < p.P && q < p.Q) out[pp * p.Q + q] = acc[i][j][e];
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Deterministic reductions of split partials
+// --------------------------------------------------------------------------
+
+// out1[i] = bf16(alpha1 * sum_s part[s][i]); out2 (optional) with alpha2.
+__global__ void k_reduce_bf16(const float *part, int splits, int64_t stride, int64_t n,
+                              uint16_t *out1, float alpha1, uint16_t *out2, float alpha2) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  for (int k = 0; k < splits; ++k) s += part[k * stride + i];
+  if (out1) out1[i] = to_bf16(s * alpha1);
+  if (out2) out2[i] = to_bf16(s * alpha2);
+}
+
+// dB[g][n][j] = bf16(alpha * sum_s part[s][g][j][n]) (partials hold dB^T).
+__global__ void k_reduce_transpose_bf16(const float *part, int splits, int groups, int64_t P,
+                                        int64_t Q, uint16_t *out, float alpha) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // index into out [g][Q][P]
+  int64_t total = (int64_t)groups * P * Q;
+  if (i >= total) return;
+  int64_t g = i / (P * Q);
+  int64_t rem = i - g * P * Q;
+  int64_t q = rem / P, pp = rem - q * P;
+  float s = 0.f;
+  for (int k = 0; k < splits; ++k) s += part[((int64_t)k * groups + g) * P * Q + pp * Q + q];
+  out[i] = to_bf16(s * alpha);
+}
+
+__global__ void k_fill_u16(uint16_t *p, int64_t n, uint16_t v) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+}  // namespace lora4

@@ -1,0 +1,675 @@
+// liblora4: the C ABI (include/lora4.h) over the gfx950 kernels.
+//
+// Host responsibilities: validate every argument before any HIP call, plan
+// the split factors and workspace layout, and sequence the kernels on the
+// caller's stream:
+//
+//   forward : Z pass (X A^T, split over K) -> reduce (Z, s Z)
+//             -> base GEMM X deq(W)^T with the rank-r tail (s Z) B^T -> Y
+//   backward: [Z pass if Z is not given] -> dZ pass (dY B, split over N) ->
+//             reduce (s dY B) -> dgrad dY deq(W) with tail dZ A -> dX
+//             -> dA = dZ^T X and dB^T = Z^T dY (split over rows) -> reduces
+//
+// The NF4 codebook and the encoder thresholds are derived here from their
+// definition ("Training LLMs on a Budget: LoRA, QLoRA, and LoftQ", section 3,
+// trick 1: 16 normal quantiles, normalised by the largest), with a local
+// inverse normal CDF.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "lora4.h"
+#include "gemm.hpp"
+#include "quant.hpp"
+
+using namespace lora4;
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// NF4 codebook
+// ---------------------------------------------------------------------------
+
+double norm_cdf(double x) { return 0.5 * std::erfc(-x / std::sqrt(2.0)); }
+
+// Inverse of the standard normal CDF: bisection to a bracket, then Newton.
+double norm_ppf(double p) {
+  double lo = -40.0, hi = 40.0;
+  for (int i = 0; i < 200; ++i) {
+    double mid = 0.5 * (lo + hi);
+    if (norm_cdf(mid) < p) lo = mid; else hi = mid;
+  }
+  double x = 0.5 * (lo + hi);
+  for (int i = 0; i < 4; ++i) {
+    double f = norm_cdf(x) - p;
+    double d = std::exp(-0.5 * x * x) / std::sqrt(2.0 * M_PI);
+    if (d == 0.0) break;
+    x -= f / d;
+  }
+  return x;
+}
+
+// Evenly spaced points start..stop (num of them), as i * step + start.
+std::vector<double> spaced(double start, double stop, int num) {
+#pragma clang fp contract(off)
+  std::vector<double> v(num);
+  const double step = (stop - start) / (double)(num - 1);
+  for (int i = 0; i < num; ++i) {
+    double y = (double)i * step;
+    y = y + start;
+    v[i] = y;
+  }
+  v[num - 1] = stop;
+  return v;
+}
+
+Nf4Table build_nf4_table() {
+#pragma clang fp contract(off)
+  // offset: mean of 1 - 1/30 and 1 - 1/32
+  const double delta = 0.5 * ((1.0 - 1.0 / 30.0) + (1.0 - 1.0 / 32.0));
+  std::vector<double> lv;
+  std::vector<double> pp = spaced(delta, 0.5, 9);
+  for (int i = 0; i < 8; ++i) lv.push_back(norm_ppf(pp[i]));          // 8 positive levels
+  std::vector<double> pn = spaced(delta, 0.5, 8);
+  for (int i = 0; i < 7; ++i) lv.push_back(-norm_ppf(pn[i]));         // 7 negative levels
+  lv.push_back(0.0);                                                   // exact zero
+  std::sort(lv.begin(), lv.end());
+  const double mx = lv.back();
+  Nf4Table t;
+  for (int i = 0; i < 16; ++i) t.q[i] = (float)(lv[i] / mx);
+  for (int i = 0; i < 15; ++i) {
+    const double mid = ((double)t.q[i] + (double)t.q[i + 1]) * 0.5;   // exact
+    float th = (float)mid;
+    if ((double)th > mid) th = std::nextafter(th, -INFINITY);
+    t.thr[i] = th;
+  }
+  return t;
+}
+
+const Nf4Table &nf4_table() {
+  static const Nf4Table t = build_nf4_table();
+  return t;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel timing (profiling aid)
+// ---------------------------------------------------------------------------
+
+struct PendingTiming {
+  const char *name;
+  hipEvent_t a, b;
+};
+
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<PendingTiming> g_pending;
+std::vector<hipEvent_t> g_free_events;
+
+hipEvent_t take_event() {
+  if (!g_free_events.empty()) {
+    hipEvent_t e = g_free_events.back();
+    g_free_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <typename Kern, typename Params>
+lora4_status launch(const char *name, Kern kernel, dim3 grid, dim3 block, const Params &params,
+                    hipStream_t stream) {
+  if (grid.x == 0 || grid.y == 0 || grid.z == 0) return LORA4_OK;
+  hipEvent_t ea = nullptr, eb = nullptr;
+  bool timed = false;
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    if (g_timing) {
+      ea = take_event();
+      eb = take_event();
+      timed = ea && eb;
+    }
+  }
+  if (timed && hipEventRecord(ea, stream) != hipSuccess) return LORA4_ERR_HIP;
+  hipLaunchKernelGGL(kernel, grid, block, 0, stream, params);
+  if (hipGetLastError() != hipSuccess) return LORA4_ERR_HIP;
+  if (timed) {
+    if (hipEventRecord(eb, stream) != hipSuccess) return LORA4_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_tmu);
+    g_pending.push_back({name, ea, eb});
+  }
+  return LORA4_OK;
+}
+
+template <typename Kern, typename... Args>
+lora4_status launch_args(const char *name, Kern kernel, dim3 grid, dim3 block, hipStream_t stream,
+                         Args... args) {
+  if (grid.x == 0 || grid.y == 0 || grid.z == 0) return LORA4_OK;
+  hipEvent_t ea = nullptr, eb = nullptr;
+  bool timed = false;
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    if (g_timing) {
+      ea = take_event();
+      eb = take_event();
+      timed = ea && eb;
+    }
+  }
+  if (timed && hipEventRecord(ea, stream) != hipSuccess) return LORA4_ERR_HIP;
+  hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+  if (hipGetLastError() != hipSuccess) return LORA4_ERR_HIP;
+  if (timed) {
+    if (hipEventRecord(eb, stream) != hipSuccess) return LORA4_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_tmu);
+    g_pending.push_back({name, ea, eb});
+  }
+  return LORA4_OK;
+}
+
+#define TRY(x)                              \
+  do {                                      \
+    lora4_status st_ = (x);                 \
+    if (st_ != LORA4_OK) return st_;        \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// Validation helpers
+// ---------------------------------------------------------------------------
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+lora4_status check_W(const lora4_W *W) {
+  if (!W) return LORA4_ERR_NULL;
+  if (W->format != LORA4_NF4 && W->format != LORA4_NF4_DQ && W->format != LORA4_MXFP4) return LORA4_ERR_FORMAT;
+  const int want = W->format == LORA4_MXFP4 ? 32 : 64;
+  if (W->block != want) return LORA4_ERR_FORMAT;
+  if (W->N < 1 || W->K < want || W->K % want != 0 || W->groups < 1) return LORA4_ERR_SHAPE;
+  if (W->N > (int64_t(1) << 31) || W->K > (int64_t(1) << 31) || W->groups > 65535) return LORA4_ERR_SHAPE;
+  if (!W->codes || !W->scales) return LORA4_ERR_NULL;
+  if (W->format == LORA4_NF4_DQ && !W->scales2) return LORA4_ERR_NULL;
+  if (!aligned16(W->codes) || !aligned16(W->scales)) return LORA4_ERR_ALIGN;
+  if (W->format == LORA4_NF4_DQ && !aligned16(W->scales2)) return LORA4_ERR_ALIGN;
+  return LORA4_OK;
+}
+
+PackedW packed_of(const lora4_W *W) {
+  PackedW p;
+  p.codes = W->codes;
+  p.scales = W->scales;
+  p.scales2 = W->scales2;
+  p.N = W->N;
+  p.K = W->K;
+  p.g_codes = W->N * (W->K / 2);
+  p.g_scales = W->N * (W->K / W->block);
+  p.g_scales2 = W->format == LORA4_NF4_DQ ? ceil_div(W->N * (W->K / 64), 256) : 0;
+  return p;
+}
+
+// ---------------------------------------------------------------------------
+// Planning: split factors and workspace layout
+// ---------------------------------------------------------------------------
+
+constexpr int TARGET_WG = 1024;  // workgroups wanted for the skinny passes
+
+int skinny_tile(int r) { return r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : 128; }
+
+// Splits of a reduction of length R (units of 64) for a skinny product
+// with `tiles` output tiles.
+int choose_split(int64_t tiles, int64_t R) {
+  int64_t want = ceil_div(TARGET_WG, std::max<int64_t>(tiles, 1));
+  int64_t maxs = std::max<int64_t>(1, R / 512);
+  return (int)std::max<int64_t>(1, std::min(want, maxs));
+}
+
+int64_t split_len(int64_t R, int splits) { return ceil_div(ceil_div(R, splits), 64) * 64; }
+
+struct Plan {
+  int64_t M, N, K, E;
+  int r;
+  int rt;             // skinny tile width (Z, dZ, TN P tile)
+  int64_t row_slots;  // row-tile slots for BM = 128
+  int zsplit;         // Z pass splits over K
+  int64_t zlen;
+  int dzsplit;        // dZ pass splits over N
+  int64_t dzlen;
+  int tq_a, tq_b;     // TN Q tiles (dA over K, dB over N)
+  int msplit_a, msplit_b;
+  // workspace offsets
+  size_t off_sz, off_zw, off_dz, off_part, bytes;
+};
+
+constexpr int BM_MAIN = 128, BN_MAIN = 128;
+constexpr int BM_SKINNY = 128;
+constexpr int TN_BQ = 128;
+
+Plan make_plan(int which, const lora4_W *W, int64_t M, int r) {
+  Plan p{};
+  p.M = M;
+  p.N = W->N;
+  p.K = W->K;
+  p.E = W->groups;
+  p.r = r;
+  p.rt = skinny_tile(r);
+  p.row_slots = ceil_div(std::max<int64_t>(M, 1), BM_MAIN) + (p.E > 1 ? p.E : 0);
+  const int64_t rtiles = ceil_div(r, p.rt);
+  p.zsplit = choose_split(p.row_slots * rtiles, p.K);
+  p.zlen = split_len(p.K, p.zsplit);
+  p.zsplit = (int)ceil_div(p.K, p.zlen);
+  p.dzsplit = choose_split(p.row_slots * rtiles, p.N);
+  p.dzlen = split_len(p.N, p.dzsplit);
+  p.dzsplit = (int)ceil_div(p.N, p.dzlen);
+  p.tq_a = (int)ceil_div(p.K, TN_BQ);
+  p.tq_b = (int)ceil_div(p.N, TN_BQ);
+  const int64_t mavg = std::max<int64_t>(1, M / p.E);
+  auto msplit = [&](int64_t qtiles) {
+    int64_t tiles = rtiles * qtiles * p.E;
+    int64_t want = ceil_div(TARGET_WG, std::max<int64_t>(tiles, 1));
+    int64_t maxs = std::max<int64_t>(1, mavg / 256);
+    return (int)std::max<int64_t>(1, std::min<int64_t>({want, maxs, 65535 / p.E}));
+  };
+  p.msplit_a = msplit(p.tq_a);
+  p.msplit_b = msplit(p.tq_b);
+
+  const size_t mr2 = align256((size_t)M * r * 2);
+  size_t off = 0;
+  p.off_sz = off;   // forward: s Z ; backward: dZ
+  off += mr2;
+  p.off_zw = off;   // backward: recomputed Z
+  if (which == 1) off += mr2;
+  p.off_dz = p.off_sz;
+  p.off_part = off;
+  size_t part = (size_t)p.zsplit * M * r * 4;
+  if (which == 1) {
+    part = std::max(part, (size_t)p.dzsplit * M * r * 4);
+    part = std::max(part, (size_t)p.msplit_a * p.E * r * p.K * 4);
+    part = std::max(part, (size_t)p.msplit_b * p.E * r * p.N * 4);
+  }
+  off += align256(part);
+  p.bytes = std::max<size_t>(off, 256);   // never 0: 0 reports invalid arguments
+  return p;
+}
+
+template <typename T>
+T *ws_at(void *ws, size_t off) {
+  return reinterpret_cast<T *>(reinterpret_cast<char *>(ws) + off);
+}
+
+// ---------------------------------------------------------------------------
+// Kernel dispatch (template instantiations by runtime shape)
+// ---------------------------------------------------------------------------
+
+template <int FMT>
+lora4_status run_nt_main(const NtParams &p, dim3 grid, hipStream_t st) {
+  return launch("gemm_nt_base", k_gemm_nt<FMT, BM_MAIN, BN_MAIN, 2>, grid, dim3(THREADS), p, st);
+}
+
+lora4_status run_nt_main_fmt(int fmt, const NtParams &p, dim3 grid, hipStream_t st) {
+  switch (fmt) {
+    case LORA4_NF4: return run_nt_main<FMT_NF4>(p, grid, st);
+    case LORA4_NF4_DQ: return run_nt_main<FMT_NF4_DQ>(p, grid, st);
+    case LORA4_MXFP4: return run_nt_main<FMT_MXFP4>(p, grid, st);
+  }
+  return LORA4_ERR_FORMAT;
+}
+
+template <int FMT>
+lora4_status run_nn_main(const NnParams &p, dim3 grid, hipStream_t st) {
+  return launch("gemm_nn_dgrad", k_gemm_nn<FMT, BM_MAIN, BN_MAIN, 2>, grid, dim3(THREADS), p, st);
+}
+
+lora4_status run_nn_main_fmt(int fmt, const NnParams &p, dim3 grid, hipStream_t st) {
+  switch (fmt) {
+    case LORA4_NF4: return run_nn_main<FMT_NF4>(p, grid, st);
+    case LORA4_NF4_DQ: return run_nn_main<FMT_NF4_DQ>(p, grid, st);
+    case LORA4_MXFP4: return run_nn_main<FMT_MXFP4>(p, grid, st);
+  }
+  return LORA4_ERR_FORMAT;
+}
+
+lora4_status run_nt_skinny(int rt, const NtParams &p, dim3 grid, hipStream_t st) {
+  switch (rt) {
+    case 16: return launch("gemm_nt_lora_down", k_gemm_nt<FMT_BF16, BM_SKINNY, 16, 4>, grid, dim3(THREADS), p, st);
+    case 32: return launch("gemm_nt_lora_down", k_gemm_nt<FMT_BF16, BM_SKINNY, 32, 4>, grid, dim3(THREADS), p, st);
+    case 64: return launch("gemm_nt_lora_down", k_gemm_nt<FMT_BF16, BM_SKINNY, 64, 4>, grid, dim3(THREADS), p, st);
+    default: return launch("gemm_nt_lora_down", k_gemm_nt<FMT_BF16, BM_SKINNY, 128, 2>, grid, dim3(THREADS), p, st);
+  }
+}
+
+lora4_status run_nn_skinny(int rt, const NnParams &p, dim3 grid, hipStream_t st) {
+  switch (rt) {
+    case 16: return launch("gemm_nn_lora_dz", k_gemm_nn<FMT_BF16, BM_SKINNY, 16, 4>, grid, dim3(THREADS), p, st);
+    case 32: return launch("gemm_nn_lora_dz", k_gemm_nn<FMT_BF16, BM_SKINNY, 32, 4>, grid, dim3(THREADS), p, st);
+    case 64: return launch("gemm_nn_lora_dz", k_gemm_nn<FMT_BF16, BM_SKINNY, 64, 4>, grid, dim3(THREADS), p, st);
+    default: return launch("gemm_nn_lora_dz", k_gemm_nn<FMT_BF16, BM_SKINNY, 128, 2>, grid, dim3(THREADS), p, st);
+  }
+}
+
+lora4_status run_tn(const char *name, int rt, const TnParams &p, dim3 grid, hipStream_t st) {
+  switch (rt) {
+    case 16: return launch(name, k_gemm_tn<16, TN_BQ, 1>, grid, dim3(THREADS), p, st);
+    case 32: return launch(name, k_gemm_tn<32, TN_BQ, 1>, grid, dim3(THREADS), p, st);
+    case 64: return launch(name, k_gemm_tn<64, TN_BQ, 1>, grid, dim3(THREADS), p, st);
+    default: return launch(name, k_gemm_tn<128, TN_BQ, 2>, grid, dim3(THREADS), p, st);
+  }
+}
+
+Mat mat(const uint16_t *p, int64_t ld, int64_t gstride = 0) { return Mat{p, ld, gstride}; }
+
+lora4_status reduce_bf16(const char *name, const float *part, int splits, int64_t stride, int64_t n,
+                         uint16_t *out1, float a1, uint16_t *out2, float a2, hipStream_t st) {
+  dim3 grid((unsigned)ceil_div(n, 256));
+  return launch_args(name, k_reduce_bf16, grid, dim3(256), st, part, splits, stride, n, out1, a1, out2, a2);
+}
+
+// Z = X A^T (per group), written as bf16 to z1 (scale a1) and z2 (scale a2).
+lora4_status z_pass(const Plan &pl, const lora4_W *W, const uint16_t *X, const uint16_t *A,
+                    const int64_t *offs, float *part, uint16_t *z1, float a1, uint16_t *z2, float a2,
+                    hipStream_t st) {
+  NtParams p{};
+  p.A = mat(X, pl.K);
+  p.B = mat(A, pl.K, (int64_t)pl.r * pl.K);
+  p.R = pl.K;
+  p.r2 = 0;
+  p.M = pl.M;
+  p.Nc = pl.r;
+  p.offsets = offs;
+  p.groups = (int)pl.E;
+  p.Rsplit = pl.zlen;
+  p.out = GemmOut{nullptr, 0, part, pl.M * pl.r, 1.0f};
+  p.tab = nf4_table();
+  dim3 grid((unsigned)ceil_div(pl.r, pl.rt), (unsigned)pl.row_slots, (unsigned)pl.zsplit);
+  TRY(run_nt_skinny(pl.rt, p, grid, st));
+  return reduce_bf16("reduce_z", part, pl.zsplit, pl.M * pl.r, pl.M * pl.r, z1, a1, z2, a2, st);
+}
+
+lora4_status check_common(const lora4_W *W, int64_t M, int32_t r, float s, const int64_t *offs) {
+  TRY(check_W(W));
+  if (M < 0 || M > (int64_t(1) << 31)) return LORA4_ERR_SHAPE;
+  if (r < 1 || r > 256) return LORA4_ERR_SHAPE;
+  if (!std::isfinite(s)) return LORA4_ERR_SHAPE;
+  if (W->groups > 1 && !offs) return LORA4_ERR_NULL;
+  if (W->groups == 1 && offs) return LORA4_ERR_SHAPE;
+  return LORA4_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+// Exported C ABI
+// ===========================================================================
+
+#pragma GCC visibility push(default)
+extern "C" {
+
+const char *lora4_version(void) { return "lora4 0.1 (gfx950)"; }
+
+const char *lora4_status_string(lora4_status s) {
+  switch (s) {
+    case LORA4_OK: return "ok";
+    case LORA4_ERR_NULL: return "a required pointer is NULL";
+    case LORA4_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case LORA4_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case LORA4_ERR_FORMAT: return "unknown format or block size";
+    case LORA4_ERR_WORKSPACE: return "workspace missing or too small";
+    case LORA4_ERR_HIP: return "a HIP call or kernel launch failed";
+    case LORA4_ERR_UNIMPLEMENTED: return "not supported by this build";
+  }
+  return "unknown status";
+}
+
+size_t lora4_workspace_bytes(int which, const lora4_W *W, int64_t M, int32_t r) {
+  if ((which != 0 && which != 1) || check_W(W) != LORA4_OK || M < 0 || r < 1 || r > 256) return 0;
+  return make_plan(which, W, M, r).bytes;
+}
+
+lora4_status lora4_forward(const lora4_W *W, const uint16_t *X, int64_t M, const uint16_t *A,
+                           const uint16_t *B, int32_t r, float s, const int64_t *group_offsets,
+                           uint16_t *Y, uint16_t *Z, uint16_t *Y_base, uint16_t *Y_lora,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  TRY(check_common(W, M, r, s, group_offsets));
+  if (!A || !B || (M > 0 && (!X || !Y))) return LORA4_ERR_NULL;
+  for (const void *q : {(const void *)X, (const void *)A, (const void *)B, (const void *)Y, (const void *)Z,
+                        (const void *)Y_base, (const void *)Y_lora, (const void *)group_offsets})
+    if (q && !aligned16(q)) return LORA4_ERR_ALIGN;
+  const Plan pl = make_plan(0, W, M, r);
+  if (!workspace) return LORA4_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LORA4_ERR_ALIGN;
+  if (workspace_bytes < pl.bytes) return LORA4_ERR_WORKSPACE;
+  if (M == 0) return LORA4_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+
+  uint16_t *sZ = ws_at<uint16_t>(workspace, pl.off_sz);
+  float *part = ws_at<float>(workspace, pl.off_part);
+  TRY(z_pass(pl, W, X, A, group_offsets, part, Z, 1.0f, sZ, s, st));
+
+  NtParams p{};
+  p.A = mat(X, pl.K);
+  p.W = packed_of(W);
+  p.R = pl.K;
+  p.A2 = mat(sZ, r);
+  p.B2 = mat(B, r, pl.N * r);
+  p.r2 = r;
+  p.M = M;
+  p.Nc = pl.N;
+  p.offsets = group_offsets;
+  p.groups = (int)pl.E;
+  p.Rsplit = pl.K;
+  p.out = GemmOut{Y, pl.N, nullptr, 0, 1.0f};
+  p.tab = nf4_table();
+  dim3 grid((unsigned)ceil_div(pl.N, BN_MAIN), (unsigned)pl.row_slots, 1);
+  TRY(run_nt_main_fmt(W->format, p, grid, st));
+  if (Y_base) {
+    NtParams q = p;
+    q.r2 = 0;
+    q.out.C = Y_base;
+    TRY(run_nt_main_fmt(W->format, q, grid, st));
+  }
+  if (Y_lora) {
+    NtParams q = p;
+    q.R = 0;
+    q.Rsplit = 64;
+    q.out.C = Y_lora;
+    TRY(run_nt_main_fmt(W->format, q, grid, st));
+  }
+  return LORA4_OK;
+}
+
+lora4_status lora4_backward(const lora4_W *W, const uint16_t *X, const uint16_t *dY, int64_t M,
+                            const uint16_t *A, const uint16_t *B, int32_t r, float s,
+                            const int64_t *group_offsets, const uint16_t *Z, uint16_t *dX,
+                            uint16_t *dA, uint16_t *dB, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+  TRY(check_common(W, M, r, s, group_offsets));
+  if (!A || !B || !dA || !dB || (M > 0 && (!X || !dY || !dX))) return LORA4_ERR_NULL;
+  for (const void *q : {(const void *)X, (const void *)dY, (const void *)A, (const void *)B, (const void *)Z,
+                        (const void *)dX, (const void *)dA, (const void *)dB, (const void *)group_offsets})
+    if (q && !aligned16(q)) return LORA4_ERR_ALIGN;
+  const Plan pl = make_plan(1, W, M, r);
+  if (!workspace) return LORA4_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LORA4_ERR_ALIGN;
+  if (workspace_bytes < pl.bytes) return LORA4_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (M == 0) {
+    const int64_t na = pl.E * r * pl.K, nb = pl.E * pl.N * r;
+    TRY(launch_args("fill_zero", k_fill_u16, dim3((unsigned)ceil_div(na, 256)), dim3(256), st, dA, na, (uint16_t)0));
+    TRY(launch_args("fill_zero", k_fill_u16, dim3((unsigned)ceil_div(nb, 256)), dim3(256), st, dB, nb, (uint16_t)0));
+    return LORA4_OK;
+  }
+
+  uint16_t *dZ = ws_at<uint16_t>(workspace, pl.off_dz);
+  float *part = ws_at<float>(workspace, pl.off_part);
+  const uint16_t *Zu = Z;
+  if (!Zu) {
+    uint16_t *Zw = ws_at<uint16_t>(workspace, pl.off_zw);
+    TRY(z_pass(pl, W, X, A, group_offsets, part, Zw, 1.0f, nullptr, 0.0f, st));
+    Zu = Zw;
+  }
+
+  // dZ = s dY B  (NN: reduction over N, output r columns)
+  {
+    NnParams p{};
+    p.A = mat(dY, pl.N);
+    p.B = mat(B, r, pl.N * r);
+    p.R = pl.N;
+    p.r2 = 0;
+    p.M = M;
+    p.Nc = r;
+    p.offsets = group_offsets;
+    p.groups = (int)pl.E;
+    p.Rsplit = pl.dzlen;
+    p.out = GemmOut{nullptr, 0, part, M * r, 1.0f};
+    p.tab = nf4_table();
+    dim3 grid((unsigned)ceil_div(r, pl.rt), (unsigned)pl.row_slots, (unsigned)pl.dzsplit);
+    TRY(run_nn_skinny(pl.rt, p, grid, st));
+    TRY(reduce_bf16("reduce_dz", part, pl.dzsplit, M * r, M * r, dZ, s, nullptr, 0.0f, st));
+  }
+
+  // dX = dY deq(W) + dZ A
+  {
+    NnParams p{};
+    p.A = mat(dY, pl.N);
+    p.W = packed_of(W);
+    p.R = pl.N;
+    p.A2 = mat(dZ, r);
+    p.B2 = mat(A, pl.K, (int64_t)r * pl.K);
+    p.r2 = r;
+    p.M = M;
+    p.Nc = pl.K;
+    p.offsets = group_offsets;
+    p.groups = (int)pl.E;
+    p.Rsplit = pl.N;
+    p.out = GemmOut{dX, pl.K, nullptr, 0, 1.0f};
+    p.tab = nf4_table();
+    dim3 grid((unsigned)ceil_div(pl.K, BN_MAIN), (unsigned)pl.row_slots, 1);
+    TRY(run_nn_main_fmt(W->format, p, grid, st));
+  }
+
+  // dA = dZ^T X
+  {
+    TnParams p{};
+    p.U = mat(dZ, r);
+    p.V = mat(X, pl.K);
+    p.P = r;
+    p.Q = pl.K;
+    p.M = M;
+    p.offsets = group_offsets;
+    p.groups = (int)pl.E;
+    p.splits = pl.msplit_a;
+    p.part = part;
+    dim3 grid((unsigned)ceil_div(r, pl.rt), (unsigned)pl.tq_a, (unsigned)(pl.msplit_a * pl.E));
+    TRY(run_tn("gemm_tn_dA", pl.rt, p, grid, st));
+    const int64_t n = pl.E * r * pl.K;
+    TRY(reduce_bf16("reduce_dA", part, pl.msplit_a, n, n, dA, 1.0f, nullptr, 0.0f, st));
+  }
+
+  // dB = s (Z^T dY)^T
+  {
+    TnParams p{};
+    p.U = mat(Zu, r);
+    p.V = mat(dY, pl.N);
+    p.P = r;
+    p.Q = pl.N;
+    p.M = M;
+    p.offsets = group_offsets;
+    p.groups = (int)pl.E;
+    p.splits = pl.msplit_b;
+    p.part = part;
+    dim3 grid((unsigned)ceil_div(r, pl.rt), (unsigned)pl.tq_b, (unsigned)(pl.msplit_b * pl.E));
+    TRY(run_tn("gemm_tn_dB", pl.rt, p, grid, st));
+    const int64_t n = pl.E * r * pl.N;
+    TRY(launch_args("reduce_dB", k_reduce_transpose_bf16, dim3((unsigned)ceil_div(n, 256)), dim3(256), st,
+                    (const float *)part, pl.msplit_b, (int)pl.E, (int64_t)r, pl.N, dB, s));
+  }
+  return LORA4_OK;
+}
+
+lora4_status quant_pack_nf4(const uint16_t *W_bf16, int64_t N, int64_t K, int32_t double_quant,
+                            uint8_t *codes, void *scales, float *scales2, void *stream) {
+  if (!W_bf16 || !codes || !scales) return LORA4_ERR_NULL;
+  if (double_quant && !scales2) return LORA4_ERR_NULL;
+  if (N < 1 || K < 64 || K % 64 != 0 || N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return LORA4_ERR_SHAPE;
+  if (!aligned16(W_bf16) || !aligned16(codes) || !aligned16(scales) || (double_quant && !aligned16(scales2)))
+    return LORA4_ERR_ALIGN;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int64_t nblk = N * (K / 64);
+  if (!double_quant) {
+    return launch_args("quant_pack_nf4", k_quant_nf4, dim3((unsigned)ceil_div(nblk, 256)), dim3(256), st,
+                       W_bf16, N, K, codes, reinterpret_cast<float *>(scales), nf4_table());
+  }
+  return launch_args("quant_pack_nf4_dq", k_quant_nf4_dq, dim3((unsigned)ceil_div(nblk, 256)), dim3(256), st,
+                     W_bf16, N, K, codes, reinterpret_cast<uint8_t *>(scales), scales2, nf4_table());
+}
+
+lora4_status quant_pack_mxfp4(const uint16_t *W_bf16, int64_t N, int64_t K, uint8_t *codes,
+                              uint8_t *scales_e8m0, void *stream) {
+  if (!W_bf16 || !codes || !scales_e8m0) return LORA4_ERR_NULL;
+  if (N < 1 || K < 32 || K % 32 != 0 || N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return LORA4_ERR_SHAPE;
+  if (!aligned16(W_bf16) || !aligned16(codes) || !aligned16(scales_e8m0)) return LORA4_ERR_ALIGN;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int64_t nblk = N * (K / 32);
+  return launch_args("quant_pack_mxfp4", k_quant_mxfp4, dim3((unsigned)ceil_div(nblk, 256)), dim3(256), st,
+                     W_bf16, N, K, codes, scales_e8m0);
+}
+
+lora4_status lora4_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_timing = on != 0;
+  return LORA4_OK;
+}
+
+int lora4_timing_collect(lora4_kernel_time *out, int max) {
+  std::vector<PendingTiming> pend;
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    pend.swap(g_pending);
+  }
+  std::map<std::string, std::pair<int64_t, double>> agg;
+  std::vector<std::string> order;
+  lora4_status st = LORA4_OK;
+  for (auto &t : pend) {
+    float ms = 0.f;
+    if (hipEventSynchronize(t.b) != hipSuccess || hipEventElapsedTime(&ms, t.a, t.b) != hipSuccess) {
+      st = LORA4_ERR_HIP;
+    }
+    auto it = agg.find(t.name);
+    if (it == agg.end()) {
+      order.push_back(t.name);
+      agg[t.name] = {1, (double)ms};
+    } else {
+      it->second.first += 1;
+      it->second.second += ms;
+    }
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    for (auto &t : pend) {
+      g_free_events.push_back(t.a);
+      g_free_events.push_back(t.b);
+    }
+  }
+  if (st != LORA4_OK) return (int)st;
+  int n = 0;
+  for (auto &name : order) {
+    if (out && n < max) {
+      std::memset(out[n].name, 0, sizeof(out[n].name));
+      std::strncpy(out[n].name, name.c_str(), sizeof(out[n].name) - 1);
+      out[n].launches = agg[name].first;
+      out[n].total_ms = agg[name].second;
+    }
+    ++n;
+  }
+  return n;
+}
+
+}  // extern "C"
+#pragma GCC visibility pop

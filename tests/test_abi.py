@@ -1,0 +1,127 @@
+"""CPU tests of the C ABI: the library loads, exports every function that
+include/lora4.h declares, and rejects bad arguments with the documented status
+before any HIP call (so these run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import lora_fine_tuning_amd as L
+from lora_fine_tuning_amd import build as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, ENULL, ESHAPE, EALIGN, EFORMAT, EWS = 0, -1, -2, -3, -4, -5
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        B.build()
+    return L.lib()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "lora4.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_0-9]+)\s*\(", text)) - {"sizeof"})
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert "lora4_forward" in names and "quant_pack_mxfp4" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.EXPORTS)
+
+
+def test_status_strings_and_version(lib):
+    assert L.status_string(0) == "ok"
+    for s in range(-7, 0):
+        assert L.status_string(s) and L.status_string(s) != "unknown status"
+    assert "gfx950" in L.version()
+
+
+def _W(fmt=1, block=64, N=1024, K=1024, groups=1, codes=256, scales=512, scales2=None):
+    return L.lora4_W(fmt, block, N, K, groups, codes, scales, scales2)
+
+
+def test_format_and_block_validation(lib):
+    assert L.lora4_workspace_bytes(0, _W(fmt=9), 16, 16) == 0
+    ws = 1 << 30
+    args = dict(X=4096, M=16, A=4096, B=4096, r=16, s=2.0, offs=None, Y=4096, Z=None, Yb=None, Yl=None,
+                ws=8192, nbytes=ws, stream=None)
+
+    def fwd(W, **kw):
+        a = dict(args, **kw)
+        return L.lora4_forward(W, a["X"], a["M"], a["A"], a["B"], a["r"], a["s"], a["offs"], a["Y"], a["Z"],
+                               a["Yb"], a["Yl"], a["ws"], a["nbytes"], a["stream"])
+
+    assert fwd(_W(fmt=9)) == EFORMAT
+    assert fwd(_W(fmt=3, block=64)) == EFORMAT            # MXFP4 needs block 32
+    assert fwd(_W(fmt=1, block=32)) == EFORMAT
+    assert fwd(_W(K=96)) == ESHAPE                        # K % 64
+    assert fwd(_W(fmt=3, block=32, K=48)) == ESHAPE
+    assert fwd(_W(N=0)) == ESHAPE
+    assert fwd(_W(fmt=2)) == ENULL                        # DQ needs scales2
+    assert fwd(_W(codes=None)) == ENULL
+    assert fwd(_W(codes=250)) == EALIGN
+    assert fwd(_W(), r=0) == ESHAPE
+    assert fwd(_W(), r=257) == ESHAPE
+    assert fwd(_W(), s=float("nan")) == ESHAPE
+    assert fwd(_W(), M=-1) == ESHAPE
+    assert fwd(_W(), X=None) == ENULL
+    assert fwd(_W(), Y=None) == ENULL
+    assert fwd(_W(), X=4100) == EALIGN
+    assert fwd(_W(), ws=None) == EWS
+    assert fwd(_W(), nbytes=16) == EWS
+    assert fwd(_W(groups=4)) == ENULL                     # grouped needs offsets
+    assert fwd(_W(), offs=4096) == ESHAPE                 # single group takes no offsets
+    assert fwd(_W(), M=0) == OK                           # nothing to launch
+
+
+def test_backward_validation(lib):
+    W = _W()
+
+    def bwd(**kw):
+        a = dict(X=4096, dY=4096, M=16, A=4096, B=4096, r=16, s=2.0, offs=None, Z=None, dX=4096, dA=4096,
+                 dB=4096, ws=8192, nbytes=1 << 30, stream=None)
+        a.update(kw)
+        return L.lora4_backward(W, a["X"], a["dY"], a["M"], a["A"], a["B"], a["r"], a["s"], a["offs"], a["Z"],
+                                a["dX"], a["dA"], a["dB"], a["ws"], a["nbytes"], a["stream"])
+
+    assert bwd(dY=None) == ENULL
+    assert bwd(dA=None) == ENULL
+    assert bwd(dB=4104) == EALIGN
+    assert bwd(nbytes=100) == EWS
+    assert bwd(r=300) == ESHAPE
+
+
+def test_quant_pack_validation(lib):
+    assert L.quant_pack_nf4(None, 16, 64, 0, 4096, 4096, None, None) == ENULL
+    assert L.quant_pack_nf4(4096, 16, 96, 0, 4096, 4096, None, None) == ESHAPE
+    assert L.quant_pack_nf4(4096, 16, 64, 1, 4096, 4096, None, None) == ENULL
+    assert L.quant_pack_nf4(4100, 16, 64, 0, 4096, 4096, None, None) == EALIGN
+    assert L.quant_pack_mxfp4(4096, 16, 48, 4096, 4096, None) == ESHAPE
+    assert L.quant_pack_mxfp4(4096, 0, 64, 4096, 4096, None) == ESHAPE
+
+
+def test_workspace_sizes(lib):
+    W = _W()
+    f = L.lora4_workspace_bytes(0, W, 4096, 16)
+    b = L.lora4_workspace_bytes(1, W, 4096, 16)
+    assert f >= 4096 * 16 * 2 and b >= f
+    assert L.lora4_workspace_bytes(0, W, 8192, 16) >= f
+    assert L.lora4_workspace_bytes(2, W, 4096, 16) == 0
+    assert L.lora4_workspace_bytes(0, W, 4096, 0) == 0
+    # the workspace stays small next to the activations
+    assert b < 4096 * 1024 * 2 * 8
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", "/nonexistent/liblora4.so")
+    with pytest.raises(RuntimeError):
+        L.lib()

@@ -1,0 +1,145 @@
+"""GPU: packing and in-kernel dequant are bit-exact against the oracle.
+
+quant_pack_* bytes must equal the oracle's bytes. The dequant inside the
+production GEMM kernels is checked with one-hot operands: with X = I (and
+B = 0) the forward returns Y = deq(W)^T exactly (one product by 1.0, exact
+zero sums, one rounding of an exact bf16 value), and with dY = I the dgrad
+returns dX = deq(W) exactly, which exercises the opposite-axis dequant.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import lora_fine_tuning_amd as L
+import synth
+from oracle import codecs, mxfp4, nf4
+from gpu_util import DEV, f64, oracle_dequant, oracle_pack, pack_gpu, print_case, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _w(shape, std, seed):
+    return synth.to_bf16(np.random.default_rng(seed).standard_normal(shape, dtype=np.float32) * np.float32(std))
+
+
+def _edge_rows(K):
+    """Rows with an all-zero block, -0, tiny (subnormal) and large values, and
+    values exactly on quantization boundaries of the first block."""
+    rows = np.zeros((6, K), dtype=np.uint16)
+    rows[1, :] = 0x8000                                  # -0 everywhere
+    rows[2, :] = 0x0001                                  # smallest subnormal
+    rows[2, 1::3] = 0x8003
+    rows[3, :] = synth.to_bf16(np.linspace(-3e38, 3e38, K).astype(np.float32))
+    v = np.array([4.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -0.75, -5.0, 7.5], dtype=np.float32)
+    rows[4, :len(v)] = synth.to_bf16(v)
+    rows[5, :] = synth.to_bf16(np.tile(np.float32([1.0, -1.0, 0.5, 1e-3]), K // 4))
+    return rows
+
+
+@pytest.mark.parametrize("fmt", [synth.NF4, synth.NF4_DQ, synth.MXFP4])
+@pytest.mark.parametrize("N,K", [(1024, 1024), (37, 192), (300, 5120)])
+def test_quant_pack_bit_exact(fmt, N, K):
+    print_case("quant_pack", fmt, N, K)
+    W = _w((N, K), 0.02, 100 + N)
+    W[:6] = _edge_rows(K)
+    pk = pack_gpu(W, fmt)
+    torch.cuda.synchronize()
+    ref = oracle_pack(W, fmt)
+    assert np.array_equal(pk.codes[0].cpu().numpy(), ref[0])
+    if fmt == synth.NF4:
+        assert np.array_equal(pk.scales[0].cpu().numpy().view(np.uint32), ref[1].view(np.uint32))
+    elif fmt == synth.NF4_DQ:
+        assert np.array_equal(pk.scales[0].cpu().numpy(), ref[1])
+        assert np.array_equal(pk.scales2[0].cpu().numpy().view(np.uint32), ref[2].view(np.uint32))
+    else:
+        assert np.array_equal(pk.scales[0].cpu().numpy(), ref[1])
+
+
+def _zero_sign(u16):
+    """Map -0 to +0: a one-hot product sums -0 with +0 terms, which IEEE
+    addition returns as +0, so the sign of a zero cannot survive the GEMM."""
+    u = np.array(u16, dtype=np.uint16, copy=True)
+    u[u == 0x8000] = 0
+    return u
+
+
+def _identity(n):
+    I = np.zeros((n, n), dtype=np.uint16)
+    I[np.arange(n), np.arange(n)] = 0x3F80                 # bf16 1.0
+    return I
+
+
+def _custom_base(fmt, N, K, seed):
+    """A packed base whose codes run through every value and whose scales sweep
+    many binades (every finite E8M0 up to 252 for MXFP4)."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    codes[0, :8] = np.arange(0, 256, 32, dtype=np.uint8) | np.arange(8, dtype=np.uint8)
+    if fmt == synth.MXFP4:
+        sc = (np.arange(N * (K // 32)) % 253).astype(np.uint8).reshape(N, K // 32)
+        return codes, sc
+    nb = K // 64
+    expo = (np.arange(N * nb) % 81 - 40).astype(np.float32)
+    sc = (np.float32(2.0) ** expo * rng.uniform(0.5, 1.0, N * nb).astype(np.float32)).reshape(N, nb)
+    sc[0, 0] = 0.0
+    if fmt == synth.NF4:
+        return codes, sc.astype(np.float32)
+    c8, c2 = nf4.double_quantize(sc)
+    return codes, c8, c2
+
+
+def _to_packed(parts, fmt, N, K):
+    codes = torch.from_numpy(parts[0]).to(DEV)[None]
+    if fmt == synth.NF4:
+        return L.PackedBase(L.LORA4_NF4, N, K, 1, codes, torch.from_numpy(parts[1]).to(DEV)[None])
+    if fmt == synth.NF4_DQ:
+        return L.PackedBase(L.LORA4_NF4_DQ, N, K, 1, codes, torch.from_numpy(parts[1]).to(DEV)[None],
+                            torch.from_numpy(parts[2]).to(DEV)[None])
+    return L.PackedBase(L.LORA4_MXFP4, N, K, 1, codes, torch.from_numpy(parts[1]).to(DEV)[None])
+
+
+@pytest.mark.parametrize("fmt", [synth.NF4, synth.NF4_DQ, synth.MXFP4])
+def test_forward_dequant_one_hot_bit_exact(fmt):
+    N, K, r = 160, 1024, 16
+    print_case("one-hot forward", fmt, N, K)
+    parts = _custom_base(fmt, N, K, 7)
+    base = _to_packed(parts, fmt, N, K)
+    ref = oracle_dequant(parts, fmt)                            # [N, K] bf16 bits
+    X = to_dev(_identity(K))
+    A = to_dev(_w((r, K), 0.03, 1))
+    B = torch.zeros((N, r), dtype=torch.bfloat16, device=DEV)
+    out = L.forward(base, X, A, B, 2.0)
+    Y = to_host(out["Y"])                                        # [K, N] == deq(W)^T
+    assert np.array_equal(_zero_sign(Y), _zero_sign(ref.T))
+
+
+@pytest.mark.parametrize("fmt", [synth.NF4, synth.NF4_DQ, synth.MXFP4])
+def test_dgrad_dequant_one_hot_bit_exact(fmt):
+    N, K, r = 192, 512, 16
+    print_case("one-hot dgrad", fmt, N, K)
+    parts = _custom_base(fmt, N, K, 8)
+    base = _to_packed(parts, fmt, N, K)
+    ref = oracle_dequant(parts, fmt)
+    dY = to_dev(_identity(N))                                    # M = N
+    X = to_dev(_w((N, K), 1.0, 2))
+    A = to_dev(_w((r, K), 0.03, 3))
+    B = torch.zeros((N, r), dtype=torch.bfloat16, device=DEV)
+    g = L.backward(base, X, dY, A, B, 2.0)
+    assert np.array_equal(_zero_sign(to_host(g["dX"])), _zero_sign(ref))   # dX = I deq(W) + 0
+    assert (to_host(g["dA"]) & 0x7FFF == 0).all()                # B = 0 kills dA
+
+
+def test_mxfp4_nan_scale_propagates():
+    N, K = 16, 64
+    codes = np.full((N, K // 2), 0x21, dtype=np.uint8)
+    sc = np.full((N, K // 32), 127, dtype=np.uint8)
+    sc[3, 1] = 255
+    base = _to_packed((codes, sc), synth.MXFP4, N, K)
+    ref = oracle_dequant((codes, sc), synth.MXFP4)
+    out = L.forward(base, to_dev(_identity(K)), to_dev(np.zeros((4, K), np.uint16)),
+                    torch.zeros((N, 4), dtype=torch.bfloat16, device=DEV), 1.0)
+    Y = codecs.bf16_to_f32(to_host(out["Y"]))
+    assert np.isnan(Y[:, 3]).all()          # the NaN scale poisons the whole output column
+    keep = [0, 1, 2] + list(range(4, N))
+    assert np.array_equal(_zero_sign(to_host(out["Y"])[:, keep]), _zero_sign(ref.T[:, keep]))
