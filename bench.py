@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Throughput of the unmerged-LoRA linear over a frozen 4-bit base on one MI355X.
+
+A step is one forward and one backward pass of every layer of the workload
+(forward through the layers in order, backward in reverse order, as in
+training), with all inputs already resident in HBM and the base packed once
+beforehand. The default workload is the Llama-3-8B-shaped layer set on 4096
+tokens with an NF4 base (64-element blocks) and rank-16 adapters (alpha 32):
+q and o 4096->4096, k and v 4096->1024, gate and up 4096->14336, down
+14336->4096.
+
+Prints one JSON line: fwd+bwd TFLOP/s (algorithmic flops 4MNK + 6Mr(N+K) per
+layer), the fraction of the bf16 dense MFMA peak, the roofline of the dominant
+kernel (timed live with HIP events on the launch stream) and the CPU oracle
+timed on a bounded sample of the same workload on the host cores.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+WORKLOADS = {"single": 1, "llama8b": 2, "llama70b": 3, "moe": 4, "longctx": 5}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama8b", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-tokens", type=int, default=1024,
+                    help="tokens per layer in the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    return ap.parse_args()
+
+
+class Layer:
+    """Device buffers of one layer (inputs, outputs, packed base)."""
+
+    def __init__(self, spec, L, torch, synth):
+        self.spec = spec
+        t = synth.inputs(spec)
+        dev = "cuda:0"
+
+        def d(a):
+            return torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
+
+        self.X, self.A, self.B, self.dY = d(t["X"]), d(t["A"]), d(t["B"]), d(t["dY"])
+        W = d(t["W"])
+        if spec.fmt == synth.MXFP4:
+            self.base = L.pack_mxfp4(W)
+        else:
+            self.base = L.pack_nf4(W, double_quant=(spec.fmt == synth.NF4_DQ))
+        del W
+        M, N, K, r, E = spec.M, spec.N, spec.K, spec.r, spec.experts
+        self.offs = None
+        if E > 1:
+            self.offs = torch.tensor(spec.offsets, dtype=torch.int64, device=dev)
+        self.Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        self.Z = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
+        self.dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        self.dA = torch.empty_like(self.A)
+        self.dB = torch.empty_like(self.B)
+        self.W = self.base.abi()
+        self.ws_bytes = max(L.lora4_workspace_bytes(0, self.W, M, r), L.lora4_workspace_bytes(1, self.W, M, r))
+
+    def fwd(self, L, ws, stream):
+        s = self.spec
+        st = L.lora4_forward(self.W, self.X.data_ptr(), s.M, self.A.data_ptr(), self.B.data_ptr(), s.r, s.s,
+                             None if self.offs is None else self.offs.data_ptr(), self.Y.data_ptr(),
+                             self.Z.data_ptr(), None, None, ws.data_ptr(), ws.numel(), stream)
+        if st:
+            raise RuntimeError(f"lora4_forward failed: {L.status_string(st)}")
+
+    def bwd(self, L, ws, stream):
+        s = self.spec
+        st = L.lora4_backward(self.W, self.X.data_ptr(), self.dY.data_ptr(), s.M, self.A.data_ptr(),
+                              self.B.data_ptr(), s.r, s.s, None if self.offs is None else self.offs.data_ptr(),
+                              self.Z.data_ptr(), self.dX.data_ptr(), self.dA.data_ptr(), self.dB.data_ptr(),
+                              ws.data_ptr(), ws.numel(), stream)
+        if st:
+            raise RuntimeError(f"lora4_backward failed: {L.status_string(st)}")
+
+
+def kernel_flops(name, spec):
+    """Algorithmic flops of one launch of the named kernel for this layer."""
+    M, N, K, r = spec.M, spec.N, spec.K, spec.r
+    return {
+        "gemm_nt_base": 2 * M * N * K + 2 * M * N * r,     # X deq(W)^T + (sZ) B^T
+        "gemm_nn_dgrad": 2 * M * N * K + 2 * M * K * r,    # dY deq(W) + dZ A
+        "gemm_nt_lora_down": 2 * M * K * r,                 # Z = X A^T
+        "gemm_nn_lora_dz": 2 * M * N * r,                   # dY B
+        "gemm_tn_dA": 2 * M * r * K,
+        "gemm_tn_dB": 2 * M * r * N,
+    }.get(name, 0)
+
+
+def cpu_baseline(specs, tokens):
+    """The oracle (never tuned) on a bounded sample: every layer of the workload,
+    the first `tokens` rows. Oracle packing is done first, untimed; the timed
+    part is what a step computes: dequant + forward + backward per layer."""
+    import numpy as np
+    import synth
+    from oracle import lora, mxfp4, nf4
+
+    prepared = []
+    for spec in specs:
+        t = synth.inputs(spec)
+        E = spec.experts
+        Ws = t["W"] if E > 1 else t["W"][None]
+        packs = []
+        for e in range(E):
+            if spec.fmt == synth.MXFP4:
+                packs.append(mxfp4.quantize(Ws[e]))
+            else:
+                c, sc = nf4.quantize(Ws[e])
+                packs.append((c, *nf4.double_quantize(sc)) if spec.fmt == synth.NF4_DQ else (c, sc))
+        m = min(tokens, spec.M)
+        prepared.append((spec, packs, t["X"][:m], t["dY"][:m], t["A"], t["B"], m))
+    flops = 0
+    t0 = time.perf_counter()
+    for spec, packs, X, dY, A, B, m in prepared:
+        for e, pk in enumerate(packs):
+            if spec.fmt == synth.MXFP4:
+                Wd = lora.as_f64(mxfp4.dequantize(*pk))
+            elif spec.fmt == synth.NF4_DQ:
+                Wd = lora.as_f64(nf4.dequantize_dq(*pk))
+            else:
+                Wd = lora.as_f64(nf4.dequantize(*pk))
+            Ae = lora.as_f64(A if spec.experts == 1 else A[e])
+            Be = lora.as_f64(B if spec.experts == 1 else B[e])
+            Xf, dYf = lora.as_f64(X), lora.as_f64(dY)
+            o = lora.forward(Xf, Wd, Ae, Be, spec.s)
+            lora.backward(Xf, Wd, Ae, Be, spec.s, dYf, Z=o["Z"])
+            flops += 4 * m * spec.N * spec.K + 6 * m * spec.r * (spec.N + spec.K)
+            if spec.experts > 1:
+                break          # sample: the first expert of a grouped layer
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "seconds": dt,
+            "sample": f"every layer of the workload at its first {tokens} tokens (first expert of grouped "
+                      f"layers): oracle dequant + forward + backward, float64 numpy"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import lora_fine_tuning_amd as L
+    import synth
+    if not os.path.exists(L.LIB_PATH):
+        from lora_fine_tuning_amd import build as B
+        B.build()
+    L.lib()
+
+    wl = WORKLOADS[args.workload]
+    specs = synth.layers(wl)
+    log(f"[bench] workload {args.workload}: {len(specs)} layers, generating inputs")
+    layers = [Layer(s, L, torch, synth) for s in specs]
+    ws = torch.empty((max(l.ws_bytes for l in layers),), dtype=torch.uint8, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    flops = sum(s.flops() for s in specs)
+
+    def step():
+        for l in layers:
+            l.fwd(L, ws, stream)
+        for l in reversed(layers):
+            l.bwd(L, ws, stream)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    def timed(k):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        e0.record()
+        for _ in range(k):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        w1 = time.perf_counter()
+        return max(e0.elapsed_time(e1), (w1 - w0) * 1e3) / k
+
+    log(f"[bench] timing {args.steps} steps")
+    ms = timed(args.steps)
+    value = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] {ms:.3f} ms/step, {value:.1f} TFLOP/s")
+
+    roofline = None
+    kernels = {}
+    if not args.no_kernel_timing:
+        # the same timed loop with every launch bracketed by HIP events on its stream
+        L.timing_enable(True)
+        L.timing_collect()
+        ms_ev = timed(args.steps)
+        kt = L.timing_collect()
+        L.timing_enable(False)
+        # per-kernel algorithmic flops: every step launches each kernel once per layer
+        kflops = {}
+        for s in specs:
+            for name in kt:
+                kflops[name] = kflops.get(name, 0) + kernel_flops(name, s)
+        for name, (n, tot) in kt.items():
+            kernels[name] = {"launches": n, "avg_us": 1e3 * tot / n, "total_ms_per_step": tot / args.steps}
+        dom = max(kt, key=lambda k: kt[k][1])
+        n, tot = kt[dom]
+        per_launch = kflops[dom] / len(specs)
+        achieved = (kflops[dom] * args.steps) / (tot * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "flops_per_launch_avg": per_launch, "avg_launch_us": round(1e3 * tot / n, 2),
+                    "ms_per_step_with_events": round(ms_ev, 4)}
+        for k, v in sorted(kernels.items(), key=lambda kv: -kv[1]["total_ms_per_step"]):
+            log(f"[bench]   {k:22s} {v['launches']:5d} launches  avg {v['avg_us']:9.1f} us  "
+                f"{v['total_ms_per_step']:.3f} ms/step")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline (oracle) on {args.cpu_tokens} tokens per layer")
+        cpu = cpu_baseline(specs, args.cpu_tokens)
+        log(f"[bench] cpu oracle {cpu['value']:.4f} TFLOP/s in {cpu['seconds']:.1f} s on {cpu['cores']} threads")
+
+    s0 = specs[0]
+    line = {
+        "metric": "fwd+bwd TFLOP/s of 4-bit-base LoRA linear; % of bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {
+            "workload": {1: "single NF4 linear", 2: "Llama-3-8B-shaped layer set", 3: "Llama-70B-shaped MXFP4 layers",
+                         4: "MoE grouped experts", 5: "long-context skinny rank"}[wl],
+            "tokens": s0.M,
+            "format": s0.fmt,
+            "rank": s0.r,
+            "alpha": s0.alpha,
+            "experts": s0.experts,
+            "layers_KxN": [[s.K, s.N] for s in specs],
+            "gflop_per_step": round(flops / 1e9, 2),
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
