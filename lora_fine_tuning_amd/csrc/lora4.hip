@@ -19,6 +19,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -27,6 +28,7 @@
 
 #include "lora4.h"
 #include "gemm.hpp"
+#include "gemm_big.hpp"
 #include "quant.hpp"
 
 using namespace lora4;
@@ -164,6 +166,43 @@ lora4_status launch_args(const char *name, Kern kernel, dim3 grid, dim3 block, h
   }
   if (timed && hipEventRecord(ea, stream) != hipSuccess) return LORA4_ERR_HIP;
   hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+  if (hipGetLastError() != hipSuccess) return LORA4_ERR_HIP;
+  if (timed) {
+    if (hipEventRecord(eb, stream) != hipSuccess) return LORA4_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_tmu);
+    g_pending.push_back({name, ea, eb});
+  }
+  return LORA4_OK;
+}
+
+template <typename Kern, typename Params>
+lora4_status launch_lds(const char *name, Kern kernel, dim3 grid, dim3 block, size_t lds, const Params &params,
+                        hipStream_t stream) {
+  if (grid.x == 0 || grid.y == 0 || grid.z == 0) return LORA4_OK;
+  // raise the dynamic LDS limit once per kernel (per device of this process)
+  static std::mutex mu;
+  static std::map<const void *, bool> done;
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    if (!done[(const void *)kernel]) {
+      if (hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
+          hipSuccess)
+        return LORA4_ERR_HIP;
+      done[(const void *)kernel] = true;
+    }
+  }
+  hipEvent_t ea = nullptr, eb = nullptr;
+  bool timed = false;
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    if (g_timing) {
+      ea = take_event();
+      eb = take_event();
+      timed = ea && eb;
+    }
+  }
+  if (timed && hipEventRecord(ea, stream) != hipSuccess) return LORA4_ERR_HIP;
+  hipLaunchKernelGGL(kernel, grid, block, lds, stream, params);
   if (hipGetLastError() != hipSuccess) return LORA4_ERR_HIP;
   if (timed) {
     if (hipEventRecord(eb, stream) != hipSuccess) return LORA4_ERR_HIP;
@@ -313,7 +352,71 @@ lora4_status run_nt_main(const NtParams &p, dim3 grid, hipStream_t st) {
   return launch("gemm_nt_base", k_gemm_nt<FMT, BM_MAIN, BN_MAIN, 2>, grid, dim3(THREADS), p, st);
 }
 
+// Large-tile path (256 x 256 tiles) for the base GEMMs when the grid fills
+// the GPU; LORA4_BIG=0/1 in the environment forces the choice.
+int big_policy() {
+  const char *e = std::getenv("LORA4_BIG");
+  return e ? std::atoi(e) : -1;
+}
+
+// The large-tile kernel addresses its operands through 32-bit buffer offsets
+// and streams 16-byte activation chunks: it needs rows that are multiples of
+// 8 elements and per-group buffers below 2 GiB.
+bool big_fits(int64_t ld_a, int64_t M, const PackedW &W) {
+  const int64_t lim = (int64_t)1 << 31;
+  return ld_a % 8 == 0 && W.g_codes < lim && ld_a * 2 * 256 < lim && W.g_scales * 4 < lim;
+}
+
+bool use_big(int64_t M, int64_t Nc, int64_t E) {
+  const int pol = big_policy();
+  if (pol >= 0) return pol != 0;
+  const int64_t tiles = (ceil_div(M, big::BM) + (E > 1 ? E : 0)) * ceil_div(Nc, big::BN);
+  return tiles >= 256;
+}
+
+template <int MODE, int FMT>
+lora4_status run_big(const char *name, const big::Params &p, hipStream_t st) {
+  return launch_lds(name, big::k_gemm_big<MODE, FMT>, dim3((unsigned)p.nblocks), dim3(big::THREADS),
+                    (size_t)big::lds_bytes(MODE), p, st);
+}
+
+template <int MODE>
+lora4_status run_big_fmt(const char *name, int fmt, const big::Params &p, hipStream_t st) {
+  switch (fmt) {
+    case LORA4_NF4: return run_big<MODE, FMT_NF4>(name, p, st);
+    case LORA4_NF4_DQ: return run_big<MODE, FMT_NF4_DQ>(name, p, st);
+    case LORA4_MXFP4: return run_big<MODE, FMT_MXFP4>(name, p, st);
+  }
+  return LORA4_ERR_FORMAT;
+}
+
+big::Params big_params(const Mat &A, const PackedW &W, int64_t R, const Mat &A2, const Mat &B2, int r2,
+                       int64_t M, int64_t Nc, const int64_t *offs, int64_t E, uint16_t *C, int64_t ldc) {
+  big::Params p{};
+  p.A = A;
+  p.W = W;
+  p.R = R;
+  p.A2 = A2;
+  p.B2 = B2;
+  p.r2 = r2;
+  p.M = M;
+  p.Nc = Nc;
+  p.offsets = offs;
+  p.groups = (int)E;
+  p.C = C;
+  p.ldc = ldc;
+  p.tiles_n = (int)ceil_div(Nc, big::BN);
+  p.nblocks = (int)((ceil_div(std::max<int64_t>(M, 1), big::BM) + (E > 1 ? E : 0)) * p.tiles_n);
+  p.tab = nf4_table();
+  return p;
+}
+
 lora4_status run_nt_main_fmt(int fmt, const NtParams &p, dim3 grid, hipStream_t st) {
+  if (p.R > 0 && big_fits(p.A.ld, p.M, p.W) && use_big(p.M, p.Nc, p.groups)) {
+    big::Params q = big_params(p.A, p.W, p.R, p.A2, p.B2, p.r2, p.M, p.Nc, p.offsets, p.groups, p.out.C,
+                               p.out.ldc);
+    return run_big_fmt<0>("gemm_nt_base", fmt, q, st);
+  }
   switch (fmt) {
     case LORA4_NF4: return run_nt_main<FMT_NF4>(p, grid, st);
     case LORA4_NF4_DQ: return run_nt_main<FMT_NF4_DQ>(p, grid, st);
@@ -328,6 +431,11 @@ lora4_status run_nn_main(const NnParams &p, dim3 grid, hipStream_t st) {
 }
 
 lora4_status run_nn_main_fmt(int fmt, const NnParams &p, dim3 grid, hipStream_t st) {
+  if (p.R > 0 && big_fits(p.A.ld, p.M, p.W) && use_big(p.M, p.Nc, p.groups)) {
+    big::Params q = big_params(p.A, p.W, p.R, p.A2, p.B2, p.r2, p.M, p.Nc, p.offsets, p.groups, p.out.C,
+                               p.out.ldc);
+    return run_big_fmt<1>("gemm_nn_dgrad", fmt, q, st);
+  }
   switch (fmt) {
     case LORA4_NF4: return run_nn_main<FMT_NF4>(p, grid, st);
     case LORA4_NF4_DQ: return run_nn_main<FMT_NF4_DQ>(p, grid, st);

@@ -19,6 +19,19 @@ from gpu_util import (DEV, TOL, dequant_rows, f64, pack_gpu, print_case, rel, to
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(params=["auto", "big", "small"])
+def tiles(request, monkeypatch):
+    """Run a test with the library's own tile choice, then forced onto the
+    256 x 256 path and the 128 x 128 path (LORA4_BIG)."""
+    if request.param == "big":
+        monkeypatch.setenv("LORA4_BIG", "1")
+    elif request.param == "small":
+        monkeypatch.setenv("LORA4_BIG", "0")
+    else:
+        monkeypatch.delenv("LORA4_BIG", raising=False)
+    return request.param
+
+
 def _run(lay, t, s=None, Z_from_forward=True, offsets=None):
     s = lay.s if s is None else s
     base = pack_gpu(t["W"], lay.fmt)
@@ -49,7 +62,7 @@ def _check_all(got, ref, keys=("Y", "Z", "Y_base", "Y_lora", "dX", "dA", "dB")):
     return errs
 
 
-def test_single_linear_workload_parity():
+def test_single_linear_workload_parity(tiles):
     lay = synth.layers(1)[0]
     print_case("workload single", lay)
     t = synth.inputs(lay)
@@ -59,7 +72,7 @@ def test_single_linear_workload_parity():
 @pytest.mark.parametrize("fmt", [synth.NF4, synth.NF4_DQ, synth.MXFP4])
 @pytest.mark.parametrize("M,K,N,r", [(200, 192, 200, 8), (64, 320, 96, 24), (300, 256, 100, 4),
                                      (129, 1024, 264, 64), (17, 512, 136, 128), (1, 64, 8, 1)])
-def test_ragged_shapes(fmt, M, K, N, r):
+def test_ragged_shapes(fmt, M, K, N, r, tiles):
     if fmt == synth.MXFP4:
         K = K - 32 if K % 64 == 0 and K > 64 else K     # exercise K % 64 == 32
     lay = synth.small_layer(M, K, N, r, fmt=fmt, index=(M + K + N + r) % 97)
@@ -68,7 +81,7 @@ def test_ragged_shapes(fmt, M, K, N, r):
     _check_all(_run(lay, t, Z_from_forward=(M % 2 == 0)), _oracle(lay, t))
 
 
-def test_b_zero_is_bitwise_base_and_kills_dA():
+def test_b_zero_is_bitwise_base_and_kills_dA(tiles):
     lay = synth.small_layer(256, 512, 384, 16, index=11)
     t = synth.inputs(lay)
     t["B"] = np.zeros_like(t["B"])
@@ -89,7 +102,7 @@ def test_a_zero_kills_dB():
     assert np.array_equal(got["Y"], got["Y_base"])
 
 
-def test_zero_base_isolates_the_lora_path():
+def test_zero_base_isolates_the_lora_path(tiles):
     # deq(W) = 0: Y = Y^LoRA and dX = dZ A, checked at full relative precision
     lay = synth.small_layer(256, 512, 384, 32, index=13)
     t = synth.inputs(lay)
@@ -100,7 +113,7 @@ def test_zero_base_isolates_the_lora_path():
     _check_all(got, ref, keys=("Y", "Y_lora", "dX", "dA", "dB"))
 
 
-def test_grouped_small_with_empty_group():
+def test_grouped_small_with_empty_group(tiles):
     K, N, r, E = 256, 96, 16, 5
     offs = [0, 70, 70, 200, 201, 333]
     for fmt in (synth.MXFP4, synth.NF4):
@@ -139,7 +152,7 @@ def test_zero_tokens():
     assert (to_host(bw["dA"]) == 0).all() and (to_host(bw["dB"]) == 0).all()
 
 
-def test_deterministic():
+def test_deterministic(tiles):
     lay = synth.small_layer(512, 1024, 768, 16, index=41)
     t = synth.inputs(lay)
     a = _run(lay, t)
@@ -160,3 +173,19 @@ def test_validation_errors_launch_nothing():
     with pytest.raises(L.Lora4Error) as ei:
         L.forward(bad, X, A, B, 2.0, workspace=torch.empty(1 << 20, dtype=torch.uint8, device=DEV))
     assert ei.value.status == -2
+
+
+def test_large_tile_shape_selected_automatically(monkeypatch):
+    # 1024 x 4096 output: 4 x 16 = 64 tiles of 256 -> small path; 4096 x 4096 -> large path.
+    monkeypatch.delenv("LORA4_BIG", raising=False)
+    lay = synth.small_layer(4096, 1024, 4096, 16, index=61)
+    t = synth.inputs(lay)
+    got = _run(lay, t)
+    rows = np.random.default_rng(0).choice(lay.M, 96, replace=False)
+    Wd = dequant_rows(t["W"], np.arange(lay.N), lay.fmt)
+    X, A, B, dY = (f64(t[k]) for k in ("X", "A", "B", "dY"))
+    ref = lora.forward(X[rows], Wd, A, B, lay.s)
+    assert rel(got["Y"][rows], ref["Y"]) <= TOL
+    bref = lora.backward(X, Wd, A, B, lay.s, dY)
+    assert rel(got["dX"][rows], bref["dX"][rows]) <= TOL
+    assert rel(got["dA"], bref["dA"]) <= TOL and rel(got["dB"], bref["dB"]) <= TOL

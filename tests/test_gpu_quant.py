@@ -99,8 +99,14 @@ def _to_packed(parts, fmt, N, K):
     return L.PackedBase(L.LORA4_MXFP4, N, K, 1, codes, torch.from_numpy(parts[1]).to(DEV)[None])
 
 
+@pytest.fixture(params=["big", "small"])
+def tiles(request, monkeypatch):
+    monkeypatch.setenv("LORA4_BIG", "1" if request.param == "big" else "0")
+    return request.param
+
+
 @pytest.mark.parametrize("fmt", [synth.NF4, synth.NF4_DQ, synth.MXFP4])
-def test_forward_dequant_one_hot_bit_exact(fmt):
+def test_forward_dequant_one_hot_bit_exact(fmt, tiles):
     N, K, r = 160, 1024, 16
     print_case("one-hot forward", fmt, N, K)
     parts = _custom_base(fmt, N, K, 7)
@@ -115,7 +121,7 @@ def test_forward_dequant_one_hot_bit_exact(fmt):
 
 
 @pytest.mark.parametrize("fmt", [synth.NF4, synth.NF4_DQ, synth.MXFP4])
-def test_dgrad_dequant_one_hot_bit_exact(fmt):
+def test_dgrad_dequant_one_hot_bit_exact(fmt, tiles):
     N, K, r = 192, 512, 16
     print_case("one-hot dgrad", fmt, N, K)
     parts = _custom_base(fmt, N, K, 8)
