@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b", choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-tokens", type=int, default=1024,
+    ap.add_argument("--cpu-tokens", type=int, default=8192,
                     help="tokens per layer in the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
@@ -97,8 +97,8 @@ def kernel_flops(name, spec):
     return {
         "gemm_nt_base": 2 * M * N * K + 2 * M * N * r,     # X deq(W)^T + (sZ) B^T
         "gemm_nn_dgrad": 2 * M * N * K + 2 * M * K * r,    # dY deq(W) + dZ A
-        "gemm_nt_lora_down": 2 * M * K * r,                 # Z = X A^T
-        "gemm_nn_lora_dz": 2 * M * N * r,                   # dY B
+        "rows_skinny_z": 2 * M * K * r,                     # Z = X A^T
+        "rows_skinny_dz": 2 * M * N * r,                    # dZ = s dY B
         "gemm_tn_dA": 2 * M * r * K,
         "gemm_tn_dB": 2 * M * r * N,
     }.get(name, 0)

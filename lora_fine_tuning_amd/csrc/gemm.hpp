@@ -651,6 +651,28 @@ __global__ void k_reduce_transpose_bf16(const float *part, int splits, int group
   out[i] = to_bf16(s * alpha);
 }
 
+// dA[i] = bf16(sum_s partA[s][i]) for i < na, then
+// dB[g][n][j] = bf16(alpha sum_s partB[s][g][j][n]) (partials hold dB^T).
+__global__ void k_reduce_dadb(const float *part_a, int splits_a, int64_t na, uint16_t *dA, const float *part_b,
+                              int splits_b, int groups, int64_t P, int64_t Q, uint16_t *dB, float alpha) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < na) {
+    float s = 0.f;
+    for (int k = 0; k < splits_a; ++k) s += part_a[k * na + i];
+    dA[i] = to_bf16(s);
+    return;
+  }
+  const int64_t ib = i - na;
+  const int64_t total = (int64_t)groups * P * Q;
+  if (ib >= total) return;
+  const int64_t g = ib / (P * Q);
+  const int64_t rem = ib - g * P * Q;
+  const int64_t q = rem / P, pp = rem - q * P;
+  float s = 0.f;
+  for (int k = 0; k < splits_b; ++k) s += part_b[((int64_t)k * groups + g) * P * Q + pp * Q + q];
+  dB[ib] = to_bf16(s * alpha);
+}
+
 __global__ void k_fill_u16(uint16_t *p, int64_t n, uint16_t v) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;

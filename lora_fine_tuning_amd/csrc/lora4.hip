@@ -29,6 +29,7 @@
 #include "lora4.h"
 #include "gemm.hpp"
 #include "gemm_big.hpp"
+#include "skinny.hpp"
 #include "quant.hpp"
 
 using namespace lora4;
@@ -284,7 +285,7 @@ struct Plan {
   int tq_a, tq_b;     // TN Q tiles (dA over K, dB over N)
   int msplit_a, msplit_b;
   // workspace offsets
-  size_t off_sz, off_zw, off_dz, off_part, bytes;
+  size_t off_sz, off_zw, off_dz, off_part, off_part_b, bytes;
 };
 
 constexpr int BM_MAIN = 128, BN_MAIN = 128;
@@ -326,14 +327,11 @@ Plan make_plan(int which, const lora4_W *W, int64_t M, int r) {
   p.off_zw = off;   // backward: recomputed Z
   if (which == 1) off += mr2;
   p.off_dz = p.off_sz;
-  p.off_part = off;
-  size_t part = (size_t)p.zsplit * M * r * 4;
+  p.off_part = off;  // backward: dA partials, then dB^T partials
   if (which == 1) {
-    part = std::max(part, (size_t)p.dzsplit * M * r * 4);
-    part = std::max(part, (size_t)p.msplit_a * p.E * r * p.K * 4);
-    part = std::max(part, (size_t)p.msplit_b * p.E * r * p.N * 4);
+    p.off_part_b = off + align256((size_t)p.msplit_a * p.E * r * p.K * 4);
+    off = p.off_part_b + align256((size_t)p.msplit_b * p.E * r * p.N * 4);
   }
-  off += align256(part);
   p.bytes = std::max<size_t>(off, 256);   // never 0: 0 reports invalid arguments
   return p;
 }
@@ -479,25 +477,61 @@ lora4_status reduce_bf16(const char *name, const float *part, int splits, int64_
   return launch_args(name, k_reduce_bf16, grid, dim3(256), st, part, splits, stride, n, out1, a1, out2, a2);
 }
 
+// Row-block rank-r product (Z = X A^T with transb 0, dY B with transb 1):
+// out1 = bf16(a1 acc), out2 = bf16(a2 acc). TJ 16-wide column blocks per
+// workgroup (up to 128 columns; grid.y covers larger r), TM 16-row blocks.
+template <int TM, int TJ>
+lora4_status run_rows_tj(int transb, const skinny::Params &p, dim3 grid, hipStream_t st) {
+  if (transb) return launch("rows_skinny_dz", skinny::k_rows_skinny<TM, TJ, 1>, grid, dim3(skinny::THREADS), p, st);
+  return launch("rows_skinny_z", skinny::k_rows_skinny<TM, TJ, 0>, grid, dim3(skinny::THREADS), p, st);
+}
+
+lora4_status rows_skinny(int transb, const uint16_t *act, int64_t ld_act, const uint16_t *w, int64_t ld_w,
+                         int64_t g_w, int64_t R, int64_t M, int r, const int64_t *offs, int64_t E, uint16_t *o1,
+                         float a1, uint16_t *o2, float a2, hipStream_t st) {
+  skinny::Params p{};
+  p.act = act;
+  p.ld_act = ld_act;
+  p.w = w;
+  p.ld_w = ld_w;
+  p.g_w = g_w;
+  p.R = R;
+  p.M = M;
+  p.r = r;
+  p.offsets = offs;
+  p.groups = (int)E;
+  p.out1 = o1;
+  p.alpha1 = a1;
+  p.out2 = o2;
+  p.alpha2 = a2;
+  const int tj = r <= 16 ? 1 : r <= 32 ? 2 : r <= 64 ? 4 : 8;
+  const int tm = (tj <= 4 && M / 16 > 4096) ? 2 : 1;
+  const int64_t slots = ceil_div(std::max<int64_t>(M, 1), 16 * tm) + (E > 1 ? E : 0);
+  dim3 grid((unsigned)slots, (unsigned)ceil_div(r, 16 * tj), 1);
+  if (tm == 2) {
+    switch (tj) {
+      case 1: return run_rows_tj<2, 1>(transb, p, grid, st);
+      case 2: return run_rows_tj<2, 2>(transb, p, grid, st);
+      default: return run_rows_tj<2, 4>(transb, p, grid, st);
+    }
+  }
+  switch (tj) {
+    case 1: return run_rows_tj<1, 1>(transb, p, grid, st);
+    case 2: return run_rows_tj<1, 2>(transb, p, grid, st);
+    case 4: return run_rows_tj<1, 4>(transb, p, grid, st);
+    default: return run_rows_tj<1, 8>(transb, p, grid, st);
+  }
+}
+
 // Z = X A^T (per group), written as bf16 to z1 (scale a1) and z2 (scale a2).
 lora4_status z_pass(const Plan &pl, const lora4_W *W, const uint16_t *X, const uint16_t *A,
-                    const int64_t *offs, float *part, uint16_t *z1, float a1, uint16_t *z2, float a2,
-                    hipStream_t st) {
-  NtParams p{};
-  p.A = mat(X, pl.K);
-  p.B = mat(A, pl.K, (int64_t)pl.r * pl.K);
-  p.R = pl.K;
-  p.r2 = 0;
-  p.M = pl.M;
-  p.Nc = pl.r;
-  p.offsets = offs;
-  p.groups = (int)pl.E;
-  p.Rsplit = pl.zlen;
-  p.out = GemmOut{nullptr, 0, part, pl.M * pl.r, 1.0f};
-  p.tab = nf4_table();
-  dim3 grid((unsigned)ceil_div(pl.r, pl.rt), (unsigned)pl.row_slots, (unsigned)pl.zsplit);
-  TRY(run_nt_skinny(pl.rt, p, grid, st));
-  return reduce_bf16("reduce_z", part, pl.zsplit, pl.M * pl.r, pl.M * pl.r, z1, a1, z2, a2, st);
+                    const int64_t *offs, uint16_t *z1, float a1, uint16_t *z2, float a2, hipStream_t st) {
+  if (!z1) {   // one output only
+    z1 = z2;
+    a1 = a2;
+    z2 = nullptr;
+  }
+  return rows_skinny(0, X, pl.K, A, pl.K, (int64_t)pl.r * pl.K, pl.K, pl.M, pl.r, offs, pl.E, z1, a1, z2, a2, st);
 }
 
 lora4_status check_common(const lora4_W *W, int64_t M, int32_t r, float s, const int64_t *offs) {
@@ -557,8 +591,7 @@ lora4_status lora4_forward(const lora4_W *W, const uint16_t *X, int64_t M, const
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
   uint16_t *sZ = ws_at<uint16_t>(workspace, pl.off_sz);
-  float *part = ws_at<float>(workspace, pl.off_part);
-  TRY(z_pass(pl, W, X, A, group_offsets, part, Z, 1.0f, sZ, s, st));
+  TRY(z_pass(pl, W, X, A, group_offsets, Z, 1.0f, sZ, s, st));
 
   NtParams p{};
   p.A = mat(X, pl.K);
@@ -619,28 +652,12 @@ lora4_status lora4_backward(const lora4_W *W, const uint16_t *X, const uint16_t 
   const uint16_t *Zu = Z;
   if (!Zu) {
     uint16_t *Zw = ws_at<uint16_t>(workspace, pl.off_zw);
-    TRY(z_pass(pl, W, X, A, group_offsets, part, Zw, 1.0f, nullptr, 0.0f, st));
+    TRY(z_pass(pl, W, X, A, group_offsets, Zw, 1.0f, nullptr, 0.0f, st));
     Zu = Zw;
   }
 
-  // dZ = s dY B  (NN: reduction over N, output r columns)
-  {
-    NnParams p{};
-    p.A = mat(dY, pl.N);
-    p.B = mat(B, r, pl.N * r);
-    p.R = pl.N;
-    p.r2 = 0;
-    p.M = M;
-    p.Nc = r;
-    p.offsets = group_offsets;
-    p.groups = (int)pl.E;
-    p.Rsplit = pl.dzlen;
-    p.out = GemmOut{nullptr, 0, part, M * r, 1.0f};
-    p.tab = nf4_table();
-    dim3 grid((unsigned)ceil_div(r, pl.rt), (unsigned)pl.row_slots, (unsigned)pl.dzsplit);
-    TRY(run_nn_skinny(pl.rt, p, grid, st));
-    TRY(reduce_bf16("reduce_dz", part, pl.dzsplit, M * r, M * r, dZ, s, nullptr, 0.0f, st));
-  }
+  // dZ = s dY B  (row blocks, reduction over N)
+  TRY(rows_skinny(1, dY, pl.N, B, r, pl.N * r, pl.N, M, r, group_offsets, pl.E, dZ, s, nullptr, 0.0f, st));
 
   // dX = dY deq(W) + dZ A
   {
@@ -662,7 +679,8 @@ lora4_status lora4_backward(const lora4_W *W, const uint16_t *X, const uint16_t 
     TRY(run_nn_main_fmt(W->format, p, grid, st));
   }
 
-  // dA = dZ^T X
+  // dA = dZ^T X and dB^T = Z^T dY, split over rows; one launch reduces both
+  float *part_b = ws_at<float>(workspace, pl.off_part_b);
   {
     TnParams p{};
     p.U = mat(dZ, r);
@@ -676,11 +694,7 @@ lora4_status lora4_backward(const lora4_W *W, const uint16_t *X, const uint16_t 
     p.part = part;
     dim3 grid((unsigned)ceil_div(r, pl.rt), (unsigned)pl.tq_a, (unsigned)(pl.msplit_a * pl.E));
     TRY(run_tn("gemm_tn_dA", pl.rt, p, grid, st));
-    const int64_t n = pl.E * r * pl.K;
-    TRY(reduce_bf16("reduce_dA", part, pl.msplit_a, n, n, dA, 1.0f, nullptr, 0.0f, st));
   }
-
-  // dB = s (Z^T dY)^T
   {
     TnParams p{};
     p.U = mat(Zu, r);
@@ -691,12 +705,15 @@ lora4_status lora4_backward(const lora4_W *W, const uint16_t *X, const uint16_t 
     p.offsets = group_offsets;
     p.groups = (int)pl.E;
     p.splits = pl.msplit_b;
-    p.part = part;
+    p.part = part_b;
     dim3 grid((unsigned)ceil_div(r, pl.rt), (unsigned)pl.tq_b, (unsigned)(pl.msplit_b * pl.E));
     TRY(run_tn("gemm_tn_dB", pl.rt, p, grid, st));
-    const int64_t n = pl.E * r * pl.N;
-    TRY(launch_args("reduce_dB", k_reduce_transpose_bf16, dim3((unsigned)ceil_div(n, 256)), dim3(256), st,
-                    (const float *)part, pl.msplit_b, (int)pl.E, (int64_t)r, pl.N, dB, s));
+  }
+  {
+    const int64_t na = pl.E * r * pl.K, nb = pl.E * r * pl.N;
+    TRY(launch_args("reduce_dA_dB", k_reduce_dadb, dim3((unsigned)ceil_div(na + nb, 256)), dim3(256), st,
+                    (const float *)part, pl.msplit_a, na, dA, (const float *)part_b, pl.msplit_b, (int)pl.E,
+                    (int64_t)r, pl.N, dB, s));
   }
   return LORA4_OK;
 }
