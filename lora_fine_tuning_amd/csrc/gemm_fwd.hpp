@@ -1,0 +1,353 @@
+// Forward dequant-GEMM with the base dequantized straight into MFMA registers:
+//
+//   Y[M, N] = X[M, K] . deq(W)[N, K]^T  (+ (s Z)[M, r] . B[N, r]^T tail)
+//
+// One workgroup = 4 waves computing a 256 x 256 tile of Y. Wave w owns output
+// columns 64 w .. 64 w + 63 for all 256 rows (8 x 2 blocks of 32 x 32, 256
+// fp32 accumulators per lane on v_mfma_f32_32x32x16_bf16), so every row of W
+// in the tile is needed by exactly one wave and deq(W) never touches LDS: each
+// lane loads 32 packed codes (16 bytes) of each of its two rows per step,
+// decodes them one step ahead in registers, and feeds them to the MFMA as the
+// first operand. The order of the reduction inside a 64-deep step is chosen so
+// that this works: in sub-step kk (16 deep), lane half h (lanes 32 h ..)
+// supplies elements k = 32 h + 8 kk .. +7 of its row, i.e. a lane's operands
+// over a step are 32 consecutive elements of one row. X is read from LDS in
+// the same order, so every product pairs the same k on both sides.
+//
+// X streams HBM/L2 -> LDS with bounds-checked direct loads into a ring of
+// STAGES buffers of 256 x 64 (the load for step s+2 is issued when step s
+// starts); one bare barrier per step. All look-ahead loads are issued
+// unconditionally (past the end they are out of range and return zeros), so
+// the number of loads in flight at each wait is a constant. The main loop is
+// unrolled twice so that the two sets of look-ahead registers swap roles
+// instead of being copied (a copy would wait for loads still in flight).
+//
+// NF4 runs decode through a 16-entry bf16 table bf16(q[i] * c) selected with
+// v_perm_b32, MXFP4 through v_cvt_scalef32_pk_bf16_fp4; NF4-DQ rebuilds
+// c = E4M3(code) * c2 first.
+#pragma once
+
+#include "gemm_big.hpp"
+
+namespace lora4 {
+namespace fwd {
+
+using big::OOB;
+using big::Params;
+using big::RunTable;
+using big::rsrc_t;
+
+constexpr int BM = 256, BN = 256, BKS = 64, THREADS = 256, STAGES = 4;
+constexpr int TILE = BM * BKS;   // one X stage, bf16 elements
+
+__host__ __device__ constexpr int lds_bytes() { return STAGES * TILE * 2; }
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * BKS + ((chunk ^ (row & 7)) << 3); }
+
+// Decoded operands of one lane for one step: row j (two 32-row blocks), four
+// sub-steps of 8 bf16 (k = 32 h + 8 kk .. +7 of the lane's row).
+struct WFrag {
+  u32x4_t w[2][4];
+};
+
+// Raw loads of one lane for one step (two rows).
+struct WRaw {
+  u32x4_t c[2];
+  uint32_t sc[2];   // NF4: fp32 bits; DQ: e4m3 code; MXFP4: e8m0 code
+  uint32_t c2[2];   // DQ second level (fp32 bits)
+};
+
+template <int FMT>
+__global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+
+  int b = blockIdx.x;
+  {
+    const int per = p.nblocks >> 3;
+    if (b < per * 8) b = (b & 7) * per + (b >> 3);
+  }
+  const int tn = b % p.tiles_n;
+  const int slot = b / p.tiles_n;
+  const RowTile rt = map_row_tile(slot, BM, p.offsets, p.groups, p.M);
+  if (rt.group < 0) return;
+  const int g = rt.group;
+  const int64_t row0 = rt.row0, row_end = rt.row_end;
+  const int64_t col0 = (int64_t)tn * BN;
+
+  const int t = threadIdx.x;
+  // the wave index is uniform: keep it (and the LDS addresses derived from
+  // it) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
+  const int l32 = lane & 31, h = lane >> 5;
+
+  // ---- X: direct loads into the LDS ring ------------------------------------
+  // wave w, chunk c covers tile rows 8 (4 c + w) .. +7; lane l: row + l / 8,
+  // stored chunk position l % 8, which holds logical chunk (l % 8) ^ (row % 8).
+  const rsrc_t a_rsrc = big::make_rsrc(p.A.p + row0 * p.A.ld, big::clamp_bytes((row_end - row0) * p.A.ld * 2));
+  // chunk c is 32 rows below chunk 0: offsets a_voff0 + c * a_cstep
+  const int a_kq = ((lane & 7) ^ ((lane >> 3) & 7)) * 8;
+  const uint32_t a_voff0 = (uint32_t)(((wave * 8 + (lane >> 3)) * p.A.ld + a_kq) * 2);
+  const uint32_t a_cstep = (uint32_t)(32 * p.A.ld * 2);
+  auto issue_a = [&](int s, uint16_t *As) {
+    const int64_t k0 = (int64_t)s * BKS;
+    const bool edge = k0 + a_kq >= p.R;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (__attribute__((address_space(3))) void *)(As + (c * 4 + wave) * 512),
+                                               16, edge ? OOB : a_voff0 + c * a_cstep, (int)(k0 * 2), 0, 0);
+  };
+
+  // ---- this lane's W rows: n = col0 + 64 wave + 32 j + l32, k = 32 h + .. ----
+  const int64_t Kw = p.W.K;
+  const int64_t nrows = p.Nc - col0;   // rows of W from the tile's first on
+  const uint8_t *codes_g = p.W.codes + g * p.W.g_codes;
+  const rsrc_t w_rsrc = big::make_rsrc(codes_g + col0 * (Kw >> 1), big::clamp_bytes(nrows * (Kw >> 1)));
+  const int sc_per_row = FMT == FMT_MXFP4 ? (int)(Kw >> 5) : (int)(Kw >> 6);
+  const int sc_bytes = FMT == FMT_NF4 ? 4 : 1;
+  const uint8_t *sbase = reinterpret_cast<const uint8_t *>(p.W.scales) + (g * p.W.g_scales) * sc_bytes;
+  const rsrc_t s_rsrc = big::make_rsrc(sbase + col0 * sc_per_row * sc_bytes, big::clamp_bytes(nrows * sc_per_row * sc_bytes));
+  const rsrc_t s2_rsrc = FMT == FMT_NF4_DQ
+                             ? big::make_rsrc(p.W.scales2 + g * p.W.g_scales2, big::clamp_bytes(p.W.g_scales2 * 4))
+                             : big::make_rsrc(p.W.codes, 0u);
+  uint32_t w_voff[2], s_voff[2];
+  int64_t s_idx0[2];   // DQ: flat index of the row's first 64-run scale
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int rloc = wave * 64 + j * 32 + l32;   // row inside the tile
+    w_voff[j] = (uint32_t)(rloc * (Kw >> 1) + h * 16);
+    s_voff[j] = (uint32_t)(rloc * sc_per_row * sc_bytes);
+    s_idx0[j] = (col0 + rloc) * sc_per_row;
+  }
+
+  auto load_w = [&](int s, WRaw &w) {
+    const int64_t k0 = (int64_t)s * BKS;
+    // this lane's half lies inside the row (MXFP4 rows may end at k % 64 == 32)
+    const bool half_ok = k0 + 32 * h < p.R;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      w.c[j] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, half_ok ? w_voff[j] : OOB, (int)(k0 >> 1), 0));
+      if constexpr (FMT == FMT_NF4) {
+        w.sc[j] = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, half_ok ? s_voff[j] : OOB, (int)((k0 >> 6) * 4), 0);
+      } else if constexpr (FMT == FMT_NF4_DQ) {
+        w.sc[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, half_ok ? s_voff[j] : OOB, (int)(k0 >> 6), 0);
+        const int64_t gi = (s_idx0[j] + (k0 >> 6)) >> 8;
+        w.c2[j] = __builtin_amdgcn_raw_buffer_load_b32(s2_rsrc, half_ok ? (uint32_t)(gi * 4) : OOB, 0, 0);
+      } else {
+        w.sc[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, half_ok ? s_voff[j] + h : OOB, (int)(k0 >> 5), 0);
+      }
+    }
+  };
+  // loads per load_w call (all issued unconditionally)
+  constexpr int W_LOADS = FMT == FMT_NF4_DQ ? 6 : 4;
+
+  // decode part `part` (0..3) of raw w into f: row j = part / 2, words
+  // q = 2 (part % 2) .. +1 (16 codes); the row's table is built at its first part.
+  auto decode_part = [&](const WRaw &w, WFrag &f, RunTable &T, float &sc, int part) {
+    const int j = part >> 1;
+    if ((part & 1) == 0) {
+      if constexpr (FMT == FMT_MXFP4) {
+        sc = e8m0_to_f32(w.sc[j] & 0xFFu);
+      } else {
+        float c;
+        if constexpr (FMT == FMT_NF4) c = __builtin_bit_cast(float, w.sc[j]);
+        else c = e4m3_to_f32(w.sc[j] & 0xFFu) * __builtin_bit_cast(float, w.c2[j]);
+        T = big::make_table(c, p.tab);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int q = (part & 1) * 2 + e;
+      if constexpr (FMT == FMT_MXFP4)
+        f.w[j][q] = big::decode8_mxfp4(w.c[j][q], sc);
+      else
+        f.w[j][q] = big::decode8_nf4(T, w.c[j][q]);
+    }
+  };
+
+  // acc[i][j]: rows 32 i .. +31, columns 64 wave + 32 j .. +31
+  f32x16_t acc[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    acc[i][0] = f32x16_t{};
+    acc[i][1] = f32x16_t{};
+  }
+
+  // wait until only the loads issued by the current step (load_w + issue_a
+  // for step s+2) may be in flight: the X stage of step s+1 has landed;
+  // lgkmcnt 0 as well.
+  constexpr int VM_OUT = 8 + W_LOADS;
+  static_assert(VM_OUT < 64, "vmcnt field");
+  constexpr int VMCNT = (VM_OUT & 15) | (7 << 4) | (0 << 8) | ((VM_OUT >> 4) << 14);
+
+  // Sub-step kk of a step: 16 MFMAs on fragments x (chunk kk of the step's X
+  // stage); fragment i is reloaded as soon as its two MFMAs have issued, from
+  // chunk kk+1, or for kk == 3 from chunk 0 of the next step's stage, so the
+  // LDS latency is always a sub-step ahead. The schedule is pinned: MFMA
+  // pairs with the LDS read of the freed fragment and a share of the VALU
+  // work (hook) between them; nothing moves across sub-steps.
+  auto sub_step = [&](const WFrag &cur, int kk, u32x4_t x[8], const uint16_t *src, int chunk, bool reload,
+                      auto &&hook) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      acc[i][0] = mfma_32x32x16(cur.w[0][kk], x[i], acc[i][0]);
+      acc[i][1] = mfma_32x32x16(cur.w[1][kk], x[i], acc[i][1]);
+      if (reload) x[i] = lds_read_b128(src + swz(i * 32 + l32, chunk));
+    }
+    hook();
+#if LORA4_SCHED_INTERLEAVE
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, LORA4_SCHED_VALU, 0);   // VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+      if (reload) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, LORA4_SCHED_VALU, 0);   // VALU
+    }
+#endif
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // step s: X of step s in stage cur (its chunk-0 fragments already in x),
+  // operands fcur. Issues step s+2 (X into stage ahead, W into rload),
+  // decodes step s+1 (rdec -> fnxt), and after sub-step 1 waits for the X of
+  // step s+1 and meets the other waves: stage nxt is then complete, and every
+  // wave is done with step s-1, whose stage the next step refills.
+  auto body = [&](int s, const uint16_t *cur, const uint16_t *nxt, uint16_t *ahead, const WRaw &rdec, WRaw &rload,
+                  const WFrag &fcur, WFrag &fnxt, u32x4_t x[8]) {
+    // W first: the decode of step s+1 then waits only for the W loads of the
+    // previous body, not for its X loads
+    load_w(s + 2, rload);
+    issue_a(s + 2, ahead);
+    RunTable T;
+    float sc = 0.0f;
+    sub_step(fcur, 0, x, cur, h * 4 + 1, true, [&] { decode_part(rdec, fnxt, T, sc, 0); });
+    sub_step(fcur, 1, x, cur, h * 4 + 2, true, [&] { decode_part(rdec, fnxt, T, sc, 1); });
+    __builtin_amdgcn_s_waitcnt(VMCNT);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    sub_step(fcur, 2, x, cur, h * 4 + 3, true, [&] { decode_part(rdec, fnxt, T, sc, 2); });
+    sub_step(fcur, 3, x, nxt, h * 4 + 0, true, [&] { decode_part(rdec, fnxt, T, sc, 3); });
+  };
+
+  const int steps = (int)((p.R + BKS - 1) / BKS);
+  WRaw r0, r1;
+  WFrag f0, f1;
+  u32x4_t x[8];
+  // ring of four stages; step s uses stage s % 4
+  uint16_t *st0 = smem, *st1 = smem + TILE, *st2 = smem + 2 * TILE, *st3 = smem + 3 * TILE;
+  issue_a(0, st0);
+  issue_a(1, st1);
+  load_w(0, r0);
+  {
+    RunTable T;
+    float sc = 0.0f;
+#pragma unroll
+    for (int part = 0; part < 4; ++part) decode_part(r0, f0, T, sc, part);
+  }
+  load_w(1, r1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = lds_read_b128(st0 + swz(i * 32 + l32, h * 4));
+  int s = 0;
+  for (; s + 2 <= steps; s += 2) {
+    body(s, st0, st1, st2, r1, r0, f0, f1, x);
+    body(s + 1, st1, st2, st3, r0, r1, f1, f0, x);
+    uint16_t *t0 = st0, *t1 = st1;   // rotate by two
+    st0 = st2;
+    st1 = st3;
+    st2 = t0;
+    st3 = t1;
+  }
+  if (s < steps) body(s, st0, st1, st2, r1, r0, f0, f1, x);
+  // the look-ahead loads past the end still write (zeros) into the ring
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // ---- rank-r tail: (s Z) B^T; Z rows through LDS, B rows to registers -----
+  if (p.r2 > 0) {
+    const uint16_t *B2 = p.B2.p + g * p.B2.gstride;
+    uint16_t *As = smem;
+    const bool b_vec = (p.B2.ld % 8) == 0;
+    for (int k0 = 0; k0 < p.r2; k0 += BKS) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int idx = t + THREADS * c;
+        const int row = idx >> 3, chunk = idx & 7;
+        uint32_t w4[4] = {0u, 0u, 0u, 0u};
+        const int64_t gr = row0 + row;
+        const int64_t gk = k0 + chunk * 8;
+        if (gr < row_end) {
+          const uint16_t *src = p.A2.p + gr * p.A2.ld + gk;
+          for (int e = 0; e < 8; ++e)
+            if (gk + e < p.r2) w4[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+        }
+        lds_write_b128(As + swz(row, chunk), u32x4_t{w4[0], w4[1], w4[2], w4[3]});
+      }
+      WFrag bt;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t n = col0 + wave * 64 + j * 32 + l32;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int64_t k = k0 + 32 * h + 8 * kk;
+          uint32_t w4[4] = {0u, 0u, 0u, 0u};
+          if (n < p.Nc && k < p.r2) {
+            const uint16_t *src = B2 + n * p.B2.ld + k;
+            if (b_vec && k + 8 <= p.r2) {
+              const u32x4_t v = *reinterpret_cast<const u32x4_t *>(src);
+              w4[0] = v[0];
+              w4[1] = v[1];
+              w4[2] = v[2];
+              w4[3] = v[3];
+            } else {
+              for (int e = 0; e < 8; ++e)
+                if (k + e < p.r2) w4[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+            }
+          }
+          bt.w[j][kk] = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
+        }
+      }
+      __syncthreads();
+      u32x4_t xt[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xt[i] = lds_read_b128(As + swz(i * 32 + l32, h * 4));
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) sub_step(bt, kk, xt, As, h * 4 + kk + 1, kk < 3, [] {});
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: register e of acc[i][j] holds
+  // Y[32 i + lane % 32][64 wave + 32 j + 8 (e / 4) + 4 (lane / 32) + e % 4]
+  const bool vec_out = (p.ldc % 4) == 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t row = row0 + i * 32 + l32;
+    if (row >= row_end) continue;
+    uint16_t *crow = p.C + row * p.ldc;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int64_t col = col0 + wave * 64 + j * 32 + r4 * 8 + h * 4;
+        const float v0 = acc[i][j][4 * r4], v1 = acc[i][j][4 * r4 + 1];
+        const float v2 = acc[i][j][4 * r4 + 2], v3 = acc[i][j][4 * r4 + 3];
+        if (vec_out && col + 4 <= p.Nc) {
+          const u32x2_t pk = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+          *reinterpret_cast<u32x2_t *>(crow + col) = pk;
+        } else {
+          const float v[4] = {v0, v1, v2, v3};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (col + e < p.Nc) crow[col + e] = to_bf16(v[e]);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace fwd
+}  // namespace lora4

@@ -29,6 +29,7 @@
 #include "lora4.h"
 #include "gemm.hpp"
 #include "gemm_big.hpp"
+#include "gemm_fwd.hpp"
 #include "skinny.hpp"
 #include "quant.hpp"
 
@@ -362,7 +363,8 @@ int big_policy() {
 // 8 elements and per-group buffers below 2 GiB.
 bool big_fits(int64_t ld_a, int64_t M, const PackedW &W) {
   const int64_t lim = (int64_t)1 << 31;
-  return ld_a % 8 == 0 && W.g_codes < lim && ld_a * 2 * 256 < lim && W.g_scales * 4 < lim;
+  return ld_a % 8 == 0 && W.g_codes < lim && ld_a * 2 * 256 < lim && W.g_scales * 4 < lim &&
+         W.g_scales2 * 4 < lim;
 }
 
 bool use_big(int64_t M, int64_t Nc, int64_t E) {
@@ -384,6 +386,28 @@ lora4_status run_big_fmt(const char *name, int fmt, const big::Params &p, hipStr
     case LORA4_NF4: return run_big<MODE, FMT_NF4>(name, p, st);
     case LORA4_NF4_DQ: return run_big<MODE, FMT_NF4_DQ>(name, p, st);
     case LORA4_MXFP4: return run_big<MODE, FMT_MXFP4>(name, p, st);
+  }
+  return LORA4_ERR_FORMAT;
+}
+
+// Forward base GEMM with deq(W) decoded straight into MFMA registers
+// (LORA4_FWD=0 in the environment selects the LDS-staged kernel instead).
+bool use_fwd_regs() {
+  const char *e = std::getenv("LORA4_FWD");
+  return e ? std::atoi(e) != 0 : true;
+}
+
+template <int FMT>
+lora4_status run_fwd(const big::Params &p, hipStream_t st) {
+  return launch_lds("gemm_nt_base", fwd::k_gemm_fwd<FMT>, dim3((unsigned)p.nblocks), dim3(fwd::THREADS),
+                    (size_t)fwd::lds_bytes(), p, st);
+}
+
+lora4_status run_fwd_fmt(int fmt, const big::Params &p, hipStream_t st) {
+  switch (fmt) {
+    case LORA4_NF4: return run_fwd<FMT_NF4>(p, st);
+    case LORA4_NF4_DQ: return run_fwd<FMT_NF4_DQ>(p, st);
+    case LORA4_MXFP4: return run_fwd<FMT_MXFP4>(p, st);
   }
   return LORA4_ERR_FORMAT;
 }
@@ -413,6 +437,7 @@ lora4_status run_nt_main_fmt(int fmt, const NtParams &p, dim3 grid, hipStream_t 
   if (p.R > 0 && big_fits(p.A.ld, p.M, p.W) && use_big(p.M, p.Nc, p.groups)) {
     big::Params q = big_params(p.A, p.W, p.R, p.A2, p.B2, p.r2, p.M, p.Nc, p.offsets, p.groups, p.out.C,
                                p.out.ldc);
+    if (use_fwd_regs()) return run_fwd_fmt(fmt, q, st);
     return run_big_fmt<0>("gemm_nt_base", fmt, q, st);
   }
   switch (fmt) {
