@@ -60,7 +60,12 @@ __device__ __forceinline__ f32x16_t mfma_32x32x16(u32x4_t a, u32x4_t b, f32x16_t
 }
 
 // Transposing 64-bit LDS read (see the layout note above).
-__device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t *p) {
+// The pointer is declared restrict so that, once inlined, the read carries
+// alias-scope metadata: without it the compiler cannot tell the read from a
+// direct-to-LDS load still in flight and drains every outstanding vector-memory
+// load before it. Every kernel here orders its LDS tiles with explicit waits
+// and barriers.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t *__restrict__ p) {
   i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(p));
   return __builtin_bit_cast(u32x2_t, v);
 }

@@ -1,0 +1,319 @@
+// Input-gradient dequant-GEMM:
+//
+//   dX[M, K] = dY[M, N] . deq(W)[N, K]   (+ dZ[M, r] . A[r, K] tail)
+//
+// The reduction runs over the rows of W, while the packed codes are contiguous
+// along K (the output), so the MFMA operand (eight consecutive reduction
+// elements per lane) needs a transpose: each thread decodes one 64-element run
+// of a W row into an LDS tile [64 reduction rows][256 output columns], and the
+// waves read it back with ds_read_b64_tr_b16.
+//
+// One workgroup = 4 waves (2 x 2) computing a 256 x 256 tile of dX; each wave
+// owns 128 x 128 (4 x 4 blocks of v_mfma_f32_32x32x16_bf16, 256 fp32
+// accumulators per lane). Per 64-deep step s:
+//  * dY of step s+1 streams HBM/L2 -> LDS with bounds-checked direct loads
+//    (two stages of 256 x 64, swizzled), issued in the first half of step s;
+//  * the packed run of step s+2 is loaded into registers in sub-step 0 of
+//    step s, and the run of step s+1 (loaded a step earlier) is decoded into
+//    the other W tile in four parts, one per sub-step;
+//  * one barrier at the end of the step.
+// All look-ahead loads are issued unconditionally (past the end they are out
+// of range and return zeros); the main loop is unrolled twice so the two sets
+// of look-ahead registers swap roles instead of being copied. The schedule of
+// each 16-MFMA sub-step is pinned: fragment reads for the next sub-step, the
+// global loads, the decode VALU work and its LDS writes are threaded between
+// the MFMAs.
+#pragma once
+
+#include "gemm_big.hpp"
+
+namespace lora4 {
+namespace dgrad {
+
+using big::B_ELEMS_NN;
+using big::LDB_NN;
+using big::OOB;
+using big::Params;
+using big::RunTable;
+using big::rsrc_t;
+using big::swz;
+using big::TILE64;
+
+constexpr int BM = 256, BN = 256, BKS = 64, THREADS = 256;
+
+__host__ __device__ constexpr int lds_bytes() { return 2 * (TILE64 + B_ELEMS_NN) * 2; }
+
+// Raw loads of one thread for one step: its 64-element run.
+struct WRaw {
+  u32x4_t c0, c1;
+  uint32_t sc;   // NF4: fp32 bits; DQ: e4m3 code; MXFP4: two e8m0 codes
+  uint32_t c2;   // DQ second level (fp32 bits)
+};
+
+template <int FMT>
+__global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  uint16_t *const As0 = smem, *const As1 = smem + TILE64;
+  uint16_t *const Bs0 = smem + 2 * TILE64, *const Bs1 = smem + 2 * TILE64 + B_ELEMS_NN;
+
+  int b = blockIdx.x;
+  {
+    const int per = p.nblocks >> 3;
+    if (b < per * 8) b = (b & 7) * per + (b >> 3);
+  }
+  const int tn = b % p.tiles_n;
+  const int slot = b / p.tiles_n;
+  const RowTile rt = map_row_tile(slot, BM, p.offsets, p.groups, p.M);
+  if (rt.group < 0) return;
+  const int g = rt.group;
+  const int64_t row0 = rt.row0, row_end = rt.row_end;
+  const int64_t col0 = (int64_t)tn * BN;
+
+  const int t = threadIdx.x;
+  // the wave index is uniform: keep it (and what derives from it) scalar
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int wm0 = (wave & 1) * 128, wn0 = (wave >> 1) * 128;
+
+  // ---- dY: direct loads into LDS; wave w, chunk c covers rows 8 (4 c + w)..
+  const rsrc_t a_rsrc = big::make_rsrc(p.A.p + row0 * p.A.ld, big::clamp_bytes((row_end - row0) * p.A.ld * 2));
+  const int a_kq = ((lane & 7) ^ ((lane >> 3) & 7)) * 8;
+  const uint32_t a_voff0 = (uint32_t)(((wave * 8 + (lane >> 3)) * p.A.ld + a_kq) * 2);
+  const uint32_t a_cstep = (uint32_t)(32 * p.A.ld * 2);
+  // dY of step s into stage As, chunks 4 half .. 4 half + 3
+  auto issue_a = [&](int s, uint16_t *As, int half) {
+    const int64_t k0 = (int64_t)s * BKS;
+    const bool edge = k0 + a_kq >= p.R;
+#pragma unroll
+    for (int c = 4 * half; c < 4 * half + 4; ++c)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (__attribute__((address_space(3))) void *)(As + (c * 4 + wave) * 512),
+                                               16, edge ? OOB : a_voff0 + c * a_cstep, (int)(k0 * 2), 0, 0);
+  };
+
+  // ---- this thread's run: reduction row k0 + t / 4, output columns
+  // col0 + 64 (t % 4) .. +63
+  const int64_t Kw = p.W.K;
+  const uint8_t *codes_g = p.W.codes + g * p.W.g_codes;
+  const rsrc_t w_rsrc = big::make_rsrc(codes_g, big::clamp_bytes(p.W.N * (Kw >> 1)));
+  const int64_t kc = col0 + (t & 3) * 64;
+  const uint32_t w_base = (uint32_t)((t >> 2) * (Kw >> 1) + (kc >> 1));
+  const uint32_t w_voff0 = kc < p.Nc ? w_base : OOB;
+  const uint32_t w_voff1 = kc + 32 < p.Nc ? w_base + 16 : OOB;
+  const int64_t w_step = (int64_t)BKS * (Kw >> 1);
+  const int sc_per_row = FMT == FMT_MXFP4 ? (int)(Kw >> 5) : (int)(Kw >> 6);
+  const int sc_bytes = FMT == FMT_NF4 ? 4 : 1;
+  const uint8_t *sbase = reinterpret_cast<const uint8_t *>(p.W.scales) + (g * p.W.g_scales) * sc_bytes;
+  const rsrc_t s_rsrc = big::make_rsrc(sbase, big::clamp_bytes(p.W.N * sc_per_row * sc_bytes));
+  const int64_t blk = FMT == FMT_MXFP4 ? (kc >> 5) : (kc >> 6);
+  const uint32_t s_voff = kc < p.Nc ? (uint32_t)(((t >> 2) * sc_per_row + blk) * sc_bytes) : OOB;
+  const uint32_t s_voff1 = kc + 32 < p.Nc ? s_voff + 1 : OOB;   // MXFP4 second code
+  const int64_t s_step = (int64_t)BKS * sc_per_row * sc_bytes;
+  const rsrc_t s2_rsrc = FMT == FMT_NF4_DQ
+                             ? big::make_rsrc(p.W.scales2 + g * p.W.g_scales2, big::clamp_bytes(p.W.g_scales2 * 4))
+                             : big::make_rsrc(p.W.codes, 0u);
+
+  auto load_w = [&](int s, WRaw &w) {
+    const int wo = (int)(w_step * s);
+    w.c0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_voff0, wo, 0));
+    w.c1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_voff1, wo, 0));
+    const int so = (int)(s_step * s);
+    if constexpr (FMT == FMT_NF4) {
+      w.sc = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, s_voff, so, 0);
+    } else if constexpr (FMT == FMT_NF4_DQ) {
+      w.sc = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, s_voff, so, 0);
+      const int64_t idx = ((int64_t)s * BKS + (t >> 2)) * sc_per_row + (kc >> 6);
+      w.c2 = __builtin_amdgcn_raw_buffer_load_b32(s2_rsrc, kc < p.Nc ? (uint32_t)((idx >> 8) * 4) : OOB, 0, 0);
+    } else {
+      // two E8M0 codes, one byte each, so that a range check on the second
+      // never discards the first
+      const uint32_t e0 = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, s_voff, so, 0);
+      const uint32_t e1 = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, s_voff1, so, 0);
+      w.sc = e0 | (e1 << 8);
+    }
+  };
+
+  // decode part `part` (0..3) of raw run w: elements 16 part .. +15 (code
+  // words 2 part, 2 part + 1) into row t / 4 of W tile Bs
+  auto decode_part = [&](const WRaw &w, uint16_t *Bs, RunTable &T, float &s0, float &s1, int part) {
+    if (part == 0) {
+      if constexpr (FMT == FMT_MXFP4) {
+        s0 = e8m0_to_f32(w.sc & 0xFFu);
+        s1 = e8m0_to_f32((w.sc >> 8) & 0xFFu);
+      } else {
+        float c;
+        if constexpr (FMT == FMT_NF4) c = __builtin_bit_cast(float, w.sc);
+        else c = e4m3_to_f32(w.sc & 0xFFu) * __builtin_bit_cast(float, w.c2);
+        T = big::make_table(c, p.tab);
+      }
+    }
+    uint16_t *dst = Bs + (t >> 2) * LDB_NN + (t & 3) * 64;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int q = 2 * part + e;
+      const uint32_t code = q < 4 ? w.c0[q] : w.c1[q - 4];
+      u32x4_t v;
+      if constexpr (FMT == FMT_MXFP4)
+        v = big::decode8_mxfp4(code, q < 4 ? s0 : s1);
+      else
+        v = big::decode8_nf4(T, code);
+      lds_write_b128(dst + 8 * q, v);
+    }
+  };
+
+  // acc[j][i]: output columns wn0 + 32 j .., rows wm0 + 32 i ..
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[j][i] = f32x16_t{};
+
+  auto read_af = [&](const uint16_t *As, int kk, u32x4_t af[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[i] = lds_read_b128(As + swz(wm0 + i * 32 + l32, kk * 2 + h));
+  };
+  auto read_bf = [&](const uint16_t *Bs, int kk, int j) -> u32x4_t {
+    return big::frag_tr32(Bs, LDB_NN, kk * 16, wn0 + j * 32, lane);
+  };
+
+  // One 64-deep step on (As, Bs). The A fragments of the next sub-step are
+  // requested at its start (double-buffered), the B fragment j of the next
+  // sub-step right after its four MFMAs; hook(kk) holds sub-step kk's share of
+  // the decode and global loads. The first fragments of a step are read at
+  // its start.
+  auto compute_step = [&](const uint16_t *As, const uint16_t *Bs, auto &&hook) {
+    u32x4_t afa[4], afb[4], bf[4];
+    read_af(As, 0, afa);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bf[j] = read_bf(Bs, 0, j);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      u32x4_t *af = (kk & 1) ? afb : afa;
+      u32x4_t *afn = (kk & 1) ? afa : afb;
+      const bool more = kk < 3;
+      if (more) read_af(As, kk + 1, afn);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[j][i] = mfma_32x32x16(bf[j], af[i], acc[j][i]);
+        if (more) bf[j] = read_bf(Bs, kk + 1, j);
+      }
+      hook(kk);
+#if LORA4_SCHED_INTERLEAVE
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // MFMA
+        if (more && m < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // LDS read
+        if (m & 1) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);              // global load
+        if ((m & 7) == 7) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);       // LDS write
+        __builtin_amdgcn_sched_group_barrier(0x002, LORA4_SCHED_VALU, 0);          // VALU
+      }
+#endif
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // step s on (Acur, Bcur): decodes step s+1 (rdec) into Bnxt, loads dY of
+  // step s+1 into Anxt and the run of step s+2 into rload; then waits for
+  // all of it and meets the other waves.
+  auto body = [&](int s, const uint16_t *Acur, const uint16_t *Bcur, uint16_t *Anxt, uint16_t *Bnxt,
+                  const WRaw &rdec, WRaw &rload) {
+    RunTable T;
+    float s0 = 0.0f, s1 = 0.0f;
+    compute_step(Acur, Bcur, [&](int kk) {
+      decode_part(rdec, Bnxt, T, s0, s1, kk);
+      if (kk == 0) load_w(s + 2, rload);
+      if (kk < 2) issue_a(s + 1, Anxt, kk);
+    });
+    __syncthreads();
+  };
+
+  const int steps = (int)((p.R + BKS - 1) / BKS);
+  WRaw r0, r1;
+  issue_a(0, As0, 0);
+  issue_a(0, As0, 1);
+  load_w(0, r0);
+  {
+    RunTable T;
+    float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+    for (int part = 0; part < 4; ++part) decode_part(r0, Bs0, T, s0, s1, part);
+  }
+  load_w(1, r1);
+  __syncthreads();
+  int s = 0;
+  for (; s + 2 <= steps; s += 2) {
+    body(s, As0, Bs0, As1, Bs1, r1, r0);
+    body(s + 1, As1, Bs1, As0, Bs0, r0, r1);
+  }
+  if (s < steps) body(s, As0, Bs0, As1, Bs1, r1, r0);
+  // every look-ahead load has landed (the barrier waits for them)
+
+  // ---- rank-r tail: dZ A, plain bf16 steps through registers ----------------
+  if (p.r2 > 0) {
+    const uint16_t *B2 = p.B2.p + g * p.B2.gstride;
+    for (int k0 = 0; k0 < p.r2; k0 += BKS) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int idx = t + THREADS * c;
+        const int row = idx >> 3, chunk = idx & 7;
+        uint32_t w4[4] = {0u, 0u, 0u, 0u};
+        const int64_t gr = row0 + row;
+        const int64_t gk = k0 + chunk * 8;
+        if (gr < row_end) {
+          const uint16_t *src = p.A2.p + gr * p.A2.ld + gk;
+          for (int j = 0; j < 8; ++j)
+            if (gk + j < p.r2) w4[j >> 1] |= (uint32_t)src[j] << (16 * (j & 1));
+        }
+        lds_write_b128(As0 + swz(row, chunk), u32x4_t{w4[0], w4[1], w4[2], w4[3]});
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int idx = t + THREADS * c;
+        const int row = idx >> 5, cc = (idx & 31) * 8;
+        uint32_t w4[4] = {0u, 0u, 0u, 0u};
+        const int64_t gr = k0 + row;
+        const int64_t gc = col0 + cc;
+        if (gr < p.r2) {
+          const uint16_t *src = B2 + gr * p.B2.ld + gc;
+          for (int j = 0; j < 8; ++j)
+            if (gc + j < p.Nc) w4[j >> 1] |= (uint32_t)src[j] << (16 * (j & 1));
+        }
+        lds_write_b128(Bs0 + row * LDB_NN + cc, u32x4_t{w4[0], w4[1], w4[2], w4[3]});
+      }
+      __syncthreads();
+      compute_step(As0, Bs0, [](int) {});
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: register e of acc[j][i] holds
+  // dX[wm0 + 32 i + lane % 32][wn0 + 32 j + 8 (e / 4) + 4 (lane / 32) + e % 4]
+  const bool vec_out = (p.ldc % 4) == 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = row0 + wm0 + i * 32 + l32;
+    if (row >= row_end) continue;
+    uint16_t *crow = p.C + row * p.ldc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int64_t col = col0 + wn0 + j * 32 + r4 * 8 + h * 4;
+        const float v0 = acc[j][i][4 * r4], v1 = acc[j][i][4 * r4 + 1];
+        const float v2 = acc[j][i][4 * r4 + 2], v3 = acc[j][i][4 * r4 + 3];
+        if (vec_out && col + 4 <= p.Nc) {
+          const u32x2_t pk = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+          *reinterpret_cast<u32x2_t *>(crow + col) = pk;
+        } else {
+          const float v[4] = {v0, v1, v2, v3};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (col + e < p.Nc) crow[col + e] = to_bf16(v[e]);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace dgrad
+}  // namespace lora4

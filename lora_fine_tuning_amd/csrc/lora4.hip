@@ -30,6 +30,7 @@
 #include "gemm.hpp"
 #include "gemm_big.hpp"
 #include "gemm_fwd.hpp"
+#include "gemm_dgrad.hpp"
 #include "skinny.hpp"
 #include "quant.hpp"
 
@@ -363,7 +364,9 @@ int big_policy() {
 // 8 elements and per-group buffers below 2 GiB.
 bool big_fits(int64_t ld_a, int64_t M, const PackedW &W) {
   const int64_t lim = (int64_t)1 << 31;
-  return ld_a % 8 == 0 && W.g_codes < lim && ld_a * 2 * 256 < lim && W.g_scales * 4 < lim &&
+  // (look-ahead loads run up to four 64-row steps past the end of W)
+  const int64_t ahead = 4 * 64 * (W.K / 2);
+  return ld_a % 8 == 0 && W.g_codes + ahead < lim && ld_a * 2 * 256 < lim && W.g_scales * 4 + ahead < lim &&
          W.g_scales2 * 4 < lim;
 }
 
@@ -408,6 +411,28 @@ lora4_status run_fwd_fmt(int fmt, const big::Params &p, hipStream_t st) {
     case LORA4_NF4: return run_fwd<FMT_NF4>(p, st);
     case LORA4_NF4_DQ: return run_fwd<FMT_NF4_DQ>(p, st);
     case LORA4_MXFP4: return run_fwd<FMT_MXFP4>(p, st);
+  }
+  return LORA4_ERR_FORMAT;
+}
+
+// Input-gradient base GEMM with pinned schedule and register ping-pong
+// (LORA4_DGRAD=0 in the environment selects the earlier kernel instead).
+bool use_dgrad_new() {
+  const char *e = std::getenv("LORA4_DGRAD");
+  return e ? std::atoi(e) != 0 : true;
+}
+
+template <int FMT>
+lora4_status run_dgrad(const big::Params &p, hipStream_t st) {
+  return launch_lds("gemm_nn_dgrad", dgrad::k_gemm_dgrad<FMT>, dim3((unsigned)p.nblocks), dim3(dgrad::THREADS),
+                    (size_t)dgrad::lds_bytes(), p, st);
+}
+
+lora4_status run_dgrad_fmt(int fmt, const big::Params &p, hipStream_t st) {
+  switch (fmt) {
+    case LORA4_NF4: return run_dgrad<FMT_NF4>(p, st);
+    case LORA4_NF4_DQ: return run_dgrad<FMT_NF4_DQ>(p, st);
+    case LORA4_MXFP4: return run_dgrad<FMT_MXFP4>(p, st);
   }
   return LORA4_ERR_FORMAT;
 }
@@ -457,6 +482,7 @@ lora4_status run_nn_main_fmt(int fmt, const NnParams &p, dim3 grid, hipStream_t 
   if (p.R > 0 && big_fits(p.A.ld, p.M, p.W) && use_big(p.M, p.Nc, p.groups)) {
     big::Params q = big_params(p.A, p.W, p.R, p.A2, p.B2, p.r2, p.M, p.Nc, p.offsets, p.groups, p.out.C,
                                p.out.ldc);
+    if (use_dgrad_new()) return run_dgrad_fmt(fmt, q, st);
     return run_big_fmt<1>("gemm_nn_dgrad", fmt, q, st);
   }
   switch (fmt) {
