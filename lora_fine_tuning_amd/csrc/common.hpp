@@ -70,6 +70,21 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t *__restrict__ p)
   return __builtin_bit_cast(u32x2_t, v);
 }
 
+// LDS layout of a [rows][64] bf16 tile (128-byte rows, eight 16-byte chunks):
+// chunk c of row r is stored at position c ^ ((r >> 1) & 7). The LDS serves a
+// 16-byte-per-lane read to 16 lanes at a time (256 bytes, 64 banks); the MFMA
+// operand reads give those 16 lanes 16 consecutive rows at one logical chunk,
+// which this places in 16 different bank groups (two rows per 128-byte
+// position, with distinct positions for rows of equal parity).
+__device__ __forceinline__ int tile64_swz(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3); }
+
+// Direct-to-LDS loads write lane l's 16 bytes at position l of a 1 KB block;
+// with block (4 c + w) holding rows 8 (4 c + w) .. +7 (c = 0..7, wave w), the
+// logical chunk lane l must fetch for the layout above.
+__device__ __forceinline__ int tile64_dma_chunk(int lane, int wave) {
+  return (lane & 7) ^ (((wave & 1) << 2) | (lane >> 4));
+}
+
 __device__ __forceinline__ u32x4_t lds_read_b128(const uint16_t *p) {
   return *reinterpret_cast<const u32x4_t *>(p);
 }

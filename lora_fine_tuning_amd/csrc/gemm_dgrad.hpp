@@ -5,8 +5,10 @@
 // The reduction runs over the rows of W, while the packed codes are contiguous
 // along K (the output), so the MFMA operand (eight consecutive reduction
 // elements per lane) needs a transpose: each thread decodes one 64-element run
-// of a W row into an LDS tile [64 reduction rows][256 output columns], and the
-// waves read it back with ds_read_b64_tr_b16.
+// of a W row into an LDS tile [64 reduction rows][256 output columns] (lane =
+// row, wave = 64-column block), and the waves read it back with
+// ds_read_b64_tr_b16. Both tiles are swizzled so that every LDS access is free
+// of bank conflicts.
 //
 // One workgroup = 4 waves (2 x 2) computing a 256 x 256 tile of dX; each wave
 // owns 128 x 128 (4 x 4 blocks of v_mfma_f32_32x32x16_bf16, 256 fp32
@@ -30,18 +32,37 @@
 namespace lora4 {
 namespace dgrad {
 
-using big::B_ELEMS_NN;
-using big::LDB_NN;
 using big::OOB;
 using big::Params;
 using big::RunTable;
 using big::rsrc_t;
-using big::swz;
-using big::TILE64;
 
 constexpr int BM = 256, BN = 256, BKS = 64, THREADS = 256;
+constexpr int TILE_A = BM * BKS;    // dY stage [256][64], tile64 layout
+constexpr int TILE_W = BKS * BN;    // deq(W) tile [64][256]
 
-__host__ __device__ constexpr int lds_bytes() { return 2 * (TILE64 + B_ELEMS_NN) * 2; }
+__host__ __device__ constexpr int lds_bytes() { return 2 * (TILE_A + TILE_W) * 2; }
+
+__device__ __forceinline__ int swz(int row, int chunk) { return tile64_swz(row, chunk); }
+
+// deq(W) tile [64 reduction rows][256 output columns]: 512-byte rows of 32
+// chunks of 16 bytes, chunk c of row n stored at c ^ wsw(n). LDS writes are
+// served 128 bytes at a time (8 lanes = 8 consecutive rows at one chunk: 8
+// distinct positions), reads 256 bytes at a time (32 lanes of a transposing
+// read = 4 rows x 4 consecutive chunks, 8 bytes each: 64 distinct banks).
+__device__ __forceinline__ int wsw(int n) { return ((n & 3) << 2) | ((n >> 1) & 3); }
+__device__ __forceinline__ int wt_off(int n, int col) { return n * BN + (((col >> 3) ^ wsw(n)) << 3) + (col & 7); }
+
+// MFMA 32x32x16 operand from the deq(W) tile: lane l gets column c0 + l % 32
+// of reduction rows k0 + 8 (l / 32) .. +7 (two transposing reads per lane).
+__device__ __forceinline__ u32x4_t frag_w(const uint16_t *Bs, int k0, int c0, int lane) {
+  const int grp = lane >> 4, j = lane & 15;
+  const int n = k0 + (grp >> 1) * 8 + (j >> 2);
+  const int col = c0 + (grp & 1) * 16 + (j & 3) * 4;
+  const u32x2_t lo = lds_read_tr16(Bs + wt_off(n, col));
+  const u32x2_t hi = lds_read_tr16(Bs + wt_off(n + 4, col));
+  return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+}
 
 // Raw loads of one thread for one step: its 64-element run.
 struct WRaw {
@@ -53,8 +74,8 @@ struct WRaw {
 template <int FMT>
 __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  uint16_t *const As0 = smem, *const As1 = smem + TILE64;
-  uint16_t *const Bs0 = smem + 2 * TILE64, *const Bs1 = smem + 2 * TILE64 + B_ELEMS_NN;
+  uint16_t *const As0 = smem, *const As1 = smem + TILE_A;
+  uint16_t *const Bs0 = smem + 2 * TILE_A, *const Bs1 = smem + 2 * TILE_A + TILE_W;
 
   int b = blockIdx.x;
   {
@@ -77,7 +98,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
 
   // ---- dY: direct loads into LDS; wave w, chunk c covers rows 8 (4 c + w)..
   const rsrc_t a_rsrc = big::make_rsrc(p.A.p + row0 * p.A.ld, big::clamp_bytes((row_end - row0) * p.A.ld * 2));
-  const int a_kq = ((lane & 7) ^ ((lane >> 3) & 7)) * 8;
+  const int a_kq = tile64_dma_chunk(lane, wave) * 8;
   const uint32_t a_voff0 = (uint32_t)(((wave * 8 + (lane >> 3)) * p.A.ld + a_kq) * 2);
   const uint32_t a_cstep = (uint32_t)(32 * p.A.ld * 2);
   // dY of step s into stage As, chunks 4 half .. 4 half + 3
@@ -90,13 +111,13 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
                                                16, edge ? OOB : a_voff0 + c * a_cstep, (int)(k0 * 2), 0, 0);
   };
 
-  // ---- this thread's run: reduction row k0 + t / 4, output columns
-  // col0 + 64 (t % 4) .. +63
+  // ---- this thread's run: reduction row k0 + lane, output columns
+  // col0 + 64 wave .. +63
   const int64_t Kw = p.W.K;
   const uint8_t *codes_g = p.W.codes + g * p.W.g_codes;
   const rsrc_t w_rsrc = big::make_rsrc(codes_g, big::clamp_bytes(p.W.N * (Kw >> 1)));
-  const int64_t kc = col0 + (t & 3) * 64;
-  const uint32_t w_base = (uint32_t)((t >> 2) * (Kw >> 1) + (kc >> 1));
+  const int64_t kc = col0 + wave * 64;
+  const uint32_t w_base = (uint32_t)(lane * (Kw >> 1) + (kc >> 1));
   const uint32_t w_voff0 = kc < p.Nc ? w_base : OOB;
   const uint32_t w_voff1 = kc + 32 < p.Nc ? w_base + 16 : OOB;
   const int64_t w_step = (int64_t)BKS * (Kw >> 1);
@@ -105,7 +126,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
   const uint8_t *sbase = reinterpret_cast<const uint8_t *>(p.W.scales) + (g * p.W.g_scales) * sc_bytes;
   const rsrc_t s_rsrc = big::make_rsrc(sbase, big::clamp_bytes(p.W.N * sc_per_row * sc_bytes));
   const int64_t blk = FMT == FMT_MXFP4 ? (kc >> 5) : (kc >> 6);
-  const uint32_t s_voff = kc < p.Nc ? (uint32_t)(((t >> 2) * sc_per_row + blk) * sc_bytes) : OOB;
+  const uint32_t s_voff = kc < p.Nc ? (uint32_t)((lane * sc_per_row + blk) * sc_bytes) : OOB;
   const uint32_t s_voff1 = kc + 32 < p.Nc ? s_voff + 1 : OOB;   // MXFP4 second code
   const int64_t s_step = (int64_t)BKS * sc_per_row * sc_bytes;
   const rsrc_t s2_rsrc = FMT == FMT_NF4_DQ
@@ -121,7 +142,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
       w.sc = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, s_voff, so, 0);
     } else if constexpr (FMT == FMT_NF4_DQ) {
       w.sc = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, s_voff, so, 0);
-      const int64_t idx = ((int64_t)s * BKS + (t >> 2)) * sc_per_row + (kc >> 6);
+      const int64_t idx = ((int64_t)s * BKS + lane) * sc_per_row + (kc >> 6);
       w.c2 = __builtin_amdgcn_raw_buffer_load_b32(s2_rsrc, kc < p.Nc ? (uint32_t)((idx >> 8) * 4) : OOB, 0, 0);
     } else {
       // two E8M0 codes, one byte each, so that a range check on the second
@@ -133,7 +154,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
   };
 
   // decode part `part` (0..3) of raw run w: elements 16 part .. +15 (code
-  // words 2 part, 2 part + 1) into row t / 4 of W tile Bs
+  // words 2 part, 2 part + 1) into row `lane` of W tile Bs
   auto decode_part = [&](const WRaw &w, uint16_t *Bs, RunTable &T, float &s0, float &s1, int part) {
     if (part == 0) {
       if constexpr (FMT == FMT_MXFP4) {
@@ -146,7 +167,6 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
         T = big::make_table(c, p.tab);
       }
     }
-    uint16_t *dst = Bs + (t >> 2) * LDB_NN + (t & 3) * 64;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int q = 2 * part + e;
@@ -156,7 +176,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
         v = big::decode8_mxfp4(code, q < 4 ? s0 : s1);
       else
         v = big::decode8_nf4(T, code);
-      lds_write_b128(dst + 8 * q, v);
+      lds_write_b128(Bs + wt_off(lane, wave * 64 + 8 * q), v);
     }
   };
 
@@ -172,7 +192,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
     for (int i = 0; i < 4; ++i) af[i] = lds_read_b128(As + swz(wm0 + i * 32 + l32, kk * 2 + h));
   };
   auto read_bf = [&](const uint16_t *Bs, int kk, int j) -> u32x4_t {
-    return big::frag_tr32(Bs, LDB_NN, kk * 16, wn0 + j * 32, lane);
+    return frag_w(Bs, kk * 16, wn0 + j * 32, lane);
   };
 
   // One 64-deep step on (As, Bs). The A fragments of the next sub-step are
@@ -278,7 +298,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
           for (int j = 0; j < 8; ++j)
             if (gc + j < p.Nc) w4[j >> 1] |= (uint32_t)src[j] << (16 * (j & 1));
         }
-        lds_write_b128(Bs0 + row * LDB_NN + cc, u32x4_t{w4[0], w4[1], w4[2], w4[3]});
+        lds_write_b128(Bs0 + wt_off(row, cc), u32x4_t{w4[0], w4[1], w4[2], w4[3]});
       }
       __syncthreads();
       compute_step(As0, Bs0, [](int) {});

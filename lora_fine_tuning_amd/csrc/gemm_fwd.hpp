@@ -14,13 +14,16 @@
 // over a step are 32 consecutive elements of one row. X is read from LDS in
 // the same order, so every product pairs the same k on both sides.
 //
-// X streams HBM/L2 -> LDS with bounds-checked direct loads into a ring of
-// STAGES buffers of 256 x 64 (the load for step s+2 is issued when step s
-// starts); one bare barrier per step. All look-ahead loads are issued
-// unconditionally (past the end they are out of range and return zeros), so
-// the number of loads in flight at each wait is a constant. The main loop is
-// unrolled twice so that the two sets of look-ahead registers swap roles
-// instead of being copied (a copy would wait for loads still in flight).
+// X streams HBM/L2 -> LDS (swizzled so the operand reads are free of bank
+// conflicts) with bounds-checked direct loads into a ring of
+// five buffers of 256 x 64 (the X of step s+3 and the W of step s+2 are
+// loaded while step s computes, spread evenly over its sub-steps so that the
+// address units never back up and stall the issuing wave); one bare barrier
+// per step, in mid-step. All look-ahead loads are issued unconditionally
+// (past the end they are out of range and return zeros), so the number of
+// loads in flight at each wait is a constant. The main loop is unrolled twice
+// so that the two sets of look-ahead registers swap roles instead of being
+// copied (a copy would wait for loads still in flight).
 //
 // NF4 runs decode through a 16-entry bf16 table bf16(q[i] * c) selected with
 // v_perm_b32, MXFP4 through v_cvt_scalef32_pk_bf16_fp4; NF4-DQ rebuilds
@@ -37,12 +40,12 @@ using big::Params;
 using big::RunTable;
 using big::rsrc_t;
 
-constexpr int BM = 256, BN = 256, BKS = 64, THREADS = 256, STAGES = 4;
+constexpr int BM = 256, BN = 256, BKS = 64, THREADS = 256, STAGES = 5;
 constexpr int TILE = BM * BKS;   // one X stage, bf16 elements
 
 __host__ __device__ constexpr int lds_bytes() { return STAGES * TILE * 2; }
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BKS + ((chunk ^ (row & 7)) << 3); }
+__device__ __forceinline__ int swz(int row, int chunk) { return tile64_swz(row, chunk); }
 
 // Decoded operands of one lane for one step: row j (two 32-row blocks), four
 // sub-steps of 8 bf16 (k = 32 h + 8 kk .. +7 of the lane's row).
@@ -82,17 +85,18 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
 
   // ---- X: direct loads into the LDS ring ------------------------------------
   // wave w, chunk c covers tile rows 8 (4 c + w) .. +7; lane l: row + l / 8,
-  // stored chunk position l % 8, which holds logical chunk (l % 8) ^ (row % 8).
+  // stored chunk position l % 8 (tile64 layout).
   const rsrc_t a_rsrc = big::make_rsrc(p.A.p + row0 * p.A.ld, big::clamp_bytes((row_end - row0) * p.A.ld * 2));
   // chunk c is 32 rows below chunk 0: offsets a_voff0 + c * a_cstep
-  const int a_kq = ((lane & 7) ^ ((lane >> 3) & 7)) * 8;
+  const int a_kq = tile64_dma_chunk(lane, wave) * 8;
   const uint32_t a_voff0 = (uint32_t)(((wave * 8 + (lane >> 3)) * p.A.ld + a_kq) * 2);
   const uint32_t a_cstep = (uint32_t)(32 * p.A.ld * 2);
-  auto issue_a = [&](int s, uint16_t *As) {
+  // X of step s into stage As, chunks 2 part .. 2 part + 1 (part 0..3)
+  auto issue_a = [&](int s, uint16_t *As, int part) {
     const int64_t k0 = (int64_t)s * BKS;
     const bool edge = k0 + a_kq >= p.R;
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+    for (int c = 2 * part; c < 2 * part + 2; ++c)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (__attribute__((address_space(3))) void *)(As + (c * 4 + wave) * 512),
                                                16, edge ? OOB : a_voff0 + c * a_cstep, (int)(k0 * 2), 0, 0);
   };
@@ -119,26 +123,29 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
     s_idx0[j] = (col0 + rloc) * sc_per_row;
   }
 
-  auto load_w = [&](int s, WRaw &w) {
+  // W of step s, part 0..3: part j < 2 loads row j's codes and scale (with
+  // its second-level scale for NF4-DQ); parts 2 and 3 load nothing, so every
+  // W load of a step is issued in its first half, a full step ahead of use
+  auto load_w = [&](int s, WRaw &w, int part) {
+    if (part >= 2) return;
     const int64_t k0 = (int64_t)s * BKS;
     // this lane's half lies inside the row (MXFP4 rows may end at k % 64 == 32)
     const bool half_ok = k0 + 32 * h < p.R;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      w.c[j] = __builtin_bit_cast(
-          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, half_ok ? w_voff[j] : OOB, (int)(k0 >> 1), 0));
-      if constexpr (FMT == FMT_NF4) {
-        w.sc[j] = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, half_ok ? s_voff[j] : OOB, (int)((k0 >> 6) * 4), 0);
-      } else if constexpr (FMT == FMT_NF4_DQ) {
-        w.sc[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, half_ok ? s_voff[j] : OOB, (int)(k0 >> 6), 0);
-        const int64_t gi = (s_idx0[j] + (k0 >> 6)) >> 8;
-        w.c2[j] = __builtin_amdgcn_raw_buffer_load_b32(s2_rsrc, half_ok ? (uint32_t)(gi * 4) : OOB, 0, 0);
-      } else {
-        w.sc[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, half_ok ? s_voff[j] + h : OOB, (int)(k0 >> 5), 0);
-      }
+    const int j = part;
+    w.c[j] = __builtin_bit_cast(
+        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, half_ok ? w_voff[j] : OOB, (int)(k0 >> 1), 0));
+    if constexpr (FMT == FMT_NF4) {
+      w.sc[j] = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, half_ok ? s_voff[j] : OOB, (int)((k0 >> 6) * 4), 0);
+    } else if constexpr (FMT == FMT_NF4_DQ) {
+      w.sc[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, half_ok ? s_voff[j] : OOB, (int)(k0 >> 6), 0);
+      const int64_t gi = (s_idx0[j] + (k0 >> 6)) >> 8;
+      w.c2[j] = __builtin_amdgcn_raw_buffer_load_b32(s2_rsrc, half_ok ? (uint32_t)(gi * 4) : OOB, 0, 0);
+    } else {
+      w.sc[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, half_ok ? s_voff[j] + h : OOB, (int)(k0 >> 5), 0);
     }
   };
-  // loads per load_w call (all issued unconditionally)
+  // loads issued by load_w over a whole step, all in parts 0 and 1 (issued
+  // unconditionally, so the count is exact)
   constexpr int W_LOADS = FMT == FMT_NF4_DQ ? 6 : 4;
 
   // decode part `part` (0..3) of raw w into f: row j = part / 2, words
@@ -173,19 +180,20 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
     acc[i][1] = f32x16_t{};
   }
 
-  // wait until only the loads issued by the current step (load_w + issue_a
-  // for step s+2) may be in flight: the X stage of step s+1 has landed;
-  // lgkmcnt 0 as well.
-  constexpr int VM_OUT = 8 + W_LOADS;
+  // At the mid-step wait of step s, the X of step s+1 (issued during step
+  // s-2) must have landed; still in flight may be everything issued during
+  // step s-1 and during sub-steps 0 and 1 of step s. lgkmcnt 0 as well.
+  constexpr int VM_OUT = (8 + W_LOADS) + (4 + W_LOADS);
   static_assert(VM_OUT < 64, "vmcnt field");
   constexpr int VMCNT = (VM_OUT & 15) | (7 << 4) | (0 << 8) | ((VM_OUT >> 4) << 14);
 
   // Sub-step kk of a step: 16 MFMAs on fragments x (chunk kk of the step's X
   // stage); fragment i is reloaded as soon as its two MFMAs have issued, from
   // chunk kk+1, or for kk == 3 from chunk 0 of the next step's stage, so the
-  // LDS latency is always a sub-step ahead. The schedule is pinned: MFMA
-  // pairs with the LDS read of the freed fragment and a share of the VALU
-  // work (hook) between them; nothing moves across sub-steps.
+  // LDS latency is always a sub-step ahead. hook() holds this sub-step's share
+  // of the VALU work (decode) and of the global loads. The schedule is pinned:
+  // MFMA pairs with the LDS read of the freed fragment, a global load every
+  // other pair, and VALU work between them; nothing moves across sub-steps.
   auto sub_step = [&](const WFrag &cur, int kk, u32x4_t x[8], const uint16_t *src, int chunk, bool reload,
                       auto &&hook) {
 #pragma unroll
@@ -202,6 +210,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
       __builtin_amdgcn_sched_group_barrier(0x002, LORA4_SCHED_VALU, 0);   // VALU
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
       if (reload) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // LDS read
+      if (i & 1) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);       // global load
       __builtin_amdgcn_sched_group_barrier(0x002, LORA4_SCHED_VALU, 0);   // VALU
     }
 #endif
@@ -209,59 +218,64 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   };
 
   // step s: X of step s in stage cur (its chunk-0 fragments already in x),
-  // operands fcur. Issues step s+2 (X into stage ahead, W into rload),
-  // decodes step s+1 (rdec -> fnxt), and after sub-step 1 waits for the X of
-  // step s+1 and meets the other waves: stage nxt is then complete, and every
-  // wave is done with step s-1, whose stage the next step refills.
+  // operands fcur. Over its four sub-steps it decodes step s+1 (rdec ->
+  // fnxt), loads the W of step s+2 (rload) and the X of step s+3 (stage
+  // ahead); after sub-step 1 it waits for the X of step s+1 and meets the
+  // other waves: stage nxt is then complete, and every wave is done with
+  // step s-1, whose stage step s+1 refills.
   auto body = [&](int s, const uint16_t *cur, const uint16_t *nxt, uint16_t *ahead, const WRaw &rdec, WRaw &rload,
                   const WFrag &fcur, WFrag &fnxt, u32x4_t x[8]) {
-    // W first: the decode of step s+1 then waits only for the W loads of the
-    // previous body, not for its X loads
-    load_w(s + 2, rload);
-    issue_a(s + 2, ahead);
     RunTable T;
     float sc = 0.0f;
-    sub_step(fcur, 0, x, cur, h * 4 + 1, true, [&] { decode_part(rdec, fnxt, T, sc, 0); });
-    sub_step(fcur, 1, x, cur, h * 4 + 2, true, [&] { decode_part(rdec, fnxt, T, sc, 1); });
+    auto work = [&](int kk) {
+      return [&, kk] {
+        decode_part(rdec, fnxt, T, sc, kk);
+        load_w(s + 2, rload, kk);
+        issue_a(s + 3, ahead, kk);
+      };
+    };
+    sub_step(fcur, 0, x, cur, h * 4 + 1, true, work(0));
+    sub_step(fcur, 1, x, cur, h * 4 + 2, true, work(1));
     __builtin_amdgcn_s_waitcnt(VMCNT);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    sub_step(fcur, 2, x, cur, h * 4 + 3, true, [&] { decode_part(rdec, fnxt, T, sc, 2); });
-    sub_step(fcur, 3, x, nxt, h * 4 + 0, true, [&] { decode_part(rdec, fnxt, T, sc, 3); });
+    sub_step(fcur, 2, x, cur, h * 4 + 3, true, work(2));
+    sub_step(fcur, 3, x, nxt, h * 4 + 0, true, work(3));
   };
 
   const int steps = (int)((p.R + BKS - 1) / BKS);
   WRaw r0, r1;
   WFrag f0, f1;
   u32x4_t x[8];
-  // ring of four stages; step s uses stage s % 4
-  uint16_t *st0 = smem, *st1 = smem + TILE, *st2 = smem + 2 * TILE, *st3 = smem + 3 * TILE;
-  issue_a(0, st0);
-  issue_a(1, st1);
-  load_w(0, r0);
+  // ring of five stages; step s uses stage s % 5
+  auto stage = [&](int i) -> uint16_t * { return smem + (i >= STAGES ? i - STAGES : i) * TILE; };
+#pragma unroll
+  for (int part = 0; part < 4; ++part) {
+    issue_a(0, stage(0), part);
+    issue_a(1, stage(1), part);
+    issue_a(2, stage(2), part);
+    load_w(0, r0, part);
+  }
   {
     RunTable T;
     float sc = 0.0f;
 #pragma unroll
     for (int part = 0; part < 4; ++part) decode_part(r0, f0, T, sc, part);
   }
-  load_w(1, r1);
+#pragma unroll
+  for (int part = 0; part < 4; ++part) load_w(1, r1, part);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] = lds_read_b128(st0 + swz(i * 32 + l32, h * 4));
-  int s = 0;
+  for (int i = 0; i < 8; ++i) x[i] = lds_read_b128(stage(0) + swz(i * 32 + l32, h * 4));
+  int s = 0, si = 0;   // si = s % 5
   for (; s + 2 <= steps; s += 2) {
-    body(s, st0, st1, st2, r1, r0, f0, f1, x);
-    body(s + 1, st1, st2, st3, r0, r1, f1, f0, x);
-    uint16_t *t0 = st0, *t1 = st1;   // rotate by two
-    st0 = st2;
-    st1 = st3;
-    st2 = t0;
-    st3 = t1;
+    body(s, stage(si), stage(si + 1), stage(si + 3), r1, r0, f0, f1, x);
+    body(s + 1, stage(si + 1), stage(si + 2), stage(si + 4), r0, r1, f1, f0, x);
+    si = si + 2 >= STAGES ? si + 2 - STAGES : si + 2;
   }
-  if (s < steps) body(s, st0, st1, st2, r1, r0, f0, f1, x);
+  if (s < steps) body(s, stage(si), stage(si + 1), stage(si + 3), r1, r0, f0, f1, x);
   // the look-ahead loads past the end still write (zeros) into the ring
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
