@@ -37,7 +37,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-tokens", type=int, default=8192,
-                    help="tokens per layer in the CPU oracle sample")
+                    help="tokens per layer in the CPU oracle sample (capped at the layer's tokens)")
+    ap.add_argument("--cpu-reps", type=int, default=3, help="passes of the CPU oracle over its sample")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB a few times (counter calibration) and exit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
     return ap.parse_args()
@@ -104,7 +107,52 @@ def kernel_flops(name, spec):
     }.get(name, 0)
 
 
-def cpu_baseline(specs, tokens):
+def csrc_digest():
+    """sha256 over the HIP sources of the library (any kernel change alters it)."""
+    import hashlib
+    d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lora_fine_tuning_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(f.encode())
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (profiles/<workload>_<kernel>_traffic.md), or None when there is none or it
+    was taken on other kernel sources."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        f"{workload}_{kernel}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("traffic:"):
+                rec = dict(kv.split("=", 1) for kv in line.split()[1:])
+    if rec.get("csrc_sha256") != csrc_digest():
+        return None
+    return {"bytes_per_launch": float(rec["bytes_per_launch"]), "fetch_bytes": float(rec["fetch_bytes"]),
+            "write_bytes": float(rec["write_bytes"])}
+
+
+def copy_probe(mib):
+    """A plain device copy of known size, for scaling the FETCH_SIZE /
+    WRITE_SIZE counters: each launch reads and writes mib MiB."""
+    import torch
+    n = mib * 1024 * 1024 // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"[copy] 3 launches of {mib} MiB read + {mib} MiB written")
+
+
+def cpu_baseline(specs, tokens, reps):
     """The oracle (never tuned) on a bounded sample: every layer of the workload,
     the first `tokens` rows. Oracle packing is done first, untimed; the timed
     part is what a step computes: dequant + forward + backward per layer."""
@@ -128,22 +176,23 @@ def cpu_baseline(specs, tokens):
         prepared.append((spec, packs, t["X"][:m], t["dY"][:m], t["A"], t["B"], m))
     flops = 0
     t0 = time.perf_counter()
-    for spec, packs, X, dY, A, B, m in prepared:
-        for e, pk in enumerate(packs):
-            if spec.fmt == synth.MXFP4:
-                Wd = lora.as_f64(mxfp4.dequantize(*pk))
-            elif spec.fmt == synth.NF4_DQ:
-                Wd = lora.as_f64(nf4.dequantize_dq(*pk))
-            else:
-                Wd = lora.as_f64(nf4.dequantize(*pk))
-            Ae = lora.as_f64(A if spec.experts == 1 else A[e])
-            Be = lora.as_f64(B if spec.experts == 1 else B[e])
-            Xf, dYf = lora.as_f64(X), lora.as_f64(dY)
-            o = lora.forward(Xf, Wd, Ae, Be, spec.s)
-            lora.backward(Xf, Wd, Ae, Be, spec.s, dYf, Z=o["Z"])
-            flops += 4 * m * spec.N * spec.K + 6 * m * spec.r * (spec.N + spec.K)
-            if spec.experts > 1:
-                break          # sample: the first expert of a grouped layer
+    for _ in range(reps):
+        for spec, packs, X, dY, A, B, m in prepared:
+            for e, pk in enumerate(packs):
+                if spec.fmt == synth.MXFP4:
+                    Wd = lora.as_f64(mxfp4.dequantize(*pk))
+                elif spec.fmt == synth.NF4_DQ:
+                    Wd = lora.as_f64(nf4.dequantize_dq(*pk))
+                else:
+                    Wd = lora.as_f64(nf4.dequantize(*pk))
+                Ae = lora.as_f64(A if spec.experts == 1 else A[e])
+                Be = lora.as_f64(B if spec.experts == 1 else B[e])
+                Xf, dYf = lora.as_f64(X), lora.as_f64(dY)
+                o = lora.forward(Xf, Wd, Ae, Be, spec.s)
+                lora.backward(Xf, Wd, Ae, Be, spec.s, dYf, Z=o["Z"])
+                flops += 4 * m * spec.N * spec.K + 6 * m * spec.r * (spec.N + spec.K)
+                if spec.experts > 1:
+                    break          # sample: the first expert of a grouped layer
     dt = time.perf_counter() - t0
     try:
         from threadpoolctl import threadpool_info
@@ -152,12 +201,16 @@ def cpu_baseline(specs, tokens):
         threads = len(os.sched_getaffinity(0))
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "seconds": dt,
-            "sample": f"every layer of the workload at its first {tokens} tokens (first expert of grouped "
-                      f"layers): oracle dequant + forward + backward, float64 numpy"}
+            "sample": f"{reps} passes over every layer of the workload at its first {tokens} tokens (capped at "
+                      f"the layer's tokens; first expert of grouped layers): oracle dequant + forward + "
+                      f"backward, float64 numpy"}
 
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -228,8 +281,10 @@ def main():
         n, tot = kt[dom]
         per_launch = kflops[dom] / len(specs)
         achieved = (kflops[dom] * args.steps) / (tot * 1e-3) / 1e12
+        tr = recorded_traffic(args.workload, dom)
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "traffic": None if tr is None else round(tr["bytes_per_launch"]),
                     "flops_per_launch_avg": per_launch, "avg_launch_us": round(1e3 * tot / n, 2),
                     "ms_per_step_with_events": round(ms_ev, 4)}
         for k, v in sorted(kernels.items(), key=lambda kv: -kv[1]["total_ms_per_step"]):
@@ -239,7 +294,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline (oracle) on {args.cpu_tokens} tokens per layer")
-        cpu = cpu_baseline(specs, args.cpu_tokens)
+        cpu = cpu_baseline(specs, args.cpu_tokens, args.cpu_reps)
         log(f"[bench] cpu oracle {cpu['value']:.4f} TFLOP/s in {cpu['seconds']:.1f} s on {cpu['cores']} threads")
 
     s0 = specs[0]

@@ -36,7 +36,7 @@
 #define LORA4_SCHED_INTERLEAVE 1
 #endif
 #ifndef LORA4_SCHED_VALU
-#define LORA4_SCHED_VALU 4
+#define LORA4_SCHED_VALU 5
 #endif
 
 namespace lora4 {
@@ -69,6 +69,12 @@ struct Params {
   int tiles_n;        // ceil(Nc / 256)
   int nblocks;        // gridDim.x
   Nf4Table tab;
+  // split reduction (forward kernel only): ksplit blocks per tile, each over
+  // split_steps 64-deep steps; ksplit > 1 writes fp32 partials
+  // Cpart[split][M][Nc] instead of C (the rank-r tail goes into split 0)
+  int ksplit;
+  int split_steps;
+  float *Cpart;
 };
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;

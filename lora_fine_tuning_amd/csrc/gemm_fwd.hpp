@@ -69,6 +69,11 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
     const int per = p.nblocks >> 3;
     if (b < per * 8) b = (b & 7) * per + (b >> 3);
   }
+  // split-major order: the blocks of one split are consecutive (and share
+  // the K range of X and W)
+  const int ntiles = p.nblocks / p.ksplit;
+  const int split = b / ntiles;
+  b -= split * ntiles;
   const int tn = b % p.tiles_n;
   const int slot = b / p.tiles_n;
   const RowTile rt = map_row_tile(slot, BM, p.offsets, p.groups, p.M);
@@ -92,8 +97,10 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   const uint32_t a_voff0 = (uint32_t)(((wave * 8 + (lane >> 3)) * p.A.ld + a_kq) * 2);
   const uint32_t a_cstep = (uint32_t)(32 * p.A.ld * 2);
   // X of step s into stage As, chunks 2 part .. 2 part + 1 (part 0..3)
+  // steps are numbered within this block's range, which starts at step sb
+  const int sb = split * p.split_steps;
   auto issue_a = [&](int s, uint16_t *As, int part) {
-    const int64_t k0 = (int64_t)s * BKS;
+    const int64_t k0 = (int64_t)(s + sb) * BKS;
     const bool edge = k0 + a_kq >= p.R;
 #pragma unroll
     for (int c = 2 * part; c < 2 * part + 2; ++c)
@@ -128,7 +135,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   // W load of a step is issued in its first half, a full step ahead of use
   auto load_w = [&](int s, WRaw &w, int part) {
     if (part >= 2) return;
-    const int64_t k0 = (int64_t)s * BKS;
+    const int64_t k0 = (int64_t)(s + sb) * BKS;
     // this lane's half lies inside the row (MXFP4 rows may end at k % 64 == 32)
     const bool half_ok = k0 + 32 * h < p.R;
     const int j = part;
@@ -244,7 +251,8 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
     sub_step(fcur, 3, x, nxt, h * 4 + 0, true, work(3));
   };
 
-  const int steps = (int)((p.R + BKS - 1) / BKS);
+  const int all_steps = (int)((p.R + BKS - 1) / BKS);
+  const int steps = min(all_steps - sb, p.split_steps);
   WRaw r0, r1;
   WFrag f0, f1;
   u32x4_t x[8];
@@ -281,7 +289,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   __syncthreads();
 
   // ---- rank-r tail: (s Z) B^T; Z rows through LDS, B rows to registers -----
-  if (p.r2 > 0) {
+  if (p.r2 > 0 && split == 0) {
     const uint16_t *B2 = p.B2.p + g * p.B2.gstride;
     uint16_t *As = smem;
     const bool b_vec = (p.B2.ld % 8) == 0;
@@ -336,6 +344,28 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
 
   // ---- epilogue: register e of acc[i][j] holds
   // Y[32 i + lane % 32][64 wave + 32 j + 8 (e / 4) + 4 (lane / 32) + e % 4]
+  if (p.ksplit > 1) {
+    // fp32 partial of this split: Cpart[split][row][col], row stride Nc
+    // (a multiple of 4 whenever the reduction is split)
+    float *pbase = p.Cpart + (int64_t)split * p.M * p.Nc;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t row = row0 + i * 32 + l32;
+      if (row >= row_end) continue;
+      float *prow = pbase + row * p.Nc;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int64_t col = col0 + wave * 64 + j * 32 + r4 * 8 + h * 4;
+          if (col < p.Nc)
+            *reinterpret_cast<f32x4_t *>(prow + col) =
+                f32x4_t{acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
+        }
+      }
+    }
+    return;
+  }
   const bool vec_out = (p.ldc % 4) == 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {

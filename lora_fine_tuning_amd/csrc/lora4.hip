@@ -265,29 +265,25 @@ constexpr int TARGET_WG = 1024;  // workgroups wanted for the skinny passes
 
 int skinny_tile(int r) { return r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : 128; }
 
-// Splits of a reduction of length R (units of 64) for a skinny product
-// with `tiles` output tiles.
-int choose_split(int64_t tiles, int64_t R) {
-  int64_t want = ceil_div(TARGET_WG, std::max<int64_t>(tiles, 1));
-  int64_t maxs = std::max<int64_t>(1, R / 512);
-  return (int)std::max<int64_t>(1, std::min(want, maxs));
-}
-
-int64_t split_len(int64_t R, int splits) { return ceil_div(ceil_div(R, splits), 64) * 64; }
+// Forward base GEMM schedule (defined with the large-tile dispatch below).
+struct FwdSched {
+  bool use;          // register-direct kernel (else the 128 x 128 kernel)
+  int ksplit;        // reduction splits
+  int split_steps;   // 64-deep steps per split
+};
+FwdSched fwd_sched(int64_t M, int64_t N, int64_t K, int64_t E, const PackedW &W);
 
 struct Plan {
   int64_t M, N, K, E;
   int r;
   int rt;             // skinny tile width (Z, dZ, TN P tile)
   int64_t row_slots;  // row-tile slots for BM = 128
-  int zsplit;         // Z pass splits over K
-  int64_t zlen;
-  int dzsplit;        // dZ pass splits over N
-  int64_t dzlen;
   int tq_a, tq_b;     // TN Q tiles (dA over K, dB over N)
   int msplit_a, msplit_b;
+  int fsplit, fsplit_steps;   // forward base GEMM: reduction splits (1: none)
+  bool fregs;                 // forward base GEMM on the register-direct kernel
   // workspace offsets
-  size_t off_sz, off_zw, off_dz, off_part, off_part_b, bytes;
+  size_t off_sz, off_zw, off_dz, off_part, off_part_b, off_party, bytes;
 };
 
 constexpr int BM_MAIN = 128, BN_MAIN = 128;
@@ -304,12 +300,6 @@ Plan make_plan(int which, const lora4_W *W, int64_t M, int r) {
   p.rt = skinny_tile(r);
   p.row_slots = ceil_div(std::max<int64_t>(M, 1), BM_MAIN) + (p.E > 1 ? p.E : 0);
   const int64_t rtiles = ceil_div(r, p.rt);
-  p.zsplit = choose_split(p.row_slots * rtiles, p.K);
-  p.zlen = split_len(p.K, p.zsplit);
-  p.zsplit = (int)ceil_div(p.K, p.zlen);
-  p.dzsplit = choose_split(p.row_slots * rtiles, p.N);
-  p.dzlen = split_len(p.N, p.dzsplit);
-  p.dzsplit = (int)ceil_div(p.N, p.dzlen);
   p.tq_a = (int)ceil_div(p.K, TN_BQ);
   p.tq_b = (int)ceil_div(p.N, TN_BQ);
   const int64_t mavg = std::max<int64_t>(1, M / p.E);
@@ -321,6 +311,10 @@ Plan make_plan(int which, const lora4_W *W, int64_t M, int r) {
   };
   p.msplit_a = msplit(p.tq_a);
   p.msplit_b = msplit(p.tq_b);
+  const FwdSched fs = fwd_sched(M, p.N, p.K, p.E, packed_of(W));
+  p.fregs = fs.use;
+  p.fsplit = fs.ksplit;
+  p.fsplit_steps = fs.split_steps;
 
   const size_t mr2 = align256((size_t)M * r * 2);
   size_t off = 0;
@@ -329,6 +323,8 @@ Plan make_plan(int which, const lora4_W *W, int64_t M, int r) {
   p.off_zw = off;   // backward: recomputed Z
   if (which == 1) off += mr2;
   p.off_dz = p.off_sz;
+  p.off_party = off;  // forward: fp32 partials of the split base GEMM
+  if (which == 0 && p.fsplit > 1) off += align256((size_t)p.fsplit * M * p.N * 4);
   p.off_part = off;  // backward: dA partials, then dB^T partials
   if (which == 1) {
     p.off_part_b = off + align256((size_t)p.msplit_a * p.E * r * p.K * 4);
@@ -368,6 +364,34 @@ bool big_fits(int64_t ld_a, int64_t M, const PackedW &W) {
   const int64_t ahead = 4 * 64 * (W.K / 2);
   return ld_a % 8 == 0 && W.g_codes + ahead < lim && ld_a * 2 * 256 < lim && W.g_scales * 4 + ahead < lim &&
          W.g_scales2 * 4 < lim;
+}
+
+// The register-direct forward kernel runs one 256 x 256 tile per CU; with
+// fewer tiles than that the reduction is split (each split writes fp32
+// partials, rows of N % 4 == 0 floats, at least 8 steps per split, partials
+// capped at 256 MiB) and a
+// deterministic reduction adds them. The automatic policy keeps the 128 x 128
+// kernel when even the split grid would leave most of the GPU idle.
+FwdSched fwd_sched(int64_t M, int64_t N, int64_t K, int64_t E, const PackedW &W) {
+  FwdSched f{false, 1, 1 << 30};
+  if (K <= 0 || M <= 0 || !big_fits(K, M, W)) return f;
+  const int pol = big_policy();
+  if (pol == 0) return f;
+  const int64_t tiles = (ceil_div(M, fwd::BM) + (E > 1 ? E : 0)) * ceil_div(N, fwd::BN);
+  const int64_t steps = ceil_div(K, fwd::BKS);
+  int64_t ks = 1;
+  if (tiles < 192 && N % 4 == 0) {
+    ks = std::min<int64_t>({256 / tiles, std::max<int64_t>(1, steps / 8), 16});
+    const int64_t cap = ((int64_t)256 << 20) / std::max<int64_t>(1, M * N * 4);
+    ks = std::max<int64_t>(1, std::min(ks, cap));
+  }
+  if (pol < 0 && tiles * ks < 192) return f;
+  f.use = true;
+  if (ks > 1) {
+    f.split_steps = (int)ceil_div(steps, ks);
+    f.ksplit = (int)ceil_div(steps, f.split_steps);
+  }
+  return f;
 }
 
 bool use_big(int64_t M, int64_t Nc, int64_t E) {
@@ -455,14 +479,34 @@ big::Params big_params(const Mat &A, const PackedW &W, int64_t R, const Mat &A2,
   p.tiles_n = (int)ceil_div(Nc, big::BN);
   p.nblocks = (int)((ceil_div(std::max<int64_t>(M, 1), big::BM) + (E > 1 ? E : 0)) * p.tiles_n);
   p.tab = nf4_table();
+  p.ksplit = 1;
+  p.split_steps = 1 << 30;
+  p.Cpart = nullptr;
   return p;
 }
 
-lora4_status run_nt_main_fmt(int fmt, const NtParams &p, dim3 grid, hipStream_t st) {
-  if (p.R > 0 && big_fits(p.A.ld, p.M, p.W) && use_big(p.M, p.Nc, p.groups)) {
+// Forward base GEMM: the register-direct kernel as the plan schedules it
+// (split partials in `party`, then reduced into the output), else the
+// 128 x 128 kernel.
+lora4_status run_nt_main_fmt(int fmt, const NtParams &p, dim3 grid, const Plan &pl, float *party, hipStream_t st) {
+  if (p.R > 0 && use_fwd_regs() && pl.fregs) {
     big::Params q = big_params(p.A, p.W, p.R, p.A2, p.B2, p.r2, p.M, p.Nc, p.offsets, p.groups, p.out.C,
                                p.out.ldc);
-    if (use_fwd_regs()) return run_fwd_fmt(fmt, q, st);
+    q.ksplit = pl.fsplit;
+    q.split_steps = pl.fsplit_steps;
+    q.nblocks *= pl.fsplit;
+    q.Cpart = party;
+    TRY(run_fwd_fmt(fmt, q, st));
+    if (pl.fsplit > 1) {
+      const int64_t n = p.M * p.Nc;
+      TRY(launch_args("reduce_y", k_reduce_bf16, dim3((unsigned)ceil_div(n, 256)), dim3(256), st,
+                      (const float *)party, pl.fsplit, n, n, p.out.C, 1.0f, (uint16_t *)nullptr, 0.0f));
+    }
+    return LORA4_OK;
+  }
+  if (!use_fwd_regs() && p.R > 0 && big_fits(p.A.ld, p.M, p.W) && use_big(p.M, p.Nc, p.groups)) {
+    big::Params q = big_params(p.A, p.W, p.R, p.A2, p.B2, p.r2, p.M, p.Nc, p.offsets, p.groups, p.out.C,
+                               p.out.ldc);
     return run_big_fmt<0>("gemm_nt_base", fmt, q, st);
   }
   switch (fmt) {
@@ -659,19 +703,20 @@ lora4_status lora4_forward(const lora4_W *W, const uint16_t *X, int64_t M, const
   p.out = GemmOut{Y, pl.N, nullptr, 0, 1.0f};
   p.tab = nf4_table();
   dim3 grid((unsigned)ceil_div(pl.N, BN_MAIN), (unsigned)pl.row_slots, 1);
-  TRY(run_nt_main_fmt(W->format, p, grid, st));
+  float *party = ws_at<float>(workspace, pl.off_party);
+  TRY(run_nt_main_fmt(W->format, p, grid, pl, party, st));
   if (Y_base) {
     NtParams q = p;
     q.r2 = 0;
     q.out.C = Y_base;
-    TRY(run_nt_main_fmt(W->format, q, grid, st));
+    TRY(run_nt_main_fmt(W->format, q, grid, pl, party, st));
   }
   if (Y_lora) {
     NtParams q = p;
     q.R = 0;
     q.Rsplit = 64;
     q.out.C = Y_lora;
-    TRY(run_nt_main_fmt(W->format, q, grid, st));
+    TRY(run_nt_main_fmt(W->format, q, grid, pl, party, st));
   }
   return LORA4_OK;
 }

@@ -189,3 +189,33 @@ def test_large_tile_shape_selected_automatically(monkeypatch):
     bref = lora.backward(X, Wd, A, B, lay.s, dY)
     assert rel(got["dX"][rows], bref["dX"][rows]) <= TOL
     assert rel(got["dA"], bref["dA"]) <= TOL and rel(got["dB"], bref["dB"]) <= TOL
+
+
+@pytest.mark.parametrize("fmt", [synth.NF4, synth.NF4_DQ, synth.MXFP4])
+@pytest.mark.parametrize("M,K,N,r", [(512, 4096, 256, 16),     # 2 tiles: 8-way split of 64 steps
+                                     (700, 2048, 1000, 16),    # ragged rows, 12 tiles: 4-way split
+                                     (300, 2048, 258, 8)])     # N % 4 != 0: no split
+def test_forward_split_reduction(fmt, M, K, N, r, monkeypatch):
+    """Forced onto the register-direct forward kernel, few-tile outputs split
+    the reduction (fp32 partials + reduction); the rank-r tail is added once."""
+    monkeypatch.setenv("LORA4_BIG", "1")
+    if fmt == synth.MXFP4 and K % 64 == 0:
+        K -= 32
+    lay = synth.small_layer(M, K, N, r, fmt=fmt, index=(M + N) % 89)
+    print_case("split", fmt, M, K, N, r)
+    t = synth.inputs(lay)
+    _check_all(_run(lay, t), _oracle(lay, t), keys=("Y", "Y_base", "Y_lora", "Z"))
+
+
+def test_forward_split_grouped(monkeypatch):
+    """Split reduction with grouped rows (one group empty)."""
+    monkeypatch.setenv("LORA4_BIG", "1")
+    K, N, r, E = 2048, 128, 16, 3
+    offs = [0, 300, 300, 420]
+    lay = synth.small_layer(offs[-1], K, N, r, fmt=synth.NF4, index=33, experts=E, offsets=offs)
+    print_case("split grouped", offs)
+    t = synth.inputs(lay)
+    got = _run(lay, t, offsets=offs)
+    Ws = [dequant_rows(t["W"][e], np.arange(N), synth.NF4) for e in range(E)]
+    fo = lora.grouped_forward(f64(t["X"]), Ws, [f64(a) for a in t["A"]], [f64(b) for b in t["B"]], lay.s, offs)
+    assert rel(got["Y"], fo["Y"]) <= TOL
