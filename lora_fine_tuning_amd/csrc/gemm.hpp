@@ -627,14 +627,48 @@ __global__ __launch_bounds__(THREADS) void k_gemm_tn(TnParams p) {
 // --------------------------------------------------------------------------
 
 // out1[i] = bf16(alpha1 * sum_s part[s][i]); out2 (optional) with alpha2.
+// out = bf16(alpha * sum_k part[k][i]), summed in split order. Four elements
+// per thread, and the loads of up to 16 splits issued before the adds.
 __global__ void k_reduce_bf16(const float *part, int splits, int64_t stride, int64_t n,
                               uint16_t *out1, float alpha1, uint16_t *out2, float alpha2) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (i >= n) return;
-  float s = 0.f;
-  for (int k = 0; k < splits; ++k) s += part[k * stride + i];
-  if (out1) out1[i] = to_bf16(s * alpha1);
-  if (out2) out2[i] = to_bf16(s * alpha2);
+  const bool vec = (n % 4) == 0 && (stride % 4) == 0;
+  if (!vec || i + 4 > n) {
+    for (int64_t e = i; e < n && e < i + 4; ++e) {
+      float s = 0.f;
+      for (int k = 0; k < splits; ++k) s += part[k * stride + e];
+      if (out1) out1[e] = to_bf16(s * alpha1);
+      if (out2) out2[e] = to_bf16(s * alpha2);
+    }
+    return;
+  }
+  f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+  int k = 0;
+  for (; k + 16 <= splits; k += 16) {
+    f32x4_t v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = *reinterpret_cast<const f32x4_t *>(part + (k + u) * stride + i);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) s += v[u];
+  }
+  if (k < splits) {
+    f32x4_t v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (k + u < splits) v[u] = *reinterpret_cast<const f32x4_t *>(part + (k + u) * stride + i);
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (k + u < splits) s += v[u];
+  }
+  if (out1) {
+    const u32x2_t w = {pack_bf16x2(s[0] * alpha1, s[1] * alpha1), pack_bf16x2(s[2] * alpha1, s[3] * alpha1)};
+    *reinterpret_cast<u32x2_t *>(out1 + i) = w;
+  }
+  if (out2) {
+    const u32x2_t w = {pack_bf16x2(s[0] * alpha2, s[1] * alpha2), pack_bf16x2(s[2] * alpha2, s[3] * alpha2)};
+    *reinterpret_cast<u32x2_t *>(out2 + i) = w;
+  }
 }
 
 // dB[g][n][j] = bf16(alpha * sum_s part[s][g][j][n]) (partials hold dB^T).

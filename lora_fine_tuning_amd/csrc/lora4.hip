@@ -272,6 +272,10 @@ struct FwdSched {
   int split_steps;   // 64-deep steps per split
 };
 FwdSched fwd_sched(int64_t M, int64_t N, int64_t K, int64_t E, const PackedW &W);
+struct SkSched;
+size_t sk_part_bytes_for(int64_t M, int64_t R, int r, int64_t E);
+lora4_status reduce_bf16(const char *name, const float *part, int splits, int64_t stride, int64_t n,
+                         uint16_t *out1, float a1, uint16_t *out2, float a2, hipStream_t st);
 
 struct Plan {
   int64_t M, N, K, E;
@@ -283,7 +287,7 @@ struct Plan {
   int fsplit, fsplit_steps;   // forward base GEMM: reduction splits (1: none)
   bool fregs;                 // forward base GEMM on the register-direct kernel
   // workspace offsets
-  size_t off_sz, off_zw, off_dz, off_part, off_part_b, off_party, bytes;
+  size_t off_sz, off_zw, off_dz, off_part, off_part_b, off_party, off_skpart, bytes;
 };
 
 constexpr int BM_MAIN = 128, BN_MAIN = 128;
@@ -323,6 +327,12 @@ Plan make_plan(int which, const lora4_W *W, int64_t M, int r) {
   p.off_zw = off;   // backward: recomputed Z
   if (which == 1) off += mr2;
   p.off_dz = p.off_sz;
+  p.off_skpart = off;  // fp32 partials of the rank-r passes (Z, then dZ)
+  {
+    size_t b = sk_part_bytes_for(M, p.K, r, p.E);
+    if (which == 1) b = std::max(b, sk_part_bytes_for(M, p.N, r, p.E));
+    off += b;
+  }
   p.off_party = off;  // forward: fp32 partials of the split base GEMM
   if (which == 0 && p.fsplit > 1) off += align256((size_t)p.fsplit * M * p.N * 4);
   p.off_part = off;  // backward: dA partials, then dB^T partials
@@ -499,8 +509,7 @@ lora4_status run_nt_main_fmt(int fmt, const NtParams &p, dim3 grid, const Plan &
     TRY(run_fwd_fmt(fmt, q, st));
     if (pl.fsplit > 1) {
       const int64_t n = p.M * p.Nc;
-      TRY(launch_args("reduce_y", k_reduce_bf16, dim3((unsigned)ceil_div(n, 256)), dim3(256), st,
-                      (const float *)party, pl.fsplit, n, n, p.out.C, 1.0f, (uint16_t *)nullptr, 0.0f));
+      TRY(reduce_bf16("reduce_y", party, pl.fsplit, n, n, p.out.C, 1.0f, nullptr, 0.0f, st));
     }
     return LORA4_OK;
   }
@@ -568,7 +577,7 @@ Mat mat(const uint16_t *p, int64_t ld, int64_t gstride = 0) { return Mat{p, ld, 
 
 lora4_status reduce_bf16(const char *name, const float *part, int splits, int64_t stride, int64_t n,
                          uint16_t *out1, float a1, uint16_t *out2, float a2, hipStream_t st) {
-  dim3 grid((unsigned)ceil_div(n, 256));
+  dim3 grid((unsigned)ceil_div(ceil_div(n, 4), 256));   // four elements per thread
   return launch_args(name, k_reduce_bf16, grid, dim3(256), st, part, splits, stride, n, out1, a1, out2, a2);
 }
 
@@ -581,9 +590,41 @@ lora4_status run_rows_tj(int transb, const skinny::Params &p, dim3 grid, hipStre
   return launch("rows_skinny_z", skinny::k_rows_skinny<TM, TJ, 0>, grid, dim3(skinny::THREADS), p, st);
 }
 
+// Rank-r row-block pass schedule: rows per workgroup 16 tm, columns 16 tj, and
+// the reduction split into at most 4 `ranges` of klen elements so that the
+// grid has about one workgroup per CU (each range at least 8 chunks of 32).
+struct SkSched {
+  int tm, tj, ranges;
+  int64_t klen;
+};
+#ifndef SK_TARGET_WG
+#define SK_TARGET_WG 256
+#endif
+#ifndef SK_MAX_RANGES
+#define SK_MAX_RANGES 4
+#endif
+SkSched sk_sched(int64_t M, int64_t R, int r, int64_t E) {
+  SkSched f{};
+  f.tj = r <= 16 ? 1 : r <= 32 ? 2 : r <= 64 ? 4 : 8;
+  f.tm = f.tj <= 2 ? 4 : f.tj == 4 ? 2 : 1;
+  const int64_t blocks = (ceil_div(std::max<int64_t>(M, 1), 16 * f.tm) + (E > 1 ? E : 0)) * ceil_div(r, 16 * f.tj);
+  const int64_t chunks = std::max<int64_t>(1, ceil_div(R, 32));
+  int64_t want = ceil_div(SK_TARGET_WG, blocks);
+  want = std::max<int64_t>(1, std::min<int64_t>({want, chunks / 8, SK_MAX_RANGES}));
+  f.klen = ceil_div(chunks, want) * 32;
+  f.ranges = (int)ceil_div(chunks * 32, f.klen);
+  return f;
+}
+
+size_t sk_part_bytes_for(int64_t M, int64_t R, int r, int64_t E) {
+  const SkSched f = sk_sched(M, R, r, E);
+  return f.ranges > 1 ? align256((size_t)f.ranges * M * r * 4) : 0;
+}
+
 lora4_status rows_skinny(int transb, const uint16_t *act, int64_t ld_act, const uint16_t *w, int64_t ld_w,
                          int64_t g_w, int64_t R, int64_t M, int r, const int64_t *offs, int64_t E, uint16_t *o1,
-                         float a1, uint16_t *o2, float a2, hipStream_t st) {
+                         float a1, uint16_t *o2, float a2, float *part, hipStream_t st) {
+  const SkSched f = sk_sched(M, R, r, E);
   skinny::Params p{};
   p.act = act;
   p.ld_act = ld_act;
@@ -599,34 +640,35 @@ lora4_status rows_skinny(int transb, const uint16_t *act, int64_t ld_act, const 
   p.alpha1 = a1;
   p.out2 = o2;
   p.alpha2 = a2;
-  const int tj = r <= 16 ? 1 : r <= 32 ? 2 : r <= 64 ? 4 : 8;
-  const int tm = (tj <= 4 && M / 16 > 4096) ? 2 : 1;
-  const int64_t slots = ceil_div(std::max<int64_t>(M, 1), 16 * tm) + (E > 1 ? E : 0);
-  dim3 grid((unsigned)slots, (unsigned)ceil_div(r, 16 * tj), 1);
-  if (tm == 2) {
-    switch (tj) {
-      case 1: return run_rows_tj<2, 1>(transb, p, grid, st);
-      case 2: return run_rows_tj<2, 2>(transb, p, grid, st);
-      default: return run_rows_tj<2, 4>(transb, p, grid, st);
-    }
+  p.klen = f.klen;
+  p.part = part;
+  const int64_t slots = ceil_div(std::max<int64_t>(M, 1), 16 * f.tm) + (E > 1 ? E : 0);
+  dim3 grid((unsigned)slots, (unsigned)ceil_div(r, 16 * f.tj), (unsigned)f.ranges);
+  lora4_status st1 = LORA4_ERR_UNIMPLEMENTED;
+  switch (f.tj) {
+    case 1: st1 = run_rows_tj<4, 1>(transb, p, grid, st); break;
+    case 2: st1 = run_rows_tj<4, 2>(transb, p, grid, st); break;
+    case 4: st1 = run_rows_tj<2, 4>(transb, p, grid, st); break;
+    default: st1 = run_rows_tj<1, 8>(transb, p, grid, st); break;
   }
-  switch (tj) {
-    case 1: return run_rows_tj<1, 1>(transb, p, grid, st);
-    case 2: return run_rows_tj<1, 2>(transb, p, grid, st);
-    case 4: return run_rows_tj<1, 4>(transb, p, grid, st);
-    default: return run_rows_tj<1, 8>(transb, p, grid, st);
+  TRY(st1);
+  if (f.ranges > 1) {
+    const int64_t n = M * r;
+    TRY(reduce_bf16(transb ? "reduce_dz" : "reduce_z", part, f.ranges, n, n, o1, a1, o2, a2, st));
   }
+  return LORA4_OK;
 }
 
-// Z = X A^T (per group), written as bf16 to z1 (scale a1) and z2 (scale a2).
 lora4_status z_pass(const Plan &pl, const lora4_W *W, const uint16_t *X, const uint16_t *A,
-                    const int64_t *offs, uint16_t *z1, float a1, uint16_t *z2, float a2, hipStream_t st) {
+                    const int64_t *offs, uint16_t *z1, float a1, uint16_t *z2, float a2, float *part,
+                    hipStream_t st) {
   if (!z1) {   // one output only
     z1 = z2;
     a1 = a2;
     z2 = nullptr;
   }
-  return rows_skinny(0, X, pl.K, A, pl.K, (int64_t)pl.r * pl.K, pl.K, pl.M, pl.r, offs, pl.E, z1, a1, z2, a2, st);
+  return rows_skinny(0, X, pl.K, A, pl.K, (int64_t)pl.r * pl.K, pl.K, pl.M, pl.r, offs, pl.E, z1, a1, z2, a2, part,
+                     st);
 }
 
 lora4_status check_common(const lora4_W *W, int64_t M, int32_t r, float s, const int64_t *offs) {
@@ -686,7 +728,7 @@ lora4_status lora4_forward(const lora4_W *W, const uint16_t *X, int64_t M, const
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
   uint16_t *sZ = ws_at<uint16_t>(workspace, pl.off_sz);
-  TRY(z_pass(pl, W, X, A, group_offsets, Z, 1.0f, sZ, s, st));
+  TRY(z_pass(pl, W, X, A, group_offsets, Z, 1.0f, sZ, s, ws_at<float>(workspace, pl.off_skpart), st));
 
   NtParams p{};
   p.A = mat(X, pl.K);
@@ -748,12 +790,13 @@ lora4_status lora4_backward(const lora4_W *W, const uint16_t *X, const uint16_t 
   const uint16_t *Zu = Z;
   if (!Zu) {
     uint16_t *Zw = ws_at<uint16_t>(workspace, pl.off_zw);
-    TRY(z_pass(pl, W, X, A, group_offsets, Zw, 1.0f, nullptr, 0.0f, st));
+    TRY(z_pass(pl, W, X, A, group_offsets, Zw, 1.0f, nullptr, 0.0f, ws_at<float>(workspace, pl.off_skpart), st));
     Zu = Zw;
   }
 
   // dZ = s dY B  (row blocks, reduction over N)
-  TRY(rows_skinny(1, dY, pl.N, B, r, pl.N * r, pl.N, M, r, group_offsets, pl.E, dZ, s, nullptr, 0.0f, st));
+  TRY(rows_skinny(1, dY, pl.N, B, r, pl.N * r, pl.N, M, r, group_offsets, pl.E, dZ, s, nullptr, 0.0f,
+                  ws_at<float>(workspace, pl.off_skpart), st));
 
   // dX = dY deq(W) + dZ A
   {

@@ -4,13 +4,17 @@
 //   dZ = dY . B       out[M, r] = sum_n dY[m, n] B[n, j]      (B  [N, r], r-contiguous)
 //
 // These are HBM-bound (about r flops per byte of activations). A workgroup owns
-// BM = 16 TM whole rows of the activations and all r output columns, so no
-// split partials or reduction launches are needed: the four waves take one
-// quarter of the reduction each (contiguous, for DRAM locality), accumulate
-// with v_mfma_f32_16x16x32_bf16, and add their partial tiles through LDS at
-// the end. Operands are loaded straight into MFMA layout (16 bytes per lane);
-// the r-contiguous B is staged per wave in LDS and read back transposed with
-// ds_read_b64_tr_b16. Outputs: out1 = bf16(alpha1 acc), out2 = bf16(alpha2 acc).
+// BM = 16 TM rows of the activations and all r output columns over one range
+// of the reduction (blockIdx.z selects the range): the four waves take one
+// quarter of the range each (contiguous, for DRAM locality), accumulate with
+// v_mfma_f32_16x16x32_bf16, and add their partial tiles through LDS at the
+// end. Splitting the reduction gives the grid enough workgroups to keep HBM
+// busy with BM large enough that the small operand (A or B, re-read once per
+// row block) stays a minor share of the traffic. Operands are loaded straight
+// into MFMA layout (16 bytes per lane); the r-contiguous B is staged per wave
+// in LDS and read back transposed with ds_read_b64_tr_b16. Outputs: with one
+// range, out1 = bf16(alpha1 acc), out2 = bf16(alpha2 acc); with several, fp32
+// partials part[range][row][col], summed by the deterministic reduction.
 #pragma once
 
 #include "common.hpp"
@@ -32,6 +36,8 @@ struct Params {
   float alpha1;
   uint16_t *out2;        // [M, r] or nullptr
   float alpha2;
+  int64_t klen;          // reduction elements per range (multiple of 32)
+  float *part;           // [ranges][M][r] fp32 when gridDim.z > 1
 };
 
 constexpr int THREADS = 256;
@@ -71,11 +77,13 @@ __global__ __launch_bounds__(THREADS) void k_rows_skinny(Params p) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const uint16_t *w = p.w + g * p.g_w;
 
-  // this wave's quarter of the reduction, in 32-wide chunks
+  // this wave's quarter of the workgroup's range, in 32-wide chunks
   const int64_t chunks = (p.R + 31) / 32;
-  const int64_t per = (chunks + 3) / 4;
-  const int64_t c_begin = wave * per;
-  const int64_t c_end = c_begin + per < chunks ? c_begin + per : chunks;
+  const int64_t r_begin = (int64_t)blockIdx.z * (p.klen / 32);
+  const int64_t r_end = r_begin + p.klen / 32 < chunks ? r_begin + p.klen / 32 : chunks;
+  const int64_t per = (r_end - r_begin + 3) / 4;
+  const int64_t c_begin = r_begin + wave * per;
+  const int64_t c_end = c_begin + per < r_end ? c_begin + per : r_end;
 
   const bool act_vec = (p.ld_act % 8) == 0;
   const bool w_vec = (p.ld_w % 8) == 0;
@@ -181,6 +189,10 @@ __global__ __launch_bounds__(THREADS) void k_rows_skinny(Params p) {
     // 16x16 result layout: lane ln holds row 4 (ln / 16) + e, column ln % 16
     const int64_t row = row0 + i * 16 + (ln >> 4) * 4 + e;
     const int col = j0 + j * 16 + (ln & 15);
+    if (gridDim.z > 1) {
+      if (row < row_end && col < p.r) p.part[((int64_t)blockIdx.z * p.M + row) * p.r + col] = v;
+      continue;
+    }
     if (row < row_end && col < p.r) {
       p.out1[row * p.r + col] = to_bf16(v * p.alpha1);
       if (p.out2) p.out2[row * p.r + col] = to_bf16(v * p.alpha2);
