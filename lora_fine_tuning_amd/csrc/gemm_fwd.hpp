@@ -14,6 +14,10 @@
 // over a step are 32 consecutive elements of one row. X is read from LDS in
 // the same order, so every product pairs the same k on both sides.
 //
+// Outputs with too few tiles to fill the GPU, and the tiles of an
+// under-filled last round, split their reduction over several blocks (fp32
+// partials per tile, summed by k_reduce_tiles in a fixed order).
+//
 // X streams HBM/L2 -> LDS (swizzled so the operand reads are free of bank
 // conflicts) with bounds-checked direct loads into a ring of
 // five buffers of 256 x 64 (the X of step s+3 and the W of step s+2 are
@@ -64,18 +68,24 @@ template <int FMT>
 __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
+  // Blocks below whole_tiles take one tile each (XCD-aware order: blocks are
+  // dealt round-robin to the 8 XCDs, so renumber them for each XCD to walk a
+  // contiguous range of tiles); the blocks after them (dispatched last) take
+  // one reduction range of one split tile each.
   int b = blockIdx.x;
-  {
-    const int per = p.nblocks >> 3;
+  int tile, split = 0;
+  const int whole = p.whole_tiles;
+  if (b < whole) {
+    const int per = whole >> 3;
     if (b < per * 8) b = (b & 7) * per + (b >> 3);
+    tile = b;
+  } else {
+    tile = whole + (b - whole) / p.ksplit;
+    split = (b - whole) % p.ksplit;
   }
-  // split-major order: the blocks of one split are consecutive (and share
-  // the K range of X and W)
-  const int ntiles = p.nblocks / p.ksplit;
-  const int split = b / ntiles;
-  b -= split * ntiles;
-  const int tn = b % p.tiles_n;
-  const int slot = b / p.tiles_n;
+  const bool is_split = tile >= whole;
+  const int tn = tile % p.tiles_n;
+  const int slot = tile / p.tiles_n;
   const RowTile rt = map_row_tile(slot, BM, p.offsets, p.groups, p.M);
   if (rt.group < 0) return;
   const int g = rt.group;
@@ -98,7 +108,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   const uint32_t a_cstep = (uint32_t)(32 * p.A.ld * 2);
   // X of step s into stage As, chunks 2 part .. 2 part + 1 (part 0..3)
   // steps are numbered within this block's range, which starts at step sb
-  const int sb = split * p.split_steps;
+  const int sb = is_split ? split * p.split_steps : 0;
   auto issue_a = [&](int s, uint16_t *As, int part) {
     const int64_t k0 = (int64_t)(s + sb) * BKS;
     const bool edge = k0 + a_kq >= p.R;
@@ -252,7 +262,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   };
 
   const int all_steps = (int)((p.R + BKS - 1) / BKS);
-  const int steps = min(all_steps - sb, p.split_steps);
+  const int steps = is_split ? min(all_steps - sb, p.split_steps) : all_steps;
   WRaw r0, r1;
   WFrag f0, f1;
   u32x4_t x[8];
@@ -344,23 +354,20 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
 
   // ---- epilogue: register e of acc[i][j] holds
   // Y[32 i + lane % 32][64 wave + 32 j + 8 (e / 4) + 4 (lane / 32) + e % 4]
-  if (p.ksplit > 1) {
-    // fp32 partial of this split: Cpart[split][row][col], row stride Nc
-    // (a multiple of 4 whenever the reduction is split)
-    float *pbase = p.Cpart + (int64_t)split * p.M * p.Nc;
+  if (is_split) {
+    // fp32 partial of this range, tile-local [256][256] (rows and columns past
+    // the output are written too and ignored by the reduction)
+    float *pt = p.Cpart + ((int64_t)(tile - whole) * p.ksplit + split) * (BM * BN);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int64_t row = row0 + i * 32 + l32;
-      if (row >= row_end) continue;
-      float *prow = pbase + row * p.Nc;
+      float *prow = pt + (i * 32 + l32) * BN;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const int64_t col = col0 + wave * 64 + j * 32 + r4 * 8 + h * 4;
-          if (col < p.Nc)
-            *reinterpret_cast<f32x4_t *>(prow + col) =
-                f32x4_t{acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
+          const int col = wave * 64 + j * 32 + r4 * 8 + h * 4;
+          *reinterpret_cast<f32x4_t *>(prow + col) =
+              f32x4_t{acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
         }
       }
     }
@@ -390,6 +397,36 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
         }
       }
     }
+  }
+}
+
+// C[tile rows][tile columns] = bf16(sum_k part[t][k][r][c]) for the split
+// tiles t = 0 .. (tile - whole_tiles); four columns per thread, splits
+// summed in order.
+__global__ void k_reduce_tiles(Params p, int split_tiles) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_tile = (int64_t)BM * (BN / 4);
+  if (idx >= (int64_t)split_tiles * per_tile) return;
+  const int t = (int)(idx / per_tile);
+  const int rem = (int)(idx - (int64_t)t * per_tile);
+  const int r = rem / (BN / 4), c = (rem % (BN / 4)) * 4;
+  const int tile = p.whole_tiles + t;
+  const int tn = tile % p.tiles_n, slot = tile / p.tiles_n;
+  const RowTile rt = map_row_tile(slot, BM, p.offsets, p.groups, p.M);
+  if (rt.group < 0) return;
+  const int64_t row = rt.row0 + r;
+  const int64_t col = (int64_t)tn * BN + c;
+  if (row >= rt.row_end || col >= p.Nc) return;
+  const float *src = p.Cpart + (int64_t)t * p.ksplit * (BM * BN) + r * BN + c;
+  f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < p.ksplit; ++k) s += *reinterpret_cast<const f32x4_t *>(src + (int64_t)k * (BM * BN));
+  uint16_t *dst = p.C + row * p.ldc + col;
+  if (col + 4 <= p.Nc && (p.ldc % 4) == 0) {
+    *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (col + e < p.Nc) dst[e] = to_bf16(s[e]);
   }
 }
 

@@ -268,7 +268,9 @@ int skinny_tile(int r) { return r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : 128
 // Forward base GEMM schedule (defined with the large-tile dispatch below).
 struct FwdSched {
   bool use;          // register-direct kernel (else the 128 x 128 kernel)
-  int ksplit;        // reduction splits
+  int whole_tiles;   // tiles computed by one block each (the first ones)
+  int split_tiles;   // tiles after them, each split over ksplit blocks
+  int ksplit;        // reduction splits of a split tile
   int split_steps;   // 64-deep steps per split
 };
 FwdSched fwd_sched(int64_t M, int64_t N, int64_t K, int64_t E, const PackedW &W);
@@ -284,8 +286,7 @@ struct Plan {
   int64_t row_slots;  // row-tile slots for BM = 128
   int tq_a, tq_b;     // TN Q tiles (dA over K, dB over N)
   int msplit_a, msplit_b;
-  int fsplit, fsplit_steps;   // forward base GEMM: reduction splits (1: none)
-  bool fregs;                 // forward base GEMM on the register-direct kernel
+  FwdSched fs;                // forward base GEMM schedule
   // workspace offsets
   size_t off_sz, off_zw, off_dz, off_part, off_part_b, off_party, off_skpart, bytes;
 };
@@ -315,10 +316,7 @@ Plan make_plan(int which, const lora4_W *W, int64_t M, int r) {
   };
   p.msplit_a = msplit(p.tq_a);
   p.msplit_b = msplit(p.tq_b);
-  const FwdSched fs = fwd_sched(M, p.N, p.K, p.E, packed_of(W));
-  p.fregs = fs.use;
-  p.fsplit = fs.ksplit;
-  p.fsplit_steps = fs.split_steps;
+  p.fs = fwd_sched(M, p.N, p.K, p.E, packed_of(W));
 
   const size_t mr2 = align256((size_t)M * r * 2);
   size_t off = 0;
@@ -334,7 +332,8 @@ Plan make_plan(int which, const lora4_W *W, int64_t M, int r) {
     off += b;
   }
   p.off_party = off;  // forward: fp32 partials of the split base GEMM
-  if (which == 0 && p.fsplit > 1) off += align256((size_t)p.fsplit * M * p.N * 4);
+  if (which == 0 && p.fs.use && p.fs.split_tiles > 0)
+    off += align256((size_t)p.fs.split_tiles * p.fs.ksplit * fwd::BM * fwd::BN * 4);
   p.off_part = off;  // backward: dA partials, then dB^T partials
   if (which == 1) {
     p.off_part_b = off + align256((size_t)p.msplit_a * p.E * r * p.K * 4);
@@ -376,28 +375,52 @@ bool big_fits(int64_t ld_a, int64_t M, const PackedW &W) {
          W.g_scales2 * 4 < lim;
 }
 
-// The register-direct forward kernel runs one 256 x 256 tile per CU; with
-// fewer tiles than that the reduction is split (each split writes fp32
-// partials, rows of N % 4 == 0 floats, at least 8 steps per split, partials
-// capped at 256 MiB) and a
-// deterministic reduction adds them. The automatic policy keeps the 128 x 128
-// kernel when even the split grid would leave most of the GPU idle.
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// The register-direct forward kernel runs one 256 x 256 tile per CU at a
+// time. Outputs with fewer tiles than ~3/4 of the CUs split the reduction of
+// every tile over several blocks (fp32 partials, at least 8 steps per split,
+// partials capped at 256 MiB), summed by a deterministic reduction. (Splitting
+// only the tiles of a half-empty last round, e.g. 896 tiles on 256 CUs, was
+// measured: the GEMM gains what the extra reduction launch costs.) The
+// automatic policy keeps the 128 x 128 kernel when even a split grid would
+// leave most of the GPU idle.
 FwdSched fwd_sched(int64_t M, int64_t N, int64_t K, int64_t E, const PackedW &W) {
-  FwdSched f{false, 1, 1 << 30};
+  FwdSched f{false, 0, 0, 1, 1 << 30};
   if (K <= 0 || M <= 0 || !big_fits(K, M, W)) return f;
   const int pol = big_policy();
   if (pol == 0) return f;
+  const int64_t cus = cu_count();
   const int64_t tiles = (ceil_div(M, fwd::BM) + (E > 1 ? E : 0)) * ceil_div(N, fwd::BN);
   const int64_t steps = ceil_div(K, fwd::BKS);
-  int64_t ks = 1;
-  if (tiles < 192 && N % 4 == 0) {
-    ks = std::min<int64_t>({256 / tiles, std::max<int64_t>(1, steps / 8), 16});
-    const int64_t cap = ((int64_t)256 << 20) / std::max<int64_t>(1, M * N * 4);
+  const int64_t max_ks = std::min<int64_t>(16, std::max<int64_t>(1, steps / 8));
+  int64_t whole = tiles, split = 0, ks = 1;
+  if (tiles < cus * 3 / 4) {
+    ks = std::min<int64_t>(cus / tiles, max_ks);
+    const int64_t cap = ((int64_t)256 << 20) / ((int64_t)fwd::BM * fwd::BN * 4 * tiles);
     ks = std::max<int64_t>(1, std::min(ks, cap));
+    if (ks > 1) {
+      whole = 0;
+      split = tiles;
+    }
   }
-  if (pol < 0 && tiles * ks < 192) return f;
+  if (pol < 0 && whole + split * ks < cus * 3 / 4) return f;
   f.use = true;
-  if (ks > 1) {
+  f.whole_tiles = (int)whole;
+  f.split_tiles = (int)split;
+  f.ksplit = (int)ks;
+  if (split > 0) {
     f.split_steps = (int)ceil_div(steps, ks);
     f.ksplit = (int)ceil_div(steps, f.split_steps);
   }
@@ -489,6 +512,7 @@ big::Params big_params(const Mat &A, const PackedW &W, int64_t R, const Mat &A2,
   p.tiles_n = (int)ceil_div(Nc, big::BN);
   p.nblocks = (int)((ceil_div(std::max<int64_t>(M, 1), big::BM) + (E > 1 ? E : 0)) * p.tiles_n);
   p.tab = nf4_table();
+  p.whole_tiles = p.nblocks;
   p.ksplit = 1;
   p.split_steps = 1 << 30;
   p.Cpart = nullptr;
@@ -499,17 +523,19 @@ big::Params big_params(const Mat &A, const PackedW &W, int64_t R, const Mat &A2,
 // (split partials in `party`, then reduced into the output), else the
 // 128 x 128 kernel.
 lora4_status run_nt_main_fmt(int fmt, const NtParams &p, dim3 grid, const Plan &pl, float *party, hipStream_t st) {
-  if (p.R > 0 && use_fwd_regs() && pl.fregs) {
+  if (p.R > 0 && use_fwd_regs() && pl.fs.use) {
     big::Params q = big_params(p.A, p.W, p.R, p.A2, p.B2, p.r2, p.M, p.Nc, p.offsets, p.groups, p.out.C,
                                p.out.ldc);
-    q.ksplit = pl.fsplit;
-    q.split_steps = pl.fsplit_steps;
-    q.nblocks *= pl.fsplit;
+    q.whole_tiles = pl.fs.whole_tiles;
+    q.ksplit = pl.fs.ksplit;
+    q.split_steps = pl.fs.split_steps;
+    q.nblocks = pl.fs.whole_tiles + pl.fs.split_tiles * pl.fs.ksplit;
     q.Cpart = party;
     TRY(run_fwd_fmt(fmt, q, st));
-    if (pl.fsplit > 1) {
-      const int64_t n = p.M * p.Nc;
-      TRY(reduce_bf16("reduce_y", party, pl.fsplit, n, n, p.out.C, 1.0f, nullptr, 0.0f, st));
+    if (pl.fs.split_tiles > 0) {
+      const int64_t n = (int64_t)pl.fs.split_tiles * fwd::BM * (fwd::BN / 4);
+      TRY(launch_args("reduce_y", fwd::k_reduce_tiles, dim3((unsigned)ceil_div(n, 256)), dim3(256), st, q,
+                      pl.fs.split_tiles));
     }
     return LORA4_OK;
   }

@@ -194,7 +194,7 @@ def test_large_tile_shape_selected_automatically(monkeypatch):
 @pytest.mark.parametrize("fmt", [synth.NF4, synth.NF4_DQ, synth.MXFP4])
 @pytest.mark.parametrize("M,K,N,r", [(512, 4096, 256, 16),     # 2 tiles: 8-way split of 64 steps
                                      (700, 2048, 1000, 16),    # ragged rows, 12 tiles: 4-way split
-                                     (300, 2048, 258, 8)])     # N % 4 != 0: no split
+                                     (300, 2048, 258, 8)])     # N % 4 != 0, ragged last columns
 def test_forward_split_reduction(fmt, M, K, N, r, monkeypatch):
     """Forced onto the register-direct forward kernel, few-tile outputs split
     the reduction (fp32 partials + reduction); the rank-r tail is added once."""
@@ -219,3 +219,26 @@ def test_forward_split_grouped(monkeypatch):
     Ws = [dequant_rows(t["W"][e], np.arange(N), synth.NF4) for e in range(E)]
     fo = lora.grouped_forward(f64(t["X"]), Ws, [f64(a) for a in t["A"]], [f64(b) for b in t["B"]], lay.s, offs)
     assert rel(got["Y"], fo["Y"]) <= TOL
+
+
+def test_forward_two_rounds_of_tiles(monkeypatch):
+    """320 output tiles (more than one per CU): the XCD-aware block order over
+    a partial second round. Checked on sampled columns of the first 96 column
+    tiles and of the last 64 of the second row tile, all rows."""
+    monkeypatch.setenv("LORA4_BIG", "1")
+    M, K, N, r = 512, 1024, 160 * 256, 16
+    lay = synth.small_layer(M, K, N, r, fmt=synth.NF4, index=7)
+    print_case("two rounds", M, K, N, r)
+    t = synth.inputs(lay)
+    base = pack_gpu(t["W"], lay.fmt)
+    X, A, B = (to_dev(t[k]) for k in ("X", "A", "B"))
+    fw = L.forward(base, X, A, B, lay.s)
+    torch.cuda.synchronize()
+    Y = to_host(fw["Y"])
+    rng = np.random.default_rng(5)
+    cols = np.sort(np.concatenate([rng.choice(96 * 256, 48, replace=False),            # whole tiles only
+                                   96 * 256 + rng.choice(64 * 256, 48, replace=False)]))
+    Wn = dequant_rows(t["W"], cols, lay.fmt)
+    Xf, Af, Bf = f64(t["X"]), f64(t["A"]), f64(t["B"])
+    ref = Xf @ Wn.T + lay.s * ((Xf @ Af.T) @ Bf[cols].T)
+    assert rel(Y[:, cols], ref) <= TOL
