@@ -69,11 +69,10 @@ struct Params {
   int tiles_n;        // ceil(Nc / 256)
   int nblocks;        // gridDim.x
   Nf4Table tab;
-  // split reduction (forward kernel only): tiles below whole_tiles run in one
-  // block each; every later tile runs in ksplit blocks of split_steps 64-deep
-  // steps, which write fp32 partials Cpart[tile - whole_tiles][split][256][256]
-  // instead of C (the rank-r tail goes into split 0)
-  int whole_tiles;
+  // split reduction (forward kernel only): every tile runs in ksplit blocks
+  // of split_steps 64-deep steps, which write fp32 partials
+  // Cpart[tile][split][256][256] instead of C (the rank-r tail goes into
+  // split 0)
   int ksplit;
   int split_steps;
   float *Cpart;

@@ -268,37 +268,51 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
   if (s < steps) body(s, As0, Bs0, As1, Bs1, r1, r0);
   // every look-ahead load has landed (the barrier waits for them)
 
-  // ---- rank-r tail: dZ A, plain bf16 steps through registers ----------------
+  // ---- rank-r tail: dZ A, plain bf16 steps through LDS -----------------------
   if (p.r2 > 0) {
     const uint16_t *B2 = p.B2.p + g * p.B2.gstride;
+    const bool a_vec = (p.A2.ld % 8) == 0;
+    const bool b_vec = (p.B2.ld % 8) == 0;
     for (int k0 = 0; k0 < p.r2; k0 += BKS) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const int idx = t + THREADS * c;
         const int row = idx >> 3, chunk = idx & 7;
-        uint32_t w4[4] = {0u, 0u, 0u, 0u};
+        u32x4_t v = {0u, 0u, 0u, 0u};
         const int64_t gr = row0 + row;
         const int64_t gk = k0 + chunk * 8;
-        if (gr < row_end) {
+        if (gr < row_end && gk < p.r2) {
           const uint16_t *src = p.A2.p + gr * p.A2.ld + gk;
-          for (int j = 0; j < 8; ++j)
-            if (gk + j < p.r2) w4[j >> 1] |= (uint32_t)src[j] << (16 * (j & 1));
+          if (a_vec && gk + 8 <= p.r2) {
+            v = *reinterpret_cast<const u32x4_t *>(src);
+          } else {
+            uint32_t w4[4] = {0u, 0u, 0u, 0u};
+            for (int e = 0; e < 8; ++e)
+              if (gk + e < p.r2) w4[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+            v = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
+          }
         }
-        lds_write_b128(As0 + swz(row, chunk), u32x4_t{w4[0], w4[1], w4[2], w4[3]});
+        lds_write_b128(As0 + swz(row, chunk), v);
       }
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const int idx = t + THREADS * c;
         const int row = idx >> 5, cc = (idx & 31) * 8;
-        uint32_t w4[4] = {0u, 0u, 0u, 0u};
+        u32x4_t v = {0u, 0u, 0u, 0u};
         const int64_t gr = k0 + row;
         const int64_t gc = col0 + cc;
-        if (gr < p.r2) {
+        if (gr < p.r2 && gc < p.Nc) {
           const uint16_t *src = B2 + gr * p.B2.ld + gc;
-          for (int j = 0; j < 8; ++j)
-            if (gc + j < p.Nc) w4[j >> 1] |= (uint32_t)src[j] << (16 * (j & 1));
+          if (b_vec && gc + 8 <= p.Nc) {
+            v = *reinterpret_cast<const u32x4_t *>(src);
+          } else {
+            uint32_t w4[4] = {0u, 0u, 0u, 0u};
+            for (int e = 0; e < 8; ++e)
+              if (gc + e < p.Nc) w4[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+            v = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
+          }
         }
-        lds_write_b128(Bs0 + wt_off(row, cc), u32x4_t{w4[0], w4[1], w4[2], w4[3]});
+        lds_write_b128(Bs0 + wt_off(row, cc), v);
       }
       __syncthreads();
       compute_step(As0, Bs0, [](int) {});
@@ -307,28 +321,38 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
   }
 
   // ---- epilogue: register e of acc[j][i] holds
-  // dX[wm0 + 32 i + lane % 32][wn0 + 32 j + 8 (e / 4) + 4 (lane / 32) + e % 4]
-  const bool vec_out = (p.ldc % 4) == 0;
+  // dX[wm0 + 32 i + lane % 32][wn0 + 32 j + 8 (e / 4) + 4 (lane / 32) + e % 4].
+  // Each wave stages its 128 x 128 bf16 block in LDS (free now; 32 KB per
+  // wave, 256-byte rows, chunk c of row r at c ^ (r % 16)) and writes it back
+  // as 4 whole 256-byte row segments per store instruction (element stores
+  // where a segment is cut by the output's edge or rows are not 16-byte
+  // aligned).
+  {
+    uint16_t *stg = smem + wave * (128 * 128);
+    auto st_off = [](int row, int chunk) { return row * 128 + ((chunk ^ (row & 15)) << 3); };
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t row = row0 + wm0 + i * 32 + l32;
-    if (row >= row_end) continue;
-    uint16_t *crow = p.C + row * p.ldc;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int64_t col = col0 + wn0 + j * 32 + r4 * 8 + h * 4;
-        const float v0 = acc[j][i][4 * r4], v1 = acc[j][i][4 * r4 + 1];
-        const float v2 = acc[j][i][4 * r4 + 2], v3 = acc[j][i][4 * r4 + 3];
-        if (vec_out && col + 4 <= p.Nc) {
-          const u32x2_t pk = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-          *reinterpret_cast<u32x2_t *>(crow + col) = pk;
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const u32x2_t pk = {pack_bf16x2(acc[j][i][4 * r4], acc[j][i][4 * r4 + 1]),
+                              pack_bf16x2(acc[j][i][4 * r4 + 2], acc[j][i][4 * r4 + 3])};
+          *reinterpret_cast<u32x2_t *>(stg + st_off(i * 32 + l32, 4 * j + r4) + 4 * h) = pk;
+        }
+    const bool vec16 = (p.ldc % 8) == 0;
+#pragma unroll 4
+    for (int q = 0; q < 32; ++q) {
+      const int row = q * 4 + (lane >> 4), chunk = lane & 15;
+      const u32x4_t v = lds_read_b128(stg + st_off(row, chunk));
+      const int64_t grow = row0 + wm0 + row;
+      const int64_t gcol = col0 + wn0 + chunk * 8;
+      if (grow < row_end && gcol < p.Nc) {
+        uint16_t *dst = p.C + grow * p.ldc + gcol;
+        if (vec16 && gcol + 8 <= p.Nc) {
+          *reinterpret_cast<u32x4_t *>(dst) = v;
         } else {
-          const float v[4] = {v0, v1, v2, v3};
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (col + e < p.Nc) crow[col + e] = to_bf16(v[e]);
+          for (int e = 0; e < 8 && gcol + e < p.Nc; ++e) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
         }
       }
     }

@@ -64,26 +64,26 @@ struct WRaw {
   uint32_t c2[2];   // DQ second level (fp32 bits)
 };
 
-template <int FMT>
+// SPLIT: every block computes one reduction range of a split tile and writes
+// fp32 partials (else one block per tile, bf16 output).
+template <int FMT, bool SPLIT>
 __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
-  // Blocks below whole_tiles take one tile each (XCD-aware order: blocks are
-  // dealt round-robin to the 8 XCDs, so renumber them for each XCD to walk a
-  // contiguous range of tiles); the blocks after them (dispatched last) take
-  // one reduction range of one split tile each.
+  // Whole tiles: XCD-aware order (blocks are dealt round-robin to the 8 XCDs;
+  // renumber them so each XCD walks a contiguous range of tiles). Split
+  // tiles: block b takes range b % ksplit of tile b / ksplit.
   int b = blockIdx.x;
   int tile, split = 0;
-  const int whole = p.whole_tiles;
-  if (b < whole) {
-    const int per = whole >> 3;
+  if constexpr (!SPLIT) {
+    const int per = p.nblocks >> 3;
     if (b < per * 8) b = (b & 7) * per + (b >> 3);
     tile = b;
   } else {
-    tile = whole + (b - whole) / p.ksplit;
-    split = (b - whole) % p.ksplit;
+    tile = b / p.ksplit;
+    split = b % p.ksplit;
   }
-  const bool is_split = tile >= whole;
+  constexpr bool is_split = SPLIT;
   const int tn = tile % p.tiles_n;
   const int slot = tile / p.tiles_n;
   const RowTile rt = map_row_tile(slot, BM, p.offsets, p.groups, p.M);
@@ -299,24 +299,35 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   __syncthreads();
 
   // ---- rank-r tail: (s Z) B^T; Z rows through LDS, B rows to registers -----
+  // (B loads of sub-steps whose reduction slots all lie past r2 are skipped:
+  // in sub-step kk lane half h holds k0 + 32 h + 8 kk ..; the MFMAs of such
+  // sub-steps still run, on zeros: branching around them costs more.)
   if (p.r2 > 0 && split == 0) {
     const uint16_t *B2 = p.B2.p + g * p.B2.gstride;
     uint16_t *As = smem;
+    const bool a_vec = (p.A2.ld % 8) == 0;
     const bool b_vec = (p.B2.ld % 8) == 0;
     for (int k0 = 0; k0 < p.r2; k0 += BKS) {
+      const int nkk = min(4, (p.r2 - k0 + 7) / 8);
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const int idx = t + THREADS * c;
         const int row = idx >> 3, chunk = idx & 7;
-        uint32_t w4[4] = {0u, 0u, 0u, 0u};
+        u32x4_t v = {0u, 0u, 0u, 0u};
         const int64_t gr = row0 + row;
         const int64_t gk = k0 + chunk * 8;
-        if (gr < row_end) {
+        if (gr < row_end && gk < p.r2) {
           const uint16_t *src = p.A2.p + gr * p.A2.ld + gk;
-          for (int e = 0; e < 8; ++e)
-            if (gk + e < p.r2) w4[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+          if (a_vec && gk + 8 <= p.r2) {
+            v = *reinterpret_cast<const u32x4_t *>(src);
+          } else {
+            uint32_t w4[4] = {0u, 0u, 0u, 0u};
+            for (int e = 0; e < 8; ++e)
+              if (gk + e < p.r2) w4[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+            v = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
+          }
         }
-        lds_write_b128(As + swz(row, chunk), u32x4_t{w4[0], w4[1], w4[2], w4[3]});
+        lds_write_b128(As + swz(row, chunk), v);
       }
       WFrag bt;
 #pragma unroll
@@ -326,7 +337,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
         for (int kk = 0; kk < 4; ++kk) {
           const int64_t k = k0 + 32 * h + 8 * kk;
           uint32_t w4[4] = {0u, 0u, 0u, 0u};
-          if (n < p.Nc && k < p.r2) {
+          if (kk < nkk && n < p.Nc && k < p.r2) {
             const uint16_t *src = B2 + n * p.B2.ld + k;
             if (b_vec && k + 8 <= p.r2) {
               const u32x4_t v = *reinterpret_cast<const u32x4_t *>(src);
@@ -354,10 +365,10 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
 
   // ---- epilogue: register e of acc[i][j] holds
   // Y[32 i + lane % 32][64 wave + 32 j + 8 (e / 4) + 4 (lane / 32) + e % 4]
-  if (is_split) {
+  if constexpr (SPLIT) {
     // fp32 partial of this range, tile-local [256][256] (rows and columns past
     // the output are written too and ignored by the reduction)
-    float *pt = p.Cpart + ((int64_t)(tile - whole) * p.ksplit + split) * (BM * BN);
+    float *pt = p.Cpart + ((int64_t)tile * p.ksplit + split) * (BM * BN);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float *prow = pt + (i * 32 + l32) * BN;
@@ -373,27 +384,35 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
     }
     return;
   }
-  const bool vec_out = (p.ldc % 4) == 0;
+  // Each wave stages its 256 x 64 bf16 block in LDS (free now; 32 KB per wave,
+  // tile64 layout) and writes it back as 8 whole 128-byte row segments per
+  // store instruction (element stores where a row segment is cut by the
+  // output's edge or the rows are not 16-byte aligned).
+  {
+    uint16_t *stg = smem + wave * (BM * 64);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t row = row0 + i * 32 + l32;
-    if (row >= row_end) continue;
-    uint16_t *crow = p.C + row * p.ldc;
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int64_t col = col0 + wave * 64 + j * 32 + r4 * 8 + h * 4;
-        const float v0 = acc[i][j][4 * r4], v1 = acc[i][j][4 * r4 + 1];
-        const float v2 = acc[i][j][4 * r4 + 2], v3 = acc[i][j][4 * r4 + 3];
-        if (vec_out && col + 4 <= p.Nc) {
-          const u32x2_t pk = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-          *reinterpret_cast<u32x2_t *>(crow + col) = pk;
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const u32x2_t pk = {pack_bf16x2(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1]),
+                              pack_bf16x2(acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3])};
+          *reinterpret_cast<u32x2_t *>(stg + tile64_swz(i * 32 + l32, 4 * j + r4) + 4 * h) = pk;
+        }
+    const bool vec16 = (p.ldc % 8) == 0;
+#pragma unroll 4
+    for (int q = 0; q < 32; ++q) {
+      const int row = q * 8 + (lane >> 3), chunk = lane & 7;
+      const u32x4_t v = lds_read_b128(stg + tile64_swz(row, chunk));
+      const int64_t grow = row0 + row;
+      const int64_t gcol = col0 + wave * 64 + chunk * 8;
+      if (grow < row_end && gcol < p.Nc) {
+        uint16_t *dst = p.C + grow * p.ldc + gcol;
+        if (vec16 && gcol + 8 <= p.Nc) {
+          *reinterpret_cast<u32x4_t *>(dst) = v;
         } else {
-          const float v[4] = {v0, v1, v2, v3};
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (col + e < p.Nc) crow[col + e] = to_bf16(v[e]);
+          for (int e = 0; e < 8 && gcol + e < p.Nc; ++e) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
         }
       }
     }
@@ -401,8 +420,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
 }
 
 // C[tile rows][tile columns] = bf16(sum_k part[t][k][r][c]) for the split
-// tiles t = 0 .. (tile - whole_tiles); four columns per thread, splits
-// summed in order.
+// tiles t; four columns per thread, splits summed in order.
 __global__ void k_reduce_tiles(Params p, int split_tiles) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per_tile = (int64_t)BM * (BN / 4);
@@ -410,7 +428,7 @@ __global__ void k_reduce_tiles(Params p, int split_tiles) {
   const int t = (int)(idx / per_tile);
   const int rem = (int)(idx - (int64_t)t * per_tile);
   const int r = rem / (BN / 4), c = (rem % (BN / 4)) * 4;
-  const int tile = p.whole_tiles + t;
+  const int tile = t;
   const int tn = tile % p.tiles_n, slot = tile / p.tiles_n;
   const RowTile rt = map_row_tile(slot, BM, p.offsets, p.groups, p.M);
   if (rt.group < 0) return;

@@ -459,7 +459,10 @@ bool use_fwd_regs() {
 
 template <int FMT>
 lora4_status run_fwd(const big::Params &p, hipStream_t st) {
-  return launch_lds("gemm_nt_base", fwd::k_gemm_fwd<FMT>, dim3((unsigned)p.nblocks), dim3(fwd::THREADS),
+  if (p.ksplit > 1)
+    return launch_lds("gemm_nt_base", fwd::k_gemm_fwd<FMT, true>, dim3((unsigned)p.nblocks), dim3(fwd::THREADS),
+                      (size_t)fwd::lds_bytes(), p, st);
+  return launch_lds("gemm_nt_base", fwd::k_gemm_fwd<FMT, false>, dim3((unsigned)p.nblocks), dim3(fwd::THREADS),
                     (size_t)fwd::lds_bytes(), p, st);
 }
 
@@ -512,7 +515,6 @@ big::Params big_params(const Mat &A, const PackedW &W, int64_t R, const Mat &A2,
   p.tiles_n = (int)ceil_div(Nc, big::BN);
   p.nblocks = (int)((ceil_div(std::max<int64_t>(M, 1), big::BM) + (E > 1 ? E : 0)) * p.tiles_n);
   p.tab = nf4_table();
-  p.whole_tiles = p.nblocks;
   p.ksplit = 1;
   p.split_steps = 1 << 30;
   p.Cpart = nullptr;
@@ -526,7 +528,6 @@ lora4_status run_nt_main_fmt(int fmt, const NtParams &p, dim3 grid, const Plan &
   if (p.R > 0 && use_fwd_regs() && pl.fs.use) {
     big::Params q = big_params(p.A, p.W, p.R, p.A2, p.B2, p.r2, p.M, p.Nc, p.offsets, p.groups, p.out.C,
                                p.out.ldc);
-    q.whole_tiles = pl.fs.whole_tiles;
     q.ksplit = pl.fs.ksplit;
     q.split_steps = pl.fs.split_steps;
     q.nblocks = pl.fs.whole_tiles + pl.fs.split_tiles * pl.fs.ksplit;
