@@ -74,6 +74,7 @@ struct WRaw {
 template <int FMT>
 __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  const uint32_t sel = big::sel_base();
   uint16_t *const As0 = smem, *const As1 = smem + TILE_A;
   uint16_t *const Bs0 = smem + 2 * TILE_A, *const Bs1 = smem + 2 * TILE_A + TILE_W;
 
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
         float c;
         if constexpr (FMT == FMT_NF4) c = __builtin_bit_cast(float, w.sc);
         else c = e4m3_to_f32(w.sc & 0xFFu) * __builtin_bit_cast(float, w.c2);
-        T = big::make_table(c, p.tab);
+        T = big::make_table(c, p.tab, sel);
       }
     }
 #pragma unroll

@@ -97,6 +97,11 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   // it) in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
   const int l32 = lane & 31, h = lane >> 5;
+  // NF4 table build: this lane's half of the levels (see make_table_pair)
+  const uint32_t sel = big::sel_base();
+  float qh[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) qh[i] = h ? p.tab.q[8 + i] : p.tab.q[i];
 
   // ---- X: direct loads into the LDS ring ------------------------------------
   // wave w, chunk c covers tile rows 8 (4 c + w) .. +7; lane l: row + l / 8,
@@ -109,9 +114,10 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   // X of step s into stage As, chunks 2 part .. 2 part + 1 (part 0..3)
   // steps are numbered within this block's range, which starts at step sb
   const int sb = is_split ? split * p.split_steps : 0;
+  const int Ri = (int)p.R;   // < 2^31 (the buffer offsets are 32-bit)
   auto issue_a = [&](int s, uint16_t *As, int part) {
-    const int64_t k0 = (int64_t)(s + sb) * BKS;
-    const bool edge = k0 + a_kq >= p.R;
+    const int k0 = (s + sb) * BKS;
+    const bool edge = k0 + a_kq >= Ri;
 #pragma unroll
     for (int c = 2 * part; c < 2 * part + 2; ++c)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (__attribute__((address_space(3))) void *)(As + (c * 4 + wave) * 512),
@@ -145,9 +151,9 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   // W load of a step is issued in its first half, a full step ahead of use
   auto load_w = [&](int s, WRaw &w, int part) {
     if (part >= 2) return;
-    const int64_t k0 = (int64_t)(s + sb) * BKS;
+    const int k0 = (s + sb) * BKS;
     // this lane's half lies inside the row (MXFP4 rows may end at k % 64 == 32)
-    const bool half_ok = k0 + 32 * h < p.R;
+    const bool half_ok = k0 + 32 * h < Ri;
     const int j = part;
     w.c[j] = __builtin_bit_cast(
         u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, half_ok ? w_voff[j] : OOB, (int)(k0 >> 1), 0));
@@ -155,7 +161,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
       w.sc[j] = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, half_ok ? s_voff[j] : OOB, (int)((k0 >> 6) * 4), 0);
     } else if constexpr (FMT == FMT_NF4_DQ) {
       w.sc[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, half_ok ? s_voff[j] : OOB, (int)(k0 >> 6), 0);
-      const int64_t gi = (s_idx0[j] + (k0 >> 6)) >> 8;
+      const int64_t gi = (s_idx0[j] + (int64_t)(k0 >> 6)) >> 8;
       w.c2[j] = __builtin_amdgcn_raw_buffer_load_b32(s2_rsrc, half_ok ? (uint32_t)(gi * 4) : OOB, 0, 0);
     } else {
       w.sc[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, half_ok ? s_voff[j] + h : OOB, (int)(k0 >> 5), 0);
@@ -165,27 +171,35 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   // unconditionally, so the count is exact)
   constexpr int W_LOADS = FMT == FMT_NF4_DQ ? 6 : 4;
 
-  // decode part `part` (0..3) of raw w into f: row j = part / 2, words
-  // q = 2 (part % 2) .. +1 (16 codes); the row's table is built at its first part.
-  auto decode_part = [&](const WRaw &w, WFrag &f, RunTable &T, float &sc, int part) {
-    const int j = part >> 1;
-    if ((part & 1) == 0) {
-      if constexpr (FMT == FMT_MXFP4) {
-        sc = e8m0_to_f32(w.sc[j] & 0xFFu);
-      } else {
-        float c;
-        if constexpr (FMT == FMT_NF4) c = __builtin_bit_cast(float, w.sc[j]);
-        else c = e4m3_to_f32(w.sc[j] & 0xFFu) * __builtin_bit_cast(float, w.c2[j]);
-        T = big::make_table(c, p.tab);
-      }
+  // Decode state of one row's run for a step: the NF4 table (shared by the
+  // lane pair, see make_table_pair) or the MXFP4 scale. It is built a
+  // sub-step or more before the run's words are decoded, so that the decode
+  // instructions never wait on the table's own chain.
+  struct RunDec {
+    RunTable T;
+    float sc;
+  };
+  auto make_run = [&](const WRaw &w, int j) -> RunDec {
+    RunDec d{};
+    if constexpr (FMT == FMT_MXFP4) {
+      d.sc = e8m0_to_f32(w.sc[j] & 0xFFu);
+    } else {
+      float c;
+      if constexpr (FMT == FMT_NF4) c = __builtin_bit_cast(float, w.sc[j]);
+      else c = e4m3_to_f32(w.sc[j] & 0xFFu) * __builtin_bit_cast(float, w.c2[j]);
+      d.T = big::make_table_pair(c, qh, sel);
     }
+    return d;
+  };
+  // decode code words q0, q0 + 1 of row j of raw w into f
+  auto decode_words = [&](const WRaw &w, WFrag &f, const RunDec &d, int j, int q0) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int q = (part & 1) * 2 + e;
+      const int q = q0 + e;
       if constexpr (FMT == FMT_MXFP4)
-        f.w[j][q] = big::decode8_mxfp4(w.c[j][q], sc);
+        f.w[j][q] = big::decode8_mxfp4(w.c[j][q], d.sc);
       else
-        f.w[j][q] = big::decode8_nf4(T, w.c[j][q]);
+        f.w[j][q] = big::decode8_nf4(d.T, w.c[j][q]);
     }
   };
 
@@ -236,29 +250,39 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
 
   // step s: X of step s in stage cur (its chunk-0 fragments already in x),
   // operands fcur. Over its four sub-steps it decodes step s+1 (rdec ->
-  // fnxt), loads the W of step s+2 (rload) and the X of step s+3 (stage
-  // ahead); after sub-step 1 it waits for the X of step s+1 and meets the
-  // other waves: stage nxt is then complete, and every wave is done with
-  // step s-1, whose stage step s+1 refills.
+  // fnxt; d0 = row 0's decode state, built by the previous step), loads the W
+  // of step s+2 (rload) and the X of step s+3 (stage ahead), and builds row
+  // 0's decode state of step s+2 for the next step; after sub-step 1 it waits
+  // for the X of step s+1 and meets the other waves: stage nxt is then
+  // complete, and every wave is done with step s-1, whose stage step s+1
+  // refills.
   auto body = [&](int s, const uint16_t *cur, const uint16_t *nxt, uint16_t *ahead, const WRaw &rdec, WRaw &rload,
-                  const WFrag &fcur, WFrag &fnxt, u32x4_t x[8]) {
-    RunTable T;
-    float sc = 0.0f;
-    auto work = [&](int kk) {
-      return [&, kk] {
-        decode_part(rdec, fnxt, T, sc, kk);
-        load_w(s + 2, rload, kk);
-        issue_a(s + 3, ahead, kk);
-      };
-    };
-    sub_step(fcur, 0, x, cur, h * 4 + 1, true, work(0));
-    sub_step(fcur, 1, x, cur, h * 4 + 2, true, work(1));
+                  const WFrag &fcur, WFrag &fnxt, u32x4_t x[8], RunDec &d0) {
+    RunDec d1;
+    sub_step(fcur, 0, x, cur, h * 4 + 1, true, [&] {
+      decode_words(rdec, fnxt, d0, 0, 0);
+      load_w(s + 2, rload, 0);
+      issue_a(s + 3, ahead, 0);
+    });
+    sub_step(fcur, 1, x, cur, h * 4 + 2, true, [&] {
+      decode_words(rdec, fnxt, d0, 0, 2);
+      d1 = make_run(rdec, 1);
+      load_w(s + 2, rload, 1);
+      issue_a(s + 3, ahead, 1);
+    });
     __builtin_amdgcn_s_waitcnt(VMCNT);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    sub_step(fcur, 2, x, cur, h * 4 + 3, true, work(2));
-    sub_step(fcur, 3, x, nxt, h * 4 + 0, true, work(3));
+    sub_step(fcur, 2, x, cur, h * 4 + 3, true, [&] {
+      decode_words(rdec, fnxt, d1, 1, 0);
+      issue_a(s + 3, ahead, 2);
+    });
+    sub_step(fcur, 3, x, nxt, h * 4 + 0, true, [&] {
+      decode_words(rdec, fnxt, d1, 1, 2);
+      d0 = make_run(rload, 0);
+      issue_a(s + 3, ahead, 3);
+    });
   };
 
   const int all_steps = (int)((p.R + BKS - 1) / BKS);
@@ -275,25 +299,26 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
     issue_a(2, stage(2), part);
     load_w(0, r0, part);
   }
-  {
-    RunTable T;
-    float sc = 0.0f;
 #pragma unroll
-    for (int part = 0; part < 4; ++part) decode_part(r0, f0, T, sc, part);
+  for (int j = 0; j < 2; ++j) {
+    const RunDec d = make_run(r0, j);
+    decode_words(r0, f0, d, j, 0);
+    decode_words(r0, f0, d, j, 2);
   }
 #pragma unroll
   for (int part = 0; part < 4; ++part) load_w(1, r1, part);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  RunDec d0 = make_run(r1, 0);
 #pragma unroll
   for (int i = 0; i < 8; ++i) x[i] = lds_read_b128(stage(0) + swz(i * 32 + l32, h * 4));
   int s = 0, si = 0;   // si = s % 5
   for (; s + 2 <= steps; s += 2) {
-    body(s, stage(si), stage(si + 1), stage(si + 3), r1, r0, f0, f1, x);
-    body(s + 1, stage(si + 1), stage(si + 2), stage(si + 4), r0, r1, f1, f0, x);
+    body(s, stage(si), stage(si + 1), stage(si + 3), r1, r0, f0, f1, x, d0);
+    body(s + 1, stage(si + 1), stage(si + 2), stage(si + 4), r0, r1, f1, f0, x, d0);
     si = si + 2 >= STAGES ? si + 2 - STAGES : si + 2;
   }
-  if (s < steps) body(s, stage(si), stage(si + 1), stage(si + 3), r1, r0, f0, f1, x);
+  if (s < steps) body(s, stage(si), stage(si + 1), stage(si + 3), r1, r0, f0, f1, x, d0);
   // the look-ahead loads past the end still write (zeros) into the ring
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
