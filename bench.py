@@ -102,8 +102,7 @@ def kernel_flops(name, spec):
         "gemm_nn_dgrad": 2 * M * N * K + 2 * M * K * r,    # dY deq(W) + dZ A
         "rows_skinny_z": 2 * M * K * r,                     # Z = X A^T
         "rows_skinny_dz": 2 * M * N * r,                    # dZ = s dY B
-        "gemm_tn_dA": 2 * M * r * K,
-        "gemm_tn_dB": 2 * M * r * N,
+        "gemm_tn_dA_dB": 2 * M * r * K + 2 * M * r * N,   # dZ^T X and Z^T dY
     }.get(name, 0)
 
 

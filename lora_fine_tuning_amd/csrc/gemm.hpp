@@ -541,7 +541,7 @@ __global__ __launch_bounds__(THREADS) void k_gemm_nn(NnParams p) {
 // --------------------------------------------------------------------------
 
 template <int BP, int BQ, int WAVES_P>
-__global__ __launch_bounds__(THREADS) void k_gemm_tn(TnParams p) {
+__device__ __forceinline__ void tn_tile(const TnParams &p, int bx, int by, int bz) {
   constexpr int WAVES_Q = 4 / WAVES_P;
   constexpr int WTP = BP / WAVES_P, WTQ = BQ / WAVES_Q;
   constexpr int FM = WTP / 16, FN = WTQ / 16;
@@ -550,10 +550,10 @@ __global__ __launch_bounds__(THREADS) void k_gemm_tn(TnParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t Us[BK * (BP + CPAD)];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[BK * (BQ + CPAD)];
 
-  const int64_t p0 = (int64_t)blockIdx.x * BP;  // note: x runs over P tiles
-  const int64_t q0 = (int64_t)blockIdx.y * BQ;
-  const int split = blockIdx.z % p.splits;
-  const int g = blockIdx.z / p.splits;
+  const int64_t p0 = (int64_t)bx * BP;
+  const int64_t q0 = (int64_t)by * BQ;
+  const int split = bz % p.splits;
+  const int g = bz / p.splits;
 
   int64_t ga = 0, gb = p.M;
   if (p.offsets) {
@@ -620,6 +620,21 @@ __global__ __launch_bounds__(THREADS) void k_gemm_tn(TnParams p) {
       }
     }
   }
+}
+
+// Two independent TN products with the same P tiling in one launch (the
+// weight gradients dA and dB of one backward). Blocks [0, na) take job a and
+// the rest job b; within a job the block index runs over P tiles fastest,
+// then Q tiles, then split + group.
+template <int BP, int BQ, int WAVES_P>
+__global__ __launch_bounds__(THREADS) void k_gemm_tn2(TnParams a, TnParams b, int ptiles, int qa, int qb,
+                                                       int64_t na) {
+  int64_t id = blockIdx.x;
+  const bool second = id >= na;
+  if (second) id -= na;
+  const TnParams p = second ? b : a;
+  const int64_t qt = second ? qb : qa;
+  tn_tile<BP, BQ, WAVES_P>(p, (int)(id % ptiles), (int)((id / ptiles) % qt), (int)(id / (ptiles * qt)));
 }
 
 // --------------------------------------------------------------------------

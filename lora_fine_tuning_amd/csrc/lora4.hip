@@ -591,12 +591,19 @@ lora4_status run_nn_skinny(int rt, const NnParams &p, dim3 grid, hipStream_t st)
   }
 }
 
-lora4_status run_tn(const char *name, int rt, const TnParams &p, dim3 grid, hipStream_t st) {
+// Both jobs share P (the rank) and so the P tiling; grid sizes of the two are
+// pa x qa x za and pa x qb x zb blocks.
+lora4_status run_tn2(const char *name, int rt, const TnParams &a, const TnParams &b, int qa, int za, int qb,
+                     int zb, hipStream_t st) {
+  const int pt = (int)ceil_div(a.P, rt);
+  const int64_t na = (int64_t)pt * qa * za, nb = (int64_t)pt * qb * zb;
+  if (na + nb > INT32_MAX) return LORA4_ERR_SHAPE;
+  const dim3 grid((unsigned)(na + nb)), block(THREADS);
   switch (rt) {
-    case 16: return launch(name, k_gemm_tn<16, TN_BQ, 1>, grid, dim3(THREADS), p, st);
-    case 32: return launch(name, k_gemm_tn<32, TN_BQ, 1>, grid, dim3(THREADS), p, st);
-    case 64: return launch(name, k_gemm_tn<64, TN_BQ, 1>, grid, dim3(THREADS), p, st);
-    default: return launch(name, k_gemm_tn<128, TN_BQ, 2>, grid, dim3(THREADS), p, st);
+    case 16: return launch_args(name, k_gemm_tn2<16, TN_BQ, 1>, grid, block, st, a, b, pt, qa, qb, na);
+    case 32: return launch_args(name, k_gemm_tn2<32, TN_BQ, 1>, grid, block, st, a, b, pt, qa, qb, na);
+    case 64: return launch_args(name, k_gemm_tn2<64, TN_BQ, 1>, grid, block, st, a, b, pt, qa, qb, na);
+    default: return launch_args(name, k_gemm_tn2<128, TN_BQ, 2>, grid, block, st, a, b, pt, qa, qb, na);
   }
 }
 
@@ -845,35 +852,28 @@ lora4_status lora4_backward(const lora4_W *W, const uint16_t *X, const uint16_t 
     TRY(run_nn_main_fmt(W->format, p, grid, st));
   }
 
-  // dA = dZ^T X and dB^T = Z^T dY, split over rows; one launch reduces both
+  // dA = dZ^T X and dB^T = Z^T dY, split over rows, in one launch; one launch
+  // reduces both
   float *part_b = ws_at<float>(workspace, pl.off_part_b);
   {
-    TnParams p{};
-    p.U = mat(dZ, r);
-    p.V = mat(X, pl.K);
-    p.P = r;
-    p.Q = pl.K;
-    p.M = M;
-    p.offsets = group_offsets;
-    p.groups = (int)pl.E;
-    p.splits = pl.msplit_a;
-    p.part = part;
-    dim3 grid((unsigned)ceil_div(r, pl.rt), (unsigned)pl.tq_a, (unsigned)(pl.msplit_a * pl.E));
-    TRY(run_tn("gemm_tn_dA", pl.rt, p, grid, st));
-  }
-  {
-    TnParams p{};
-    p.U = mat(Zu, r);
-    p.V = mat(dY, pl.N);
-    p.P = r;
-    p.Q = pl.N;
-    p.M = M;
-    p.offsets = group_offsets;
-    p.groups = (int)pl.E;
-    p.splits = pl.msplit_b;
-    p.part = part_b;
-    dim3 grid((unsigned)ceil_div(r, pl.rt), (unsigned)pl.tq_b, (unsigned)(pl.msplit_b * pl.E));
-    TRY(run_tn("gemm_tn_dB", pl.rt, p, grid, st));
+    TnParams pa{};
+    pa.U = mat(dZ, r);
+    pa.V = mat(X, pl.K);
+    pa.P = r;
+    pa.Q = pl.K;
+    pa.M = M;
+    pa.offsets = group_offsets;
+    pa.groups = (int)pl.E;
+    pa.splits = pl.msplit_a;
+    pa.part = part;
+    TnParams pb = pa;
+    pb.U = mat(Zu, r);
+    pb.V = mat(dY, pl.N);
+    pb.Q = pl.N;
+    pb.splits = pl.msplit_b;
+    pb.part = part_b;
+    TRY(run_tn2("gemm_tn_dA_dB", pl.rt, pa, pb, pl.tq_a, (int)(pl.msplit_a * pl.E), pl.tq_b,
+                (int)(pl.msplit_b * pl.E), st));
   }
   {
     const int64_t na = pl.E * r * pl.K, nb = pl.E * r * pl.N;
