@@ -76,7 +76,109 @@ struct Params {
   int ksplit;
   int split_steps;
   float *Cpart;
+  // rank-r tail operand given as fp32 partial sums over reduction ranges
+  // (A2part[range][M][r2], absolute rows; A2 is then unused): the tail adds
+  // the A2parts ranges in order and uses bf16(A2scale * sum). Blocks of
+  // column tile 0 also store bf16(A2alpha1 * sum) to A2out1 and
+  // bf16(A2alpha2 * sum) to A2out2 ([M, r2] each, either may be null) for the
+  // passes that follow.
+  const float *A2part;
+  int A2parts;        // 1 .. A2_MAX_PARTS
+  float A2scale;
+  uint16_t *A2out1;
+  float A2alpha1;
+  uint16_t *A2out2;
+  float A2alpha2;
 };
+
+constexpr int A2_MAX_PARTS = 4;
+
+// Sum over the partial ranges (in range order, from +0) of the 8 tail
+// operand values of row gr, columns gk .. gk + 7 (zero past r2).
+__device__ __forceinline__ void a2_part_sum(const Params &p, int64_t gr, int64_t gk, float (&v)[8]) {
+  float q[A2_MAX_PARTS][8];
+  const int64_t stride = p.M * p.r2;
+  const float *src = p.A2part + gr * p.r2 + gk;
+  const bool vec = (p.r2 % 4) == 0 && gk + 8 <= p.r2;
+#pragma unroll
+  for (int r = 0; r < A2_MAX_PARTS; ++r) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[r][e] = 0.0f;
+    if (r < p.A2parts) {
+      const float *sr = src + r * stride;
+      if (vec) {
+        const f32x4_t lo = *reinterpret_cast<const f32x4_t *>(sr);
+        const f32x4_t hi = *reinterpret_cast<const f32x4_t *>(sr + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          q[r][e] = lo[e];
+          q[r][e + 4] = hi[e];
+        }
+      } else {
+        for (int e = 0; e < 8; ++e)
+          if (gk + e < p.r2) q[r][e] = sr[e];
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float t = 0.0f;
+#pragma unroll
+    for (int r = 0; r < A2_MAX_PARTS; ++r)
+      if (r < p.A2parts) t += q[r][e];
+    v[e] = t;
+  }
+}
+
+__device__ __forceinline__ u32x4_t pack_scaled8(const float (&v)[8], float a) {
+  return u32x4_t{pack_bf16x2(a * v[0], a * v[1]), pack_bf16x2(a * v[2], a * v[3]), pack_bf16x2(a * v[4], a * v[5]),
+                 pack_bf16x2(a * v[6], a * v[7])};
+}
+
+// bf16 row piece [gr][gk .. gk + 7] of an [M, r2] output (elements past r2
+// dropped; one 16-byte store when the row piece is whole and aligned).
+__device__ __forceinline__ void store_a2_piece(uint16_t *out, int r2, int64_t gr, int64_t gk, u32x4_t v) {
+  uint16_t *dst = out + gr * r2 + gk;
+  if ((r2 % 8) == 0) {
+    *reinterpret_cast<u32x4_t *>(dst) = v;
+  } else {
+    for (int e = 0; e < 8; ++e)
+      if (gk + e < r2) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+  }
+}
+
+// One 64-column step (k0 ..) of the tail operand from the partials into the
+// LDS tile `As` (256 rows, bf16, 8-column chunk c of row i at
+// As + lds_off(i, c)): thread t owns row t; chunks past r2 are zero.
+template <typename Off>
+__device__ __forceinline__ void a2_parts_to_lds(const Params &p, uint16_t *As, Off lds_off, int64_t row0,
+                                                int64_t row_end, int k0, int t, bool store_out) {
+  const int64_t gr = row0 + t;
+  const bool row_ok = gr < row_end;
+#pragma unroll 1
+  for (int c0 = 0; c0 < 8; c0 += 2) {
+    float v[2][8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t gk = k0 + 8 * (c0 + u);
+      if (row_ok && gk < p.r2) {
+        a2_part_sum(p, gr, gk, v[u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[u][e] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t gk = k0 + 8 * (c0 + u);
+      lds_write_b128(As + lds_off(t, c0 + u), pack_scaled8(v[u], p.A2scale));
+      if (store_out && row_ok && gk < p.r2) {
+        if (p.A2out1) store_a2_piece(p.A2out1, p.r2, gr, gk, pack_scaled8(v[u], p.A2alpha1));
+        if (p.A2out2) store_a2_piece(p.A2out2, p.r2, gr, gk, pack_scaled8(v[u], p.A2alpha2));
+      }
+    }
+  }
+}
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 

@@ -334,25 +334,29 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
     const bool b_vec = (p.B2.ld % 8) == 0;
     for (int k0 = 0; k0 < p.r2; k0 += BKS) {
       const int nkk = min(4, (p.r2 - k0 + 7) / 8);
+      if (p.A2part) {
+        big::a2_parts_to_lds(p, As, [](int i, int c) { return swz(i, c); }, row0, row_end, k0, t, col0 == 0);
+      } else {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int idx = t + THREADS * c;
-        const int row = idx >> 3, chunk = idx & 7;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        const int64_t gr = row0 + row;
-        const int64_t gk = k0 + chunk * 8;
-        if (gr < row_end && gk < p.r2) {
-          const uint16_t *src = p.A2.p + gr * p.A2.ld + gk;
-          if (a_vec && gk + 8 <= p.r2) {
-            v = *reinterpret_cast<const u32x4_t *>(src);
-          } else {
-            uint32_t w4[4] = {0u, 0u, 0u, 0u};
-            for (int e = 0; e < 8; ++e)
-              if (gk + e < p.r2) w4[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
-            v = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
+        for (int c = 0; c < 8; ++c) {
+          const int idx = t + THREADS * c;
+          const int row = idx >> 3, chunk = idx & 7;
+          u32x4_t v = {0u, 0u, 0u, 0u};
+          const int64_t gr = row0 + row;
+          const int64_t gk = k0 + chunk * 8;
+          if (gr < row_end && gk < p.r2) {
+            const uint16_t *src = p.A2.p + gr * p.A2.ld + gk;
+            if (a_vec && gk + 8 <= p.r2) {
+              v = *reinterpret_cast<const u32x4_t *>(src);
+            } else {
+              uint32_t w4[4] = {0u, 0u, 0u, 0u};
+              for (int e = 0; e < 8; ++e)
+                if (gk + e < p.r2) w4[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+              v = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
+            }
           }
+          lds_write_b128(As + swz(row, chunk), v);
         }
-        lds_write_b128(As + swz(row, chunk), v);
       }
       WFrag bt;
 #pragma unroll

@@ -521,13 +521,46 @@ big::Params big_params(const Mat &A, const PackedW &W, int64_t R, const Mat &A2,
   return p;
 }
 
+// Rank-r tail operand handed to a GEMM as fp32 partials of the skinny pass
+// (the GEMM sums them; see big::Params::A2part).
+struct TailParts {
+  const float *part;
+  int parts;
+  float scale;
+  uint16_t *out1;
+  float alpha1;
+  uint16_t *out2;
+  float alpha2;
+};
+
+void apply_tail_parts(big::Params &q, const TailParts *tp) {
+  if (!tp) return;
+  q.A2part = tp->part;
+  q.A2parts = tp->parts;
+  q.A2scale = tp->scale;
+  q.A2out1 = tp->out1;
+  q.A2alpha1 = tp->alpha1;
+  q.A2out2 = tp->out2;
+  q.A2alpha2 = tp->alpha2;
+}
+
+// Whether the forward base pass runs the register-direct kernel, and the
+// backward dgrad pass the 256 x 256 dgrad kernel (the kernels that can take
+// their tail operand as partials).
+bool fwd_regs_taken(int64_t R, const Plan &pl) { return R > 0 && use_fwd_regs() && pl.fs.use; }
+bool dgrad_taken(int64_t R, int64_t ld_a, int64_t M, const PackedW &W, int64_t Nc, int64_t E) {
+  return R > 0 && big_fits(ld_a, M, W) && use_big(M, Nc, E) && use_dgrad_new();
+}
+
 // Forward base GEMM: the register-direct kernel as the plan schedules it
 // (split partials in `party`, then reduced into the output), else the
 // 128 x 128 kernel.
-lora4_status run_nt_main_fmt(int fmt, const NtParams &p, dim3 grid, const Plan &pl, float *party, hipStream_t st) {
-  if (p.R > 0 && use_fwd_regs() && pl.fs.use) {
+lora4_status run_nt_main_fmt(int fmt, const NtParams &p, dim3 grid, const Plan &pl, float *party,
+                             const TailParts *tp, hipStream_t st) {
+  if (fwd_regs_taken(p.R, pl)) {
     big::Params q = big_params(p.A, p.W, p.R, p.A2, p.B2, p.r2, p.M, p.Nc, p.offsets, p.groups, p.out.C,
                                p.out.ldc);
+    apply_tail_parts(q, tp);
     q.ksplit = pl.fs.ksplit;
     q.split_steps = pl.fs.split_steps;
     q.nblocks = pl.fs.whole_tiles + pl.fs.split_tiles * pl.fs.ksplit;
@@ -540,6 +573,7 @@ lora4_status run_nt_main_fmt(int fmt, const NtParams &p, dim3 grid, const Plan &
     }
     return LORA4_OK;
   }
+  if (tp) return LORA4_ERR_UNIMPLEMENTED;   // (callers check the same predicates)
   if (!use_fwd_regs() && p.R > 0 && big_fits(p.A.ld, p.M, p.W) && use_big(p.M, p.Nc, p.groups)) {
     big::Params q = big_params(p.A, p.W, p.R, p.A2, p.B2, p.r2, p.M, p.Nc, p.offsets, p.groups, p.out.C,
                                p.out.ldc);
@@ -558,11 +592,17 @@ lora4_status run_nn_main(const NnParams &p, dim3 grid, hipStream_t st) {
   return launch("gemm_nn_dgrad", k_gemm_nn<FMT, BM_MAIN, BN_MAIN, 2>, grid, dim3(THREADS), p, st);
 }
 
-lora4_status run_nn_main_fmt(int fmt, const NnParams &p, dim3 grid, hipStream_t st) {
+lora4_status run_nn_main_fmt(int fmt, const NnParams &p, dim3 grid, const TailParts *tp, hipStream_t st) {
+  if (dgrad_taken(p.R, p.A.ld, p.M, p.W, p.Nc, p.groups)) {
+    big::Params q = big_params(p.A, p.W, p.R, p.A2, p.B2, p.r2, p.M, p.Nc, p.offsets, p.groups, p.out.C,
+                               p.out.ldc);
+    apply_tail_parts(q, tp);
+    return run_dgrad_fmt(fmt, q, st);
+  }
+  if (tp) return LORA4_ERR_UNIMPLEMENTED;   // (callers check the same predicates)
   if (p.R > 0 && big_fits(p.A.ld, p.M, p.W) && use_big(p.M, p.Nc, p.groups)) {
     big::Params q = big_params(p.A, p.W, p.R, p.A2, p.B2, p.r2, p.M, p.Nc, p.offsets, p.groups, p.out.C,
                                p.out.ldc);
-    if (use_dgrad_new()) return run_dgrad_fmt(fmt, q, st);
     return run_big_fmt<1>("gemm_nn_dgrad", fmt, q, st);
   }
   switch (fmt) {
@@ -657,7 +697,7 @@ size_t sk_part_bytes_for(int64_t M, int64_t R, int r, int64_t E) {
 
 lora4_status rows_skinny(int transb, const uint16_t *act, int64_t ld_act, const uint16_t *w, int64_t ld_w,
                          int64_t g_w, int64_t R, int64_t M, int r, const int64_t *offs, int64_t E, uint16_t *o1,
-                         float a1, uint16_t *o2, float a2, float *part, hipStream_t st) {
+                         float a1, uint16_t *o2, float a2, float *part, bool defer_reduce, hipStream_t st) {
   const SkSched f = sk_sched(M, R, r, E);
   skinny::Params p{};
   p.act = act;
@@ -686,7 +726,7 @@ lora4_status rows_skinny(int transb, const uint16_t *act, int64_t ld_act, const 
     default: st1 = run_rows_tj<1, 8>(transb, p, grid, st); break;
   }
   TRY(st1);
-  if (f.ranges > 1) {
+  if (f.ranges > 1 && !defer_reduce) {
     const int64_t n = M * r;
     TRY(reduce_bf16(transb ? "reduce_dz" : "reduce_z", part, f.ranges, n, n, o1, a1, o2, a2, st));
   }
@@ -695,13 +735,13 @@ lora4_status rows_skinny(int transb, const uint16_t *act, int64_t ld_act, const 
 
 lora4_status z_pass(const Plan &pl, const lora4_W *W, const uint16_t *X, const uint16_t *A,
                     const int64_t *offs, uint16_t *z1, float a1, uint16_t *z2, float a2, float *part,
-                    hipStream_t st) {
+                    bool defer_reduce, hipStream_t st) {
   if (!z1) {   // one output only
     z1 = z2;
     a1 = a2;
     z2 = nullptr;
   }
-  return rows_skinny(0, X, pl.K, A, pl.K, (int64_t)pl.r * pl.K, pl.K, pl.M, pl.r, offs, pl.E, z1, a1, z2, a2, part,
+  return rows_skinny(0, X, pl.K, A, pl.K, (int64_t)pl.r * pl.K, pl.K, pl.M, pl.r, offs, pl.E, z1, a1, z2, a2, part, defer_reduce,
                      st);
 }
 
@@ -761,8 +801,16 @@ lora4_status lora4_forward(const lora4_W *W, const uint16_t *X, int64_t M, const
   if (M == 0) return LORA4_OK;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
+  // Z = X A^T. With the reduction split into ranges and the register-direct
+  // base kernel, that kernel's tail adds the fp32 range partials itself (and
+  // its column-tile-0 blocks store Z, and s Z for a Y_lora pass); otherwise
+  // the partials are reduced into Z and s Z here.
   uint16_t *sZ = ws_at<uint16_t>(workspace, pl.off_sz);
-  TRY(z_pass(pl, W, X, A, group_offsets, Z, 1.0f, sZ, s, ws_at<float>(workspace, pl.off_skpart), st));
+  float *skpart = ws_at<float>(workspace, pl.off_skpart);
+  const SkSched zs = sk_sched(M, pl.K, r, pl.E);
+  const bool z_tail = zs.ranges > 1 && zs.ranges <= big::A2_MAX_PARTS && fwd_regs_taken(pl.K, pl);
+  const TailParts ztp{skpart, zs.ranges, s, Z, 1.0f, Y_lora ? sZ : nullptr, s};
+  TRY(z_pass(pl, W, X, A, group_offsets, Z, 1.0f, sZ, s, skpart, z_tail, st));
 
   NtParams p{};
   p.A = mat(X, pl.K);
@@ -780,19 +828,19 @@ lora4_status lora4_forward(const lora4_W *W, const uint16_t *X, int64_t M, const
   p.tab = nf4_table();
   dim3 grid((unsigned)ceil_div(pl.N, BN_MAIN), (unsigned)pl.row_slots, 1);
   float *party = ws_at<float>(workspace, pl.off_party);
-  TRY(run_nt_main_fmt(W->format, p, grid, pl, party, st));
+  TRY(run_nt_main_fmt(W->format, p, grid, pl, party, z_tail ? &ztp : nullptr, st));
   if (Y_base) {
     NtParams q = p;
     q.r2 = 0;
     q.out.C = Y_base;
-    TRY(run_nt_main_fmt(W->format, q, grid, pl, party, st));
+    TRY(run_nt_main_fmt(W->format, q, grid, pl, party, nullptr, st));
   }
   if (Y_lora) {
     NtParams q = p;
     q.R = 0;
     q.Rsplit = 64;
     q.out.C = Y_lora;
-    TRY(run_nt_main_fmt(W->format, q, grid, pl, party, st));
+    TRY(run_nt_main_fmt(W->format, q, grid, pl, party, nullptr, st));
   }
   return LORA4_OK;
 }
@@ -824,13 +872,21 @@ lora4_status lora4_backward(const lora4_W *W, const uint16_t *X, const uint16_t 
   const uint16_t *Zu = Z;
   if (!Zu) {
     uint16_t *Zw = ws_at<uint16_t>(workspace, pl.off_zw);
-    TRY(z_pass(pl, W, X, A, group_offsets, Zw, 1.0f, nullptr, 0.0f, ws_at<float>(workspace, pl.off_skpart), st));
+    TRY(z_pass(pl, W, X, A, group_offsets, Zw, 1.0f, nullptr, 0.0f, ws_at<float>(workspace, pl.off_skpart), false,
+               st));
     Zu = Zw;
   }
 
-  // dZ = s dY B  (row blocks, reduction over N)
-  TRY(rows_skinny(1, dY, pl.N, B, r, pl.N * r, pl.N, M, r, group_offsets, pl.E, dZ, s, nullptr, 0.0f,
-                  ws_at<float>(workspace, pl.off_skpart), st));
+  // dZ = s dY B  (row blocks, reduction over N). With the reduction split
+  // into ranges and the 256 x 256 dgrad kernel, that kernel's tail adds the
+  // fp32 range partials (its column-tile-0 blocks store dZ for the dA pass).
+  float *skpart = ws_at<float>(workspace, pl.off_skpart);
+  const SkSched dzs = sk_sched(M, pl.N, r, pl.E);
+  const bool dz_tail = dzs.ranges > 1 && dzs.ranges <= big::A2_MAX_PARTS &&
+                       dgrad_taken(pl.N, pl.N, M, packed_of(W), pl.K, pl.E);
+  const TailParts dztp{skpart, dzs.ranges, s, dZ, s, nullptr, 0.0f};
+  TRY(rows_skinny(1, dY, pl.N, B, r, pl.N * r, pl.N, M, r, group_offsets, pl.E, dZ, s, nullptr, 0.0f, skpart,
+                  dz_tail, st));
 
   // dX = dY deq(W) + dZ A
   {
@@ -849,7 +905,7 @@ lora4_status lora4_backward(const lora4_W *W, const uint16_t *X, const uint16_t 
     p.out = GemmOut{dX, pl.K, nullptr, 0, 1.0f};
     p.tab = nf4_table();
     dim3 grid((unsigned)ceil_div(pl.K, BN_MAIN), (unsigned)pl.row_slots, 1);
-    TRY(run_nn_main_fmt(W->format, p, grid, st));
+    TRY(run_nn_main_fmt(W->format, p, grid, dz_tail ? &dztp : nullptr, st));
   }
 
   // dA = dZ^T X and dB^T = Z^T dY, split over rows, in one launch; one launch

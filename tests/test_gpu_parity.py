@@ -242,3 +242,46 @@ def test_forward_two_rounds_of_tiles(monkeypatch):
     Xf, Af, Bf = f64(t["X"]), f64(t["A"]), f64(t["B"])
     ref = Xf @ Wn.T + lay.s * ((Xf @ Af.T) @ Bf[cols].T)
     assert rel(Y[:, cols], ref) <= TOL
+
+
+@pytest.mark.parametrize("r", [16, 12, 20])
+@pytest.mark.parametrize("grouped", [False, True])
+def test_tails_add_rank_r_partials(r, grouped, monkeypatch):
+    """With the rank-r reductions split into ranges, the forward and dgrad
+    GEMM tails add the fp32 range partials themselves (no separate reduction
+    launch) and store Z / dZ for the passes that follow: r % 4 != 0 takes the
+    element loads, r % 8 != 0 the element stores."""
+    monkeypatch.setenv("LORA4_BIG", "1")
+    K, N = 1024, 1024
+    offs = [0, 130, 130, 300] if grouped else None
+    M = 300
+    lay = synth.small_layer(M, K, N, r, fmt=synth.NF4, index=40 + r, experts=3 if grouped else 1, offsets=offs)
+    print_case("tail partials", r, offs)
+    t = synth.inputs(lay)
+    L.timing_enable(True)
+    try:
+        L.timing_collect()
+        got = _run(lay, t, offsets=offs)
+        names = set(L.timing_collect())
+    finally:
+        L.timing_enable(False)
+    assert "reduce_z" not in names and "reduce_dz" not in names, names
+    assert "rows_skinny_z" in names and "rows_skinny_dz" in names, names
+    if not grouped:
+        _check_all(got, _oracle(lay, t))
+    else:
+        Ws = [dequant_rows(t["W"][e], np.arange(N), synth.NF4) for e in range(3)]
+        As = [f64(a) for a in t["A"]]
+        Bs = [f64(b) for b in t["B"]]
+        fo = lora.grouped_forward(f64(t["X"]), Ws, As, Bs, lay.s, offs)
+        bo = lora.grouped_backward(f64(t["X"]), Ws, As, Bs, lay.s, f64(t["dY"]), offs)
+        for k in ("Y", "Z"):
+            assert rel(got[k], fo[k]) <= TOL, k
+        assert rel(got["dX"], bo["dX"]) <= TOL
+        for e in (0, 2):
+            assert rel(got["dA"][e], bo["dA"][e]) <= TOL and rel(got["dB"][e], bo["dB"][e]) <= TOL, e
+    # no Z output requested: the tail still sums the partials for Y
+    base = pack_gpu(t["W"], lay.fmt)
+    o = None if offs is None else torch.tensor(offs, dtype=torch.int64, device=DEV)
+    fw = L.forward(base, to_dev(t["X"]), to_dev(t["A"]), to_dev(t["B"]), lay.s, group_offsets=o, want_z=False)
+    assert np.array_equal(to_host(fw["Y"]), got["Y"])
