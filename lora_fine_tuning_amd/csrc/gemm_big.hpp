@@ -229,15 +229,9 @@ __device__ __forceinline__ RunTable make_table(float c, const Nf4Table &tab, uin
   return r;
 }
 
-// The same table for a run shared by lanes l and l + 32 (same row, same
-// scale): lane half h builds entries 8 h .. 8 h + 7 (qh[i] = q[8 h + i]), and
-// one v_permlane32_swap per byte-plane register gives every lane both
-// halves (element 0: the lower lane's value, element 1: the upper lane's).
-// 20 instructions instead of 32. All 64 lanes must be active.
-__device__ __forceinline__ RunTable make_table_pair(float c, const float qh[8], uint32_t sel) {
-  uint32_t t[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) t[k] = pack_bf16x2(qh[2 * k] * c, qh[2 * k + 1] * c);
+// Second stage of make_table_pair (below), from this lane's four bf16 pairs
+// t[k] = (q[8 h + 2 k] c, q[8 h + 2 k + 1] c).
+__device__ __forceinline__ RunTable table_pair_from(const uint32_t t[4], uint32_t sel) {
   const uint32_t l0 = perm(t[1], t[0], 0x06040200u), l1 = perm(t[3], t[2], 0x06040200u);
   const uint32_t h0 = perm(t[1], t[0], 0x07050301u), h1 = perm(t[3], t[2], 0x07050301u);
   const auto sl0 = __builtin_amdgcn_permlane32_swap(l0, l0, false, false);
@@ -255,6 +249,18 @@ __device__ __forceinline__ RunTable make_table_pair(float c, const float qh[8], 
   r.hi[3] = sh1[1];
   r.sel = sel;
   return r;
+}
+
+// The same table for a run shared by lanes l and l + 32 (same row, same
+// scale): lane half h builds entries 8 h .. 8 h + 7 (qh[i] = q[8 h + i]), and
+// one v_permlane32_swap per byte-plane register gives every lane both
+// halves (element 0: the lower lane's value, element 1: the upper lane's).
+// 20 instructions instead of 32. All 64 lanes must be active.
+__device__ __forceinline__ RunTable make_table_pair(float c, const float qh[8], uint32_t sel) {
+  uint32_t t[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) t[k] = pack_bf16x2(qh[2 * k] * c, qh[2 * k + 1] * c);
+  return table_pair_from(t, sel);
 }
 
 // 4 indices (bytes 0..15) -> low and high bytes of T[idx].

@@ -44,6 +44,13 @@ using big::Params;
 using big::RunTable;
 using big::rsrc_t;
 
+#ifndef LORA4_FWD_SLICED
+#define LORA4_FWD_SLICED 1
+#endif
+#ifndef LORA4_SLICE_V1
+#define LORA4_SLICE_V1 5
+#endif
+
 constexpr int BM = 256, BN = 256, BKS = 64, THREADS = 256, STAGES = 5;
 constexpr int TILE = BM * BKS;   // one X stage, bf16 elements
 
@@ -285,6 +292,162 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
     });
   };
 
+#if LORA4_FWD_SLICED
+  // ---- the same step with its VALU and load work dealt out by hand: every
+  // MFMA pair of a sub-step gets one slice (a stage of a code word's decode,
+  // of a table build, or one global load), fenced so that nothing moves
+  // between pairs.
+  struct WordDec {
+    uint32_t i0, i1, L0, H0, L1, H1;
+  };
+  struct RunBuild {
+    float c;
+    float pr[8];
+  };
+  // X of step s, chunk c (0..7) of stage As
+  auto issue_a1 = [&](int s, uint16_t *As, int c) {
+    const int k0 = (s + sb) * BKS;
+    const bool edge = k0 + a_kq >= Ri;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (__attribute__((address_space(3))) void *)(As + (c * 4 + wave) * 512),
+                                             16, edge ? OOB : a_voff0 + c * a_cstep, (int)(k0 * 2), 0, 0);
+  };
+  // W of step s, row j: scale (and NF4-DQ second-level scale), then codes
+  auto load_w_scale = [&](int s, WRaw &w, int j) {
+    const int k0 = (s + sb) * BKS;
+    const bool half_ok = k0 + 32 * h < Ri;
+    if constexpr (FMT == FMT_NF4) {
+      w.sc[j] = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, half_ok ? s_voff[j] : OOB, (int)((k0 >> 6) * 4), 0);
+    } else if constexpr (FMT == FMT_NF4_DQ) {
+      w.sc[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, half_ok ? s_voff[j] : OOB, (int)(k0 >> 6), 0);
+      const int64_t gi = (s_idx0[j] + (int64_t)(k0 >> 6)) >> 8;
+      w.c2[j] = __builtin_amdgcn_raw_buffer_load_b32(s2_rsrc, half_ok ? (uint32_t)(gi * 4) : OOB, 0, 0);
+    } else {
+      w.sc[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, half_ok ? s_voff[j] + h : OOB, (int)(k0 >> 5), 0);
+    }
+  };
+  auto load_w_codes = [&](int s, WRaw &w, int j) {
+    const int k0 = (s + sb) * BKS;
+    const bool half_ok = k0 + 32 * h < Ri;
+    w.c[j] = __builtin_bit_cast(
+        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, half_ok ? w_voff[j] : OOB, (int)(k0 >> 1), 0));
+  };
+  // slice i of decoding words q0, q0 + 1 of row j of w into f
+  auto dec_slice = [&](int i, const WRaw &w, WFrag &f, const RunDec &d, int j, int q0, WordDec (&wd)[2]) {
+    if constexpr (FMT == FMT_MXFP4) {
+      // one conversion (a bf16 pair) per slice
+      const int q = q0 + (i >> 2);
+      uint32_t v;
+      switch (i & 3) {
+        case 0: v = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w.c[j][q], d.sc, 0)); break;
+        case 1: v = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w.c[j][q], d.sc, 1)); break;
+        case 2: v = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w.c[j][q], d.sc, 2)); break;
+        default: v = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w.c[j][q], d.sc, 3)); break;
+      }
+      f.w[j][q][i & 3] = v;
+    } else {
+      auto unpack = [](uint32_t c, WordDec &o) {
+        const uint32_t ev = c & 0x0F0F0F0Fu;          // n0 n2 n4 n6
+        const uint32_t od = (c >> 4) & 0x0F0F0F0Fu;   // n1 n3 n5 n7
+        o.i0 = big::perm(od, ev, 0x05010400u);        // n0 n1 n2 n3
+        o.i1 = big::perm(od, ev, 0x07030602u);        // n4 n5 n6 n7
+      };
+      auto fin = [](const WordDec &o) -> u32x4_t {
+        return u32x4_t{big::perm(o.H0, o.L0, 0x05010400u), big::perm(o.H0, o.L0, 0x07030602u),
+                       big::perm(o.H1, o.L1, 0x05010400u), big::perm(o.H1, o.L1, 0x07030602u)};
+      };
+      switch (i) {
+        case 0: unpack(w.c[j][q0], wd[0]); break;
+        case 1: big::lookup4(d.T, wd[0].i0, wd[0].L0, wd[0].H0); break;
+        case 2: big::lookup4(d.T, wd[0].i1, wd[0].L1, wd[0].H1); break;
+        case 3:
+          f.w[j][q0] = fin(wd[0]);
+          unpack(w.c[j][q0 + 1], wd[1]);
+          break;
+        case 4: big::lookup4(d.T, wd[1].i0, wd[1].L0, wd[1].H0); break;
+        case 5: big::lookup4(d.T, wd[1].i1, wd[1].L1, wd[1].H1); break;
+        case 6: f.w[j][q0 + 1] = fin(wd[1]); break;
+        default: break;
+      }
+    }
+  };
+  // slice i of building the decode state of row j of w into out
+  auto run_slice = [&](int i, const WRaw &w, int j, RunBuild &rb, RunDec &out) {
+    if constexpr (FMT == FMT_MXFP4) {
+      if (i == 7) out.sc = e8m0_to_f32(w.sc[j] & 0xFFu);
+    } else {
+      if (i == 0) {
+        if constexpr (FMT == FMT_NF4) rb.c = __builtin_bit_cast(float, w.sc[j]);
+        else rb.c = e4m3_to_f32(w.sc[j] & 0xFFu) * __builtin_bit_cast(float, w.c2[j]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) rb.pr[k] = qh[k] * rb.c;
+      } else if (i == 6) {
+#pragma unroll
+        for (int k = 4; k < 8; ++k) rb.pr[k] = qh[k] * rb.c;
+      } else if (i == 7) {
+        uint32_t t4[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) t4[k] = pack_bf16x2(rb.pr[2 * k], rb.pr[2 * k + 1]);
+        out.T = big::table_pair_from(t4, sel);
+      }
+    }
+  };
+  auto sub_step_s = [&](const WFrag &cur, int kk, u32x4_t x[8], const uint16_t *src, int chunk, auto &&slice) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      acc[i][0] = mfma_32x32x16(cur.w[0][kk], x[i], acc[i][0]);
+      acc[i][1] = mfma_32x32x16(cur.w[1][kk], x[i], acc[i][1]);
+      x[i] = lds_read_b128(src + swz(i * 32 + l32, chunk));
+      slice(i);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, LORA4_SLICE_V1, 0);    // VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                 // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);                 // global load
+      __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);                // VALU
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto body_s = [&](int s, const uint16_t *cur, const uint16_t *nxt, uint16_t *ahead, const WRaw &rdec,
+                    WRaw &rload, const WFrag &fcur, WFrag &fnxt, u32x4_t x[8], RunDec &d0) {
+    RunDec d1{};
+    RunBuild rb;
+    WordDec wd[2];
+    sub_step_s(fcur, 0, x, cur, h * 4 + 1, [&](int i) {
+      dec_slice(i, rdec, fnxt, d0, 0, 0, wd);
+      if (i == 0) load_w_scale(s + 2, rload, 0);
+      if (i == 2) issue_a1(s + 3, ahead, 0);
+      if (i == 4) load_w_codes(s + 2, rload, 0);
+      if (i == 6) issue_a1(s + 3, ahead, 1);
+    });
+    sub_step_s(fcur, 1, x, cur, h * 4 + 2, [&](int i) {
+      dec_slice(i, rdec, fnxt, d0, 0, 2, wd);
+      run_slice(i, rdec, 1, rb, d1);
+      if (i == 0) load_w_scale(s + 2, rload, 1);
+      if (i == 2) issue_a1(s + 3, ahead, 2);
+      if (i == 4) load_w_codes(s + 2, rload, 1);
+      if (i == 6) issue_a1(s + 3, ahead, 3);
+    });
+    __builtin_amdgcn_s_waitcnt(VMCNT);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    sub_step_s(fcur, 2, x, cur, h * 4 + 3, [&](int i) {
+      dec_slice(i, rdec, fnxt, d1, 1, 0, wd);
+      if (i == 2) issue_a1(s + 3, ahead, 4);
+      if (i == 6) issue_a1(s + 3, ahead, 5);
+    });
+    sub_step_s(fcur, 3, x, nxt, h * 4 + 0, [&](int i) {
+      dec_slice(i, rdec, fnxt, d1, 1, 2, wd);
+      run_slice(i, rload, 0, rb, d0);
+      if (i == 2) issue_a1(s + 3, ahead, 6);
+      if (i == 6) issue_a1(s + 3, ahead, 7);
+    });
+  };
+#define LORA4_FWD_BODY body_s
+#else
+#define LORA4_FWD_BODY body
+#endif
+
   const int all_steps = (int)((p.R + BKS - 1) / BKS);
   const int steps = is_split ? min(all_steps - sb, p.split_steps) : all_steps;
   WRaw r0, r1;
@@ -314,11 +477,12 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   for (int i = 0; i < 8; ++i) x[i] = lds_read_b128(stage(0) + swz(i * 32 + l32, h * 4));
   int s = 0, si = 0;   // si = s % 5
   for (; s + 2 <= steps; s += 2) {
-    body(s, stage(si), stage(si + 1), stage(si + 3), r1, r0, f0, f1, x, d0);
-    body(s + 1, stage(si + 1), stage(si + 2), stage(si + 4), r0, r1, f1, f0, x, d0);
+    LORA4_FWD_BODY(s, stage(si), stage(si + 1), stage(si + 3), r1, r0, f0, f1, x, d0);
+    LORA4_FWD_BODY(s + 1, stage(si + 1), stage(si + 2), stage(si + 4), r0, r1, f1, f0, x, d0);
     si = si + 2 >= STAGES ? si + 2 - STAGES : si + 2;
   }
-  if (s < steps) body(s, stage(si), stage(si + 1), stage(si + 3), r1, r0, f0, f1, x, d0);
+  if (s < steps) LORA4_FWD_BODY(s, stage(si), stage(si + 1), stage(si + 3), r1, r0, f0, f1, x, d0);
+#undef LORA4_FWD_BODY
   // the look-ahead loads past the end still write (zeros) into the ring
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
