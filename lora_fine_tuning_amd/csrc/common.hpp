@@ -59,6 +59,13 @@ __device__ __forceinline__ f32x16_t mfma_32x32x16(u32x4_t a, u32x4_t b, f32x16_t
                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// Pins a value to this point of the instruction stream: an empty volatile asm
+// that "redefines" it, so that work feeding it cannot sink below and work
+// using it cannot rise above (the hand-built schedules fence their slices
+// with it). No instruction is emitted.
+__device__ __forceinline__ void pin(uint32_t &v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void pin(float &v) { asm volatile("" : "+v"(v)); }
+
 // Transposing 64-bit LDS read (see the layout note above).
 // The pointer is declared restrict so that, once inlined, the read carries
 // alias-scope metadata: without it the compiler cannot tell the read from a

@@ -215,10 +215,8 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi_src, uint32_t lo_src, uint3
   return __builtin_amdgcn_perm(hi_src, lo_src, sel);
 }
 
-__device__ __forceinline__ RunTable make_table(float c, const Nf4Table &tab, uint32_t sel) {
-  uint32_t t[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) t[j] = pack_bf16x2(tab.q[2 * j] * c, tab.q[2 * j + 1] * c);
+// Byte planes of the table from its bf16 pairs t[j] = (T[2 j], T[2 j + 1]).
+__device__ __forceinline__ RunTable table_from(const uint32_t t[8], uint32_t sel) {
   RunTable r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -227,6 +225,13 @@ __device__ __forceinline__ RunTable make_table(float c, const Nf4Table &tab, uin
   }
   r.sel = sel;
   return r;
+}
+
+__device__ __forceinline__ RunTable make_table(float c, const Nf4Table &tab, uint32_t sel) {
+  uint32_t t[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) t[j] = pack_bf16x2(tab.q[2 * j] * c, tab.q[2 * j + 1] * c);
+  return table_from(t, sel);
 }
 
 // Second stage of make_table_pair (below), from this lane's four bf16 pairs

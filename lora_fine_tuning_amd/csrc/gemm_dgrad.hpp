@@ -37,6 +37,13 @@ using big::Params;
 using big::RunTable;
 using big::rsrc_t;
 
+#ifndef LORA4_DGRAD_SLICED
+#define LORA4_DGRAD_SLICED 1
+#endif
+#ifndef LORA4_SLICE_V1
+#define LORA4_SLICE_V1 5
+#endif
+
 constexpr int BM = 256, BN = 256, BKS = 64, THREADS = 256;
 constexpr int TILE_A = BM * BKS;    // dY stage [256][64], tile64 layout
 constexpr int TILE_W = BKS * BN;    // deq(W) tile [64][256]
@@ -248,6 +255,164 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
     __syncthreads();
   };
 
+#if LORA4_DGRAD_SLICED
+  // ---- the same step dealt out by hand over its 32 MFMA pairs (slice G =
+  // 8 kk + m = MFMAs of block row j = m / 2, columns 2 (m % 2) ..), fenced
+  // per pair: slices 0-3 build the NF4 table of run rdec, then its eight code
+  // words go through four stages each (unpack; low-index lookup; high-index
+  // lookup; interleave + LDS write), word w in slices 3 + 3 w .. 6 + 3 w; the
+  // dY chunks of step s+1 go out in slices 0-7 and the run of step s+2 in
+  // slices 8-10. At slice 28 every wave waits for its dY chunks and LDS writes
+  // and meets the others; the next step's first fragments are then read
+  // behind the last MFMAs of this one.
+  struct WordDec {
+    uint32_t i0, i1, L0, H0, L1, H1;
+  };
+  struct TabBuild {
+    float c;
+    float pr[16];
+    uint32_t t[8];
+  };
+  auto issue_a1 = [&](int s, uint16_t *As, int c) {
+    const int64_t k0 = (int64_t)s * BKS;
+    const bool edge = k0 + a_kq >= p.R;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (__attribute__((address_space(3))) void *)(As + (c * 4 + wave) * 512),
+                                             16, edge ? OOB : a_voff0 + c * a_cstep, (int)(k0 * 2), 0, 0);
+  };
+  // global loads of run s after the dY chunks: codes 0..3, codes 4..7, scales
+  constexpr int W_LOADS_D = FMT == FMT_NF4 ? 3 : 4;
+  auto load_w1 = [&](int s, WRaw &w, int part) {
+    const int wo = (int)(w_step * s);
+    const int so = (int)(s_step * s);
+    if (part == 0) {
+      w.c0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_voff0, wo, 0));
+    } else if (part == 1) {
+      w.c1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_voff1, wo, 0));
+    } else if constexpr (FMT == FMT_NF4) {
+      w.sc = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, s_voff, so, 0);
+    } else if constexpr (FMT == FMT_NF4_DQ) {
+      w.sc = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, s_voff, so, 0);
+      const int64_t idx = ((int64_t)s * BKS + lane) * sc_per_row + (kc >> 6);
+      w.c2 = __builtin_amdgcn_raw_buffer_load_b32(s2_rsrc, kc < p.Nc ? (uint32_t)((idx >> 8) * 4) : OOB, 0, 0);
+    } else {
+      const uint32_t e0 = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, s_voff, so, 0);
+      const uint32_t e1 = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, s_voff1, so, 0);
+      w.sc = e0 | (e1 << 8);
+    }
+  };
+  auto tab_stage = [&](int st, const WRaw &w, TabBuild &tb, RunTable &T, float &s0, float &s1) {
+    if constexpr (FMT == FMT_MXFP4) {
+      if (st == 0) {
+        s0 = e8m0_to_f32(w.sc & 0xFFu);
+        s1 = e8m0_to_f32((w.sc >> 8) & 0xFFu);
+      }
+    } else if (st == 0) {
+      if constexpr (FMT == FMT_NF4) tb.c = __builtin_bit_cast(float, w.sc);
+      else tb.c = e4m3_to_f32(w.sc & 0xFFu) * __builtin_bit_cast(float, w.c2);
+      pin(tb.c);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) tb.pr[k] = p.tab.q[k] * tb.c;
+    } else if (st == 1) {
+      pin(tb.c);
+#pragma unroll
+      for (int k = 8; k < 16; ++k) tb.pr[k] = p.tab.q[k] * tb.c;
+    } else if (st == 2) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) tb.t[k] = pack_bf16x2(tb.pr[2 * k], tb.pr[2 * k + 1]);
+    } else {
+      T = big::table_from(tb.t, sel);
+    }
+  };
+  auto word_stage = [&](int st, const WRaw &w, int q, WordDec &o, const RunTable &T, float s0, float s1,
+                        uint16_t *Bs) {
+    uint32_t code = q < 4 ? w.c0[q] : w.c1[q - 4];
+    if (st == 0) pin(code);
+    if constexpr (FMT == FMT_MXFP4) {
+      const float sc = q < 4 ? s0 : s1;
+      if (st == 0) {
+        o.L0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(code, sc, 0));
+        o.H0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(code, sc, 1));
+      } else if (st == 1) {
+        o.L1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(code, sc, 2));
+        o.H1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(code, sc, 3));
+      } else if (st == 3) {
+        lds_write_b128(Bs + wt_off(lane, wave * 64 + 8 * q), u32x4_t{o.L0, o.H0, o.L1, o.H1});
+      }
+    } else {
+      if (st == 0) {
+        const uint32_t ev = code & 0x0F0F0F0Fu;          // n0 n2 n4 n6
+        const uint32_t od = (code >> 4) & 0x0F0F0F0Fu;   // n1 n3 n5 n7
+        o.i0 = big::perm(od, ev, 0x05010400u);           // n0 n1 n2 n3
+        o.i1 = big::perm(od, ev, 0x07030602u);           // n4 n5 n6 n7
+        pin(o.i0);
+        pin(o.i1);
+      } else if (st == 1) {
+        big::lookup4(T, o.i0, o.L0, o.H0);
+      } else if (st == 2) {
+        big::lookup4(T, o.i1, o.L1, o.H1);
+      } else {
+        lds_write_b128(Bs + wt_off(lane, wave * 64 + 8 * q),
+                       u32x4_t{big::perm(o.H0, o.L0, 0x05010400u), big::perm(o.H0, o.L0, 0x07030602u),
+                               big::perm(o.H1, o.L1, 0x05010400u), big::perm(o.H1, o.L1, 0x07030602u)});
+      }
+    }
+  };
+  // wait for this wave's dY chunks (the run loads issued after them may stay
+  // in flight) and LDS accesses, then meet the other waves
+  constexpr int VM_D = W_LOADS_D;
+  constexpr int VMCNT_D = (VM_D & 15) | (7 << 4) | (0 << 8) | ((VM_D >> 4) << 14);
+  u32x4_t afa[4], afb[4], bf[4];
+  auto step_s = [&](int s, const uint16_t *Acur, const uint16_t *Bcur, uint16_t *Anxt, uint16_t *Bnxt,
+                    const WRaw &rdec, WRaw &rload) {
+    RunTable T;
+    float s0 = 0.0f, s1 = 0.0f;
+    TabBuild tb;
+    WordDec wd[2];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      u32x4_t *af = (kk & 1) ? afb : afa;
+      u32x4_t *afn = (kk & 1) ? afa : afb;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int G = kk * 8 + m;
+        const int j = m >> 1, i0 = (m & 1) * 2;
+        acc[j][i0] = mfma_32x32x16(bf[j], af[i0], acc[j][i0]);
+        acc[j][i0 + 1] = mfma_32x32x16(bf[j], af[i0 + 1], acc[j][i0 + 1]);
+        if (kk < 3) {
+          if (m < 4) afn[m] = lds_read_b128(Acur + swz(wm0 + m * 32 + l32, (kk + 1) * 2 + h));
+          if (m & 1) bf[j] = read_bf(Bcur, kk + 1, j);
+        } else if (m == 4) {
+          __builtin_amdgcn_s_waitcnt(VMCNT_D);
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_s_barrier();
+          asm volatile("" ::: "memory");
+          read_af(Anxt, 0, afa);
+          bf[0] = read_bf(Bnxt, 0, 0);
+          bf[1] = read_bf(Bnxt, 0, 1);
+        } else if (m == 5 || m == 7) {
+          bf[j] = read_bf(Bnxt, 0, j);
+        }
+        if (G < 4) tab_stage(G, rdec, tb, T, s0, s1);
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const int st = G - (3 + 3 * w);
+          if (st >= 0 && st < 4) word_stage(st, rdec, w, wd[w & 1], T, s0, s1, Bnxt);
+        }
+        if (G < 8) issue_a1(s + 1, Anxt, G);
+        else if (G < 11) load_w1(s + 2, rload, G - 8);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, LORA4_SLICE_V1, 0);    // VALU
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);                 // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);                 // LDS write
+        __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);                 // global load
+        __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);                // VALU
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+#endif
+
   const int steps = (int)((p.R + BKS - 1) / BKS);
   WRaw r0, r1;
   issue_a(0, As0, 0);
@@ -260,6 +425,23 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
     for (int part = 0; part < 4; ++part) decode_part(r0, Bs0, T, s0, s1, part);
   }
   load_w(1, r1);
+#if LORA4_DGRAD_SLICED
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  read_af(As0, 0, afa);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) bf[j] = read_bf(Bs0, 0, j);
+  int s = 0;
+  for (; s + 2 <= steps; s += 2) {
+    step_s(s, As0, Bs0, As1, Bs1, r1, r0);
+    step_s(s + 1, As1, Bs1, As0, Bs0, r0, r1);
+  }
+  if (s < steps) step_s(s, As0, Bs0, As1, Bs1, r1, r0);
+  // the look-ahead loads past the end still write (zeros) into the stages,
+  // and the last step's prefetch reads the stage the tail reuses
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+#else
   __syncthreads();
   int s = 0;
   for (; s + 2 <= steps; s += 2) {
@@ -268,6 +450,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
   }
   if (s < steps) body(s, As0, Bs0, As1, Bs1, r1, r0);
   // every look-ahead load has landed (the barrier waits for them)
+#endif
 
   // ---- rank-r tail: dZ A, plain bf16 steps through LDS -----------------------
   if (p.r2 > 0) {
