@@ -17,14 +17,13 @@
 //    (two stages of 256 x 64, swizzled), issued in the first half of step s;
 //  * the packed run of step s+2 is loaded into registers in sub-step 0 of
 //    step s, and the run of step s+1 (loaded a step earlier) is decoded into
-//    the other W tile in four parts, one per sub-step;
-//  * one barrier at the end of the step.
+//    the other W tile over the step;
+//  * one barrier, inside the last sub-step, after which the first operand
+//    fragments of step s+1 are read behind the last MFMAs of step s.
 // All look-ahead loads are issued unconditionally (past the end they are out
 // of range and return zeros); the main loop is unrolled twice so the two sets
-// of look-ahead registers swap roles instead of being copied. The schedule of
-// each 16-MFMA sub-step is pinned: fragment reads for the next sub-step, the
-// global loads, the decode VALU work and its LDS writes are threaded between
-// the MFMAs.
+// of look-ahead registers swap roles instead of being copied. The schedule is
+// built by hand, one slice of work per pair of MFMAs (see below).
 #pragma once
 
 #include "gemm_big.hpp"
@@ -37,11 +36,8 @@ using big::Params;
 using big::RunTable;
 using big::rsrc_t;
 
-#ifndef LORA4_DGRAD_SLICED
-#define LORA4_DGRAD_SLICED 1
-#endif
-#ifndef LORA4_SLICE_V1
-#define LORA4_SLICE_V1 5
+#ifndef LORA4_DGRAD_V1
+#define LORA4_DGRAD_V1 5
 #endif
 
 constexpr int BM = 256, BN = 256, BKS = 64, THREADS = 256;
@@ -240,23 +236,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
     }
   };
 
-  // step s on (Acur, Bcur): decodes step s+1 (rdec) into Bnxt, loads dY of
-  // step s+1 into Anxt and the run of step s+2 into rload; then waits for
-  // all of it and meets the other waves.
-  auto body = [&](int s, const uint16_t *Acur, const uint16_t *Bcur, uint16_t *Anxt, uint16_t *Bnxt,
-                  const WRaw &rdec, WRaw &rload) {
-    RunTable T;
-    float s0 = 0.0f, s1 = 0.0f;
-    compute_step(Acur, Bcur, [&](int kk) {
-      decode_part(rdec, Bnxt, T, s0, s1, kk);
-      if (kk == 0) load_w(s + 2, rload);
-      if (kk < 2) issue_a(s + 1, Anxt, kk);
-    });
-    __syncthreads();
-  };
-
-#if LORA4_DGRAD_SLICED
-  // ---- the same step dealt out by hand over its 32 MFMA pairs (slice G =
+  // ---- the step dealt out by hand over its 32 MFMA pairs (slice G =
   // 8 kk + m = MFMAs of block row j = m / 2, columns 2 (m % 2) ..), fenced
   // per pair: slices 0-3 build the NF4 table of run rdec, then its eight code
   // words go through four stages each (unpack; low-index lookup; high-index
@@ -401,7 +381,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
         if (G < 8) issue_a1(s + 1, Anxt, G);
         else if (G < 11) load_w1(s + 2, rload, G - 8);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, LORA4_SLICE_V1, 0);    // VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, LORA4_DGRAD_V1, 0);    // VALU
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);                 // LDS read
         __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);                 // LDS write
@@ -411,7 +391,6 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
       }
     }
   };
-#endif
 
   const int steps = (int)((p.R + BKS - 1) / BKS);
   WRaw r0, r1;
@@ -425,7 +404,6 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
     for (int part = 0; part < 4; ++part) decode_part(r0, Bs0, T, s0, s1, part);
   }
   load_w(1, r1);
-#if LORA4_DGRAD_SLICED
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   read_af(As0, 0, afa);
@@ -441,16 +419,6 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
   // and the last step's prefetch reads the stage the tail reuses
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-#else
-  __syncthreads();
-  int s = 0;
-  for (; s + 2 <= steps; s += 2) {
-    body(s, As0, Bs0, As1, Bs1, r1, r0);
-    body(s + 1, As1, Bs1, As0, Bs0, r0, r1);
-  }
-  if (s < steps) body(s, As0, Bs0, As1, Bs1, r1, r0);
-  // every look-ahead load has landed (the barrier waits for them)
-#endif
 
   // ---- rank-r tail: dZ A, plain bf16 steps through LDS -----------------------
   if (p.r2 > 0) {

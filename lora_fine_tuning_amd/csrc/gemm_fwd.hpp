@@ -27,7 +27,9 @@
 // (past the end they are out of range and return zeros), so the number of
 // loads in flight at each wait is a constant. The main loop is unrolled twice
 // so that the two sets of look-ahead registers swap roles instead of being
-// copied (a copy would wait for loads still in flight).
+// copied (a copy would wait for loads still in flight). The work between the
+// MFMAs (decode stages, table builds, global loads) is dealt to the MFMA pairs
+// by hand, one slice per pair, fenced so the compiler keeps it there.
 //
 // NF4 runs decode through a 16-entry bf16 table bf16(q[i] * c) selected with
 // v_perm_b32, MXFP4 through v_cvt_scalef32_pk_bf16_fp4; NF4-DQ rebuilds
@@ -44,9 +46,6 @@ using big::Params;
 using big::RunTable;
 using big::rsrc_t;
 
-#ifndef LORA4_FWD_SLICED
-#define LORA4_FWD_SLICED 1
-#endif
 #ifndef LORA4_SLICE_V1
 #define LORA4_SLICE_V1 5
 #endif
@@ -255,44 +254,6 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // step s: X of step s in stage cur (its chunk-0 fragments already in x),
-  // operands fcur. Over its four sub-steps it decodes step s+1 (rdec ->
-  // fnxt; d0 = row 0's decode state, built by the previous step), loads the W
-  // of step s+2 (rload) and the X of step s+3 (stage ahead), and builds row
-  // 0's decode state of step s+2 for the next step; after sub-step 1 it waits
-  // for the X of step s+1 and meets the other waves: stage nxt is then
-  // complete, and every wave is done with step s-1, whose stage step s+1
-  // refills.
-  auto body = [&](int s, const uint16_t *cur, const uint16_t *nxt, uint16_t *ahead, const WRaw &rdec, WRaw &rload,
-                  const WFrag &fcur, WFrag &fnxt, u32x4_t x[8], RunDec &d0) {
-    RunDec d1;
-    sub_step(fcur, 0, x, cur, h * 4 + 1, true, [&] {
-      decode_words(rdec, fnxt, d0, 0, 0);
-      load_w(s + 2, rload, 0);
-      issue_a(s + 3, ahead, 0);
-    });
-    sub_step(fcur, 1, x, cur, h * 4 + 2, true, [&] {
-      decode_words(rdec, fnxt, d0, 0, 2);
-      d1 = make_run(rdec, 1);
-      load_w(s + 2, rload, 1);
-      issue_a(s + 3, ahead, 1);
-    });
-    __builtin_amdgcn_s_waitcnt(VMCNT);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    sub_step(fcur, 2, x, cur, h * 4 + 3, true, [&] {
-      decode_words(rdec, fnxt, d1, 1, 0);
-      issue_a(s + 3, ahead, 2);
-    });
-    sub_step(fcur, 3, x, nxt, h * 4 + 0, true, [&] {
-      decode_words(rdec, fnxt, d1, 1, 2);
-      d0 = make_run(rload, 0);
-      issue_a(s + 3, ahead, 3);
-    });
-  };
-
-#if LORA4_FWD_SLICED
   // ---- the same step with its VALU and load work dealt out by hand: every
   // MFMA pair of a sub-step gets one slice (a stage of a code word's decode,
   // of a table build, or one global load), fenced so that nothing moves
@@ -443,10 +404,6 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
       if (i == 6) issue_a1(s + 3, ahead, 7);
     });
   };
-#define LORA4_FWD_BODY body_s
-#else
-#define LORA4_FWD_BODY body
-#endif
 
   const int all_steps = (int)((p.R + BKS - 1) / BKS);
   const int steps = is_split ? min(all_steps - sb, p.split_steps) : all_steps;
@@ -477,12 +434,11 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   for (int i = 0; i < 8; ++i) x[i] = lds_read_b128(stage(0) + swz(i * 32 + l32, h * 4));
   int s = 0, si = 0;   // si = s % 5
   for (; s + 2 <= steps; s += 2) {
-    LORA4_FWD_BODY(s, stage(si), stage(si + 1), stage(si + 3), r1, r0, f0, f1, x, d0);
-    LORA4_FWD_BODY(s + 1, stage(si + 1), stage(si + 2), stage(si + 4), r0, r1, f1, f0, x, d0);
+    body_s(s, stage(si), stage(si + 1), stage(si + 3), r1, r0, f0, f1, x, d0);
+    body_s(s + 1, stage(si + 1), stage(si + 2), stage(si + 4), r0, r1, f1, f0, x, d0);
     si = si + 2 >= STAGES ? si + 2 - STAGES : si + 2;
   }
-  if (s < steps) LORA4_FWD_BODY(s, stage(si), stage(si + 1), stage(si + 3), r1, r0, f0, f1, x, d0);
-#undef LORA4_FWD_BODY
+  if (s < steps) body_s(s, stage(si), stage(si + 1), stage(si + 3), r1, r0, f0, f1, x, d0);
   // the look-ahead loads past the end still write (zeros) into the ring
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
