@@ -79,18 +79,31 @@ typedef enum {
 /* The frozen 4-bit base W, logically [N = d_out, K = d_in] per group.
  *  format, block : LORA4_NF4 / LORA4_NF4_DQ with block 64, LORA4_MXFP4 with 32.
  *  N, K          : rows and columns of one group; K % block == 0, K >= block.
- *  groups        : 1 for a plain linear; E for E experts stored back to back.
- *  codes         : uint8 [groups][N][K/2]; byte j of a row holds element 2j
- *                  in its low nibble and element 2j+1 in its high nibble.
- *  scales        : NF4    : float [groups][N][K/64]
- *                  NF4_DQ : uint8 E4M3 codes [groups][N][K/64]
- *                  MXFP4  : uint8 E8M0 codes [groups][N][K/32] (value 2^(E-127))
+ *  groups        : 1 for a plain linear; E for E experts stored back to back,
+ *                  each taking lora4_packed_bytes(format, N, K, part) bytes
+ *                  of codes (part 0), scales (1) and scales2 (2).
+ * Each group's [N, K] is stored in tiles of 64 rows by 64 elements: RB =
+ * ceil(N/64) row blocks, KB = ceil(K/64) k blocks, tile (rb, kb) is tile
+ * number t = rb*KB + kb; row i of a tile is row 64*rb + i of W, element j of
+ * it is element 64*kb + j. Rows past N and elements past K are zero padding.
+ *  codes         : uint8, 2048 bytes per tile at 2048*t; row i at 32*i; byte
+ *                  j of a row holds element 2j in its low nibble and element
+ *                  2j+1 in its high nibble.
+ *  scales        : NF4    : float, 64 per tile at 64*t; entry i = the scale of
+ *                           row i's 64 elements
+ *                  NF4_DQ : uint8 E4M3 codes, 64 per tile at 64*t, as NF4
+ *                  MXFP4  : uint8 E8M0 codes (value 2^(E-127)), 128 per tile
+ *                           at 128*t; entry 2i+h = the scale of elements
+ *                           32h .. 32h+31 of row i
  *  scales2       : NF4_DQ only: float [groups][ceil(N*K/64 / 256)], the
  *                  second-level scale of each run of 256 consecutive
- *                  first-level scales of one group (row-major order); the
- *                  rebuilt scale is fp32(E4M3(code) * scales2). NULL otherwise.
+ *                  first-level scales of one group, counted in row-major
+ *                  order (row n, block b: n*(K/64) + b); the rebuilt scale
+ *                  is fp32(E4M3(code) * scales2). NULL otherwise.
  * The dequantized element is bf16(fp32(q[code] * scale)) for NF4 (q the
- * 16-level NF4 codebook) and bf16(e2m1(code) * 2^(E-127)) for MXFP4.
+ * 16-level NF4 codebook) and bf16(e2m1(code) * 2^(E-127)) for MXFP4. The
+ * tiles let every global load of codes in the GEMMs cover whole contiguous
+ * rows of a tile (the kernels read one tile per wave and step).
  */
 typedef struct lora4_W {
   int32_t format;
@@ -102,6 +115,11 @@ typedef struct lora4_W {
   const void *scales;
   const float *scales2;
 } lora4_W;
+
+/* Bytes of one packed [N, K] matrix (one group) in format: part 0 the codes,
+ * 1 the first-level scales, 2 the NF4-DQ second-level scales (0 for the
+ * other formats). Returns 0 for invalid arguments. */
+size_t lora4_packed_bytes(int32_t format, int64_t N, int64_t K, int32_t part);
 
 /* Workspace (bytes) that lora4_forward (which = 0) or lora4_backward
  * (which = 1) needs for this W, M tokens and rank r. Returns 0 for invalid
@@ -148,11 +166,13 @@ lora4_status lora4_backward(const lora4_W *W, const uint16_t *X, const uint16_t 
  * scales ("Training LLMs on a Budget", section 3, tricks 1 and 2): code = the
  * NF4 level nearest to fp32(w / absmax), ties to the lower level; an
  * all-zero block encodes as the zero level.
- *  double_quant == 0: codes uint8 [N][K/2], scales float [N][K/64], scales2 unused.
+ *  double_quant == 0: codes and float scales in the tiled layout of lora4_W,
+ *    scales2 unused.
  *  double_quant != 0: codes as above; scales receives uint8 E4M3 codes
- *    [N][K/64] of scale / group max (nearest, ties to even); scales2 receives
+ *    (tiled) of scale / group max (nearest, ties to even); scales2 receives
  *    float [ceil(N*K/64/256)] group maxima (a group's code is 0 if its max is 0).
- * Codes are always chosen with the exact fp32 scale. */
+ * Codes are always chosen with the exact fp32 scale. Buffer sizes:
+ * lora4_packed_bytes(format, N, K, 0..2); the padding is written as zero. */
 lora4_status quant_pack_nf4(const uint16_t *W_bf16, int64_t N, int64_t K, int32_t double_quant,
                             uint8_t *codes, void *scales, float *scales2, void *stream);
 
@@ -161,7 +181,9 @@ lora4_status quant_pack_nf4(const uint16_t *W_bf16, int64_t N, int64_t K, int32_
  * E = clamp(floor(log2 amax) - 2, -127, 127) + 127 (E = 0 for an all-zero
  * block), and each element's E2M1 code is the nearest value to w * 2^-(E-127),
  * ties to the even code, saturating at +-6, sign copied from w.
- *  codes : uint8 [N][K/2]; scales_e8m0 : uint8 [N][K/32]. */
+ *  codes, scales_e8m0 : the tiled layout of lora4_W, sized by
+ *  lora4_packed_bytes(LORA4_MXFP4, N, K, 0 / 1); the padding is written as
+ *  zero (E8M0 padding code 0). */
 lora4_status quant_pack_mxfp4(const uint16_t *W_bf16, int64_t N, int64_t K,
                               uint8_t *codes, uint8_t *scales_e8m0, void *stream);
 

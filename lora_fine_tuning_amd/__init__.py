@@ -8,7 +8,7 @@ every call raises; there is no fallback.
 
 Low-level functions carry the ABI's names and signatures (pointers as ints):
 ``lora4_forward``, ``lora4_backward``, ``lora4_workspace_bytes``,
-``quant_pack_nf4``, ``quant_pack_mxfp4``. The torch-level helpers ``pack_nf4``,
+``lora4_packed_bytes``, ``quant_pack_nf4``, ``quant_pack_mxfp4``. The torch-level helpers ``pack_nf4``,
 ``pack_mxfp4``, ``forward`` and ``backward`` allocate outputs with torch and call
 them.
 """
@@ -25,7 +25,7 @@ LORA4_NF4, LORA4_NF4_DQ, LORA4_MXFP4 = 1, 2, 3
 FORMATS = {"nf4": LORA4_NF4, "nf4_dq": LORA4_NF4_DQ, "mxfp4": LORA4_MXFP4}
 BLOCK = {LORA4_NF4: 64, LORA4_NF4_DQ: 64, LORA4_MXFP4: 32}
 
-EXPORTS = ["lora4_forward", "lora4_backward", "lora4_workspace_bytes", "quant_pack_nf4",
+EXPORTS = ["lora4_forward", "lora4_backward", "lora4_workspace_bytes", "lora4_packed_bytes", "quant_pack_nf4",
            "quant_pack_mxfp4", "lora4_status_string", "lora4_timing_enable", "lora4_timing_collect",
            "lora4_version"]
 
@@ -64,6 +64,8 @@ def lib():
         L.lora4_backward.restype = ctypes.c_int
         L.lora4_workspace_bytes.argtypes = [ctypes.c_int, Wp, i64, i32]
         L.lora4_workspace_bytes.restype = sz
+        L.lora4_packed_bytes.argtypes = [i32, i64, i64, i32]
+        L.lora4_packed_bytes.restype = sz
         L.quant_pack_nf4.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp]
         L.quant_pack_nf4.restype = ctypes.c_int
         L.quant_pack_mxfp4.argtypes = [vp, i64, i64, vp, vp, vp]
@@ -94,6 +96,10 @@ def _check(status, what):
 
 def lora4_workspace_bytes(which, W, M, r):
     return lib().lora4_workspace_bytes(which, ctypes.byref(W), M, r)
+
+
+def lora4_packed_bytes(fmt, N, K, part):
+    return lib().lora4_packed_bytes(fmt, N, K, part)
 
 
 def lora4_forward(W, X, M, A, B, r, s, group_offsets, Y, Z, Y_base, Y_lora, workspace, workspace_bytes,
@@ -148,13 +154,14 @@ def _stream():
 
 @dataclass
 class PackedBase:
-    """A frozen 4-bit base on the device, [groups][N][K] logically."""
+    """A frozen 4-bit base on the device, [groups][N][K] logically, stored in
+    the library's 64 x 64 tiles (include/lora4.h, lora4_W)."""
     fmt: int
     N: int
     K: int
     groups: int
-    codes: "object"            # torch uint8 [groups, N, K/2]
-    scales: "object"           # float32 or uint8 [groups, N, K/block]
+    codes: "object"            # torch uint8 [groups, packed_bytes(part 0)]
+    scales: "object"           # float32 or uint8 [groups, scale entries]
     scales2: Optional["object"] = None
 
     def abi(self):
@@ -168,19 +175,22 @@ def pack_nf4(W, double_quant=False):
     Ws = W if W.dim() == 3 else W.unsqueeze(0)
     E, N, K = Ws.shape
     dev = W.device
-    codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device=dev)
+    fmt = LORA4_NF4_DQ if double_quant else LORA4_NF4
+    sizes = [lora4_packed_bytes(fmt, N, K, part) for part in range(3)]
+    if sizes[0] == 0:
+        raise ValueError("invalid shape for NF4 packing")
+    codes = torch.empty((E, sizes[0]), dtype=torch.uint8, device=dev)
     if double_quant:
-        scales = torch.empty((E, N, K // 64), dtype=torch.uint8, device=dev)
-        ng = -(-(N * K // 64) // 256)
-        scales2 = torch.empty((E, ng), dtype=torch.float32, device=dev)
+        scales = torch.empty((E, sizes[1]), dtype=torch.uint8, device=dev)
+        scales2 = torch.empty((E, sizes[2] // 4), dtype=torch.float32, device=dev)
     else:
-        scales = torch.empty((E, N, K // 64), dtype=torch.float32, device=dev)
+        scales = torch.empty((E, sizes[1] // 4), dtype=torch.float32, device=dev)
         scales2 = None
     for e in range(E):
         st = quant_pack_nf4(_ptr(Ws[e]), N, K, 1 if double_quant else 0, _ptr(codes[e]), _ptr(scales[e]),
                             _ptr(scales2[e]) if double_quant else None, _stream())
         _check(st, "quant_pack_nf4")
-    return PackedBase(LORA4_NF4_DQ if double_quant else LORA4_NF4, N, K, E, codes, scales, scales2)
+    return PackedBase(fmt, N, K, E, codes, scales, scales2)
 
 
 def pack_mxfp4(W):
@@ -189,8 +199,11 @@ def pack_mxfp4(W):
     Ws = W if W.dim() == 3 else W.unsqueeze(0)
     E, N, K = Ws.shape
     dev = W.device
-    codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device=dev)
-    scales = torch.empty((E, N, K // 32), dtype=torch.uint8, device=dev)
+    sizes = [lora4_packed_bytes(LORA4_MXFP4, N, K, part) for part in range(2)]
+    if sizes[0] == 0:
+        raise ValueError("invalid shape for MXFP4 packing")
+    codes = torch.empty((E, sizes[0]), dtype=torch.uint8, device=dev)
+    scales = torch.empty((E, sizes[1]), dtype=torch.uint8, device=dev)
     for e in range(E):
         _check(quant_pack_mxfp4(_ptr(Ws[e]), N, K, _ptr(codes[e]), _ptr(scales[e]), _stream()),
                "quant_pack_mxfp4")

@@ -91,13 +91,37 @@ __device__ __forceinline__ void dequant32_mxfp4(u32x4_t codes, float scale, uint
   }
 }
 
+// Storage of a packed base: each group's [N, K] is cut into tiles of 64 rows
+// by 64 elements (RB = ceil(N / 64) row blocks, KB = ceil(K / 64) k blocks;
+// tile (rb, kb) is number rb KB + kb). A tile's codes are 2048 contiguous
+// bytes, 32 per row (byte j: elements 2j, 2j+1 of the block in its low and
+// high nibble); its scales are 64 contiguous entries (one per row, NF4 and
+// NF4-DQ) or 128 (two per row, MXFP4). Rows past N and elements past K are
+// zero. One step of either GEMM reads one tile per wave, so every global load
+// of codes covers whole contiguous rows of a tile.
+__host__ __device__ constexpr int64_t w_blocks(int64_t x) { return (x + 63) >> 6; }
+
+// byte of the codes holding elements k, k + 1 (k even) of row n
+__host__ __device__ constexpr int64_t w_code_off(int64_t KB, int64_t n, int64_t k) {
+  return (((n >> 6) * KB + (k >> 6)) << 11) + ((n & 63) << 5) + ((k & 63) >> 1);
+}
+// scale entry of the 64-element block of (n, k) (NF4, NF4-DQ)
+__host__ __device__ constexpr int64_t w_scale64_idx(int64_t KB, int64_t n, int64_t k) {
+  return (((n >> 6) * KB + (k >> 6)) << 6) + (n & 63);
+}
+// scale entry of the 32-element block of (n, k) (MXFP4)
+__host__ __device__ constexpr int64_t w_scale32_idx(int64_t KB, int64_t n, int64_t k) {
+  return (((n >> 6) * KB + (k >> 6)) << 7) + ((n & 63) << 1) + ((k >> 5) & 1);
+}
+
 // A packed base W as the kernels see it (one group; the kernels add the
 // group offsets).
 struct PackedW {
-  const uint8_t *codes;   // [groups][N][K/2]
-  const void *scales;     // fp32 (NF4), e4m3 u8 (NF4_DQ), e8m0 u8 (MXFP4)
+  const uint8_t *codes;   // [groups][RB KB tiles][64][32]
+  const void *scales;     // fp32 (NF4), e4m3 u8 (NF4_DQ), e8m0 u8 (MXFP4), tiled
   const float *scales2;   // NF4_DQ second level, [groups][ceil(N*K/64/256)]
   int64_t N, K;
+  int64_t KB;             // k blocks of 64
   int64_t g_codes;        // bytes per group
   int64_t g_scales;       // scale entries per group
   int64_t g_scales2;      // second-level entries per group
@@ -109,15 +133,16 @@ template <int FMT>
 __device__ __forceinline__ float block_scale(const PackedW &w, int g, int64_t n, int64_t k) {
   if constexpr (FMT == FMT_NF4) {
     const float *s = reinterpret_cast<const float *>(w.scales) + g * w.g_scales;
-    return s[n * (w.K >> 6) + (k >> 6)];
+    return s[w_scale64_idx(w.KB, n, k)];
   } else if constexpr (FMT == FMT_NF4_DQ) {
     const uint8_t *s = reinterpret_cast<const uint8_t *>(w.scales) + g * w.g_scales;
-    int64_t idx = n * (w.K >> 6) + (k >> 6);
+    // the second-level groups run over the scales in row-major order
+    const int64_t idx = n * (w.K >> 6) + (k >> 6);
     float c2 = w.scales2[g * w.g_scales2 + (idx >> 8)];
-    return e4m3_to_f32(s[idx]) * c2;
+    return e4m3_to_f32(s[w_scale64_idx(w.KB, n, k)]) * c2;
   } else {
     const uint8_t *s = reinterpret_cast<const uint8_t *>(w.scales) + g * w.g_scales;
-    return e8m0_to_f32(s[n * (w.K >> 5) + (k >> 5)]);
+    return e8m0_to_f32(s[w_scale32_idx(w.KB, n, k)]);
   }
 }
 
@@ -125,7 +150,7 @@ __device__ __forceinline__ float block_scale(const PackedW &w, int g, int64_t n,
 template <int FMT>
 __device__ __forceinline__ void dequant_row32(const PackedW &w, int g, int64_t n, int64_t k,
                                               const float *qlds, uint32_t out[16]) {
-  const uint8_t *src = w.codes + g * w.g_codes + n * (w.K >> 1) + (k >> 1);
+  const uint8_t *src = w.codes + g * w.g_codes + w_code_off(w.KB, n, k);
   u32x4_t codes = ldg_b128_cached(src);
   float sc = block_scale<FMT>(w, g, n, k);
   if constexpr (FMT == FMT_MXFP4) {

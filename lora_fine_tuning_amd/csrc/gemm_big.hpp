@@ -1,33 +1,9 @@
-// Large-tile dequant-GEMM for the two dense contractions of the layer:
-//
-//   NT (forward): Y[M, N]  = X[M, K]  . deq(W)[N, K]^T  (+ (s Z) B^T tail)
-//   NN (dgrad):   dX[M, K] = dY[M, N] . deq(W)[N, K]    (+ dZ A tail)
-//
-// One workgroup = 256 threads = 4 waves (2 x 2) computing a 256 x 256 output
-// tile; each wave owns 128 x 128 (4 x 4 MFMA 32x32x16 tiles, 256 fp32
-// accumulators per lane, held in the accumulation registers). The reduction
-// advances 64 per step through two LDS buffers, one barrier per step.
-//
-// Data movement per step:
-//  * the activation slab (256 rows x 64) goes from HBM/L2 straight into LDS
-//    with buffer_load_dwordx4 ... lds (no staging registers); the buffer
-//    descriptor's range check zero-fills rows past the tile's group and
-//    columns past the reduction length;
-//  * each thread loads one 64-element run of packed W (32 bytes + its scale)
-//    into registers two steps ahead and dequantizes it into the other LDS
-//    buffer while the MFMAs of the current step run;
-//  * NT keeps deq(W) K-contiguous; NN keeps it as it lies in memory (rows =
-//    reduction index) and feeds the MFMA with ds_read_b64_tr_b16.
-//
-// LDS layout of K-contiguous 256 x 64 tiles: rows of 128 bytes, the eight
-// 16-byte chunks of row r stored at chunk position (chunk ^ (r & 7)), so the
-// MFMA operand reads of 8 consecutive rows hit 8 different bank groups.
-//
-// NF4 runs are decoded through a 16-entry bf16 table bf16(q[i] * c) selected
-// with v_perm_b32 (bit-identical to bf16(fp32(q[code] * c)) per element);
-// MXFP4 uses v_cvt_scalef32_pk_bf16_fp4. The MFMA operands are swapped
-// (deq(W) first) so each lane holds four consecutive output columns of one
-// row, stored as one 8-byte write.
+// Shared pieces of the two 256 x 256 dequant-GEMMs (gemm_fwd.hpp,
+// gemm_dgrad.hpp): their parameter block, buffer descriptors for bounds-checked
+// loads, the NF4 run tables (16-entry bf16 tables bf16(q[i] c) whose byte
+// planes are selected with v_perm_b32, bit-identical to bf16(fp32(q[code] c))
+// per element), the MXFP4 decode through v_cvt_scalef32_pk_bf16_fp4, and the
+// rank-r tail operand taken from fp32 range partials.
 #pragma once
 
 #include "formats.hpp"
@@ -42,17 +18,9 @@
 namespace lora4 {
 namespace big {
 
-constexpr int BM = 256, BN = 256, BKS = 64;
-constexpr int THREADS = 256;
-constexpr int TILE64 = BM * BKS;        // 256 x 64 bf16, unpadded (swizzled)
-constexpr int LDB_NN = BN + 16;         // NN: W~ tile [64][272]
-constexpr int B_ELEMS_NN = BKS * LDB_NN;
+constexpr int BM = 256, BN = 256, BKS = 64;   // tile of both GEMMs
 constexpr uint32_t RSRC_WORD3 = 0x00020000u;   // raw 32-bit buffer, gfx9 family
 constexpr uint32_t OOB = 0x80000000u;           // an offset past any range
-
-__host__ __device__ constexpr int lds_bytes(int mode) {
-  return 2 * (TILE64 + (mode == 0 ? TILE64 : B_ELEMS_NN)) * 2;
-}
 
 struct Params {
   Mat A;              // [M, R] activations (absolute rows), ld % 8 == 0
@@ -190,8 +158,6 @@ __device__ __forceinline__ uint32_t clamp_bytes(int64_t b) {
   return b <= 0 ? 0u : (b >= (int64_t)0x7FFFFFFF ? 0x7FFFFFFFu : (uint32_t)b);
 }
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BKS + ((chunk ^ (row & 7)) << 3); }
-
 // ---------------------------------------------------------------------------
 // NF4 dequant through a per-run bf16 table and byte permutes
 // ---------------------------------------------------------------------------
@@ -300,379 +266,6 @@ __device__ __forceinline__ u32x4_t decode8_mxfp4(uint32_t c, float s) {
                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, s, 3))};
 }
 
-// MFMA 32x32x16 operand from a column-contiguous LDS tile (rows = reduction):
-// lane l gets column c0 + l % 32 of reduction rows k0 + 8 (l / 32) .. +7,
-// built from two transposing reads per 16-lane group.
-__device__ __forceinline__ u32x4_t frag_tr32(const uint16_t *lds, int ldr, int k0, int c0, int lane) {
-  const int grp = lane >> 4, j = lane & 15;
-  const uint16_t *p = lds + (k0 + (grp >> 1) * 8 + (j >> 2)) * ldr + c0 + (grp & 1) * 16 + (j & 3) * 4;
-  u32x2_t lo = lds_read_tr16(p);
-  u32x2_t hi = lds_read_tr16(p + 4 * ldr);
-  return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-}
-
-// ---------------------------------------------------------------------------
-// The kernel
-// ---------------------------------------------------------------------------
-
-template <int MODE, int FMT>
-__global__ __launch_bounds__(THREADS, 1) void k_gemm_big(Params p) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  const uint32_t sel = sel_base();
-  constexpr int B_ELEMS = MODE == 0 ? TILE64 : B_ELEMS_NN;
-  uint16_t *const As0 = smem, *const As1 = smem + TILE64;
-  uint16_t *const Bs0 = smem + 2 * TILE64, *const Bs1 = smem + 2 * TILE64 + B_ELEMS;
-
-  // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs; renumber
-  // so that each XCD walks a contiguous range of tiles (shared operands in
-  // its own L2).
-  int b = blockIdx.x;
-  {
-    const int per = p.nblocks >> 3;
-    if (b < per * 8) b = (b & 7) * per + (b >> 3);
-  }
-  const int tn = b % p.tiles_n;
-  const int slot = b / p.tiles_n;
-  const RowTile rt = map_row_tile(slot, BM, p.offsets, p.groups, p.M);
-  if (rt.group < 0) return;
-  const int g = rt.group;
-  const int64_t row0 = rt.row0, row_end = rt.row_end;
-  const int64_t col0 = (int64_t)tn * BN;
-
-  const int t = threadIdx.x;
-  const int wave = t >> 6, lane = t & 63;
-  const int wm0 = (wave & 1) * 128, wn0 = (wave >> 1) * 128;
-
-  // ---- activation slab: direct HBM/L2 -> LDS --------------------------------
-  // wave w, chunk c covers tile rows 8 (4 c + w) .. +7; lane l: row + l / 8,
-  // stored chunk l % 8 which holds logical chunk (l % 8) ^ (row % 8).
-  const rsrc_t a_rsrc = make_rsrc(p.A.p + row0 * p.A.ld, clamp_bytes((row_end - row0) * p.A.ld * 2));
-  uint32_t a_voff[8];
-  int a_kq = ((lane & 7) ^ ((lane >> 3) & 7)) * 8;   // logical column of this lane's chunk
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int row = (c * 4 + wave) * 8 + (lane >> 3);
-    a_voff[c] = (uint32_t)((row * p.A.ld + a_kq) * 2);
-  }
-  auto issue_a = [&](int s, uint16_t *As) {
-    const int64_t k0 = (int64_t)s * BKS;
-    const bool edge = k0 + a_kq >= p.R;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (__attribute__((address_space(3))) void *)(As + (c * 4 + wave) * 512),
-                                               16, edge ? OOB : a_voff[c], (int)(k0 * 2), 0, 0);
-    }
-  };
-
-  // ---- packed W run of this thread ---------------------------------------------
-  // NT: row n = col0 + t, elements k0 .. k0+63 of step s.
-  // NN: reduction row n = k0 + t / 4, output columns col0 + 64 (t % 4) .. +63.
-  const int64_t Kw = p.W.K;
-  const uint8_t *codes_g = p.W.codes + g * p.W.g_codes;
-  rsrc_t w_rsrc, s_rsrc;
-  uint32_t w_voff[2], s_voff;
-  int64_t w_step, s_step;          // byte advance per step (NT: along K; NN: 64 rows)
-  if constexpr (MODE == 0) {
-    const int64_t rows = p.Nc - col0;
-    w_rsrc = make_rsrc(codes_g + col0 * (Kw >> 1), clamp_bytes(rows * (Kw >> 1)));
-    w_voff[0] = (uint32_t)(t * (Kw >> 1));
-    w_voff[1] = w_voff[0] + 16;
-    w_step = BKS / 2;
-  } else {
-    w_rsrc = make_rsrc(codes_g, clamp_bytes(p.W.N * (Kw >> 1)));
-    const int64_t kc = col0 + (t & 3) * 64;
-    const uint32_t base = (uint32_t)((t >> 2) * (Kw >> 1) + (kc >> 1));
-    w_voff[0] = kc < p.Nc ? base : OOB;
-    w_voff[1] = kc + 32 < p.Nc ? base + 16 : OOB;
-    w_step = (int64_t)BKS * (Kw >> 1);
-  }
-  // scales: NF4 fp32 / NF4_DQ e4m3 byte / MXFP4 two e8m0 bytes per run
-  const int sc_per_row = FMT == FMT_MXFP4 ? (int)(Kw >> 5) : (int)(Kw >> 6);
-  const int sc_bytes = FMT == FMT_NF4 ? 4 : 1;
-  {
-    const uint8_t *sb = reinterpret_cast<const uint8_t *>(p.W.scales) + (g * p.W.g_scales) * sc_bytes;
-    if constexpr (MODE == 0) {
-      const int64_t rows = p.Nc - col0;
-      s_rsrc = make_rsrc(sb + col0 * sc_per_row * sc_bytes, clamp_bytes(rows * sc_per_row * sc_bytes));
-      s_voff = (uint32_t)(t * sc_per_row * sc_bytes);
-      s_step = (FMT == FMT_MXFP4 ? 2 : 1) * sc_bytes;
-    } else {
-      s_rsrc = make_rsrc(sb, clamp_bytes(p.W.N * sc_per_row * sc_bytes));
-      const int64_t kc = col0 + (t & 3) * 64;
-      const int64_t blk = FMT == FMT_MXFP4 ? (kc >> 5) : (kc >> 6);
-      s_voff = kc < p.Nc ? (uint32_t)(((t >> 2) * sc_per_row + blk) * sc_bytes) : OOB;
-      s_step = (int64_t)BKS * sc_per_row * sc_bytes;
-    }
-  }
-  const float *scales2_g = FMT == FMT_NF4_DQ ? p.W.scales2 + g * p.W.g_scales2 : nullptr;
-
-  struct WR {
-    u32x4_t c0, c1;
-    uint32_t sc;       // raw scale bits (fp32 bits, or e4m3 / e8m0 codes)
-    float c2;          // DQ second level
-  };
-  auto load_w = [&](int s, WR &w) {
-    const int wo = (int)(w_step * s);
-    // NT runs run along K: the second half of the last run lies past the row
-    // when K % 64 == 32 (MXFP4), so it is masked rather than read from the
-    // next row. NN masks its column halves once, in w_voff.
-    const bool h1 = MODE == 1 || (int64_t)s * BKS + 32 < p.R;
-    w.c0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_voff[0], wo, 0));
-    w.c1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, h1 ? w_voff[1] : OOB, wo, 0));
-    const int so = (int)(s_step * s);
-    if constexpr (FMT == FMT_NF4) {
-      w.sc = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, s_voff, so, 0);
-    } else if constexpr (FMT == FMT_NF4_DQ) {
-      w.sc = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, s_voff, so, 0);
-      int64_t idx;
-      if constexpr (MODE == 0)
-        idx = (col0 + t) * sc_per_row + (int64_t)s;
-      else
-        idx = ((int64_t)s * BKS + (t >> 2)) * sc_per_row + ((col0 + (t & 3) * 64) >> 6);
-      const int64_t ng = p.W.g_scales2;
-      const int64_t gi = idx >> 8;
-      w.c2 = gi < ng ? scales2_g[gi] : 0.0f;
-    } else {
-      // two E8M0 codes, loaded one byte at a time so that a range check on
-      // the second never discards the first
-      const bool s1 = MODE == 0 ? h1 : (col0 + (t & 3) * 64 + 32 < p.Nc);
-      const uint32_t e0 = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, s_voff, so, 0);
-      const uint32_t e1 = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, s1 ? s_voff + 1 : OOB, so, 0);
-      w.sc = e0 | (e1 << 8);
-    }
-  };
-
-  // Dequantize the run in w into B tile Bs, chunks [2 part, 2 part + 2) of 8:
-  // called in four parts between the MFMA sub-steps so the VALU work
-  // overlaps the matrix cores.
-  auto dequant_part = [&](const WR &w, const RunTable &T, float s0, float s1, uint16_t *Bs, int part) {
-    uint16_t *dst = MODE == 0 ? Bs : Bs + (t >> 2) * LDB_NN + (t & 3) * 64;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int q = 2 * part + h;
-      const uint32_t code = q < 4 ? w.c0[q] : w.c1[q - 4];
-      u32x4_t v;
-      if constexpr (FMT == FMT_MXFP4)
-        v = decode8_mxfp4(code, q < 4 ? s0 : s1);
-      else
-        v = decode8_nf4(T, code);
-      if constexpr (MODE == 0)
-        lds_write_b128(dst + swz(t, q), v);
-      else
-        lds_write_b128(dst + 8 * q, v);
-    }
-  };
-  auto run_setup = [&](const WR &w, RunTable &T, float &s0, float &s1) {
-    if constexpr (FMT == FMT_MXFP4) {
-      s0 = e8m0_to_f32(w.sc & 0xFFu);
-      s1 = e8m0_to_f32((w.sc >> 8) & 0xFFu);
-    } else {
-      float c;
-      if constexpr (FMT == FMT_NF4) c = __builtin_bit_cast(float, w.sc);
-      else c = e4m3_to_f32(w.sc & 0xFFu) * w.c2;
-      T = make_table(c, p.tab, sel);
-      s0 = s1 = 0.0f;
-    }
-  };
-  auto dequant_store = [&](const WR &w, uint16_t *Bs) {
-    RunTable T;
-    float s0, s1;
-    run_setup(w, T, s0, s1);
-#pragma unroll
-    for (int part = 0; part < 4; ++part) dequant_part(w, T, s0, s1, Bs, part);
-  };
-
-  // acc[j][i]: 32 x 32 block (n-block j, m-block i) of this wave's 128 x 128
-  f32x16_t acc[4][4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[j][i] = f32x16_t{};
-
-  // One 64-deep step of MFMAs on tiles (As, Bs). The operand reads are
-  // software-pipelined: the next B fragment, and at the start of each
-  // 16-deep sub-step the next sub-step's A fragments, are requested before
-  // the current MFMAs issue, so LDS latency overlaps the matrix cores.
-  // hook(kk) runs after sub-step kk's MFMAs (used to interleave dequant).
-  auto load_af = [&](const uint16_t *As, int kk, u32x4_t af[4]) {
-    const int q = kk * 2 + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) af[i] = lds_read_b128(As + swz(wm0 + i * 32 + (lane & 31), q));
-  };
-  auto load_bf = [&](const uint16_t *Bs, int kk, int j) -> u32x4_t {
-    if constexpr (MODE == 0)
-      return lds_read_b128(Bs + swz(wn0 + j * 32 + (lane & 31), kk * 2 + (lane >> 5)));
-    else
-      return frag_tr32(Bs, LDB_NN, kk * 16, wn0 + j * 32, lane);
-  };
-  auto compute_step = [&](const uint16_t *As, const uint16_t *Bs, auto &&hook) {
-    u32x4_t af0[4], af1[4];
-    load_af(As, 0, af0);
-    u32x4_t bcur = load_bf(Bs, 0, 0);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      u32x4_t *af = (kk & 1) ? af1 : af0;
-      u32x4_t *afn = (kk & 1) ? af0 : af1;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x4_t bnext = bcur;
-        if (j < 3)
-          bnext = load_bf(Bs, kk, j + 1);
-        else if (kk < 3)
-          bnext = load_bf(Bs, kk + 1, 0);
-        if (j == 0 && kk < 3) load_af(As, kk + 1, afn);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[j][i] = mfma_32x32x16(bcur, af[i], acc[j][i]);
-        bcur = bnext;
-      }
-      hook(kk);
-#if LORA4_SCHED_INTERLEAVE
-      // ask the scheduler to thread the hook's VALU work between this
-      // sub-step's 16 MFMAs (each MFMA leaves the VALU free for a while)
-#pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, LORA4_SCHED_VALU, 0);   // VALU
-      }
-#endif
-    }
-  };
-  auto compute = [&](const uint16_t *As, const uint16_t *Bs) {
-    compute_step(As, Bs, [](int) {});
-  };
-
-  const int steps = (int)((p.R + BKS - 1) / BKS);
-  WR wa, wb;   // W registers for steps s+1 (wa) and s+2 (wb)
-  if (steps > 0) {
-    issue_a(0, As0);
-    load_w(0, wa);
-    dequant_store(wa, Bs0);
-    if (steps > 1) load_w(1, wa);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  // loads in flight per thread from one load_w (codes + scale bytes)
-  constexpr int W_LOADS = FMT == FMT_NF4 ? 3 : 4;
-  // s_waitcnt that waits until at most W_LOADS vector-memory loads are
-  // outstanding: the direct LDS loads of the next step, issued before
-  // load_w, have then landed, while the W loads two steps ahead stay in
-  // flight across the barrier
-  // (lgkmcnt 0: this wave's LDS writes are done before the barrier).
-  constexpr int VMCNT_W = (W_LOADS & 15) | (7 << 4) | (0 << 8) | ((W_LOADS >> 4) << 14);
-  // all but the last step: compute step s while step s+1 is dequantized and
-  // loaded (one code path, so the accumulators stay put across iterations)
-  for (int s = 0; s + 1 < steps; ++s) {
-    const bool odd = s & 1;
-    uint16_t *Acur = odd ? As1 : As0, *Bcur = odd ? Bs1 : Bs0;
-    uint16_t *Anxt = odd ? As0 : As1, *Bnxt = odd ? Bs0 : Bs1;
-    issue_a(s + 1, Anxt);
-    const bool w_ahead = s + 2 < steps;
-    if (w_ahead) load_w(s + 2, wb);
-    RunTable T;
-    float s0, s1;
-    run_setup(wa, T, s0, s1);
-    compute_step(Acur, Bcur, [&](int kk) { dequant_part(wa, T, s0, s1, Bnxt, kk); });
-    wa = wb;
-    if (w_ahead)
-      __builtin_amdgcn_s_waitcnt(VMCNT_W);
-    else
-      __builtin_amdgcn_s_waitcnt(0);
-    // a bare barrier: the waits above are all this step needs, and a full
-    // workgroup fence would also drain the W loads still in flight
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  }
-  if (steps > 0) {
-    const bool odd = (steps - 1) & 1;
-    compute(odd ? As1 : As0, odd ? Bs1 : Bs0);
-    __syncthreads();
-  }
-
-  // ---- rank-r tail: (s Z) B^T (NT) or dZ A (NN), plain bf16 steps ------------
-  if (p.r2 > 0) {
-    const uint16_t *B2 = p.B2.p + g * p.B2.gstride;
-    for (int k0 = 0; k0 < p.r2; k0 += BKS) {
-      // activation tail [256 x 64] and the adapter tile, through registers
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int idx = t + THREADS * c;
-        const int row = idx >> 3, chunk = idx & 7;
-        uint32_t w4[4] = {0u, 0u, 0u, 0u};
-        const int64_t gr = row0 + row;
-        const int64_t gk = k0 + chunk * 8;
-        if (gr < row_end) {
-          const uint16_t *src = p.A2.p + gr * p.A2.ld + gk;
-          for (int j = 0; j < 8; ++j)
-            if (gk + j < p.r2) w4[j >> 1] |= (uint32_t)src[j] << (16 * (j & 1));
-        }
-        lds_write_b128(As0 + swz(row, chunk), u32x4_t{w4[0], w4[1], w4[2], w4[3]});
-      }
-      if constexpr (MODE == 0) {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const int idx = t + THREADS * c;
-          const int row = idx >> 3, chunk = idx & 7;
-          uint32_t w4[4] = {0u, 0u, 0u, 0u};
-          const int64_t gn = col0 + row;
-          const int64_t gk = k0 + chunk * 8;
-          if (gn < p.Nc) {
-            const uint16_t *src = B2 + gn * p.B2.ld + gk;
-            for (int j = 0; j < 8; ++j)
-              if (gk + j < p.r2) w4[j >> 1] |= (uint32_t)src[j] << (16 * (j & 1));
-          }
-          lds_write_b128(Bs0 + swz(row, chunk), u32x4_t{w4[0], w4[1], w4[2], w4[3]});
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const int idx = t + THREADS * c;
-          const int row = idx >> 5, cc = (idx & 31) * 8;
-          uint32_t w4[4] = {0u, 0u, 0u, 0u};
-          const int64_t gr = k0 + row;
-          const int64_t gc = col0 + cc;
-          if (gr < p.r2) {
-            const uint16_t *src = B2 + gr * p.B2.ld + gc;
-            for (int j = 0; j < 8; ++j)
-              if (gc + j < p.Nc) w4[j >> 1] |= (uint32_t)src[j] << (16 * (j & 1));
-          }
-          lds_write_b128(Bs0 + row * LDB_NN + cc, u32x4_t{w4[0], w4[1], w4[2], w4[3]});
-        }
-      }
-      __syncthreads();
-      compute(As0, Bs0);
-      __syncthreads();
-    }
-  }
-
-  // ---- epilogue: register r of acc[j][i] holds
-  // C[wm0 + 32 i + lane % 32][wn0 + 32 j + 8 (r / 4) + 4 (lane / 32) + r % 4]
-  const bool vec_out = (p.ldc % 4) == 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t row = row0 + wm0 + i * 32 + (lane & 31);
-    if (row >= row_end) continue;
-    uint16_t *crow = p.C + row * p.ldc;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int64_t col = col0 + wn0 + j * 32 + r4 * 8 + (lane >> 5) * 4;
-        const float v0 = acc[j][i][4 * r4], v1 = acc[j][i][4 * r4 + 1];
-        const float v2 = acc[j][i][4 * r4 + 2], v3 = acc[j][i][4 * r4 + 3];
-        if (vec_out && col + 4 <= p.Nc) {
-          u32x2_t pk = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-          *reinterpret_cast<u32x2_t *>(crow + col) = pk;
-        } else {
-          const float v[4] = {v0, v1, v2, v3};
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (col + e < p.Nc) crow[col + e] = to_bf16(v[e]);
-        }
-      }
-    }
-  }
-}
 
 }  // namespace big
 }  // namespace lora4

@@ -131,26 +131,36 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   };
 
   // ---- this lane's W rows: n = col0 + 64 wave + 32 j + l32, k = 32 h + .. ----
-  const int64_t Kw = p.W.K;
-  const int64_t nrows = p.Nc - col0;   // rows of W from the tile's first on
+  // The wave's 64 rows are one row block of the tiled base: per step it reads
+  // tile (rb, k0 / 64), 2048 contiguous bytes of codes (row i at 32 i) and 64
+  // or 128 contiguous scale entries. Row blocks past the base read nothing
+  // (out-of-range descriptor).
+  const int64_t KB = p.W.KB;
+  const int64_t rb = (col0 >> 6) + wave;
+  const bool rb_ok = rb < w_blocks(p.W.N);
   const uint8_t *codes_g = p.W.codes + g * p.W.g_codes;
-  const rsrc_t w_rsrc = big::make_rsrc(codes_g + col0 * (Kw >> 1), big::clamp_bytes(nrows * (Kw >> 1)));
-  const int sc_per_row = FMT == FMT_MXFP4 ? (int)(Kw >> 5) : (int)(Kw >> 6);
-  const int sc_bytes = FMT == FMT_NF4 ? 4 : 1;
+  const rsrc_t w_rsrc = big::make_rsrc(rb_ok ? codes_g + rb * KB * 2048 : codes_g,
+                                       rb_ok ? big::clamp_bytes(KB * 2048) : 0u);
+  constexpr int sc_bytes = FMT == FMT_NF4 ? 4 : 1;
+  constexpr int sc_tile = FMT == FMT_MXFP4 ? 128 : 64 * sc_bytes;   // scale bytes per tile
   const uint8_t *sbase = reinterpret_cast<const uint8_t *>(p.W.scales) + (g * p.W.g_scales) * sc_bytes;
-  const rsrc_t s_rsrc = big::make_rsrc(sbase + col0 * sc_per_row * sc_bytes, big::clamp_bytes(nrows * sc_per_row * sc_bytes));
+  const rsrc_t s_rsrc = big::make_rsrc(rb_ok ? sbase + rb * KB * sc_tile : sbase,
+                                       rb_ok ? big::clamp_bytes(KB * sc_tile) : 0u);
   const rsrc_t s2_rsrc = FMT == FMT_NF4_DQ
                              ? big::make_rsrc(p.W.scales2 + g * p.W.g_scales2, big::clamp_bytes(p.W.g_scales2 * 4))
                              : big::make_rsrc(p.W.codes, 0u);
   uint32_t w_voff[2], s_voff[2];
-  int64_t s_idx0[2];   // DQ: flat index of the row's first 64-run scale
+  int64_t s_idx0[2];   // DQ: row-major index of the row's first 64-run scale
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int rloc = wave * 64 + j * 32 + l32;   // row inside the tile
-    w_voff[j] = (uint32_t)(rloc * (Kw >> 1) + h * 16);
-    s_voff[j] = (uint32_t)(rloc * sc_per_row * sc_bytes);
-    s_idx0[j] = (col0 + rloc) * sc_per_row;
+    const int i = j * 32 + l32;   // row inside the row block
+    w_voff[j] = (uint32_t)(i * 32 + h * 16);
+    s_voff[j] = (uint32_t)(FMT == FMT_MXFP4 ? i * 2 + h : i * sc_bytes);
+    s_idx0[j] = (col0 + wave * 64 + i) * (p.W.K >> 6);
   }
+  // per-step offsets of tile (rb, k0 / 64)
+  auto w_step_off = [](int k0) { return (int)((k0 >> 6) << 11); };
+  auto s_step_off = [](int k0) { return (int)((k0 >> 6) * sc_tile); };
 
   // W of step s, part 0..3: part j < 2 loads row j's codes and scale (with
   // its second-level scale for NF4-DQ); parts 2 and 3 load nothing, so every
@@ -162,15 +172,15 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
     const bool half_ok = k0 + 32 * h < Ri;
     const int j = part;
     w.c[j] = __builtin_bit_cast(
-        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, half_ok ? w_voff[j] : OOB, (int)(k0 >> 1), 0));
+        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, half_ok ? w_voff[j] : OOB, w_step_off(k0), 0));
     if constexpr (FMT == FMT_NF4) {
-      w.sc[j] = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, half_ok ? s_voff[j] : OOB, (int)((k0 >> 6) * 4), 0);
+      w.sc[j] = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, half_ok ? s_voff[j] : OOB, s_step_off(k0), 0);
     } else if constexpr (FMT == FMT_NF4_DQ) {
-      w.sc[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, half_ok ? s_voff[j] : OOB, (int)(k0 >> 6), 0);
+      w.sc[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, half_ok ? s_voff[j] : OOB, s_step_off(k0), 0);
       const int64_t gi = (s_idx0[j] + (int64_t)(k0 >> 6)) >> 8;
       w.c2[j] = __builtin_amdgcn_raw_buffer_load_b32(s2_rsrc, half_ok ? (uint32_t)(gi * 4) : OOB, 0, 0);
     } else {
-      w.sc[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, half_ok ? s_voff[j] + h : OOB, (int)(k0 >> 5), 0);
+      w.sc[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, half_ok ? s_voff[j] : OOB, s_step_off(k0), 0);
     }
   };
   // loads issued by load_w over a whole step, all in parts 0 and 1 (issued
@@ -277,20 +287,20 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
     const int k0 = (s + sb) * BKS;
     const bool half_ok = k0 + 32 * h < Ri;
     if constexpr (FMT == FMT_NF4) {
-      w.sc[j] = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, half_ok ? s_voff[j] : OOB, (int)((k0 >> 6) * 4), 0);
+      w.sc[j] = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, half_ok ? s_voff[j] : OOB, s_step_off(k0), 0);
     } else if constexpr (FMT == FMT_NF4_DQ) {
-      w.sc[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, half_ok ? s_voff[j] : OOB, (int)(k0 >> 6), 0);
+      w.sc[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, half_ok ? s_voff[j] : OOB, s_step_off(k0), 0);
       const int64_t gi = (s_idx0[j] + (int64_t)(k0 >> 6)) >> 8;
       w.c2[j] = __builtin_amdgcn_raw_buffer_load_b32(s2_rsrc, half_ok ? (uint32_t)(gi * 4) : OOB, 0, 0);
     } else {
-      w.sc[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, half_ok ? s_voff[j] + h : OOB, (int)(k0 >> 5), 0);
+      w.sc[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, half_ok ? s_voff[j] : OOB, s_step_off(k0), 0);
     }
   };
   auto load_w_codes = [&](int s, WRaw &w, int j) {
     const int k0 = (s + sb) * BKS;
     const bool half_ok = k0 + 32 * h < Ri;
     w.c[j] = __builtin_bit_cast(
-        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, half_ok ? w_voff[j] : OOB, (int)(k0 >> 1), 0));
+        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, half_ok ? w_voff[j] : OOB, w_step_off(k0), 0));
   };
   // slice i of decoding words q0, q0 + 1 of row j of w into f
   auto dec_slice = [&](int i, const WRaw &w, WFrag &f, const RunDec &d, int j, int q0, WordDec (&wd)[2]) {

@@ -251,8 +251,9 @@ PackedW packed_of(const lora4_W *W) {
   p.scales2 = W->scales2;
   p.N = W->N;
   p.K = W->K;
-  p.g_codes = W->N * (W->K / 2);
-  p.g_scales = W->N * (W->K / W->block);
+  p.KB = w_blocks(W->K);
+  p.g_codes = w_blocks(W->N) * p.KB * 2048;
+  p.g_scales = w_blocks(W->N) * p.KB * (W->format == LORA4_MXFP4 ? 128 : 64);
   p.g_scales2 = W->format == LORA4_NF4_DQ ? ceil_div(W->N * (W->K / 64), 256) : 0;
   return p;
 }
@@ -364,13 +365,13 @@ int big_policy() {
   return e ? std::atoi(e) : -1;
 }
 
-// The large-tile kernel addresses its operands through 32-bit buffer offsets
-// and streams 16-byte activation chunks: it needs rows that are multiples of
+// The large-tile kernels address their operands through 32-bit buffer offsets
+// and stream 16-byte activation chunks: they need rows that are multiples of
 // 8 elements and per-group buffers below 2 GiB.
 bool big_fits(int64_t ld_a, int64_t M, const PackedW &W) {
   const int64_t lim = (int64_t)1 << 31;
-  // (look-ahead loads run up to four 64-row steps past the end of W)
-  const int64_t ahead = 4 * 64 * (W.K / 2);
+  // (look-ahead loads run up to four row blocks of tiles past the end of W)
+  const int64_t ahead = 4 * W.KB * 2048;
   return ld_a % 8 == 0 && W.g_codes + ahead < lim && ld_a * 2 * 256 < lim && W.g_scales * 4 + ahead < lim &&
          W.g_scales2 * 4 < lim;
 }
@@ -434,29 +435,7 @@ bool use_big(int64_t M, int64_t Nc, int64_t E) {
   return tiles >= 256;
 }
 
-template <int MODE, int FMT>
-lora4_status run_big(const char *name, const big::Params &p, hipStream_t st) {
-  return launch_lds(name, big::k_gemm_big<MODE, FMT>, dim3((unsigned)p.nblocks), dim3(big::THREADS),
-                    (size_t)big::lds_bytes(MODE), p, st);
-}
-
-template <int MODE>
-lora4_status run_big_fmt(const char *name, int fmt, const big::Params &p, hipStream_t st) {
-  switch (fmt) {
-    case LORA4_NF4: return run_big<MODE, FMT_NF4>(name, p, st);
-    case LORA4_NF4_DQ: return run_big<MODE, FMT_NF4_DQ>(name, p, st);
-    case LORA4_MXFP4: return run_big<MODE, FMT_MXFP4>(name, p, st);
-  }
-  return LORA4_ERR_FORMAT;
-}
-
-// Forward base GEMM with deq(W) decoded straight into MFMA registers
-// (LORA4_FWD=0 in the environment selects the LDS-staged kernel instead).
-bool use_fwd_regs() {
-  const char *e = std::getenv("LORA4_FWD");
-  return e ? std::atoi(e) != 0 : true;
-}
-
+// Forward base GEMM with deq(W) decoded straight into MFMA registers.
 template <int FMT>
 lora4_status run_fwd(const big::Params &p, hipStream_t st) {
   if (p.ksplit > 1)
@@ -475,13 +454,7 @@ lora4_status run_fwd_fmt(int fmt, const big::Params &p, hipStream_t st) {
   return LORA4_ERR_FORMAT;
 }
 
-// Input-gradient base GEMM with pinned schedule and register ping-pong
-// (LORA4_DGRAD=0 in the environment selects the earlier kernel instead).
-bool use_dgrad_new() {
-  const char *e = std::getenv("LORA4_DGRAD");
-  return e ? std::atoi(e) != 0 : true;
-}
-
+// Input-gradient base GEMM (deq(W) through a transposed LDS tile).
 template <int FMT>
 lora4_status run_dgrad(const big::Params &p, hipStream_t st) {
   return launch_lds("gemm_nn_dgrad", dgrad::k_gemm_dgrad<FMT>, dim3((unsigned)p.nblocks), dim3(dgrad::THREADS),
@@ -547,9 +520,9 @@ void apply_tail_parts(big::Params &q, const TailParts *tp) {
 // Whether the forward base pass runs the register-direct kernel, and the
 // backward dgrad pass the 256 x 256 dgrad kernel (the kernels that can take
 // their tail operand as partials).
-bool fwd_regs_taken(int64_t R, const Plan &pl) { return R > 0 && use_fwd_regs() && pl.fs.use; }
+bool fwd_regs_taken(int64_t R, const Plan &pl) { return R > 0 && pl.fs.use; }
 bool dgrad_taken(int64_t R, int64_t ld_a, int64_t M, const PackedW &W, int64_t Nc, int64_t E) {
-  return R > 0 && big_fits(ld_a, M, W) && use_big(M, Nc, E) && use_dgrad_new();
+  return R > 0 && big_fits(ld_a, M, W) && use_big(M, Nc, E);
 }
 
 // Forward base GEMM: the register-direct kernel as the plan schedules it
@@ -574,11 +547,6 @@ lora4_status run_nt_main_fmt(int fmt, const NtParams &p, dim3 grid, const Plan &
     return LORA4_OK;
   }
   if (tp) return LORA4_ERR_UNIMPLEMENTED;   // (callers check the same predicates)
-  if (!use_fwd_regs() && p.R > 0 && big_fits(p.A.ld, p.M, p.W) && use_big(p.M, p.Nc, p.groups)) {
-    big::Params q = big_params(p.A, p.W, p.R, p.A2, p.B2, p.r2, p.M, p.Nc, p.offsets, p.groups, p.out.C,
-                               p.out.ldc);
-    return run_big_fmt<0>("gemm_nt_base", fmt, q, st);
-  }
   switch (fmt) {
     case LORA4_NF4: return run_nt_main<FMT_NF4>(p, grid, st);
     case LORA4_NF4_DQ: return run_nt_main<FMT_NF4_DQ>(p, grid, st);
@@ -600,11 +568,6 @@ lora4_status run_nn_main_fmt(int fmt, const NnParams &p, dim3 grid, const TailPa
     return run_dgrad_fmt(fmt, q, st);
   }
   if (tp) return LORA4_ERR_UNIMPLEMENTED;   // (callers check the same predicates)
-  if (p.R > 0 && big_fits(p.A.ld, p.M, p.W) && use_big(p.M, p.Nc, p.groups)) {
-    big::Params q = big_params(p.A, p.W, p.R, p.A2, p.B2, p.r2, p.M, p.Nc, p.offsets, p.groups, p.out.C,
-                               p.out.ldc);
-    return run_big_fmt<1>("gemm_nn_dgrad", fmt, q, st);
-  }
   switch (fmt) {
     case LORA4_NF4: return run_nn_main<FMT_NF4>(p, grid, st);
     case LORA4_NF4_DQ: return run_nn_main<FMT_NF4_DQ>(p, grid, st);
@@ -940,6 +903,31 @@ lora4_status lora4_backward(const lora4_W *W, const uint16_t *X, const uint16_t 
   return LORA4_OK;
 }
 
+size_t lora4_packed_bytes(int32_t format, int64_t N, int64_t K, int32_t part) {
+  const int64_t block = format == LORA4_MXFP4 ? 32 : 64;
+  if (format != LORA4_NF4 && format != LORA4_NF4_DQ && format != LORA4_MXFP4) return 0;
+  if (N < 1 || K < block || K % block != 0 || N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return 0;
+  const int64_t tiles = w_blocks(N) * w_blocks(K);
+  switch (part) {
+    case 0: return (size_t)(tiles * 2048);
+    case 1: return (size_t)(tiles * (format == LORA4_MXFP4 ? 128 : format == LORA4_NF4 ? 256 : 64));
+    case 2: return format == LORA4_NF4_DQ ? (size_t)(ceil_div(N * (K / 64), 256) * 4) : 0;
+  }
+  return 0;
+}
+
+// Clears a packed matrix's codes and scales when the tiles have padding (rows
+// past N, elements past K), which the quant kernels do not write.
+lora4_status clear_padding(int64_t N, int64_t K, int32_t format, uint8_t *codes, void *scales, hipStream_t st) {
+  if (N % 64 == 0 && K % 64 == 0) return LORA4_OK;
+  const int64_t nc = (int64_t)lora4_packed_bytes(format, N, K, 0) / 2;
+  const int64_t ns = (int64_t)lora4_packed_bytes(format, N, K, 1) / 2;
+  TRY(launch_args("fill_zero", k_fill_u16, dim3((unsigned)ceil_div(nc, 256)), dim3(256), st,
+                  reinterpret_cast<uint16_t *>(codes), nc, (uint16_t)0));
+  return launch_args("fill_zero", k_fill_u16, dim3((unsigned)ceil_div(ns, 256)), dim3(256), st,
+                     reinterpret_cast<uint16_t *>(scales), ns, (uint16_t)0);
+}
+
 lora4_status quant_pack_nf4(const uint16_t *W_bf16, int64_t N, int64_t K, int32_t double_quant,
                             uint8_t *codes, void *scales, float *scales2, void *stream) {
   if (!W_bf16 || !codes || !scales) return LORA4_ERR_NULL;
@@ -948,6 +936,7 @@ lora4_status quant_pack_nf4(const uint16_t *W_bf16, int64_t N, int64_t K, int32_
   if (!aligned16(W_bf16) || !aligned16(codes) || !aligned16(scales) || (double_quant && !aligned16(scales2)))
     return LORA4_ERR_ALIGN;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  TRY(clear_padding(N, K, double_quant ? LORA4_NF4_DQ : LORA4_NF4, codes, scales, st));
   const int64_t nblk = N * (K / 64);
   if (!double_quant) {
     return launch_args("quant_pack_nf4", k_quant_nf4, dim3((unsigned)ceil_div(nblk, 256)), dim3(256), st,
@@ -963,6 +952,7 @@ lora4_status quant_pack_mxfp4(const uint16_t *W_bf16, int64_t N, int64_t K, uint
   if (N < 1 || K < 32 || K % 32 != 0 || N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return LORA4_ERR_SHAPE;
   if (!aligned16(W_bf16) || !aligned16(codes) || !aligned16(scales_e8m0)) return LORA4_ERR_ALIGN;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  TRY(clear_padding(N, K, LORA4_MXFP4, codes, scales_e8m0, st));
   const int64_t nblk = N * (K / 32);
   return launch_args("quant_pack_mxfp4", k_quant_mxfp4, dim3((unsigned)ceil_div(nblk, 256)), dim3(256), st,
                      W_bf16, N, K, codes, scales_e8m0);

@@ -13,6 +13,10 @@
 // per block of 32, X = floor(log2 amax) - 2 clamped to [-127, 127]
 // (X = -127 for an all-zero block), E = X + 127, v = w * 2^-X, code = nearest
 // E2M1 magnitude (ties to the even code, saturating at 6) with w's sign.
+//
+// Codes and first-level scales are written in the 64 x 64 tile order of the
+// packed base (w_code_off, w_scale64_idx, w_scale32_idx); the caller clears
+// the padding of the last row and k blocks beforehand.
 #pragma once
 
 #include "formats.hpp"
@@ -107,8 +111,9 @@ __global__ void k_quant_nf4(const uint16_t *W, int64_t N, int64_t K, uint8_t *co
   uint32_t w[32];
   load_block64(W, K, n, b, w);
   const float c = absmax64(w);
-  nf4_encode_block(w, c, tab, codes + n * (K >> 1) + b * 32);
-  scales[i] = c;
+  const int64_t KB = w_blocks(K);
+  nf4_encode_block(w, c, tab, codes + w_code_off(KB, n, b * 64));
+  scales[w_scale64_idx(KB, n, b * 64)] = c;
 }
 
 // NF4 with double quantization: one 256-thread workgroup per group of 256
@@ -126,7 +131,7 @@ __global__ __launch_bounds__(256) void k_quant_nf4_dq(const uint16_t *W, int64_t
     const int64_t n = i / nb, b = i - n * nb;
     load_block64(W, K, n, b, w);
     c = absmax64(w);
-    nf4_encode_block(w, c, tab, codes + n * (K >> 1) + b * 32);
+    nf4_encode_block(w, c, tab, codes + w_code_off(w_blocks(K), n, b * 64));
   }
   red[threadIdx.x] = c;
   __syncthreads();
@@ -137,7 +142,8 @@ __global__ __launch_bounds__(256) void k_quant_nf4_dq(const uint16_t *W, int64_t
   const float c2 = red[0];
   if (i < total) {
     const float ratio = (c2 == 0.0f) ? 0.0f : c / c2;
-    code8[i] = (uint8_t)e4m3_encode_rne(ratio);
+    const int64_t n = i / nb, b = i - n * nb;
+    code8[w_scale64_idx(w_blocks(K), n, b * 64)] = (uint8_t)e4m3_encode_rne(ratio);
   }
   if (threadIdx.x == 0) scales2[blockIdx.x] = c2;
 }
@@ -198,8 +204,9 @@ __global__ void k_quant_mxfp4(const uint16_t *W, int64_t N, int64_t K, uint8_t *
     }
     out[d] = word;
   }
-  *reinterpret_cast<u32x4_t *>(codes + n * (K >> 1) + b * 16) = u32x4_t{out[0], out[1], out[2], out[3]};
-  e8m0[i] = (uint8_t)(X + 127);
+  const int64_t KB = w_blocks(K);
+  *reinterpret_cast<u32x4_t *>(codes + w_code_off(KB, n, b * 32)) = u32x4_t{out[0], out[1], out[2], out[3]};
+  e8m0[w_scale32_idx(KB, n, b * 32)] = (uint8_t)(X + 127);
 }
 
 }  // namespace lora4

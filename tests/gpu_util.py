@@ -34,6 +34,40 @@ def pack_gpu(W_u16, fmt):
     return L.pack_nf4(Wd, double_quant=(fmt == synth.NF4_DQ))
 
 
+def _blocks(x):
+    return -(-x // 64)
+
+
+def tile_codes(codes, N, K):
+    """Row-major codes [N, K/2] -> the library's storage: 64 x 64-element tiles
+    (2048 bytes, 32 per row), tile (rb, kb) at rb * KB + kb, zero padding."""
+    RB, KB = _blocks(N), _blocks(K)
+    buf = np.zeros((RB * 64, KB * 32), dtype=np.uint8)
+    buf[:N, :codes.shape[1]] = codes
+    return np.ascontiguousarray(buf.reshape(RB, 64, KB, 32).transpose(0, 2, 1, 3)).reshape(-1)
+
+
+def tile_scales(sc, N, K):
+    """Row-major first-level scales [N, K/64] (NF4, NF4-DQ) or [N, K/32]
+    (MXFP4) -> the library's storage: 64 (or 128) entries per tile, row i's
+    entries contiguous, zero padding."""
+    RB, KB = _blocks(N), _blocks(K)
+    per = 2 if sc.shape[1] == K // 32 else 1   # MXFP4: two 32-element blocks per row and tile
+    buf = np.zeros((RB * 64, KB * per), dtype=sc.dtype)
+    buf[:N, :sc.shape[1]] = sc
+    return np.ascontiguousarray(buf.reshape(RB, 64, KB, per).transpose(0, 2, 1, 3)).reshape(-1)
+
+
+def untile_rows(flat, N, K, rows, per_row):
+    """Rows of a tiled array (codes: per_row = 32 bytes per 64 elements;
+    scales: 1 or 2 entries per 64 elements) back in row-major order, K-padding
+    dropped."""
+    RB, KB = _blocks(N), _blocks(K)
+    t = flat.reshape(RB, KB, 64, per_row).transpose(0, 2, 1, 3).reshape(RB * 64, KB * per_row)
+    width = K // 2 if per_row == 32 else (K // 64 if per_row == 1 else K // 32)
+    return t[rows, :width]
+
+
 def oracle_pack(W_u16, fmt):
     """Oracle packing of one [N, K] matrix: (codes, scales[, scales2])."""
     if fmt == synth.MXFP4:

@@ -125,3 +125,18 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(L, "LIB_PATH", "/nonexistent/liblora4.so")
     with pytest.raises(RuntimeError):
         L.lib()
+
+
+def test_packed_bytes(lib):
+    # 64 x 64 tiles: 2048 code bytes and 64 (NF4: fp32, DQ: u8) or 128 (MXFP4) scale entries per tile
+    assert L.lora4_packed_bytes(L.LORA4_NF4, 1024, 1024, 0) == 16 * 16 * 2048
+    assert L.lora4_packed_bytes(L.LORA4_NF4, 1024, 1024, 1) == 16 * 16 * 64 * 4
+    assert L.lora4_packed_bytes(L.LORA4_NF4, 1024, 1024, 2) == 0
+    assert L.lora4_packed_bytes(L.LORA4_NF4_DQ, 37, 192, 0) == 1 * 3 * 2048
+    assert L.lora4_packed_bytes(L.LORA4_NF4_DQ, 37, 192, 1) == 1 * 3 * 64
+    assert L.lora4_packed_bytes(L.LORA4_NF4_DQ, 37, 192, 2) == 4 * -(-(37 * 3) // 256)
+    assert L.lora4_packed_bytes(L.LORA4_MXFP4, 65, 96, 0) == 2 * 2 * 2048
+    assert L.lora4_packed_bytes(L.LORA4_MXFP4, 65, 96, 1) == 2 * 2 * 128
+    for bad in [(L.LORA4_NF4, 10, 96, 0), (L.LORA4_MXFP4, 0, 64, 0), (L.LORA4_MXFP4, 8, 48, 0), (9, 64, 64, 0),
+                (L.LORA4_NF4, 64, 64, 3)]:
+        assert L.lora4_packed_bytes(*bad) == 0, bad

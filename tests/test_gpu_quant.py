@@ -14,7 +14,8 @@ import torch
 import lora_fine_tuning_amd as L
 import synth
 from oracle import codecs, mxfp4, nf4
-from gpu_util import DEV, f64, oracle_dequant, oracle_pack, pack_gpu, print_case, to_dev, to_host
+from gpu_util import (DEV, f64, oracle_dequant, oracle_pack, pack_gpu, print_case, tile_codes, tile_scales, to_dev,
+                      to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -46,14 +47,16 @@ def test_quant_pack_bit_exact(fmt, N, K):
     pk = pack_gpu(W, fmt)
     torch.cuda.synchronize()
     ref = oracle_pack(W, fmt)
-    assert np.array_equal(pk.codes[0].cpu().numpy(), ref[0])
+    # the library stores the oracle's row-major codes and scales in 64 x 64
+    # tiles (include/lora4.h); padding is zero
+    assert np.array_equal(pk.codes[0].cpu().numpy(), tile_codes(ref[0], N, K))
     if fmt == synth.NF4:
-        assert np.array_equal(pk.scales[0].cpu().numpy().view(np.uint32), ref[1].view(np.uint32))
+        assert np.array_equal(pk.scales[0].cpu().numpy().view(np.uint32), tile_scales(ref[1], N, K).view(np.uint32))
     elif fmt == synth.NF4_DQ:
-        assert np.array_equal(pk.scales[0].cpu().numpy(), ref[1])
+        assert np.array_equal(pk.scales[0].cpu().numpy(), tile_scales(ref[1], N, K))
         assert np.array_equal(pk.scales2[0].cpu().numpy().view(np.uint32), ref[2].view(np.uint32))
     else:
-        assert np.array_equal(pk.scales[0].cpu().numpy(), ref[1])
+        assert np.array_equal(pk.scales[0].cpu().numpy(), tile_scales(ref[1], N, K))
 
 
 def _zero_sign(u16):
@@ -90,13 +93,14 @@ def _custom_base(fmt, N, K, seed):
 
 
 def _to_packed(parts, fmt, N, K):
-    codes = torch.from_numpy(parts[0]).to(DEV)[None]
+    """Row-major codes and scales, stored in the library's tiles on the GPU."""
+    codes = torch.from_numpy(tile_codes(parts[0], N, K)).to(DEV)[None]
+    sc = torch.from_numpy(tile_scales(parts[1], N, K)).to(DEV)[None]
     if fmt == synth.NF4:
-        return L.PackedBase(L.LORA4_NF4, N, K, 1, codes, torch.from_numpy(parts[1]).to(DEV)[None])
+        return L.PackedBase(L.LORA4_NF4, N, K, 1, codes, sc)
     if fmt == synth.NF4_DQ:
-        return L.PackedBase(L.LORA4_NF4_DQ, N, K, 1, codes, torch.from_numpy(parts[1]).to(DEV)[None],
-                            torch.from_numpy(parts[2]).to(DEV)[None])
-    return L.PackedBase(L.LORA4_MXFP4, N, K, 1, codes, torch.from_numpy(parts[1]).to(DEV)[None])
+        return L.PackedBase(L.LORA4_NF4_DQ, N, K, 1, codes, sc, torch.from_numpy(parts[2]).to(DEV)[None])
+    return L.PackedBase(L.LORA4_MXFP4, N, K, 1, codes, sc)
 
 
 @pytest.fixture(params=["big", "small"])

@@ -23,7 +23,7 @@ import torch
 import lora_fine_tuning_amd as L
 import synth
 from oracle import codecs, lora, mxfp4, nf4
-from gpu_util import DEV, TOL, f64, print_case, to_dev, to_host
+from gpu_util import DEV, TOL, f64, print_case, tile_codes, tile_scales, to_dev, to_host, untile_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -105,17 +105,19 @@ def _check_layer(lay, rng, n_rows=64, n_cols=64, n_kblk=2):
         if lay.fmt == synth.NF4_DQ:
             c, sc = nf4.quantize(We)
             c8, c2 = nf4.double_quantize(sc)
-            assert np.array_equal(codes[e], c)
-            assert np.array_equal(scales[e], c8)
+            assert np.array_equal(codes[e], tile_codes(c, lay.N, lay.K))
+            assert np.array_equal(scales[e], tile_scales(c8, lay.N, lay.K))
             assert np.array_equal(scales2[e].view(np.uint32), c2.view(np.uint32))
             full_dq = nf4.dequantize_dq(c, c8, c2)
         else:
             pc, ps = _oracle_pack_rows(We, nrows, lay.fmt)
-            assert np.array_equal(codes[e][nrows], pc)
+            assert np.array_equal(untile_rows(codes[e], lay.N, lay.K, nrows, 32), pc)
+            per = 2 if lay.fmt == synth.MXFP4 else 1
+            got_s = untile_rows(scales[e], lay.N, lay.K, nrows, per)
             if lay.fmt == synth.NF4:
-                assert np.array_equal(scales[e][nrows].view(np.uint32), ps.view(np.uint32))
+                assert np.array_equal(got_s.view(np.uint32), ps.view(np.uint32))
             else:
-                assert np.array_equal(scales[e][nrows], ps)
+                assert np.array_equal(got_s, ps)
         if Me == 0:
             continue
         mrows = np.sort(rng.choice(Me, min(n_rows, Me), replace=False))
