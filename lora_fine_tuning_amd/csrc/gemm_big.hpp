@@ -61,6 +61,29 @@ struct Params {
 
 constexpr int A2_MAX_PARTS = 4;
 
+#ifndef LORA4_GROUP_M
+#define LORA4_GROUP_M 4
+#endif
+
+// Tile t of a slots x tiles_n grid of output tiles in grouped order: runs of
+// LORA4_GROUP_M row tiles are walked column by column, so that the tiles one
+// XCD runs at the same time (a contiguous range of t) share activation row
+// tiles and W column tiles in its L2.
+__device__ __forceinline__ void grouped_tile(int t, int tiles_n, int slots, int &slot, int &tn) {
+  if (LORA4_GROUP_M <= 1) {
+    slot = t / tiles_n;
+    tn = t - slot * tiles_n;
+    return;
+  }
+  const int per_group = LORA4_GROUP_M * tiles_n;
+  const int gi = t / per_group;
+  const int r = t - gi * per_group;
+  const int g0 = gi * LORA4_GROUP_M;
+  const int rows = slots - g0 < LORA4_GROUP_M ? slots - g0 : LORA4_GROUP_M;
+  tn = r / rows;
+  slot = g0 + (r - tn * rows);
+}
+
 // Sum over the partial ranges (in range order, from +0) of the 8 tail
 // operand values of row gr, columns gk .. gk + 7 (zero past r2).
 __device__ __forceinline__ void a2_part_sum(const Params &p, int64_t gr, int64_t gk, float (&v)[8]) {

@@ -86,8 +86,8 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
     const int per = p.nblocks >> 3;
     if (b < per * 8) b = (b & 7) * per + (b >> 3);
   }
-  const int tn = b % p.tiles_n;
-  const int slot = b / p.tiles_n;
+  int tn, slot;
+  big::grouped_tile(b, p.tiles_n, p.nblocks / p.tiles_n, slot, tn);
   const RowTile rt = map_row_tile(slot, BM, p.offsets, p.groups, p.M);
   if (rt.group < 0) return;
   const int g = rt.group;

@@ -90,8 +90,13 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
     split = b % p.ksplit;
   }
   constexpr bool is_split = SPLIT;
-  const int tn = tile % p.tiles_n;
-  const int slot = tile / p.tiles_n;
+  int tn, slot;
+  if constexpr (!SPLIT) {
+    big::grouped_tile(tile, p.tiles_n, p.nblocks / p.tiles_n, slot, tn);
+  } else {
+    tn = tile % p.tiles_n;   // (the reduction of the split tiles uses this order)
+    slot = tile / p.tiles_n;
+  }
   const RowTile rt = map_row_tile(slot, BM, p.offsets, p.groups, p.M);
   if (rt.group < 0) return;
   const int g = rt.group;
