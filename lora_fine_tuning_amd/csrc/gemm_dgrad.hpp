@@ -202,18 +202,18 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
     return frag_w(Bs, kk * 16, wn0 + j * 32, lane);
   };
 
-  // One 64-deep step on (As, Bs). The A fragments of the next sub-step are
-  // requested at its start (double-buffered), the B fragment j of the next
-  // sub-step right after its four MFMAs; hook(kk) holds sub-step kk's share of
-  // the decode and global loads. The first fragments of a step are read at
-  // its start.
-  auto compute_step = [&](const uint16_t *As, const uint16_t *Bs, auto &&hook) {
+  // The first nk sub-steps of a 64-deep step on (As, Bs), for the rank-r
+  // tail. The A fragments of the next sub-step are requested at its start
+  // (double-buffered), the B fragment j of the next sub-step right after its
+  // four MFMAs; the first fragments are read at the start.
+  auto compute_step = [&](const uint16_t *As, const uint16_t *Bs, int nk) {
     u32x4_t afa[4], afb[4], bf[4];
     read_af(As, 0, afa);
 #pragma unroll
     for (int j = 0; j < 4; ++j) bf[j] = read_bf(Bs, 0, j);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
+      if (kk >= nk) break;
       u32x4_t *af = (kk & 1) ? afb : afa;
       u32x4_t *afn = (kk & 1) ? afa : afb;
       const bool more = kk < 3;
@@ -224,15 +224,11 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
         for (int i = 0; i < 4; ++i) acc[j][i] = mfma_32x32x16(bf[j], af[i], acc[j][i]);
         if (more) bf[j] = read_bf(Bs, kk + 1, j);
       }
-      hook(kk);
 #if LORA4_SCHED_INTERLEAVE
 #pragma unroll
       for (int m = 0; m < 16; ++m) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // MFMA
         if (more && m < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // LDS read
-        if (m & 1) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);              // global load
-        if ((m & 7) == 7) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);       // LDS write
-        __builtin_amdgcn_sched_group_barrier(0x002, LORA4_SCHED_VALU, 0);          // VALU
       }
 #endif
       __builtin_amdgcn_sched_barrier(0);
@@ -474,7 +470,8 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
         lds_write_b128(Bs0 + wt_off(row, cc), v);
       }
       __syncthreads();
-      compute_step(As0, Bs0, [](int) {});
+      // sub-step kk covers reduction rows k0 + 16 kk .. +15: only those below r2
+      compute_step(As0, Bs0, min(4, (p.r2 - k0 + 15) / 16));
       __syncthreads();
     }
   }

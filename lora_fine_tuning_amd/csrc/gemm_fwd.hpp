@@ -459,9 +459,8 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   __syncthreads();
 
   // ---- rank-r tail: (s Z) B^T; Z rows through LDS, B rows to registers -----
-  // (B loads of sub-steps whose reduction slots all lie past r2 are skipped:
-  // in sub-step kk lane half h holds k0 + 32 h + 8 kk ..; the MFMAs of such
-  // sub-steps still run, on zeros: branching around them costs more.)
+  // (sub-steps whose reduction slots all lie past r2 are skipped: in
+  // sub-step kk lane half h holds k0 + 32 h + 8 kk ..)
   if (p.r2 > 0 && split == 0) {
     const uint16_t *B2 = p.B2.p + g * p.B2.gstride;
     uint16_t *As = smem;
@@ -522,7 +521,8 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) xt[i] = lds_read_b128(As + swz(i * 32 + l32, h * 4));
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) sub_step(bt, kk, xt, As, h * 4 + kk + 1, kk < 3, [] {});
+      for (int kk = 0; kk < 4; ++kk)
+        if (kk < nkk) sub_step(bt, kk, xt, As, h * 4 + kk + 1, kk < 3, [] {});
       __syncthreads();
     }
   }
