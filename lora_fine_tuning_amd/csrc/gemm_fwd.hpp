@@ -434,64 +434,18 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
     issue_a(2, stage(2), part);
     load_w(0, r0, part);
   }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const RunDec d = make_run(r0, j);
-    decode_words(r0, f0, d, j, 0);
-    decode_words(r0, f0, d, j, 2);
-  }
-#pragma unroll
-  for (int part = 0; part < 4; ++part) load_w(1, r1, part);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  RunDec d0 = make_run(r1, 0);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] = lds_read_b128(stage(0) + swz(i * 32 + l32, h * 4));
-  int s = 0, si = 0;   // si = s % 5
-  for (; s + 2 <= steps; s += 2) {
-    body_s(s, stage(si), stage(si + 1), stage(si + 3), r1, r0, f0, f1, x, d0);
-    body_s(s + 1, stage(si + 1), stage(si + 2), stage(si + 4), r0, r1, f1, f0, x, d0);
-    si = si + 2 >= STAGES ? si + 2 - STAGES : si + 2;
-  }
-  if (s < steps) body_s(s, stage(si), stage(si + 1), stage(si + 3), r1, r0, f0, f1, x, d0);
-  // the look-ahead loads past the end still write (zeros) into the ring
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  // ---- rank-r tail: (s Z) B^T; Z rows through LDS, B rows to registers -----
-  // (sub-steps whose reduction slots all lie past r2 are skipped: in
-  // sub-step kk lane half h holds k0 + 32 h + 8 kk ..)
+  // ---- rank-r product (s Z) B^T first, into the zeroed accumulators: Z rows
+  // through LDS stage 4 (free until step 1 refills it), B rows to registers.
+  // Its operand loads are issued right behind the first X and W loads, so
+  // their latency overlaps. (Sub-steps whose reduction slots all lie past r2
+  // are skipped: in sub-step kk lane half h holds k0 + 32 h + 8 kk ..)
   if (p.r2 > 0 && split == 0) {
     const uint16_t *B2 = p.B2.p + g * p.B2.gstride;
-    uint16_t *As = smem;
+    uint16_t *As = stage(4);
     const bool a_vec = (p.A2.ld % 8) == 0;
     const bool b_vec = (p.B2.ld % 8) == 0;
     for (int k0 = 0; k0 < p.r2; k0 += BKS) {
       const int nkk = min(4, (p.r2 - k0 + 7) / 8);
-      if (p.A2part) {
-        big::a2_parts_to_lds(p, As, [](int i, int c) { return swz(i, c); }, row0, row_end, k0, t, col0 == 0);
-      } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const int idx = t + THREADS * c;
-          const int row = idx >> 3, chunk = idx & 7;
-          u32x4_t v = {0u, 0u, 0u, 0u};
-          const int64_t gr = row0 + row;
-          const int64_t gk = k0 + chunk * 8;
-          if (gr < row_end && gk < p.r2) {
-            const uint16_t *src = p.A2.p + gr * p.A2.ld + gk;
-            if (a_vec && gk + 8 <= p.r2) {
-              v = *reinterpret_cast<const u32x4_t *>(src);
-            } else {
-              uint32_t w4[4] = {0u, 0u, 0u, 0u};
-              for (int e = 0; e < 8; ++e)
-                if (gk + e < p.r2) w4[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
-              v = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
-            }
-          }
-          lds_write_b128(As + swz(row, chunk), v);
-        }
-      }
       WFrag bt;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -516,6 +470,30 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
           bt.w[j][kk] = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
         }
       }
+      if (p.A2part) {
+        big::a2_parts_to_lds(p, As, [](int i, int c) { return swz(i, c); }, row0, row_end, k0, t, col0 == 0);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const int idx = t + THREADS * c;
+          const int row = idx >> 3, chunk = idx & 7;
+          u32x4_t v = {0u, 0u, 0u, 0u};
+          const int64_t gr = row0 + row;
+          const int64_t gk = k0 + chunk * 8;
+          if (gr < row_end && gk < p.r2) {
+            const uint16_t *src = p.A2.p + gr * p.A2.ld + gk;
+            if (a_vec && gk + 8 <= p.r2) {
+              v = *reinterpret_cast<const u32x4_t *>(src);
+            } else {
+              uint32_t w4[4] = {0u, 0u, 0u, 0u};
+              for (int e = 0; e < 8; ++e)
+                if (gk + e < p.r2) w4[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+              v = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
+            }
+          }
+          lds_write_b128(As + swz(row, chunk), v);
+        }
+      }
       __syncthreads();
       u32x4_t xt[8];
 #pragma unroll
@@ -523,9 +501,34 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
         if (kk < nkk) sub_step(bt, kk, xt, As, h * 4 + kk + 1, kk < 3, [] {});
-      __syncthreads();
+      if (k0 + BKS < p.r2) __syncthreads();   // before the next chunk restages
     }
   }
+
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const RunDec d = make_run(r0, j);
+    decode_words(r0, f0, d, j, 0);
+    decode_words(r0, f0, d, j, 2);
+  }
+#pragma unroll
+  for (int part = 0; part < 4; ++part) load_w(1, r1, part);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  RunDec d0 = make_run(r1, 0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = lds_read_b128(stage(0) + swz(i * 32 + l32, h * 4));
+  int s = 0, si = 0;   // si = s % 5
+  for (; s + 2 <= steps; s += 2) {
+    body_s(s, stage(si), stage(si + 1), stage(si + 3), r1, r0, f0, f1, x, d0);
+    body_s(s + 1, stage(si + 1), stage(si + 2), stage(si + 4), r0, r1, f1, f0, x, d0);
+    si = si + 2 >= STAGES ? si + 2 - STAGES : si + 2;
+  }
+  if (s < steps) body_s(s, stage(si), stage(si + 1), stage(si + 3), r1, r0, f0, f1, x, d0);
+  // the look-ahead loads past the end still write (zeros) into the ring, which
+  // the epilogue reuses
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
   // ---- epilogue: register e of acc[i][j] holds
   // Y[32 i + lane % 32][64 wave + 32 j + 8 (e / 4) + 4 (lane / 32) + e % 4]
