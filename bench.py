@@ -43,6 +43,9 @@ def parse():
                     help="only run a plain device copy of MIB MiB a few times (counter calibration) and exit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--blas-context", action="store_true",
+                    help="also time torch's bf16 GEMMs (hipBLASLt) on already-dequantized W of the same shapes "
+                         "(context only)")
     return ap.parse_args()
 
 
@@ -106,6 +109,24 @@ def kernel_flops(name, spec):
     }.get(name, 0)
 
 
+BITS_PER_WEIGHT = {"nf4": 4.5, "nf4_dq": 4.127, "mxfp4": 4.25}   # codes + scales
+
+
+def kernel_bytes(name, spec):
+    """Algorithmic HBM bytes of one launch of the named kernel for this layer:
+    the rank-r passes' activation reads and small operands; the packed base
+    (codes + scales) for the two dequant-GEMMs."""
+    M, N, K, r, E = spec.M, spec.N, spec.K, spec.r, spec.experts
+    wp = E * N * K * BITS_PER_WEIGHT[spec.fmt] / 8
+    return {
+        "rows_skinny_z": 2 * M * K + 2 * E * r * K + 2 * M * r,       # X, A -> Z
+        "rows_skinny_dz": 2 * M * N + 2 * E * N * r + 2 * M * r,      # dY, B -> dZ
+        "gemm_tn_dA_dB": 2 * M * (K + N) + 4 * M * r,                 # X, dY, dZ, Z
+        "gemm_nt_base": wp,
+        "gemm_nn_dgrad": wp,
+    }.get(name, 0)
+
+
 def csrc_digest():
     """sha256 over the HIP sources of the library (any kernel change alters it)."""
     import hashlib
@@ -149,6 +170,42 @@ def copy_probe(mib):
         b.copy_(a)
     torch.cuda.synchronize()
     log(f"[copy] 3 launches of {mib} MiB read + {mib} MiB written")
+
+
+def blas_context(specs, torch, steps):
+    """Context only: torch's bf16 GEMMs (hipBLASLt) for the two base products
+    of every layer, X W^T and dY W, on a bf16 W of the same shape (as if it
+    had been dequantized beforehand; the rank-r terms are left out)."""
+    dev = "cuda:0"
+    mats = []
+    for s in specs:
+        if s.experts > 1:
+            continue
+        g = torch.Generator(device=dev).manual_seed(1)
+        X = torch.randn((s.M, s.K), device=dev, generator=g).bfloat16()
+        dY = torch.randn((s.M, s.N), device=dev, generator=g).bfloat16()
+        W = (torch.randn((s.N, s.K), device=dev, generator=g) * 0.02).bfloat16()
+        mats.append((X, dY, W, W.t().contiguous()))
+
+    def run():
+        for X, dY, W, Wt in mats:
+            torch.mm(X, Wt)
+            torch.mm(dY, W)
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    fl = sum(4 * s.M * s.N * s.K for s in specs if s.experts == 1)
+    return {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+            "what": "torch.mm bf16 (hipBLASLt), X W^T and dY W per layer, W already bf16"}
 
 
 def cpu_baseline(specs, tokens, reps):
@@ -260,6 +317,32 @@ def main():
     value = flops / (ms * 1e-3) / 1e12
     log(f"[bench] {ms:.3f} ms/step, {value:.1f} TFLOP/s")
 
+    # the two passes on their own (same loop, forward-only / backward-only steps)
+    def timed_pass(fn, k):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(k):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / k
+
+    fwd_flops = sum(2 * s.M * s.N * s.K + 2 * s.M * s.r * (s.N + s.K) for s in specs)
+    ms_f = timed_pass(lambda: [l.fwd(L, ws, stream) for l in layers], args.steps)
+    ms_b = timed_pass(lambda: [l.bwd(L, ws, stream) for l in reversed(layers)], args.steps)
+    passes = {"fwd_ms": round(ms_f, 4), "fwd_tflops": round(fwd_flops / (ms_f * 1e-3) / 1e12, 2),
+              "bwd_ms": round(ms_b, 4), "bwd_tflops": round((flops - fwd_flops) / (ms_b * 1e-3) / 1e12, 2)}
+    log(f"[bench] forward {ms_f:.3f} ms ({passes['fwd_tflops']} TFLOP/s), "
+        f"backward {ms_b:.3f} ms ({passes['bwd_tflops']} TFLOP/s)")
+
+    blas = None
+    if args.blas_context:
+        blas = blas_context(specs, torch, args.steps)
+        log(f"[bench] hipBLASLt bf16 on dequantized W (context): {blas['ms']:.3f} ms/step, "
+            f"{blas['tflops']:.1f} TFLOP/s")
+
     roofline = None
     kernels = {}
     if not args.no_kernel_timing:
@@ -274,8 +357,15 @@ def main():
         for s in specs:
             for name in kt:
                 kflops[name] = kflops.get(name, 0) + kernel_flops(name, s)
+        kbytes = {}
+        for s in specs:
+            for name in kt:
+                kbytes[name] = kbytes.get(name, 0) + kernel_bytes(name, s)
         for name, (n, tot) in kt.items():
             kernels[name] = {"launches": n, "avg_us": 1e3 * tot / n, "total_ms_per_step": tot / args.steps}
+            if kbytes.get(name):
+                # algorithmic bytes per step over the kernel's time per step (HBM peak 8 TB/s)
+                kernels[name]["algorithmic_gbps"] = round(kbytes[name] / (tot / args.steps * 1e-3) / 1e9, 1)
         dom = max(kt, key=lambda k: kt[k][1])
         n, tot = kt[dom]
         per_launch = kflops[dom] / len(specs)
@@ -324,8 +414,11 @@ def main():
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "passes": passes,
         "kernels": kernels,
     }
+    if blas is not None:
+        line["blas_context"] = blas
     print(json.dumps(line), flush=True)
 
 
