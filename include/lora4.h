@@ -162,6 +162,33 @@ lora4_status lora4_backward(const lora4_W *W, const uint16_t *X, const uint16_t 
                             uint16_t *dX, uint16_t *dA, uint16_t *dB,
                             void *workspace, size_t workspace_bytes, void *stream);
 
+/* Several LoRA adapters over one shared base: adapter a applies to rows
+ * adapter_offsets[a] .. adapter_offsets[a+1]-1 of X, Y, dY and dX ("Fine-Tuning
+ * 4-Bit Models", section "Case 3": adapters trained in BF16 over a native
+ * 4-bit base are kept separate and served over it with multi-LoRA).
+ *  W        : one group (W->groups == 1), read by every adapter.
+ *  adapters : 1 .. 65535; A is bf16 [adapters][r, K], B [adapters][N, r], and
+ *             dA, dB have the same shapes (zero for an adapter with no rows).
+ *  adapter_offsets : adapters == 1: NULL. Otherwise a DEVICE int64 array of
+ *             adapters+1 non-decreasing row offsets, [0] == 0, [adapters] == M
+ *             (rows are pre-sorted by adapter).
+ * Everything else as lora4_forward / lora4_backward; the workspace is sized by
+ * lora4_workspace_bytes_multi (which = 0 forward, 1 backward; 0 returned for
+ * invalid arguments). Validation errors: LORA4_ERR_SHAPE if W->groups != 1 or
+ * adapters is out of range, LORA4_ERR_NULL if adapters > 1 without offsets. */
+size_t lora4_workspace_bytes_multi(int which, const lora4_W *W, int64_t adapters, int64_t M, int32_t r);
+lora4_status lora4_forward_multi(const lora4_W *W, int64_t adapters, const uint16_t *X, int64_t M,
+                                 const uint16_t *A, const uint16_t *B, int32_t r, float s,
+                                 const int64_t *adapter_offsets, uint16_t *Y, uint16_t *Z,
+                                 uint16_t *Y_base, uint16_t *Y_lora,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+lora4_status lora4_backward_multi(const lora4_W *W, int64_t adapters, const uint16_t *X,
+                                  const uint16_t *dY, int64_t M, const uint16_t *A,
+                                  const uint16_t *B, int32_t r, float s,
+                                  const int64_t *adapter_offsets, const uint16_t *Z,
+                                  uint16_t *dX, uint16_t *dA, uint16_t *dB,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
 /* Quantize a bf16 base W [N, K] (K % 64 == 0) to NF4 with per-64 fp32 absmax
  * scales ("Training LLMs on a Budget", section 3, tricks 1 and 2): code = the
  * NF4 level nearest to fp32(w / absmax), ties to the lower level; an

@@ -25,7 +25,8 @@ LORA4_NF4, LORA4_NF4_DQ, LORA4_MXFP4 = 1, 2, 3
 FORMATS = {"nf4": LORA4_NF4, "nf4_dq": LORA4_NF4_DQ, "mxfp4": LORA4_MXFP4}
 BLOCK = {LORA4_NF4: 64, LORA4_NF4_DQ: 64, LORA4_MXFP4: 32}
 
-EXPORTS = ["lora4_forward", "lora4_backward", "lora4_workspace_bytes", "lora4_packed_bytes", "quant_pack_nf4",
+EXPORTS = ["lora4_forward", "lora4_backward", "lora4_workspace_bytes", "lora4_packed_bytes",
+           "lora4_forward_multi", "lora4_backward_multi", "lora4_workspace_bytes_multi", "quant_pack_nf4",
            "quant_pack_mxfp4", "lora4_status_string", "lora4_timing_enable", "lora4_timing_collect",
            "lora4_version"]
 
@@ -66,6 +67,12 @@ def lib():
         L.lora4_workspace_bytes.restype = sz
         L.lora4_packed_bytes.argtypes = [i32, i64, i64, i32]
         L.lora4_packed_bytes.restype = sz
+        L.lora4_forward_multi.argtypes = [Wp, i64, vp, i64, vp, vp, i32, f32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.lora4_forward_multi.restype = ctypes.c_int
+        L.lora4_backward_multi.argtypes = [Wp, i64, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.lora4_backward_multi.restype = ctypes.c_int
+        L.lora4_workspace_bytes_multi.argtypes = [ctypes.c_int, Wp, i64, i64, i32]
+        L.lora4_workspace_bytes_multi.restype = sz
         L.quant_pack_nf4.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp]
         L.quant_pack_nf4.restype = ctypes.c_int
         L.quant_pack_mxfp4.argtypes = [vp, i64, i64, vp, vp, vp]
@@ -112,6 +119,22 @@ def lora4_backward(W, X, dY, M, A, B, r, s, group_offsets, Z, dX, dA, dB, worksp
                    stream):
     return lib().lora4_backward(ctypes.byref(W), X, dY, M, A, B, r, s, group_offsets, Z, dX, dA, dB,
                                 workspace, workspace_bytes, stream)
+
+
+def lora4_forward_multi(W, adapters, X, M, A, B, r, s, adapter_offsets, Y, Z, Y_base, Y_lora, workspace,
+                        workspace_bytes, stream):
+    return lib().lora4_forward_multi(ctypes.byref(W), adapters, X, M, A, B, r, s, adapter_offsets, Y, Z, Y_base,
+                                     Y_lora, workspace, workspace_bytes, stream)
+
+
+def lora4_backward_multi(W, adapters, X, dY, M, A, B, r, s, adapter_offsets, Z, dX, dA, dB, workspace,
+                         workspace_bytes, stream):
+    return lib().lora4_backward_multi(ctypes.byref(W), adapters, X, dY, M, A, B, r, s, adapter_offsets, Z, dX,
+                                      dA, dB, workspace, workspace_bytes, stream)
+
+
+def lora4_workspace_bytes_multi(which, W, adapters, M, r):
+    return lib().lora4_workspace_bytes_multi(which, ctypes.byref(W), adapters, M, r)
 
 
 def quant_pack_nf4(W_bf16, N, K, double_quant, codes, scales, scales2, stream):
@@ -235,6 +258,50 @@ def forward(base, X, A, B, s, group_offsets=None, want_z=True, want_parts=False,
                        _ptr(Yb), _ptr(Yl), _ptr(workspace), workspace.numel(), _stream())
     _check(st, "lora4_forward")
     return {"Y": Y, "Z": Z, "Y_base": Yb, "Y_lora": Yl}
+
+
+def forward_multi(base, X, A, B, s, adapter_offsets=None, want_z=True, want_parts=False, workspace=None):
+    """Several adapters over one shared base: A [adapters, r, K], B [adapters, N, r]
+    (rows of X pre-sorted by adapter, adapter_offsets a device int64 [adapters+1])."""
+    import torch
+    M = X.shape[0]
+    adapters, r = A.shape[0], A.shape[1]
+    dev = X.device
+    Y = torch.empty((M, base.N), dtype=torch.bfloat16, device=dev)
+    Z = torch.empty((M, r), dtype=torch.bfloat16, device=dev) if want_z else None
+    Yb = torch.empty_like(Y) if want_parts else None
+    Yl = torch.empty_like(Y) if want_parts else None
+    W = base.abi()
+    if workspace is None:
+        n = lora4_workspace_bytes_multi(0, W, adapters, M, r)
+        if n == 0:
+            raise ValueError("invalid arguments for lora4_workspace_bytes_multi")
+        workspace = torch.empty((n,), dtype=torch.uint8, device=dev)
+    st = lora4_forward_multi(W, adapters, _ptr(X), M, _ptr(A), _ptr(B), r, float(s), _ptr(adapter_offsets),
+                             _ptr(Y), _ptr(Z), _ptr(Yb), _ptr(Yl), _ptr(workspace), workspace.numel(), _stream())
+    _check(st, "lora4_forward_multi")
+    return {"Y": Y, "Z": Z, "Y_base": Yb, "Y_lora": Yl}
+
+
+def backward_multi(base, X, dY, A, B, s, Z=None, adapter_offsets=None, workspace=None):
+    """dX, dA [adapters, r, K], dB [adapters, N, r] for several adapters over one base."""
+    import torch
+    M = X.shape[0]
+    adapters, r = A.shape[0], A.shape[1]
+    dX = torch.empty((M, base.K), dtype=torch.bfloat16, device=X.device)
+    dA = torch.empty_like(A)
+    dB = torch.empty_like(B)
+    W = base.abi()
+    if workspace is None:
+        n = lora4_workspace_bytes_multi(1, W, adapters, M, r)
+        if n == 0:
+            raise ValueError("invalid arguments for lora4_workspace_bytes_multi")
+        workspace = torch.empty((n,), dtype=torch.uint8, device=X.device)
+    st = lora4_backward_multi(W, adapters, _ptr(X), _ptr(dY), M, _ptr(A), _ptr(B), r, float(s),
+                              _ptr(adapter_offsets), _ptr(Z), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(workspace),
+                              workspace.numel(), _stream())
+    _check(st, "lora4_backward_multi")
+    return {"dX": dX, "dA": dA, "dB": dB}
 
 
 def backward(base, X, dY, A, B, s, Z=None, group_offsets=None, workspace=None):

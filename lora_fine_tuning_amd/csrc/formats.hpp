@@ -125,12 +125,17 @@ struct PackedW {
   int64_t g_codes;        // bytes per group
   int64_t g_scales;       // scale entries per group
   int64_t g_scales2;      // second-level entries per group
+  int32_t shared;         // 1: one W for every row group (adapters over one base)
 };
+
+// group of W that row group g reads
+__device__ __forceinline__ int w_group(const PackedW &w, int g) { return w.shared ? 0 : g; }
 
 // Scale of the block holding (row n, element k) of group g, as the fp32
 // operand the dequantizer needs (the E8M0 operand for MXFP4).
 template <int FMT>
 __device__ __forceinline__ float block_scale(const PackedW &w, int g, int64_t n, int64_t k) {
+  g = w_group(w, g);
   if constexpr (FMT == FMT_NF4) {
     const float *s = reinterpret_cast<const float *>(w.scales) + g * w.g_scales;
     return s[w_scale64_idx(w.KB, n, k)];
@@ -150,7 +155,7 @@ __device__ __forceinline__ float block_scale(const PackedW &w, int g, int64_t n,
 template <int FMT>
 __device__ __forceinline__ void dequant_row32(const PackedW &w, int g, int64_t n, int64_t k,
                                               const float *qlds, uint32_t out[16]) {
-  const uint8_t *src = w.codes + g * w.g_codes + w_code_off(w.KB, n, k);
+  const uint8_t *src = w.codes + w_group(w, g) * w.g_codes + w_code_off(w.KB, n, k);
   u32x4_t codes = ldg_b128_cached(src);
   float sc = block_scale<FMT>(w, g, n, k);
   if constexpr (FMT == FMT_MXFP4) {

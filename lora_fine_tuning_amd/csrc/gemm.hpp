@@ -228,7 +228,7 @@ __global__ __launch_bounds__(THREADS) void k_gemm_nt(NtParams p) {
           u32x4_t cz = {0u, 0u, 0u, 0u};
           float sc = 0.f;
           if (idx < BN * 2 && n < p.Nc && k < re) {
-            const uint8_t *src = p.W.codes + g * p.W.g_codes + w_code_off(p.W.KB, n, k);
+            const uint8_t *src = p.W.codes + w_group(p.W, g) * p.W.g_codes + w_code_off(p.W.KB, n, k);
             cz = ldg_b128_cached(src);
             sc = block_scale<FMT>(p.W, g, n, k);
           }
@@ -453,7 +453,7 @@ __global__ __launch_bounds__(THREADS) void k_gemm_nn(NnParams p) {
           u32x4_t cz = {0u, 0u, 0u, 0u};
           float sc = 0.f;
           if (idx < BK * TPR && n < re && k < p.Nc) {
-            const uint8_t *src = p.W.codes + g * p.W.g_codes + w_code_off(p.W.KB, n, k);
+            const uint8_t *src = p.W.codes + w_group(p.W, g) * p.W.g_codes + w_code_off(p.W.KB, n, k);
             cz = ldg_b128_cached(src);
             sc = block_scale<FMT>(p.W, g, n, k);
           }

@@ -120,7 +120,8 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
   // base: its 32 bytes of codes at 32 lane, its scale entries contiguous
   const int64_t Kw = p.W.K;
   const int64_t KB = p.W.KB;
-  const uint8_t *codes_g = p.W.codes + g * p.W.g_codes;
+  const int gw = w_group(p.W, g);   // group of W
+  const uint8_t *codes_g = p.W.codes + gw * p.W.g_codes;
   const rsrc_t w_rsrc = big::make_rsrc(codes_g, big::clamp_bytes(p.W.g_codes));
   const int64_t kc = col0 + wave * 64;
   const uint32_t w_base = (uint32_t)((kc >> 6) * 2048 + lane * 32);
@@ -130,14 +131,14 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
   const int sc_per_row = (int)(Kw >> 6);   // NF4-DQ: scales per row, row-major (second level)
   constexpr int sc_bytes = FMT == FMT_NF4 ? 4 : 1;
   constexpr int sc_tile = FMT == FMT_MXFP4 ? 128 : 64 * sc_bytes;   // scale bytes per tile
-  const uint8_t *sbase = reinterpret_cast<const uint8_t *>(p.W.scales) + (g * p.W.g_scales) * sc_bytes;
+  const uint8_t *sbase = reinterpret_cast<const uint8_t *>(p.W.scales) + (gw * p.W.g_scales) * sc_bytes;
   const rsrc_t s_rsrc = big::make_rsrc(sbase, big::clamp_bytes(p.W.g_scales * sc_bytes));
   const uint32_t s_voff =
       kc < p.Nc ? (uint32_t)((kc >> 6) * sc_tile + (FMT == FMT_MXFP4 ? lane * 2 : lane * sc_bytes)) : OOB;
   const uint32_t s_voff1 = kc + 32 < p.Nc ? s_voff + 1 : OOB;   // MXFP4 second code
   const int64_t s_step = KB * sc_tile;
   const rsrc_t s2_rsrc = FMT == FMT_NF4_DQ
-                             ? big::make_rsrc(p.W.scales2 + g * p.W.g_scales2, big::clamp_bytes(p.W.g_scales2 * 4))
+                             ? big::make_rsrc(p.W.scales2 + gw * p.W.g_scales2, big::clamp_bytes(p.W.g_scales2 * 4))
                              : big::make_rsrc(p.W.codes, 0u);
 
   auto load_w = [&](int s, WRaw &w) {

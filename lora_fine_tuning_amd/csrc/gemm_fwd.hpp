@@ -143,16 +143,17 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   const int64_t KB = p.W.KB;
   const int64_t rb = (col0 >> 6) + wave;
   const bool rb_ok = rb < w_blocks(p.W.N);
-  const uint8_t *codes_g = p.W.codes + g * p.W.g_codes;
+  const int gw = w_group(p.W, g);   // group of W
+  const uint8_t *codes_g = p.W.codes + gw * p.W.g_codes;
   const rsrc_t w_rsrc = big::make_rsrc(rb_ok ? codes_g + rb * KB * 2048 : codes_g,
                                        rb_ok ? big::clamp_bytes(KB * 2048) : 0u);
   constexpr int sc_bytes = FMT == FMT_NF4 ? 4 : 1;
   constexpr int sc_tile = FMT == FMT_MXFP4 ? 128 : 64 * sc_bytes;   // scale bytes per tile
-  const uint8_t *sbase = reinterpret_cast<const uint8_t *>(p.W.scales) + (g * p.W.g_scales) * sc_bytes;
+  const uint8_t *sbase = reinterpret_cast<const uint8_t *>(p.W.scales) + (gw * p.W.g_scales) * sc_bytes;
   const rsrc_t s_rsrc = big::make_rsrc(rb_ok ? sbase + rb * KB * sc_tile : sbase,
                                        rb_ok ? big::clamp_bytes(KB * sc_tile) : 0u);
   const rsrc_t s2_rsrc = FMT == FMT_NF4_DQ
-                             ? big::make_rsrc(p.W.scales2 + g * p.W.g_scales2, big::clamp_bytes(p.W.g_scales2 * 4))
+                             ? big::make_rsrc(p.W.scales2 + gw * p.W.g_scales2, big::clamp_bytes(p.W.g_scales2 * 4))
                              : big::make_rsrc(p.W.codes, 0u);
   uint32_t w_voff[2], s_voff[2];
   int64_t s_idx0[2];   // DQ: row-major index of the row's first 64-run scale

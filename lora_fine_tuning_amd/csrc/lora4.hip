@@ -244,7 +244,17 @@ lora4_status check_W(const lora4_W *W) {
   return LORA4_OK;
 }
 
-PackedW packed_of(const lora4_W *W) {
+// A base as the host plans for it: the ABI description, the number of row
+// groups, and whether one W serves every group (several adapters over one
+// base) instead of one W per group (experts).
+struct Base {
+  const lora4_W *W;
+  int64_t E;
+  bool shared;
+};
+
+PackedW packed_of(const Base &b) {
+  const lora4_W *W = b.W;
   PackedW p;
   p.codes = W->codes;
   p.scales = W->scales;
@@ -255,6 +265,7 @@ PackedW packed_of(const lora4_W *W) {
   p.g_codes = w_blocks(W->N) * p.KB * 2048;
   p.g_scales = w_blocks(W->N) * p.KB * (W->format == LORA4_MXFP4 ? 128 : 64);
   p.g_scales2 = W->format == LORA4_NF4_DQ ? ceil_div(W->N * (W->K / 64), 256) : 0;
+  p.shared = b.shared ? 1 : 0;
   return p;
 }
 
@@ -296,12 +307,13 @@ constexpr int BM_MAIN = 128, BN_MAIN = 128;
 constexpr int BM_SKINNY = 128;
 constexpr int TN_BQ = 128;
 
-Plan make_plan(int which, const lora4_W *W, int64_t M, int r) {
+Plan make_plan(int which, const Base &b, int64_t M, int r) {
+  const lora4_W *W = b.W;
   Plan p{};
   p.M = M;
   p.N = W->N;
   p.K = W->K;
-  p.E = W->groups;
+  p.E = b.E;
   p.r = r;
   p.rt = skinny_tile(r);
   p.row_slots = ceil_div(std::max<int64_t>(M, 1), BM_MAIN) + (p.E > 1 ? p.E : 0);
@@ -317,7 +329,7 @@ Plan make_plan(int which, const lora4_W *W, int64_t M, int r) {
   };
   p.msplit_a = msplit(p.tq_a);
   p.msplit_b = msplit(p.tq_b);
-  p.fs = fwd_sched(M, p.N, p.K, p.E, packed_of(W));
+  p.fs = fwd_sched(M, p.N, p.K, p.E, packed_of(b));
 
   const size_t mr2 = align256((size_t)M * r * 2);
   size_t off = 0;
@@ -708,13 +720,14 @@ lora4_status z_pass(const Plan &pl, const lora4_W *W, const uint16_t *X, const u
                      st);
 }
 
-lora4_status check_common(const lora4_W *W, int64_t M, int32_t r, float s, const int64_t *offs) {
-  TRY(check_W(W));
+lora4_status check_common(const Base &b, int64_t M, int32_t r, float s, const int64_t *offs) {
+  TRY(check_W(b.W));
+  if (b.shared && (b.W->groups != 1 || b.E < 1 || b.E > 65535)) return LORA4_ERR_SHAPE;
   if (M < 0 || M > (int64_t(1) << 31)) return LORA4_ERR_SHAPE;
   if (r < 1 || r > 256) return LORA4_ERR_SHAPE;
   if (!std::isfinite(s)) return LORA4_ERR_SHAPE;
-  if (W->groups > 1 && !offs) return LORA4_ERR_NULL;
-  if (W->groups == 1 && offs) return LORA4_ERR_SHAPE;
+  if (b.E > 1 && !offs) return LORA4_ERR_NULL;
+  if (b.E == 1 && offs) return LORA4_ERR_SHAPE;
   return LORA4_OK;
 }
 
@@ -743,21 +756,33 @@ const char *lora4_status_string(lora4_status s) {
   return "unknown status";
 }
 
-size_t lora4_workspace_bytes(int which, const lora4_W *W, int64_t M, int32_t r) {
-  if ((which != 0 && which != 1) || check_W(W) != LORA4_OK || M < 0 || r < 1 || r > 256) return 0;
-  return make_plan(which, W, M, r).bytes;
+static size_t workspace_bytes_of(int which, const Base &b, int64_t M, int32_t r) {
+  if ((which != 0 && which != 1) || check_W(b.W) != LORA4_OK || M < 0 || r < 1 || r > 256) return 0;
+  if (b.shared && (b.W->groups != 1 || b.E < 1 || b.E > 65535)) return 0;
+  return make_plan(which, b, M, r).bytes;
 }
 
-lora4_status lora4_forward(const lora4_W *W, const uint16_t *X, int64_t M, const uint16_t *A,
+size_t lora4_workspace_bytes(int which, const lora4_W *W, int64_t M, int32_t r) {
+  if (!W) return 0;
+  return workspace_bytes_of(which, Base{W, W->groups, false}, M, r);
+}
+
+size_t lora4_workspace_bytes_multi(int which, const lora4_W *W, int64_t adapters, int64_t M, int32_t r) {
+  if (!W) return 0;
+  return workspace_bytes_of(which, Base{W, adapters, true}, M, r);
+}
+
+static lora4_status forward_impl(const Base &bs, const uint16_t *X, int64_t M, const uint16_t *A,
                            const uint16_t *B, int32_t r, float s, const int64_t *group_offsets,
                            uint16_t *Y, uint16_t *Z, uint16_t *Y_base, uint16_t *Y_lora,
                            void *workspace, size_t workspace_bytes, void *stream) {
-  TRY(check_common(W, M, r, s, group_offsets));
+  TRY(check_common(bs, M, r, s, group_offsets));
+  const lora4_W *W = bs.W;
   if (!A || !B || (M > 0 && (!X || !Y))) return LORA4_ERR_NULL;
   for (const void *q : {(const void *)X, (const void *)A, (const void *)B, (const void *)Y, (const void *)Z,
                         (const void *)Y_base, (const void *)Y_lora, (const void *)group_offsets})
     if (q && !aligned16(q)) return LORA4_ERR_ALIGN;
-  const Plan pl = make_plan(0, W, M, r);
+  const Plan pl = make_plan(0, bs, M, r);
   if (!workspace) return LORA4_ERR_WORKSPACE;
   if (!aligned16(workspace)) return LORA4_ERR_ALIGN;
   if (workspace_bytes < pl.bytes) return LORA4_ERR_WORKSPACE;
@@ -777,7 +802,7 @@ lora4_status lora4_forward(const lora4_W *W, const uint16_t *X, int64_t M, const
 
   NtParams p{};
   p.A = mat(X, pl.K);
-  p.W = packed_of(W);
+  p.W = packed_of(bs);
   p.R = pl.K;
   p.A2 = mat(sZ, r);
   p.B2 = mat(B, r, pl.N * r);
@@ -808,17 +833,18 @@ lora4_status lora4_forward(const lora4_W *W, const uint16_t *X, int64_t M, const
   return LORA4_OK;
 }
 
-lora4_status lora4_backward(const lora4_W *W, const uint16_t *X, const uint16_t *dY, int64_t M,
+static lora4_status backward_impl(const Base &bs, const uint16_t *X, const uint16_t *dY, int64_t M,
                             const uint16_t *A, const uint16_t *B, int32_t r, float s,
                             const int64_t *group_offsets, const uint16_t *Z, uint16_t *dX,
                             uint16_t *dA, uint16_t *dB, void *workspace, size_t workspace_bytes,
                             void *stream) {
-  TRY(check_common(W, M, r, s, group_offsets));
+  TRY(check_common(bs, M, r, s, group_offsets));
+  const lora4_W *W = bs.W;
   if (!A || !B || !dA || !dB || (M > 0 && (!X || !dY || !dX))) return LORA4_ERR_NULL;
   for (const void *q : {(const void *)X, (const void *)dY, (const void *)A, (const void *)B, (const void *)Z,
                         (const void *)dX, (const void *)dA, (const void *)dB, (const void *)group_offsets})
     if (q && !aligned16(q)) return LORA4_ERR_ALIGN;
-  const Plan pl = make_plan(1, W, M, r);
+  const Plan pl = make_plan(1, bs, M, r);
   if (!workspace) return LORA4_ERR_WORKSPACE;
   if (!aligned16(workspace)) return LORA4_ERR_ALIGN;
   if (workspace_bytes < pl.bytes) return LORA4_ERR_WORKSPACE;
@@ -846,7 +872,7 @@ lora4_status lora4_backward(const lora4_W *W, const uint16_t *X, const uint16_t 
   float *skpart = ws_at<float>(workspace, pl.off_skpart);
   const SkSched dzs = sk_sched(M, pl.N, r, pl.E);
   const bool dz_tail = dzs.ranges > 1 && dzs.ranges <= big::A2_MAX_PARTS &&
-                       dgrad_taken(pl.N, pl.N, M, packed_of(W), pl.K, pl.E);
+                       dgrad_taken(pl.N, pl.N, M, packed_of(bs), pl.K, pl.E);
   const TailParts dztp{skpart, dzs.ranges, s, dZ, s, nullptr, 0.0f};
   TRY(rows_skinny(1, dY, pl.N, B, r, pl.N * r, pl.N, M, r, group_offsets, pl.E, dZ, s, nullptr, 0.0f, skpart,
                   dz_tail, st));
@@ -855,7 +881,7 @@ lora4_status lora4_backward(const lora4_W *W, const uint16_t *X, const uint16_t 
   {
     NnParams p{};
     p.A = mat(dY, pl.N);
-    p.W = packed_of(W);
+    p.W = packed_of(bs);
     p.R = pl.N;
     p.A2 = mat(dZ, r);
     p.B2 = mat(A, pl.K, (int64_t)r * pl.K);
@@ -901,6 +927,43 @@ lora4_status lora4_backward(const lora4_W *W, const uint16_t *X, const uint16_t 
                     (int64_t)r, pl.N, dB, s));
   }
   return LORA4_OK;
+}
+
+lora4_status lora4_forward(const lora4_W *W, const uint16_t *X, int64_t M, const uint16_t *A,
+                           const uint16_t *B, int32_t r, float s, const int64_t *group_offsets,
+                           uint16_t *Y, uint16_t *Z, uint16_t *Y_base, uint16_t *Y_lora,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  if (!W) return LORA4_ERR_NULL;
+  return forward_impl(Base{W, W->groups, false}, X, M, A, B, r, s, group_offsets, Y, Z, Y_base, Y_lora, workspace,
+                      workspace_bytes, stream);
+}
+
+lora4_status lora4_backward(const lora4_W *W, const uint16_t *X, const uint16_t *dY, int64_t M,
+                            const uint16_t *A, const uint16_t *B, int32_t r, float s,
+                            const int64_t *group_offsets, const uint16_t *Z, uint16_t *dX,
+                            uint16_t *dA, uint16_t *dB, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+  if (!W) return LORA4_ERR_NULL;
+  return backward_impl(Base{W, W->groups, false}, X, dY, M, A, B, r, s, group_offsets, Z, dX, dA, dB, workspace,
+                       workspace_bytes, stream);
+}
+
+lora4_status lora4_forward_multi(const lora4_W *W, int64_t adapters, const uint16_t *X, int64_t M,
+                                 const uint16_t *A, const uint16_t *B, int32_t r, float s,
+                                 const int64_t *adapter_offsets, uint16_t *Y, uint16_t *Z, uint16_t *Y_base,
+                                 uint16_t *Y_lora, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!W) return LORA4_ERR_NULL;
+  return forward_impl(Base{W, adapters, true}, X, M, A, B, r, s, adapter_offsets, Y, Z, Y_base, Y_lora, workspace,
+                      workspace_bytes, stream);
+}
+
+lora4_status lora4_backward_multi(const lora4_W *W, int64_t adapters, const uint16_t *X, const uint16_t *dY,
+                                  int64_t M, const uint16_t *A, const uint16_t *B, int32_t r, float s,
+                                  const int64_t *adapter_offsets, const uint16_t *Z, uint16_t *dX, uint16_t *dA,
+                                  uint16_t *dB, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!W) return LORA4_ERR_NULL;
+  return backward_impl(Base{W, adapters, true}, X, dY, M, A, B, r, s, adapter_offsets, Z, dX, dA, dB, workspace,
+                       workspace_bytes, stream);
 }
 
 size_t lora4_packed_bytes(int32_t format, int64_t N, int64_t K, int32_t part) {

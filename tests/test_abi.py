@@ -140,3 +140,38 @@ def test_packed_bytes(lib):
     for bad in [(L.LORA4_NF4, 10, 96, 0), (L.LORA4_MXFP4, 0, 64, 0), (L.LORA4_MXFP4, 8, 48, 0), (9, 64, 64, 0),
                 (L.LORA4_NF4, 64, 64, 3)]:
         assert L.lora4_packed_bytes(*bad) == 0, bad
+
+
+def test_multi_adapter_validation(lib):
+    """Several adapters over one shared base: W must be one group, adapters in
+    range, offsets required for more than one adapter (nothing is launched)."""
+    args = dict(X=4096, M=16, A=4096, B=4096, r=16, s=2.0, offs=None, Y=4096, Z=None, Yb=None, Yl=None,
+                ws=8192, nbytes=1 << 30, stream=None)
+
+    def fwd(W, adapters, **kw):
+        a = dict(args, **kw)
+        return L.lora4_forward_multi(W, adapters, a["X"], a["M"], a["A"], a["B"], a["r"], a["s"], a["offs"],
+                                     a["Y"], a["Z"], a["Yb"], a["Yl"], a["ws"], a["nbytes"], a["stream"])
+
+    def bwd(W, adapters, **kw):
+        a = dict(X=4096, dY=4096, M=16, A=4096, B=4096, r=16, s=2.0, offs=None, Z=None, dX=4096, dA=4096,
+                 dB=4096, ws=8192, nbytes=1 << 30, stream=None)
+        a.update(kw)
+        return L.lora4_backward_multi(W, adapters, a["X"], a["dY"], a["M"], a["A"], a["B"], a["r"], a["s"],
+                                      a["offs"], a["Z"], a["dX"], a["dA"], a["dB"], a["ws"], a["nbytes"],
+                                      a["stream"])
+
+    assert fwd(_W(groups=2), 4, offs=4096) == ESHAPE       # the base is one shared group
+    assert fwd(_W(), 0) == ESHAPE
+    assert fwd(_W(), 70000, offs=4096) == ESHAPE
+    assert fwd(_W(), 4) == ENULL                           # several adapters need offsets
+    assert fwd(_W(), 1, offs=4096) == ESHAPE               # one adapter takes none
+    assert fwd(_W(), 4, offs=4096, M=0) == OK              # nothing to launch
+    assert bwd(_W(groups=3), 2, offs=4096) == ESHAPE
+    assert bwd(_W(), 3) == ENULL
+    assert bwd(_W(), 3, offs=4096, dA=None) == ENULL
+    W = _W()
+    assert L.lora4_workspace_bytes_multi(0, W, 4, 1024, 16) > 0
+    assert L.lora4_workspace_bytes_multi(1, W, 4, 1024, 16) > 0
+    assert L.lora4_workspace_bytes_multi(0, W, 0, 1024, 16) == 0
+    assert L.lora4_workspace_bytes_multi(0, _W(groups=2), 4, 1024, 16) == 0
