@@ -23,7 +23,7 @@ import time
 
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
-WORKLOADS = {"single": 1, "llama8b": 2, "llama70b": 3, "moe": 4, "longctx": 5}
+WORKLOADS = {"single": 1, "llama8b": 2, "llama70b": 3, "moe": 4, "longctx": 5, "multilora": 6}
 
 
 def log(*a):
@@ -77,22 +77,37 @@ class Layer:
         self.dA = torch.empty_like(self.A)
         self.dB = torch.empty_like(self.B)
         self.W = self.base.abi()
-        self.ws_bytes = max(L.lora4_workspace_bytes(0, self.W, M, r), L.lora4_workspace_bytes(1, self.W, M, r))
+        if spec.shared_base:
+            self.ws_bytes = max(L.lora4_workspace_bytes_multi(0, self.W, E, M, r),
+                                L.lora4_workspace_bytes_multi(1, self.W, E, M, r))
+        else:
+            self.ws_bytes = max(L.lora4_workspace_bytes(0, self.W, M, r), L.lora4_workspace_bytes(1, self.W, M, r))
 
     def fwd(self, L, ws, stream):
         s = self.spec
-        st = L.lora4_forward(self.W, self.X.data_ptr(), s.M, self.A.data_ptr(), self.B.data_ptr(), s.r, s.s,
-                             None if self.offs is None else self.offs.data_ptr(), self.Y.data_ptr(),
-                             self.Z.data_ptr(), None, None, ws.data_ptr(), ws.numel(), stream)
+        if s.shared_base:
+            st = L.lora4_forward_multi(self.W, s.experts, self.X.data_ptr(), s.M, self.A.data_ptr(),
+                                       self.B.data_ptr(), s.r, s.s, self.offs.data_ptr(), self.Y.data_ptr(),
+                                       self.Z.data_ptr(), None, None, ws.data_ptr(), ws.numel(), stream)
+        else:
+            st = L.lora4_forward(self.W, self.X.data_ptr(), s.M, self.A.data_ptr(), self.B.data_ptr(), s.r, s.s,
+                                 None if self.offs is None else self.offs.data_ptr(), self.Y.data_ptr(),
+                                 self.Z.data_ptr(), None, None, ws.data_ptr(), ws.numel(), stream)
         if st:
             raise RuntimeError(f"lora4_forward failed: {L.status_string(st)}")
 
     def bwd(self, L, ws, stream):
         s = self.spec
-        st = L.lora4_backward(self.W, self.X.data_ptr(), self.dY.data_ptr(), s.M, self.A.data_ptr(),
-                              self.B.data_ptr(), s.r, s.s, None if self.offs is None else self.offs.data_ptr(),
-                              self.Z.data_ptr(), self.dX.data_ptr(), self.dA.data_ptr(), self.dB.data_ptr(),
-                              ws.data_ptr(), ws.numel(), stream)
+        if s.shared_base:
+            st = L.lora4_backward_multi(self.W, s.experts, self.X.data_ptr(), self.dY.data_ptr(), s.M,
+                                        self.A.data_ptr(), self.B.data_ptr(), s.r, s.s, self.offs.data_ptr(),
+                                        self.Z.data_ptr(), self.dX.data_ptr(), self.dA.data_ptr(),
+                                        self.dB.data_ptr(), ws.data_ptr(), ws.numel(), stream)
+        else:
+            st = L.lora4_backward(self.W, self.X.data_ptr(), self.dY.data_ptr(), s.M, self.A.data_ptr(),
+                                  self.B.data_ptr(), s.r, s.s, None if self.offs is None else self.offs.data_ptr(),
+                                  self.Z.data_ptr(), self.dX.data_ptr(), self.dA.data_ptr(), self.dB.data_ptr(),
+                                  ws.data_ptr(), ws.numel(), stream)
         if st:
             raise RuntimeError(f"lora4_backward failed: {L.status_string(st)}")
 
@@ -117,7 +132,7 @@ def kernel_bytes(name, spec):
     the rank-r passes' activation reads and small operands; the packed base
     (codes + scales) for the two dequant-GEMMs."""
     M, N, K, r, E = spec.M, spec.N, spec.K, spec.r, spec.experts
-    wp = E * N * K * BITS_PER_WEIGHT[spec.fmt] / 8
+    wp = (1 if spec.shared_base else E) * N * K * BITS_PER_WEIGHT[spec.fmt] / 8
     return {
         "rows_skinny_z": 2 * M * K + 2 * E * r * K + 2 * M * r,       # X, A -> Z
         "rows_skinny_dz": 2 * M * N + 2 * E * N * r + 2 * M * r,      # dY, B -> dZ
@@ -220,9 +235,9 @@ def cpu_baseline(specs, tokens, reps):
     for spec in specs:
         t = synth.inputs(spec)
         E = spec.experts
-        Ws = t["W"] if E > 1 else t["W"][None]
+        Ws = t["W"] if E > 1 and not spec.shared_base else t["W"][None]
         packs = []
-        for e in range(E):
+        for e in range(len(Ws)):
             if spec.fmt == synth.MXFP4:
                 packs.append(mxfp4.quantize(Ws[e]))
             else:
@@ -403,12 +418,13 @@ def main():
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "config": {
             "workload": {1: "single NF4 linear", 2: "Llama-3-8B-shaped layer set", 3: "Llama-70B-shaped MXFP4 layers",
-                         4: "MoE grouped experts", 5: "long-context skinny rank"}[wl],
+                         4: "MoE grouped experts", 5: "long-context skinny rank", 6: "16 LoRA adapters over each Llama-3-8B-shaped base"}[wl],
             "tokens": s0.M,
             "format": s0.fmt,
             "rank": s0.r,
             "alpha": s0.alpha,
-            "experts": s0.experts,
+            "experts": 1 if s0.shared_base else s0.experts,
+            "adapters": s0.experts if s0.shared_base else 1,
             "layers_KxN": [[s.K, s.N] for s in specs],
             "gflop_per_step": round(flops / 1e9, 2),
         },

@@ -57,7 +57,51 @@ struct Params {
   float A2alpha1;
   uint16_t *A2out2;
   float A2alpha2;
+  // 1: one W for every row group (adapters over one base): the output tiles
+  // ignore the groups, and the rank-r part runs once per group that has rows
+  // in the tile, with that group's B2 (forward) or A (dgrad). The kernels
+  // take it as a template argument (SHARED) too, so that the per-group code
+  // is compiled only where it runs.
+  int shared_rows;
 };
+
+// Row tile of block slot: per group (experts), or over all M rows when the
+// groups share W.
+template <bool SHARED>
+__device__ __forceinline__ RowTile tile_rows(const Params &p, int slot, int BM) {
+  return SHARED ? map_row_tile(slot, BM, nullptr, 1, p.M) : map_row_tile(slot, BM, p.offsets, p.groups, p.M);
+}
+
+// The group holding row `row` (offsets non-decreasing, [0] = 0, [groups] = M):
+// the last g with offsets[g] <= row.
+__device__ __forceinline__ int group_of_row(const int64_t *offsets, int groups, int64_t row) {
+  int lo = 0, hi = groups - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (offsets[mid] <= row) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Calls f(group, ra, rb) for each group with rows [ra, rb) (non-empty) in
+// the row range [row0, row_hi) of a tile that ignores the groups, in group
+// order, with a barrier between calls (f stages through LDS). (Tiles ignore
+// the groups only where there are several, so offsets is given.)
+template <typename F>
+__device__ __forceinline__ void for_tile_groups(const Params &p, int64_t row0, int64_t row_hi, F &&f) {
+  const int g_lo = group_of_row(p.offsets, p.groups, row0);
+  const int g_hi = group_of_row(p.offsets, p.groups, row_hi - 1);
+  bool first = true;
+  for (int gg = g_lo; gg <= g_hi; ++gg) {
+    const int64_t ra = p.offsets[gg] > row0 ? p.offsets[gg] : row0;
+    const int64_t rb = p.offsets[gg + 1] < row_hi ? p.offsets[gg + 1] : row_hi;
+    if (ra >= rb) continue;
+    if (!first) __syncthreads();
+    first = false;
+    f(gg, ra, rb);
+  }
+}
 
 constexpr int A2_MAX_PARTS = 4;
 
@@ -139,13 +183,14 @@ __device__ __forceinline__ void store_a2_piece(uint16_t *out, int r2, int64_t gr
 }
 
 // One 64-column step (k0 ..) of the tail operand from the partials into the
-// LDS tile `As` (256 rows, bf16, 8-column chunk c of row i at
-// As + lds_off(i, c)): thread t owns row t; chunks past r2 are zero.
-template <typename Off>
+// LDS tile `As` (256 rows from row0, bf16, 8-column chunk c of row i at
+// As + lds_off(i, c)): thread t owns row row0 + t; rows outside [ra, rb) and
+// chunks past r2 are zero. (LO: ra may lie above row0; else ra == row0.)
+template <bool LO, typename Off>
 __device__ __forceinline__ void a2_parts_to_lds(const Params &p, uint16_t *As, Off lds_off, int64_t row0,
-                                                int64_t row_end, int k0, int t, bool store_out) {
+                                                int64_t ra, int64_t rb, int k0, int t, bool store_out) {
   const int64_t gr = row0 + t;
-  const bool row_ok = gr < row_end;
+  const bool row_ok = (!LO || gr >= ra) && gr < rb;
 #pragma unroll 1
   for (int c0 = 0; c0 < 8; c0 += 2) {
     float v[2][8];

@@ -74,7 +74,8 @@ struct WRaw {
   uint32_t c2;   // DQ second level (fp32 bits)
 };
 
-template <int FMT>
+// SHARED: the row tiles ignore the groups (Params::shared_rows).
+template <int FMT, bool SHARED>
 __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const uint32_t sel = big::sel_base();
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
   }
   int tn, slot;
   big::grouped_tile(b, p.tiles_n, p.nblocks / p.tiles_n, slot, tn);
-  const RowTile rt = map_row_tile(slot, BM, p.offsets, p.groups, p.M);
+  const RowTile rt = big::tile_rows<SHARED>(p, slot, BM);
   if (rt.group < 0) return;
   const int g = rt.group;
   const int64_t row0 = rt.row0, row_end = rt.row_end;
@@ -421,60 +422,68 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
   __syncthreads();
 
   // ---- rank-r tail: dZ A, plain bf16 steps through LDS -----------------------
+  // Where the row tiles ignore the groups (one base for several adapters),
+  // each group with rows in the tile adds its own product over its rows only.
   if (p.r2 > 0) {
-    const uint16_t *B2 = p.B2.p + g * p.B2.gstride;
     const bool a_vec = (p.A2.ld % 8) == 0;
     const bool b_vec = (p.B2.ld % 8) == 0;
-    for (int k0 = 0; k0 < p.r2; k0 += BKS) {
-      if (p.A2part) {
-        big::a2_parts_to_lds(p, As0, [](int i, int c) { return swz(i, c); }, row0, row_end, k0, t, col0 == 0);
-      } else {
+    // tile rows [ra, rb) times group gg's B2 (ra == row0 unless SHARED); ends
+    // with a barrier, so the stages are free again
+    auto rank_r = [&](int gg, int64_t ra, int64_t rb) {
+      const uint16_t *B2 = p.B2.p + gg * p.B2.gstride;
+      for (int k0 = 0; k0 < p.r2; k0 += BKS) {
+        if (p.A2part) {
+          big::a2_parts_to_lds<SHARED>(p, As0, [](int i, int c) { return swz(i, c); }, row0, ra, rb, k0, t, col0 == 0);
+        } else {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const int idx = t + THREADS * c;
+            const int row = idx >> 3, chunk = idx & 7;
+            u32x4_t v = {0u, 0u, 0u, 0u};
+            const int64_t gr = row0 + row;
+            const int64_t gk = k0 + chunk * 8;
+            if ((!SHARED || gr >= ra) && gr < rb && gk < p.r2) {
+              const uint16_t *src = p.A2.p + gr * p.A2.ld + gk;
+              if (a_vec && gk + 8 <= p.r2) {
+                v = *reinterpret_cast<const u32x4_t *>(src);
+              } else {
+                uint32_t w4[4] = {0u, 0u, 0u, 0u};
+                for (int e = 0; e < 8; ++e)
+                  if (gk + e < p.r2) w4[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+                v = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
+              }
+            }
+            lds_write_b128(As0 + swz(row, chunk), v);
+          }
+        }
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           const int idx = t + THREADS * c;
-          const int row = idx >> 3, chunk = idx & 7;
+          const int row = idx >> 5, cc = (idx & 31) * 8;
           u32x4_t v = {0u, 0u, 0u, 0u};
-          const int64_t gr = row0 + row;
-          const int64_t gk = k0 + chunk * 8;
-          if (gr < row_end && gk < p.r2) {
-            const uint16_t *src = p.A2.p + gr * p.A2.ld + gk;
-            if (a_vec && gk + 8 <= p.r2) {
+          const int64_t gr = k0 + row;
+          const int64_t gc = col0 + cc;
+          if (gr < p.r2 && gc < p.Nc) {
+            const uint16_t *src = B2 + gr * p.B2.ld + gc;
+            if (b_vec && gc + 8 <= p.Nc) {
               v = *reinterpret_cast<const u32x4_t *>(src);
             } else {
               uint32_t w4[4] = {0u, 0u, 0u, 0u};
               for (int e = 0; e < 8; ++e)
-                if (gk + e < p.r2) w4[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+                if (gc + e < p.Nc) w4[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
               v = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
             }
           }
-          lds_write_b128(As0 + swz(row, chunk), v);
+          lds_write_b128(Bs0 + wt_off(row, cc), v);
         }
+        __syncthreads();
+        // sub-step kk covers reduction rows k0 + 16 kk .. +15: only those below r2
+        compute_step(As0, Bs0, min(4, (p.r2 - k0 + 15) / 16));
+        __syncthreads();
       }
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int idx = t + THREADS * c;
-        const int row = idx >> 5, cc = (idx & 31) * 8;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        const int64_t gr = k0 + row;
-        const int64_t gc = col0 + cc;
-        if (gr < p.r2 && gc < p.Nc) {
-          const uint16_t *src = B2 + gr * p.B2.ld + gc;
-          if (b_vec && gc + 8 <= p.Nc) {
-            v = *reinterpret_cast<const u32x4_t *>(src);
-          } else {
-            uint32_t w4[4] = {0u, 0u, 0u, 0u};
-            for (int e = 0; e < 8; ++e)
-              if (gc + e < p.Nc) w4[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
-            v = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
-          }
-        }
-        lds_write_b128(Bs0 + wt_off(row, cc), v);
-      }
-      __syncthreads();
-      // sub-step kk covers reduction rows k0 + 16 kk .. +15: only those below r2
-      compute_step(As0, Bs0, min(4, (p.r2 - k0 + 15) / 16));
-      __syncthreads();
-    }
+    };
+    if constexpr (SHARED) big::for_tile_groups(p, row0, min(row0 + BM, row_end), rank_r);
+    else rank_r(g, row0, row_end);
   }
 
   // ---- epilogue: register e of acc[j][i] holds

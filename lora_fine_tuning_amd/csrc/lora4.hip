@@ -273,7 +273,7 @@ PackedW packed_of(const Base &b) {
 // Planning: split factors and workspace layout
 // ---------------------------------------------------------------------------
 
-constexpr int TARGET_WG = 1024;  // workgroups wanted for the skinny passes
+constexpr int TARGET_WG = 1024;  // workgroups wanted for the rank-r TN passes (dA, dB)
 
 int skinny_tile(int r) { return r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : 128; }
 
@@ -415,7 +415,7 @@ FwdSched fwd_sched(int64_t M, int64_t N, int64_t K, int64_t E, const PackedW &W)
   const int pol = big_policy();
   if (pol == 0) return f;
   const int64_t cus = cu_count();
-  const int64_t tiles = (ceil_div(M, fwd::BM) + (E > 1 ? E : 0)) * ceil_div(N, fwd::BN);
+  const int64_t tiles = (ceil_div(M, fwd::BM) + (E > 1 && !W.shared ? E : 0)) * ceil_div(N, fwd::BN);
   const int64_t steps = ceil_div(K, fwd::BKS);
   const int64_t max_ks = std::min<int64_t>(16, std::max<int64_t>(1, steps / 8));
   int64_t whole = tiles, split = 0, ks = 1;
@@ -448,13 +448,18 @@ bool use_big(int64_t M, int64_t Nc, int64_t E) {
 }
 
 // Forward base GEMM with deq(W) decoded straight into MFMA registers.
-template <int FMT>
+template <int FMT, bool SHARED>
 lora4_status run_fwd(const big::Params &p, hipStream_t st) {
   if (p.ksplit > 1)
-    return launch_lds("gemm_nt_base", fwd::k_gemm_fwd<FMT, true>, dim3((unsigned)p.nblocks), dim3(fwd::THREADS),
-                      (size_t)fwd::lds_bytes(), p, st);
-  return launch_lds("gemm_nt_base", fwd::k_gemm_fwd<FMT, false>, dim3((unsigned)p.nblocks), dim3(fwd::THREADS),
-                    (size_t)fwd::lds_bytes(), p, st);
+    return launch_lds("gemm_nt_base", fwd::k_gemm_fwd<FMT, true, SHARED>, dim3((unsigned)p.nblocks),
+                      dim3(fwd::THREADS), (size_t)fwd::lds_bytes(), p, st);
+  return launch_lds("gemm_nt_base", fwd::k_gemm_fwd<FMT, false, SHARED>, dim3((unsigned)p.nblocks),
+                    dim3(fwd::THREADS), (size_t)fwd::lds_bytes(), p, st);
+}
+
+template <int FMT>
+lora4_status run_fwd(const big::Params &p, hipStream_t st) {
+  return p.shared_rows ? run_fwd<FMT, true>(p, st) : run_fwd<FMT, false>(p, st);
 }
 
 lora4_status run_fwd_fmt(int fmt, const big::Params &p, hipStream_t st) {
@@ -469,8 +474,11 @@ lora4_status run_fwd_fmt(int fmt, const big::Params &p, hipStream_t st) {
 // Input-gradient base GEMM (deq(W) through a transposed LDS tile).
 template <int FMT>
 lora4_status run_dgrad(const big::Params &p, hipStream_t st) {
-  return launch_lds("gemm_nn_dgrad", dgrad::k_gemm_dgrad<FMT>, dim3((unsigned)p.nblocks), dim3(dgrad::THREADS),
-                    (size_t)dgrad::lds_bytes(), p, st);
+  if (p.shared_rows)
+    return launch_lds("gemm_nn_dgrad", dgrad::k_gemm_dgrad<FMT, true>, dim3((unsigned)p.nblocks),
+                      dim3(dgrad::THREADS), (size_t)dgrad::lds_bytes(), p, st);
+  return launch_lds("gemm_nn_dgrad", dgrad::k_gemm_dgrad<FMT, false>, dim3((unsigned)p.nblocks),
+                    dim3(dgrad::THREADS), (size_t)dgrad::lds_bytes(), p, st);
 }
 
 lora4_status run_dgrad_fmt(int fmt, const big::Params &p, hipStream_t st) {
@@ -498,7 +506,10 @@ big::Params big_params(const Mat &A, const PackedW &W, int64_t R, const Mat &A2,
   p.C = C;
   p.ldc = ldc;
   p.tiles_n = (int)ceil_div(Nc, big::BN);
-  p.nblocks = (int)((ceil_div(std::max<int64_t>(M, 1), big::BM) + (E > 1 ? E : 0)) * p.tiles_n);
+  // one W for every group: the row tiles run over all M rows, regardless of
+  // the groups (which then only select the rank-r operands)
+  p.shared_rows = W.shared && E > 1 ? 1 : 0;
+  p.nblocks = (int)((ceil_div(std::max<int64_t>(M, 1), big::BM) + (E > 1 && !p.shared_rows ? E : 0)) * p.tiles_n);
   p.tab = nf4_table();
   p.ksplit = 1;
   p.split_steps = 1 << 30;
@@ -534,7 +545,7 @@ void apply_tail_parts(big::Params &q, const TailParts *tp) {
 // their tail operand as partials).
 bool fwd_regs_taken(int64_t R, const Plan &pl) { return R > 0 && pl.fs.use; }
 bool dgrad_taken(int64_t R, int64_t ld_a, int64_t M, const PackedW &W, int64_t Nc, int64_t E) {
-  return R > 0 && big_fits(ld_a, M, W) && use_big(M, Nc, E);
+  return R > 0 && big_fits(ld_a, M, W) && use_big(M, Nc, W.shared ? 1 : E);
 }
 
 // Forward base GEMM: the register-direct kernel as the plan schedules it

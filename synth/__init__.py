@@ -18,6 +18,10 @@ Workloads (rows ``M`` are tokens, a layer is ``K = d_in -> N = d_out``):
    groups, one per expert.
 5. ``longctx``: M=32768 tokens, 5120->5120, NF4 with double-quantized
    scales, rank 128, alpha 256.
+6. ``multilora``: the ``llama8b`` layer set with 16 rank-16 adapters over
+   each layer's one NF4 base, the 4096 tokens split among the adapters at
+   15 cut points drawn uniformly without replacement (groups of 1 to ~700
+   rows).
 
 Distributions (all drawn in float32 and rounded to bf16, round to nearest
 even): X ~ N(0,1), dY ~ N(0,1), W ~ N(0, 0.02) (NF4 workloads) or
@@ -49,6 +53,7 @@ class Layer:
     w_std: float
     experts: int = 1
     offsets: Optional[List[int]] = field(default=None)
+    shared_base: bool = False        # groups are adapters over one W (not experts)
 
     @property
     def s(self):
@@ -63,7 +68,7 @@ class Layer:
         return 4 * self.M * self.N * self.K + 6 * self.M * self.r * (self.N + self.K)
 
 
-WORKLOAD_NAMES = {1: "single", 2: "llama8b", 3: "llama70b", 4: "moe", 5: "longctx"}
+WORKLOAD_NAMES = {1: "single", 2: "llama8b", 3: "llama70b", 4: "moe", 5: "longctx", 6: "multilora"}
 
 
 def moe_routing(tokens=4096, experts=64, topk=8, seed=1000 * 4 + TID["logits"]):
@@ -101,6 +106,14 @@ def layers(workload):
                 for i, (n, k, nn) in enumerate(shapes)]
     if w == 5:
         return [Layer(5, 0, "proj", 32768, 5120, 5120, 128, 256.0, NF4_DQ, 0.02)]
+    if w == 6:
+        rng = np.random.Generator(np.random.PCG64(1000 * 6 + TID["logits"]))
+        cuts = np.sort(rng.choice(np.arange(1, 4096), 15, replace=False))
+        offs = [0] + [int(c) for c in cuts] + [4096]
+        shapes = [("q", 4096, 4096), ("k", 4096, 1024), ("v", 4096, 1024), ("o", 4096, 4096),
+                  ("gate", 4096, 14336), ("up", 4096, 14336), ("down", 14336, 4096)]
+        return [Layer(6, i, n, 4096, k, nn, 16, 32.0, NF4, 0.02, experts=16, offsets=offs, shared_base=True)
+                for i, (n, k, nn) in enumerate(shapes)]
     raise ValueError(f"unknown workload {workload}")
 
 
@@ -130,7 +143,8 @@ def draw(workload, layer, name, shape, dist, scale):
 
 
 def inputs(lay, names=("X", "W", "A", "B", "dY")):
-    """bf16 inputs of one layer. Grouped layers stack W, A, B per expert."""
+    """bf16 inputs of one layer. Grouped layers stack W, A, B per expert;
+    layers whose groups share one base stack only A and B."""
     E = lay.experts
     out = {}
     for nm in names:
@@ -139,7 +153,7 @@ def inputs(lay, names=("X", "W", "A", "B", "dY")):
         elif nm == "dY":
             out[nm] = draw(lay.workload, lay.index, "dY", (lay.M, lay.N), "normal", 1.0)
         elif nm == "W":
-            shape = (lay.N, lay.K) if E == 1 else (E, lay.N, lay.K)
+            shape = (lay.N, lay.K) if E == 1 or lay.shared_base else (E, lay.N, lay.K)
             out[nm] = draw(lay.workload, lay.index, "W", shape, "normal", lay.w_std)
         elif nm == "A":
             shape = (lay.r, lay.K) if E == 1 else (E, lay.r, lay.K)

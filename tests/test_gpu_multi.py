@@ -43,9 +43,17 @@ def _case(fmt, M, K, N, r, offs, index):
     return lay, t, W, got
 
 
+OFFSETS = {
+    "four": [0, 100, 100, 260, 300],                # one adapter with no rows
+    # twelve adapters, several inside one 256-row tile, empty ones at both ends
+    "twelve": [0, 0, 7, 30, 31, 64, 128, 129, 200, 250, 299, 300, 300],
+}
+
+
 @pytest.mark.parametrize("fmt", [synth.NF4, synth.MXFP4, synth.NF4_DQ])
-def test_adapters_over_one_base(fmt, tiles):
-    offs = [0, 100, 100, 260, 300]                  # four adapters, one with no rows
+@pytest.mark.parametrize("cut", sorted(OFFSETS))
+def test_adapters_over_one_base(fmt, cut, tiles):
+    offs = OFFSETS[cut]
     lay, t, W, got = _case(fmt, 300, 512, 384, 16, offs, index=51)
     print_case("multi", fmt, offs)
     G = len(offs) - 1
