@@ -19,6 +19,8 @@ the source pages, cited by page title and section:
   tricks"), the memory table (section 3).
 * "Fine-Tuning 4-Bit Models: Adapting a Base That Only Ships Quantized":
   MXFP4 with a 32-element E8M0 block scale (section "Case 2").
+* The Crusoe post, "Forward pass in inference": the MXFP4-native base
+  product (activations as MXFP8, a reading; see ``mxfp8``).
 
 Floating-point products are evaluated in float64 on exactly representable
 bf16 inputs. Encodings (bf16 rounding, NF4, E4M3, E2M1, E8M0) are written out
@@ -35,10 +37,14 @@ Parity status per function (what pins it is listed in ``tests/``):
                      trips and the pages' bits-per-weight figures.
 * mxfp4.*            pinned by the OCP E2M1 value table, exhaustive code x
                      scale products and brute force.
+* mxfp8.*            pinned by torch's float8_e4m3fn conversion, the scale
+                     property, round trips of on-grid blocks, the zero and
+                     subnormal blocks, the plain forward on on-grid X and the
+                     E4M3 error bound.
 * lora.*             pinned by finite differences, pure-Python loops, the
                      merge identity and the B = 0 / A = 0 special cases.
 """
 
-from . import codecs, nf4, mxfp4, lora  # noqa: F401
+from . import codecs, nf4, mxfp4, lora, mxfp8  # noqa: F401
 
-__all__ = ["codecs", "nf4", "mxfp4", "lora"]
+__all__ = ["codecs", "nf4", "mxfp4", "lora", "mxfp8"]
