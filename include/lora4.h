@@ -214,6 +214,46 @@ lora4_status quant_pack_nf4(const uint16_t *W_bf16, int64_t N, int64_t K, int32_
 lora4_status quant_pack_mxfp4(const uint16_t *W_bf16, int64_t N, int64_t K,
                               uint8_t *codes, uint8_t *scales_e8m0, void *stream);
 
+/* ---- MX-native forward of an MXFP4 base -------------------------------------
+ * "Quantized weights, full precision", section "Forward pass in inference"
+ * (and "Forward pass in training": the same operations in the training
+ * forward): where the hardware has MXFP4-native operations the base product
+ * of an MXFP4 base runs natively while the adapters stay in bf16. The pages
+ * leave the activation format open; here X enters the base product as MXFP8
+ * (OCP MX v1.0): per 32 consecutive elements of a row the E8M0 code
+ * E = clamp(floor(log2 amax) - 8, -127, 127) + 127 (E = 0 for an all-zero
+ * block), and each element's E4M3 code is the nearest value to
+ * x * 2^-(E-127), ties to the even code, saturating at +-448, sign copied
+ * from x (-0 gives 0x80).
+ *
+ * Quantize bf16 X [M, K] (K % 32 == 0) to MXFP8, row-major:
+ *  codes       : uint8 [M, K] E4M3 codes.
+ *  scales_e8m0 : uint8 [M, K / 32].
+ * Device pointers, 16-byte aligned. M may be 0 (nothing is launched). */
+lora4_status quant_pack_mxfp8(const uint16_t *X, int64_t M, int64_t K, uint8_t *codes,
+                              uint8_t *scales_e8m0, void *stream);
+
+/* Workspace (bytes) that lora4_forward_mx needs for this W, M tokens and rank
+ * r (0 for invalid arguments). */
+size_t lora4_workspace_bytes_mx(const lora4_W *W, int64_t M, int32_t r);
+
+/* MX-native forward of one plain layer (W->format == LORA4_MXFP4,
+ * W->groups == 1):
+ *   Y = mxfp8(X) deq(W)^T + s (X A^T) B^T,  Z = X A^T
+ * The base product runs on the block-scaled MFMA with X as MXFP8 (quantized
+ * into the workspace) and W's E2M1 codes and E8M0 scales as stored; Z and the
+ * LoRA term use the bf16 X. Accumulation in fp32; Y rounded once to bf16.
+ *  X : bf16 [M, K]; A : bf16 [r, K]; B : bf16 [N, r]; 1 <= r <= 256; s finite.
+ *  Y : bf16 [M, N] output. Z : bf16 [M, r] output, may be NULL.
+ *  workspace, workspace_bytes : device scratch, >= lora4_workspace_bytes_mx.
+ * Errors: LORA4_ERR_FORMAT if W is not MXFP4, LORA4_ERR_SHAPE for grouped W
+ * or sizes past the 32-bit buffer offsets, and as lora4_forward otherwise.
+ * M may be 0: nothing is launched, and X, Y may then be NULL. */
+lora4_status lora4_forward_mx(const lora4_W *W, const uint16_t *X, int64_t M,
+                              const uint16_t *A, const uint16_t *B, int32_t r, float s,
+                              uint16_t *Y, uint16_t *Z, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
 /* A static, human-readable name for a status code. */
 const char *lora4_status_string(lora4_status status);
 

@@ -27,8 +27,8 @@ BLOCK = {LORA4_NF4: 64, LORA4_NF4_DQ: 64, LORA4_MXFP4: 32}
 
 EXPORTS = ["lora4_forward", "lora4_backward", "lora4_workspace_bytes", "lora4_packed_bytes",
            "lora4_forward_multi", "lora4_backward_multi", "lora4_workspace_bytes_multi", "quant_pack_nf4",
-           "quant_pack_mxfp4", "lora4_status_string", "lora4_timing_enable", "lora4_timing_collect",
-           "lora4_version"]
+           "quant_pack_mxfp4", "quant_pack_mxfp8", "lora4_workspace_bytes_mx", "lora4_forward_mx",
+           "lora4_status_string", "lora4_timing_enable", "lora4_timing_collect", "lora4_version"]
 
 
 class Lora4Error(RuntimeError):
@@ -77,6 +77,12 @@ def lib():
         L.quant_pack_nf4.restype = ctypes.c_int
         L.quant_pack_mxfp4.argtypes = [vp, i64, i64, vp, vp, vp]
         L.quant_pack_mxfp4.restype = ctypes.c_int
+        L.quant_pack_mxfp8.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.quant_pack_mxfp8.restype = ctypes.c_int
+        L.lora4_workspace_bytes_mx.argtypes = [Wp, i64, i32]
+        L.lora4_workspace_bytes_mx.restype = sz
+        L.lora4_forward_mx.argtypes = [Wp, vp, i64, vp, vp, i32, f32, vp, vp, vp, sz, vp]
+        L.lora4_forward_mx.restype = ctypes.c_int
         L.lora4_status_string.argtypes = [ctypes.c_int]
         L.lora4_status_string.restype = ctypes.c_char_p
         L.lora4_timing_enable.argtypes = [ctypes.c_int]
@@ -143,6 +149,18 @@ def quant_pack_nf4(W_bf16, N, K, double_quant, codes, scales, scales2, stream):
 
 def quant_pack_mxfp4(W_bf16, N, K, codes, scales_e8m0, stream):
     return lib().quant_pack_mxfp4(W_bf16, N, K, codes, scales_e8m0, stream)
+
+
+def quant_pack_mxfp8(X, M, K, codes, scales_e8m0, stream):
+    return lib().quant_pack_mxfp8(X, M, K, codes, scales_e8m0, stream)
+
+
+def lora4_workspace_bytes_mx(W, M, r):
+    return lib().lora4_workspace_bytes_mx(ctypes.byref(W), M, r)
+
+
+def lora4_forward_mx(W, X, M, A, B, r, s, Y, Z, workspace, workspace_bytes, stream):
+    return lib().lora4_forward_mx(ctypes.byref(W), X, M, A, B, r, s, Y, Z, workspace, workspace_bytes, stream)
 
 
 def timing_enable(on=True):
@@ -319,3 +337,35 @@ def backward(base, X, dY, A, B, s, Z=None, group_offsets=None, workspace=None):
                         _ptr(dX), _ptr(dA), _ptr(dB), _ptr(workspace), workspace.numel(), _stream())
     _check(st, "lora4_backward")
     return {"dX": dX, "dA": dA, "dB": dB}
+
+
+def mxfp8(X):
+    """bf16 X [M, K] (K % 32 == 0, on the GPU) -> MXFP8 E4M3 codes [M, K] and
+    E8M0 scales [M, K / 32], both uint8."""
+    import torch
+    M, K = X.shape
+    codes = torch.empty((M, K), dtype=torch.uint8, device=X.device)
+    scales = torch.empty((M, K // 32), dtype=torch.uint8, device=X.device)
+    _check(quant_pack_mxfp8(_ptr(X), M, K, _ptr(codes), _ptr(scales), _stream()), "quant_pack_mxfp8")
+    return codes, scales
+
+
+def forward_mx(base, X, A, B, s, want_z=True, workspace=None):
+    """MX-native forward of a plain MXFP4 layer: Y (and Z) for bf16 X [M, K],
+    A [r, K], B [N, r]; the base product takes X as MXFP8."""
+    import torch
+    M = X.shape[0]
+    r = A.shape[-2]
+    dev = X.device
+    Y = torch.empty((M, base.N), dtype=torch.bfloat16, device=dev)
+    Z = torch.empty((M, r), dtype=torch.bfloat16, device=dev) if want_z else None
+    W = base.abi()
+    if workspace is None:
+        n = lora4_workspace_bytes_mx(W, M, r)
+        if n == 0:
+            raise ValueError("invalid arguments for lora4_workspace_bytes_mx")
+        workspace = torch.empty((n,), dtype=torch.uint8, device=dev)
+    st = lora4_forward_mx(W, _ptr(X), M, _ptr(A), _ptr(B), r, float(s), _ptr(Y), _ptr(Z), _ptr(workspace),
+                          workspace.numel(), _stream())
+    _check(st, "lora4_forward_mx")
+    return {"Y": Y, "Z": Z}

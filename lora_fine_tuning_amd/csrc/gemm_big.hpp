@@ -63,6 +63,12 @@ struct Params {
   // take it as a template argument (SHARED) too, so that the per-group code
   // is compiled only where it runs.
   int shared_rows;
+  // MX-native forward: X as MXFP8, E4M3 codes [rows padded to 256][ld8]
+  // (zero padding; ld8 = K rounded up to 64) and E8M0 scales in the order
+  // k_quant_mxfp8 writes for the GEMM
+  const uint8_t *X8;
+  const uint8_t *X8s;
+  int64_t ld8;
 };
 
 // Row tile of block slot: per group (experts), or over all M rows when the

@@ -31,6 +31,7 @@
 #include "gemm_big.hpp"
 #include "gemm_fwd.hpp"
 #include "gemm_dgrad.hpp"
+#include "mx.hpp"
 #include "skinny.hpp"
 #include "quant.hpp"
 
@@ -742,6 +743,79 @@ lora4_status check_common(const Base &b, int64_t M, int32_t r, float s, const in
   return LORA4_OK;
 }
 
+// ---------------------------------------------------------------------------
+// MX-native forward: MXFP8 activations times an MXFP4 base on the scaled MFMA
+// ---------------------------------------------------------------------------
+
+// Split schedule of the MX GEMM: the same rule as the bf16 forward's (few
+// output tiles split the reduction), without its choice of tile path.
+FwdSched mx_sched(int64_t M, int64_t N, int64_t K) {
+  FwdSched f{true, 0, 0, 1, 1 << 30};
+  const int64_t cus = cu_count();
+  const int64_t tiles = ceil_div(std::max<int64_t>(M, 1), mx::BM) * ceil_div(N, mx::BN);
+  const int64_t steps = ceil_div(K, mx::BKS);
+  const int64_t max_ks = std::min<int64_t>(16, std::max<int64_t>(1, steps / 8));
+  int64_t ks = 1;
+  if (tiles < cus * 3 / 4) {
+    ks = std::min<int64_t>(cus / tiles, max_ks);
+    const int64_t cap = ((int64_t)256 << 20) / ((int64_t)mx::BM * mx::BN * 4 * tiles);
+    ks = std::max<int64_t>(1, std::min(ks, cap));
+  }
+  if (ks > 1) {
+    f.split_tiles = (int)tiles;
+    f.split_steps = (int)ceil_div(steps, ks);
+    f.ksplit = (int)ceil_div(steps, f.split_steps);
+  } else {
+    f.whole_tiles = (int)tiles;
+  }
+  return f;
+}
+
+// Workspace of the MX forward: the plain forward's s Z and rank-r partials,
+// then the split partials, the MXFP8 codes [Mp][Kp] and their scales.
+struct MxPlan {
+  Plan pl;
+  FwdSched fs;
+  int64_t Mp, Kp;
+  size_t off_party, off_x8, off_xs, bytes;
+};
+
+MxPlan make_mx_plan(const lora4_W *W, int64_t M, int r) {
+  MxPlan q;
+  q.pl = make_plan(0, Base{W, 1, false}, M, r);
+  q.fs = mx_sched(M, W->N, W->K);
+  q.Mp = ceil_div(std::max<int64_t>(M, 1), mx::BM) * mx::BM;
+  q.Kp = ceil_div(W->K, mx::BKS) * mx::BKS;
+  size_t off = q.pl.off_party;
+  q.off_party = off;
+  if (q.fs.split_tiles > 0) off += align256((size_t)q.fs.split_tiles * q.fs.ksplit * mx::BM * mx::BN * 4);
+  q.off_x8 = off;
+  off += align256((size_t)q.Mp * q.Kp);
+  q.off_xs = off;
+  off += align256((size_t)(q.Kp / 64) * (q.Mp / 256) * 512);
+  q.bytes = off;
+  return q;
+}
+
+lora4_status check_mx(const lora4_W *W, int64_t M, int32_t r, float s) {
+  TRY(check_common(Base{W, 1, false}, M, r, s, nullptr));
+  if (W->format != LORA4_MXFP4) return LORA4_ERR_FORMAT;
+  if (W->groups != 1) return LORA4_ERR_SHAPE;
+  // 32-bit buffer offsets: one row tile of codes, the scale table, the base
+  const int64_t Mp = ceil_div(std::max<int64_t>(M, 1), mx::BM) * mx::BM, Kp = ceil_div(W->K, mx::BKS) * mx::BKS;
+  if ((int64_t)mx::BM * Kp > 0x7FFFFFFF || (Kp / 64) * (Mp / 256) * 512 > 0x7FFFFFFF) return LORA4_ERR_SHAPE;
+  if (w_blocks(W->K) * 2048 > 0x7FFFFFFF) return LORA4_ERR_SHAPE;
+  return LORA4_OK;
+}
+
+template <bool GEMM>
+lora4_status run_quant_mxfp8(const uint16_t *X, int64_t ldx, int64_t M, int64_t K, uint8_t *codes, int64_t ldc,
+                             int64_t Mp, int64_t Kp, uint8_t *scales, hipStream_t st) {
+  const int64_t n = Mp * (Kp / 8);
+  return launch_args("quant_mxfp8", mx::k_quant_mxfp8<GEMM>, dim3((unsigned)ceil_div(n, 256)), dim3(256), st, X,
+                     ldx, M, K, codes, ldc, Mp, Kp, scales);
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -1030,6 +1104,69 @@ lora4_status quant_pack_mxfp4(const uint16_t *W_bf16, int64_t N, int64_t K, uint
   const int64_t nblk = N * (K / 32);
   return launch_args("quant_pack_mxfp4", k_quant_mxfp4, dim3((unsigned)ceil_div(nblk, 256)), dim3(256), st,
                      W_bf16, N, K, codes, scales_e8m0);
+}
+
+lora4_status quant_pack_mxfp8(const uint16_t *X, int64_t M, int64_t K, uint8_t *codes, uint8_t *scales_e8m0,
+                              void *stream) {
+  if (M < 0 || K < 32 || K % 32 != 0 || M > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return LORA4_ERR_SHAPE;
+  if (M == 0) return LORA4_OK;
+  if (!X || !codes || !scales_e8m0) return LORA4_ERR_NULL;
+  if (!aligned16(X) || !aligned16(codes) || !aligned16(scales_e8m0)) return LORA4_ERR_ALIGN;
+  return run_quant_mxfp8<false>(X, K, M, K, codes, K, M, K, scales_e8m0, reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t lora4_workspace_bytes_mx(const lora4_W *W, int64_t M, int32_t r) {
+  if (check_mx(W, M, r, 1.0f) != LORA4_OK) return 0;
+  return make_mx_plan(W, M, r).bytes;
+}
+
+lora4_status lora4_forward_mx(const lora4_W *W, const uint16_t *X, int64_t M, const uint16_t *A, const uint16_t *B,
+                              int32_t r, float s, uint16_t *Y, uint16_t *Z, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+  TRY(check_mx(W, M, r, s));
+  if (!A || !B || (M > 0 && (!X || !Y))) return LORA4_ERR_NULL;
+  for (const void *q : {(const void *)X, (const void *)A, (const void *)B, (const void *)Y, (const void *)Z})
+    if (q && !aligned16(q)) return LORA4_ERR_ALIGN;
+  const MxPlan mp = make_mx_plan(W, M, r);
+  const Plan &pl = mp.pl;
+  if (!workspace) return LORA4_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LORA4_ERR_ALIGN;
+  if (workspace_bytes < mp.bytes) return LORA4_ERR_WORKSPACE;
+  if (M == 0) return LORA4_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+
+  uint8_t *x8 = ws_at<uint8_t>(workspace, mp.off_x8);
+  uint8_t *xs = ws_at<uint8_t>(workspace, mp.off_xs);
+  TRY(run_quant_mxfp8<true>(X, pl.K, M, pl.K, x8, mp.Kp, mp.Mp, mp.Kp, xs, st));
+
+  // Z = X A^T from the bf16 X; the GEMM adds the range partials itself
+  // where there are several (and its column-tile-0 blocks store Z)
+  uint16_t *sZ = ws_at<uint16_t>(workspace, pl.off_sz);
+  float *skpart = ws_at<float>(workspace, pl.off_skpart);
+  const SkSched zs = sk_sched(M, pl.K, r, 1);
+  const bool z_tail = zs.ranges > 1 && zs.ranges <= big::A2_MAX_PARTS;
+  const TailParts ztp{skpart, zs.ranges, s, Z, 1.0f, nullptr, 0.0f};
+  TRY(z_pass(pl, W, X, A, nullptr, Z, 1.0f, sZ, s, skpart, z_tail, st));
+
+  big::Params q = big_params(mat(X, pl.K), packed_of(Base{W, 1, false}), pl.K, mat(sZ, r), mat(B, r, pl.N * r), r, M,
+                             pl.N, nullptr, 1, Y, pl.N);
+  if (z_tail) apply_tail_parts(q, &ztp);
+  q.X8 = x8;
+  q.X8s = xs;
+  q.ld8 = mp.Kp;
+  q.ksplit = mp.fs.ksplit;
+  q.split_steps = mp.fs.split_steps;
+  q.nblocks = mp.fs.whole_tiles + mp.fs.split_tiles * mp.fs.ksplit;
+  q.Cpart = ws_at<float>(workspace, mp.off_party);
+  if (mp.fs.split_tiles > 0) {
+    TRY(launch_lds("gemm_mx_base", mx::k_gemm_fwd_mx<true>, dim3((unsigned)q.nblocks), dim3(mx::THREADS),
+                   (size_t)mx::lds_bytes(), q, st));
+    const int64_t n = (int64_t)mp.fs.split_tiles * mx::BM * (mx::BN / 4);
+    return launch_args("reduce_y", fwd::k_reduce_tiles, dim3((unsigned)ceil_div(n, 256)), dim3(256), st, q,
+                       mp.fs.split_tiles);
+  }
+  return launch_lds("gemm_mx_base", mx::k_gemm_fwd_mx<false>, dim3((unsigned)q.nblocks), dim3(mx::THREADS),
+                    (size_t)mx::lds_bytes(), q, st);
 }
 
 lora4_status lora4_timing_enable(int on) {

@@ -175,3 +175,37 @@ def test_multi_adapter_validation(lib):
     assert L.lora4_workspace_bytes_multi(1, W, 4, 1024, 16) > 0
     assert L.lora4_workspace_bytes_multi(0, W, 0, 1024, 16) == 0
     assert L.lora4_workspace_bytes_multi(0, _W(groups=2), 4, 1024, 16) == 0
+
+
+def test_mx_forward_validation(lib):
+    """MX-native forward: MXFP4 base only, one group, the workspace it asks
+    for; the MXFP8 packer wants K % 32 == 0 (nothing is launched)."""
+    W = _W(fmt=L.LORA4_MXFP4, block=32, N=1024, K=1024)
+    need = L.lora4_workspace_bytes_mx(W, 4096, 16)
+    # the MXFP8 codes [M, K] and their scales are part of the workspace
+    assert need >= 4096 * 1024 + 4096 * 1024 // 32
+    assert L.lora4_workspace_bytes_mx(_W(), 4096, 16) == 0                    # NF4 base
+    assert L.lora4_workspace_bytes_mx(_W(fmt=L.LORA4_MXFP4, block=32, groups=2), 16, 16) == 0
+
+    def fwd(Wd, **kw):
+        a = dict(X=4096, M=16, A=4096, B=4096, r=16, s=2.0, Y=4096, Z=None, ws=8192, nbytes=need, stream=None)
+        a.update(kw)
+        return L.lora4_forward_mx(Wd, a["X"], a["M"], a["A"], a["B"], a["r"], a["s"], a["Y"], a["Z"], a["ws"],
+                                  a["nbytes"], a["stream"])
+
+    assert fwd(_W()) == EFORMAT
+    assert fwd(_W(fmt=L.LORA4_MXFP4, block=32, groups=2)) == ESHAPE
+    assert fwd(W, r=0) == ESHAPE
+    assert fwd(W, s=float("nan")) == ESHAPE
+    assert fwd(W, A=None) == ENULL
+    assert fwd(W, Y=None) == ENULL
+    assert fwd(W, X=4100) == EALIGN
+    assert fwd(W, ws=None) == EWS
+    assert fwd(W, nbytes=need - 1, M=4096) == EWS
+    assert fwd(W, M=0, X=None, Y=None) == OK
+    assert L.quant_pack_mxfp8(4096, 16, 48, 4096, 4096, None) == ESHAPE
+    assert L.quant_pack_mxfp8(4096, 16, 16, 4096, 4096, None) == ESHAPE
+    assert L.quant_pack_mxfp8(4096, -1, 64, 4096, 4096, None) == ESHAPE
+    assert L.quant_pack_mxfp8(None, 16, 64, 4096, 4096, None) == ENULL
+    assert L.quant_pack_mxfp8(4096, 16, 64, 4104, 4096, None) == EALIGN
+    assert L.quant_pack_mxfp8(None, 0, 64, None, None, None) == OK
