@@ -22,6 +22,7 @@ import sys
 import time
 
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0         # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 WORKLOADS = {"single": 1, "llama8b": 2, "llama70b": 3, "moe": 4, "longctx": 5, "multilora": 6}
 
@@ -41,6 +42,9 @@ def parse():
     ap.add_argument("--cpu-reps", type=int, default=3, help="passes of the CPU oracle over its sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (counter calibration) and exit")
+    ap.add_argument("--mx", action="store_true",
+                    help="forward through the MX-native path (MXFP8 activations x MXFP4 base on the scaled "
+                         "MFMA); plain MXFP4 layer sets only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--blas-context", action="store_true",
@@ -52,8 +56,9 @@ def parse():
 class Layer:
     """Device buffers of one layer (inputs, outputs, packed base)."""
 
-    def __init__(self, spec, L, torch, synth):
+    def __init__(self, spec, L, torch, synth, mx=False):
         self.spec = spec
+        self.mx = mx
         t = synth.inputs(spec)
         dev = "cuda:0"
 
@@ -82,10 +87,15 @@ class Layer:
                                 L.lora4_workspace_bytes_multi(1, self.W, E, M, r))
         else:
             self.ws_bytes = max(L.lora4_workspace_bytes(0, self.W, M, r), L.lora4_workspace_bytes(1, self.W, M, r))
+        if mx:
+            self.ws_bytes = max(self.ws_bytes, L.lora4_workspace_bytes_mx(self.W, M, r))
 
     def fwd(self, L, ws, stream):
         s = self.spec
-        if s.shared_base:
+        if self.mx:
+            st = L.lora4_forward_mx(self.W, self.X.data_ptr(), s.M, self.A.data_ptr(), self.B.data_ptr(), s.r, s.s,
+                                    self.Y.data_ptr(), self.Z.data_ptr(), ws.data_ptr(), ws.numel(), stream)
+        elif s.shared_base:
             st = L.lora4_forward_multi(self.W, s.experts, self.X.data_ptr(), s.M, self.A.data_ptr(),
                                        self.B.data_ptr(), s.r, s.s, self.offs.data_ptr(), self.Y.data_ptr(),
                                        self.Z.data_ptr(), None, None, ws.data_ptr(), ws.numel(), stream)
@@ -117,6 +127,7 @@ def kernel_flops(name, spec):
     M, N, K, r = spec.M, spec.N, spec.K, spec.r
     return {
         "gemm_nt_base": 2 * M * N * K + 2 * M * N * r,     # X deq(W)^T + (sZ) B^T
+        "gemm_mx_base": 2 * M * N * K + 2 * M * N * r,     # mxfp8(X) W4^T + (sZ) B^T
         "gemm_nn_dgrad": 2 * M * N * K + 2 * M * K * r,    # dY deq(W) + dZ A
         "rows_skinny_z": 2 * M * K * r,                     # Z = X A^T
         "rows_skinny_dz": 2 * M * N * r,                    # dZ = s dY B
@@ -139,6 +150,8 @@ def kernel_bytes(name, spec):
         "gemm_tn_dA_dB": 2 * M * (K + N) + 4 * M * r,                 # X, dY, dZ, Z
         "gemm_nt_base": wp,
         "gemm_nn_dgrad": wp,
+        "gemm_mx_base": wp,
+        "quant_mxfp8": 2 * M * K + M * K + M * K // 32,                # X -> E4M3 codes + E8M0
     }.get(name, 0)
 
 
@@ -297,8 +310,11 @@ def main():
 
     wl = WORKLOADS[args.workload]
     specs = synth.layers(wl)
+    if args.mx and any(s.fmt != synth.MXFP4 or s.experts != 1 for s in specs):
+        print("--mx needs a workload of plain MXFP4 layers (llama70b)", file=sys.stderr)
+        sys.exit(2)
     log(f"[bench] workload {args.workload}: {len(specs)} layers, generating inputs")
-    layers = [Layer(s, L, torch, synth) for s in specs]
+    layers = [Layer(s, L, torch, synth, mx=args.mx) for s in specs]
     ws = torch.empty((max(l.ws_bytes for l in layers),), dtype=torch.uint8, device="cuda:0")
     stream = torch.cuda.current_stream().cuda_stream
     flops = sum(s.flops() for s in specs)
@@ -385,9 +401,11 @@ def main():
         n, tot = kt[dom]
         per_launch = kflops[dom] / len(specs)
         achieved = (kflops[dom] * args.steps) / (tot * 1e-3) / 1e12
-        tr = recorded_traffic(args.workload, dom)
-        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        tr = recorded_traffic(args.workload + ("_mx" if args.mx else ""), dom)
+        # the MX GEMM multiplies E4M3 by E2M1: it is priced at the fp8 dense peak
+        peak = PEAK_FP8_TFLOPS if dom == "gemm_mx_base" else PEAK_BF16_TFLOPS
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                     "traffic": None if tr is None else round(tr["bytes_per_launch"]),
                     "flops_per_launch_avg": per_launch, "avg_launch_us": round(1e3 * tot / n, 2),
                     "ms_per_step_with_events": round(ms_ev, 4)}
@@ -413,12 +431,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "mxfp8 x mxfp4 forward, bf16 backward" if args.mx else "bf16",
         "data": "synthetic",
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "config": {
             "workload": {1: "single NF4 linear", 2: "Llama-3-8B-shaped layer set", 3: "Llama-70B-shaped MXFP4 layers",
-                         4: "MoE grouped experts", 5: "long-context skinny rank", 6: "16 LoRA adapters over each Llama-3-8B-shaped base"}[wl],
+                         4: "MoE grouped experts", 5: "long-context skinny rank",
+                         6: "16 LoRA adapters over each Llama-3-8B-shaped base"}[wl]
+                        + (" (MX-native forward)" if args.mx else ""),
             "tokens": s0.M,
             "format": s0.fmt,
             "rank": s0.r,

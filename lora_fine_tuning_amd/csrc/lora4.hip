@@ -811,9 +811,10 @@ lora4_status check_mx(const lora4_W *W, int64_t M, int32_t r, float s) {
 template <bool GEMM>
 lora4_status run_quant_mxfp8(const uint16_t *X, int64_t ldx, int64_t M, int64_t K, uint8_t *codes, int64_t ldc,
                              int64_t Mp, int64_t Kp, uint8_t *scales, hipStream_t st) {
-  const int64_t n = Mp * (Kp / 8);
-  return launch_args("quant_mxfp8", mx::k_quant_mxfp8<GEMM>, dim3((unsigned)ceil_div(n, 256)), dim3(256), st, X,
-                     ldx, M, K, codes, ldc, Mp, Kp, scales);
+  const int64_t n = ceil_div(Mp, 256) * ceil_div(Kp, 256);   // one workgroup per 256 rows x 256 columns
+  if (n > 0x7FFFFFFF) return LORA4_ERR_SHAPE;
+  return launch_args("quant_mxfp8", mx::k_quant_mxfp8<GEMM>, dim3((unsigned)n), dim3(256), st, X, ldx, M, K, codes,
+                     ldc, Mp, Kp, scales);
 }
 
 }  // namespace

@@ -52,87 +52,75 @@ __device__ __forceinline__ int mx8_exponent(uint32_t a) {
   return x < -127 ? -127 : (x > 127 ? 127 : x);
 }
 
-// E4M3FN code of x * 2^-Xe (x given as bf16 bits): nearest, ties to even,
-// saturating at 448 (0x7E), sign bit copied (so -0 gives 0x80). Integer
-// arithmetic on the significand, exact for every input.
-__device__ __forceinline__ uint32_t mx8_code(uint32_t u, int Xe) {
-  const uint32_t sgn = (u >> 8) & 0x80u;
-  const int e = (int)((u >> 7) & 0xFFu);
-  uint32_t sig = u & 0x7Fu;
-  int E2;   // |x| * 2^-Xe = sig * 2^E2
-  if (e == 0) {
-    E2 = -133 - Xe;
-  } else {
-    sig |= 0x80u;
-    E2 = e - 134 - Xe;
-  }
-  if (sig == 0) return sgn;
-  const int L = (31 - __builtin_clz(sig)) + E2;   // floor(log2 v)
-  const int qe = L - 3 > -9 ? L - 3 : -9;          // exponent of the E4M3 quantum at v
-  const int sh = qe - E2;
-  uint32_t n;   // v / 2^qe rounded, 0 .. 16
-  if (sh <= 0) {
-    n = sig << (-sh);
-  } else if (sh >= 9) {
-    n = 0;   // sig < 2^8 <= 2^(sh-1): below half a quantum
-  } else {
-    const uint32_t q = sig >> sh, rem = sig & ((1u << sh) - 1u), half = 1u << (sh - 1);
-    n = q + ((rem > half || (rem == half && (q & 1u))) ? 1u : 0u);
-  }
-  if (n == 0) return sgn;
-  int ex = qe;
-  if (n >= 16) {   // rounded up into the next binade
-    n >>= 1;
-    ex += 1;
-  }
-  if (n < 8) return sgn | n;   // subnormal: n * 2^-9
-  const int ev = ex + 10;      // value (n / 8) * 2^(ex + 3), exponent bias 7
-  if (ev > 15 || (ev == 15 && n == 15)) return sgn | 0x7Eu;
-  return sgn | ((uint32_t)ev << 3) | (n - 8);
+// E4M3FN codes of two bf16 elements (the low and high halves of u) times
+// 2^-Xe: |x| 2^-Xe is exact in fp32 (a power-of-two scaling; Xe >= -127, so
+// 2^-Xe is a normal float), clamped to 448 and converted by v_cvt_pk_fp8_f32
+// (nearest, ties to even; every clamped value is in range); the sign bits are
+// copied from x afterwards, so -0 and negative values too small for E4M3 keep
+// their sign. Returns the two codes in the low 16 bits.
+__device__ __forceinline__ uint32_t mx8_code2(uint32_t u, float scale) {
+  const float f0 = fminf(fabsf(__uint_as_float(u << 16)) * scale, 448.0f);
+  const float f1 = fminf(fabsf(__uint_as_float(u & 0xFFFF0000u)) * scale, 448.0f);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false) & 0xFFFFu;
+  return c | ((u >> 8) & 0x80u) | ((u >> 16) & 0x8000u);
 }
 
-// X bf16 [M][ldx] -> E4M3 codes [Mp][ldc] and E8M0 scales, one thread per 8
-// elements, the 4 lanes of a quad holding one 32-element block (K % 32 == 0).
-// Rows [0, Mp) x columns [0, Kp) are written; outside [0, M) x [0, K) the
-// codes are 0 (and the GEMM-order scales 0). GEMM: scales in the GEMM's order
-// (step s = k / 64, row tile T = row / 256, half h = k / 32 % 2, then 32 rows
-// of 8 bytes: row % 32, block (row % 256) / 32), else row-major [M][K / 32].
+// X bf16 [M][ldx] -> E4M3 codes [Mp][ldc] and E8M0 scales (K % 32 == 0).
+// One workgroup per 256 rows x 256 columns; per pass the 256 threads cover
+// 8 rows x 256 columns, one thread per 8 elements, so every load instruction
+// reads whole 512-byte row segments; the 4 lanes of a quad hold one 32-element
+// block. Rows [0, Mp) x columns [0, Kp) are written; outside [0, M) x [0, K)
+// the codes are 0 (and the GEMM-order scales 0). GEMM: scales in the GEMM's
+// order (step s = k / 64, row tile T = row / 256, half h = k / 32 % 2, then 32
+// rows of 8 bytes: row % 32, block (row % 256) / 32), gathered in LDS and
+// written as whole 512-byte runs (Mp % 256 == 0); else row-major [M][K / 32].
 template <bool GEMM>
-__global__ void k_quant_mxfp8(const uint16_t *X, int64_t ldx, int64_t M, int64_t K, uint8_t *codes, int64_t ldc,
-                              int64_t Mp, int64_t Kp, uint8_t *scales) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t per_row = Kp >> 3;
-  const int64_t row = idx / per_row;
-  if (row >= Mp) return;   // (whole quads: per_row is a multiple of 4)
-  const int64_t k = (idx - row * per_row) * 8;
-  const bool in = row < M && k < K;
-  u32x4_t v = {0u, 0u, 0u, 0u};
-  if (in) v = *reinterpret_cast<const u32x4_t *>(X + row * ldx + k);
-  uint32_t a = 0;
+__global__ __launch_bounds__(256) void k_quant_mxfp8(const uint16_t *X, int64_t ldx, int64_t M, int64_t K,
+                                                     uint8_t *codes, int64_t ldc, int64_t Mp, int64_t Kp,
+                                                     uint8_t *scales) {
+  __shared__ uint8_t sc_lds[GEMM ? 4 * 512 : 4];
+  const int64_t CB = (Kp + 255) >> 8;   // 256-column chunks
+  const int64_t cb = blockIdx.x % CB, T = blockIdx.x / CB;
+  const int t = threadIdx.x;
+  const int64_t k = cb * 256 + (t & 31) * 8;
+  const int hh = (int)((k >> 5) & 1), sl = (t & 31) >> 3;   // block half, step within the chunk
+  for (int pass = 0; pass < 32; ++pass) {
+    const int rl = pass * 8 + (t >> 5);   // row within the tile
+    const int64_t row = T * 256 + rl;
+    const bool row_ok = row < Mp, col_ok = k < Kp;
+    const bool in = row < M && k < K;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (in) v = *reinterpret_cast<const u32x4_t *>(X + row * ldx + k);
+    uint32_t a = 0;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    a = max(a, v[e] & 0x7FFFu);
-    a = max(a, (v[e] >> 16) & 0x7FFFu);
+    for (int e = 0; e < 4; ++e) {
+      a = max(a, v[e] & 0x7FFFu);
+      a = max(a, (v[e] >> 16) & 0x7FFFu);
+    }
+    a = max(a, (uint32_t)__shfl_xor((int)a, 1));
+    a = max(a, (uint32_t)__shfl_xor((int)a, 2));
+    const int Xe = mx8_exponent(a);
+    const float scale = __uint_as_float((uint32_t)(127 - Xe) << 23);   // 2^-Xe
+    const uint32_t w0 = mx8_code2(v[0], scale) | (mx8_code2(v[1], scale) << 16);
+    const uint32_t w1 = mx8_code2(v[2], scale) | (mx8_code2(v[3], scale) << 16);
+    if (row_ok && col_ok) *reinterpret_cast<u32x2v_t *>(codes + row * ldc + k) = u32x2v_t{w0, w1};
+    if ((t & 3) == 0) {
+      const uint8_t E = (uint8_t)(Xe + 127);
+      if constexpr (GEMM) {
+        sc_lds[(sl * 2 + hh) * 256 + (rl & 31) * 8 + (rl >> 5)] = in ? E : (uint8_t)0;
+      } else if (in) {
+        scales[row * (K >> 5) + (k >> 5)] = E;
+      }
+    }
   }
-  a = max(a, (uint32_t)__shfl_xor((int)a, 1));
-  a = max(a, (uint32_t)__shfl_xor((int)a, 2));
-  const int Xe = mx8_exponent(a);
-  uint32_t w[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const uint32_t c0 = mx8_code(v[2 * q] & 0xFFFFu, Xe), c1 = mx8_code(v[2 * q] >> 16, Xe);
-    const uint32_t c2 = mx8_code(v[2 * q + 1] & 0xFFFFu, Xe), c3 = mx8_code(v[2 * q + 1] >> 16, Xe);
-    w[q] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
-  }
-  *reinterpret_cast<u32x2v_t *>(codes + row * ldc + k) = u32x2v_t{w[0], w[1]};
-  if ((threadIdx.x & 3) == 0) {
-    const uint8_t E = (uint8_t)(Xe + 127);
-    if constexpr (GEMM) {
-      const int64_t s = k >> 6, T = row >> 8;
-      const int hh = (int)((k >> 5) & 1), i = (int)((row >> 5) & 7), l = (int)(row & 31);
-      scales[((s * (Mp >> 8) + T) * 2 + hh) * 256 + l * 8 + i] = in ? E : (uint8_t)0;
-    } else if (in) {
-      scales[row * (K >> 5) + (k >> 5)] = E;
+  if constexpr (GEMM) {
+    __syncthreads();
+    // run s (4 per chunk) of 512 bytes: (h, row % 32, block) for step cb * 4 + s
+    const int run = t >> 6;
+    const int64_t s = cb * 4 + run;
+    if (s * 64 < Kp) {
+      const u32x2v_t q = *reinterpret_cast<const u32x2v_t *>(sc_lds + run * 512 + (t & 63) * 8);
+      *reinterpret_cast<u32x2v_t *>(scales + (s * (Mp >> 8) + T) * 512 + (t & 63) * 8) = q;
     }
   }
 }
