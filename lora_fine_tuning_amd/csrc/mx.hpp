@@ -28,7 +28,14 @@ using big::rsrc_t;
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2v_t __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 256, BN = 256, BKS = 64, THREADS = 256, STAGES = 4;
+#ifndef LORA4_MX_STAGES
+#define LORA4_MX_STAGES 5
+#endif
+#ifndef LORA4_MX_AHEAD
+#define LORA4_MX_AHEAD 4
+#endif
+// X stages in the LDS ring; steps ahead that W and the X scales are loaded
+constexpr int BM = 256, BN = 256, BKS = 64, THREADS = 256, STAGES = LORA4_MX_STAGES, AHEAD = LORA4_MX_AHEAD;
 constexpr int TILE8 = BM * BKS;        // one MXFP8 X stage, bytes
 constexpr int ZTILE = BM * BKS * 2;    // bf16 staging tile of the rank-r product, bytes
 constexpr int EPI = 4 * BM * 64 * 2;   // epilogue: each wave's 256 x 64 bf16 block
@@ -241,9 +248,9 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd_mx(Params p) {
 
 #pragma unroll
   for (int s = 0; s < STAGES; ++s) issue_x(s, s);
-  MxRegs g0, g1;
-  load_regs(0, g0);
-  load_regs(1, g1);
+  MxRegs g[AHEAD];
+#pragma unroll
+  for (int u = 0; u < AHEAD; ++u) load_regs(u, g[u]);
 
   // ---- rank-r product (s Z) B^T into the zeroed accumulators (split 0),
   // bf16 MFMAs: Z rows through the staging tile, B rows to registers; lane
@@ -329,12 +336,14 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd_mx(Params p) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) read_x(0, i);
 
-  // At the start of step s the X of step s + 1 (issued during step s - 3)
-  // and the registers of step s (issued at the end of step s - 2) must have
-  // landed; still in flight may be what step s - 1 issued: its X (4 loads)
-  // and the registers of step s + 1 (5 loads). lgkmcnt 0: this wave's reads
-  // of the stage refilled below have returned.
-  constexpr int VM_OUT = 9;
+  // At the start of step s the X of step s + 1 (issued during step
+  // s + 1 - STAGES) and the registers of step s (issued at the end of step
+  // s - AHEAD) must have landed; still in flight may be what the AHEAD - 1
+  // steps after that issued: 4 X loads and 5 register loads each
+  // (STAGES - 1 >= AHEAD, so the X of step s + 1 is older than those).
+  // lgkmcnt 0: this wave's reads of the stage refilled below have returned.
+  static_assert(STAGES - 1 >= AHEAD && AHEAD >= 2, "load distances");
+  constexpr int VM_OUT = (AHEAD - 1) * 9;
   constexpr int VMCNT = (VM_OUT & 15) | (7 << 4) | (0 << 8) | ((VM_OUT >> 4) << 14);
   auto step = [&](int s, MxRegs &g) {
     __builtin_amdgcn_s_waitcnt(VMCNT);
@@ -342,8 +351,8 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd_mx(Params p) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     // every wave has read stage s % 4 (during step s - 1): refill it
-    issue_x(s + STAGES, s & (STAGES - 1));
-    const int nxt = (s + 1) & (STAGES - 1);
+    issue_x(s + STAGES, s % STAGES);
+    const int nxt = (s + 1) % STAGES;
     i32x8_t w[2];
     int sw[2];
 #pragma unroll
@@ -358,14 +367,17 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd_mx(Params p) {
       acc[i][1] = mfma_scale_fp4_fp8(w[1], xf[i], acc[i][1], sw[1], sx);
       read_x(nxt, i);
     }
-    load_regs(s + 2, g);
+    load_regs(s + AHEAD, g);
   };
+  // AHEAD register sets in rotation (the loop is unrolled AHEAD times)
   int s = 0;
-  for (; s + 2 <= steps; s += 2) {
-    step(s, g0);
-    step(s + 1, g1);
+  for (; s + AHEAD <= steps; s += AHEAD) {
+#pragma unroll
+    for (int u = 0; u < AHEAD; ++u) step(s + u, g[u]);
   }
-  if (s < steps) step(s, g0);
+#pragma unroll
+  for (int u = 0; u < AHEAD - 1; ++u)
+    if (s + u < steps) step(s + u, g[u]);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
