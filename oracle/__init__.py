@@ -19,6 +19,9 @@ the source pages, cited by page title and section:
   tricks"), the memory table (section 3).
 * "Fine-Tuning 4-Bit Models: Adapting a Base That Only Ships Quantized":
   MXFP4 with a 32-element E8M0 block scale (section "Case 2").
+* "Fine-Tuning 4-Bit Models", section "Case 2: An NVFP4 deployment
+  checkpoint is what you were handed": NVFP4, E2M1 with an FP8 scale per
+  16-element micro-block (see ``nvfp4`` for the readings).
 * The Crusoe post, "Forward pass in inference": the MXFP4-native base
   product (activations as MXFP8, a reading; see ``mxfp8``).
 
@@ -37,6 +40,10 @@ Parity status per function (what pins it is listed in ``tests/``):
                      trips and the pages' bits-per-weight figures.
 * mxfp4.*            pinned by the OCP E2M1 value table, exhaustive code x
                      scale products and brute force.
+* nvfp4.*            pinned by torch's float8_e4m3fn rounding of amax / 6,
+                     brute-force nearest elements, exact tie midpoints, on-grid
+                     round trips, exact dequant and the page's finer-than-MXFP4
+                     claim on Gaussian weights.
 * mxfp8.*            pinned by torch's float8_e4m3fn conversion, the scale
                      property, round trips of on-grid blocks, the zero and
                      subnormal blocks, the plain forward on on-grid X and the
@@ -45,6 +52,6 @@ Parity status per function (what pins it is listed in ``tests/``):
                      merge identity and the B = 0 / A = 0 special cases.
 """
 
-from . import codecs, nf4, mxfp4, lora, mxfp8  # noqa: F401
+from . import codecs, nf4, mxfp4, nvfp4, lora, mxfp8  # noqa: F401
 
-__all__ = ["codecs", "nf4", "mxfp4", "lora", "mxfp8"]
+__all__ = ["codecs", "nf4", "mxfp4", "nvfp4", "lora", "mxfp8"]
