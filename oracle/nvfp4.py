@@ -48,6 +48,9 @@ def encode_codes(w_bf16, sc_e4m3, block=BLOCK):
     s = np.repeat(e4m3_decode(sc_e4m3), block, axis=1)
     with np.errstate(divide="ignore", invalid="ignore"):
         a = np.where(s > 0, np.abs(w) / np.where(s > 0, s, 1.0), 0.0)
+    # saturate first: where the scale itself saturated (amax / 6 > 448), w / s
+    # can be so large that the distances to the 8 magnitudes no longer differ
+    a = np.minimum(a, 6.0)
     d = np.abs(a[..., None] - _MAGS)
     dmin = d.min(axis=-1, keepdims=True)
     codes = np.arange(8)

@@ -113,3 +113,20 @@ def test_finer_than_mxfp4_on_gaussian_weights():
     e_nv = err(nvfp4.dequantize(*nvfp4.quantize(w)))
     e_mx = err(mxfp4.dequantize(*mxfp4.quantize(w)))
     assert e_nv < e_mx, (e_nv, e_mx)
+
+
+def test_saturation_of_scale_and_elements():
+    """Blocks whose amax / 6 exceeds 448: the scale saturates at 448 and every
+    element past 6 * 448 takes the largest magnitude, sign kept."""
+    row = np.array([3e38, -3e38, 1e30, -5000.0, 2688.0, 2689.0, 100.0, -1.0] * 2, np.float32)
+    w = to_bf16(row[None, :])
+    packed, sc = nvfp4.quantize(w)
+    assert sc[0, 0] == 0x7E
+    c = unpack_nibbles(packed)[0]
+    wf = codecs.bf16_to_f32(w)[0].astype(np.float64)
+    for j in range(16):
+        a = min(abs(wf[j]) / 448.0, 6.0)
+        want = min(range(8), key=lambda m: (abs(a - E2M1[m]), m % 2))
+        assert c[j] & 7 == want, (j, wf[j])
+        assert c[j] >> 3 == (1 if wf[j] < 0 else 0)
+    assert c[0] == 7 and c[1] == 15 and c[2] == 7 and c[3] == 15
