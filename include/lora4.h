@@ -58,11 +58,16 @@ extern "C" {
  *                 double quantization).
  *  LORA4_MXFP4  : E2M1 codes with one E8M0 scale per 32 consecutive
  *                 K-elements ("Fine-Tuning 4-Bit Models", section "Case 2").
+ *  LORA4_NVFP4  : E2M1 codes with one E4M3 (FP8) scale per 16 consecutive
+ *                 K-elements, no per-tensor scale ("Fine-Tuning 4-Bit Models",
+ *                 section "Case 2: An NVFP4 deployment checkpoint is what you
+ *                 were handed"); K % 32 == 0.
  */
 typedef enum {
   LORA4_NF4 = 1,
   LORA4_NF4_DQ = 2,
-  LORA4_MXFP4 = 3
+  LORA4_MXFP4 = 3,
+  LORA4_NVFP4 = 4
 } lora4_format;
 
 typedef enum {
@@ -77,8 +82,10 @@ typedef enum {
 } lora4_status;
 
 /* The frozen 4-bit base W, logically [N = d_out, K = d_in] per group.
- *  format, block : LORA4_NF4 / LORA4_NF4_DQ with block 64, LORA4_MXFP4 with 32.
- *  N, K          : rows and columns of one group; K % block == 0, K >= block.
+ *  format, block : LORA4_NF4 / LORA4_NF4_DQ with block 64, LORA4_MXFP4 with 32,
+ *                  LORA4_NVFP4 with 16.
+ *  N, K          : rows and columns of one group; K % block == 0, K >= block
+ *                  (NVFP4: K % 32 == 0).
  *  groups        : 1 for a plain linear; E for E experts stored back to back,
  *                  each taking lora4_packed_bytes(format, N, K, part) bytes
  *                  of codes (part 0), scales (1) and scales2 (2).
@@ -95,13 +102,17 @@ typedef enum {
  *                  MXFP4  : uint8 E8M0 codes (value 2^(E-127)), 128 per tile
  *                           at 128*t; entry 2i+h = the scale of elements
  *                           32h .. 32h+31 of row i
+ *                  NVFP4  : uint8 E4M3 codes, 256 per tile at 256*t; entry
+ *                           4i+q = the scale of elements 16q .. 16q+15 of
+ *                           row i
  *  scales2       : NF4_DQ only: float [groups][ceil(N*K/64 / 256)], the
  *                  second-level scale of each run of 256 consecutive
  *                  first-level scales of one group, counted in row-major
  *                  order (row n, block b: n*(K/64) + b); the rebuilt scale
  *                  is fp32(E4M3(code) * scales2). NULL otherwise.
  * The dequantized element is bf16(fp32(q[code] * scale)) for NF4 (q the
- * 16-level NF4 codebook) and bf16(e2m1(code) * 2^(E-127)) for MXFP4. The
+ * 16-level NF4 codebook), bf16(e2m1(code) * 2^(E-127)) for MXFP4 and
+ * bf16(e2m1(code) * e4m3(scale)) (exact) for NVFP4. The
  * tiles let every global load of codes in the GEMMs cover whole contiguous
  * rows of a tile (the kernels read one tile per wave and step).
  */
@@ -253,6 +264,19 @@ lora4_status lora4_forward_mx(const lora4_W *W, const uint16_t *X, int64_t M,
                               const uint16_t *A, const uint16_t *B, int32_t r, float s,
                               uint16_t *Y, uint16_t *Z, void *workspace, size_t workspace_bytes,
                               void *stream);
+
+/* Quantize a bf16 base W [N, K] (K % 32 == 0) to NVFP4 ("Fine-Tuning 4-Bit
+ * Models", section "Case 2: An NVFP4 deployment checkpoint is what you were
+ * handed": an FP8 scale per 16-element micro-block). No per-tensor scale: per
+ * 16-element block the E4M3 code of amax / 6 (nearest, ties to even,
+ * saturating at 448; 0 for an all-zero block), and each element's E2M1 code
+ * is the nearest value to w / s with s that code's value (ties to the even
+ * code, saturating at +-6, sign copied; magnitude 0 where s == 0).
+ *  codes, scales_e4m3 : the tiled layout of lora4_W (256 scale bytes per
+ *  tile, row i's four at 4 i), sized by lora4_packed_bytes(LORA4_NVFP4, N,
+ *  K, 0 / 1); the padding is written as zero. */
+lora4_status quant_pack_nvfp4(const uint16_t *W_bf16, int64_t N, int64_t K,
+                              uint8_t *codes, uint8_t *scales_e4m3, void *stream);
 
 /* A static, human-readable name for a status code. */
 const char *lora4_status_string(lora4_status status);

@@ -21,13 +21,13 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblora4.so")
 
-LORA4_NF4, LORA4_NF4_DQ, LORA4_MXFP4 = 1, 2, 3
-FORMATS = {"nf4": LORA4_NF4, "nf4_dq": LORA4_NF4_DQ, "mxfp4": LORA4_MXFP4}
-BLOCK = {LORA4_NF4: 64, LORA4_NF4_DQ: 64, LORA4_MXFP4: 32}
+LORA4_NF4, LORA4_NF4_DQ, LORA4_MXFP4, LORA4_NVFP4 = 1, 2, 3, 4
+FORMATS = {"nf4": LORA4_NF4, "nf4_dq": LORA4_NF4_DQ, "mxfp4": LORA4_MXFP4, "nvfp4": LORA4_NVFP4}
+BLOCK = {LORA4_NF4: 64, LORA4_NF4_DQ: 64, LORA4_MXFP4: 32, LORA4_NVFP4: 16}
 
 EXPORTS = ["lora4_forward", "lora4_backward", "lora4_workspace_bytes", "lora4_packed_bytes",
            "lora4_forward_multi", "lora4_backward_multi", "lora4_workspace_bytes_multi", "quant_pack_nf4",
-           "quant_pack_mxfp4", "quant_pack_mxfp8", "lora4_workspace_bytes_mx", "lora4_forward_mx",
+           "quant_pack_mxfp4", "quant_pack_nvfp4", "quant_pack_mxfp8", "lora4_workspace_bytes_mx", "lora4_forward_mx",
            "lora4_status_string", "lora4_timing_enable", "lora4_timing_collect", "lora4_version"]
 
 
@@ -77,6 +77,8 @@ def lib():
         L.quant_pack_nf4.restype = ctypes.c_int
         L.quant_pack_mxfp4.argtypes = [vp, i64, i64, vp, vp, vp]
         L.quant_pack_mxfp4.restype = ctypes.c_int
+        L.quant_pack_nvfp4.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.quant_pack_nvfp4.restype = ctypes.c_int
         L.quant_pack_mxfp8.argtypes = [vp, i64, i64, vp, vp, vp]
         L.quant_pack_mxfp8.restype = ctypes.c_int
         L.lora4_workspace_bytes_mx.argtypes = [Wp, i64, i32]
@@ -149,6 +151,10 @@ def quant_pack_nf4(W_bf16, N, K, double_quant, codes, scales, scales2, stream):
 
 def quant_pack_mxfp4(W_bf16, N, K, codes, scales_e8m0, stream):
     return lib().quant_pack_mxfp4(W_bf16, N, K, codes, scales_e8m0, stream)
+
+
+def quant_pack_nvfp4(W_bf16, N, K, codes, scales_e4m3, stream):
+    return lib().quant_pack_nvfp4(W_bf16, N, K, codes, scales_e4m3, stream)
 
 
 def quant_pack_mxfp8(X, M, K, codes, scales_e8m0, stream):
@@ -249,6 +255,23 @@ def pack_mxfp4(W):
         _check(quant_pack_mxfp4(_ptr(Ws[e]), N, K, _ptr(codes[e]), _ptr(scales[e]), _stream()),
                "quant_pack_mxfp4")
     return PackedBase(LORA4_MXFP4, N, K, E, codes, scales, None)
+
+
+def pack_nvfp4(W):
+    """Quantize bf16 W ([N, K] or [E, N, K], on the GPU) to NVFP4 on the GPU."""
+    import torch
+    Ws = W if W.dim() == 3 else W.unsqueeze(0)
+    E, N, K = Ws.shape
+    dev = W.device
+    sizes = [lora4_packed_bytes(LORA4_NVFP4, N, K, part) for part in range(2)]
+    if sizes[0] == 0:
+        raise ValueError("invalid shape for NVFP4 packing")
+    codes = torch.empty((E, sizes[0]), dtype=torch.uint8, device=dev)
+    scales = torch.empty((E, sizes[1]), dtype=torch.uint8, device=dev)
+    for e in range(E):
+        _check(quant_pack_nvfp4(_ptr(Ws[e]), N, K, _ptr(codes[e]), _ptr(scales[e]), _stream()),
+               "quant_pack_nvfp4")
+    return PackedBase(LORA4_NVFP4, N, K, E, codes, scales, None)
 
 
 def workspace_for(which, base, M, r):

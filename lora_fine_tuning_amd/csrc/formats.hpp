@@ -25,7 +25,7 @@
 
 namespace lora4 {
 
-enum Fmt : int { FMT_BF16 = 0, FMT_NF4 = 1, FMT_NF4_DQ = 2, FMT_MXFP4 = 3 };
+enum Fmt : int { FMT_BF16 = 0, FMT_NF4 = 1, FMT_NF4_DQ = 2, FMT_MXFP4 = 3, FMT_NVFP4 = 4 };
 
 // The NF4 levels (ascending) and the 15 decision thresholds of the encoder.
 // thr[i] is the largest fp32 value not above the exact midpoint of levels i
@@ -80,6 +80,32 @@ __device__ __forceinline__ void dequant32_nf4(u32x4_t codes, float scale, const 
 
 // Dequantize 32 consecutive MXFP4 elements (16 code bytes) sharing one E8M0
 // scale into 16 words of bf16 pairs.
+// 8 E2M1 codes (one word) times an arbitrary fp32 scale into 4 bf16 pairs:
+// the convert's own scale operand applies only its exponent, so the codes are
+// converted to fp32 at scale 1 and multiplied by s (E2M1 x E4M3 has at most 6
+// significant bits: exact, and so is the bf16 rounding).
+template <int SEL>
+__device__ __forceinline__ uint32_t nvfp4_pair_t(uint32_t c, float s) {
+  const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, SEL);
+  return pack_bf16x2(f[0] * s, f[1] * s);
+}
+__device__ __forceinline__ u32x4_t decode8_nvfp4(uint32_t c, float s) {
+  return u32x4_t{nvfp4_pair_t<0>(c, s), nvfp4_pair_t<1>(c, s), nvfp4_pair_t<2>(c, s), nvfp4_pair_t<3>(c, s)};
+}
+
+// Dequantize 32 consecutive NVFP4 elements (16 code bytes) with the scales
+// s0 (elements 0..15) and s1 (16..31) into 16 words of bf16 pairs.
+__device__ __forceinline__ void dequant32_nvfp4(u32x4_t codes, float s0, float s1, uint32_t out[16]) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const u32x4_t v = decode8_nvfp4(codes[d], d < 2 ? s0 : s1);
+    out[4 * d + 0] = v[0];
+    out[4 * d + 1] = v[1];
+    out[4 * d + 2] = v[2];
+    out[4 * d + 3] = v[3];
+  }
+}
+
 __device__ __forceinline__ void dequant32_mxfp4(u32x4_t codes, float scale, uint32_t out[16]) {
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
@@ -113,12 +139,17 @@ __host__ __device__ constexpr int64_t w_scale64_idx(int64_t KB, int64_t n, int64
 __host__ __device__ constexpr int64_t w_scale32_idx(int64_t KB, int64_t n, int64_t k) {
   return (((n >> 6) * KB + (k >> 6)) << 7) + ((n & 63) << 1) + ((k >> 5) & 1);
 }
+// scale entry of the 16-element block of (n, k) (NVFP4: 256 per tile, row i's
+// four at 4 i)
+__host__ __device__ constexpr int64_t w_scale16_idx(int64_t KB, int64_t n, int64_t k) {
+  return (((n >> 6) * KB + (k >> 6)) << 8) + ((n & 63) << 2) + ((k >> 4) & 3);
+}
 
 // A packed base W as the kernels see it (one group; the kernels add the
 // group offsets).
 struct PackedW {
   const uint8_t *codes;   // [groups][RB KB tiles][64][32]
-  const void *scales;     // fp32 (NF4), e4m3 u8 (NF4_DQ), e8m0 u8 (MXFP4), tiled
+  const void *scales;     // fp32 (NF4), e4m3 u8 (NF4_DQ, NVFP4), e8m0 u8 (MXFP4), tiled
   const float *scales2;   // NF4_DQ second level, [groups][ceil(N*K/64/256)]
   int64_t N, K;
   int64_t KB;             // k blocks of 64
@@ -132,7 +163,8 @@ struct PackedW {
 __device__ __forceinline__ int w_group(const PackedW &w, int g) { return w.shared ? 0 : g; }
 
 // Scale of the block holding (row n, element k) of group g, as the fp32
-// operand the dequantizer needs (the E8M0 operand for MXFP4).
+// operand the dequantizer needs (the E8M0 operand for MXFP4; for NVFP4 the
+// 16-element block's E4M3 value).
 template <int FMT>
 __device__ __forceinline__ float block_scale(const PackedW &w, int g, int64_t n, int64_t k) {
   g = w_group(w, g);
@@ -145,6 +177,9 @@ __device__ __forceinline__ float block_scale(const PackedW &w, int g, int64_t n,
     const int64_t idx = n * (w.K >> 6) + (k >> 6);
     float c2 = w.scales2[g * w.g_scales2 + (idx >> 8)];
     return e4m3_to_f32(s[w_scale64_idx(w.KB, n, k)]) * c2;
+  } else if constexpr (FMT == FMT_NVFP4) {
+    const uint8_t *s = reinterpret_cast<const uint8_t *>(w.scales) + g * w.g_scales;
+    return e4m3_to_f32(s[w_scale16_idx(w.KB, n, k)]);
   } else {
     const uint8_t *s = reinterpret_cast<const uint8_t *>(w.scales) + g * w.g_scales;
     return e8m0_to_f32(s[w_scale32_idx(w.KB, n, k)]);
@@ -158,7 +193,9 @@ __device__ __forceinline__ void dequant_row32(const PackedW &w, int g, int64_t n
   const uint8_t *src = w.codes + w_group(w, g) * w.g_codes + w_code_off(w.KB, n, k);
   u32x4_t codes = ldg_b128_cached(src);
   float sc = block_scale<FMT>(w, g, n, k);
-  if constexpr (FMT == FMT_MXFP4) {
+  if constexpr (FMT == FMT_NVFP4) {
+    dequant32_nvfp4(codes, sc, block_scale<FMT>(w, g, n, k + 16), out);
+  } else if constexpr (FMT == FMT_MXFP4) {
     dequant32_mxfp4(codes, sc, out);
   } else {
     dequant32_nf4(codes, sc, qlds, out);

@@ -159,6 +159,7 @@ struct PackedSlabRegs {
   static constexpr int NT = ROWS * 2 / THREADS > 0 ? ROWS * 2 / THREADS : 1;
   u32x4_t codes[NT];
   float scale[NT];
+  float scale2[NT];   // NVFP4: elements 16..31 of the piece
 };
 
 // --------------------------------------------------------------------------
@@ -226,14 +227,16 @@ __global__ __launch_bounds__(THREADS) void k_gemm_nt(NtParams p) {
           int row = idx >> 1, half = idx & 1;
           int64_t n = col0 + row, k = k0 + half * 32;
           u32x4_t cz = {0u, 0u, 0u, 0u};
-          float sc = 0.f;
+          float sc = 0.f, sc2 = 0.f;
           if (idx < BN * 2 && n < p.Nc && k < re) {
             const uint8_t *src = p.W.codes + w_group(p.W, g) * p.W.g_codes + w_code_off(p.W.KB, n, k);
             cz = ldg_b128_cached(src);
             sc = block_scale<FMT>(p.W, g, n, k);
+            if constexpr (FMT == FMT_NVFP4) sc2 = block_scale<FMT>(p.W, g, n, k + 16);
           }
           rb_pk.codes[c] = cz;
           rb_pk.scale[c] = sc;
+          rb_pk.scale2[c] = sc2;
         }
       }
     } else {
@@ -254,7 +257,9 @@ __global__ __launch_bounds__(THREADS) void k_gemm_nt(NtParams p) {
         if (idx < BN * 2) {
           int row = idx >> 1, half = idx & 1;
           uint32_t w[16];
-          if constexpr (FMT == FMT_MXFP4) {
+          if constexpr (FMT == FMT_NVFP4) {
+            dequant32_nvfp4(rb_pk.codes[c], rb_pk.scale[c], rb_pk.scale2[c], w);
+          } else if constexpr (FMT == FMT_MXFP4) {
             dequant32_mxfp4(rb_pk.codes[c], rb_pk.scale[c], w);
           } else if constexpr (FMT != FMT_BF16) {
             dequant32_nf4(rb_pk.codes[c], rb_pk.scale[c], qlds, w);
@@ -376,6 +381,7 @@ struct PackedColSlabRegs {
   static constexpr int NT = (BK * TPR + THREADS - 1) / THREADS;
   u32x4_t codes[NT];
   float scale[NT];
+  float scale2[NT];   // NVFP4: elements 16..31 of the piece
 };
 
 // Operand fetch for a column-contiguous LDS tile (rows = reduction): the
@@ -451,14 +457,16 @@ __global__ __launch_bounds__(THREADS) void k_gemm_nn(NnParams p) {
           int row = idx / TPR, part = idx % TPR;
           int64_t n = k0 + row, k = col0 + part * 32;
           u32x4_t cz = {0u, 0u, 0u, 0u};
-          float sc = 0.f;
+          float sc = 0.f, sc2 = 0.f;
           if (idx < BK * TPR && n < re && k < p.Nc) {
             const uint8_t *src = p.W.codes + w_group(p.W, g) * p.W.g_codes + w_code_off(p.W.KB, n, k);
             cz = ldg_b128_cached(src);
             sc = block_scale<FMT>(p.W, g, n, k);
+            if constexpr (FMT == FMT_NVFP4) sc2 = block_scale<FMT>(p.W, g, n, k + 16);
           }
           rb_pk.codes[c] = cz;
           rb_pk.scale[c] = sc;
+          rb_pk.scale2[c] = sc2;
         }
       }
     } else {
@@ -480,7 +488,9 @@ __global__ __launch_bounds__(THREADS) void k_gemm_nn(NnParams p) {
         if (idx < BK * TPR) {
           int row = idx / TPR, part = idx % TPR;
           uint32_t w[16];
-          if constexpr (FMT == FMT_MXFP4) {
+          if constexpr (FMT == FMT_NVFP4) {
+            dequant32_nvfp4(rb_pk.codes[c], rb_pk.scale[c], rb_pk.scale2[c], w);
+          } else if constexpr (FMT == FMT_MXFP4) {
             dequant32_mxfp4(rb_pk.codes[c], rb_pk.scale[c], w);
           } else if constexpr (FMT != FMT_BF16) {
             dequant32_nf4(rb_pk.codes[c], rb_pk.scale[c], qlds, w);

@@ -70,7 +70,7 @@ __device__ __forceinline__ u32x4_t frag_w(const uint16_t *Bs, int k0, int c0, in
 // Raw loads of one thread for one step: its 64-element run.
 struct WRaw {
   u32x4_t c0, c1;
-  uint32_t sc;   // NF4: fp32 bits; DQ: e4m3 code; MXFP4: two e8m0 codes
+  uint32_t sc;   // NF4: fp32 bits; DQ: e4m3 code; MXFP4: two e8m0 codes; NVFP4: four e4m3 codes
   uint32_t c2;   // DQ second level (fp32 bits)
 };
 
@@ -131,12 +131,16 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
   const int64_t w_step = KB * 2048;   // one row block of tiles per step
   const int sc_per_row = (int)(Kw >> 6);   // NF4-DQ: scales per row, row-major (second level)
   constexpr int sc_bytes = FMT == FMT_NF4 ? 4 : 1;
-  constexpr int sc_tile = FMT == FMT_MXFP4 ? 128 : 64 * sc_bytes;   // scale bytes per tile
+  constexpr int sc_tile = FMT == FMT_MXFP4 ? 128 : FMT == FMT_NVFP4 ? 256 : 64 * sc_bytes;   // scale bytes per tile
   const uint8_t *sbase = reinterpret_cast<const uint8_t *>(p.W.scales) + (gw * p.W.g_scales) * sc_bytes;
   const rsrc_t s_rsrc = big::make_rsrc(sbase, big::clamp_bytes(p.W.g_scales * sc_bytes));
   const uint32_t s_voff =
-      kc < p.Nc ? (uint32_t)((kc >> 6) * sc_tile + (FMT == FMT_MXFP4 ? lane * 2 : lane * sc_bytes)) : OOB;
-  const uint32_t s_voff1 = kc + 32 < p.Nc ? s_voff + 1 : OOB;   // MXFP4 second code
+      kc < p.Nc ? (uint32_t)((kc >> 6) * sc_tile + (FMT == FMT_MXFP4   ? lane * 2
+                                                   : FMT == FMT_NVFP4 ? lane * 4
+                                                                      : lane * sc_bytes))
+                : OOB;
+  // MXFP4: second code; NVFP4: third and fourth codes (the run's second half)
+  const uint32_t s_voff1 = kc + 32 < p.Nc ? s_voff + (FMT == FMT_NVFP4 ? 2 : 1) : OOB;
   const int64_t s_step = KB * sc_tile;
   const rsrc_t s2_rsrc = FMT == FMT_NF4_DQ
                              ? big::make_rsrc(p.W.scales2 + gw * p.W.g_scales2, big::clamp_bytes(p.W.g_scales2 * 4))
@@ -153,6 +157,11 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
       w.sc = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, s_voff, so, 0);
       const int64_t idx = ((int64_t)s * BKS + lane) * sc_per_row + (kc >> 6);
       w.c2 = __builtin_amdgcn_raw_buffer_load_b32(s2_rsrc, kc < p.Nc ? (uint32_t)((idx >> 8) * 4) : OOB, 0, 0);
+    } else if constexpr (FMT == FMT_NVFP4) {
+      // two E4M3 codes per half of the run, loaded per half as for MXFP4
+      const uint32_t e0 = __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, s_voff, so, 0);
+      const uint32_t e1 = __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, s_voff1, so, 0);
+      w.sc = e0 | (e1 << 16);
     } else {
       // two E8M0 codes, one byte each, so that a range check on the second
       // never discards the first
@@ -169,6 +178,8 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
       if constexpr (FMT == FMT_MXFP4) {
         s0 = e8m0_to_f32(w.sc & 0xFFu);
         s1 = e8m0_to_f32((w.sc >> 8) & 0xFFu);
+      } else if constexpr (FMT == FMT_NVFP4) {
+        // (the scale of each 16-element block is decoded with its words)
       } else {
         float c;
         if constexpr (FMT == FMT_NF4) c = __builtin_bit_cast(float, w.sc);
@@ -183,6 +194,8 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
       u32x4_t v;
       if constexpr (FMT == FMT_MXFP4)
         v = big::decode8_mxfp4(code, q < 4 ? s0 : s1);
+      else if constexpr (FMT == FMT_NVFP4)
+        v = decode8_nvfp4(code, e4m3_to_f32((w.sc >> (8 * (q >> 1))) & 0xFFu));
       else
         v = big::decode8_nf4(T, code);
       lds_write_b128(Bs + wt_off(lane, wave * 64 + 8 * q), v);
@@ -248,6 +261,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
   // behind the last MFMAs of this one.
   struct WordDec {
     uint32_t i0, i1, L0, H0, L1, H1;
+    float sc;   // NVFP4: the word's E4M3 block scale
   };
   struct TabBuild {
     float c;
@@ -275,6 +289,10 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
       w.sc = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, s_voff, so, 0);
       const int64_t idx = ((int64_t)s * BKS + lane) * sc_per_row + (kc >> 6);
       w.c2 = __builtin_amdgcn_raw_buffer_load_b32(s2_rsrc, kc < p.Nc ? (uint32_t)((idx >> 8) * 4) : OOB, 0, 0);
+    } else if constexpr (FMT == FMT_NVFP4) {
+      const uint32_t e0 = __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, s_voff, so, 0);
+      const uint32_t e1 = __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, s_voff1, so, 0);
+      w.sc = e0 | (e1 << 16);
     } else {
       const uint32_t e0 = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, s_voff, so, 0);
       const uint32_t e1 = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, s_voff1, so, 0);
@@ -282,7 +300,9 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
     }
   };
   auto tab_stage = [&](int st, const WRaw &w, TabBuild &tb, RunTable &T, float &s0, float &s1) {
-    if constexpr (FMT == FMT_MXFP4) {
+    if constexpr (FMT == FMT_NVFP4) {
+      // (no run state: each word decodes its own block scale)
+    } else if constexpr (FMT == FMT_MXFP4) {
       if (st == 0) {
         s0 = e8m0_to_f32(w.sc & 0xFFu);
         s1 = e8m0_to_f32((w.sc >> 8) & 0xFFu);
@@ -308,7 +328,18 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
                         uint16_t *Bs) {
     uint32_t code = q < 4 ? w.c0[q] : w.c1[q - 4];
     if (st == 0) pin(code);
-    if constexpr (FMT == FMT_MXFP4) {
+    if constexpr (FMT == FMT_NVFP4) {
+      if (st == 0) {
+        o.sc = e4m3_to_f32((w.sc >> (8 * (q >> 1))) & 0xFFu);
+        o.L0 = nvfp4_pair_t<0>(code, o.sc);
+        o.H0 = nvfp4_pair_t<1>(code, o.sc);
+      } else if (st == 1) {
+        o.L1 = nvfp4_pair_t<2>(code, o.sc);
+        o.H1 = nvfp4_pair_t<3>(code, o.sc);
+      } else if (st == 3) {
+        lds_write_b128(Bs + wt_off(lane, wave * 64 + 8 * q), u32x4_t{o.L0, o.H0, o.L1, o.H1});
+      }
+    } else if constexpr (FMT == FMT_MXFP4) {
       const float sc = q < 4 ? s0 : s1;
       if (st == 0) {
         o.L0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(code, sc, 0));

@@ -149,7 +149,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   const rsrc_t w_rsrc = big::make_rsrc(rb_ok ? codes_g + rb * KB * 2048 : codes_g,
                                        rb_ok ? big::clamp_bytes(KB * 2048) : 0u);
   constexpr int sc_bytes = FMT == FMT_NF4 ? 4 : 1;
-  constexpr int sc_tile = FMT == FMT_MXFP4 ? 128 : 64 * sc_bytes;   // scale bytes per tile
+  constexpr int sc_tile = FMT == FMT_MXFP4 ? 128 : FMT == FMT_NVFP4 ? 256 : 64 * sc_bytes;   // scale bytes per tile
   const uint8_t *sbase = reinterpret_cast<const uint8_t *>(p.W.scales) + (gw * p.W.g_scales) * sc_bytes;
   const rsrc_t s_rsrc = big::make_rsrc(rb_ok ? sbase + rb * KB * sc_tile : sbase,
                                        rb_ok ? big::clamp_bytes(KB * sc_tile) : 0u);
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   for (int j = 0; j < 2; ++j) {
     const int i = j * 32 + l32;   // row inside the row block
     w_voff[j] = (uint32_t)(i * 32 + h * 16);
-    s_voff[j] = (uint32_t)(FMT == FMT_MXFP4 ? i * 2 + h : i * sc_bytes);
+    s_voff[j] = (uint32_t)(FMT == FMT_MXFP4 ? i * 2 + h : FMT == FMT_NVFP4 ? i * 4 + h * 2 : i * sc_bytes);
     s_idx0[j] = (col0 + wave * 64 + i) * (p.W.K >> 6);
   }
   // per-step offsets of tile (rb, k0 / 64)
@@ -186,6 +186,8 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
       w.sc[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, half_ok ? s_voff[j] : OOB, s_step_off(k0), 0);
       const int64_t gi = (s_idx0[j] + (int64_t)(k0 >> 6)) >> 8;
       w.c2[j] = __builtin_amdgcn_raw_buffer_load_b32(s2_rsrc, half_ok ? (uint32_t)(gi * 4) : OOB, 0, 0);
+    } else if constexpr (FMT == FMT_NVFP4) {   // the lane half's two E4M3 scales
+      w.sc[j] = __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, half_ok ? s_voff[j] : OOB, s_step_off(k0), 0);
     } else {
       w.sc[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, half_ok ? s_voff[j] : OOB, s_step_off(k0), 0);
     }
@@ -201,11 +203,15 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   struct RunDec {
     RunTable T;
     float sc;
+    float sc2;   // NVFP4: scale of code words 2, 3 (sc: words 0, 1)
   };
   auto make_run = [&](const WRaw &w, int j) -> RunDec {
     RunDec d{};
     if constexpr (FMT == FMT_MXFP4) {
       d.sc = e8m0_to_f32(w.sc[j] & 0xFFu);
+    } else if constexpr (FMT == FMT_NVFP4) {
+      d.sc = e4m3_to_f32(w.sc[j] & 0xFFu);
+      d.sc2 = e4m3_to_f32((w.sc[j] >> 8) & 0xFFu);
     } else {
       float c;
       if constexpr (FMT == FMT_NF4) c = __builtin_bit_cast(float, w.sc[j]);
@@ -221,6 +227,8 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
       const int q = q0 + e;
       if constexpr (FMT == FMT_MXFP4)
         f.w[j][q] = big::decode8_mxfp4(w.c[j][q], d.sc);
+      else if constexpr (FMT == FMT_NVFP4)
+        f.w[j][q] = decode8_nvfp4(w.c[j][q], q < 2 ? d.sc : d.sc2);
       else
         f.w[j][q] = big::decode8_nf4(d.T, w.c[j][q]);
     }
@@ -299,6 +307,8 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
       w.sc[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, half_ok ? s_voff[j] : OOB, s_step_off(k0), 0);
       const int64_t gi = (s_idx0[j] + (int64_t)(k0 >> 6)) >> 8;
       w.c2[j] = __builtin_amdgcn_raw_buffer_load_b32(s2_rsrc, half_ok ? (uint32_t)(gi * 4) : OOB, 0, 0);
+    } else if constexpr (FMT == FMT_NVFP4) {   // the lane half's two E4M3 scales
+      w.sc[j] = __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, half_ok ? s_voff[j] : OOB, s_step_off(k0), 0);
     } else {
       w.sc[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, half_ok ? s_voff[j] : OOB, s_step_off(k0), 0);
     }
@@ -311,7 +321,19 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   };
   // slice i of decoding words q0, q0 + 1 of row j of w into f
   auto dec_slice = [&](int i, const WRaw &w, WFrag &f, const RunDec &d, int j, int q0, WordDec (&wd)[2]) {
-    if constexpr (FMT == FMT_MXFP4) {
+    if constexpr (FMT == FMT_NVFP4) {
+      // one bf16 pair per slice: convert at scale 1, multiply by the E4M3 scale
+      const int q = q0 + (i >> 2);
+      const float sc = q0 == 0 ? d.sc : d.sc2;
+      uint32_t v;
+      switch (i & 3) {
+        case 0: v = nvfp4_pair_t<0>(w.c[j][q], sc); break;
+        case 1: v = nvfp4_pair_t<1>(w.c[j][q], sc); break;
+        case 2: v = nvfp4_pair_t<2>(w.c[j][q], sc); break;
+        default: v = nvfp4_pair_t<3>(w.c[j][q], sc); break;
+      }
+      f.w[j][q][i & 3] = v;
+    } else if constexpr (FMT == FMT_MXFP4) {
       // one conversion (a bf16 pair) per slice
       const int q = q0 + (i >> 2);
       uint32_t v;
@@ -352,6 +374,9 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   auto run_slice = [&](int i, const WRaw &w, int j, RunBuild &rb, RunDec &out) {
     if constexpr (FMT == FMT_MXFP4) {
       if (i == 7) out.sc = e8m0_to_f32(w.sc[j] & 0xFFu);
+    } else if constexpr (FMT == FMT_NVFP4) {
+      if (i == 6) out.sc = e4m3_to_f32(w.sc[j] & 0xFFu);
+      if (i == 7) out.sc2 = e4m3_to_f32((w.sc[j] >> 8) & 0xFFu);
     } else {
       if (i == 0) {
         if constexpr (FMT == FMT_NF4) rb.c = __builtin_bit_cast(float, w.sc[j]);

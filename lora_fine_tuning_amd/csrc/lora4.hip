@@ -233,10 +233,13 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 lora4_status check_W(const lora4_W *W) {
   if (!W) return LORA4_ERR_NULL;
-  if (W->format != LORA4_NF4 && W->format != LORA4_NF4_DQ && W->format != LORA4_MXFP4) return LORA4_ERR_FORMAT;
-  const int want = W->format == LORA4_MXFP4 ? 32 : 64;
+  if (W->format != LORA4_NF4 && W->format != LORA4_NF4_DQ && W->format != LORA4_MXFP4 && W->format != LORA4_NVFP4)
+    return LORA4_ERR_FORMAT;
+  const int want = W->format == LORA4_MXFP4 ? 32 : W->format == LORA4_NVFP4 ? 16 : 64;
   if (W->block != want) return LORA4_ERR_FORMAT;
-  if (W->N < 1 || W->K < want || W->K % want != 0 || W->groups < 1) return LORA4_ERR_SHAPE;
+  // K: whole blocks, and whole 32-element halves of a 64-deep step (NVFP4)
+  const int kmul = want < 32 ? 32 : want;
+  if (W->N < 1 || W->K < kmul || W->K % kmul != 0 || W->groups < 1) return LORA4_ERR_SHAPE;
   if (W->N > (int64_t(1) << 31) || W->K > (int64_t(1) << 31) || W->groups > 65535) return LORA4_ERR_SHAPE;
   if (!W->codes || !W->scales) return LORA4_ERR_NULL;
   if (W->format == LORA4_NF4_DQ && !W->scales2) return LORA4_ERR_NULL;
@@ -264,7 +267,7 @@ PackedW packed_of(const Base &b) {
   p.K = W->K;
   p.KB = w_blocks(W->K);
   p.g_codes = w_blocks(W->N) * p.KB * 2048;
-  p.g_scales = w_blocks(W->N) * p.KB * (W->format == LORA4_MXFP4 ? 128 : 64);
+  p.g_scales = w_blocks(W->N) * p.KB * (W->format == LORA4_MXFP4 ? 128 : W->format == LORA4_NVFP4 ? 256 : 64);
   p.g_scales2 = W->format == LORA4_NF4_DQ ? ceil_div(W->N * (W->K / 64), 256) : 0;
   p.shared = b.shared ? 1 : 0;
   return p;
@@ -468,6 +471,7 @@ lora4_status run_fwd_fmt(int fmt, const big::Params &p, hipStream_t st) {
     case LORA4_NF4: return run_fwd<FMT_NF4>(p, st);
     case LORA4_NF4_DQ: return run_fwd<FMT_NF4_DQ>(p, st);
     case LORA4_MXFP4: return run_fwd<FMT_MXFP4>(p, st);
+    case LORA4_NVFP4: return run_fwd<FMT_NVFP4>(p, st);
   }
   return LORA4_ERR_FORMAT;
 }
@@ -487,6 +491,7 @@ lora4_status run_dgrad_fmt(int fmt, const big::Params &p, hipStream_t st) {
     case LORA4_NF4: return run_dgrad<FMT_NF4>(p, st);
     case LORA4_NF4_DQ: return run_dgrad<FMT_NF4_DQ>(p, st);
     case LORA4_MXFP4: return run_dgrad<FMT_MXFP4>(p, st);
+    case LORA4_NVFP4: return run_dgrad<FMT_NVFP4>(p, st);
   }
   return LORA4_ERR_FORMAT;
 }
@@ -575,6 +580,7 @@ lora4_status run_nt_main_fmt(int fmt, const NtParams &p, dim3 grid, const Plan &
     case LORA4_NF4: return run_nt_main<FMT_NF4>(p, grid, st);
     case LORA4_NF4_DQ: return run_nt_main<FMT_NF4_DQ>(p, grid, st);
     case LORA4_MXFP4: return run_nt_main<FMT_MXFP4>(p, grid, st);
+    case LORA4_NVFP4: return run_nt_main<FMT_NVFP4>(p, grid, st);
   }
   return LORA4_ERR_FORMAT;
 }
@@ -596,6 +602,7 @@ lora4_status run_nn_main_fmt(int fmt, const NnParams &p, dim3 grid, const TailPa
     case LORA4_NF4: return run_nn_main<FMT_NF4>(p, grid, st);
     case LORA4_NF4_DQ: return run_nn_main<FMT_NF4_DQ>(p, grid, st);
     case LORA4_MXFP4: return run_nn_main<FMT_MXFP4>(p, grid, st);
+    case LORA4_NVFP4: return run_nn_main<FMT_NVFP4>(p, grid, st);
   }
   return LORA4_ERR_FORMAT;
 }
@@ -1053,13 +1060,15 @@ lora4_status lora4_backward_multi(const lora4_W *W, int64_t adapters, const uint
 }
 
 size_t lora4_packed_bytes(int32_t format, int64_t N, int64_t K, int32_t part) {
-  const int64_t block = format == LORA4_MXFP4 ? 32 : 64;
-  if (format != LORA4_NF4 && format != LORA4_NF4_DQ && format != LORA4_MXFP4) return 0;
+  // K granularity: the block (NF4: 64, MXFP4: 32); NVFP4 (16-element blocks) whole 32-element halves
+  const int64_t block = format == LORA4_MXFP4 || format == LORA4_NVFP4 ? 32 : 64;
+  if (format != LORA4_NF4 && format != LORA4_NF4_DQ && format != LORA4_MXFP4 && format != LORA4_NVFP4) return 0;
   if (N < 1 || K < block || K % block != 0 || N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return 0;
   const int64_t tiles = w_blocks(N) * w_blocks(K);
   switch (part) {
     case 0: return (size_t)(tiles * 2048);
-    case 1: return (size_t)(tiles * (format == LORA4_MXFP4 ? 128 : format == LORA4_NF4 ? 256 : 64));
+    case 1:
+      return (size_t)(tiles * (format == LORA4_MXFP4 ? 128 : format == LORA4_NF4 || format == LORA4_NVFP4 ? 256 : 64));
     case 2: return format == LORA4_NF4_DQ ? (size_t)(ceil_div(N * (K / 64), 256) * 4) : 0;
   }
   return 0;
@@ -1168,6 +1177,18 @@ lora4_status lora4_forward_mx(const lora4_W *W, const uint16_t *X, int64_t M, co
   }
   return launch_lds("gemm_mx_base", mx::k_gemm_fwd_mx<false>, dim3((unsigned)q.nblocks), dim3(mx::THREADS),
                     (size_t)mx::lds_bytes(), q, st);
+}
+
+lora4_status quant_pack_nvfp4(const uint16_t *W_bf16, int64_t N, int64_t K, uint8_t *codes,
+                              uint8_t *scales_e4m3, void *stream) {
+  if (!W_bf16 || !codes || !scales_e4m3) return LORA4_ERR_NULL;
+  if (N < 1 || K < 32 || K % 32 != 0 || N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return LORA4_ERR_SHAPE;
+  if (!aligned16(W_bf16) || !aligned16(codes) || !aligned16(scales_e4m3)) return LORA4_ERR_ALIGN;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  TRY(clear_padding(N, K, LORA4_NVFP4, codes, scales_e4m3, st));
+  const int64_t nblk = N * (K / 16);
+  return launch_args("quant_pack_nvfp4", k_quant_nvfp4, dim3((unsigned)ceil_div(nblk, 256)), dim3(256), st,
+                     W_bf16, N, K, codes, scales_e4m3);
 }
 
 lora4_status lora4_timing_enable(int on) {

@@ -209,4 +209,58 @@ __global__ void k_quant_mxfp4(const uint16_t *W, int64_t N, int64_t K, uint8_t *
   e8m0[w_scale32_idx(KB, n, b * 32)] = (uint8_t)(X + 127);
 }
 
+// NVFP4: one thread per 16-element block. Scale code = E4M3 of amax / 6
+// (the division is correctly rounded; amax / 6 is either exact in fp32 or not
+// an E4M3 midpoint, so rounding it once more is exact), s = its value; each
+// element's magnitude code counts the E2M1 midpoints below |w| / s, compared
+// as |w| against midpoint x s (exact products), ties to the even code,
+// saturating at 6; s == 0 gives magnitude 0. Sign copied.
+__device__ __forceinline__ uint32_t nvfp4_mag_code(float a, float s) {
+  if (!(s > 0.0f)) return 0u;
+  return (uint32_t)(a > 0.25f * s) + (uint32_t)(a >= 0.75f * s) + (uint32_t)(a > 1.25f * s) +
+         (uint32_t)(a >= 1.75f * s) + (uint32_t)(a > 2.5f * s) + (uint32_t)(a >= 3.5f * s) + (uint32_t)(a > 5.0f * s);
+}
+
+__global__ void k_quant_nvfp4(const uint16_t *W, int64_t N, int64_t K, uint8_t *codes, uint8_t *e4m3) {
+  const int64_t nb = K >> 4;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= N * nb) return;
+  const int64_t n = i / nb, b = i - n * nb;
+  const u32x4_t *src = reinterpret_cast<const u32x4_t *>(W + n * K + b * 16);
+  uint32_t w[8];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const u32x4_t v = src[q];
+    w[4 * q] = v[0];
+    w[4 * q + 1] = v[1];
+    w[4 * q + 2] = v[2];
+    w[4 * q + 3] = v[3];
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[j] & 0xFFFFu)));
+    amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[j] >> 16)));
+  }
+  const uint32_t sc = e4m3_encode_rne(fminf(amax / 6.0f, 448.0f));
+  const float sv = e4m3_to_f32(sc);
+  uint32_t out[2];
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const uint32_t pair = w[4 * d + h];
+      const uint32_t lo16 = pair & 0xFFFFu, hi16 = pair >> 16;
+      const uint32_t ca = nvfp4_mag_code(fabsf(bf16_bits_to_f32(lo16)), sv) | ((lo16 >> 15) << 3);
+      const uint32_t cb = nvfp4_mag_code(fabsf(bf16_bits_to_f32(hi16)), sv) | ((hi16 >> 15) << 3);
+      word |= (ca | (cb << 4)) << (8 * h);
+    }
+    out[d] = word;
+  }
+  const int64_t KB = w_blocks(K);
+  *reinterpret_cast<u32x2_t *>(codes + w_code_off(KB, n, b * 16)) = u32x2_t{out[0], out[1]};
+  e4m3[w_scale16_idx(KB, n, b * 16)] = (uint8_t)sc;
+}
+
 }  // namespace lora4

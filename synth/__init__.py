@@ -35,7 +35,7 @@ from typing import List, Optional
 
 import numpy as np
 
-NF4, NF4_DQ, MXFP4 = "nf4", "nf4_dq", "mxfp4"
+NF4, NF4_DQ, MXFP4, NVFP4 = "nf4", "nf4_dq", "mxfp4", "nvfp4"
 TID = {"X": 1, "W": 2, "A": 3, "B": 4, "dY": 5, "logits": 6}
 
 
@@ -61,7 +61,7 @@ class Layer:
 
     @property
     def block(self):
-        return 32 if self.fmt == MXFP4 else 64
+        return {MXFP4: 32, NVFP4: 16}.get(self.fmt, 64)
 
     def flops(self):
         """Algorithmic fwd+bwd flops: 4MNK + 6Mr(N+K) (no dW, Z kept)."""

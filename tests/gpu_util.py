@@ -6,7 +6,7 @@ import torch
 
 import lora_fine_tuning_amd as L
 import synth
-from oracle import codecs, lora, mxfp4, nf4
+from oracle import codecs, lora, mxfp4, nf4, nvfp4
 
 DEV = "cuda:0"
 TOL = 5e-3   # relative Frobenius error bar for float outputs
@@ -31,6 +31,8 @@ def pack_gpu(W_u16, fmt):
     Wd = to_dev(W_u16)
     if fmt == synth.MXFP4:
         return L.pack_mxfp4(Wd)
+    if fmt == synth.NVFP4:
+        return L.pack_nvfp4(Wd)
     return L.pack_nf4(Wd, double_quant=(fmt == synth.NF4_DQ))
 
 
@@ -52,7 +54,7 @@ def tile_scales(sc, N, K):
     (MXFP4) -> the library's storage: 64 (or 128) entries per tile, row i's
     entries contiguous, zero padding."""
     RB, KB = _blocks(N), _blocks(K)
-    per = 2 if sc.shape[1] == K // 32 else 1   # MXFP4: two 32-element blocks per row and tile
+    per = sc.shape[1] * 64 // K                # entries per row and tile: 1 (NF4), 2 (MXFP4), 4 (NVFP4)
     buf = np.zeros((RB * 64, KB * per), dtype=sc.dtype)
     buf[:N, :sc.shape[1]] = sc
     return np.ascontiguousarray(buf.reshape(RB, 64, KB, per).transpose(0, 2, 1, 3)).reshape(-1)
@@ -64,7 +66,7 @@ def untile_rows(flat, N, K, rows, per_row):
     dropped."""
     RB, KB = _blocks(N), _blocks(K)
     t = flat.reshape(RB, KB, 64, per_row).transpose(0, 2, 1, 3).reshape(RB * 64, KB * per_row)
-    width = K // 2 if per_row == 32 else (K // 64 if per_row == 1 else K // 32)
+    width = K // 2 if per_row == 32 else {1: K // 64, 2: K // 32, 4: K // 16}[per_row]
     return t[rows, :width]
 
 
@@ -72,6 +74,8 @@ def oracle_pack(W_u16, fmt):
     """Oracle packing of one [N, K] matrix: (codes, scales[, scales2])."""
     if fmt == synth.MXFP4:
         return mxfp4.quantize(W_u16)
+    if fmt == synth.NVFP4:
+        return nvfp4.quantize(W_u16)
     codes, sc = nf4.quantize(W_u16)
     if fmt == synth.NF4_DQ:
         c8, c2 = nf4.double_quantize(sc)
@@ -83,6 +87,8 @@ def oracle_dequant(packed, fmt):
     """bf16 bits of the oracle dequant of an oracle packing."""
     if fmt == synth.MXFP4:
         return mxfp4.dequantize(packed[0], packed[1])
+    if fmt == synth.NVFP4:
+        return nvfp4.dequantize(packed[0], packed[1])
     if fmt == synth.NF4_DQ:
         return nf4.dequantize_dq(packed[0], packed[1], packed[2])
     return nf4.dequantize(packed[0], packed[1])

@@ -64,6 +64,8 @@ def test_format_and_block_validation(lib):
     assert fwd(_W(fmt=1, block=32)) == EFORMAT
     assert fwd(_W(K=96)) == ESHAPE                        # K % 64
     assert fwd(_W(fmt=3, block=32, K=48)) == ESHAPE
+    assert fwd(_W(fmt=4, block=32)) == EFORMAT            # NVFP4 needs block 16
+    assert fwd(_W(fmt=4, block=16, K=48)) == ESHAPE       # ... and K % 32 == 0
     assert fwd(_W(N=0)) == ESHAPE
     assert fwd(_W(fmt=2)) == ENULL                        # DQ needs scales2
     assert fwd(_W(codes=None)) == ENULL
@@ -137,6 +139,9 @@ def test_packed_bytes(lib):
     assert L.lora4_packed_bytes(L.LORA4_NF4_DQ, 37, 192, 2) == 4 * -(-(37 * 3) // 256)
     assert L.lora4_packed_bytes(L.LORA4_MXFP4, 65, 96, 0) == 2 * 2 * 2048
     assert L.lora4_packed_bytes(L.LORA4_MXFP4, 65, 96, 1) == 2 * 2 * 128
+    assert L.lora4_packed_bytes(L.LORA4_NVFP4, 65, 96, 0) == 2 * 2 * 2048
+    assert L.lora4_packed_bytes(L.LORA4_NVFP4, 65, 96, 1) == 2 * 2 * 256
+    assert L.lora4_packed_bytes(L.LORA4_NVFP4, 65, 48, 0) == 0      # K % 32 != 0
     for bad in [(L.LORA4_NF4, 10, 96, 0), (L.LORA4_MXFP4, 0, 64, 0), (L.LORA4_MXFP4, 8, 48, 0), (9, 64, 64, 0),
                 (L.LORA4_NF4, 64, 64, 3)]:
         assert L.lora4_packed_bytes(*bad) == 0, bad
@@ -209,3 +214,10 @@ def test_mx_forward_validation(lib):
     assert L.quant_pack_mxfp8(None, 16, 64, 4096, 4096, None) == ENULL
     assert L.quant_pack_mxfp8(4096, 16, 64, 4104, 4096, None) == EALIGN
     assert L.quant_pack_mxfp8(None, 0, 64, None, None, None) == OK
+
+
+def test_nvfp4_packer_validation(lib):
+    assert L.quant_pack_nvfp4(4096, 64, 48, 4096, 4096, None) == ESHAPE    # K % 32
+    assert L.quant_pack_nvfp4(4096, 0, 64, 4096, 4096, None) == ESHAPE
+    assert L.quant_pack_nvfp4(None, 64, 64, 4096, 4096, None) == ENULL
+    assert L.quant_pack_nvfp4(4096, 64, 64, 4100, 4096, None) == EALIGN

@@ -69,11 +69,11 @@ def test_single_linear_workload_parity(tiles):
     _check_all(_run(lay, t), _oracle(lay, t))
 
 
-@pytest.mark.parametrize("fmt", [synth.NF4, synth.NF4_DQ, synth.MXFP4])
+@pytest.mark.parametrize("fmt", [synth.NF4, synth.NF4_DQ, synth.MXFP4, synth.NVFP4])
 @pytest.mark.parametrize("M,K,N,r", [(200, 192, 200, 8), (64, 320, 96, 24), (300, 256, 100, 4),
                                      (129, 1024, 264, 64), (17, 512, 136, 128), (1, 64, 8, 1)])
 def test_ragged_shapes(fmt, M, K, N, r, tiles):
-    if fmt == synth.MXFP4:
+    if fmt in (synth.MXFP4, synth.NVFP4):
         K = K - 32 if K % 64 == 0 and K > 64 else K     # exercise K % 64 == 32
     lay = synth.small_layer(M, K, N, r, fmt=fmt, index=(M + K + N + r) % 97)
     print_case("ragged", fmt, M, K, N, r)
@@ -191,7 +191,7 @@ def test_large_tile_shape_selected_automatically(monkeypatch):
     assert rel(got["dA"], bref["dA"]) <= TOL and rel(got["dB"], bref["dB"]) <= TOL
 
 
-@pytest.mark.parametrize("fmt", [synth.NF4, synth.NF4_DQ, synth.MXFP4])
+@pytest.mark.parametrize("fmt", [synth.NF4, synth.NF4_DQ, synth.MXFP4, synth.NVFP4])
 @pytest.mark.parametrize("M,K,N,r", [(512, 4096, 256, 16),     # 2 tiles: 8-way split of 64 steps
                                      (700, 2048, 1000, 16),    # ragged rows, 12 tiles: 4-way split
                                      (300, 2048, 258, 8)])     # N % 4 != 0, ragged last columns
@@ -199,7 +199,7 @@ def test_forward_split_reduction(fmt, M, K, N, r, monkeypatch):
     """Forced onto the register-direct forward kernel, few-tile outputs split
     the reduction (fp32 partials + reduction); the rank-r tail is added once."""
     monkeypatch.setenv("LORA4_BIG", "1")
-    if fmt == synth.MXFP4 and K % 64 == 0:
+    if fmt in (synth.MXFP4, synth.NVFP4) and K % 64 == 0:
         K -= 32
     lay = synth.small_layer(M, K, N, r, fmt=fmt, index=(M + N) % 89)
     print_case("split", fmt, M, K, N, r)

@@ -38,7 +38,7 @@ def _edge_rows(K):
     return rows
 
 
-@pytest.mark.parametrize("fmt", [synth.NF4, synth.NF4_DQ, synth.MXFP4])
+@pytest.mark.parametrize("fmt", [synth.NF4, synth.NF4_DQ, synth.MXFP4, synth.NVFP4])
 @pytest.mark.parametrize("N,K", [(1024, 1024), (37, 192), (300, 5120)])
 def test_quant_pack_bit_exact(fmt, N, K):
     print_case("quant_pack", fmt, N, K)
@@ -75,12 +75,17 @@ def _identity(n):
 
 def _custom_base(fmt, N, K, seed):
     """A packed base whose codes run through every value and whose scales sweep
-    many binades (every finite E8M0 up to 252 for MXFP4)."""
+    many binades (every finite E8M0 up to 252 for MXFP4, every finite E4M3
+    for NVFP4)."""
     rng = np.random.default_rng(seed)
     codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
     codes[0, :8] = np.arange(0, 256, 32, dtype=np.uint8) | np.arange(8, dtype=np.uint8)
     if fmt == synth.MXFP4:
         sc = (np.arange(N * (K // 32)) % 253).astype(np.uint8).reshape(N, K // 32)
+        return codes, sc
+    if fmt == synth.NVFP4:
+        sc = (np.arange(N * (K // 16)) % 0x7F).astype(np.uint8).reshape(N, K // 16)   # 0x00 .. 0x7E
+        sc = sc | ((np.arange(N * (K // 16)) // 0x7F % 2) << 7).astype(np.uint8).reshape(N, K // 16)
         return codes, sc
     nb = K // 64
     expo = (np.arange(N * nb) % 81 - 40).astype(np.float32)
@@ -100,6 +105,8 @@ def _to_packed(parts, fmt, N, K):
         return L.PackedBase(L.LORA4_NF4, N, K, 1, codes, sc)
     if fmt == synth.NF4_DQ:
         return L.PackedBase(L.LORA4_NF4_DQ, N, K, 1, codes, sc, torch.from_numpy(parts[2]).to(DEV)[None])
+    if fmt == synth.NVFP4:
+        return L.PackedBase(L.LORA4_NVFP4, N, K, 1, codes, sc)
     return L.PackedBase(L.LORA4_MXFP4, N, K, 1, codes, sc)
 
 
@@ -109,7 +116,7 @@ def tiles(request, monkeypatch):
     return request.param
 
 
-@pytest.mark.parametrize("fmt", [synth.NF4, synth.NF4_DQ, synth.MXFP4])
+@pytest.mark.parametrize("fmt", [synth.NF4, synth.NF4_DQ, synth.MXFP4, synth.NVFP4])
 def test_forward_dequant_one_hot_bit_exact(fmt, tiles):
     N, K, r = 160, 1024, 16
     print_case("one-hot forward", fmt, N, K)
@@ -124,7 +131,7 @@ def test_forward_dequant_one_hot_bit_exact(fmt, tiles):
     assert np.array_equal(_zero_sign(Y), _zero_sign(ref.T))
 
 
-@pytest.mark.parametrize("fmt", [synth.NF4, synth.NF4_DQ, synth.MXFP4])
+@pytest.mark.parametrize("fmt", [synth.NF4, synth.NF4_DQ, synth.MXFP4, synth.NVFP4])
 def test_dgrad_dequant_one_hot_bit_exact(fmt, tiles):
     N, K, r = 192, 512, 16
     print_case("one-hot dgrad", fmt, N, K)
