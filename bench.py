@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--cpu-reps", type=int, default=3, help="passes of the CPU oracle over its sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (counter calibration) and exit")
+    ap.add_argument("--fmt", choices=["nf4", "nf4_dq", "mxfp4", "nvfp4"], default=None,
+                    help="store every base of the workload in this format instead of its own")
     ap.add_argument("--mx", action="store_true",
                     help="forward through the MX-native path (MXFP8 activations x MXFP4 base on the scaled "
                          "MFMA); plain MXFP4 layer sets only")
@@ -69,6 +71,8 @@ class Layer:
         W = d(t["W"])
         if spec.fmt == synth.MXFP4:
             self.base = L.pack_mxfp4(W)
+        elif spec.fmt == synth.NVFP4:
+            self.base = L.pack_nvfp4(W)
         else:
             self.base = L.pack_nf4(W, double_quant=(spec.fmt == synth.NF4_DQ))
         del W
@@ -135,7 +139,7 @@ def kernel_flops(name, spec):
     }.get(name, 0)
 
 
-BITS_PER_WEIGHT = {"nf4": 4.5, "nf4_dq": 4.127, "mxfp4": 4.25}   # codes + scales
+BITS_PER_WEIGHT = {"nf4": 4.5, "nf4_dq": 4.127, "mxfp4": 4.25, "nvfp4": 4.5}   # codes + scales
 
 
 def kernel_bytes(name, spec):
@@ -242,7 +246,7 @@ def cpu_baseline(specs, tokens, reps):
     part is what a step computes: dequant + forward + backward per layer."""
     import numpy as np
     import synth
-    from oracle import lora, mxfp4, nf4
+    from oracle import lora, mxfp4, nf4, nvfp4
 
     prepared = []
     for spec in specs:
@@ -253,6 +257,8 @@ def cpu_baseline(specs, tokens, reps):
         for e in range(len(Ws)):
             if spec.fmt == synth.MXFP4:
                 packs.append(mxfp4.quantize(Ws[e]))
+            elif spec.fmt == synth.NVFP4:
+                packs.append(nvfp4.quantize(Ws[e]))
             else:
                 c, sc = nf4.quantize(Ws[e])
                 packs.append((c, *nf4.double_quantize(sc)) if spec.fmt == synth.NF4_DQ else (c, sc))
@@ -265,6 +271,8 @@ def cpu_baseline(specs, tokens, reps):
             for e, pk in enumerate(packs):
                 if spec.fmt == synth.MXFP4:
                     Wd = lora.as_f64(mxfp4.dequantize(*pk))
+                elif spec.fmt == synth.NVFP4:
+                    Wd = lora.as_f64(nvfp4.dequantize(*pk))
                 elif spec.fmt == synth.NF4_DQ:
                     Wd = lora.as_f64(nf4.dequantize_dq(*pk))
                 else:
@@ -310,6 +318,9 @@ def main():
 
     wl = WORKLOADS[args.workload]
     specs = synth.layers(wl)
+    if args.fmt:
+        import dataclasses
+        specs = [dataclasses.replace(s, fmt=args.fmt) for s in specs]
     if args.mx and any(s.fmt != synth.MXFP4 or s.experts != 1 for s in specs):
         print("--mx needs a workload of plain MXFP4 layers (llama70b)", file=sys.stderr)
         sys.exit(2)
