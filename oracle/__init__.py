@@ -22,6 +22,8 @@ the source pages, cited by page title and section:
 * "Fine-Tuning 4-Bit Models", section "Case 2: An NVFP4 deployment
   checkpoint is what you were handed": NVFP4, E2M1 with an FP8 scale per
   16-element micro-block (see ``nvfp4`` for the readings).
+* "Training LLMs on a Budget", section 4: LoftQ, alternating quantization
+  and a rank-r SVD of the residual (see ``loftq``).
 * The Crusoe post, "Forward pass in inference": the MXFP4-native base
   product (activations as MXFP8, a reading; see ``mxfp8``).
 
@@ -48,10 +50,14 @@ Parity status per function (what pins it is listed in ``tests/``):
                      property, round trips of on-grid blocks, the zero and
                      subnormal blocks, the plain forward on on-grid X and the
                      E4M3 error bound.
+* loftq.*            pinned by the page's 3 x 3 worked example, the
+                     non-increasing error of the rounding loop (the page's
+                     256 x 256 rank-8 setup), Eckart-Young on known singular
+                     values and NF4 LoftQ against plain NF4.
 * lora.*             pinned by finite differences, pure-Python loops, the
                      merge identity and the B = 0 / A = 0 special cases.
 """
 
-from . import codecs, nf4, mxfp4, nvfp4, lora, mxfp8  # noqa: F401
+from . import codecs, nf4, mxfp4, nvfp4, lora, mxfp8, loftq  # noqa: F401
 
-__all__ = ["codecs", "nf4", "mxfp4", "nvfp4", "lora", "mxfp8"]
+__all__ = ["codecs", "nf4", "mxfp4", "nvfp4", "lora", "mxfp8", "loftq"]
