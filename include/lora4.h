@@ -278,6 +278,29 @@ lora4_status lora4_forward_mx(const lora4_W *W, const uint16_t *X, int64_t M,
 lora4_status quant_pack_nvfp4(const uint16_t *W_bf16, int64_t N, int64_t K,
                               uint8_t *codes, uint8_t *scales_e4m3, void *stream);
 
+/* ---- LoftQ initialisation ----------------------------------------------------
+ * "Training LLMs on a Budget", section 4: choose the NF4 base Q and the
+ * adapter so that Q + s B A is close to W at step 0, by alternating
+ * Q <- NF4(bf16(W - s B A)) with B A <- the best rank-r approximation of
+ * W - Q (split as U sqrt(S), sqrt(S) V^T); iters SVD steps (the page's
+ * default is 5), the last one after the last quantization, so the returned
+ * Q and B A belong together. The rank-r approximation is computed by a
+ * randomized subspace iteration on the fp32 residual (r + 16 columns, 8 power
+ * iterations, orthonormalized by Cholesky QR), not by an exact SVD.
+ * Synchronizes the stream (the small c x c steps run on the host).
+ *  W        : bf16 [N, K], K % 64 == 0; 1 <= r <= 128, r + 16 <= min(N, K);
+ *             1 <= iters <= 64; s the layer's adapter scale (finite, != 0).
+ *  codes, scales, scales2 : the NF4 (double_quant == 0) or NF4-DQ packing of
+ *             the last Q, as quant_pack_nf4 writes it.
+ *  A        : bf16 [r, K] output; B : bf16 [N, r] output (divided by s).
+ *  workspace, workspace_bytes : device scratch, >= lora4_loftq_workspace_bytes
+ *             (which returns 0 for invalid sizes). */
+size_t lora4_loftq_workspace_bytes(int64_t N, int64_t K, int32_t r);
+lora4_status lora4_loftq_init(const uint16_t *W_bf16, int64_t N, int64_t K, int32_t r, int32_t iters,
+                              float s, int32_t double_quant, uint8_t *codes, void *scales,
+                              float *scales2, uint16_t *A, uint16_t *B, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
 /* A static, human-readable name for a status code. */
 const char *lora4_status_string(lora4_status status);
 

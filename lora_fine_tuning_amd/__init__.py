@@ -28,6 +28,7 @@ BLOCK = {LORA4_NF4: 64, LORA4_NF4_DQ: 64, LORA4_MXFP4: 32, LORA4_NVFP4: 16}
 EXPORTS = ["lora4_forward", "lora4_backward", "lora4_workspace_bytes", "lora4_packed_bytes",
            "lora4_forward_multi", "lora4_backward_multi", "lora4_workspace_bytes_multi", "quant_pack_nf4",
            "quant_pack_mxfp4", "quant_pack_nvfp4", "quant_pack_mxfp8", "lora4_workspace_bytes_mx", "lora4_forward_mx",
+           "lora4_loftq_workspace_bytes", "lora4_loftq_init",
            "lora4_status_string", "lora4_timing_enable", "lora4_timing_collect", "lora4_version"]
 
 
@@ -85,6 +86,10 @@ def lib():
         L.lora4_workspace_bytes_mx.restype = sz
         L.lora4_forward_mx.argtypes = [Wp, vp, i64, vp, vp, i32, f32, vp, vp, vp, sz, vp]
         L.lora4_forward_mx.restype = ctypes.c_int
+        L.lora4_loftq_workspace_bytes.argtypes = [i64, i64, i32]
+        L.lora4_loftq_workspace_bytes.restype = sz
+        L.lora4_loftq_init.argtypes = [vp, i64, i64, i32, i32, f32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.lora4_loftq_init.restype = ctypes.c_int
         L.lora4_status_string.argtypes = [ctypes.c_int]
         L.lora4_status_string.restype = ctypes.c_char_p
         L.lora4_timing_enable.argtypes = [ctypes.c_int]
@@ -163,6 +168,16 @@ def quant_pack_mxfp8(X, M, K, codes, scales_e8m0, stream):
 
 def lora4_workspace_bytes_mx(W, M, r):
     return lib().lora4_workspace_bytes_mx(ctypes.byref(W), M, r)
+
+
+def lora4_loftq_workspace_bytes(N, K, r):
+    return lib().lora4_loftq_workspace_bytes(N, K, r)
+
+
+def lora4_loftq_init(W, N, K, r, iters, s, double_quant, codes, scales, scales2, A, B, workspace,
+                     workspace_bytes, stream):
+    return lib().lora4_loftq_init(W, N, K, r, iters, s, double_quant, codes, scales, scales2, A, B, workspace,
+                                  workspace_bytes, stream)
 
 
 def lora4_forward_mx(W, X, M, A, B, r, s, Y, Z, workspace, workspace_bytes, stream):
@@ -392,3 +407,30 @@ def forward_mx(base, X, A, B, s, want_z=True, workspace=None):
                           workspace.numel(), _stream())
     _check(st, "lora4_forward_mx")
     return {"Y": Y, "Z": Z}
+
+
+def loftq_init(W, r, iters=5, s=1.0, double_quant=False):
+    """LoftQ initialisation of a bf16 W [N, K] on the GPU: returns the NF4
+    (or NF4-DQ) PackedBase of the base and the adapter A [r, K], B [N, r]
+    (B divided by the layer scale s)."""
+    import torch
+    N, K = W.shape
+    dev = W.device
+    fmt = LORA4_NF4_DQ if double_quant else LORA4_NF4
+    sizes = [lora4_packed_bytes(fmt, N, K, part) for part in range(3)]
+    codes = torch.empty((1, sizes[0]), dtype=torch.uint8, device=dev)
+    if double_quant:
+        scales = torch.empty((1, sizes[1]), dtype=torch.uint8, device=dev)
+        scales2 = torch.empty((1, sizes[2] // 4), dtype=torch.float32, device=dev)
+    else:
+        scales = torch.empty((1, sizes[1] // 4), dtype=torch.float32, device=dev)
+        scales2 = None
+    A = torch.empty((r, K), dtype=torch.bfloat16, device=dev)
+    B = torch.empty((N, r), dtype=torch.bfloat16, device=dev)
+    n = lora4_loftq_workspace_bytes(N, K, r)
+    if n == 0:
+        raise ValueError("invalid arguments for lora4_loftq_workspace_bytes")
+    ws = torch.empty((n,), dtype=torch.uint8, device=dev)
+    _check(lora4_loftq_init(_ptr(W), N, K, r, iters, float(s), 1 if double_quant else 0, _ptr(codes), _ptr(scales),
+                            _ptr(scales2), _ptr(A), _ptr(B), _ptr(ws), ws.numel(), _stream()), "lora4_loftq_init")
+    return PackedBase(fmt, N, K, 1, codes, scales, scales2), A, B

@@ -32,6 +32,7 @@
 #include "gemm_fwd.hpp"
 #include "gemm_dgrad.hpp"
 #include "mx.hpp"
+#include "loftq.hpp"
 #include "skinny.hpp"
 #include "quant.hpp"
 
@@ -815,6 +816,153 @@ lora4_status check_mx(const lora4_W *W, int64_t M, int32_t r, float s) {
   return LORA4_OK;
 }
 
+// ---------------------------------------------------------------------------
+// LoftQ: host steps of the subspace iteration
+// ---------------------------------------------------------------------------
+
+constexpr int LOFTQ_OVERSAMPLE = 16;   // columns beyond r in the subspace
+constexpr int LOFTQ_POWER = 8;         // power iterations (R R^T applied 8 times)
+
+struct LoftqPlan {
+  int c;
+  size_t off_T, off_R, off_Y, off_Y2, off_Z, off_Z2, off_G, off_M, off_B, off_AT, bytes;
+};
+
+LoftqPlan make_loftq_plan(int64_t N, int64_t K, int r) {
+  LoftqPlan p{};
+  p.c = r + LOFTQ_OVERSAMPLE;
+  size_t off = 0;
+  auto take = [&](size_t b) {
+    const size_t o = off;
+    off += align256(b);
+    return o;
+  };
+  p.off_T = take((size_t)N * K * 2);
+  p.off_R = take((size_t)N * K * 4);
+  p.off_Y = take((size_t)N * p.c * 4);
+  p.off_Y2 = take((size_t)N * p.c * 4);
+  p.off_Z = take((size_t)K * p.c * 4);
+  p.off_Z2 = take((size_t)K * p.c * 4);
+  p.off_G = take((size_t)p.c * p.c * 4);
+  p.off_M = take((size_t)p.c * p.c * 4);
+  p.off_B = take((size_t)N * r * 4);
+  p.off_AT = take((size_t)K * r * 4);
+  p.bytes = off;
+  return p;
+}
+
+lora4_status run_mat(bool trans, const float *X, int64_t ldx, int64_t rows, int64_t inner, const float *M, int c,
+                     float *out, hipStream_t st) {
+  const dim3 grid((unsigned)ceil_div(rows, loftq::MAT_ROWS));
+  if (trans) return launch_args("loftq_mat_tn", loftq::k_mat<true>, grid, dim3(256), st, X, ldx, rows, inner, M, c, out);
+  return launch_args("loftq_mat_nn", loftq::k_mat<false>, grid, dim3(256), st, X, ldx, rows, inner, M, c, out);
+}
+
+// c x c Gram matrix of the columns of Y [rows][c] to the host (double).
+lora4_status gram_to_host(const float *Y, int64_t rows, int c, float *G_dev, std::vector<double> &G, hipStream_t st) {
+  TRY(run_mat(true, Y, c, c, rows, Y, c, G_dev, st));
+  std::vector<float> g((size_t)c * c);
+  if (hipMemcpyAsync(g.data(), G_dev, g.size() * 4, hipMemcpyDeviceToHost, st) != hipSuccess) return LORA4_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return LORA4_ERR_HIP;
+  G.assign(g.begin(), g.end());
+  return LORA4_OK;
+}
+
+lora4_status upload(const std::vector<double> &M, float *dst, hipStream_t st, std::vector<float> &stage) {
+  stage.assign(M.begin(), M.end());
+  if (hipMemcpyAsync(dst, stage.data(), stage.size() * 4, hipMemcpyHostToDevice, st) != hipSuccess)
+    return LORA4_ERR_HIP;
+  return hipStreamSynchronize(st) == hipSuccess ? LORA4_OK : LORA4_ERR_HIP;   // (stage is reused)
+}
+
+// Orthonormalize the columns of Y [rows][c] (CholeskyQR, twice): Y <- Y L^-T
+// with Y^T Y = L L^T. A Gram matrix that is not positive definite (Y of lower
+// rank) gets a small diagonal shift.
+lora4_status orthonormalize(float *Y, float *tmp, int64_t rows, int c, float *G_dev, float *M_dev, hipStream_t st) {
+  std::vector<double> G, M((size_t)c * c), L((size_t)c * c);
+  std::vector<float> stage;
+  for (int pass = 0; pass < 2; ++pass) {
+    TRY(gram_to_host(Y, rows, c, G_dev, G, st));
+    double tr = 0;
+    for (int i = 0; i < c; ++i) tr += G[(size_t)i * c + i];
+    const double eps = 1e-12 * (tr > 0 ? tr : 1.0);
+    std::fill(L.begin(), L.end(), 0.0);
+    for (int j = 0; j < c; ++j) {
+      double d = G[(size_t)j * c + j] + eps;
+      for (int k = 0; k < j; ++k) d -= L[(size_t)j * c + k] * L[(size_t)j * c + k];
+      d = d > eps ? std::sqrt(d) : std::sqrt(eps);
+      L[(size_t)j * c + j] = d;
+      for (int i = j + 1; i < c; ++i) {
+        double v = G[(size_t)i * c + j];
+        for (int k = 0; k < j; ++k) v -= L[(size_t)i * c + k] * L[(size_t)j * c + k];
+        L[(size_t)i * c + j] = v / d;
+      }
+    }
+    // M = L^-T (upper triangular): solve L^T M = I column by column
+    std::fill(M.begin(), M.end(), 0.0);
+    for (int col = 0; col < c; ++col)
+      for (int i = c - 1; i >= 0; --i) {
+        double v = (i == col) ? 1.0 : 0.0;
+        for (int k = i + 1; k < c; ++k) v -= L[(size_t)k * c + i] * M[(size_t)k * c + col];
+        M[(size_t)i * c + col] = v / L[(size_t)i * c + i];
+      }
+    TRY(upload(M, M_dev, st, stage));
+    TRY(run_mat(false, Y, c, rows, c, M_dev, c, tmp, st));
+    if (hipMemcpyAsync(Y, tmp, (size_t)rows * c * 4, hipMemcpyDeviceToDevice, st) != hipSuccess) return LORA4_ERR_HIP;
+  }
+  return LORA4_OK;
+}
+
+// Eigen-decomposition of a symmetric c x c matrix (cyclic Jacobi): values in
+// descending order, vectors as columns of V.
+void jacobi_eigen(std::vector<double> A, int c, std::vector<double> &vals, std::vector<double> &V) {
+  V.assign((size_t)c * c, 0.0);
+  for (int i = 0; i < c; ++i) V[(size_t)i * c + i] = 1.0;
+  for (int sweep = 0; sweep < 100; ++sweep) {
+    double off = 0, tot = 0;
+    for (int i = 0; i < c; ++i)
+      for (int j = 0; j < c; ++j) {
+        const double a = A[(size_t)i * c + j] * A[(size_t)i * c + j];
+        tot += a;
+        if (i != j) off += a;
+      }
+    if (off <= 1e-30 * (tot > 0 ? tot : 1.0)) break;
+    for (int p = 0; p < c - 1; ++p)
+      for (int q = p + 1; q < c; ++q) {
+        const double apq = A[(size_t)p * c + q];
+        if (apq == 0.0) continue;
+        const double theta = (A[(size_t)q * c + q] - A[(size_t)p * c + p]) / (2 * apq);
+        const double t = (theta >= 0 ? 1.0 : -1.0) / (std::fabs(theta) + std::sqrt(theta * theta + 1));
+        const double cs = 1 / std::sqrt(t * t + 1), sn = t * cs;
+        for (int k = 0; k < c; ++k) {   // A <- A J (columns p, q)
+          const double akp = A[(size_t)k * c + p], akq = A[(size_t)k * c + q];
+          A[(size_t)k * c + p] = cs * akp - sn * akq;
+          A[(size_t)k * c + q] = sn * akp + cs * akq;
+        }
+        for (int k = 0; k < c; ++k) {   // A <- J^T A (rows p, q)
+          const double apk = A[(size_t)p * c + k], aqk = A[(size_t)q * c + k];
+          A[(size_t)p * c + k] = cs * apk - sn * aqk;
+          A[(size_t)q * c + k] = sn * apk + cs * aqk;
+        }
+        for (int k = 0; k < c; ++k) {   // V <- V J
+          const double vkp = V[(size_t)k * c + p], vkq = V[(size_t)k * c + q];
+          V[(size_t)k * c + p] = cs * vkp - sn * vkq;
+          V[(size_t)k * c + q] = sn * vkp + cs * vkq;
+        }
+      }
+  }
+  std::vector<int> idx(c);
+  for (int i = 0; i < c; ++i) idx[i] = i;
+  std::sort(idx.begin(), idx.end(), [&](int a, int b) { return A[(size_t)a * c + a] > A[(size_t)b * c + b]; });
+  std::vector<double> V2((size_t)c * c);
+  vals.resize(c);
+  for (int j = 0; j < c; ++j) {
+    vals[j] = A[(size_t)idx[j] * c + idx[j]];
+    for (int i = 0; i < c; ++i) V2[(size_t)i * c + j] = V[(size_t)i * c + idx[j]];
+  }
+  V.swap(V2);
+}
+
 template <bool GEMM>
 lora4_status run_quant_mxfp8(const uint16_t *X, int64_t ldx, int64_t M, int64_t K, uint8_t *codes, int64_t ldc,
                              int64_t Mp, int64_t Kp, uint8_t *scales, hipStream_t st) {
@@ -1189,6 +1337,88 @@ lora4_status quant_pack_nvfp4(const uint16_t *W_bf16, int64_t N, int64_t K, uint
   const int64_t nblk = N * (K / 16);
   return launch_args("quant_pack_nvfp4", k_quant_nvfp4, dim3((unsigned)ceil_div(nblk, 256)), dim3(256), st,
                      W_bf16, N, K, codes, scales_e4m3);
+}
+
+size_t lora4_loftq_workspace_bytes(int64_t N, int64_t K, int32_t r) {
+  if (N < 1 || K < 64 || K % 64 != 0 || N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return 0;
+  if (r < 1 || r > 128 || r + LOFTQ_OVERSAMPLE > N || r + LOFTQ_OVERSAMPLE > K) return 0;
+  return make_loftq_plan(N, K, r).bytes;
+}
+
+lora4_status lora4_loftq_init(const uint16_t *W, int64_t N, int64_t K, int32_t r, int32_t iters, float s,
+                              int32_t double_quant, uint8_t *codes, void *scales, float *scales2, uint16_t *A,
+                              uint16_t *B, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!W || !codes || !scales || !A || !B || (double_quant && !scales2)) return LORA4_ERR_NULL;
+  if (N < 1 || K < 64 || K % 64 != 0 || N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return LORA4_ERR_SHAPE;
+  if (r < 1 || r > 128 || r + LOFTQ_OVERSAMPLE > N || r + LOFTQ_OVERSAMPLE > K) return LORA4_ERR_SHAPE;
+  if (iters < 1 || iters > 64 || !std::isfinite(s) || s == 0.0f) return LORA4_ERR_SHAPE;
+  for (const void *q : {(const void *)W, (const void *)codes, (const void *)scales, (const void *)A,
+                        (const void *)B, (const void *)scales2})
+    if (q && !aligned16(q)) return LORA4_ERR_ALIGN;
+  const LoftqPlan lp = make_loftq_plan(N, K, r);
+  if (!workspace) return LORA4_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LORA4_ERR_ALIGN;
+  if (workspace_bytes < lp.bytes) return LORA4_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int c = lp.c;
+  uint16_t *T = ws_at<uint16_t>(workspace, lp.off_T);
+  float *R = ws_at<float>(workspace, lp.off_R), *Y = ws_at<float>(workspace, lp.off_Y);
+  float *Y2 = ws_at<float>(workspace, lp.off_Y2), *Z = ws_at<float>(workspace, lp.off_Z);
+  float *Z2 = ws_at<float>(workspace, lp.off_Z2), *G = ws_at<float>(workspace, lp.off_G);
+  float *Md = ws_at<float>(workspace, lp.off_M), *Bf = ws_at<float>(workspace, lp.off_B);
+  float *ATf = ws_at<float>(workspace, lp.off_AT);
+  const lora4_W Wq{double_quant ? LORA4_NF4_DQ : LORA4_NF4, 64, N, K, 1, codes, scales, scales2};
+  const PackedW Qp = packed_of(Base{&Wq, 1, false});
+  const int64_t nk = N * K;
+  std::vector<double> Gh, vals, V, Mh;
+  std::vector<float> stage;
+  for (int it = 0; it < iters; ++it) {
+    // Q_t = NF4(bf16(W - B_{t-1} A_{t-1})), R_t = W - Q_t
+    TRY(launch_args("loftq_shift", loftq::k_shift, dim3((unsigned)ceil_div(nk, 256)), dim3(256), st, W,
+                    (const float *)Bf, (const float *)ATf, N, K, it == 0 ? 0 : (int)r, T));
+    TRY(quant_pack_nf4(T, N, K, double_quant, codes, scales, scales2, stream));
+    const dim3 rg((unsigned)ceil_div(N * (K / 32), 256));
+    if (double_quant)
+      TRY(launch_args("loftq_residual", loftq::k_residual<FMT_NF4_DQ>, rg, dim3(256), st, W, Qp, nf4_table(), R));
+    else
+      TRY(launch_args("loftq_residual", loftq::k_residual<FMT_NF4>, rg, dim3(256), st, W, Qp, nf4_table(), R));
+    // top-r subspace of R: Y = orth(R Omega), then (R R^T) applied LOFTQ_POWER times
+    TRY(launch_args("loftq_start", loftq::k_rademacher, dim3((unsigned)ceil_div(K * c, 256)), dim3(256), st, Z2,
+                    K * c, (uint64_t)0x5EED0000u + (uint64_t)it));
+    TRY(run_mat(false, R, K, N, K, Z2, c, Y, st));
+    TRY(orthonormalize(Y, Y2, N, c, G, Md, st));
+    for (int q = 0; q < LOFTQ_POWER; ++q) {
+      TRY(run_mat(true, R, K, K, N, Y, c, Z, st));
+      TRY(orthonormalize(Z, Z2, K, c, G, Md, st));
+      TRY(run_mat(false, R, K, N, K, Z, c, Y, st));
+      TRY(orthonormalize(Y, Y2, N, c, G, Md, st));
+    }
+    // R ~ Y Z^T with Z = R^T Y; Z^T = U S V^T from the eigenvectors of Z^T Z:
+    // B = Y U_r S_r^(1/2), A^T = Z U_r S_r^(-1/2)
+    TRY(run_mat(true, R, K, K, N, Y, c, Z, st));
+    TRY(gram_to_host(Z, K, c, G, Gh, st));
+    jacobi_eigen(Gh, c, vals, V);
+    const double smax = vals[0] > 0 ? std::sqrt(vals[0]) : 0.0;
+    Mh.assign((size_t)c * r, 0.0);
+    for (int i = 0; i < c; ++i)
+      for (int j = 0; j < r; ++j) {
+        const double sg = vals[j] > 0 ? std::sqrt(vals[j]) : 0.0;
+        Mh[(size_t)i * r + j] = V[(size_t)i * c + j] * std::sqrt(sg);
+      }
+    TRY(upload(Mh, Md, st, stage));
+    TRY(run_mat(false, Y, c, N, c, Md, r, Bf, st));
+    for (int i = 0; i < c; ++i)
+      for (int j = 0; j < r; ++j) {
+        const double sg = vals[j] > 0 ? std::sqrt(vals[j]) : 0.0;
+        Mh[(size_t)i * r + j] = sg > 1e-30 * (smax > 0 ? smax : 1.0) ? V[(size_t)i * c + j] / std::sqrt(sg) : 0.0;
+      }
+    TRY(upload(Mh, Md, st, stage));
+    TRY(run_mat(false, Z, c, K, c, Md, r, ATf, st));
+  }
+  TRY(launch_args("loftq_out", loftq::k_to_bf16, dim3((unsigned)ceil_div(N * r, 256)), dim3(256), st,
+                  (const float *)Bf, N * r, 1.0f / s, B));
+  return launch_args("loftq_out", loftq::k_to_bf16_t, dim3((unsigned)ceil_div(K * r, 256)), dim3(256), st,
+                     (const float *)ATf, K, (int)r, 1.0f, A);
 }
 
 lora4_status lora4_timing_enable(int on) {

@@ -221,3 +221,28 @@ def test_nvfp4_packer_validation(lib):
     assert L.quant_pack_nvfp4(4096, 0, 64, 4096, 4096, None) == ESHAPE
     assert L.quant_pack_nvfp4(None, 64, 64, 4096, 4096, None) == ENULL
     assert L.quant_pack_nvfp4(4096, 64, 64, 4100, 4096, None) == EALIGN
+
+
+def test_loftq_validation(lib):
+    assert L.lora4_loftq_workspace_bytes(256, 512, 16) >= 256 * 512 * 6
+    assert L.lora4_loftq_workspace_bytes(256, 500, 16) == 0              # K % 64
+    assert L.lora4_loftq_workspace_bytes(256, 512, 129) == 0             # r <= 128
+    assert L.lora4_loftq_workspace_bytes(20, 512, 16) == 0               # r + 8 <= N
+    need = L.lora4_loftq_workspace_bytes(256, 512, 16)
+
+    def init(**kw):
+        a = dict(W=4096, N=256, K=512, r=16, iters=5, s=2.0, dq=0, codes=4096, scales=4096, scales2=None,
+                 A=4096, B=4096, ws=8192, nbytes=need, stream=None)
+        a.update(kw)
+        return L.lora4_loftq_init(a["W"], a["N"], a["K"], a["r"], a["iters"], a["s"], a["dq"], a["codes"],
+                                  a["scales"], a["scales2"], a["A"], a["B"], a["ws"], a["nbytes"], a["stream"])
+
+    assert init(W=None) == ENULL
+    assert init(dq=1) == ENULL                                            # DQ needs scales2
+    assert init(K=500) == ESHAPE
+    assert init(r=0) == ESHAPE
+    assert init(iters=0) == ESHAPE
+    assert init(s=0.0) == ESHAPE
+    assert init(A=4100) == EALIGN
+    assert init(ws=None) == EWS
+    assert init(nbytes=need - 1) == EWS
