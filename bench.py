@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--mx", action="store_true",
                     help="forward through the MX-native path (MXFP8 activations x MXFP4 base on the scaled "
                          "MFMA); plain MXFP4 layer sets only")
+    ap.add_argument("--loftq", action="store_true",
+                    help="time the LoftQ initialisation (5 iterations, NF4) of the workload's bases instead of a step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--blas-context", action="store_true",
@@ -298,6 +300,37 @@ def cpu_baseline(specs, tokens, reps):
                       f"backward, float64 numpy"}
 
 
+def loftq_bench(args, specs, L, torch, synth):
+    """Wall time of lora4_loftq_init (5 iterations, NF4, the layer's rank and
+    scale) over the workload's bases, with the library's per-kernel times."""
+    Ws = []
+    for s in specs:
+        t = synth.inputs(s)
+        W = t["W"] if s.experts == 1 else t["W"][0]
+        Ws.append((s, torch.from_numpy(W.view("int16")).view(torch.bfloat16).to("cuda:0")))
+    for s, W in Ws[:1]:
+        L.loftq_init(W, s.r, iters=1, s=s.s)          # warm-up (first launches)
+    torch.cuda.synchronize()
+    L.timing_enable(True)
+    L.timing_collect()
+    t0 = time.perf_counter()
+    for s, W in Ws:
+        L.loftq_init(W, s.r, iters=5, s=s.s)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3
+    kt = L.timing_collect()
+    L.timing_enable(False)
+    kernels = {k: {"launches": n, "total_ms": round(tot, 3)} for k, (n, tot) in kt.items()}
+    for k, v in sorted(kernels.items(), key=lambda kv: -kv[1]["total_ms"]):
+        log(f"[loftq]   {k:18s} {v['launches']:6d} launches  {v['total_ms']:9.2f} ms")
+    log(f"[loftq] {len(Ws)} bases, 5 iterations each: {ms:.1f} ms")
+    print(json.dumps({"metric": "LoftQ initialisation time of the workload's bases (5 iterations, NF4)",
+                      "value": round(ms, 2), "unit": "ms", "higher_is_better": False, "n_gpus": 1,
+                      "config": {"workload": args.workload, "layers_KxN": [[s.K, s.N] for s in specs],
+                                 "rank": specs[0].r},
+                      "kernels": kernels}), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -324,6 +357,9 @@ def main():
     if args.mx and any(s.fmt != synth.MXFP4 or s.experts != 1 for s in specs):
         print("--mx needs a workload of plain MXFP4 layers (llama70b)", file=sys.stderr)
         sys.exit(2)
+    if args.loftq:
+        loftq_bench(args, specs, L, torch, synth)
+        return
     log(f"[bench] workload {args.workload}: {len(specs)} layers, generating inputs")
     layers = [Layer(s, L, torch, synth, mx=args.mx) for s in specs]
     ws = torch.empty((max(l.ws_bytes for l in layers),), dtype=torch.uint8, device="cuda:0")

@@ -19,11 +19,13 @@ constexpr int MAX_C = 144;      // widest M (r + 16 for r <= 128)
 // out[o][j] = sum_t X(o, t) M[t][j] for o < rows, j < c, t < inner, with
 // X(o, t) = X[o][t] (TRANS = false, X is [rows][ldx]) or X[t][o] (TRANS =
 // true, X is [inner][ldx]); M is [inner][c], out [rows][c], all fp32. One
-// workgroup per 32 output rows; thread t owns row t % 32 and columns
-// t / 32 + 8 u; the sum over t runs in order (deterministic).
+// workgroup per 32 output rows and reduction range (blockIdx.y: t in
+// [y per_split, (y + 1) per_split), written to out + y rows c); thread t
+// owns row t % 32 and columns t / 32 + 8 u; the sum over t runs in order
+// (deterministic).
 template <bool TRANS>
 __global__ __launch_bounds__(256) void k_mat(const float *X, int64_t ldx, int64_t rows, int64_t inner,
-                                             const float *M, int c, float *out) {
+                                             const float *M, int c, float *out, int64_t per_split) {
   __shared__ float xs[MAT_CHUNK][MAT_ROWS + 1];
   __shared__ float ms[MAT_CHUNK][MAX_C];
   const int t = threadIdx.x;
@@ -33,7 +35,10 @@ __global__ __launch_bounds__(256) void k_mat(const float *X, int64_t ldx, int64_
   float acc[NU];
 #pragma unroll
   for (int u = 0; u < NU; ++u) acc[u] = 0.0f;
-  for (int64_t t0 = 0; t0 < inner; t0 += MAT_CHUNK) {
+  const int64_t t_lo = (int64_t)blockIdx.y * per_split;
+  const int64_t t_hi = t_lo + per_split < inner ? t_lo + per_split : inner;
+  out += (int64_t)blockIdx.y * rows * c;
+  for (int64_t t0 = t_lo; t0 < t_hi; t0 += MAT_CHUNK) {
     // stage X(o0 .. +31, t0 .. +31) as xs[t][o] and M(t0 .. +31, 0 .. c)
     for (int e = t; e < MAT_CHUNK * MAT_ROWS; e += 256) {
       int tt, oo;
@@ -46,13 +51,13 @@ __global__ __launch_bounds__(256) void k_mat(const float *X, int64_t ldx, int64_
       }
       const int64_t gt = t0 + tt, go = o0 + oo;
       float v = 0.0f;
-      if (gt < inner && go < rows) v = TRANS ? X[gt * ldx + go] : X[go * ldx + gt];
+      if (gt < t_hi && go < rows) v = TRANS ? X[gt * ldx + go] : X[go * ldx + gt];
       xs[tt][oo] = v;
     }
     for (int e = t; e < MAT_CHUNK * c; e += 256) {
       const int tt = e / c, j = e % c;
       const int64_t gt = t0 + tt;
-      ms[tt][j] = gt < inner ? M[gt * c + j] : 0.0f;
+      ms[tt][j] = gt < t_hi ? M[gt * c + j] : 0.0f;
     }
     __syncthreads();
     for (int tt = 0; tt < MAT_CHUNK; ++tt) {
@@ -73,6 +78,15 @@ __global__ __launch_bounds__(256) void k_mat(const float *X, int64_t ldx, int64_
       if (j < c) out[o * c + j] = acc[u];
     }
   }
+}
+
+// out[i] = sum over the S partials part[s][i], in order.
+__global__ void k_sum_parts(const float *part, int S, int64_t n, float *out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float v = 0.0f;
+  for (int s = 0; s < S; ++s) v += part[s * n + i];
+  out[i] = v;
 }
 
 // T[n][k] = bf16(W[n][k] - sum_j B[n][j] AT[k][j]) (B [N][r], AT [K][r] fp32;

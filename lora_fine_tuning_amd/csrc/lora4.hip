@@ -823,9 +823,11 @@ lora4_status check_mx(const lora4_W *W, int64_t M, int32_t r, float s) {
 constexpr int LOFTQ_OVERSAMPLE = 16;   // columns beyond r in the subspace
 constexpr int LOFTQ_POWER = 8;         // power iterations (R R^T applied 8 times)
 
+constexpr int LOFTQ_MAX_SPLIT = 64;   // reduction ranges of a product with few output rows
+
 struct LoftqPlan {
   int c;
-  size_t off_T, off_R, off_Y, off_Y2, off_Z, off_Z2, off_G, off_M, off_B, off_AT, bytes;
+  size_t off_T, off_R, off_Y, off_Y2, off_Z, off_Z2, off_G, off_M, off_B, off_AT, off_P, bytes;
 };
 
 LoftqPlan make_loftq_plan(int64_t N, int64_t K, int r) {
@@ -847,20 +849,37 @@ LoftqPlan make_loftq_plan(int64_t N, int64_t K, int r) {
   p.off_M = take((size_t)p.c * p.c * 4);
   p.off_B = take((size_t)N * r * 4);
   p.off_AT = take((size_t)K * r * 4);
+  p.off_P = take((size_t)LOFTQ_MAX_SPLIT * p.c * p.c * 4);   // partials of the c x c products
   p.bytes = off;
   return p;
 }
 
+// out = X M or X^T M (k_mat); a product with few output rows (the c x c
+// Gram matrices) splits its reduction over up to LOFTQ_MAX_SPLIT workgroups
+// into fp32 partials (parts, rows * c each) summed in order afterwards.
 lora4_status run_mat(bool trans, const float *X, int64_t ldx, int64_t rows, int64_t inner, const float *M, int c,
-                     float *out, hipStream_t st) {
-  const dim3 grid((unsigned)ceil_div(rows, loftq::MAT_ROWS));
-  if (trans) return launch_args("loftq_mat_tn", loftq::k_mat<true>, grid, dim3(256), st, X, ldx, rows, inner, M, c, out);
-  return launch_args("loftq_mat_nn", loftq::k_mat<false>, grid, dim3(256), st, X, ldx, rows, inner, M, c, out);
+                     float *out, hipStream_t st, float *parts = nullptr) {
+  const int64_t tiles = ceil_div(rows, loftq::MAT_ROWS);
+  int64_t S = 1;
+  if (parts && tiles < 64) S = std::min<int64_t>(LOFTQ_MAX_SPLIT, std::max<int64_t>(1, inner / 512));
+  const int64_t per = ceil_div(inner, S * loftq::MAT_CHUNK) * loftq::MAT_CHUNK;
+  S = ceil_div(inner, per);
+  const dim3 grid((unsigned)tiles, (unsigned)S);
+  float *dst = S > 1 ? parts : out;
+  if (trans)
+    TRY(launch_args("loftq_mat_tn", loftq::k_mat<true>, grid, dim3(256), st, X, ldx, rows, inner, M, c, dst, per));
+  else
+    TRY(launch_args("loftq_mat_nn", loftq::k_mat<false>, grid, dim3(256), st, X, ldx, rows, inner, M, c, dst, per));
+  if (S == 1) return LORA4_OK;
+  const int64_t n = rows * c;
+  return launch_args("loftq_sum", loftq::k_sum_parts, dim3((unsigned)ceil_div(n, 256)), dim3(256), st,
+                     (const float *)parts, (int)S, n, out);
 }
 
 // c x c Gram matrix of the columns of Y [rows][c] to the host (double).
-lora4_status gram_to_host(const float *Y, int64_t rows, int c, float *G_dev, std::vector<double> &G, hipStream_t st) {
-  TRY(run_mat(true, Y, c, c, rows, Y, c, G_dev, st));
+lora4_status gram_to_host(const float *Y, int64_t rows, int c, float *G_dev, float *parts, std::vector<double> &G,
+                          hipStream_t st) {
+  TRY(run_mat(true, Y, c, c, rows, Y, c, G_dev, st, parts));
   std::vector<float> g((size_t)c * c);
   if (hipMemcpyAsync(g.data(), G_dev, g.size() * 4, hipMemcpyDeviceToHost, st) != hipSuccess) return LORA4_ERR_HIP;
   if (hipStreamSynchronize(st) != hipSuccess) return LORA4_ERR_HIP;
@@ -878,11 +897,12 @@ lora4_status upload(const std::vector<double> &M, float *dst, hipStream_t st, st
 // Orthonormalize the columns of Y [rows][c] (CholeskyQR, twice): Y <- Y L^-T
 // with Y^T Y = L L^T. A Gram matrix that is not positive definite (Y of lower
 // rank) gets a small diagonal shift.
-lora4_status orthonormalize(float *Y, float *tmp, int64_t rows, int c, float *G_dev, float *M_dev, hipStream_t st) {
+lora4_status orthonormalize(float *Y, float *tmp, int64_t rows, int c, float *G_dev, float *M_dev, float *parts,
+                            hipStream_t st) {
   std::vector<double> G, M((size_t)c * c), L((size_t)c * c);
   std::vector<float> stage;
   for (int pass = 0; pass < 2; ++pass) {
-    TRY(gram_to_host(Y, rows, c, G_dev, G, st));
+    TRY(gram_to_host(Y, rows, c, G_dev, parts, G, st));
     double tr = 0;
     for (int i = 0; i < c; ++i) tr += G[(size_t)i * c + i];
     const double eps = 1e-12 * (tr > 0 ? tr : 1.0);
@@ -1367,6 +1387,7 @@ lora4_status lora4_loftq_init(const uint16_t *W, int64_t N, int64_t K, int32_t r
   float *Z2 = ws_at<float>(workspace, lp.off_Z2), *G = ws_at<float>(workspace, lp.off_G);
   float *Md = ws_at<float>(workspace, lp.off_M), *Bf = ws_at<float>(workspace, lp.off_B);
   float *ATf = ws_at<float>(workspace, lp.off_AT);
+  float *P = ws_at<float>(workspace, lp.off_P);
   const lora4_W Wq{double_quant ? LORA4_NF4_DQ : LORA4_NF4, 64, N, K, 1, codes, scales, scales2};
   const PackedW Qp = packed_of(Base{&Wq, 1, false});
   const int64_t nk = N * K;
@@ -1386,17 +1407,17 @@ lora4_status lora4_loftq_init(const uint16_t *W, int64_t N, int64_t K, int32_t r
     TRY(launch_args("loftq_start", loftq::k_rademacher, dim3((unsigned)ceil_div(K * c, 256)), dim3(256), st, Z2,
                     K * c, (uint64_t)0x5EED0000u + (uint64_t)it));
     TRY(run_mat(false, R, K, N, K, Z2, c, Y, st));
-    TRY(orthonormalize(Y, Y2, N, c, G, Md, st));
+    TRY(orthonormalize(Y, Y2, N, c, G, Md, P, st));
     for (int q = 0; q < LOFTQ_POWER; ++q) {
       TRY(run_mat(true, R, K, K, N, Y, c, Z, st));
-      TRY(orthonormalize(Z, Z2, K, c, G, Md, st));
+      TRY(orthonormalize(Z, Z2, K, c, G, Md, P, st));
       TRY(run_mat(false, R, K, N, K, Z, c, Y, st));
-      TRY(orthonormalize(Y, Y2, N, c, G, Md, st));
+      TRY(orthonormalize(Y, Y2, N, c, G, Md, P, st));
     }
     // R ~ Y Z^T with Z = R^T Y; Z^T = U S V^T from the eigenvectors of Z^T Z:
     // B = Y U_r S_r^(1/2), A^T = Z U_r S_r^(-1/2)
     TRY(run_mat(true, R, K, K, N, Y, c, Z, st));
-    TRY(gram_to_host(Z, K, c, G, Gh, st));
+    TRY(gram_to_host(Z, K, c, G, P, Gh, st));
     jacobi_eigen(Gh, c, vals, V);
     const double smax = vals[0] > 0 ? std::sqrt(vals[0]) : 0.0;
     Mh.assign((size_t)c * r, 0.0);
