@@ -49,6 +49,8 @@ def parse():
                          "MFMA); plain MXFP4 layer sets only")
     ap.add_argument("--loftq", action="store_true",
                     help="time the LoftQ initialisation (5 iterations, NF4) of the workload's bases instead of a step")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and time its replays (the same kernels, fewer launch gaps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--blas-context", action="store_true",
@@ -366,11 +368,14 @@ def main():
     stream = torch.cuda.current_stream().cuda_stream
     flops = sum(s.flops() for s in specs)
 
-    def step():
+    def step_eager():
+        st = torch.cuda.current_stream().cuda_stream   # the capturing stream inside a graph capture
         for l in layers:
-            l.fwd(L, ws, stream)
+            l.fwd(L, ws, st)
         for l in reversed(layers):
-            l.bwd(L, ws, stream)
+            l.bwd(L, ws, st)
+
+    step = step_eager
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -390,6 +395,23 @@ def main():
         w1 = time.perf_counter()
         return max(e0.elapsed_time(e1), (w1 - w0) * 1e3) / k
 
+    graph = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step_eager()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step_eager()
+        torch.cuda.synchronize()
+        step = graph.replay
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        log("[bench] one step captured in a HIP graph; timing its replays")
     log(f"[bench] timing {args.steps} steps")
     ms = timed(args.steps)
     value = flops / (ms * 1e-3) / 1e12
