@@ -78,7 +78,7 @@ typedef enum {
   LORA4_ERR_FORMAT = -4,        /* unknown format, or block does not match it    */
   LORA4_ERR_WORKSPACE = -5,     /* workspace NULL or smaller than required       */
   LORA4_ERR_HIP = -6,           /* a HIP call or kernel launch failed            */
-  LORA4_ERR_UNIMPLEMENTED = -7  /* valid request this build does not support     */
+  LORA4_ERR_UNIMPLEMENTED = -7  /* valid request the library does not support   */
 } lora4_status;
 
 /* The frozen 4-bit base W, logically [N = d_out, K = d_in] per group.

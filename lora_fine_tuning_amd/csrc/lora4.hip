@@ -1012,7 +1012,7 @@ const char *lora4_status_string(lora4_status s) {
     case LORA4_ERR_FORMAT: return "unknown format or block size";
     case LORA4_ERR_WORKSPACE: return "workspace missing or too small";
     case LORA4_ERR_HIP: return "a HIP call or kernel launch failed";
-    case LORA4_ERR_UNIMPLEMENTED: return "not supported by this build";
+    case LORA4_ERR_UNIMPLEMENTED: return "not supported by the library";
   }
   return "unknown status";
 }
