@@ -22,7 +22,7 @@ import torch
 
 import lora_fine_tuning_amd as L
 import synth
-from oracle import codecs, lora, mxfp4, nf4
+from oracle import codecs, lora, mxfp4, nf4, nvfp4
 from gpu_util import DEV, TOL, f64, print_case, tile_codes, tile_scales, to_dev, to_host, untile_rows
 
 pytestmark = pytest.mark.gpu
@@ -30,7 +30,12 @@ pytestmark = pytest.mark.gpu
 
 def _pack_gpu(W, fmt):
     Wd = to_dev(W)
-    out = L.pack_mxfp4(Wd) if fmt == synth.MXFP4 else L.pack_nf4(Wd, double_quant=(fmt == synth.NF4_DQ))
+    if fmt == synth.MXFP4:
+        out = L.pack_mxfp4(Wd)
+    elif fmt == synth.NVFP4:
+        out = L.pack_nvfp4(Wd)
+    else:
+        out = L.pack_nf4(Wd, double_quant=(fmt == synth.NF4_DQ))
     del Wd
     return out
 
@@ -38,12 +43,16 @@ def _pack_gpu(W, fmt):
 def _oracle_pack_rows(W, rows, fmt):
     if fmt == synth.MXFP4:
         return mxfp4.quantize(W[rows])
+    if fmt == synth.NVFP4:
+        return nvfp4.quantize(W[rows])
     return nf4.quantize(W[rows])
 
 
 def _dequant(parts, fmt):
     if fmt == synth.MXFP4:
         return mxfp4.dequantize(*parts)
+    if fmt == synth.NVFP4:
+        return nvfp4.dequantize(*parts)
     if fmt == synth.NF4_DQ:
         return nf4.dequantize_dq(*parts)
     return nf4.dequantize(*parts)
@@ -61,6 +70,8 @@ def _deq_cols(W, k0, k1, fmt, full_dq=None):
     sub = np.ascontiguousarray(W[:, k0:k1])
     if fmt == synth.MXFP4:
         return f64(mxfp4.dequantize(*mxfp4.quantize(sub)))
+    if fmt == synth.NVFP4:
+        return f64(nvfp4.dequantize(*nvfp4.quantize(sub)))
     return f64(nf4.dequantize(*nf4.quantize(sub)))
 
 
@@ -112,7 +123,7 @@ def _check_layer(lay, rng, n_rows=64, n_cols=64, n_kblk=2):
         else:
             pc, ps = _oracle_pack_rows(We, nrows, lay.fmt)
             assert np.array_equal(untile_rows(codes[e], lay.N, lay.K, nrows, 32), pc)
-            per = 2 if lay.fmt == synth.MXFP4 else 1
+            per = {synth.MXFP4: 2, synth.NVFP4: 4}.get(lay.fmt, 1)
             got_s = untile_rows(scales[e], lay.N, lay.K, nrows, per)
             if lay.fmt == synth.NF4:
                 assert np.array_equal(got_s.view(np.uint32), ps.view(np.uint32))
@@ -158,3 +169,12 @@ def _layers(w):
 def test_workload_layer(w, i):
     lay = synth.layers(w)[i]
     _check_layer(lay, np.random.default_rng(100 * w + i))
+
+
+@pytest.mark.parametrize("i", [0, 4, 6])
+def test_workload_layer_nvfp4(i):
+    """Layers of the 8B set (4096 -> 4096, 4096 -> 14336, 14336 -> 4096) with an
+    NVFP4 base, as bench.py --fmt nvfp4 runs them."""
+    import dataclasses
+    lay = dataclasses.replace(synth.layers(2)[i], fmt=synth.NVFP4)
+    _check_layer(lay, np.random.default_rng(700 + i))
