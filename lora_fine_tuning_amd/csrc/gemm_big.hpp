@@ -90,23 +90,30 @@ __device__ __forceinline__ int group_of_row(const int64_t *offsets, int groups, 
   return lo;
 }
 
-// Calls f(group, ra, rb) for each group with rows [ra, rb) (non-empty) in
-// the row range [row0, row_hi) of a tile that ignores the groups, in group
-// order, with a barrier between calls (f stages through LDS). (Tiles ignore
-// the groups only where there are several, so offsets is given.)
-template <typename F>
-__device__ __forceinline__ void for_tile_groups(const Params &p, int64_t row0, int64_t row_hi, F &&f) {
-  const int g_lo = group_of_row(p.offsets, p.groups, row0);
-  const int g_hi = group_of_row(p.offsets, p.groups, row_hi - 1);
-  bool first = true;
-  for (int gg = g_lo; gg <= g_hi; ++gg) {
-    const int64_t ra = p.offsets[gg] > row0 ? p.offsets[gg] : row0;
-    const int64_t rb = p.offsets[gg + 1] < row_hi ? p.offsets[gg + 1] : row_hi;
-    if (ra >= rb) continue;
-    if (!first) __syncthreads();
-    first = false;
-    f(gg, ra, rb);
-  }
+// The groups with rows in the row range [row0, row_hi) of a tile that
+// ignores the groups (offsets given: tiles ignore the groups only where
+// there are several): their tail products run as one product whose
+// reduction puts the groups' rank columns side by side, group g0 + i at
+// columns i rp .. i rp + r2 - 1 (rp = r2 rounded up to 8). A row's operand
+// is zero outside its own group's columns and each group's B rows fill its
+// columns, so the sum over the wider reduction is each row's own group's
+// product (a block-diagonal operand), in one pass for all the groups.
+struct TileGroups {
+  int g0, n, rp;
+};
+
+__device__ __forceinline__ TileGroups tile_groups(const Params &p, int64_t row0, int64_t row_hi) {
+  TileGroups tg;
+  tg.g0 = group_of_row(p.offsets, p.groups, row0);
+  tg.n = group_of_row(p.offsets, p.groups, row_hi - 1) - tg.g0 + 1;
+  tg.rp = (p.r2 + 7) & ~7;
+  return tg;
+}
+
+// Index within the tile's groups of the group holding row gr (-1 for a row
+// past the tile's range).
+__device__ __forceinline__ int row_group(const Params &p, const TileGroups &tg, int64_t gr, int64_t row_hi) {
+  return gr < row_hi ? group_of_row(p.offsets + tg.g0, tg.n, gr) : -1;
 }
 
 constexpr int A2_MAX_PARTS = 4;
@@ -190,21 +197,29 @@ __device__ __forceinline__ void store_a2_piece(uint16_t *out, int r2, int64_t gr
 
 // One 64-column step (k0 ..) of the tail operand from the partials into the
 // LDS tile `As` (256 rows from row0, bf16, 8-column chunk c of row i at
-// As + lds_off(i, c)): thread t owns row row0 + t; rows outside [ra, rb) and
-// chunks past r2 are zero. (LO: ra may lie above row0; else ra == row0.)
-template <bool LO, typename Off>
+// As + lds_off(i, c)): thread t owns row row0 + t; rows at or past rb and
+// chunks past r2 are zero. SHARED: the columns are those of the tile's groups
+// side by side (rp per group) and the row's own group is the tile's group
+// `my` (-1: none), its other groups' columns zero.
+template <bool SHARED, typename Off>
 __device__ __forceinline__ void a2_parts_to_lds(const Params &p, uint16_t *As, Off lds_off, int64_t row0,
-                                                int64_t ra, int64_t rb, int k0, int t, bool store_out) {
+                                                int64_t rb, int k0, int t, bool store_out, int rp = 0, int my = 0) {
   const int64_t gr = row0 + t;
-  const bool row_ok = (!LO || gr >= ra) && gr < rb;
+  const bool row_ok = gr < rb;
 #pragma unroll 1
   for (int c0 = 0; c0 < 8; c0 += 2) {
     float v[2][8];
+    bool ok[2];
+    int64_t gk[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int64_t gk = k0 + 8 * (c0 + u);
-      if (row_ok && gk < p.r2) {
-        a2_part_sum(p, gr, gk, v[u]);
+      const int kc = k0 + 8 * (c0 + u);
+      int gi = 0;
+      if constexpr (SHARED) gi = kc / rp;
+      gk[u] = kc - gi * rp;
+      ok[u] = row_ok && gi == my && gk[u] < p.r2;
+      if (ok[u]) {
+        a2_part_sum(p, gr, gk[u], v[u]);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[u][e] = 0.0f;
@@ -212,13 +227,40 @@ __device__ __forceinline__ void a2_parts_to_lds(const Params &p, uint16_t *As, O
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int64_t gk = k0 + 8 * (c0 + u);
       lds_write_b128(As + lds_off(t, c0 + u), pack_scaled8(v[u], p.A2scale));
-      if (store_out && row_ok && gk < p.r2) {
-        if (p.A2out1) store_a2_piece(p.A2out1, p.r2, gr, gk, pack_scaled8(v[u], p.A2alpha1));
-        if (p.A2out2) store_a2_piece(p.A2out2, p.r2, gr, gk, pack_scaled8(v[u], p.A2alpha2));
+      if (store_out && ok[u]) {
+        if (p.A2out1) store_a2_piece(p.A2out1, p.r2, gr, gk[u], pack_scaled8(v[u], p.A2alpha1));
+        if (p.A2out2) store_a2_piece(p.A2out2, p.r2, gr, gk[u], pack_scaled8(v[u], p.A2alpha2));
       }
     }
+  }
+}
+
+// The same step from the bf16 operand rows of A2, thread t owning row
+// row0 + t (the SHARED layout of a2_parts_to_lds).
+template <typename Off>
+__device__ __forceinline__ void a2_rows_to_lds(const Params &p, uint16_t *As, Off lds_off, int64_t row0, int64_t rb,
+                                               int k0, int t, int rp, int my) {
+  const int64_t gr = row0 + t;
+  const bool a_vec = (p.A2.ld % 8) == 0;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int kc = k0 + 8 * c;
+    const int gi = kc / rp;
+    const int64_t gk = kc - gi * rp;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (gr < rb && gi == my && gk < p.r2) {
+      const uint16_t *src = p.A2.p + gr * p.A2.ld + gk;
+      if (a_vec && gk + 8 <= p.r2) {
+        v = *reinterpret_cast<const u32x4_t *>(src);
+      } else {
+        uint32_t w4[4] = {0u, 0u, 0u, 0u};
+        for (int e = 0; e < 8; ++e)
+          if (gk + e < p.r2) w4[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+        v = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
+      }
+    }
+    lds_write_b128(As + lds_off(t, c), v);
   }
 }
 

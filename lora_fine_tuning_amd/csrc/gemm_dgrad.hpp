@@ -454,67 +454,76 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
 
   // ---- rank-r tail: dZ A, plain bf16 steps through LDS -----------------------
   // Where the row tiles ignore the groups (one base for several adapters),
-  // each group with rows in the tile adds its own product over its rows only.
+  // the tile's groups run as one block-diagonal product (big::TileGroups):
+  // reduction row k is row k - i rp of the tile's group i. Each step ends
+  // with a barrier, so the stages are free again.
   if (p.r2 > 0) {
     const bool a_vec = (p.A2.ld % 8) == 0;
     const bool b_vec = (p.B2.ld % 8) == 0;
-    // tile rows [ra, rb) times group gg's B2 (ra == row0 unless SHARED); ends
-    // with a barrier, so the stages are free again
-    auto rank_r = [&](int gg, int64_t ra, int64_t rb) {
-      const uint16_t *B2 = p.B2.p + gg * p.B2.gstride;
-      for (int k0 = 0; k0 < p.r2; k0 += BKS) {
-        if (p.A2part) {
-          big::a2_parts_to_lds<SHARED>(p, As0, [](int i, int c) { return swz(i, c); }, row0, ra, rb, k0, t, col0 == 0);
-        } else {
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const int idx = t + THREADS * c;
-            const int row = idx >> 3, chunk = idx & 7;
-            u32x4_t v = {0u, 0u, 0u, 0u};
-            const int64_t gr = row0 + row;
-            const int64_t gk = k0 + chunk * 8;
-            if ((!SHARED || gr >= ra) && gr < rb && gk < p.r2) {
-              const uint16_t *src = p.A2.p + gr * p.A2.ld + gk;
-              if (a_vec && gk + 8 <= p.r2) {
-                v = *reinterpret_cast<const u32x4_t *>(src);
-              } else {
-                uint32_t w4[4] = {0u, 0u, 0u, 0u};
-                for (int e = 0; e < 8; ++e)
-                  if (gk + e < p.r2) w4[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
-                v = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
-              }
-            }
-            lds_write_b128(As0 + swz(row, chunk), v);
-          }
-        }
+    const int64_t row_hi = min(row0 + BM, row_end);
+    big::TileGroups tg{g, 1, p.r2};
+    int my = 0;
+    if constexpr (SHARED) {
+      tg = big::tile_groups(p, row0, row_hi);
+      my = big::row_group(p, tg, row0 + t, row_hi);
+    }
+    const int rc = tg.n * tg.rp;   // reduction length
+    for (int k0 = 0; k0 < rc; k0 += BKS) {
+      if (p.A2part) {
+        big::a2_parts_to_lds<SHARED>(p, As0, [](int i, int c) { return swz(i, c); }, row0, row_hi, k0, t, col0 == 0,
+                                     tg.rp, my);
+      } else if constexpr (SHARED) {
+        big::a2_rows_to_lds(p, As0, [](int i, int c) { return swz(i, c); }, row0, row_hi, k0, t, tg.rp, my);
+      } else {
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           const int idx = t + THREADS * c;
-          const int row = idx >> 5, cc = (idx & 31) * 8;
+          const int row = idx >> 3, chunk = idx & 7;
           u32x4_t v = {0u, 0u, 0u, 0u};
-          const int64_t gr = k0 + row;
-          const int64_t gc = col0 + cc;
-          if (gr < p.r2 && gc < p.Nc) {
-            const uint16_t *src = B2 + gr * p.B2.ld + gc;
-            if (b_vec && gc + 8 <= p.Nc) {
+          const int64_t gr = row0 + row;
+          const int64_t gk = k0 + chunk * 8;
+          if (gr < row_end && gk < p.r2) {
+            const uint16_t *src = p.A2.p + gr * p.A2.ld + gk;
+            if (a_vec && gk + 8 <= p.r2) {
               v = *reinterpret_cast<const u32x4_t *>(src);
             } else {
               uint32_t w4[4] = {0u, 0u, 0u, 0u};
               for (int e = 0; e < 8; ++e)
-                if (gc + e < p.Nc) w4[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+                if (gk + e < p.r2) w4[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
               v = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
             }
           }
-          lds_write_b128(Bs0 + wt_off(row, cc), v);
+          lds_write_b128(As0 + swz(row, chunk), v);
         }
-        __syncthreads();
-        // sub-step kk covers reduction rows k0 + 16 kk .. +15: only those below r2
-        compute_step(As0, Bs0, min(4, (p.r2 - k0 + 15) / 16));
-        __syncthreads();
       }
-    };
-    if constexpr (SHARED) big::for_tile_groups(p, row0, min(row0 + BM, row_end), rank_r);
-    else rank_r(g, row0, row_end);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int idx = t + THREADS * c;
+        const int row = idx >> 5, cc = (idx & 31) * 8;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        const int kr = k0 + row;
+        int gi = 0;
+        if constexpr (SHARED) gi = kr / tg.rp;
+        const int64_t gr = kr - gi * tg.rp;
+        const int64_t gc = col0 + cc;
+        if (kr < rc && gr < p.r2 && gc < p.Nc) {
+          const uint16_t *src = p.B2.p + (tg.g0 + gi) * p.B2.gstride + gr * p.B2.ld + gc;
+          if (b_vec && gc + 8 <= p.Nc) {
+            v = *reinterpret_cast<const u32x4_t *>(src);
+          } else {
+            uint32_t w4[4] = {0u, 0u, 0u, 0u};
+            for (int e = 0; e < 8; ++e)
+              if (gc + e < p.Nc) w4[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+            v = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
+          }
+        }
+        lds_write_b128(Bs0 + wt_off(row, cc), v);
+      }
+      __syncthreads();
+      // sub-step kk covers reduction rows k0 + 16 kk .. +15: only those below rc
+      compute_step(As0, Bs0, min(4, (rc - k0 + 15) / 16));
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: register e of acc[j][i] holds

@@ -467,76 +467,85 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   // their latency overlaps. (Sub-steps whose reduction slots all lie past r2
   // are skipped: in sub-step kk lane half h holds k0 + 32 h + 8 kk ..)
   // Where the row tiles ignore the groups (one base for several adapters),
-  // each group with rows in the tile adds its own product over its rows only.
+  // the tile's groups run as one block-diagonal product (big::TileGroups):
+  // reduction column k is column k - i rp of the tile's group i.
   if (p.r2 > 0 && split == 0) {
     uint16_t *As = stage(4);
     const bool a_vec = (p.A2.ld % 8) == 0;
     const bool b_vec = (p.B2.ld % 8) == 0;
-    // tile rows [ra, rb) times group gg's B2 (ra == row0 unless SHARED)
-    auto rank_r = [&](int gg, int64_t ra, int64_t rb) {
-      const uint16_t *B2 = p.B2.p + gg * p.B2.gstride;
-      for (int k0 = 0; k0 < p.r2; k0 += BKS) {
-        const int nkk = min(4, (p.r2 - k0 + 7) / 8);
-        WFrag bt;
+    const int64_t row_hi = min(row0 + BM, row_end);
+    big::TileGroups tg{g, 1, p.r2};
+    int my = 0;
+    if constexpr (SHARED) {
+      tg = big::tile_groups(p, row0, row_hi);
+      my = big::row_group(p, tg, row0 + t, row_hi);
+    }
+    const int rc = tg.n * tg.rp;   // reduction length
+    for (int k0 = 0; k0 < rc; k0 += BKS) {
+      const int nkk = min(4, (rc - k0 + 7) / 8);
+      WFrag bt;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int64_t n = col0 + wave * 64 + j * 32 + l32;
+      for (int j = 0; j < 2; ++j) {
+        const int64_t n = col0 + wave * 64 + j * 32 + l32;
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            const int64_t k = k0 + 32 * h + 8 * kk;
-            uint32_t w4[4] = {0u, 0u, 0u, 0u};
-            if (kk < nkk && n < p.Nc && k < p.r2) {
-              const uint16_t *src = B2 + n * p.B2.ld + k;
-              if (b_vec && k + 8 <= p.r2) {
-                const u32x4_t v = *reinterpret_cast<const u32x4_t *>(src);
-                w4[0] = v[0];
-                w4[1] = v[1];
-                w4[2] = v[2];
-                w4[3] = v[3];
-              } else {
-                for (int e = 0; e < 8; ++e)
-                  if (k + e < p.r2) w4[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
-              }
+        for (int kk = 0; kk < 4; ++kk) {
+          const int kc = k0 + 32 * h + 8 * kk;
+          int gi = 0;
+          if constexpr (SHARED) gi = kc / tg.rp;
+          const int64_t k = kc - gi * tg.rp;
+          uint32_t w4[4] = {0u, 0u, 0u, 0u};
+          if (kk < nkk && n < p.Nc && kc < rc && k < p.r2) {
+            const uint16_t *src = p.B2.p + (tg.g0 + gi) * p.B2.gstride + n * p.B2.ld + k;
+            if (b_vec && k + 8 <= p.r2) {
+              const u32x4_t v = *reinterpret_cast<const u32x4_t *>(src);
+              w4[0] = v[0];
+              w4[1] = v[1];
+              w4[2] = v[2];
+              w4[3] = v[3];
+            } else {
+              for (int e = 0; e < 8; ++e)
+                if (k + e < p.r2) w4[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
             }
-            bt.w[j][kk] = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
           }
+          bt.w[j][kk] = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
         }
-        if (p.A2part) {
-          big::a2_parts_to_lds<SHARED>(p, As, [](int i, int c) { return swz(i, c); }, row0, ra, rb, k0, t, col0 == 0);
-        } else {
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const int idx = t + THREADS * c;
-            const int row = idx >> 3, chunk = idx & 7;
-            u32x4_t v = {0u, 0u, 0u, 0u};
-            const int64_t gr = row0 + row;
-            const int64_t gk = k0 + chunk * 8;
-            if ((!SHARED || gr >= ra) && gr < rb && gk < p.r2) {
-              const uint16_t *src = p.A2.p + gr * p.A2.ld + gk;
-              if (a_vec && gk + 8 <= p.r2) {
-                v = *reinterpret_cast<const u32x4_t *>(src);
-              } else {
-                uint32_t w4[4] = {0u, 0u, 0u, 0u};
-                for (int e = 0; e < 8; ++e)
-                  if (gk + e < p.r2) w4[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
-                v = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
-              }
-            }
-            lds_write_b128(As + swz(row, chunk), v);
-          }
-        }
-        __syncthreads();
-        u32x4_t xt[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) xt[i] = lds_read_b128(As + swz(i * 32 + l32, h * 4));
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          if (kk < nkk) sub_step(bt, kk, xt, As, h * 4 + kk + 1, kk < 3, [] {});
-        if (k0 + BKS < p.r2) __syncthreads();   // before the next chunk restages
       }
-    };
-    if constexpr (SHARED) big::for_tile_groups(p, row0, min(row0 + BM, row_end), rank_r);
-    else rank_r(g, row0, row_end);
+      if (p.A2part) {
+        big::a2_parts_to_lds<SHARED>(p, As, [](int i, int c) { return swz(i, c); }, row0, row_hi, k0, t, col0 == 0,
+                                     tg.rp, my);
+      } else if constexpr (SHARED) {
+        big::a2_rows_to_lds(p, As, [](int i, int c) { return swz(i, c); }, row0, row_hi, k0, t, tg.rp, my);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const int idx = t + THREADS * c;
+          const int row = idx >> 3, chunk = idx & 7;
+          u32x4_t v = {0u, 0u, 0u, 0u};
+          const int64_t gr = row0 + row;
+          const int64_t gk = k0 + chunk * 8;
+          if (gr < row_end && gk < p.r2) {
+            const uint16_t *src = p.A2.p + gr * p.A2.ld + gk;
+            if (a_vec && gk + 8 <= p.r2) {
+              v = *reinterpret_cast<const u32x4_t *>(src);
+            } else {
+              uint32_t w4[4] = {0u, 0u, 0u, 0u};
+              for (int e = 0; e < 8; ++e)
+                if (gk + e < p.r2) w4[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+              v = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
+            }
+          }
+          lds_write_b128(As + swz(row, chunk), v);
+        }
+      }
+      __syncthreads();
+      u32x4_t xt[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xt[i] = lds_read_b128(As + swz(i * 32 + l32, h * 4));
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        if (kk < nkk) sub_step(bt, kk, xt, As, h * 4 + kk + 1, kk < 3, [] {});
+      if (k0 + BKS < rc) __syncthreads();   // before the next chunk restages
+    }
   }
 
 #pragma unroll

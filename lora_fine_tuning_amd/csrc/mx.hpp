@@ -286,7 +286,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd_mx(Params p) {
         }
       }
       if (p.A2part) {
-        big::a2_parts_to_lds<false>(p, Zs, [](int i, int c) { return tile64_swz(i, c); }, row0, row0, p.M, k0, t,
+        big::a2_parts_to_lds<false>(p, Zs, [](int i, int c) { return tile64_swz(i, c); }, row0, p.M, k0, t,
                                     col0 == 0);
       } else {
 #pragma unroll

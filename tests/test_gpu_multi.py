@@ -77,6 +77,30 @@ def test_adapters_over_one_base(fmt, cut, tiles):
     assert rel(got["Y_base"], Xf @ Wd.T) <= TOL
 
 
+@pytest.mark.parametrize("r", [12, 40, 72])
+def test_ranks_off_the_8_grid(r, tiles):
+    """Ranks that are not multiples of 8 (one adapter's rank columns padded to
+    the next multiple of 8 where a tile's adapters run as one product) and a
+    rank above 64."""
+    offs = OFFSETS["twelve"]
+    lay, t, W, got = _case(synth.NF4, 300, 512, 384, r, offs, index=53)
+    print_case("multi r", r, offs)
+    G = len(offs) - 1
+    Wd = dequant_rows(W, np.arange(lay.N), synth.NF4)
+    Ws = [Wd] * G
+    As = [f64(a) for a in t["A"]]
+    Bs = [f64(b) for b in t["B"]]
+    fo = lora.grouped_forward(f64(t["X"]), Ws, As, Bs, lay.s, offs)
+    bo = lora.grouped_backward(f64(t["X"]), Ws, As, Bs, lay.s, f64(t["dY"]), offs)
+    for k in ("Y", "Z"):
+        assert rel(got[k], fo[k]) <= TOL, k
+    assert rel(got["dX"], bo["dX"]) <= TOL
+    for e in range(G):
+        if offs[e + 1] > offs[e]:
+            assert rel(got["dA"][e], bo["dA"][e]) <= TOL, e
+            assert rel(got["dB"][e], bo["dB"][e]) <= TOL, e
+
+
 def test_one_adapter_is_the_plain_layer():
     """adapters == 1 takes the plain layer's path: results are bitwise equal."""
     lay = synth.small_layer(256, 1024, 512, 16, index=52)

@@ -1,9 +1,10 @@
 """GPU parity at the full sizes of the benchmark workloads.
 
 Every layer of the Llama-3-8B-shaped set (NF4), the Llama-70B-shaped MXFP4 layers,
-the 64-expert MoE layers (grouped, MXFP4) and the long-context NF4 layer with
-double-quantized scales runs through lora4_forward / lora4_backward exactly as
-bench.py calls them. The oracle cannot redo whole layers, so it checks:
+the 64-expert MoE layers (grouped, MXFP4), the long-context NF4 layer with
+double-quantized scales and the 16-adapter layers over one base run through
+the library's entry points exactly as bench.py calls them. The oracle cannot
+redo whole layers, so it checks:
 
 * packing: sampled rows of the codes and scales, bit for bit (the whole matrix
   for double quantization, whose scale groups span rows);
@@ -90,8 +91,13 @@ def _check_layer(lay, rng, n_rows=64, n_cols=64, n_kblk=2):
     base = _pack_gpu(t["W"], lay.fmt)
     X, A, B, dY = (to_dev(t[k]) for k in ("X", "A", "B", "dY"))
     offs = None if E == 1 else torch.tensor(lay.offsets, dtype=torch.int64, device=DEV)
-    fw = L.forward(base, X, A, B, lay.s, group_offsets=offs)
-    bw = L.backward(base, X, dY, A, B, lay.s, Z=fw["Z"], group_offsets=offs)
+    shared = lay.shared_base
+    if shared:
+        fw = L.forward_multi(base, X, A, B, lay.s, adapter_offsets=offs)
+        bw = L.backward_multi(base, X, dY, A, B, lay.s, Z=fw["Z"], adapter_offsets=offs)
+    else:
+        fw = L.forward(base, X, A, B, lay.s, group_offsets=offs)
+        bw = L.backward(base, X, dY, A, B, lay.s, Z=fw["Z"], group_offsets=offs)
     torch.cuda.synchronize()
     Y, Z = to_host(fw["Y"]), to_host(fw["Z"])
     dX, dA, dB = to_host(bw["dX"]), to_host(bw["dA"]), to_host(bw["dB"])
@@ -105,7 +111,8 @@ def _check_layer(lay, rng, n_rows=64, n_cols=64, n_kblk=2):
     s = lay.s
     for e in experts:
         a, b = (0, lay.M) if E == 1 else (lay.offsets[e], lay.offsets[e + 1])
-        We = t["W"] if E == 1 else t["W"][e]
+        We = t["W"] if E == 1 or shared else t["W"][e]
+        q = 0 if shared else e                                       # packing of We
         Ae = f64(t["A"] if E == 1 else t["A"][e])
         Be = f64(t["B"] if E == 1 else t["B"][e])
         Xe, dYe = t["X"][a:b], t["dY"][a:b]
@@ -116,15 +123,15 @@ def _check_layer(lay, rng, n_rows=64, n_cols=64, n_kblk=2):
         if lay.fmt == synth.NF4_DQ:
             c, sc = nf4.quantize(We)
             c8, c2 = nf4.double_quantize(sc)
-            assert np.array_equal(codes[e], tile_codes(c, lay.N, lay.K))
-            assert np.array_equal(scales[e], tile_scales(c8, lay.N, lay.K))
-            assert np.array_equal(scales2[e].view(np.uint32), c2.view(np.uint32))
+            assert np.array_equal(codes[q], tile_codes(c, lay.N, lay.K))
+            assert np.array_equal(scales[q], tile_scales(c8, lay.N, lay.K))
+            assert np.array_equal(scales2[q].view(np.uint32), c2.view(np.uint32))
             full_dq = nf4.dequantize_dq(c, c8, c2)
         else:
             pc, ps = _oracle_pack_rows(We, nrows, lay.fmt)
-            assert np.array_equal(untile_rows(codes[e], lay.N, lay.K, nrows, 32), pc)
+            assert np.array_equal(untile_rows(codes[q], lay.N, lay.K, nrows, 32), pc)
             per = {synth.MXFP4: 2, synth.NVFP4: 4}.get(lay.fmt, 1)
-            got_s = untile_rows(scales[e], lay.N, lay.K, nrows, per)
+            got_s = untile_rows(scales[q], lay.N, lay.K, nrows, per)
             if lay.fmt == synth.NF4:
                 assert np.array_equal(got_s.view(np.uint32), ps.view(np.uint32))
             else:
@@ -169,6 +176,15 @@ def _layers(w):
 def test_workload_layer(w, i):
     lay = synth.layers(w)[i]
     _check_layer(lay, np.random.default_rng(100 * w + i))
+
+
+@pytest.mark.parametrize("i", [0, 1, 4, 6])
+def test_workload_layer_multilora(i):
+    """Layers of the 8B set with 16 rank-16 adapters over the one NF4 base,
+    4096 tokens cut into groups of 1 to ~700 rows, as bench.py --workload
+    multilora runs them (several adapters inside most 256-row tiles)."""
+    lay = synth.layers(6)[i]
+    _check_layer(lay, np.random.default_rng(600 + i))
 
 
 @pytest.mark.parametrize("i", [0, 4, 6])
