@@ -50,7 +50,7 @@ OFFSETS = {
 }
 
 
-@pytest.mark.parametrize("fmt", [synth.NF4, synth.MXFP4, synth.NF4_DQ])
+@pytest.mark.parametrize("fmt", [synth.NF4, synth.MXFP4, synth.NF4_DQ, synth.NVFP4])
 @pytest.mark.parametrize("cut", sorted(OFFSETS))
 def test_adapters_over_one_base(fmt, cut, tiles):
     offs = OFFSETS[cut]
