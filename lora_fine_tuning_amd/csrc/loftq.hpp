@@ -12,70 +12,118 @@
 namespace lora4 {
 namespace loftq {
 
-constexpr int MAT_ROWS = 32;    // output rows per workgroup of k_mat
-constexpr int MAT_CHUNK = 32;   // reduction chunk staged in LDS
-constexpr int MAX_C = 144;      // widest M (r + 16 for r <= 128)
+constexpr int MAT_ROWS = 256;   // output rows per workgroup of k_mat
+constexpr int MAT_COLS = 32;    // output columns per workgroup (blockIdx.z: column block)
+constexpr int MAT_CHUNK = 16;   // reduction rows per LDS stage
+
+// Up to four consecutive floats at p (n valid, zero past them; one 16-byte
+// load where vec and all four are valid).
+__device__ __forceinline__ f32x4_t load4f(const float *p, int64_t n, bool vec) {
+  f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+  if (vec && n >= 4) return *reinterpret_cast<const f32x4_t *>(p);
+  for (int e = 0; e < 4; ++e)
+    if (e < n) v[e] = p[e];
+  return v;
+}
 
 // out[o][j] = sum_t X(o, t) M[t][j] for o < rows, j < c, t < inner, with
 // X(o, t) = X[o][t] (TRANS = false, X is [rows][ldx]) or X[t][o] (TRANS =
-// true, X is [inner][ldx]); M is [inner][c], out [rows][c], all fp32. One
-// workgroup per 32 output rows and reduction range (blockIdx.y: t in
-// [y per_split, (y + 1) per_split), written to out + y rows c); thread t
-// owns row t % 32 and columns t / 32 + 8 u; the sum over t runs in order
-// (deterministic).
+// true, X is [inner][ldx]); M is [inner][c], out [rows][c], all fp32. A
+// workgroup owns 256 output rows x 32 columns (blockIdx.x, blockIdx.z) over
+// one reduction range (blockIdx.y: t in [y per_split, (y + 1) per_split),
+// written to out + y rows c); thread i owns rows 4 (i / 4) .. +3 and columns
+// 8 (i % 4) .. +7. The range streams through two LDS stages of 16 reduction
+// rows (the next stage's loads in flight during this one's FMAs), and every
+// output sums its range in order (deterministic).
 template <bool TRANS>
 __global__ __launch_bounds__(256) void k_mat(const float *X, int64_t ldx, int64_t rows, int64_t inner,
                                              const float *M, int c, float *out, int64_t per_split) {
-  __shared__ float xs[MAT_CHUNK][MAT_ROWS + 1];
-  __shared__ float ms[MAT_CHUNK][MAX_C];
+  __shared__ __attribute__((aligned(16))) float xs[2][MAT_CHUNK][MAT_ROWS + 4];
+  __shared__ __attribute__((aligned(16))) float ms[2][MAT_CHUNK][MAT_COLS];
   const int t = threadIdx.x;
   const int64_t o0 = (int64_t)blockIdx.x * MAT_ROWS;
-  const int ro = t & 31, cg = t >> 5;
-  constexpr int NU = (MAX_C + 7) / 8;
-  float acc[NU];
-#pragma unroll
-  for (int u = 0; u < NU; ++u) acc[u] = 0.0f;
+  const int j0 = blockIdx.z * MAT_COLS;
   const int64_t t_lo = (int64_t)blockIdx.y * per_split;
   const int64_t t_hi = t_lo + per_split < inner ? t_lo + per_split : inner;
   out += (int64_t)blockIdx.y * rows * c;
-  for (int64_t t0 = t_lo; t0 < t_hi; t0 += MAT_CHUNK) {
-    // stage X(o0 .. +31, t0 .. +31) as xs[t][o] and M(t0 .. +31, 0 .. c)
-    for (int e = t; e < MAT_CHUNK * MAT_ROWS; e += 256) {
-      int tt, oo;
-      if (TRANS) {   // rows of X are reduction rows: read along o
-        tt = e / MAT_ROWS;
-        oo = e % MAT_ROWS;
-      } else {       // rows of X are output rows: read along t
-        oo = e / MAT_CHUNK;
-        tt = e % MAT_CHUNK;
-      }
-      const int64_t gt = t0 + tt, go = o0 + oo;
-      float v = 0.0f;
-      if (gt < t_hi && go < rows) v = TRANS ? X[gt * ldx + go] : X[go * ldx + gt];
-      xs[tt][oo] = v;
-    }
-    for (int e = t; e < MAT_CHUNK * c; e += 256) {
-      const int tt = e / c, j = e % c;
-      const int64_t gt = t0 + tt;
-      ms[tt][j] = gt < t_hi ? M[gt * c + j] : 0.0f;
-    }
-    __syncthreads();
-    for (int tt = 0; tt < MAT_CHUNK; ++tt) {
-      const float x = xs[tt][ro];
+  const bool vec = (ldx % 4) == 0;
+  const int rg = t >> 2, cq = t & 3;
+
+  float acc[4][8];
 #pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        const int j = cg + 8 * u;
-        if (j < c) acc[u] = fmaf(x, ms[tt][j], acc[u]);
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 8; ++b) acc[a][b] = 0.f;
+
+  // one stage: X as xs[t - k0][o - o0], M as ms[t - k0][j - j0] (zero outside)
+  f32x4_t xv[4];
+  float mv[2];
+  auto load = [&](int64_t k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (TRANS) {   // X rows are reduction rows: 256 consecutive outputs per row
+        const int64_t gk = k0 + (t >> 6) + 4 * i, go = o0 + 4 * (t & 63);
+        xv[i] = gk < t_hi && go < rows ? load4f(X + gk * ldx + go, rows - go, vec) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      } else {       // X rows are output rows: 16 consecutive reduction elements per row
+        const int64_t go = o0 + t, gk = k0 + 4 * i;
+        xv[i] = go < rows && gk < t_hi ? load4f(X + go * ldx + gk, t_hi - gk, vec) : f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
     }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = 2 * t + u, kk = e >> 5, jj = e & 31;
+      const int64_t gk = k0 + kk;
+      mv[u] = gk < t_hi && j0 + jj < c ? M[gk * c + j0 + jj] : 0.f;
+    }
+  };
+  auto store = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (TRANS) {
+        *reinterpret_cast<f32x4_t *>(&xs[b][(t >> 6) + 4 * i][4 * (t & 63)]) = xv[i];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xs[b][4 * i + e][t] = xv[i][e];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) ms[b][(2 * t + u) >> 5][(2 * t + u) & 31] = mv[u];
+  };
+
+  const int64_t nch = t_hi > t_lo ? (t_hi - t_lo + MAT_CHUNK - 1) / MAT_CHUNK : 0;
+  if (nch > 0) {
+    load(t_lo);
+    store(0);
+  }
+  __syncthreads();
+  for (int64_t ci = 0; ci < nch; ++ci) {
+    const int b = (int)(ci & 1);
+    if (ci + 1 < nch) load(t_lo + (ci + 1) * MAT_CHUNK);
+#pragma unroll 4
+    for (int kk = 0; kk < MAT_CHUNK; ++kk) {
+      const f32x4_t x = *reinterpret_cast<const f32x4_t *>(&xs[b][kk][4 * rg]);
+      const f32x4_t m0 = *reinterpret_cast<const f32x4_t *>(&ms[b][kk][8 * cq]);
+      const f32x4_t m1 = *reinterpret_cast<const f32x4_t *>(&ms[b][kk][8 * cq + 4]);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[a][e] = fmaf(x[a], m0[e], acc[a][e]);
+          acc[a][4 + e] = fmaf(x[a], m1[e], acc[a][4 + e]);
+        }
+      }
+    }
+    if (ci + 1 < nch) store(b ^ 1);   // the stage read one iteration ago
     __syncthreads();
   }
-  const int64_t o = o0 + ro;
-  if (o < rows) {
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int j = cg + 8 * u;
-      if (j < c) out[o * c + j] = acc[u];
+  for (int a = 0; a < 4; ++a) {
+    const int64_t o = o0 + 4 * rg + a;
+    if (o >= rows) continue;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = j0 + 8 * cq + e;
+      if (j < c) out[o * c + j] = acc[a][e];
     }
   }
 }
@@ -90,15 +138,41 @@ __global__ void k_sum_parts(const float *part, int S, int64_t n, float *out) {
 }
 
 // T[n][k] = bf16(W[n][k] - sum_j B[n][j] AT[k][j]) (B [N][r], AT [K][r] fp32;
-// r = 0 copies W).
+// r = 0 copies W), the sum over j in order. One thread per 8 consecutive
+// elements of a row (K % 8 == 0): its B row is shared by the 8, and where r %
+// 4 == 0 both operands come in 16-byte loads.
 __global__ void k_shift(const uint16_t *W, const float *B, const float *AT, int64_t N, int64_t K, int r,
                         uint16_t *T) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (i >= N * K) return;
   const int64_t n = i / K, k = i - n * K;
-  float v = bf16_bits_to_f32(W[i]);
-  for (int j = 0; j < r; ++j) v = fmaf(-B[n * r + j], AT[k * r + j], v);
-  T[i] = to_bf16(v);
+  const u32x4_t w = *reinterpret_cast<const u32x4_t *>(W + i);
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = bf16_bits_to_f32((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+  const float *b = B + n * r;
+  const float *at = AT + k * r;
+  if ((r % 4) == 0) {
+    for (int j = 0; j < r; j += 4) {
+      const f32x4_t b4 = *reinterpret_cast<const f32x4_t *>(b + j);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const f32x4_t a4 = *reinterpret_cast<const f32x4_t *>(at + e * r + j);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[e] = fmaf(-b4[q], a4[q], v[e]);
+      }
+    }
+  } else {
+    for (int j = 0; j < r; ++j) {
+      const float bj = b[j];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = fmaf(-bj, at[e * r + j], v[e]);
+    }
+  }
+  uint32_t o[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) o[q] = (uint32_t)to_bf16(v[2 * q]) | ((uint32_t)to_bf16(v[2 * q + 1]) << 16);
+  *reinterpret_cast<u32x4_t *>(T + i) = u32x4_t{o[0], o[1], o[2], o[3]};
 }
 
 // R[n][k] = W[n][k] - deq(Q)[n][k] in fp32, one thread per 32 elements of a row.

@@ -830,11 +830,13 @@ lora4_status check_mx(const lora4_W *W, int64_t M, int32_t r, float s) {
 constexpr int LOFTQ_OVERSAMPLE = 16;   // columns beyond r in the subspace
 constexpr int LOFTQ_POWER = 8;         // power iterations (R R^T applied 8 times)
 
-constexpr int LOFTQ_MAX_SPLIT = 64;   // reduction ranges of a product with few output rows
+constexpr int LOFTQ_MAX_SPLIT = 64;             // reduction ranges of one product
+constexpr int64_t LOFTQ_TARGET_WG = 1024;        // workgroups wanted per product
+constexpr size_t LOFTQ_PART_BYTES = 64u << 20;   // fp32 partials of the split products
 
 struct LoftqPlan {
   int c;
-  size_t off_T, off_R, off_Y, off_Y2, off_Z, off_Z2, off_G, off_M, off_B, off_AT, off_P, bytes;
+  size_t off_T, off_R, off_Y, off_Y2, off_Z, off_Z2, off_G, off_M, off_B, off_AT, off_P, part_bytes, bytes;
 };
 
 LoftqPlan make_loftq_plan(int64_t N, int64_t K, int r) {
@@ -856,22 +858,26 @@ LoftqPlan make_loftq_plan(int64_t N, int64_t K, int r) {
   p.off_M = take((size_t)p.c * p.c * 4);
   p.off_B = take((size_t)N * r * 4);
   p.off_AT = take((size_t)K * r * 4);
-  p.off_P = take((size_t)LOFTQ_MAX_SPLIT * p.c * p.c * 4);   // partials of the c x c products
+  p.off_P = take(std::max(LOFTQ_PART_BYTES, (size_t)LOFTQ_MAX_SPLIT * p.c * p.c * 4));   // split partials
+  p.part_bytes = std::max(LOFTQ_PART_BYTES, (size_t)LOFTQ_MAX_SPLIT * p.c * p.c * 4);
   p.bytes = off;
   return p;
 }
 
-// out = X M or X^T M (k_mat); a product with few output rows (the c x c
-// Gram matrices) splits its reduction over up to LOFTQ_MAX_SPLIT workgroups
-// into fp32 partials (parts, rows * c each) summed in order afterwards.
+// out = X M or X^T M (k_mat). The reduction is split over enough ranges to
+// give the grid ~LOFTQ_TARGET_WG workgroups (at most LOFTQ_MAX_SPLIT, at
+// least 256 reduction rows each, partials within `part_bytes` of `parts`),
+// the fp32 partials summed in order afterwards.
 lora4_status run_mat(bool trans, const float *X, int64_t ldx, int64_t rows, int64_t inner, const float *M, int c,
-                     float *out, hipStream_t st, float *parts = nullptr) {
-  const int64_t tiles = ceil_div(rows, loftq::MAT_ROWS);
-  int64_t S = 1;
-  if (parts && tiles < 64) S = std::min<int64_t>(LOFTQ_MAX_SPLIT, std::max<int64_t>(1, inner / 512));
+                     float *out, float *parts, size_t part_bytes, hipStream_t st) {
+  const int64_t tiles = ceil_div(rows, loftq::MAT_ROWS), cblocks = ceil_div(c, loftq::MAT_COLS);
+  int64_t S = std::min<int64_t>({ceil_div(LOFTQ_TARGET_WG, tiles * cblocks), LOFTQ_MAX_SPLIT,
+                                 std::max<int64_t>(1, inner / 256),
+                                 std::max<int64_t>(1, (int64_t)(part_bytes / ((size_t)rows * c * 4)))});
+  S = std::max<int64_t>(1, S);
   const int64_t per = ceil_div(inner, S * loftq::MAT_CHUNK) * loftq::MAT_CHUNK;
   S = ceil_div(inner, per);
-  const dim3 grid((unsigned)tiles, (unsigned)S);
+  const dim3 grid((unsigned)tiles, (unsigned)S, (unsigned)cblocks);
   float *dst = S > 1 ? parts : out;
   if (trans)
     TRY(launch_args("loftq_mat_tn", loftq::k_mat<true>, grid, dim3(256), st, X, ldx, rows, inner, M, c, dst, per));
@@ -884,9 +890,9 @@ lora4_status run_mat(bool trans, const float *X, int64_t ldx, int64_t rows, int6
 }
 
 // c x c Gram matrix of the columns of Y [rows][c] to the host (double).
-lora4_status gram_to_host(const float *Y, int64_t rows, int c, float *G_dev, float *parts, std::vector<double> &G,
-                          hipStream_t st) {
-  TRY(run_mat(true, Y, c, c, rows, Y, c, G_dev, st, parts));
+lora4_status gram_to_host(const float *Y, int64_t rows, int c, float *G_dev, float *parts, size_t part_bytes,
+                          std::vector<double> &G, hipStream_t st) {
+  TRY(run_mat(true, Y, c, c, rows, Y, c, G_dev, parts, part_bytes, st));
   std::vector<float> g((size_t)c * c);
   if (hipMemcpyAsync(g.data(), G_dev, g.size() * 4, hipMemcpyDeviceToHost, st) != hipSuccess) return LORA4_ERR_HIP;
   if (hipStreamSynchronize(st) != hipSuccess) return LORA4_ERR_HIP;
@@ -905,11 +911,11 @@ lora4_status upload(const std::vector<double> &M, float *dst, hipStream_t st, st
 // with Y^T Y = L L^T. A Gram matrix that is not positive definite (Y of lower
 // rank) gets a small diagonal shift.
 lora4_status orthonormalize(float *Y, float *tmp, int64_t rows, int c, float *G_dev, float *M_dev, float *parts,
-                            hipStream_t st) {
+                            size_t part_bytes, hipStream_t st) {
   std::vector<double> G, M((size_t)c * c), L((size_t)c * c);
   std::vector<float> stage;
   for (int pass = 0; pass < 2; ++pass) {
-    TRY(gram_to_host(Y, rows, c, G_dev, parts, G, st));
+    TRY(gram_to_host(Y, rows, c, G_dev, parts, part_bytes, G, st));
     double tr = 0;
     for (int i = 0; i < c; ++i) tr += G[(size_t)i * c + i];
     const double eps = 1e-12 * (tr > 0 ? tr : 1.0);
@@ -934,7 +940,7 @@ lora4_status orthonormalize(float *Y, float *tmp, int64_t rows, int c, float *G_
         M[(size_t)i * c + col] = v / L[(size_t)i * c + i];
       }
     TRY(upload(M, M_dev, st, stage));
-    TRY(run_mat(false, Y, c, rows, c, M_dev, c, tmp, st));
+    TRY(run_mat(false, Y, c, rows, c, M_dev, c, tmp, parts, part_bytes, st));
     if (hipMemcpyAsync(Y, tmp, (size_t)rows * c * 4, hipMemcpyDeviceToDevice, st) != hipSuccess) return LORA4_ERR_HIP;
   }
   return LORA4_OK;
@@ -1395,6 +1401,7 @@ lora4_status lora4_loftq_init(const uint16_t *W, int64_t N, int64_t K, int32_t r
   float *Md = ws_at<float>(workspace, lp.off_M), *Bf = ws_at<float>(workspace, lp.off_B);
   float *ATf = ws_at<float>(workspace, lp.off_AT);
   float *P = ws_at<float>(workspace, lp.off_P);
+  const size_t PB = lp.part_bytes;
   const lora4_W Wq{double_quant ? LORA4_NF4_DQ : LORA4_NF4, 64, N, K, 1, codes, scales, scales2};
   const PackedW Qp = packed_of(Base{&Wq, 1, false});
   const int64_t nk = N * K;
@@ -1402,7 +1409,7 @@ lora4_status lora4_loftq_init(const uint16_t *W, int64_t N, int64_t K, int32_t r
   std::vector<float> stage;
   for (int it = 0; it < iters; ++it) {
     // Q_t = NF4(bf16(W - B_{t-1} A_{t-1})), R_t = W - Q_t
-    TRY(launch_args("loftq_shift", loftq::k_shift, dim3((unsigned)ceil_div(nk, 256)), dim3(256), st, W,
+    TRY(launch_args("loftq_shift", loftq::k_shift, dim3((unsigned)ceil_div(nk / 8, 256)), dim3(256), st, W,
                     (const float *)Bf, (const float *)ATf, N, K, it == 0 ? 0 : (int)r, T));
     TRY(quant_pack_nf4(T, N, K, double_quant, codes, scales, scales2, stream));
     const dim3 rg((unsigned)ceil_div(N * (K / 32), 256));
@@ -1413,18 +1420,18 @@ lora4_status lora4_loftq_init(const uint16_t *W, int64_t N, int64_t K, int32_t r
     // top-r subspace of R: Y = orth(R Omega), then (R R^T) applied LOFTQ_POWER times
     TRY(launch_args("loftq_start", loftq::k_rademacher, dim3((unsigned)ceil_div(K * c, 256)), dim3(256), st, Z2,
                     K * c, (uint64_t)0x5EED0000u + (uint64_t)it));
-    TRY(run_mat(false, R, K, N, K, Z2, c, Y, st));
-    TRY(orthonormalize(Y, Y2, N, c, G, Md, P, st));
+    TRY(run_mat(false, R, K, N, K, Z2, c, Y, P, PB, st));
+    TRY(orthonormalize(Y, Y2, N, c, G, Md, P, PB, st));
     for (int q = 0; q < LOFTQ_POWER; ++q) {
-      TRY(run_mat(true, R, K, K, N, Y, c, Z, st));
-      TRY(orthonormalize(Z, Z2, K, c, G, Md, P, st));
-      TRY(run_mat(false, R, K, N, K, Z, c, Y, st));
-      TRY(orthonormalize(Y, Y2, N, c, G, Md, P, st));
+      TRY(run_mat(true, R, K, K, N, Y, c, Z, P, PB, st));
+      TRY(orthonormalize(Z, Z2, K, c, G, Md, P, PB, st));
+      TRY(run_mat(false, R, K, N, K, Z, c, Y, P, PB, st));
+      TRY(orthonormalize(Y, Y2, N, c, G, Md, P, PB, st));
     }
     // R ~ Y Z^T with Z = R^T Y; Z^T = U S V^T from the eigenvectors of Z^T Z:
     // B = Y U_r S_r^(1/2), A^T = Z U_r S_r^(-1/2)
-    TRY(run_mat(true, R, K, K, N, Y, c, Z, st));
-    TRY(gram_to_host(Z, K, c, G, P, Gh, st));
+    TRY(run_mat(true, R, K, K, N, Y, c, Z, P, PB, st));
+    TRY(gram_to_host(Z, K, c, G, P, PB, Gh, st));
     jacobi_eigen(Gh, c, vals, V);
     const double smax = vals[0] > 0 ? std::sqrt(vals[0]) : 0.0;
     Mh.assign((size_t)c * r, 0.0);
@@ -1434,14 +1441,14 @@ lora4_status lora4_loftq_init(const uint16_t *W, int64_t N, int64_t K, int32_t r
         Mh[(size_t)i * r + j] = V[(size_t)i * c + j] * std::sqrt(sg);
       }
     TRY(upload(Mh, Md, st, stage));
-    TRY(run_mat(false, Y, c, N, c, Md, r, Bf, st));
+    TRY(run_mat(false, Y, c, N, c, Md, r, Bf, P, PB, st));
     for (int i = 0; i < c; ++i)
       for (int j = 0; j < r; ++j) {
         const double sg = vals[j] > 0 ? std::sqrt(vals[j]) : 0.0;
         Mh[(size_t)i * r + j] = sg > 1e-30 * (smax > 0 ? smax : 1.0) ? V[(size_t)i * c + j] / std::sqrt(sg) : 0.0;
       }
     TRY(upload(Mh, Md, st, stage));
-    TRY(run_mat(false, Z, c, K, c, Md, r, ATf, st));
+    TRY(run_mat(false, Z, c, K, c, Md, r, ATf, P, PB, st));
   }
   TRY(launch_args("loftq_out", loftq::k_to_bf16, dim3((unsigned)ceil_div(N * r, 256)), dim3(256), st,
                   (const float *)Bf, N * r, 1.0f / s, B));
