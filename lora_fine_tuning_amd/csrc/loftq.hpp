@@ -128,6 +128,57 @@ __global__ __launch_bounds__(256) void k_mat(const float *X, int64_t ldx, int64_
   }
 }
 
+constexpr int CHOL_MAX_C = 64;   // widest c whose factor fits the LDS in fp64 (2 c^2 doubles)
+
+// The CholeskyQR factor on the device: M = L^-T with G + eps I = L L^T, G the
+// c x c Gram matrix (fp32, symmetric), eps = 1e-12 trace(G) (1e-12 if the
+// trace is not positive), a pivot not above eps taken as sqrt(eps); in
+// double, M written as fp32 [c][c]. One workgroup, c <= CHOL_MAX_C. The
+// factor is right-looking (after column j, every entry below and right of it
+// subtracts its column-j product) and L^T M = I is solved from the last row
+// up (after row i of M, every row above subtracts its row-i product), so each
+// entry takes the same operations in the same order as the host's sums.
+__global__ __launch_bounds__(256) void k_chol_inv(const float *G, int c, float *M) {
+  __shared__ double A[CHOL_MAX_C * CHOL_MAX_C];   // G + eps I, its lower part becoming L
+  __shared__ double R[CHOL_MAX_C * CHOL_MAX_C];   // I, becoming M
+  const int t = threadIdx.x;
+  double tr = 0.0;   // every thread sums the diagonal in the same order
+  for (int i = 0; i < c; ++i) tr += (double)G[i * c + i];
+  const double eps = 1e-12 * (tr > 0 ? tr : 1.0);
+  for (int e = t; e < c * c; e += 256) {
+    const int i = e / c, k = e - i * c;
+    A[e] = i == k ? (double)G[e] + eps : (double)G[e];
+    R[e] = i == k ? 1.0 : 0.0;
+  }
+  __syncthreads();
+  for (int j = 0; j < c; ++j) {
+    if (t == 0) {
+      const double d = A[j * c + j];
+      A[j * c + j] = d > eps ? sqrt(d) : sqrt(eps);
+    }
+    __syncthreads();
+    const double d = A[j * c + j];
+    for (int i = j + 1 + t; i < c; i += 256) A[i * c + j] = A[i * c + j] / d;
+    __syncthreads();
+    const int w = c - j - 1;   // trailing block rows/columns j + 1 .. c - 1
+    for (int e = t; e < w * w; e += 256) {
+      const int i = j + 1 + e / w, k = j + 1 + e % w;
+      if (k <= i) A[i * c + k] -= A[i * c + j] * A[k * c + j];
+    }
+    __syncthreads();
+  }
+  for (int i = c - 1; i >= 0; --i) {
+    for (int col = t; col < c; col += 256) R[i * c + col] = R[i * c + col] / A[i * c + i];
+    __syncthreads();
+    for (int e = t; e < i * c; e += 256) {   // rows 0 .. i - 1
+      const int ii = e / c, col = e - ii * c;
+      R[ii * c + col] -= A[i * c + ii] * R[i * c + col];
+    }
+    __syncthreads();
+  }
+  for (int e = t; e < c * c; e += 256) M[e] = (float)R[e];
+}
+
 // out[i] = sum over the S partials part[s][i], in order.
 __global__ void k_sum_parts(const float *part, int S, int64_t n, float *out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;

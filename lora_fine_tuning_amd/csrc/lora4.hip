@@ -909,9 +909,20 @@ lora4_status upload(const std::vector<double> &M, float *dst, hipStream_t st, st
 
 // Orthonormalize the columns of Y [rows][c] (CholeskyQR, twice): Y <- Y L^-T
 // with Y^T Y = L L^T. A Gram matrix that is not positive definite (Y of lower
-// rank) gets a small diagonal shift.
+// rank) gets a small diagonal shift. The factor is computed on the device
+// (k_chol_inv) where c <= CHOL_MAX_C, else on the host, by the same steps.
 lora4_status orthonormalize(float *Y, float *tmp, int64_t rows, int c, float *G_dev, float *M_dev, float *parts,
                             size_t part_bytes, hipStream_t st) {
+  if (c <= loftq::CHOL_MAX_C) {   // the factor on the device: no host round trip
+    for (int pass = 0; pass < 2; ++pass) {
+      TRY(run_mat(true, Y, c, c, rows, Y, c, G_dev, parts, part_bytes, st));
+      TRY(launch_args("loftq_chol", loftq::k_chol_inv, dim3(1), dim3(256), st, (const float *)G_dev, c, M_dev));
+      TRY(run_mat(false, Y, c, rows, c, M_dev, c, tmp, parts, part_bytes, st));
+      if (hipMemcpyAsync(Y, tmp, (size_t)rows * c * 4, hipMemcpyDeviceToDevice, st) != hipSuccess)
+        return LORA4_ERR_HIP;
+    }
+    return LORA4_OK;
+  }
   std::vector<double> G, M((size_t)c * c), L((size_t)c * c);
   std::vector<float> stage;
   for (int pass = 0; pass < 2; ++pass) {
@@ -936,7 +947,7 @@ lora4_status orthonormalize(float *Y, float *tmp, int64_t rows, int c, float *G_
     for (int col = 0; col < c; ++col)
       for (int i = c - 1; i >= 0; --i) {
         double v = (i == col) ? 1.0 : 0.0;
-        for (int k = i + 1; k < c; ++k) v -= L[(size_t)k * c + i] * M[(size_t)k * c + col];
+        for (int k = c - 1; k > i; --k) v -= L[(size_t)k * c + i] * M[(size_t)k * c + col];
         M[(size_t)i * c + col] = v / L[(size_t)i * c + i];
       }
     TRY(upload(M, M_dev, st, stage));
