@@ -110,6 +110,21 @@ __device__ __forceinline__ TileGroups tile_groups(const Params &p, int64_t row0,
   return tg;
 }
 
+// Whether the reduction columns [k0, k0 + width) hold no row of the tile:
+// every tile group they belong to has no rows in [row0, row_hi). (Empty
+// groups between the tile's first and last would otherwise cost full steps
+// of zeros.) Uniform across the workgroup.
+__device__ __forceinline__ bool cols_empty(const Params &p, const TileGroups &tg, int k0, int width, int64_t row0,
+                                           int64_t row_hi) {
+  const int gi_lo = k0 / tg.rp;
+  const int gi_hi = min((k0 + width - 1) / tg.rp, tg.n - 1);
+  for (int gi = gi_lo; gi <= gi_hi; ++gi) {
+    const int64_t a = max(p.offsets[tg.g0 + gi], row0), b = min(p.offsets[tg.g0 + gi + 1], row_hi);
+    if (a < b) return false;
+  }
+  return true;
+}
+
 // Index within the tile's groups of the group holding row gr (-1 for a row
 // past the tile's range).
 __device__ __forceinline__ int row_group(const Params &p, const TileGroups &tg, int64_t gr, int64_t row_hi) {

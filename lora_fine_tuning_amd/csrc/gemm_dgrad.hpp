@@ -469,6 +469,8 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
     }
     const int rc = tg.n * tg.rp;   // reduction length
     for (int k0 = 0; k0 < rc; k0 += BKS) {
+      if constexpr (SHARED)
+        if (big::cols_empty(p, tg, k0, BKS, row0, row_hi)) continue;
       if (p.A2part) {
         big::a2_parts_to_lds<SHARED>(p, As0, [](int i, int c) { return swz(i, c); }, row0, row_hi, k0, t, col0 == 0,
                                      tg.rp, my);

@@ -482,6 +482,8 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
     }
     const int rc = tg.n * tg.rp;   // reduction length
     for (int k0 = 0; k0 < rc; k0 += BKS) {
+      if constexpr (SHARED)
+        if (big::cols_empty(p, tg, k0, BKS, row0, row_hi)) continue;
       const int nkk = min(4, (rc - k0 + 7) / 8);
       WFrag bt;
 #pragma unroll

@@ -48,6 +48,11 @@ OFFSETS = {
     # twelve adapters, several inside one 256-row tile, empty ones at both ends
     "twelve": [0, 0, 7, 30, 31, 64, 128, 129, 200, 250, 299, 300, 300],
 }
+# 200 adapters, rows for 8 of them: tiles span many adapters without rows
+_rows = np.zeros(200, dtype=np.int64)
+for a, m in [(3, 20), (40, 50), (41, 1), (90, 100), (150, 29), (151, 60), (180, 30), (199, 10)]:
+    _rows[a] = m
+OFFSETS["sparse"] = [0] + np.cumsum(_rows).tolist()
 
 
 @pytest.mark.parametrize("fmt", [synth.NF4, synth.MXFP4, synth.NF4_DQ, synth.NVFP4])
