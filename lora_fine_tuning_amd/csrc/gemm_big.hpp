@@ -90,9 +90,10 @@ __device__ __forceinline__ int group_of_row(const int64_t *offsets, int groups, 
   return lo;
 }
 
-// The groups with rows in the row range [row0, row_hi) of a tile that
-// ignores the groups (offsets given: tiles ignore the groups only where
-// there are several): their tail products run as one product whose
+// The groups of a tile that ignores the groups (offsets given: tiles ignore
+// the groups only where there are several), from the one holding row0 to the
+// one holding row_hi - 1 (those between may have no rows; cols_empty skips
+// them): their tail products run as one product whose
 // reduction puts the groups' rank columns side by side, group g0 + i at
 // columns i rp .. i rp + r2 - 1 (rp = r2 rounded up to 8). A row's operand
 // is zero outside its own group's columns and each group's B rows fill its
