@@ -214,6 +214,84 @@ def _stream():
     return torch.cuda.current_stream().cuda_stream
 
 
+def _need(t, name, shape, dtype, device=None):
+    """Raises ValueError unless t is a dense tensor of this shape and dtype (on
+    `device` when given). The C ABI receives raw pointers only, so a short or
+    mis-typed buffer would be read or written past its end by the kernels."""
+    import torch
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def check_layer_args(base, X, A, B, dY=None, Z=None, offsets=None, adapters=None, outputs=()):
+    """Validates the tensors of one layer call before any pointer reaches the
+    library: bf16, contiguous, on X's device, X [M, K], A [(G,) r, K],
+    B [(G,) N, r], dY [M, N], Z [M, r], offsets int64 [G + 1]; G is the
+    base's expert count, or `adapters` for several adapters over one base.
+    `outputs` holds (name, tensor, shape) triples of caller-given outputs.
+    Returns (M, r, G). Pure host logic (CPU tensors work)."""
+    import torch
+    bf = torch.bfloat16
+    if X is None or X.dim() != 2:
+        raise ValueError("X must be a 2-D tensor [M, K]")
+    dev = X.device
+    M = X.shape[0]
+    _need(X, "X", (M, base.K), bf, dev)
+    G = base.groups if adapters is None else int(adapters)
+    if adapters is not None and base.groups != 1:
+        raise ValueError("several adapters need a base with one group")
+    if A is None or A.dim() not in (2, 3):
+        raise ValueError("A must be [r, K] or [groups, r, K]")
+    if A.dim() == 2 and G != 1:
+        raise ValueError(f"A must be [groups={G}, r, K]")
+    r = A.shape[-2]
+    a_shape = (r, base.K) if A.dim() == 2 else (G, r, base.K)
+    b_shape = (base.N, r) if A.dim() == 2 else (G, base.N, r)
+    _need(A, "A", a_shape, bf, dev)
+    _need(B, "B", b_shape, bf, dev)
+    if dY is not None:
+        _need(dY, "dY", (M, base.N), bf, dev)
+    if Z is not None:
+        _need(Z, "Z", (M, r), bf, dev)
+    if G > 1:
+        _need(offsets, "group offsets", (G + 1,), torch.int64, dev)
+    elif offsets is not None:
+        raise ValueError("group offsets are only taken with several groups")
+    for name, t, shape in outputs:
+        if t is not None:
+            _need(t, name, shape, bf, dev)
+    for name, t in (("codes", base.codes), ("scales", base.scales), ("scales2", base.scales2)):
+        if t is not None and (t.device != dev or not t.is_contiguous()):
+            raise ValueError(f"base {name} must be contiguous on {dev}")
+    return M, r, G
+
+
+def _check_workspace(ws, need, dev):
+    import torch
+    if ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous() or ws.device != dev:
+        raise ValueError("workspace must be a contiguous 1-D uint8 tensor on the layer's device")
+    if ws.numel() < need:
+        raise ValueError(f"workspace has {ws.numel()} bytes, {need} needed")
+
+
+def _check_pack_input(W):
+    import torch
+    if W is None or W.dim() not in (2, 3):
+        raise ValueError("W must be [N, K] or [E, N, K]")
+    if W.dtype != torch.bfloat16 or not W.is_contiguous():
+        raise ValueError("W must be a contiguous bf16 tensor")
+
+
 @dataclass
 class PackedBase:
     """A frozen 4-bit base on the device, [groups][N][K] logically, stored in
@@ -234,6 +312,7 @@ class PackedBase:
 def pack_nf4(W, double_quant=False):
     """Quantize bf16 W ([N, K] or [E, N, K], on the GPU) to NF4 on the GPU."""
     import torch
+    _check_pack_input(W)
     Ws = W if W.dim() == 3 else W.unsqueeze(0)
     E, N, K = Ws.shape
     dev = W.device
@@ -258,6 +337,7 @@ def pack_nf4(W, double_quant=False):
 def pack_mxfp4(W):
     """Quantize bf16 W ([N, K] or [E, N, K], on the GPU) to MXFP4 on the GPU."""
     import torch
+    _check_pack_input(W)
     Ws = W if W.dim() == 3 else W.unsqueeze(0)
     E, N, K = Ws.shape
     dev = W.device
@@ -275,6 +355,7 @@ def pack_mxfp4(W):
 def pack_nvfp4(W):
     """Quantize bf16 W ([N, K] or [E, N, K], on the GPU) to NVFP4 on the GPU."""
     import torch
+    _check_pack_input(W)
     Ws = W if W.dim() == 3 else W.unsqueeze(0)
     E, N, K = Ws.shape
     dev = W.device
@@ -297,62 +378,86 @@ def workspace_for(which, base, M, r):
     return torch.empty((n,), dtype=torch.uint8, device=base.codes.device)
 
 
-def forward(base, X, A, B, s, group_offsets=None, want_z=True, want_parts=False, workspace=None):
-    """Y (and Z, Y_base, Y_lora) for bf16 X [M, K], A [(E,) r, K], B [(E,) N, r]."""
+def _out(t, shape, dev):
     import torch
-    M = X.shape[0]
-    r = A.shape[-2]
+    return torch.empty(shape, dtype=torch.bfloat16, device=dev) if t is None else t
+
+
+def forward(base, X, A, B, s, group_offsets=None, want_z=True, want_parts=False, workspace=None, out=None):
+    """Y (and Z, Y_base, Y_lora) for bf16 X [M, K], A [(E,) r, K], B [(E,) N, r].
+    `out` may hold caller-allocated outputs under the keys Y, Z, Y_base, Y_lora."""
+    out = out or {}
+    M, r, _ = check_layer_args(base, X, A, B, offsets=group_offsets, outputs=[
+        ("Y", out.get("Y"), (X.shape[0], base.N)), ("Z", out.get("Z"), (X.shape[0], A.shape[-2])),
+        ("Y_base", out.get("Y_base"), (X.shape[0], base.N)), ("Y_lora", out.get("Y_lora"), (X.shape[0], base.N))])
     dev = X.device
-    Y = torch.empty((M, base.N), dtype=torch.bfloat16, device=dev)
-    Z = torch.empty((M, r), dtype=torch.bfloat16, device=dev) if want_z else None
-    Yb = torch.empty_like(Y) if want_parts else None
-    Yl = torch.empty_like(Y) if want_parts else None
+    Y = _out(out.get("Y"), (M, base.N), dev)
+    Z = _out(out.get("Z"), (M, r), dev) if want_z or out.get("Z") is not None else None
+    Yb = _out(out.get("Y_base"), (M, base.N), dev) if want_parts or out.get("Y_base") is not None else None
+    Yl = _out(out.get("Y_lora"), (M, base.N), dev) if want_parts or out.get("Y_lora") is not None else None
     W = base.abi()
+    need = lora4_workspace_bytes(0, W, M, r)
+    if need == 0:
+        raise ValueError("invalid arguments for lora4_workspace_bytes")
     if workspace is None:
         workspace = workspace_for(0, base, M, r)
+    _check_workspace(workspace, need, dev)
     st = lora4_forward(W, _ptr(X), M, _ptr(A), _ptr(B), r, float(s), _ptr(group_offsets), _ptr(Y), _ptr(Z),
                        _ptr(Yb), _ptr(Yl), _ptr(workspace), workspace.numel(), _stream())
     _check(st, "lora4_forward")
     return {"Y": Y, "Z": Z, "Y_base": Yb, "Y_lora": Yl}
 
 
-def forward_multi(base, X, A, B, s, adapter_offsets=None, want_z=True, want_parts=False, workspace=None):
+def forward_multi(base, X, A, B, s, adapter_offsets=None, want_z=True, want_parts=False, workspace=None, out=None):
     """Several adapters over one shared base: A [adapters, r, K], B [adapters, N, r]
     (rows of X pre-sorted by adapter, adapter_offsets a device int64 [adapters+1])."""
-    import torch
-    M = X.shape[0]
-    adapters, r = A.shape[0], A.shape[1]
+    out = out or {}
+    if A is None or A.dim() != 3:
+        raise ValueError("A must be [adapters, r, K]")
+    adapters = A.shape[0]
+    M, r, _ = check_layer_args(base, X, A, B, offsets=adapter_offsets, adapters=adapters, outputs=[
+        ("Y", out.get("Y"), (X.shape[0], base.N)), ("Z", out.get("Z"), (X.shape[0], A.shape[-2])),
+        ("Y_base", out.get("Y_base"), (X.shape[0], base.N)), ("Y_lora", out.get("Y_lora"), (X.shape[0], base.N))])
     dev = X.device
-    Y = torch.empty((M, base.N), dtype=torch.bfloat16, device=dev)
-    Z = torch.empty((M, r), dtype=torch.bfloat16, device=dev) if want_z else None
-    Yb = torch.empty_like(Y) if want_parts else None
-    Yl = torch.empty_like(Y) if want_parts else None
+    Y = _out(out.get("Y"), (M, base.N), dev)
+    Z = _out(out.get("Z"), (M, r), dev) if want_z or out.get("Z") is not None else None
+    Yb = _out(out.get("Y_base"), (M, base.N), dev) if want_parts or out.get("Y_base") is not None else None
+    Yl = _out(out.get("Y_lora"), (M, base.N), dev) if want_parts or out.get("Y_lora") is not None else None
     W = base.abi()
+    n = lora4_workspace_bytes_multi(0, W, adapters, M, r)
+    if n == 0:
+        raise ValueError("invalid arguments for lora4_workspace_bytes_multi")
     if workspace is None:
-        n = lora4_workspace_bytes_multi(0, W, adapters, M, r)
-        if n == 0:
-            raise ValueError("invalid arguments for lora4_workspace_bytes_multi")
+        import torch
         workspace = torch.empty((n,), dtype=torch.uint8, device=dev)
+    _check_workspace(workspace, n, dev)
     st = lora4_forward_multi(W, adapters, _ptr(X), M, _ptr(A), _ptr(B), r, float(s), _ptr(adapter_offsets),
                              _ptr(Y), _ptr(Z), _ptr(Yb), _ptr(Yl), _ptr(workspace), workspace.numel(), _stream())
     _check(st, "lora4_forward_multi")
     return {"Y": Y, "Z": Z, "Y_base": Yb, "Y_lora": Yl}
 
 
-def backward_multi(base, X, dY, A, B, s, Z=None, adapter_offsets=None, workspace=None):
+def backward_multi(base, X, dY, A, B, s, Z=None, adapter_offsets=None, workspace=None, out=None):
     """dX, dA [adapters, r, K], dB [adapters, N, r] for several adapters over one base."""
     import torch
-    M = X.shape[0]
-    adapters, r = A.shape[0], A.shape[1]
-    dX = torch.empty((M, base.K), dtype=torch.bfloat16, device=X.device)
-    dA = torch.empty_like(A)
-    dB = torch.empty_like(B)
+    out = out or {}
+    if A is None or A.dim() != 3:
+        raise ValueError("A must be [adapters, r, K]")
+    adapters = A.shape[0]
+    M, r, _ = check_layer_args(base, X, A, B, dY=dY, Z=Z, offsets=adapter_offsets, adapters=adapters, outputs=[
+        ("dX", out.get("dX"), (X.shape[0], base.K)), ("dA", out.get("dA"), tuple(A.shape)),
+        ("dB", out.get("dB"), tuple(B.shape))])
+    dev = X.device
+    dX = _out(out.get("dX"), (M, base.K), dev)
+    dA = out.get("dA") if out.get("dA") is not None else torch.empty_like(A)
+    dB = out.get("dB") if out.get("dB") is not None else torch.empty_like(B)
     W = base.abi()
+    n = lora4_workspace_bytes_multi(1, W, adapters, M, r)
+    if n == 0:
+        raise ValueError("invalid arguments for lora4_workspace_bytes_multi")
     if workspace is None:
-        n = lora4_workspace_bytes_multi(1, W, adapters, M, r)
-        if n == 0:
-            raise ValueError("invalid arguments for lora4_workspace_bytes_multi")
-        workspace = torch.empty((n,), dtype=torch.uint8, device=X.device)
+        workspace = torch.empty((n,), dtype=torch.uint8, device=dev)
+    _check_workspace(workspace, n, dev)
     st = lora4_backward_multi(W, adapters, _ptr(X), _ptr(dY), M, _ptr(A), _ptr(B), r, float(s),
                               _ptr(adapter_offsets), _ptr(Z), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(workspace),
                               workspace.numel(), _stream())
@@ -360,17 +465,25 @@ def backward_multi(base, X, dY, A, B, s, Z=None, adapter_offsets=None, workspace
     return {"dX": dX, "dA": dA, "dB": dB}
 
 
-def backward(base, X, dY, A, B, s, Z=None, group_offsets=None, workspace=None):
-    """dX, dA, dB for bf16 inputs (Z from forward, or None to recompute)."""
+def backward(base, X, dY, A, B, s, Z=None, group_offsets=None, workspace=None, out=None):
+    """dX, dA, dB for bf16 inputs (Z from forward, or None to recompute).
+    `out` may hold caller-allocated outputs under the keys dX, dA, dB."""
     import torch
-    M = X.shape[0]
-    r = A.shape[-2]
-    dX = torch.empty((M, base.K), dtype=torch.bfloat16, device=X.device)
-    dA = torch.empty_like(A)
-    dB = torch.empty_like(B)
+    out = out or {}
+    M, r, _ = check_layer_args(base, X, A, B, dY=dY, Z=Z, offsets=group_offsets, outputs=[
+        ("dX", out.get("dX"), (X.shape[0], base.K)), ("dA", out.get("dA"), tuple(A.shape)),
+        ("dB", out.get("dB"), tuple(B.shape))])
+    dev = X.device
+    dX = _out(out.get("dX"), (M, base.K), dev)
+    dA = out.get("dA") if out.get("dA") is not None else torch.empty_like(A)
+    dB = out.get("dB") if out.get("dB") is not None else torch.empty_like(B)
     W = base.abi()
+    need = lora4_workspace_bytes(1, W, M, r)
+    if need == 0:
+        raise ValueError("invalid arguments for lora4_workspace_bytes")
     if workspace is None:
         workspace = workspace_for(1, base, M, r)
+    _check_workspace(workspace, need, dev)
     st = lora4_backward(W, _ptr(X), _ptr(dY), M, _ptr(A), _ptr(B), r, float(s), _ptr(group_offsets), _ptr(Z),
                         _ptr(dX), _ptr(dA), _ptr(dB), _ptr(workspace), workspace.numel(), _stream())
     _check(st, "lora4_backward")
@@ -381,7 +494,10 @@ def mxfp8(X):
     """bf16 X [M, K] (K % 32 == 0, on the GPU) -> MXFP8 E4M3 codes [M, K] and
     E8M0 scales [M, K / 32], both uint8."""
     import torch
+    if X is None or X.dim() != 2:
+        raise ValueError("X must be [M, K]")
     M, K = X.shape
+    _need(X, "X", (M, K), torch.bfloat16)
     codes = torch.empty((M, K), dtype=torch.uint8, device=X.device)
     scales = torch.empty((M, K // 32), dtype=torch.uint8, device=X.device)
     _check(quant_pack_mxfp8(_ptr(X), M, K, _ptr(codes), _ptr(scales), _stream()), "quant_pack_mxfp8")
@@ -392,8 +508,7 @@ def forward_mx(base, X, A, B, s, want_z=True, workspace=None):
     """MX-native forward of a plain MXFP4 layer: Y (and Z) for bf16 X [M, K],
     A [r, K], B [N, r]; the base product takes X as MXFP8."""
     import torch
-    M = X.shape[0]
-    r = A.shape[-2]
+    M, r, _ = check_layer_args(base, X, A, B)
     dev = X.device
     Y = torch.empty((M, base.N), dtype=torch.bfloat16, device=dev)
     Z = torch.empty((M, r), dtype=torch.bfloat16, device=dev) if want_z else None
@@ -414,10 +529,15 @@ def loftq_init(W, r, iters=5, s=1.0, double_quant=False):
     (or NF4-DQ) PackedBase of the base and the adapter A [r, K], B [N, r]
     (B divided by the layer scale s)."""
     import torch
+    if W is None or W.dim() != 2:
+        raise ValueError("W must be [N, K]")
+    _check_pack_input(W)
     N, K = W.shape
     dev = W.device
     fmt = LORA4_NF4_DQ if double_quant else LORA4_NF4
     sizes = [lora4_packed_bytes(fmt, N, K, part) for part in range(3)]
+    if sizes[0] == 0:
+        raise ValueError("invalid shape for NF4 packing")
     codes = torch.empty((1, sizes[0]), dtype=torch.uint8, device=dev)
     if double_quant:
         scales = torch.empty((1, sizes[1]), dtype=torch.uint8, device=dev)

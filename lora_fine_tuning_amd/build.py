@@ -11,9 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "liblora4.so")
-SOURCES = [os.path.join(HERE, "csrc", "lora4.hip")]
-HEADERS = [os.path.join(HERE, "csrc", f) for f in ("common.hpp", "formats.hpp", "gemm.hpp", "gemm_big.hpp", "quant.hpp")]
-HEADERS.append(os.path.join(ROOT, "include", "lora4.h"))
+SOURCES = [os.path.join(HERE, "csrc", "lora4.hip")]   # includes every csrc/*.hpp
 
 FLAGS = [
     "--offload-arch=gfx950",

@@ -696,20 +696,6 @@ __global__ void k_reduce_bf16(const float *part, int splits, int64_t stride, int
   }
 }
 
-// dB[g][n][j] = bf16(alpha * sum_s part[s][g][j][n]) (partials hold dB^T).
-__global__ void k_reduce_transpose_bf16(const float *part, int splits, int groups, int64_t P,
-                                        int64_t Q, uint16_t *out, float alpha) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // index into out [g][Q][P]
-  int64_t total = (int64_t)groups * P * Q;
-  if (i >= total) return;
-  int64_t g = i / (P * Q);
-  int64_t rem = i - g * P * Q;
-  int64_t q = rem / P, pp = rem - q * P;
-  float s = 0.f;
-  for (int k = 0; k < splits; ++k) s += part[((int64_t)k * groups + g) * P * Q + pp * Q + q];
-  out[i] = to_bf16(s * alpha);
-}
-
 // dA[i] = bf16(sum_s partA[s][i]) for i < na, then
 // dB[g][n][j] = bf16(alpha sum_s partB[s][g][j][n]) (partials hold dB^T).
 __global__ void k_reduce_dadb(const float *part_a, int splits_a, int64_t na, uint16_t *dA, const float *part_b,

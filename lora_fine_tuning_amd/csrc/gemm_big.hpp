@@ -8,15 +8,12 @@
 
 #include "formats.hpp"
 
-#ifndef LORA4_SCHED_INTERLEAVE
-#define LORA4_SCHED_INTERLEAVE 1
-#endif
-#ifndef LORA4_SCHED_VALU
-#define LORA4_SCHED_VALU 5
-#endif
-
 namespace lora4 {
 namespace big {
+
+// VALU instructions the scheduling hints place between the two MFMAs of a pair
+// in the sub-steps without hand-dealt slices (the rank-r product).
+constexpr int SCHED_VALU = 5;
 
 constexpr int BM = 256, BN = 256, BKS = 64;   // tile of both GEMMs
 constexpr uint32_t RSRC_WORD3 = 0x00020000u;   // raw 32-bit buffer, gfx9 family
@@ -134,25 +131,19 @@ __device__ __forceinline__ int row_group(const Params &p, const TileGroups &tg, 
 
 constexpr int A2_MAX_PARTS = 4;
 
-#ifndef LORA4_GROUP_M
-#define LORA4_GROUP_M 4
-#endif
+// Row tiles per group of the tile order below (2 and 8 measured slower).
+constexpr int GROUP_M = 4;
 
 // Tile t of a slots x tiles_n grid of output tiles in grouped order: runs of
-// LORA4_GROUP_M row tiles are walked column by column, so that the tiles one
+// GROUP_M row tiles are walked column by column, so that the tiles one
 // XCD runs at the same time (a contiguous range of t) share activation row
 // tiles and W column tiles in its L2.
 __device__ __forceinline__ void grouped_tile(int t, int tiles_n, int slots, int &slot, int &tn) {
-  if (LORA4_GROUP_M <= 1) {
-    slot = t / tiles_n;
-    tn = t - slot * tiles_n;
-    return;
-  }
-  const int per_group = LORA4_GROUP_M * tiles_n;
+  const int per_group = GROUP_M * tiles_n;
   const int gi = t / per_group;
   const int r = t - gi * per_group;
-  const int g0 = gi * LORA4_GROUP_M;
-  const int rows = slots - g0 < LORA4_GROUP_M ? slots - g0 : LORA4_GROUP_M;
+  const int g0 = gi * GROUP_M;
+  const int rows = slots - g0 < GROUP_M ? slots - g0 : GROUP_M;
   tn = r / rows;
   slot = g0 + (r - tn * rows);
 }

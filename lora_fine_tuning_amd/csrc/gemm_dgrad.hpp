@@ -36,9 +36,9 @@ using big::Params;
 using big::RunTable;
 using big::rsrc_t;
 
-#ifndef LORA4_DGRAD_V1
-#define LORA4_DGRAD_V1 5
-#endif
+// VALU instructions placed between the two MFMAs of a pair in the hand-dealt
+// sub-steps.
+constexpr int SLICE_V1 = 5;
 
 constexpr int BM = 256, BN = 256, BKS = 64, THREADS = 256;
 constexpr int TILE_A = BM * BKS;    // dY stage [256][64], tile64 layout
@@ -239,13 +239,11 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
         for (int i = 0; i < 4; ++i) acc[j][i] = mfma_32x32x16(bf[j], af[i], acc[j][i]);
         if (more) bf[j] = read_bf(Bs, kk + 1, j);
       }
-#if LORA4_SCHED_INTERLEAVE
 #pragma unroll
       for (int m = 0; m < 16; ++m) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // MFMA
         if (more && m < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // LDS read
       }
-#endif
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -413,7 +411,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
         if (G < 8) issue_a1(s + 1, Anxt, G);
         else if (G < 11) load_w1(s + 2, rload, G - 8);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, LORA4_DGRAD_V1, 0);    // VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, SLICE_V1, 0);    // VALU
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);                 // LDS read
         __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);                 // LDS write

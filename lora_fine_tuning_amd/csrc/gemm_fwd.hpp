@@ -46,9 +46,9 @@ using big::Params;
 using big::RunTable;
 using big::rsrc_t;
 
-#ifndef LORA4_SLICE_V1
-#define LORA4_SLICE_V1 5
-#endif
+// VALU instructions placed between the two MFMAs of a pair in the hand-dealt
+// sub-steps (the rest of the pair's slice follows its LDS read and loads).
+constexpr int SLICE_V1 = 5;
 
 constexpr int BM = 256, BN = 256, BKS = 64, THREADS = 256, STAGES = 5;
 constexpr int TILE = BM * BKS;   // one X stage, bf16 elements
@@ -265,17 +265,15 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
       if (reload) x[i] = lds_read_b128(src + swz(i * 32 + l32, chunk));
     }
     hook();
-#if LORA4_SCHED_INTERLEAVE
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, LORA4_SCHED_VALU, 0);   // VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, big::SCHED_VALU, 0);   // VALU
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
       if (reload) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // LDS read
       if (i & 1) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);       // global load
-      __builtin_amdgcn_sched_group_barrier(0x002, LORA4_SCHED_VALU, 0);   // VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, big::SCHED_VALU, 0);   // VALU
     }
-#endif
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -402,7 +400,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
       x[i] = lds_read_b128(src + swz(i * 32 + l32, chunk));
       slice(i);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, LORA4_SLICE_V1, 0);    // VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, SLICE_V1, 0);    // VALU
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                 // LDS read
       __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);                 // global load

@@ -130,52 +130,78 @@ hipEvent_t take_event() {
   return e;
 }
 
-template <typename Kern, typename Params>
-lora4_status launch(const char *name, Kern kernel, dim3 grid, dim3 block, const Params &params,
-                    hipStream_t stream) {
-  if (grid.x == 0 || grid.y == 0 || grid.z == 0) return LORA4_OK;
+// Runs `go` (which enqueues one kernel on `stream`), bracketed by two timing
+// events when timing is on. An error still pending from earlier work on the
+// thread is reported before anything is launched (so it is not pinned on this
+// kernel); on any failure the events go back to the pool.
+template <typename Go>
+lora4_status launch_timed(const char *name, hipStream_t stream, Go &&go) {
+  if (hipPeekAtLastError() != hipSuccess) return LORA4_ERR_HIP;
   hipEvent_t ea = nullptr, eb = nullptr;
-  bool timed = false;
   {
     std::lock_guard<std::mutex> lk(g_tmu);
     if (g_timing) {
       ea = take_event();
       eb = take_event();
-      timed = ea && eb;
     }
   }
-  if (timed && hipEventRecord(ea, stream) != hipSuccess) return LORA4_ERR_HIP;
-  hipLaunchKernelGGL(kernel, grid, block, 0, stream, params);
-  if (hipGetLastError() != hipSuccess) return LORA4_ERR_HIP;
+  auto give_back = [&] {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    if (ea) g_free_events.push_back(ea);
+    if (eb) g_free_events.push_back(eb);
+  };
+  const bool timed = ea && eb;
+  if (!timed && (ea || eb)) {   // only one event could be had: run untimed
+    give_back();
+    ea = eb = nullptr;
+  }
+  if (timed && hipEventRecord(ea, stream) != hipSuccess) {
+    give_back();
+    return LORA4_ERR_HIP;
+  }
+  go();
+  if (hipGetLastError() != hipSuccess) {
+    give_back();
+    return LORA4_ERR_HIP;
+  }
   if (timed) {
-    if (hipEventRecord(eb, stream) != hipSuccess) return LORA4_ERR_HIP;
+    if (hipEventRecord(eb, stream) != hipSuccess) {
+      give_back();
+      return LORA4_ERR_HIP;
+    }
     std::lock_guard<std::mutex> lk(g_tmu);
     g_pending.push_back({name, ea, eb});
   }
   return LORA4_OK;
 }
 
+template <typename Kern, typename Params>
+lora4_status launch(const char *name, Kern kernel, dim3 grid, dim3 block, const Params &params,
+                    hipStream_t stream) {
+  if (grid.x == 0 || grid.y == 0 || grid.z == 0) return LORA4_OK;
+  return launch_timed(name, stream, [&] { hipLaunchKernelGGL(kernel, grid, block, 0, stream, params); });
+}
+
 template <typename Kern, typename... Args>
 lora4_status launch_args(const char *name, Kern kernel, dim3 grid, dim3 block, hipStream_t stream,
                          Args... args) {
   if (grid.x == 0 || grid.y == 0 || grid.z == 0) return LORA4_OK;
-  hipEvent_t ea = nullptr, eb = nullptr;
-  bool timed = false;
-  {
-    std::lock_guard<std::mutex> lk(g_tmu);
-    if (g_timing) {
-      ea = take_event();
-      eb = take_event();
-      timed = ea && eb;
-    }
-  }
-  if (timed && hipEventRecord(ea, stream) != hipSuccess) return LORA4_ERR_HIP;
-  hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
-  if (hipGetLastError() != hipSuccess) return LORA4_ERR_HIP;
-  if (timed) {
-    if (hipEventRecord(eb, stream) != hipSuccess) return LORA4_ERR_HIP;
-    std::lock_guard<std::mutex> lk(g_tmu);
-    g_pending.push_back({name, ea, eb});
+  return launch_timed(name, stream, [&] { hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...); });
+}
+
+// Raises a kernel's dynamic LDS limit, once per (device, kernel): the
+// attribute belongs to the kernel object of the device that is current.
+lora4_status set_lds_limit(const void *kernel, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void *>, bool> done;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LORA4_ERR_HIP;
+  std::lock_guard<std::mutex> lk(mu);
+  bool &d = done[{dev, kernel}];
+  if (!d) {
+    if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return LORA4_ERR_HIP;
+    d = true;
   }
   return LORA4_OK;
 }
@@ -184,37 +210,9 @@ template <typename Kern, typename Params>
 lora4_status launch_lds(const char *name, Kern kernel, dim3 grid, dim3 block, size_t lds, const Params &params,
                         hipStream_t stream) {
   if (grid.x == 0 || grid.y == 0 || grid.z == 0) return LORA4_OK;
-  // raise the dynamic LDS limit once per kernel (per device of this process)
-  static std::mutex mu;
-  static std::map<const void *, bool> done;
-  {
-    std::lock_guard<std::mutex> lk(mu);
-    if (!done[(const void *)kernel]) {
-      if (hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
-          hipSuccess)
-        return LORA4_ERR_HIP;
-      done[(const void *)kernel] = true;
-    }
-  }
-  hipEvent_t ea = nullptr, eb = nullptr;
-  bool timed = false;
-  {
-    std::lock_guard<std::mutex> lk(g_tmu);
-    if (g_timing) {
-      ea = take_event();
-      eb = take_event();
-      timed = ea && eb;
-    }
-  }
-  if (timed && hipEventRecord(ea, stream) != hipSuccess) return LORA4_ERR_HIP;
-  hipLaunchKernelGGL(kernel, grid, block, lds, stream, params);
-  if (hipGetLastError() != hipSuccess) return LORA4_ERR_HIP;
-  if (timed) {
-    if (hipEventRecord(eb, stream) != hipSuccess) return LORA4_ERR_HIP;
-    std::lock_guard<std::mutex> lk(g_tmu);
-    g_pending.push_back({name, ea, eb});
-  }
-  return LORA4_OK;
+  const lora4_status st = set_lds_limit((const void *)kernel, lds);
+  if (st != LORA4_OK) return st;
+  return launch_timed(name, stream, [&] { hipLaunchKernelGGL(kernel, grid, block, lds, stream, params); });
 }
 
 #define TRY(x)                              \
@@ -608,24 +606,6 @@ lora4_status run_nn_main_fmt(int fmt, const NnParams &p, dim3 grid, const TailPa
   return LORA4_ERR_FORMAT;
 }
 
-lora4_status run_nt_skinny(int rt, const NtParams &p, dim3 grid, hipStream_t st) {
-  switch (rt) {
-    case 16: return launch("gemm_nt_lora_down", k_gemm_nt<FMT_BF16, BM_SKINNY, 16, 4>, grid, dim3(THREADS), p, st);
-    case 32: return launch("gemm_nt_lora_down", k_gemm_nt<FMT_BF16, BM_SKINNY, 32, 4>, grid, dim3(THREADS), p, st);
-    case 64: return launch("gemm_nt_lora_down", k_gemm_nt<FMT_BF16, BM_SKINNY, 64, 4>, grid, dim3(THREADS), p, st);
-    default: return launch("gemm_nt_lora_down", k_gemm_nt<FMT_BF16, BM_SKINNY, 128, 2>, grid, dim3(THREADS), p, st);
-  }
-}
-
-lora4_status run_nn_skinny(int rt, const NnParams &p, dim3 grid, hipStream_t st) {
-  switch (rt) {
-    case 16: return launch("gemm_nn_lora_dz", k_gemm_nn<FMT_BF16, BM_SKINNY, 16, 4>, grid, dim3(THREADS), p, st);
-    case 32: return launch("gemm_nn_lora_dz", k_gemm_nn<FMT_BF16, BM_SKINNY, 32, 4>, grid, dim3(THREADS), p, st);
-    case 64: return launch("gemm_nn_lora_dz", k_gemm_nn<FMT_BF16, BM_SKINNY, 64, 4>, grid, dim3(THREADS), p, st);
-    default: return launch("gemm_nn_lora_dz", k_gemm_nn<FMT_BF16, BM_SKINNY, 128, 2>, grid, dim3(THREADS), p, st);
-  }
-}
-
 // Both jobs share P (the rank) and so the P tiling; grid sizes of the two are
 // pa x qa x za and pa x qb x zb blocks.
 lora4_status run_tn2(const char *name, int rt, const TnParams &a, const TnParams &b, int qa, int za, int qb,
@@ -668,19 +648,12 @@ struct SkSched {
   int tm, tj, ranges;
   int64_t klen;
 };
-#ifndef SK_TARGET_WG
-#define SK_TARGET_WG 512
-#endif
-#ifndef SK_MAX_RANGES
-#define SK_MAX_RANGES 4
-#endif
+constexpr int64_t SK_TARGET_WG = 512;   // workgroups wanted per pass
+constexpr int64_t SK_MAX_RANGES = 4;    // (8 measured 0.5% slower on the 8B layer set)
 SkSched sk_sched(int64_t M, int64_t R, int r, int64_t E) {
   SkSched f{};
   f.tj = r <= 16 ? 1 : r <= 32 ? 2 : r <= 64 ? 4 : 8;
-#ifndef SK_TM_R16
-#define SK_TM_R16 2
-#endif
-  f.tm = f.tj == 1 ? SK_TM_R16 : f.tj == 2 ? 4 : f.tj == 4 ? 2 : 1;
+  f.tm = f.tj == 1 ? 2 : f.tj == 2 ? 4 : f.tj == 4 ? 2 : 1;
   const int64_t blocks = (ceil_div(std::max<int64_t>(M, 1), 16 * f.tm) + (E > 1 ? E : 0)) * ceil_div(r, 16 * f.tj);
   const int64_t chunks = std::max<int64_t>(1, ceil_div(R, 32));
   int64_t want = ceil_div(SK_TARGET_WG, blocks);

@@ -28,14 +28,8 @@ using big::rsrc_t;
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2v_t __attribute__((ext_vector_type(2)));
 
-#ifndef LORA4_MX_STAGES
-#define LORA4_MX_STAGES 5
-#endif
-#ifndef LORA4_MX_AHEAD
-#define LORA4_MX_AHEAD 4
-#endif
 // X stages in the LDS ring; steps ahead that W and the X scales are loaded
-constexpr int BM = 256, BN = 256, BKS = 64, THREADS = 256, STAGES = LORA4_MX_STAGES, AHEAD = LORA4_MX_AHEAD;
+constexpr int BM = 256, BN = 256, BKS = 64, THREADS = 256, STAGES = 5, AHEAD = 4;
 constexpr int TILE8 = BM * BKS;        // one MXFP8 X stage, bytes
 constexpr int ZTILE = BM * BKS * 2;    // bf16 staging tile of the rank-r product, bytes
 constexpr int EPI = 4 * BM * 64 * 2;   // epilogue: each wave's 256 x 64 bf16 block

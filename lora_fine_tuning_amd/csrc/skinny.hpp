@@ -84,20 +84,10 @@ __global__ __launch_bounds__(THREADS) void k_rows_skinny(Params p) {
   const int64_t chunks = (p.R + 31) / 32;
   const int64_t r_begin = (int64_t)blockIdx.z * (p.klen / 32);
   const int64_t r_end = r_begin + p.klen / 32 < chunks ? r_begin + p.klen / 32 : chunks;
-#ifndef SK_INTERLEAVE
-#define SK_INTERLEAVE 1
-#endif
-#if SK_INTERLEAVE
   // waves interleaved (wave w takes chunks w, w + 4, ..): the four waves read
   // neighbouring 64-byte pieces of each row at about the same time
   const int64_t n_local = r_end - r_begin > wave ? (r_end - r_begin - wave + 3) / 4 : 0;
   auto cmap = [&](int64_t i) { return r_begin + wave + 4 * i; };
-#else
-  const int64_t per = (r_end - r_begin + 3) / 4;
-  const int64_t c_first = r_begin + wave * per;
-  const int64_t n_local = c_first < r_end ? (c_first + per < r_end ? per : r_end - c_first) : 0;
-  auto cmap = [&](int64_t i) { return c_first + i; };
-#endif
 
   const bool act_vec = (p.ld_act % 8) == 0;
   const bool w_vec = (p.ld_w % 8) == 0;
