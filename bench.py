@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--cpu-reps", type=int, default=3, help="passes of the CPU oracle over its sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (counter calibration) and exit")
+    ap.add_argument("--peak-probe", action="store_true",
+                    help="only measure the roofline denominators (bf16 MFMA rate, HBM read and copy bandwidth) "
+                         "and exit")
     ap.add_argument("--fmt", choices=["nf4", "nf4_dq", "mxfp4", "nvfp4"], default=None,
                     help="store every base of the workload in this format instead of its own")
     ap.add_argument("--mx", action="store_true",
@@ -163,6 +166,29 @@ def kernel_bytes(name, spec):
     }.get(name, 0)
 
 
+def hbm_summary(specs, kernels, steps):
+    """Achieved HBM rates (GB/s, against the 8 TB/s peak): the packed base
+    (codes + scales) over the time of each base GEMM, and the algorithmic bytes
+    of the rank-r passes over theirs; for grouped layers also the packed bytes
+    of one expert and its rows."""
+    out = {"peak_gbps": PEAK_HBM_GBS}
+    for name, v in kernels.items():
+        if "algorithmic_gbps" in v:
+            out[name + "_gbps"] = v["algorithmic_gbps"]
+    s0 = specs[0]
+    if s0.experts > 1 and not s0.shared_base:
+        counts = [b - a for a, b in zip(s0.offsets[:-1], s0.offsets[1:])]
+        per = [round(s.N * s.K * BITS_PER_WEIGHT[s.fmt] / 8) for s in specs]
+        out["per_expert"] = {"experts": s0.experts, "rows_min": min(counts), "rows_avg": sum(counts) / len(counts),
+                             "rows_max": max(counts), "packed_bytes_per_expert": per}
+        for name in ("gemm_nt_base", "gemm_nn_dgrad"):
+            if name in kernels:
+                t_exp = kernels[name]["total_ms_per_step"] * 1e-3 / (len(specs) * s0.experts)
+                out["per_expert"][name + "_us"] = round(t_exp * 1e6, 3)
+                out["per_expert"][name + "_packed_gbps"] = round(sum(per) / len(per) / t_exp / 1e9, 1)
+    return out
+
+
 def csrc_digest():
     """sha256 over the HIP sources of the library (any kernel change alters it)."""
     import hashlib
@@ -206,6 +232,64 @@ def copy_probe(mib):
         b.copy_(a)
     torch.cuda.synchronize()
     log(f"[copy] 3 launches of {mib} MiB read + {mib} MiB written")
+
+
+def peak_probe():
+    """Measured denominators: the rate of back-to-back v_mfma_f32_32x32x16_bf16
+    on every SIMD (libpeakprobe), the HBM read bandwidth of a 4 GiB buffer read
+    once with 16-byte loads, and a torch device copy of 2 GiB. Best of 5 runs
+    each; one JSON line."""
+    import ctypes
+    import torch
+    from lora_fine_tuning_amd import build as B
+    if not os.path.exists(B.PROBE_LIB):
+        B.build()
+    P = ctypes.CDLL(B.PROBE_LIB)
+    P.peak_probe_mfma_flops.restype = ctypes.c_double
+    P.peak_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    P.peak_probe_mfma.restype = ctypes.c_float
+    P.peak_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    P.peak_probe_read.restype = ctypes.c_float
+    P.peak_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    st = torch.cuda.current_stream().cuda_stream
+    blocks, iters = 2048, 2048
+    out = torch.empty((blocks * 256,), dtype=torch.float32, device="cuda:0")
+    P.peak_probe_mfma(blocks, 64, out.data_ptr(), st)          # warm-up
+    ms = [P.peak_probe_mfma(blocks, iters, out.data_ptr(), st) for _ in range(5)]
+    if min(ms) <= 0:
+        raise RuntimeError("peak_probe_mfma failed")
+    mfma = P.peak_probe_mfma_flops(blocks, iters) / (min(ms) * 1e-3) / 1e12
+    log(f"[probe] bf16 MFMA {mfma:.1f} TFLOP/s (runs {', '.join(f'{m:.3f}' for m in ms)} ms)")
+    nbytes = 4 << 30
+    buf = torch.ones((nbytes // 4,), dtype=torch.float32, device="cuda:0")
+    rblocks = 256 * 32
+    rout = torch.empty((rblocks * 256,), dtype=torch.float32, device="cuda:0")
+    P.peak_probe_read(buf.data_ptr(), nbytes, rblocks, rout.data_ptr(), st)
+    rms = [P.peak_probe_read(buf.data_ptr(), nbytes, rblocks, rout.data_ptr(), st) for _ in range(5)]
+    read = nbytes / (min(rms) * 1e-3) / 1e9
+    log(f"[probe] HBM read {read:.0f} GB/s")
+    half = buf[: nbytes // 8]
+    dst = torch.empty_like(half)
+    dst.copy_(half)
+    torch.cuda.synchronize()
+    cms = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(half)
+        e1.record()
+        torch.cuda.synchronize()
+        cms.append(e0.elapsed_time(e1))
+    copy = 2 * half.numel() * 4 / (min(cms) * 1e-3) / 1e9
+    log(f"[probe] device copy {copy:.0f} GB/s (read + write)")
+    print(json.dumps({"metric": "measured roofline denominators", "bf16_mfma_tflops": round(mfma, 1),
+                      "bf16_mfma_frac_of_spec": round(mfma / PEAK_BF16_TFLOPS, 4),
+                      "hbm_read_gbps": round(read, 1), "hbm_copy_gbps": round(copy, 1),
+                      "hbm_read_frac_of_spec": round(read / PEAK_HBM_GBS, 4),
+                      "mfma_probe": {"blocks": blocks, "threads": 256, "iters": iters, "chains": 8,
+                                     "ms": [round(m, 4) for m in ms]},
+                      "read_probe": {"bytes": nbytes, "blocks": rblocks, "ms": [round(m, 4) for m in rms]}}),
+          flush=True)
 
 
 def blas_context(specs, torch, steps):
@@ -269,8 +353,12 @@ def cpu_baseline(specs, tokens, reps):
         m = min(tokens, spec.M)
         prepared.append((spec, packs, t["X"][:m], t["dY"][:m], t["A"], t["B"], m))
     flops = 0
+    done = 0
     t0 = time.perf_counter()
     for _ in range(reps):
+        if done and time.perf_counter() - t0 > 15.0:
+            break                  # enough CPU time for a stable rate (large workloads)
+        done += 1
         for spec, packs, X, dY, A, B, m in prepared:
             for e, pk in enumerate(packs):
                 if spec.fmt == synth.MXFP4:
@@ -290,16 +378,50 @@ def cpu_baseline(specs, tokens, reps):
                 if spec.experts > 1:
                     break          # sample: the first expert of a grouped layer
     dt = time.perf_counter() - t0
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    blas = blas_info()
+    threads = blas.pop("threads", None) or len(os.sched_getaffinity(0))
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "seconds": dt,
-            "sample": f"{reps} passes over every layer of the workload at its first {tokens} tokens (capped at "
+            "seconds": dt, "precision": "float64 (the oracle's own arithmetic)", "cpu": cpu_model(),
+            "host_cpus": len(os.sched_getaffinity(0)), "blas": blas,
+            "sample": f"{done} passes over every layer of the workload at its first {tokens} tokens (capped at "
                       f"the layer's tokens; first expert of grouped layers): oracle dequant + forward + "
                       f"backward, float64 numpy"}
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_info():
+    """numpy's BLAS (name, version, threads in use) as threadpoolctl and numpy
+    report it."""
+    out = {}
+    try:
+        from threadpoolctl import threadpool_info
+        for d in threadpool_info():
+            if d.get("user_api") == "blas":
+                out = {"library": d.get("internal_api"), "version": d.get("version"),
+                       "threads": d.get("num_threads"), "arch": d.get("architecture")}
+                break
+    except Exception:
+        pass
+    try:
+        import numpy as np
+        cfg = np.show_config(mode="dicts")
+        b = cfg.get("Build Dependencies", {}).get("blas", {})
+        out.setdefault("library", b.get("name"))
+        out["numpy_blas"] = f"{b.get('name')} {b.get('version')}"
+    except Exception:
+        pass
+    return out
 
 
 def loftq_bench(args, specs, L, torch, synth):
@@ -337,6 +459,9 @@ def main():
     args = parse()
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.peak_probe:
+        peak_probe()
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -445,6 +570,8 @@ def main():
 
     roofline = None
     kernels = {}
+    hbm = None
+    line_extra = {}
     if not args.no_kernel_timing:
         # the same timed loop with every launch bracketed by HIP events on its stream
         L.timing_enable(True)
@@ -481,7 +608,10 @@ def main():
         for k, v in sorted(kernels.items(), key=lambda kv: -kv[1]["total_ms_per_step"]):
             log(f"[bench]   {k:22s} {v['launches']:5d} launches  avg {v['avg_us']:9.1f} us  "
                 f"{v['total_ms_per_step']:.3f} ms/step")
+        hbm = hbm_summary(specs, kernels, args.steps)
 
+    if hbm is not None:
+        line_extra["hbm"] = hbm
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline (oracle) on {args.cpu_tokens} tokens per layer")
@@ -524,6 +654,7 @@ def main():
     }
     if blas is not None:
         line["blas_context"] = blas
+    line.update(line_extra)
     print(json.dumps(line), flush=True)
 
 

@@ -225,6 +225,28 @@ lora4_status quant_pack_nf4(const uint16_t *W_bf16, int64_t N, int64_t K, int32_
 lora4_status quant_pack_mxfp4(const uint16_t *W_bf16, int64_t N, int64_t K,
                               uint8_t *codes, uint8_t *scales_e8m0, void *stream);
 
+/* A base that ships only in 4 bits, packed row-major ("Fine-Tuning 4-Bit
+ * Models", section "Case 3: Only a 4-bit-native checkpoint ships": the native
+ * base is loaded as it is and adapted without a bf16 copy), rearranged into
+ * the tiled storage of lora4_W, bit for bit, on the stream:
+ *  codes_rm  : uint8 [groups][N][K/2]; byte j of a row holds element 2j in its
+ *              low nibble and element 2j+1 in its high nibble.
+ *  scales_rm : NF4    : float [groups][N][K/64] (absmax per 64 elements)
+ *              NF4_DQ : uint8 E4M3 codes [groups][N][K/64]
+ *              MXFP4  : uint8 E8M0 codes [groups][N][K/32]
+ *              NVFP4  : uint8 E4M3 codes [groups][N][K/16]
+ *  codes, scales : outputs, lora4_packed_bytes(format, N, K, 0 / 1) bytes per
+ *              group, groups back to back; the padding is written as zero.
+ * NF4-DQ second-level scales have the same order in both layouts: the
+ * caller's float [groups][ceil(N*K/64/256)] array serves lora4_W.scales2 as
+ * it is. K % 64 == 0 for NF4 / NF4-DQ, K % 32 == 0 for MXFP4 / NVFP4.
+ * Device pointers, 16-byte aligned, input and output buffers distinct.
+ * Errors: LORA4_ERR_FORMAT, LORA4_ERR_SHAPE, LORA4_ERR_NULL, LORA4_ERR_ALIGN
+ * before anything is launched; LORA4_ERR_HIP for a failed launch. */
+lora4_status lora4_import_rowmajor(int32_t format, int64_t N, int64_t K, int64_t groups,
+                                   const uint8_t *codes_rm, const void *scales_rm,
+                                   uint8_t *codes, void *scales, void *stream);
+
 /* ---- MX-native forward of an MXFP4 base -------------------------------------
  * "Quantized weights, full precision", section "Forward pass in inference"
  * (and "Forward pass in training": the same operations in the training

@@ -28,7 +28,7 @@ BLOCK = {LORA4_NF4: 64, LORA4_NF4_DQ: 64, LORA4_MXFP4: 32, LORA4_NVFP4: 16}
 EXPORTS = ["lora4_forward", "lora4_backward", "lora4_workspace_bytes", "lora4_packed_bytes",
            "lora4_forward_multi", "lora4_backward_multi", "lora4_workspace_bytes_multi", "quant_pack_nf4",
            "quant_pack_mxfp4", "quant_pack_nvfp4", "quant_pack_mxfp8", "lora4_workspace_bytes_mx", "lora4_forward_mx",
-           "lora4_loftq_workspace_bytes", "lora4_loftq_init",
+           "lora4_loftq_workspace_bytes", "lora4_loftq_init", "lora4_import_rowmajor",
            "lora4_status_string", "lora4_timing_enable", "lora4_timing_collect", "lora4_version"]
 
 
@@ -90,6 +90,8 @@ def lib():
         L.lora4_loftq_workspace_bytes.restype = sz
         L.lora4_loftq_init.argtypes = [vp, i64, i64, i32, i32, f32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.lora4_loftq_init.restype = ctypes.c_int
+        L.lora4_import_rowmajor.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp]
+        L.lora4_import_rowmajor.restype = ctypes.c_int
         L.lora4_status_string.argtypes = [ctypes.c_int]
         L.lora4_status_string.restype = ctypes.c_char_p
         L.lora4_timing_enable.argtypes = [ctypes.c_int]
@@ -178,6 +180,10 @@ def lora4_loftq_init(W, N, K, r, iters, s, double_quant, codes, scales, scales2,
                      workspace_bytes, stream):
     return lib().lora4_loftq_init(W, N, K, r, iters, s, double_quant, codes, scales, scales2, A, B, workspace,
                                   workspace_bytes, stream)
+
+
+def lora4_import_rowmajor(fmt, N, K, groups, codes_rm, scales_rm, codes, scales, stream):
+    return lib().lora4_import_rowmajor(fmt, N, K, groups, codes_rm, scales_rm, codes, scales, stream)
 
 
 def lora4_forward_mx(W, X, M, A, B, r, s, Y, Z, workspace, workspace_bytes, stream):
@@ -368,6 +374,41 @@ def pack_nvfp4(W):
         _check(quant_pack_nvfp4(_ptr(Ws[e]), N, K, _ptr(codes[e]), _ptr(scales[e]), _stream()),
                "quant_pack_nvfp4")
     return PackedBase(LORA4_NVFP4, N, K, E, codes, scales, None)
+
+
+def import_rowmajor(fmt, codes_rm, scales_rm, scales2=None):
+    """A base already packed row-major (codes uint8 [(E,) N, K/2], scales
+    [(E,) N, K/block]: float32 for NF4, uint8 otherwise; NF4-DQ second-level
+    scales float32 [(E,) ceil(N K/64/256)]) -> a PackedBase in the library's
+    tiled storage (rearranged on the GPU, bit for bit)."""
+    import torch
+    fmt = FORMATS.get(fmt, fmt)
+    if fmt not in BLOCK:
+        raise ValueError("unknown format")
+    c = codes_rm if codes_rm.dim() == 3 else codes_rm.unsqueeze(0)
+    sc = scales_rm if scales_rm.dim() == 3 else scales_rm.unsqueeze(0)
+    E, N, half = c.shape
+    K = 2 * half
+    dev = c.device
+    _need(c, "codes", (E, N, half), torch.uint8, dev)
+    _need(sc, "scales", (E, N, K // BLOCK[fmt]), torch.float32 if fmt == LORA4_NF4 else torch.uint8, dev)
+    sizes = [lora4_packed_bytes(fmt, N, K, part) for part in range(3)]
+    if sizes[0] == 0:
+        raise ValueError("invalid shape for this format")
+    codes = torch.empty((E, sizes[0]), dtype=torch.uint8, device=dev)
+    if fmt == LORA4_NF4:
+        scales = torch.empty((E, sizes[1] // 4), dtype=torch.float32, device=dev)
+    else:
+        scales = torch.empty((E, sizes[1]), dtype=torch.uint8, device=dev)
+    s2 = None
+    if fmt == LORA4_NF4_DQ:
+        if scales2 is None:
+            raise ValueError("NF4-DQ needs its second-level scales")
+        s2 = scales2 if scales2.dim() == 2 else scales2.unsqueeze(0)
+        _need(s2, "scales2", (E, sizes[2] // 4), torch.float32, dev)
+    _check(lora4_import_rowmajor(fmt, N, K, E, _ptr(c), _ptr(sc), _ptr(codes), _ptr(scales), _stream()),
+           "lora4_import_rowmajor")
+    return PackedBase(fmt, N, K, E, codes, scales, s2)
 
 
 def workspace_for(which, base, M, r):

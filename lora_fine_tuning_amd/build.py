@@ -12,6 +12,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "liblora4.so")
 SOURCES = [os.path.join(HERE, "csrc", "lora4.hip")]   # includes every csrc/*.hpp
+# measured roofline denominators (MFMA rate, HBM read bandwidth), beside the library
+PROBE_LIB = os.path.join(HERE, "libpeakprobe.so")
+PROBE_SOURCES = [os.path.join(HERE, "csrc", "peak_probe.hip")]
 
 FLAGS = [
     "--offload-arch=gfx950",
@@ -35,17 +38,23 @@ def hipcc():
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose=False):
-    """Compile the library; returns its path. Always recompiles."""
+def _compile(sources, out, verbose):
     cmd = [hipcc(), *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-           *SOURCES, "-o", LIB + ".tmp"]
+           *sources, "-o", out + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("hipcc failed")
-    os.replace(LIB + ".tmp", LIB)
+    os.replace(out + ".tmp", out)
+
+
+def build(verbose=False):
+    """Compile the library and the peak probe; returns the library's path.
+    Always recompiles."""
+    _compile(PROBE_SOURCES, PROBE_LIB, verbose)
+    _compile(SOURCES, LIB, verbose)
     return LIB
 
 

@@ -31,8 +31,12 @@ struct Params {
   int groups;
   uint16_t *C;
   int64_t ldc;
-  int tiles_n;        // ceil(Nc / 256)
+  int tiles_n;        // output column tiles (ceil(Nc / 256); the forward's 128 x 128 kernel: ceil(Nc / 128))
   int nblocks;        // gridDim.x
+  int nslots;         // row-tile slots (tiles_n x nslots tiles in grouped order)
+  // forward, whole-tile launches: the first nfull tiles in grouped order run
+  // whole, the ntail after them as two 256 x 128 halves (blocks nfull ..)
+  int nfull, ntail;
   Nf4Table tab;
   // split reduction (forward kernel only): every tile runs in ksplit blocks
   // of split_steps 64-deep steps, which write fp32 partials

@@ -70,39 +70,24 @@ struct WRaw {
   uint32_t c2[2];   // DQ second level (fp32 bits)
 };
 
-// SPLIT: every block computes one reduction range of a split tile and writes
-// fp32 partials (else one block per tile, bf16 output). SHARED: the row
-// tiles ignore the groups (Params::shared_rows).
-template <int FMT, bool SPLIT, bool SHARED>
-__global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-
-  // Whole tiles: XCD-aware order (blocks are dealt round-robin to the 8 XCDs;
-  // renumber them so each XCD walks a contiguous range of tiles). Split
-  // tiles: block b takes range b % ksplit of tile b / ksplit.
-  int b = blockIdx.x;
-  int tile, split = 0;
-  if constexpr (!SPLIT) {
-    const int per = p.nblocks >> 3;
-    if (b < per * 8) b = (b & 7) * per + (b >> 3);
-    tile = b;
-  } else {
-    tile = b / p.ksplit;
-    split = b % p.ksplit;
-  }
+// One output tile of TBM rows x 128 NJ columns: wave w owns the 32 NJ columns
+// from col0 + 32 NJ w (NJ 32-column blocks) for all TBM rows (TBM / 32 row
+// blocks). SPLIT (TBM 256, NJ 2 only): the block computes reduction range
+// `split` of the tile and writes fp32 partials. SHARED: the row tiles ignore
+// the groups (Params::shared_rows). `tile` is the tile's index in the split
+// partials.
+template <int FMT, bool SPLIT, bool SHARED, int TBM, int NJ>
+__device__ __forceinline__ void fwd_tile(const Params &p, uint16_t *smem, int slot, int64_t col0, int tile,
+                                         int split) {
+  static_assert(!SPLIT || (TBM == BM && NJ == 2), "split partials are laid out for 256 x 256 tiles");
+  constexpr int RB = TBM / 32;       // 32-row blocks: MFMA row blocks per wave, X chunks per step
+  constexpr int WN = 32 * NJ;        // columns per wave
+  constexpr int CPS = 8 / RB;        // hand-dealt slices per MFMA row block (8 slices per sub-step)
   constexpr bool is_split = SPLIT;
-  int tn, slot;
-  if constexpr (!SPLIT) {
-    big::grouped_tile(tile, p.tiles_n, p.nblocks / p.tiles_n, slot, tn);
-  } else {
-    tn = tile % p.tiles_n;   // (the reduction of the split tiles uses this order)
-    slot = tile / p.tiles_n;
-  }
-  const RowTile rt = big::tile_rows<SHARED>(p, slot, BM);
+  const RowTile rt = big::tile_rows<SHARED>(p, slot, TBM);
   if (rt.group < 0) return;
   const int g = rt.group;
   const int64_t row0 = rt.row0, row_end = rt.row_end;
-  const int64_t col0 = (int64_t)tn * BN;
 
   const int t = threadIdx.x;
   // the wave index is uniform: keep it (and the LDS addresses derived from
@@ -131,18 +116,20 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
     const int k0 = (s + sb) * BKS;
     const bool edge = k0 + a_kq >= Ri;
 #pragma unroll
-    for (int c = 2 * part; c < 2 * part + 2; ++c)
+    for (int c = 2 * part; c < 2 * part + 2 && c < RB; ++c)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (__attribute__((address_space(3))) void *)(As + (c * 4 + wave) * 512),
                                                16, edge ? OOB : a_voff0 + c * a_cstep, (int)(k0 * 2), 0, 0);
   };
 
-  // ---- this lane's W rows: n = col0 + 64 wave + 32 j + l32, k = 32 h + .. ----
-  // The wave's 64 rows are one row block of the tiled base: per step it reads
-  // tile (rb, k0 / 64), 2048 contiguous bytes of codes (row i at 32 i) and 64
-  // or 128 contiguous scale entries. Row blocks past the base read nothing
-  // (out-of-range descriptor).
+  // ---- this lane's W rows: n = wcol0 + 32 j + l32, k = 32 h + .. ----------
+  // The wave's WN rows lie in one row block of the tiled base (from row i0 of
+  // it): per step it reads tile (rb, k0 / 64), its rows' 32 contiguous bytes of
+  // codes each (row i at 32 i) and their scale entries. Row blocks past the
+  // base read nothing (out-of-range descriptor).
   const int64_t KB = p.W.KB;
-  const int64_t rb = (col0 >> 6) + wave;
+  const int64_t wcol0 = col0 + (int64_t)wave * WN;
+  const int64_t rb = wcol0 >> 6;
+  const int i0 = (int)(wcol0 & 63);
   const bool rb_ok = rb < w_blocks(p.W.N);
   const int gw = w_group(p.W, g);   // group of W
   const uint8_t *codes_g = p.W.codes + gw * p.W.g_codes;
@@ -159,11 +146,11 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   uint32_t w_voff[2], s_voff[2];
   int64_t s_idx0[2];   // DQ: row-major index of the row's first 64-run scale
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int i = j * 32 + l32;   // row inside the row block
+  for (int j = 0; j < NJ; ++j) {
+    const int i = i0 + j * 32 + l32;   // row inside the row block
     w_voff[j] = (uint32_t)(i * 32 + h * 16);
     s_voff[j] = (uint32_t)(FMT == FMT_MXFP4 ? i * 2 + h : FMT == FMT_NVFP4 ? i * 4 + h * 2 : i * sc_bytes);
-    s_idx0[j] = (col0 + wave * 64 + i) * (p.W.K >> 6);
+    s_idx0[j] = (wcol0 + j * 32 + l32) * (p.W.K >> 6);
   }
   // per-step offsets of tile (rb, k0 / 64)
   auto w_step_off = [](int k0) { return (int)((k0 >> 6) << 11); };
@@ -173,7 +160,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   // its second-level scale for NF4-DQ); parts 2 and 3 load nothing, so every
   // W load of a step is issued in its first half, a full step ahead of use
   auto load_w = [&](int s, WRaw &w, int part) {
-    if (part >= 2) return;
+    if (part >= NJ) return;
     const int k0 = (s + sb) * BKS;
     // this lane's half lies inside the row (MXFP4 rows may end at k % 64 == 32)
     const bool half_ok = k0 + 32 * h < Ri;
@@ -192,9 +179,9 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
       w.sc[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, half_ok ? s_voff[j] : OOB, s_step_off(k0), 0);
     }
   };
-  // loads issued by load_w over a whole step, all in parts 0 and 1 (issued
-  // unconditionally, so the count is exact)
-  constexpr int W_LOADS = FMT == FMT_NF4_DQ ? 6 : 4;
+  // loads issued by load_w over a whole step, all in parts 0 .. NJ - 1
+  // (issued unconditionally, so the count is exact)
+  constexpr int W_LOADS = (FMT == FMT_NF4_DQ ? 3 : 2) * NJ;
 
   // Decode state of one row's run for a step: the NF4 table (shared by the
   // lane pair, see make_table_pair) or the MXFP4 scale. It is built a
@@ -234,18 +221,19 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
     }
   };
 
-  // acc[i][j]: rows 32 i .. +31, columns 64 wave + 32 j .. +31
-  f32x16_t acc[8][2];
+  // acc[i][j]: rows 32 i .. +31, columns WN wave + 32 j .. +31
+  f32x16_t acc[RB][NJ];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    acc[i][0] = f32x16_t{};
-    acc[i][1] = f32x16_t{};
-  }
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16_t{};
 
   // At the mid-step wait of step s, the X of step s+1 (issued during step
   // s-2) must have landed; still in flight may be everything issued during
-  // step s-1 and during sub-steps 0 and 1 of step s. lgkmcnt 0 as well.
-  constexpr int VM_OUT = (8 + W_LOADS) + (4 + W_LOADS);
+  // step s-1 and during sub-steps 0 and 1 of step s (X chunks go out two per
+  // sub-step from sub-step 0, W loads in sub-steps 0 .. NJ - 1). lgkmcnt 0 as
+  // well.
+  constexpr int VM_OUT = (RB + W_LOADS) + ((RB < 4 ? RB : 4) + W_LOADS);
   static_assert(VM_OUT < 64, "vmcnt field");
   constexpr int VMCNT = (VM_OUT & 15) | (7 << 4) | (0 << 8) | ((VM_OUT >> 4) << 14);
 
@@ -256,23 +244,24 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   // of the VALU work (decode) and of the global loads. The schedule is pinned:
   // MFMA pairs with the LDS read of the freed fragment, a global load every
   // other pair, and VALU work between them; nothing moves across sub-steps.
-  auto sub_step = [&](const WFrag &cur, int kk, u32x4_t x[8], const uint16_t *src, int chunk, bool reload,
+  auto sub_step = [&](const WFrag &cur, int kk, u32x4_t x[RB], const uint16_t *src, int chunk, bool reload,
                       auto &&hook) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      acc[i][0] = mfma_32x32x16(cur.w[0][kk], x[i], acc[i][0]);
-      acc[i][1] = mfma_32x32x16(cur.w[1][kk], x[i], acc[i][1]);
+    for (int i = 0; i < RB; ++i) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_32x32x16(cur.w[j][kk], x[i], acc[i][j]);
       if (reload) x[i] = lds_read_b128(src + swz(i * 32 + l32, chunk));
     }
     hook();
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, big::SCHED_VALU, 0);   // VALU
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+    for (int i = 0; i < RB; ++i) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, big::SCHED_VALU, 0);   // VALU
+      }
       if (reload) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // LDS read
       if (i & 1) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);       // global load
-      __builtin_amdgcn_sched_group_barrier(0x002, big::SCHED_VALU, 0);   // VALU
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -392,56 +381,63 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
       }
     }
   };
-  auto sub_step_s = [&](const WFrag &cur, int kk, u32x4_t x[8], const uint16_t *src, int chunk, auto &&slice) {
+  // (a row block's MFMAs carry CPS consecutive slices of the sub-step's 8,
+  // so the work dealt per step is the same for every tile shape)
+  auto sub_step_s = [&](const WFrag &cur, int kk, u32x4_t x[RB], const uint16_t *src, int chunk, auto &&slice) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      acc[i][0] = mfma_32x32x16(cur.w[0][kk], x[i], acc[i][0]);
-      acc[i][1] = mfma_32x32x16(cur.w[1][kk], x[i], acc[i][1]);
+    for (int i = 0; i < RB; ++i) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_32x32x16(cur.w[j][kk], x[i], acc[i][j]);
       x[i] = lds_read_b128(src + swz(i * 32 + l32, chunk));
-      slice(i);
+#pragma unroll
+      for (int c = 0; c < CPS; ++c) slice(i * CPS + c);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, SLICE_V1, 0);    // VALU
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, SLICE_V1, 0);          // VALU
+      if (NJ > 1) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                 // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);                 // global load
-      __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);                // VALU
+      __builtin_amdgcn_sched_group_barrier(0x010, 2 * CPS, 0);           // global load
+      __builtin_amdgcn_sched_group_barrier(0x002, 32 * CPS, 0);          // VALU
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   auto body_s = [&](int s, const uint16_t *cur, const uint16_t *nxt, uint16_t *ahead, const WRaw &rdec,
-                    WRaw &rload, const WFrag &fcur, WFrag &fnxt, u32x4_t x[8], RunDec &d0) {
+                    WRaw &rload, const WFrag &fcur, WFrag &fnxt, u32x4_t x[RB], RunDec &d0) {
     RunDec d1{};
     RunBuild rb;
     WordDec wd[2];
+    // X chunks c < RB of step s + 3 go out two per sub-step, from sub-step 0
+    auto x_chunk = [&](int c) {
+      if (c < RB) issue_a1(s + 3, ahead, c);
+    };
     sub_step_s(fcur, 0, x, cur, h * 4 + 1, [&](int i) {
       dec_slice(i, rdec, fnxt, d0, 0, 0, wd);
       if (i == 0) load_w_scale(s + 2, rload, 0);
-      if (i == 2) issue_a1(s + 3, ahead, 0);
+      if (i == 2) x_chunk(0);
       if (i == 4) load_w_codes(s + 2, rload, 0);
-      if (i == 6) issue_a1(s + 3, ahead, 1);
+      if (i == 6) x_chunk(1);
     });
     sub_step_s(fcur, 1, x, cur, h * 4 + 2, [&](int i) {
       dec_slice(i, rdec, fnxt, d0, 0, 2, wd);
-      run_slice(i, rdec, 1, rb, d1);
-      if (i == 0) load_w_scale(s + 2, rload, 1);
-      if (i == 2) issue_a1(s + 3, ahead, 2);
-      if (i == 4) load_w_codes(s + 2, rload, 1);
-      if (i == 6) issue_a1(s + 3, ahead, 3);
+      if (NJ > 1) run_slice(i, rdec, 1, rb, d1);
+      if (NJ > 1 && i == 0) load_w_scale(s + 2, rload, 1);
+      if (i == 2) x_chunk(2);
+      if (NJ > 1 && i == 4) load_w_codes(s + 2, rload, 1);
+      if (i == 6) x_chunk(3);
     });
     __builtin_amdgcn_s_waitcnt(VMCNT);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     sub_step_s(fcur, 2, x, cur, h * 4 + 3, [&](int i) {
-      dec_slice(i, rdec, fnxt, d1, 1, 0, wd);
-      if (i == 2) issue_a1(s + 3, ahead, 4);
-      if (i == 6) issue_a1(s + 3, ahead, 5);
+      if (NJ > 1) dec_slice(i, rdec, fnxt, d1, 1, 0, wd);
+      if (i == 2) x_chunk(4);
+      if (i == 6) x_chunk(5);
     });
     sub_step_s(fcur, 3, x, nxt, h * 4 + 0, [&](int i) {
-      dec_slice(i, rdec, fnxt, d1, 1, 2, wd);
+      if (NJ > 1) dec_slice(i, rdec, fnxt, d1, 1, 2, wd);
       run_slice(i, rload, 0, rb, d0);
-      if (i == 2) issue_a1(s + 3, ahead, 6);
-      if (i == 6) issue_a1(s + 3, ahead, 7);
+      if (i == 2) x_chunk(6);
+      if (i == 6) x_chunk(7);
     });
   };
 
@@ -449,7 +445,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   const int steps = is_split ? min(all_steps - sb, p.split_steps) : all_steps;
   WRaw r0, r1;
   WFrag f0, f1;
-  u32x4_t x[8];
+  u32x4_t x[RB];
   // ring of five stages; step s uses stage s % 5
   auto stage = [&](int i) -> uint16_t * { return smem + (i >= STAGES ? i - STAGES : i) * TILE; };
 #pragma unroll
@@ -471,7 +467,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
     uint16_t *As = stage(4);
     const bool a_vec = (p.A2.ld % 8) == 0;
     const bool b_vec = (p.B2.ld % 8) == 0;
-    const int64_t row_hi = min(row0 + BM, row_end);
+    const int64_t row_hi = min(row0 + TBM, row_end);
     big::TileGroups tg{g, 1, p.r2};
     int my = 0;
     if constexpr (SHARED) {
@@ -485,8 +481,8 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
       const int nkk = min(4, (rc - k0 + 7) / 8);
       WFrag bt;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int64_t n = col0 + wave * 64 + j * 32 + l32;
+      for (int j = 0; j < NJ; ++j) {
+        const int64_t n = wcol0 + j * 32 + l32;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const int kc = k0 + 32 * h + 8 * kk;
@@ -511,13 +507,14 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
         }
       }
       if (p.A2part) {
-        big::a2_parts_to_lds<SHARED>(p, As, [](int i, int c) { return swz(i, c); }, row0, row_hi, k0, t, col0 == 0,
-                                     tg.rp, my);
+        if (t < TBM)
+          big::a2_parts_to_lds<SHARED>(p, As, [](int i, int c) { return swz(i, c); }, row0, row_hi, k0, t,
+                                       col0 == 0, tg.rp, my);
       } else if constexpr (SHARED) {
-        big::a2_rows_to_lds(p, As, [](int i, int c) { return swz(i, c); }, row0, row_hi, k0, t, tg.rp, my);
+        if (t < TBM) big::a2_rows_to_lds(p, As, [](int i, int c) { return swz(i, c); }, row0, row_hi, k0, t, tg.rp, my);
       } else {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
+        for (int c = 0; c < RB; ++c) {
           const int idx = t + THREADS * c;
           const int row = idx >> 3, chunk = idx & 7;
           u32x4_t v = {0u, 0u, 0u, 0u};
@@ -538,9 +535,9 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
         }
       }
       __syncthreads();
-      u32x4_t xt[8];
+      u32x4_t xt[RB];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) xt[i] = lds_read_b128(As + swz(i * 32 + l32, h * 4));
+      for (int i = 0; i < RB; ++i) xt[i] = lds_read_b128(As + swz(i * 32 + l32, h * 4));
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
         if (kk < nkk) sub_step(bt, kk, xt, As, h * 4 + kk + 1, kk < 3, [] {});
@@ -549,7 +546,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   }
 
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < NJ; ++j) {
     const RunDec d = make_run(r0, j);
     decode_words(r0, f0, d, j, 0);
     decode_words(r0, f0, d, j, 2);
@@ -560,7 +557,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   __syncthreads();
   RunDec d0 = make_run(r1, 0);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] = lds_read_b128(stage(0) + swz(i * 32 + l32, h * 4));
+  for (int i = 0; i < RB; ++i) x[i] = lds_read_b128(stage(0) + swz(i * 32 + l32, h * 4));
   int s = 0, si = 0;   // si = s % 5
   for (; s + 2 <= steps; s += 2) {
     body_s(s, stage(si), stage(si + 1), stage(si + 3), r1, r0, f0, f1, x, d0);
@@ -580,7 +577,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
     // the output are written too and ignored by the reduction)
     float *pt = p.Cpart + ((int64_t)tile * p.ksplit + split) * (BM * BN);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < RB; ++i) {
       float *prow = pt + (i * 32 + l32) * BN;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -594,16 +591,19 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
     }
     return;
   }
-  // Each wave stages its 256 x 64 bf16 block in LDS (free now; 32 KB per wave,
-  // tile64 layout) and writes it back as 8 whole 128-byte row segments per
-  // store instruction (element stores where a row segment is cut by the
-  // output's edge or the rows are not 16-byte aligned).
+  // Each wave stages its TBM x WN bf16 block in LDS (free now; tile64 layout,
+  // chunks 0 .. 4 NJ - 1 of each row) and writes it back as whole row
+  // segments of 16 NJ lanes per store instruction (element stores where a
+  // row segment is cut by the output's edge or the rows are not 16-byte
+  // aligned).
   {
-    uint16_t *stg = smem + wave * (BM * 64);
+    constexpr int CH = 4 * NJ;           // 16-byte chunks per staged row
+    constexpr int RPI = 64 / CH;         // rows per store instruction
+    uint16_t *stg = smem + wave * (TBM * 64);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < RB; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const u32x2_t pk = {pack_bf16x2(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1]),
@@ -612,11 +612,11 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
         }
     const bool vec16 = (p.ldc % 8) == 0;
 #pragma unroll 4
-    for (int q = 0; q < 32; ++q) {
-      const int row = q * 8 + (lane >> 3), chunk = lane & 7;
+    for (int q = 0; q < TBM / RPI; ++q) {
+      const int row = q * RPI + lane / CH, chunk = lane % CH;
       const u32x4_t v = lds_read_b128(stg + tile64_swz(row, chunk));
       const int64_t grow = row0 + row;
-      const int64_t gcol = col0 + wave * 64 + chunk * 8;
+      const int64_t gcol = wcol0 + chunk * 8;
       if (grow < row_end && gcol < p.Nc) {
         uint16_t *dst = p.C + grow * p.ldc + gcol;
         if (vec16 && gcol + 8 <= p.Nc) {
@@ -627,6 +627,51 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
       }
     }
   }
+}
+
+// Full 256 x 256 tiles (blocks below p.nfull, in grouped tile order, each XCD
+// walking a contiguous range of them) and, after them, the last p.ntail tiles
+// of that order as two 256 x 128 halves each: when the full tiles leave a
+// last round that fills half the GPU or less, its tiles run as twice as many
+// half tiles, one round in about half the time. SPLIT: block b computes range
+// b % ksplit of tile b / ksplit (no halves).
+template <int FMT, bool SPLIT, bool SHARED>
+__global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  int b = blockIdx.x;
+  if constexpr (SPLIT) {
+    const int tile = b / p.ksplit;
+    const int tn = tile % p.tiles_n, slot = tile / p.tiles_n;   // (the reduction of the split tiles uses this order)
+    fwd_tile<FMT, true, SHARED, BM, 2>(p, smem, slot, (int64_t)tn * BN, tile, b % p.ksplit);
+  } else {
+    int slot, tn;
+    if (b < p.nfull) {
+      const int per = p.nfull >> 3;
+      if (b < per * 8) b = (b & 7) * per + (b >> 3);
+      big::grouped_tile(b, p.tiles_n, p.nslots, slot, tn);
+      fwd_tile<FMT, false, SHARED, BM, 2>(p, smem, slot, (int64_t)tn * BN, b, 0);
+    } else {
+      int u = b - p.nfull;
+      const int per = (2 * p.ntail) >> 3;
+      if (u < per * 8) u = (u & 7) * per + (u >> 3);
+      big::grouped_tile(p.nfull + (u >> 1), p.tiles_n, p.nslots, slot, tn);
+      fwd_tile<FMT, false, SHARED, BM, 1>(p, smem, slot, (int64_t)tn * BN + (u & 1) * (BN / 2), 0, 0);
+    }
+  }
+}
+
+// 128 x 128 tiles, for outputs whose 256 x 256 tiles would fill too little of
+// the GPU (e.g. 4096 x 1024: 64 tiles, 256 of these). p.tiles_n counts
+// 128-column tiles and p.nslots 128-row slots.
+template <int FMT, bool SHARED>
+__global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd_small(Params p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  int b = blockIdx.x;
+  const int per = p.nblocks >> 3;
+  if (b < per * 8) b = (b & 7) * per + (b >> 3);
+  int slot, tn;
+  big::grouped_tile(b, p.tiles_n, p.nslots, slot, tn);
+  fwd_tile<FMT, false, SHARED, 128, 1>(p, smem, slot, (int64_t)tn * 128, b, 0);
 }
 
 // C[tile rows][tile columns] = bf16(sum_k part[t][k][r][c]) for the split

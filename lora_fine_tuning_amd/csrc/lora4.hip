@@ -282,12 +282,15 @@ int skinny_tile(int r) { return r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : 128
 
 // Forward base GEMM schedule (defined with the large-tile dispatch below).
 struct FwdSched {
-  bool use;          // register-direct kernel (else the 128 x 128 kernel)
-  int whole_tiles;   // tiles computed by one block each (the first ones)
-  int split_tiles;   // tiles after them, each split over ksplit blocks
+  bool use;          // register-direct kernels (else the 128 x 128 LDS kernel)
+  int whole_tiles;   // 256 x 256 tiles computed by one block each (the first ones)
+  int split_tiles;   // or: tiles each split over ksplit blocks
   int ksplit;        // reduction splits of a split tile
   int split_steps;   // 64-deep steps per split
+  int tail_tiles;    // 256 x 256 tiles after the whole ones, run as two 256 x 128 halves
+  bool small;        // or: 128 x 128 tiles (k_gemm_fwd_small)
 };
+constexpr FwdSched FWD_LDS_KERNEL{false, 0, 0, 1, 1 << 30, 0, false};
 FwdSched fwd_sched(int64_t M, int64_t N, int64_t K, int64_t E, const PackedW &W);
 struct SkSched;
 size_t sk_part_bytes_for(int64_t M, int64_t R, int r, int64_t E);
@@ -404,42 +407,67 @@ int cu_count() {
   return cached[dev];
 }
 
-// The register-direct forward kernel runs one 256 x 256 tile per CU at a
-// time. Outputs with fewer tiles than ~3/4 of the CUs split the reduction of
-// every tile over several blocks (fp32 partials, at least 8 steps per split,
-// partials capped at 256 MiB), summed by a deterministic reduction. (Splitting
-// only the tiles of a half-empty last round, e.g. 896 tiles on 256 CUs, was
-// measured: the GEMM gains what the extra reduction launch costs.) The
-// automatic policy keeps the 128 x 128 kernel when even a split grid would
-// leave most of the GPU idle.
+// Forced forward tile shapes for tests and measurements (LORA4_FWD_TILES):
+// "small" (128 x 128 tiles), "half" (every 256 x 256 tile as two halves),
+// "mixed" (the second half of the tiles as halves), "whole" (256 x 256 tiles
+// only, no halves); anything else or unset: automatic.
+int fwd_tiles_policy() {
+  const char *e = std::getenv("LORA4_FWD_TILES");
+  if (!e) return 0;
+  const std::string v(e);
+  return v == "small" ? 1 : v == "half" ? 2 : v == "mixed" ? 3 : v == "whole" ? 4 : 0;
+}
+
+// The register-direct forward kernels run one tile per CU at a time:
+// * enough 256 x 256 tiles for 3/4 of the CUs: whole tiles, except that when
+//   the last round would fill half the CUs or less (e.g. 896 tiles on 256
+//   CUs: 3.5 rounds), its tiles run as two 256 x 128 halves each, a full
+//   round of half the length;
+// * else, enough 128 x 128 tiles for 3/4 of the CUs (e.g. 4096 x 1024: 64 of
+//   256 x 256, 256 of 128 x 128): those;
+// * else the reduction of every 256 x 256 tile is split over several blocks
+//   (fp32 partials, at least 8 steps per split, partials capped at 256 MiB),
+//   summed by a deterministic reduction.
+// The automatic policy keeps the 128 x 128 LDS kernel when even a split grid
+// would leave most of the GPU idle.
 FwdSched fwd_sched(int64_t M, int64_t N, int64_t K, int64_t E, const PackedW &W) {
-  FwdSched f{false, 0, 0, 1, 1 << 30};
+  FwdSched f = FWD_LDS_KERNEL;
   if (K <= 0 || M <= 0 || !big_fits(K, M, W)) return f;
   const int pol = big_policy();
   if (pol == 0) return f;
+  const int force = fwd_tiles_policy();
   const int64_t cus = cu_count();
-  const int64_t tiles = (ceil_div(M, fwd::BM) + (E > 1 && !W.shared ? E : 0)) * ceil_div(N, fwd::BN);
+  const int64_t groups = E > 1 && !W.shared ? E : 0;
+  const int64_t tiles = (ceil_div(M, fwd::BM) + groups) * ceil_div(N, fwd::BN);
+  const int64_t tiles128 = (ceil_div(M, 128) + groups) * ceil_div(N, 128);
+  f.use = true;
+  if (force == 1 || (force == 0 && tiles < cus * 3 / 4 && tiles128 >= cus * 3 / 4)) {
+    f.small = true;
+    return f;
+  }
+  if (force >= 2 || tiles >= cus * 3 / 4) {
+    const int64_t rem = tiles % cus;
+    int64_t tail = 0;
+    if (force == 2) tail = tiles;
+    else if (force == 3) tail = tiles / 2;
+    else if (force == 0 && tiles > cus && rem > 0 && rem <= cus / 2) tail = rem;
+    f.whole_tiles = (int)(tiles - tail);
+    f.tail_tiles = (int)tail;
+    return f;
+  }
   const int64_t steps = ceil_div(K, fwd::BKS);
   const int64_t max_ks = std::min<int64_t>(16, std::max<int64_t>(1, steps / 8));
-  int64_t whole = tiles, split = 0, ks = 1;
-  if (tiles < cus * 3 / 4) {
-    ks = std::min<int64_t>(cus / tiles, max_ks);
-    const int64_t cap = ((int64_t)256 << 20) / ((int64_t)fwd::BM * fwd::BN * 4 * tiles);
-    ks = std::max<int64_t>(1, std::min(ks, cap));
-    if (ks > 1) {
-      whole = 0;
-      split = tiles;
-    }
+  int64_t ks = std::min<int64_t>(cus / tiles, max_ks);
+  const int64_t cap = ((int64_t)256 << 20) / ((int64_t)fwd::BM * fwd::BN * 4 * tiles);
+  ks = std::max<int64_t>(1, std::min(ks, cap));
+  if (pol < 0 && tiles * ks < cus * 3 / 4) return FWD_LDS_KERNEL;
+  if (ks == 1) {
+    f.whole_tiles = (int)tiles;
+    return f;
   }
-  if (pol < 0 && whole + split * ks < cus * 3 / 4) return f;
-  f.use = true;
-  f.whole_tiles = (int)whole;
-  f.split_tiles = (int)split;
-  f.ksplit = (int)ks;
-  if (split > 0) {
-    f.split_steps = (int)ceil_div(steps, ks);
-    f.ksplit = (int)ceil_div(steps, f.split_steps);
-  }
+  f.split_tiles = (int)tiles;
+  f.split_steps = (int)ceil_div(steps, ks);
+  f.ksplit = (int)ceil_div(steps, f.split_steps);
   return f;
 }
 
@@ -452,7 +480,10 @@ bool use_big(int64_t M, int64_t Nc, int64_t E) {
 
 // Forward base GEMM with deq(W) decoded straight into MFMA registers.
 template <int FMT, bool SHARED>
-lora4_status run_fwd(const big::Params &p, hipStream_t st) {
+lora4_status run_fwd(const big::Params &p, bool small, hipStream_t st) {
+  if (small)
+    return launch_lds("gemm_nt_base", fwd::k_gemm_fwd_small<FMT, SHARED>, dim3((unsigned)p.nblocks),
+                      dim3(fwd::THREADS), (size_t)fwd::lds_bytes(), p, st);
   if (p.ksplit > 1)
     return launch_lds("gemm_nt_base", fwd::k_gemm_fwd<FMT, true, SHARED>, dim3((unsigned)p.nblocks),
                       dim3(fwd::THREADS), (size_t)fwd::lds_bytes(), p, st);
@@ -461,16 +492,16 @@ lora4_status run_fwd(const big::Params &p, hipStream_t st) {
 }
 
 template <int FMT>
-lora4_status run_fwd(const big::Params &p, hipStream_t st) {
-  return p.shared_rows ? run_fwd<FMT, true>(p, st) : run_fwd<FMT, false>(p, st);
+lora4_status run_fwd(const big::Params &p, bool small, hipStream_t st) {
+  return p.shared_rows ? run_fwd<FMT, true>(p, small, st) : run_fwd<FMT, false>(p, small, st);
 }
 
-lora4_status run_fwd_fmt(int fmt, const big::Params &p, hipStream_t st) {
+lora4_status run_fwd_fmt(int fmt, const big::Params &p, bool small, hipStream_t st) {
   switch (fmt) {
-    case LORA4_NF4: return run_fwd<FMT_NF4>(p, st);
-    case LORA4_NF4_DQ: return run_fwd<FMT_NF4_DQ>(p, st);
-    case LORA4_MXFP4: return run_fwd<FMT_MXFP4>(p, st);
-    case LORA4_NVFP4: return run_fwd<FMT_NVFP4>(p, st);
+    case LORA4_NF4: return run_fwd<FMT_NF4>(p, small, st);
+    case LORA4_NF4_DQ: return run_fwd<FMT_NF4_DQ>(p, small, st);
+    case LORA4_MXFP4: return run_fwd<FMT_MXFP4>(p, small, st);
+    case LORA4_NVFP4: return run_fwd<FMT_NVFP4>(p, small, st);
   }
   return LORA4_ERR_FORMAT;
 }
@@ -514,7 +545,10 @@ big::Params big_params(const Mat &A, const PackedW &W, int64_t R, const Mat &A2,
   // one W for every group: the row tiles run over all M rows, regardless of
   // the groups (which then only select the rank-r operands)
   p.shared_rows = W.shared && E > 1 ? 1 : 0;
-  p.nblocks = (int)((ceil_div(std::max<int64_t>(M, 1), big::BM) + (E > 1 && !p.shared_rows ? E : 0)) * p.tiles_n);
+  p.nslots = (int)(ceil_div(std::max<int64_t>(M, 1), big::BM) + (E > 1 && !p.shared_rows ? E : 0));
+  p.nblocks = p.nslots * p.tiles_n;
+  p.nfull = p.nblocks;
+  p.ntail = 0;
   p.tab = nf4_table();
   p.ksplit = 1;
   p.split_steps = 1 << 30;
@@ -564,9 +598,17 @@ lora4_status run_nt_main_fmt(int fmt, const NtParams &p, dim3 grid, const Plan &
     apply_tail_parts(q, tp);
     q.ksplit = pl.fs.ksplit;
     q.split_steps = pl.fs.split_steps;
-    q.nblocks = pl.fs.whole_tiles + pl.fs.split_tiles * pl.fs.ksplit;
+    if (pl.fs.small) {
+      q.tiles_n = (int)ceil_div(q.Nc, 128);
+      q.nslots = (int)(ceil_div(std::max<int64_t>(q.M, 1), 128) + (q.groups > 1 && !q.shared_rows ? q.groups : 0));
+      q.nblocks = q.nslots * q.tiles_n;
+    } else {
+      q.nfull = pl.fs.whole_tiles;
+      q.ntail = pl.fs.tail_tiles;
+      q.nblocks = pl.fs.whole_tiles + 2 * pl.fs.tail_tiles + pl.fs.split_tiles * pl.fs.ksplit;
+    }
     q.Cpart = party;
-    TRY(run_fwd_fmt(fmt, q, st));
+    TRY(run_fwd_fmt(fmt, q, pl.fs.small, st));
     if (pl.fs.split_tiles > 0) {
       const int64_t n = (int64_t)pl.fs.split_tiles * fwd::BM * (fwd::BN / 4);
       TRY(launch_args("reduce_y", fwd::k_reduce_tiles, dim3((unsigned)ceil_div(n, 256)), dim3(256), st, q,
@@ -738,7 +780,7 @@ lora4_status check_common(const Base &b, int64_t M, int32_t r, float s, const in
 // Split schedule of the MX GEMM: the same rule as the bf16 forward's (few
 // output tiles split the reduction), without its choice of tile path.
 FwdSched mx_sched(int64_t M, int64_t N, int64_t K) {
-  FwdSched f{true, 0, 0, 1, 1 << 30};
+  FwdSched f{true, 0, 0, 1, 1 << 30, 0, false};
   const int64_t cus = cu_count();
   const int64_t tiles = ceil_div(std::max<int64_t>(M, 1), mx::BM) * ceil_div(N, mx::BN);
   const int64_t steps = ceil_div(K, mx::BKS);
@@ -1279,6 +1321,32 @@ lora4_status quant_pack_mxfp4(const uint16_t *W_bf16, int64_t N, int64_t K, uint
   const int64_t nblk = N * (K / 32);
   return launch_args("quant_pack_mxfp4", k_quant_mxfp4, dim3((unsigned)ceil_div(nblk, 256)), dim3(256), st,
                      W_bf16, N, K, codes, scales_e8m0);
+}
+
+lora4_status lora4_import_rowmajor(int32_t format, int64_t N, int64_t K, int64_t groups, const uint8_t *codes_rm,
+                                   const void *scales_rm, uint8_t *codes, void *scales, void *stream) {
+  if (format != LORA4_NF4 && format != LORA4_NF4_DQ && format != LORA4_MXFP4 && format != LORA4_NVFP4)
+    return LORA4_ERR_FORMAT;
+  const int64_t kmul = format == LORA4_NF4 || format == LORA4_NF4_DQ ? 64 : 32;
+  if (N < 1 || K < kmul || K % kmul != 0 || groups < 1 || groups > 65535 || N > (int64_t(1) << 31) ||
+      K > (int64_t(1) << 31))
+    return LORA4_ERR_SHAPE;
+  if (!codes_rm || !scales_rm || !codes || !scales) return LORA4_ERR_NULL;
+  if (!aligned16(codes_rm) || !aligned16(scales_rm) || !aligned16(codes) || !aligned16(scales))
+    return LORA4_ERR_ALIGN;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int64_t nc = groups * w_blocks(N) * w_blocks(K) * 128;   // 16-byte pieces of codes
+  TRY(launch_args("import_codes", k_retile_codes, dim3((unsigned)ceil_div(nc, 256)), dim3(256), st, codes_rm, N,
+                  K, groups, codes));
+  const int epr = format == LORA4_MXFP4 ? 2 : format == LORA4_NVFP4 ? 4 : 1;
+  const int64_t ns = groups * w_blocks(N) * w_blocks(K) * 64 * epr;
+  const dim3 grid((unsigned)ceil_div(ns, 256));
+  if (format == LORA4_NF4)
+    return launch_args("import_scales", k_retile_scales<float>, grid, dim3(256), st,
+                       reinterpret_cast<const float *>(scales_rm), N, K, groups, epr, reinterpret_cast<float *>(scales));
+  return launch_args("import_scales", k_retile_scales<uint8_t>, grid, dim3(256), st,
+                     reinterpret_cast<const uint8_t *>(scales_rm), N, K, groups, epr,
+                     reinterpret_cast<uint8_t *>(scales));
 }
 
 lora4_status quant_pack_mxfp8(const uint16_t *X, int64_t M, int64_t K, uint8_t *codes, uint8_t *scales_e8m0,

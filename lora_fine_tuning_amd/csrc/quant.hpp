@@ -263,4 +263,50 @@ __global__ void k_quant_nvfp4(const uint16_t *W, int64_t N, int64_t K, uint8_t *
   e4m3[w_scale16_idx(KB, n, b * 16)] = (uint8_t)sc;
 }
 
+// ---------------------------------------------------------------------------
+// A base that ships already packed, in row-major order, into the tiled
+// storage: codes [groups][N][K/2] and first-level scales [groups][N][K/block]
+// rearranged bit for bit (padding written as zero). K % 32 == 0, so a 16-byte
+// piece of a row's codes is either whole inside the row or past its end.
+// ---------------------------------------------------------------------------
+
+// One thread per 16-byte piece c of the output: tile c / 128, row (c / 2) % 64,
+// half c % 2.
+__global__ void k_retile_codes(const uint8_t *src, int64_t N, int64_t K, int64_t groups, uint8_t *dst) {
+  const int64_t KB = w_blocks(K);
+  const int64_t per_group = w_blocks(N) * KB * 128;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= groups * per_group) return;
+  const int64_t g = idx / per_group;
+  const int64_t c = idx - g * per_group;
+  const int64_t t = c >> 7;
+  const int64_t rb = t / KB, kb = t - rb * KB;
+  const int64_t n = rb * 64 + ((c >> 1) & 63);
+  const int64_t byte0 = kb * 32 + (c & 1) * 16;
+  const int64_t row_bytes = K >> 1;
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (n < N && byte0 < row_bytes) v = *reinterpret_cast<const u32x4_t *>(src + (g * N + n) * row_bytes + byte0);
+  *reinterpret_cast<u32x4_t *>(dst + idx * 16) = v;
+}
+
+// One thread per scale entry of the output; a tile holds epr entries per row
+// (1: NF4 and NF4-DQ, 2: MXFP4, 4: NVFP4), row i's at epr i .. epr i + epr - 1,
+// entry q of row n of tile (rb, kb) being row-major column kb epr + q.
+template <typename T>
+__global__ void k_retile_scales(const T *src, int64_t N, int64_t K, int64_t groups, int epr, T *dst) {
+  const int64_t KB = w_blocks(K);
+  const int64_t per_tile = 64 * epr;
+  const int64_t per_group = w_blocks(N) * KB * per_tile;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= groups * per_group) return;
+  const int64_t g = idx / per_group;
+  const int64_t e = idx - g * per_group;
+  const int64_t t = e / per_tile, within = e - t * per_tile;
+  const int64_t rb = t / KB, kb = t - rb * KB;
+  const int64_t n = rb * 64 + within / epr;
+  const int64_t col = kb * epr + within % epr;
+  const int64_t cols = K * epr / 64;
+  dst[idx] = (n < N && col < cols) ? src[(g * N + n) * cols + col] : T(0);
+}
+
 }  // namespace lora4

@@ -246,3 +246,16 @@ def test_loftq_validation(lib):
     assert init(A=4100) == EALIGN
     assert init(ws=None) == EWS
     assert init(nbytes=need - 1) == EWS
+
+
+def test_import_rowmajor_validation(lib):
+    imp = L.lora4_import_rowmajor
+    assert imp(9, 64, 64, 1, 256, 256, 256, 256, None) == EFORMAT
+    assert imp(1, 64, 96, 1, 256, 256, 256, 256, None) == ESHAPE        # NF4: K % 64
+    assert imp(3, 64, 48, 1, 256, 256, 256, 256, None) == ESHAPE        # MXFP4: K % 32
+    assert imp(3, 0, 64, 1, 256, 256, 256, 256, None) == ESHAPE
+    assert imp(3, 64, 64, 0, 256, 256, 256, 256, None) == ESHAPE
+    assert imp(1, 64, 64, 1, None, 256, 256, 256, None) == ENULL
+    assert imp(1, 64, 64, 1, 256, 256, 256, None, None) == ENULL
+    assert imp(1, 64, 64, 1, 256, 258, 256, 256, None) == EALIGN
+    assert imp(4, 64, 64, 1, 256, 256, 264, 256, None) == EALIGN

@@ -80,3 +80,42 @@ def test_five_iterations_match_the_oracle_error(dq):
     print("[loftq5]", naive, e_ref, e_gpu, flush=True)
     assert abs(e_gpu - e_ref) <= 0.02 * e_ref
     assert e_gpu < 0.95 * naive
+
+
+def test_llama8b_base_shapes():
+    """Bases of the Llama-3-8B-shaped set at their full size: the k projection
+    (1024 x 4096) through the five-iteration loop against the oracle's error,
+    and the q projection (4096 x 4096) through one iteration against the
+    Eckart-Young optimum of its NF4 residual."""
+    import synth
+    lay_k = synth.layers(2)[1]
+    Wk = synth.inputs(lay_k, names=("W",))["W"]
+    print_case("loftq 8b k", Wk.shape)
+    base, A, B = L.loftq_init(to_dev(Wk), lay_k.r, iters=5, s=lay_k.s)
+    torch.cuda.synchronize()
+    N, K = Wk.shape
+    rows = np.arange(N)
+    from gpu_util import untile_rows
+    codes = untile_rows(base.codes[0].cpu().numpy(), N, K, rows, 32)
+    scv = untile_rows(base.scales[0].cpu().numpy().view(np.float32), N, K, rows, 1)
+    Q = bf16_to_f32(nf4.dequantize(codes, scv)).astype(np.float64)
+    W = f64(Wk)
+    e_gpu = np.linalg.norm(W - Q - lay_k.s * f64(to_host(B)) @ f64(to_host(A)))
+    _, _, _, e_ref = loftq.loftq_nf4(Wk, lay_k.r, iters=5, s=lay_k.s)
+    print("[loftq 8b k]", e_ref, e_gpu, flush=True)
+    assert abs(e_gpu - e_ref) <= 0.02 * e_ref
+
+    lay_q = synth.layers(2)[0]
+    Wq = synth.inputs(lay_q, names=("W",))["W"]
+    print_case("loftq 8b q", Wq.shape)
+    base, A, B = L.loftq_init(to_dev(Wq), lay_q.r, iters=1, s=1.0)
+    torch.cuda.synchronize()
+    c, sc = nf4.quantize(Wq)
+    N, K = Wq.shape
+    assert np.array_equal(base.codes[0].cpu().numpy(), tile_codes(c, N, K))
+    R = f64(Wq) - bf16_to_f32(nf4.dequantize(c, sc)).astype(np.float64)
+    S = np.linalg.svd(R, compute_uv=False)
+    e_opt = np.sqrt(np.sum(S[lay_q.r:] ** 2))
+    e_gpu = np.linalg.norm(R - f64(to_host(B)) @ f64(to_host(A)))
+    print("[loftq 8b q]", e_opt, e_gpu, flush=True)
+    assert e_gpu <= e_opt * (1 + 5e-3)

@@ -10,20 +10,16 @@ import torch
 import lora_fine_tuning_amd as L
 import synth
 from oracle import lora
-from gpu_util import DEV, TOL, dequant_cols, dequant_rows, f64, pack_gpu, print_case, rel, to_dev, to_host
+from gpu_util import (DEV, TILE_PATHS, TOL, dequant_cols, dequant_rows, f64, pack_gpu, print_case, rel, set_tiles,
+                      to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(params=["auto", "big", "small"])
+@pytest.fixture(params=TILE_PATHS)
 def tiles(request, monkeypatch):
-    if request.param == "big":
-        monkeypatch.setenv("LORA4_BIG", "1")
-    elif request.param == "small":
-        monkeypatch.setenv("LORA4_BIG", "0")
-    else:
-        monkeypatch.delenv("LORA4_BIG", raising=False)
-    return request.param
+    """Runs a test on each tile path of the library (gpu_util.set_tiles)."""
+    return set_tiles(monkeypatch, request.param)
 
 
 def _case(fmt, M, K, N, r, offs, index):

@@ -11,7 +11,7 @@ module states).
 * Y and Z against the oracle within the relative Frobenius bar on ragged
   shapes (M, N off the tiles, K % 64 == 32, several ranks), few-tile outputs
   (split reduction) and long reductions (rank-r range partials in the GEMM);
-* a full 70B-size layer on sampled rows and columns.
+* every layer of the 70B set at full size, every element.
 """
 
 import numpy as np
@@ -21,7 +21,8 @@ import torch
 import lora_fine_tuning_amd as L
 import synth
 from oracle import codecs, lora, mxfp4, mxfp8
-from gpu_util import DEV, TOL, f64, pack_gpu, print_case, rel, to_dev, to_host
+from gpu_util import (DEV, TOL, compare_full, f64, guarded, oracle_pack_full, pack_gpu, print_case, rel,
+                      to_dev, to_host, write_report)
 
 pytestmark = pytest.mark.gpu
 
@@ -131,22 +132,36 @@ def test_mx_forward_repeatable_and_m0():
     assert e["Y"].shape == (0, 384)
 
 
-def test_mx_forward_full_size_sampled():
-    """4096 tokens through an 8192 -> 28672 MXFP4 layer (the 70B gate/up
-    shape), checked on sampled rows and columns; W comes from the seeded layer
-    generator of the 70B workload."""
-    lay = [l for l in synth.layers(3) if l.K == 8192 and l.N == 28672][0]
-    t = synth.inputs(lay)
+@pytest.mark.parametrize("i", [0, 1, 2])
+def test_mx_forward_full_size(i):
+    """Every layer of the Llama-70B-shaped MXFP4 set (8192 tokens) through the
+    MX-native forward, every element of Y and Z against the MX oracle (the
+    element bound of gpu_util), outputs and workspace between guard bands."""
+    lay = synth.layers(3)[i]
+    t = synth.inputs(lay, names=("X", "W", "A", "B"))
     M, K, N, r = lay.M, lay.K, lay.N, lay.r
     print_case("mx full", lay.name, M, K, N, r)
     base = pack_gpu(t["W"], synth.MXFP4)
-    out = L.forward_mx(base, to_dev(t["X"]), to_dev(t["A"]), to_dev(t["B"]), lay.s)
+    nws = L.lora4_workspace_bytes_mx(base.abi(), M, r)
+    ws, chk_ws = guarded((nws,), torch.uint8)
+    Y, chk_y = guarded((M, N))
+    Z, chk_z = guarded((M, r))
+    # (the inputs stay referenced until the kernels have run: a tensor freed
+    # after its pointer is taken could be refilled by the next copy)
+    Xd, Ad, Bd = to_dev(t["X"]), to_dev(t["A"]), to_dev(t["B"])
+    st = L.lora4_forward_mx(base.abi(), Xd.data_ptr(), M, Ad.data_ptr(), Bd.data_ptr(), r, lay.s, Y.data_ptr(),
+                            Z.data_ptr(), ws.data_ptr(), nws, torch.cuda.current_stream().cuda_stream)
+    assert st == 0, L.status_string(st)
     torch.cuda.synchronize()
-    Y, Z = to_host(out["Y"]), to_host(out["Z"])
-    rng = np.random.default_rng(7)
-    rows = np.sort(rng.choice(M, 48, replace=False))
-    cols = np.sort(rng.choice(N, 64, replace=False))
-    wc, ws = mxfp4.quantize(t["W"][cols])
-    ref = mxfp8.forward(t["X"][rows], wc, ws, t["A"], t["B"][cols], lay.s)
-    assert rel(Y[np.ix_(rows, cols)], ref["Y"]) <= TOL
-    assert rel(Z[rows], ref["Z"]) <= TOL
+    for chk, nm in ((chk_ws, "workspace"), (chk_y, "Y"), (chk_z, "Z")):
+        chk(nm)
+    Yh, Zh = to_host(Y), to_host(Z)
+    del Y, Z, ws, base, Xd, Ad, Bd
+    torch.cuda.empty_cache()
+    wc, ws_ = oracle_pack_full(t["W"], synth.MXFP4)
+    ref = mxfp8.forward(t["X"], wc, ws_, t["A"], t["B"], lay.s)
+    report = {}
+    compare_full("Y", Yh, ref["Y"], abs(lay.s) * (np.abs(ref["Z"]) @ np.abs(f64(t["B"])).T), report)
+    compare_full("Z", Zh, ref["Z"], None, report)
+    print("[parity] mx", lay.name, report, flush=True)
+    write_report(f"llama70b-mx {lay.name} M={M} K={K} N={N} r={r}", report)

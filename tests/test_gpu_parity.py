@@ -14,22 +14,16 @@ import torch
 import lora_fine_tuning_amd as L
 import synth
 from oracle import lora
-from gpu_util import (DEV, TOL, dequant_rows, f64, pack_gpu, print_case, rel, to_dev, to_host)
+from gpu_util import (DEV, TILE_PATHS, TOL, dequant_rows, f64, pack_gpu, print_case, rel, set_tiles, to_dev,
+                      to_host)
 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(params=["auto", "big", "small"])
+@pytest.fixture(params=TILE_PATHS)
 def tiles(request, monkeypatch):
-    """Run a test with the library's own tile choice, then forced onto the
-    256 x 256 path and the 128 x 128 path (LORA4_BIG)."""
-    if request.param == "big":
-        monkeypatch.setenv("LORA4_BIG", "1")
-    elif request.param == "small":
-        monkeypatch.setenv("LORA4_BIG", "0")
-    else:
-        monkeypatch.delenv("LORA4_BIG", raising=False)
-    return request.param
+    """Runs a test on each tile path of the library (gpu_util.set_tiles)."""
+    return set_tiles(monkeypatch, request.param)
 
 
 def _run(lay, t, s=None, Z_from_forward=True, offsets=None):
@@ -166,13 +160,23 @@ def test_validation_errors_launch_nothing():
     t = synth.inputs(lay)
     base = pack_gpu(t["W"], lay.fmt)
     X, A, B = to_dev(t["X"]), to_dev(t["A"]), to_dev(t["B"])
-    with pytest.raises(L.Lora4Error) as ei:
-        L.forward(base, X, A, B, 2.0, workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
-    assert ei.value.status == -5
+    Y = torch.full((64, 64), 7.0, dtype=torch.bfloat16, device=DEV)
+    st = torch.cuda.current_stream().cuda_stream
+    # the library's own checks (raw ABI): a short workspace, a K off the block grid
+    small = torch.empty(16, dtype=torch.uint8, device=DEV)
+    assert L.lora4_forward(base.abi(), X.data_ptr(), 64, A.data_ptr(), B.data_ptr(), 8, 2.0, None, Y.data_ptr(),
+                           None, None, None, small.data_ptr(), 16, st) == -5
     bad = L.PackedBase(base.fmt, base.N, 96, 1, base.codes, base.scales)
-    with pytest.raises(L.Lora4Error) as ei:
-        L.forward(bad, X, A, B, 2.0, workspace=torch.empty(1 << 20, dtype=torch.uint8, device=DEV))
-    assert ei.value.status == -2
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=DEV)
+    assert L.lora4_forward(bad.abi(), X.data_ptr(), 64, A.data_ptr(), B.data_ptr(), 8, 2.0, None, Y.data_ptr(),
+                           None, None, None, ws.data_ptr(), 1 << 20, st) == -2
+    torch.cuda.synchronize()
+    assert (Y.float() == 7.0).all()            # nothing was launched
+    # the binding refuses both before calling the library
+    with pytest.raises(ValueError):
+        L.forward(base, X, A, B, 2.0, workspace=small)
+    with pytest.raises(ValueError):
+        L.forward(bad, X, A, B, 2.0, workspace=ws)
 
 
 def test_large_tile_shape_selected_automatically(monkeypatch):

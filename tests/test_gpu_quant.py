@@ -14,8 +14,8 @@ import torch
 import lora_fine_tuning_amd as L
 import synth
 from oracle import codecs, mxfp4, nf4
-from gpu_util import (DEV, f64, oracle_dequant, oracle_pack, pack_gpu, print_case, tile_codes, tile_scales, to_dev,
-                      to_host)
+from gpu_util import (DEV, f64, oracle_dequant, oracle_pack, pack_gpu, print_case, set_tiles, tile_codes, tile_scales,
+                      to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -110,10 +110,10 @@ def _to_packed(parts, fmt, N, K):
     return L.PackedBase(L.LORA4_MXFP4, N, K, 1, codes, sc)
 
 
-@pytest.fixture(params=["big", "small"])
+@pytest.fixture(params=["big", "small", "half", "fwdsmall"])
 def tiles(request, monkeypatch):
-    monkeypatch.setenv("LORA4_BIG", "1" if request.param == "big" else "0")
-    return request.param
+    """Runs a test on each tile path of the library (gpu_util.set_tiles)."""
+    return set_tiles(monkeypatch, request.param)
 
 
 @pytest.mark.parametrize("fmt", [synth.NF4, synth.NF4_DQ, synth.MXFP4, synth.NVFP4])
@@ -160,3 +160,69 @@ def test_mxfp4_nan_scale_propagates():
     assert np.isnan(Y[:, 3]).all()          # the NaN scale poisons the whole output column
     keep = [0, 1, 2] + list(range(4, N))
     assert np.array_equal(_zero_sign(to_host(out["Y"])[:, keep]), _zero_sign(ref.T[:, keep]))
+
+
+def _top_scale_base():
+    """MXFP4 rows whose block scales are the two largest finite E8M0 codes,
+    253 (2^126) and 254 (2^127): finite products (|e2m1| <= 3 at 253, <= 1.5
+    at 254) must come out exact; in row 40 one element overflows to +inf
+    (2 x 2^127) and in row 41 one to -inf (-6 x 2^126), every other element of
+    those rows being zero."""
+    N, K = 64, 64
+    rng = np.random.default_rng(11)
+    sc = np.full((N, K // 32), 127, dtype=np.uint8)
+    mags = rng.integers(0, 8, size=(N, K), dtype=np.uint8)
+    for n in range(32):
+        for b in range(2):
+            E = 253 + (n + b) % 2
+            sc[n, b] = E
+            lim = 5 if E == 253 else 3                  # magnitude codes of 3 and 1.5
+            mags[n, 32 * b:32 * b + 32] = np.minimum(mags[n, 32 * b:32 * b + 32], lim)
+    signs = rng.integers(0, 2, size=(N, K), dtype=np.uint8) << 3
+    codes4 = mags | signs
+    codes4[40, :32] = 0
+    codes4[40, 5] = 4                                   # +2 x 2^127 -> +inf
+    sc[40, 0] = 254
+    codes4[41, 32:] = 0
+    codes4[41, 33] = 8 | 7                              # -6 x 2^126 -> -inf
+    sc[41, 1] = 253
+    return (codes4[:, 0::2] | (codes4[:, 1::2] << 4)).astype(np.uint8), sc
+
+
+def _check_top_scale_product(out, ref, inf_at):
+    """out == ref (one-hot product: each output one dequantized element) on
+    every column of ref without an infinity; a column holding one (inf_at:
+    (row, column) -> sign) gives that infinity, with its sign, at its position. The column's other outputs each
+    add 0 x inf: IEEE gives NaN, a multiplier that takes 0 x inf as 0 gives
+    the exact finite element; each must be one of the two. Returns how many
+    were NaN."""
+    o = codecs.bf16_to_f32(out)
+    nans = 0
+    for (i, j), sign in inf_at.items():
+        assert np.isinf(o[i, j]) and np.sign(o[i, j]) == sign
+        rows = [m for m in range(out.shape[0]) if m != i]
+        col, exp = out[rows, j], ref[rows, j]
+        isnan = np.isnan(o[rows, j])
+        assert np.all(isnan | (_zero_sign(col) == _zero_sign(exp)))
+        nans += int(isnan.sum())
+    keep = [j for j in range(out.shape[1]) if j not in {c for _, c in inf_at}]
+    assert np.array_equal(_zero_sign(out[:, keep]), _zero_sign(ref[:, keep]))
+    return nans
+
+
+def test_mxfp4_top_scales_one_hot(tiles):
+    """E8M0 253 and 254 through both production GEMMs with one-hot operands."""
+    N, K, r = 64, 64, 4
+    parts = _top_scale_base()
+    base = _to_packed(parts, synth.MXFP4, N, K)
+    ref = oracle_dequant(parts, synth.MXFP4)                       # [N, K] bf16 bits
+    assert ref[40, 5] == 0x7F80 and ref[41, 33] == 0xFF80          # the oracle's +inf / -inf
+    zA = to_dev(np.zeros((r, K), np.uint16))
+    zB = torch.zeros((N, r), dtype=torch.bfloat16, device=DEV)
+    Y = to_host(L.forward(base, to_dev(_identity(K)), zA, zB, 1.0)["Y"])     # [K, N] = deq(W)^T
+    n_fwd = _check_top_scale_product(Y, ref.T, {(5, 40): 1, (33, 41): -1})
+    dX = to_host(L.backward(base, to_dev(_w((N, K), 1.0, 5)), to_dev(_identity(N)), zA, zB, 1.0)["dX"])
+    # dX = deq(W) [N, K]: an infinity at (n, k) meets the zeros of dY's other
+    # rows along column k of dX
+    n_bwd = _check_top_scale_product(dX, ref, {(40, 5): 1, (41, 33): -1})
+    print("[top scales] NaN outputs from 0 x inf: forward", n_fwd, "dgrad", n_bwd, flush=True)
