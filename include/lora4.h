@@ -37,6 +37,11 @@
  *    caller's workspace, sized by lora4_workspace_bytes().
  *  - Calls are re-entrant; two calls that share output or workspace buffers
  *    on different streams race.
+ *  - State kept between calls (all of it guarded for concurrent callers):
+ *    the NF4 table, built once and never changed; per device, the CU count
+ *    and which kernels have had their LDS limit raised; the opt-in kernel
+ *    timing record (lora4_timing_enable / lora4_timing_collect). No other
+ *    state outlives a call.
  */
 #ifndef LORA4_H
 #define LORA4_H

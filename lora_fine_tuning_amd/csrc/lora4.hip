@@ -276,7 +276,10 @@ PackedW packed_of(const Base &b) {
 // Planning: split factors and workspace layout
 // ---------------------------------------------------------------------------
 
-constexpr int TARGET_WG = 1024;  // workgroups wanted for the rank-r TN passes (dA, dB)
+// Workgroups wanted for the rank-r TN passes (dA, dB) at rank 16; wider
+// rank tiles do more work per workgroup and take proportionally fewer row
+// splits (fewer fp32 partials to write and reduce).
+constexpr int TARGET_WG = 1024;
 
 int skinny_tile(int r) { return r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : 128; }
 
@@ -329,7 +332,7 @@ Plan make_plan(int which, const Base &b, int64_t M, int r) {
   const int64_t mavg = std::max<int64_t>(1, M / p.E);
   auto msplit = [&](int64_t qtiles) {
     int64_t tiles = rtiles * qtiles * p.E;
-    int64_t want = ceil_div(TARGET_WG, std::max<int64_t>(tiles, 1));
+    int64_t want = ceil_div(TARGET_WG * 16 / p.rt, std::max<int64_t>(tiles, 1));
     int64_t maxs = std::max<int64_t>(1, mavg / 256);
     return (int)std::max<int64_t>(1, std::min<int64_t>({want, maxs, 65535 / p.E}));
   };
@@ -695,7 +698,10 @@ constexpr int64_t SK_MAX_RANGES = 4;    // (8 measured 0.5% slower on the 8B lay
 SkSched sk_sched(int64_t M, int64_t R, int r, int64_t E) {
   SkSched f{};
   f.tj = r <= 16 ? 1 : r <= 32 ? 2 : r <= 64 ? 4 : 8;
-  f.tm = f.tj == 1 ? 2 : f.tj == 2 ? 4 : f.tj == 4 ? 2 : 1;
+  // 64-row blocks from rank 17 on: every block re-reads the small operand
+  // (A or B) over its range, so taller blocks cut that traffic (at rank 128,
+  // 16-row blocks read A from L2 eight times as often as X itself)
+  f.tm = f.tj == 1 ? 2 : 4;
   const int64_t blocks = (ceil_div(std::max<int64_t>(M, 1), 16 * f.tm) + (E > 1 ? E : 0)) * ceil_div(r, 16 * f.tj);
   const int64_t chunks = std::max<int64_t>(1, ceil_div(R, 32));
   int64_t want = ceil_div(SK_TARGET_WG, blocks);
@@ -739,8 +745,8 @@ lora4_status rows_skinny(int transb, const uint16_t *act, int64_t ld_act, const 
       st1 = f.tm == 2 ? run_rows_tj<2, 1>(transb, p, grid, st) : run_rows_tj<4, 1>(transb, p, grid, st);
       break;
     case 2: st1 = run_rows_tj<4, 2>(transb, p, grid, st); break;
-    case 4: st1 = run_rows_tj<2, 4>(transb, p, grid, st); break;
-    default: st1 = run_rows_tj<1, 8>(transb, p, grid, st); break;
+    case 4: st1 = run_rows_tj<4, 4>(transb, p, grid, st); break;
+    default: st1 = run_rows_tj<4, 8>(transb, p, grid, st); break;
   }
   TRY(st1);
   if (f.ranges > 1 && !defer_reduce) {

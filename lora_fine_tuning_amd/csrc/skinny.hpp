@@ -69,7 +69,11 @@ __global__ __launch_bounds__(THREADS) void k_rows_skinny(Params p) {
   // per-wave staging of the transposed operand: 32 reduction rows x BN (+pad)
   constexpr int LDS_T = BN + 16;
   __shared__ __attribute__((aligned(16))) uint16_t stage[TRANSB ? 4 * 32 * LDS_T : 8];
-  __shared__ __attribute__((aligned(16))) float red[4][TM * TJ * 4][64];
+  // the four waves' partial tiles are added through LDS in rounds of RS
+  // accumulator slots (at most 32 KB)
+  constexpr int SLOTS = TM * TJ * 4;
+  constexpr int RS = SLOTS < 32 ? SLOTS : 32;
+  __shared__ __attribute__((aligned(16))) float red[4][RS][64];
 
   const RowTile rt = map_row_tile(blockIdx.x, BM, p.offsets, p.groups, p.M);
   if (rt.group < 0) return;
@@ -177,29 +181,32 @@ __global__ __launch_bounds__(THREADS) void k_rows_skinny(Params p) {
     if (i + UNR < n_local) compute_group(i + UNR, af1, bw1);
   }
 
-  // add the four waves' partial tiles
+  // add the four waves' partial tiles, RS slots at a time
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int r0 = 0; r0 < SLOTS; r0 += RS) {
+    if (r0 > 0) __syncthreads();   // the previous round's reads are done
 #pragma unroll
-    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) red[wave][(i * TJ + j) * 4 + e][lane] = acc[i][j][e];
-  __syncthreads();
-  constexpr int OUTS = TM * TJ * 4 * 64;   // accumulator slots per wave
-  for (int o = threadIdx.x; o < OUTS; o += THREADS) {
-    const int slot = o / 64, ln = o % 64;
-    const float v = red[0][slot][ln] + red[1][slot][ln] + red[2][slot][ln] + red[3][slot][ln];
-    const int i = (slot / 4) / TJ, j = (slot / 4) % TJ, e = slot % 4;
-    // 16x16 result layout: lane ln holds row 4 (ln / 16) + e, column ln % 16
-    const int64_t row = row0 + i * 16 + (ln >> 4) * 4 + e;
-    const int col = j0 + j * 16 + (ln & 15);
-    if (gridDim.z > 1) {
-      if (row < row_end && col < p.r) p.part[((int64_t)blockIdx.z * p.M + row) * p.r + col] = v;
-      continue;
+    for (int q = 0; q < RS; ++q) {
+      const int slot = r0 + q;
+      red[wave][q][lane] = acc[(slot / 4) / TJ][(slot / 4) % TJ][slot % 4];
     }
-    if (row < row_end && col < p.r) {
-      p.out1[row * p.r + col] = to_bf16(v * p.alpha1);
-      if (p.out2) p.out2[row * p.r + col] = to_bf16(v * p.alpha2);
+    __syncthreads();
+    for (int o = threadIdx.x; o < RS * 64; o += THREADS) {
+      const int q = o / 64, ln = o % 64;
+      const int slot = r0 + q;
+      const float v = red[0][q][ln] + red[1][q][ln] + red[2][q][ln] + red[3][q][ln];
+      const int i = (slot / 4) / TJ, j = (slot / 4) % TJ, e = slot % 4;
+      // 16x16 result layout: lane ln holds row 4 (ln / 16) + e, column ln % 16
+      const int64_t row = row0 + i * 16 + (ln >> 4) * 4 + e;
+      const int col = j0 + j * 16 + (ln & 15);
+      if (gridDim.z > 1) {
+        if (row < row_end && col < p.r) p.part[((int64_t)blockIdx.z * p.M + row) * p.r + col] = v;
+        continue;
+      }
+      if (row < row_end && col < p.r) {
+        p.out1[row * p.r + col] = to_bf16(v * p.alpha1);
+        if (p.out2) p.out2[row * p.r + col] = to_bf16(v * p.alpha2);
+      }
     }
   }
 }
