@@ -40,8 +40,9 @@
  *  - State kept between calls (all of it guarded for concurrent callers):
  *    the NF4 table, built once and never changed; per device, the CU count
  *    and which kernels have had their LDS limit raised; the opt-in kernel
- *    timing record (lora4_timing_enable / lora4_timing_collect). No other
- *    state outlives a call.
+ *    timing record (lora4_timing_enable / lora4_timing_collect); the static
+ *    scratch array of lora4_forward_noalloc, one per device. No other state
+ *    outlives a call.
  */
 #ifndef LORA4_H
 #define LORA4_H
@@ -83,7 +84,8 @@ typedef enum {
   LORA4_ERR_FORMAT = -4,        /* unknown format, or block does not match it    */
   LORA4_ERR_WORKSPACE = -5,     /* workspace NULL or smaller than required       */
   LORA4_ERR_HIP = -6,           /* a HIP call or kernel launch failed            */
-  LORA4_ERR_UNIMPLEMENTED = -7  /* valid request the library does not support   */
+  LORA4_ERR_UNIMPLEMENTED = -7, /* valid request the library does not support   */
+  LORA4_ERR_SCRATCH = -8        /* request exceeds the allocation-free scratch   */
 } lora4_status;
 
 /* The frozen 4-bit base W, logically [N = d_out, K = d_in] per group.
@@ -177,6 +179,25 @@ lora4_status lora4_backward(const lora4_W *W, const uint16_t *X, const uint16_t 
                             const int64_t *group_offsets, const uint16_t *Z,
                             uint16_t *dX, uint16_t *dA, uint16_t *dB,
                             void *workspace, size_t workspace_bytes, void *stream);
+
+/* Forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * arguments of lora4_forward without the workspace. Its scratch is a static
+ * device array of LORA4_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on until the process ends; no call allocates or frees device
+ * memory (with kernel timing on, only events already pooled are used).
+ * Every call on one GPU uses that GPU's array and leaves its contents behind
+ * (nothing in it has to start at zero): calls that overlap on one GPU, e.g.
+ * on two streams, race. A request whose forward needs more scratch returns
+ * LORA4_ERR_SCRATCH before anything is launched; outputs whose split
+ * reduction would not fit run unsplit instead. Results are those of
+ * lora4_forward (bit for bit where both run the same schedule). */
+#define LORA4_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+lora4_status lora4_forward_noalloc(const lora4_W *W, const uint16_t *X, int64_t M,
+                                   const uint16_t *A, const uint16_t *B, int32_t r, float s,
+                                   const int64_t *group_offsets,
+                                   uint16_t *Y, uint16_t *Z, uint16_t *Y_base, uint16_t *Y_lora,
+                                   void *stream);
 
 /* Several LoRA adapters over one shared base: adapter a applies to rows
  * adapter_offsets[a] .. adapter_offsets[a+1]-1 of X, Y, dY and dX ("Fine-Tuning

@@ -25,7 +25,7 @@ LORA4_NF4, LORA4_NF4_DQ, LORA4_MXFP4, LORA4_NVFP4 = 1, 2, 3, 4
 FORMATS = {"nf4": LORA4_NF4, "nf4_dq": LORA4_NF4_DQ, "mxfp4": LORA4_MXFP4, "nvfp4": LORA4_NVFP4}
 BLOCK = {LORA4_NF4: 64, LORA4_NF4_DQ: 64, LORA4_MXFP4: 32, LORA4_NVFP4: 16}
 
-EXPORTS = ["lora4_forward", "lora4_backward", "lora4_workspace_bytes", "lora4_packed_bytes",
+EXPORTS = ["lora4_forward", "lora4_forward_noalloc", "lora4_backward", "lora4_workspace_bytes", "lora4_packed_bytes",
            "lora4_forward_multi", "lora4_backward_multi", "lora4_workspace_bytes_multi", "quant_pack_nf4",
            "quant_pack_mxfp4", "quant_pack_nvfp4", "quant_pack_mxfp8", "lora4_workspace_bytes_mx", "lora4_forward_mx",
            "lora4_loftq_workspace_bytes", "lora4_loftq_init", "lora4_import_rowmajor",
@@ -62,6 +62,8 @@ def lib():
         Wp = ctypes.POINTER(lora4_W)
         L.lora4_forward.argtypes = [Wp, vp, i64, vp, vp, i32, f32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.lora4_forward.restype = ctypes.c_int
+        L.lora4_forward_noalloc.argtypes = [Wp, vp, i64, vp, vp, i32, f32, vp, vp, vp, vp, vp, vp]
+        L.lora4_forward_noalloc.restype = ctypes.c_int
         L.lora4_backward.argtypes = [Wp, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.lora4_backward.restype = ctypes.c_int
         L.lora4_workspace_bytes.argtypes = [ctypes.c_int, Wp, i64, i32]
@@ -128,6 +130,11 @@ def lora4_forward(W, X, M, A, B, r, s, group_offsets, Y, Z, Y_base, Y_lora, work
                   stream):
     return lib().lora4_forward(ctypes.byref(W), X, M, A, B, r, s, group_offsets, Y, Z, Y_base, Y_lora,
                                workspace, workspace_bytes, stream)
+
+
+def lora4_forward_noalloc(W, X, M, A, B, r, s, group_offsets, Y, Z, Y_base, Y_lora, stream):
+    return lib().lora4_forward_noalloc(ctypes.byref(W), X, M, A, B, r, s, group_offsets, Y, Z, Y_base, Y_lora,
+                                       stream)
 
 
 def lora4_backward(W, X, dY, M, A, B, r, s, group_offsets, Z, dX, dA, dB, workspace, workspace_bytes,
@@ -446,6 +453,25 @@ def forward(base, X, A, B, s, group_offsets=None, want_z=True, want_parts=False,
     st = lora4_forward(W, _ptr(X), M, _ptr(A), _ptr(B), r, float(s), _ptr(group_offsets), _ptr(Y), _ptr(Z),
                        _ptr(Yb), _ptr(Yl), _ptr(workspace), workspace.numel(), _stream())
     _check(st, "lora4_forward")
+    return {"Y": Y, "Z": Z, "Y_base": Yb, "Y_lora": Yl}
+
+
+def forward_noalloc(base, X, A, B, s, group_offsets=None, want_z=True, want_parts=False, out=None):
+    """lora4_forward through the entry point that allocates nothing (its
+    scratch is the library's static device array): same arguments as
+    forward() without the workspace."""
+    out = out or {}
+    M, r, _ = check_layer_args(base, X, A, B, offsets=group_offsets, outputs=[
+        ("Y", out.get("Y"), (X.shape[0], base.N)), ("Z", out.get("Z"), (X.shape[0], A.shape[-2])),
+        ("Y_base", out.get("Y_base"), (X.shape[0], base.N)), ("Y_lora", out.get("Y_lora"), (X.shape[0], base.N))])
+    dev = X.device
+    Y = _out(out.get("Y"), (M, base.N), dev)
+    Z = _out(out.get("Z"), (M, r), dev) if want_z or out.get("Z") is not None else None
+    Yb = _out(out.get("Y_base"), (M, base.N), dev) if want_parts or out.get("Y_base") is not None else None
+    Yl = _out(out.get("Y_lora"), (M, base.N), dev) if want_parts or out.get("Y_lora") is not None else None
+    st = lora4_forward_noalloc(base.abi(), _ptr(X), M, _ptr(A), _ptr(B), r, float(s), _ptr(group_offsets),
+                               _ptr(Y), _ptr(Z), _ptr(Yb), _ptr(Yl), _stream())
+    _check(st, "lora4_forward_noalloc")
     return {"Y": Y, "Z": Z, "Y_base": Yb, "Y_lora": Yl}
 
 

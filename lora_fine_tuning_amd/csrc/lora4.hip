@@ -119,7 +119,12 @@ bool g_timing = false;
 std::vector<PendingTiming> g_pending;
 std::vector<hipEvent_t> g_free_events;
 
+// Set while lora4_forward_noalloc runs on this thread: timing then takes
+// events from the pool only and never creates one.
+thread_local bool tl_no_alloc = false;
+
 hipEvent_t take_event() {
+  if (tl_no_alloc && g_free_events.empty()) return nullptr;
   if (!g_free_events.empty()) {
     hipEvent_t e = g_free_events.back();
     g_free_events.pop_back();
@@ -316,7 +321,9 @@ constexpr int BM_MAIN = 128, BN_MAIN = 128;
 constexpr int BM_SKINNY = 128;
 constexpr int TN_BQ = 128;
 
-Plan make_plan(int which, const Base &b, int64_t M, int r) {
+// cap: the workspace there is (the allocation-free forward's fixed scratch);
+// a forward whose split partials would not fit runs the tiles unsplit.
+Plan make_plan(int which, const Base &b, int64_t M, int r, size_t cap = SIZE_MAX) {
   const lora4_W *W = b.W;
   Plan p{};
   p.M = M;
@@ -362,6 +369,11 @@ Plan make_plan(int which, const Base &b, int64_t M, int r) {
     off = p.off_part_b + align256((size_t)p.msplit_b * p.E * r * p.N * 4);
   }
   p.bytes = std::max<size_t>(off, 256);   // never 0: 0 reports invalid arguments
+  if (p.bytes > cap && which == 0 && p.fs.use && p.fs.split_tiles > 0) {
+    p.bytes -= align256((size_t)p.fs.split_tiles * p.fs.ksplit * fwd::BM * fwd::BN * 4);
+    p.off_part = p.off_party;
+    p.fs = FWD_LDS_KERNEL;   // the 128 x 128 kernel, no partials
+  }
   return p;
 }
 
@@ -1039,6 +1051,37 @@ lora4_status run_quant_mxfp8(const uint16_t *X, int64_t ldx, int64_t M, int64_t 
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free forward: one static device array that every
+// GPU the library runs on holds (its own copy) until the process ends. Host
+// code never uses the array's name as an address: the device address is
+// taken once per device with hipGetSymbolAddress, with that device current.
+// ---------------------------------------------------------------------------
+
+static __device__ __attribute__((aligned(256))) unsigned char scratch[LORA4_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES] = {};
+
+// The current device's copy of `scratch` (looked up on its first use there).
+lora4_status scratch_for_current_device(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return LORA4_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return LORA4_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return LORA4_OK;
+}
+
+}  // namespace
+
 // ===========================================================================
 // Exported C ABI
 // ===========================================================================
@@ -1058,6 +1101,7 @@ const char *lora4_status_string(lora4_status s) {
     case LORA4_ERR_WORKSPACE: return "workspace missing or too small";
     case LORA4_ERR_HIP: return "a HIP call or kernel launch failed";
     case LORA4_ERR_UNIMPLEMENTED: return "not supported by the library";
+    case LORA4_ERR_SCRATCH: return "request needs more than the allocation-free scratch holds";
   }
   return "unknown status";
 }
@@ -1081,14 +1125,15 @@ size_t lora4_workspace_bytes_multi(int which, const lora4_W *W, int64_t adapters
 static lora4_status forward_impl(const Base &bs, const uint16_t *X, int64_t M, const uint16_t *A,
                            const uint16_t *B, int32_t r, float s, const int64_t *group_offsets,
                            uint16_t *Y, uint16_t *Z, uint16_t *Y_base, uint16_t *Y_lora,
-                           void *workspace, size_t workspace_bytes, void *stream) {
+                           void *workspace, size_t workspace_bytes, void *stream, size_t cap = SIZE_MAX) {
   TRY(check_common(bs, M, r, s, group_offsets));
   const lora4_W *W = bs.W;
   if (!A || !B || (M > 0 && (!X || !Y))) return LORA4_ERR_NULL;
   for (const void *q : {(const void *)X, (const void *)A, (const void *)B, (const void *)Y, (const void *)Z,
                         (const void *)Y_base, (const void *)Y_lora, (const void *)group_offsets})
     if (q && !aligned16(q)) return LORA4_ERR_ALIGN;
-  const Plan pl = make_plan(0, bs, M, r);
+  const Plan pl = make_plan(0, bs, M, r, cap);
+  if (cap != SIZE_MAX && pl.bytes > cap) return LORA4_ERR_SCRATCH;
   if (!workspace) return LORA4_ERR_WORKSPACE;
   if (!aligned16(workspace)) return LORA4_ERR_ALIGN;
   if (workspace_bytes < pl.bytes) return LORA4_ERR_WORKSPACE;
@@ -1242,6 +1287,21 @@ lora4_status lora4_forward(const lora4_W *W, const uint16_t *X, int64_t M, const
   if (!W) return LORA4_ERR_NULL;
   return forward_impl(Base{W, W->groups, false}, X, M, A, B, r, s, group_offsets, Y, Z, Y_base, Y_lora, workspace,
                       workspace_bytes, stream);
+}
+
+lora4_status lora4_forward_noalloc(const lora4_W *W, const uint16_t *X, int64_t M, const uint16_t *A,
+                                   const uint16_t *B, int32_t r, float s, const int64_t *group_offsets,
+                                   uint16_t *Y, uint16_t *Z, uint16_t *Y_base, uint16_t *Y_lora, void *stream) {
+  if (!W) return LORA4_ERR_NULL;
+  TRY(check_common(Base{W, W->groups, false}, M, r, s, group_offsets));
+  void *ws = nullptr;
+  TRY(scratch_for_current_device(&ws));
+  struct Guard {
+    Guard() { tl_no_alloc = true; }
+    ~Guard() { tl_no_alloc = false; }
+  } guard;
+  return forward_impl(Base{W, W->groups, false}, X, M, A, B, r, s, group_offsets, Y, Z, Y_base, Y_lora, ws,
+                      LORA4_NOALLOC_SCRATCH_BYTES, stream, LORA4_NOALLOC_SCRATCH_BYTES);
 }
 
 lora4_status lora4_backward(const lora4_W *W, const uint16_t *X, const uint16_t *dY, int64_t M,
