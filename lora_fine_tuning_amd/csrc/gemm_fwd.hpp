@@ -75,16 +75,16 @@ struct WRaw {
 // blocks). SPLIT (TBM 256, NJ 2 only): the block computes reduction range
 // `split` of the tile and writes fp32 partials. SHARED: the row tiles ignore
 // the groups (Params::shared_rows). `tile` is the tile's index in the split
-// partials.
+// partials. rt: the tile's rows (from the slot's 256-row tile; a short last
+// tile of a group runs with TBM 64 or 128 over the same rows).
 template <int FMT, bool SPLIT, bool SHARED, int TBM, int NJ>
-__device__ __forceinline__ void fwd_tile(const Params &p, uint16_t *smem, int slot, int64_t col0, int tile,
+__device__ __forceinline__ void fwd_tile(const Params &p, uint16_t *smem, const RowTile &rt, int64_t col0, int tile,
                                          int split) {
   static_assert(!SPLIT || (TBM == BM && NJ == 2), "split partials are laid out for 256 x 256 tiles");
   constexpr int RB = TBM / 32;       // 32-row blocks: MFMA row blocks per wave, X chunks per step
   constexpr int WN = 32 * NJ;        // columns per wave
   constexpr int CPS = 8 / RB;        // hand-dealt slices per MFMA row block (8 slices per sub-step)
   constexpr bool is_split = SPLIT;
-  const RowTile rt = big::tile_rows<SHARED>(p, slot, TBM);
   if (rt.group < 0) return;
   const int g = rt.group;
   const int64_t row0 = rt.row0, row_end = rt.row_end;
@@ -629,6 +629,19 @@ __device__ __forceinline__ void fwd_tile(const Params &p, uint16_t *smem, int sl
   }
 }
 
+// A whole 256-row tile whose rows end within 64 (128) rows of its start runs
+// with 64 (128) row tiles' code: 2 (4) of the 8 row blocks of MFMAs, the same W
+// decode. (The last tile of an expert's rows, or of M, is often short.)
+template <int FMT, bool SHARED>
+__device__ __forceinline__ void fwd_whole_tile(const Params &p, uint16_t *smem, const RowTile &rt, int64_t col0,
+                                               int tile) {
+  if (rt.group < 0) return;
+  const int64_t rows = rt.row_end - rt.row0;
+  if (p.short_tiles && rows <= 64) fwd_tile<FMT, false, SHARED, 64, 2>(p, smem, rt, col0, tile, 0);
+  else if (p.short_tiles && rows <= 128) fwd_tile<FMT, false, SHARED, 128, 2>(p, smem, rt, col0, tile, 0);
+  else fwd_tile<FMT, false, SHARED, BM, 2>(p, smem, rt, col0, tile, 0);
+}
+
 // Full 256 x 256 tiles (blocks below p.nfull, in grouped tile order, each XCD
 // walking a contiguous range of them) and, after them, the last p.ntail tiles
 // of that order as two 256 x 128 halves each: when the full tiles leave a
@@ -642,20 +655,22 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   if constexpr (SPLIT) {
     const int tile = b / p.ksplit;
     const int tn = tile % p.tiles_n, slot = tile / p.tiles_n;   // (the reduction of the split tiles uses this order)
-    fwd_tile<FMT, true, SHARED, BM, 2>(p, smem, slot, (int64_t)tn * BN, tile, b % p.ksplit);
+    const RowTile rt = big::tile_rows<SHARED>(p, slot, BM);
+    fwd_tile<FMT, true, SHARED, BM, 2>(p, smem, rt, (int64_t)tn * BN, tile, b % p.ksplit);
   } else {
     int slot, tn;
     if (b < p.nfull) {
       const int per = p.nfull >> 3;
       if (b < per * 8) b = (b & 7) * per + (b >> 3);
       big::grouped_tile(b, p.tiles_n, p.nslots, slot, tn);
-      fwd_tile<FMT, false, SHARED, BM, 2>(p, smem, slot, (int64_t)tn * BN, b, 0);
+      fwd_whole_tile<FMT, SHARED>(p, smem, big::tile_rows<SHARED>(p, slot, BM), (int64_t)tn * BN, b);
     } else {
       int u = b - p.nfull;
       const int per = (2 * p.ntail) >> 3;
       if (u < per * 8) u = (u & 7) * per + (u >> 3);
       big::grouped_tile(p.nfull + (u >> 1), p.tiles_n, p.nslots, slot, tn);
-      fwd_tile<FMT, false, SHARED, BM, 1>(p, smem, slot, (int64_t)tn * BN + (u & 1) * (BN / 2), 0, 0);
+      fwd_tile<FMT, false, SHARED, BM, 1>(p, smem, big::tile_rows<SHARED>(p, slot, BM),
+                                          (int64_t)tn * BN + (u & 1) * (BN / 2), 0, 0);
     }
   }
 }
@@ -671,7 +686,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd_small(Params p) {
   if (b < per * 8) b = (b & 7) * per + (b >> 3);
   int slot, tn;
   big::grouped_tile(b, p.tiles_n, p.nslots, slot, tn);
-  fwd_tile<FMT, false, SHARED, 128, 1>(p, smem, slot, (int64_t)tn * 128, b, 0);
+  fwd_tile<FMT, false, SHARED, 128, 1>(p, smem, big::tile_rows<SHARED>(p, slot, 128), (int64_t)tn * 128, b, 0);
 }
 
 // C[tile rows][tile columns] = bf16(sum_k part[t][k][r][c]) for the split

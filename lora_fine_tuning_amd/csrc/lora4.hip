@@ -425,12 +425,13 @@ int cu_count() {
 // Forced forward tile shapes for tests and measurements (LORA4_FWD_TILES):
 // "small" (128 x 128 tiles), "half" (every 256 x 256 tile as two halves),
 // "mixed" (the second half of the tiles as halves), "whole" (256 x 256 tiles
-// only, no halves); anything else or unset: automatic.
+// only, no halves), "noshort" (automatic, but short last row tiles run the
+// 256-row code); anything else or unset: automatic.
 int fwd_tiles_policy() {
   const char *e = std::getenv("LORA4_FWD_TILES");
   if (!e) return 0;
   const std::string v(e);
-  return v == "small" ? 1 : v == "half" ? 2 : v == "mixed" ? 3 : v == "whole" ? 4 : 0;
+  return v == "small" ? 1 : v == "half" ? 2 : v == "mixed" ? 3 : v == "whole" ? 4 : v == "noshort" ? 5 : 0;
 }
 
 // The register-direct forward kernels run one tile per CU at a time:
@@ -450,7 +451,8 @@ FwdSched fwd_sched(int64_t M, int64_t N, int64_t K, int64_t E, const PackedW &W)
   if (K <= 0 || M <= 0 || !big_fits(K, M, W)) return f;
   const int pol = big_policy();
   if (pol == 0) return f;
-  const int force = fwd_tiles_policy();
+  int force = fwd_tiles_policy();
+  if (force == 5) force = 0;   // (short tiles: big_params)
   const int64_t cus = cu_count();
   const int64_t groups = E > 1 && !W.shared ? E : 0;
   const int64_t tiles = (ceil_div(M, fwd::BM) + groups) * ceil_div(N, fwd::BN);
@@ -564,6 +566,7 @@ big::Params big_params(const Mat &A, const PackedW &W, int64_t R, const Mat &A2,
   p.nblocks = p.nslots * p.tiles_n;
   p.nfull = p.nblocks;
   p.ntail = 0;
+  p.short_tiles = fwd_tiles_policy() == 5 ? 0 : 1;
   p.tab = nf4_table();
   p.ksplit = 1;
   p.split_steps = 1 << 30;
