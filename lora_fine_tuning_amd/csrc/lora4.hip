@@ -17,6 +17,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -411,15 +412,16 @@ bool big_fits(int64_t ld_a, int64_t M, const PackedW &W) {
 
 // Compute units of the current device (cached per device).
 int cu_count() {
-  static int cached[64] = {0};
+  // per device; concurrent first calls may both query, and store the same value
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cached[dev]) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (!n) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 // Forced forward tile shapes for tests and measurements (LORA4_FWD_TILES):
@@ -1362,6 +1364,12 @@ lora4_status clear_padding(int64_t N, int64_t K, int32_t format, uint8_t *codes,
                      reinterpret_cast<uint16_t *>(scales), ns, (uint16_t)0);
 }
 
+// Grid of the packers that take one lane per 8 elements (grid-strided past
+// PACK_MAX_BLOCKS workgroups).
+dim3 pack_grid(int64_t N, int64_t K) {
+  return dim3((unsigned)std::min<int64_t>(ceil_div(N * (K / 8), PACK_THREADS), PACK_MAX_BLOCKS));
+}
+
 lora4_status quant_pack_nf4(const uint16_t *W_bf16, int64_t N, int64_t K, int32_t double_quant,
                             uint8_t *codes, void *scales, float *scales2, void *stream) {
   if (!W_bf16 || !codes || !scales) return LORA4_ERR_NULL;
@@ -1371,13 +1379,14 @@ lora4_status quant_pack_nf4(const uint16_t *W_bf16, int64_t N, int64_t K, int32_
     return LORA4_ERR_ALIGN;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   TRY(clear_padding(N, K, double_quant ? LORA4_NF4_DQ : LORA4_NF4, codes, scales, st));
-  const int64_t nblk = N * (K / 64);
   if (!double_quant) {
-    return launch_args("quant_pack_nf4", k_quant_nf4, dim3((unsigned)ceil_div(nblk, 256)), dim3(256), st,
-                       W_bf16, N, K, codes, reinterpret_cast<float *>(scales), nf4_table());
+    return launch_args("quant_pack_nf4", k_quant_nf4, pack_grid(N, K), dim3(PACK_THREADS), st, W_bf16, N, K, codes,
+                       reinterpret_cast<float *>(scales), nf4_table());
   }
-  return launch_args("quant_pack_nf4_dq", k_quant_nf4_dq, dim3((unsigned)ceil_div(nblk, 256)), dim3(256), st,
-                     W_bf16, N, K, codes, reinterpret_cast<uint8_t *>(scales), scales2, nf4_table());
+  // one workgroup per second-level group of 256 blocks
+  const int64_t nblk = N * (K / 64);
+  return launch_args("quant_pack_nf4_dq", k_quant_nf4_dq, dim3((unsigned)ceil_div(nblk, 256)), dim3(PACK_THREADS),
+                     st, W_bf16, N, K, codes, reinterpret_cast<uint8_t *>(scales), scales2, nf4_table());
 }
 
 lora4_status quant_pack_mxfp4(const uint16_t *W_bf16, int64_t N, int64_t K, uint8_t *codes,
@@ -1387,9 +1396,8 @@ lora4_status quant_pack_mxfp4(const uint16_t *W_bf16, int64_t N, int64_t K, uint
   if (!aligned16(W_bf16) || !aligned16(codes) || !aligned16(scales_e8m0)) return LORA4_ERR_ALIGN;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   TRY(clear_padding(N, K, LORA4_MXFP4, codes, scales_e8m0, st));
-  const int64_t nblk = N * (K / 32);
-  return launch_args("quant_pack_mxfp4", k_quant_mxfp4, dim3((unsigned)ceil_div(nblk, 256)), dim3(256), st,
-                     W_bf16, N, K, codes, scales_e8m0);
+  return launch_args("quant_pack_mxfp4", k_quant_mxfp4, pack_grid(N, K), dim3(PACK_THREADS), st, W_bf16, N, K,
+                     codes, scales_e8m0);
 }
 
 lora4_status lora4_import_rowmajor(int32_t format, int64_t N, int64_t K, int64_t groups, const uint8_t *codes_rm,
@@ -1488,9 +1496,8 @@ lora4_status quant_pack_nvfp4(const uint16_t *W_bf16, int64_t N, int64_t K, uint
   if (!aligned16(W_bf16) || !aligned16(codes) || !aligned16(scales_e4m3)) return LORA4_ERR_ALIGN;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   TRY(clear_padding(N, K, LORA4_NVFP4, codes, scales_e4m3, st));
-  const int64_t nblk = N * (K / 16);
-  return launch_args("quant_pack_nvfp4", k_quant_nvfp4, dim3((unsigned)ceil_div(nblk, 256)), dim3(256), st,
-                     W_bf16, N, K, codes, scales_e4m3);
+  return launch_args("quant_pack_nvfp4", k_quant_nvfp4, pack_grid(N, K), dim3(PACK_THREADS), st, W_bf16, N, K,
+                     codes, scales_e4m3);
 }
 
 size_t lora4_loftq_workspace_bytes(int64_t N, int64_t K, int32_t r) {
