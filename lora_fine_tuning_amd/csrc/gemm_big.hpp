@@ -37,9 +37,6 @@ struct Params {
   // forward, whole-tile launches: the first nfull tiles in grouped order run
   // whole, the ntail after them as two 256 x 128 halves (blocks nfull ..)
   int nfull, ntail;
-  // forward: whole tiles whose rows end within 64 / 128 rows run the shorter
-  // tiles' code (0: always the 256-row code)
-  int short_tiles;
   Nf4Table tab;
   // split reduction (forward kernel only): every tile runs in ksplit blocks
   // of split_steps 64-deep steps, which write fp32 partials

@@ -26,6 +26,8 @@
 // built by hand, one slice of work per pair of MFMAs (see below).
 #pragma once
 
+#include <type_traits>
+
 #include "gemm_big.hpp"
 
 namespace lora4 {
@@ -209,9 +211,10 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[j][i] = f32x16_t{};
 
-  auto read_af = [&](const uint16_t *As, int kk, u32x4_t af[4]) {
+  auto read_af = [&](const uint16_t *As, int kk, u32x4_t af[4], int nblk = 4) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) af[i] = lds_read_b128(As + swz(wm0 + i * 32 + l32, kk * 2 + h));
+    for (int i = 0; i < 4; ++i)
+      if (i < nblk) af[i] = lds_read_b128(As + swz(wm0 + i * 32 + l32, kk * 2 + h));
   };
   auto read_bf = [&](const uint16_t *Bs, int kk, int j) -> u32x4_t {
     return frag_w(Bs, kk * 16, wn0 + j * 32, lane);
@@ -372,8 +375,11 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
   constexpr int VM_D = W_LOADS_D;
   constexpr int VMCNT_D = (VM_D & 15) | (7 << 4) | (0 << 8) | ((VM_D >> 4) << 14);
   u32x4_t afa[4], afb[4], bf[4];
-  auto step_s = [&](int s, const uint16_t *Acur, const uint16_t *Bcur, uint16_t *Anxt, uint16_t *Bnxt,
-                    const WRaw &rdec, WRaw &rload) {
+  // IA (a std::integral_constant): how many of the wave's four 32-row blocks
+  // hold rows of the tile; MFMAs and operand reads of the others are left out
+  auto step_s = [&](auto ia, int s, const uint16_t *Acur, const uint16_t *Bcur, uint16_t *Anxt, uint16_t *Bnxt,
+                    const WRaw &rdec, WRaw &rload) __attribute__((always_inline)) {
+    constexpr int IA = decltype(ia)::value;
     RunTable T;
     float s0 = 0.0f, s1 = 0.0f;
     TabBuild tb;
@@ -386,20 +392,22 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
       for (int m = 0; m < 8; ++m) {
         const int G = kk * 8 + m;
         const int j = m >> 1, i0 = (m & 1) * 2;
-        acc[j][i0] = mfma_32x32x16(bf[j], af[i0], acc[j][i0]);
-        acc[j][i0 + 1] = mfma_32x32x16(bf[j], af[i0 + 1], acc[j][i0 + 1]);
+        if (i0 < IA) acc[j][i0] = mfma_32x32x16(bf[j], af[i0], acc[j][i0]);
+        if (i0 + 1 < IA) acc[j][i0 + 1] = mfma_32x32x16(bf[j], af[i0 + 1], acc[j][i0 + 1]);
         if (kk < 3) {
-          if (m < 4) afn[m] = lds_read_b128(Acur + swz(wm0 + m * 32 + l32, (kk + 1) * 2 + h));
-          if (m & 1) bf[j] = read_bf(Bcur, kk + 1, j);
+          if (m < IA) afn[m] = lds_read_b128(Acur + swz(wm0 + m * 32 + l32, (kk + 1) * 2 + h));
+          if (IA > 0 && (m & 1)) bf[j] = read_bf(Bcur, kk + 1, j);
         } else if (m == 4) {
           __builtin_amdgcn_s_waitcnt(VMCNT_D);
           asm volatile("" ::: "memory");
           __builtin_amdgcn_s_barrier();
           asm volatile("" ::: "memory");
-          read_af(Anxt, 0, afa);
-          bf[0] = read_bf(Bnxt, 0, 0);
-          bf[1] = read_bf(Bnxt, 0, 1);
-        } else if (m == 5 || m == 7) {
+          read_af(Anxt, 0, afa, IA);
+          if (IA > 0) {
+            bf[0] = read_bf(Bnxt, 0, 0);
+            bf[1] = read_bf(Bnxt, 0, 1);
+          }
+        } else if (IA > 0 && (m == 5 || m == 7)) {
           bf[j] = read_bf(Bnxt, 0, j);
         }
         if (G < 4) tab_stage(G, rdec, tb, T, s0, s1);
@@ -436,15 +444,31 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
   load_w(1, r1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  read_af(As0, 0, afa);
+  // the main loop with IA active row blocks (every wave meets the same
+  // barriers whatever its IA)
+  auto main_loop = [&](auto ia) __attribute__((always_inline)) {
+    constexpr int IA = decltype(ia)::value;
+    read_af(As0, 0, afa, IA);
+    if (IA > 0) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) bf[j] = read_bf(Bs0, 0, j);
-  int s = 0;
-  for (; s + 2 <= steps; s += 2) {
-    step_s(s, As0, Bs0, As1, Bs1, r1, r0);
-    step_s(s + 1, As1, Bs1, As0, Bs0, r0, r1);
+      for (int j = 0; j < 4; ++j) bf[j] = read_bf(Bs0, 0, j);
+    }
+    int s = 0;
+    for (; s + 2 <= steps; s += 2) {
+      step_s(ia, s, As0, Bs0, As1, Bs1, r1, r0);
+      step_s(ia, s + 1, As1, Bs1, As0, Bs0, r0, r1);
+    }
+    if (s < steps) step_s(ia, s, As0, Bs0, As1, Bs1, r1, r0);
+  };
+  // A tile with at most 64 rows (the last tile of an expert's rows, or of M)
+  // keeps the full-tile schedule, but only its first two row blocks compute:
+  // the waves of rows 128.. skip every MFMA, those of rows 0.. skip half.
+  if (row_end - row0 <= 64) {
+    if (wm0 == 0) main_loop(std::integral_constant<int, 2>{});
+    else main_loop(std::integral_constant<int, 0>{});
+  } else {
+    main_loop(std::integral_constant<int, 4>{});
   }
-  if (s < steps) step_s(s, As0, Bs0, As1, Bs1, r1, r0);
   // the look-ahead loads past the end still write (zeros) into the stages,
   // and the last step's prefetch reads the stage the tail reuses
   __builtin_amdgcn_s_waitcnt(0);

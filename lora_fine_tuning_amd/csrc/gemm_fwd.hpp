@@ -629,16 +629,18 @@ __device__ __forceinline__ void fwd_tile(const Params &p, uint16_t *smem, const 
   }
 }
 
-// A whole 256-row tile whose rows end within 64 (128) rows of its start runs
-// with 64 (128) row tiles' code: 2 (4) of the 8 row blocks of MFMAs, the same W
-// decode. (The last tile of an expert's rows, or of M, is often short.)
-template <int FMT, bool SHARED>
+// SHORT: a whole 256-row tile whose rows end within 64 (128) rows of its start
+// runs with 64 (128) row tiles' code: 2 (4) of the 8 row blocks of MFMAs, the
+// same W decode. (The last tile of an expert's rows is often short.) Only the
+// grouped launches take it: the kernels sit at 254-255 of 256 VGPRs, and with
+// the extra paths the MXFP4 one spills 3 registers.
+template <int FMT, bool SHARED, bool SHORT>
 __device__ __forceinline__ void fwd_whole_tile(const Params &p, uint16_t *smem, const RowTile &rt, int64_t col0,
                                                int tile) {
   if (rt.group < 0) return;
   const int64_t rows = rt.row_end - rt.row0;
-  if (p.short_tiles && rows <= 64) fwd_tile<FMT, false, SHARED, 64, 2>(p, smem, rt, col0, tile, 0);
-  else if (p.short_tiles && rows <= 128) fwd_tile<FMT, false, SHARED, 128, 2>(p, smem, rt, col0, tile, 0);
+  if (SHORT && rows <= 64) fwd_tile<FMT, false, SHARED, 64, 2>(p, smem, rt, col0, tile, 0);
+  else if (SHORT && rows <= 128) fwd_tile<FMT, false, SHARED, 128, 2>(p, smem, rt, col0, tile, 0);
   else fwd_tile<FMT, false, SHARED, BM, 2>(p, smem, rt, col0, tile, 0);
 }
 
@@ -647,8 +649,8 @@ __device__ __forceinline__ void fwd_whole_tile(const Params &p, uint16_t *smem, 
 // of that order as two 256 x 128 halves each: when the full tiles leave a
 // last round that fills half the GPU or less, its tiles run as twice as many
 // half tiles, one round in about half the time. SPLIT: block b computes range
-// b % ksplit of tile b / ksplit (no halves).
-template <int FMT, bool SPLIT, bool SHARED>
+// b % ksplit of tile b / ksplit (no halves). SHORT: see fwd_whole_tile.
+template <int FMT, bool SPLIT, bool SHARED, bool SHORT = false>
 __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   int b = blockIdx.x;
@@ -663,7 +665,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_fwd(Params p) {
       const int per = p.nfull >> 3;
       if (b < per * 8) b = (b & 7) * per + (b >> 3);
       big::grouped_tile(b, p.tiles_n, p.nslots, slot, tn);
-      fwd_whole_tile<FMT, SHARED>(p, smem, big::tile_rows<SHARED>(p, slot, BM), (int64_t)tn * BN, b);
+      fwd_whole_tile<FMT, SHARED, SHORT>(p, smem, big::tile_rows<SHARED>(p, slot, BM), (int64_t)tn * BN, b);
     } else {
       int u = b - p.nfull;
       const int per = (2 * p.ntail) >> 3;

@@ -506,6 +506,12 @@ lora4_status run_fwd(const big::Params &p, bool small, hipStream_t st) {
   if (p.ksplit > 1)
     return launch_lds("gemm_nt_base", fwd::k_gemm_fwd<FMT, true, SHARED>, dim3((unsigned)p.nblocks),
                       dim3(fwd::THREADS), (size_t)fwd::lds_bytes(), p, st);
+  if constexpr (!SHARED) {
+    // per-expert row tiles: short last tiles of a group run shorter tiles' code
+    if (p.groups > 1 && fwd_tiles_policy() != 5)
+      return launch_lds("gemm_nt_base", fwd::k_gemm_fwd<FMT, false, false, true>, dim3((unsigned)p.nblocks),
+                        dim3(fwd::THREADS), (size_t)fwd::lds_bytes(), p, st);
+  }
   return launch_lds("gemm_nt_base", fwd::k_gemm_fwd<FMT, false, SHARED>, dim3((unsigned)p.nblocks),
                     dim3(fwd::THREADS), (size_t)fwd::lds_bytes(), p, st);
 }
@@ -568,7 +574,6 @@ big::Params big_params(const Mat &A, const PackedW &W, int64_t R, const Mat &A2,
   p.nblocks = p.nslots * p.tiles_n;
   p.nfull = p.nblocks;
   p.ntail = 0;
-  p.short_tiles = fwd_tiles_policy() == 5 ? 0 : 1;
   p.tab = nf4_table();
   p.ksplit = 1;
   p.split_steps = 1 << 30;
@@ -1085,6 +1090,12 @@ lora4_status scratch_for_current_device(void **out) {
   return LORA4_OK;
 }
 
+// Grid of the packers that take one lane per 8 elements (grid-strided past
+// PACK_MAX_BLOCKS workgroups).
+dim3 pack_grid(int64_t N, int64_t K) {
+  return dim3((unsigned)std::min<int64_t>(ceil_div(N * (K / 8), PACK_THREADS), PACK_MAX_BLOCKS));
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -1362,12 +1373,6 @@ lora4_status clear_padding(int64_t N, int64_t K, int32_t format, uint8_t *codes,
                   reinterpret_cast<uint16_t *>(codes), nc, (uint16_t)0));
   return launch_args("fill_zero", k_fill_u16, dim3((unsigned)ceil_div(ns, 256)), dim3(256), st,
                      reinterpret_cast<uint16_t *>(scales), ns, (uint16_t)0);
-}
-
-// Grid of the packers that take one lane per 8 elements (grid-strided past
-// PACK_MAX_BLOCKS workgroups).
-dim3 pack_grid(int64_t N, int64_t K) {
-  return dim3((unsigned)std::min<int64_t>(ceil_div(N * (K / 8), PACK_THREADS), PACK_MAX_BLOCKS));
 }
 
 lora4_status quant_pack_nf4(const uint16_t *W_bf16, int64_t N, int64_t K, int32_t double_quant,
