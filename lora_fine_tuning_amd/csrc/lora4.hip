@@ -314,13 +314,38 @@ struct Plan {
   int tq_a, tq_b;     // TN Q tiles (dA over K, dB over N)
   int msplit_a, msplit_b;
   FwdSched fs;                // forward base GEMM schedule
+  int lds_splits;             // reduction splits of the 128 x 128 base GEMM (forward or dgrad), 1: none
   // workspace offsets
-  size_t off_sz, off_zw, off_dz, off_part, off_part_b, off_party, off_skpart, bytes;
+  size_t off_sz, off_zw, off_dz, off_part, off_part_b, off_party, off_skpart, off_partx, bytes;
 };
 
 constexpr int BM_MAIN = 128, BN_MAIN = 128;
 constexpr int BM_SKINNY = 128;
 constexpr int TN_BQ = 128;
+
+int cu_count();
+bool big_fits(int64_t ld_a, int64_t M, const PackedW &W);
+bool use_big(int64_t M, int64_t Nc, int64_t E);
+
+// Reduction splits for the 128 x 128 base GEMM on a grid of `blocks`
+// workgroups (R: reduction length): when the grid fills less than half the
+// CUs, the reduction is cut into ranges of at least two 64-deep steps so that
+// the grid approaches one workgroup per CU (fp32 partials of at most 64 MiB,
+// summed in range order by k_reduce_bf16). 1: no split.
+constexpr int LDS_SPLIT_MIN_STEPS = 2;
+constexpr int64_t LDS_SPLIT_MAX_BYTES = (int64_t)64 << 20;
+int lds_splits_for(int64_t blocks, int64_t R, int64_t M, int64_t Nc) {
+  const int64_t cus = cu_count();
+  if (R <= 0 || blocks <= 0 || 2 * blocks > cus) return 1;
+  const int64_t steps = ceil_div(R, BK);
+  int64_t k = std::min<int64_t>(steps / LDS_SPLIT_MIN_STEPS, cus / blocks);
+  k = std::min<int64_t>(k, LDS_SPLIT_MAX_BYTES / std::max<int64_t>(1, M * Nc * 4));
+  if (k < 2) return 1;
+  // equal ranges of whole steps; the count actually needed for them
+  const int64_t per = ceil_div(steps, k);
+  return (int)ceil_div(steps, per);
+}
+int64_t lds_split_len(int splits, int64_t R) { return ceil_div(ceil_div(R, BK), (int64_t)splits) * BK; }
 
 // cap: the workspace there is (the allocation-free forward's fixed scratch);
 // a forward whose split partials would not fit runs the tiles unsplit.
@@ -347,6 +372,14 @@ Plan make_plan(int which, const Base &b, int64_t M, int r, size_t cap = SIZE_MAX
   p.msplit_a = msplit(p.tq_a);
   p.msplit_b = msplit(p.tq_b);
   p.fs = fwd_sched(M, p.N, p.K, p.E, packed_of(b));
+  p.lds_splits = 1;
+  {
+    const PackedW pw = packed_of(b);
+    if (which == 0 && !p.fs.use)
+      p.lds_splits = lds_splits_for(p.row_slots * ceil_div(p.N, BN_MAIN), p.K, M, p.N);
+    if (which == 1 && !(big_fits(p.N, M, pw) && use_big(M, p.K, pw.shared ? 1 : p.E)))
+      p.lds_splits = lds_splits_for(p.row_slots * ceil_div(p.K, BN_MAIN), p.N, M, p.K);
+  }
 
   const size_t mr2 = align256((size_t)M * r * 2);
   size_t off = 0;
@@ -369,11 +402,18 @@ Plan make_plan(int which, const Base &b, int64_t M, int r, size_t cap = SIZE_MAX
     p.off_part_b = off + align256((size_t)p.msplit_a * p.E * r * p.K * 4);
     off = p.off_part_b + align256((size_t)p.msplit_b * p.E * r * p.N * 4);
   }
+  p.off_partx = off;  // fp32 partials of the split 128 x 128 base GEMM
+  if (p.lds_splits > 1) off += align256((size_t)p.lds_splits * M * (which == 0 ? p.N : p.K) * 4);
   p.bytes = std::max<size_t>(off, 256);   // never 0: 0 reports invalid arguments
   if (p.bytes > cap && which == 0 && p.fs.use && p.fs.split_tiles > 0) {
     p.bytes -= align256((size_t)p.fs.split_tiles * p.fs.ksplit * fwd::BM * fwd::BN * 4);
     p.off_part = p.off_party;
+    p.off_partx = p.off_party;
     p.fs = FWD_LDS_KERNEL;   // the 128 x 128 kernel, no partials
+  }
+  if (p.bytes > cap && p.lds_splits > 1) {
+    p.bytes -= align256((size_t)p.lds_splits * M * (which == 0 ? p.N : p.K) * 4);
+    p.lds_splits = 1;        // unsplit, no partials
   }
   return p;
 }
@@ -616,7 +656,7 @@ bool dgrad_taken(int64_t R, int64_t ld_a, int64_t M, const PackedW &W, int64_t N
 // (split partials in `party`, then reduced into the output), else the
 // 128 x 128 kernel.
 lora4_status run_nt_main_fmt(int fmt, const NtParams &p, dim3 grid, const Plan &pl, float *party,
-                             const TailParts *tp, hipStream_t st) {
+                             float *partx, const TailParts *tp, hipStream_t st) {
   if (fwd_regs_taken(p.R, pl)) {
     big::Params q = big_params(p.A, p.W, p.R, p.A2, p.B2, p.r2, p.M, p.Nc, p.offsets, p.groups, p.out.C,
                                p.out.ldc);
@@ -642,13 +682,26 @@ lora4_status run_nt_main_fmt(int fmt, const NtParams &p, dim3 grid, const Plan &
     return LORA4_OK;
   }
   if (tp) return LORA4_ERR_UNIMPLEMENTED;   // (callers check the same predicates)
-  switch (fmt) {
-    case LORA4_NF4: return run_nt_main<FMT_NF4>(p, grid, st);
-    case LORA4_NF4_DQ: return run_nt_main<FMT_NF4_DQ>(p, grid, st);
-    case LORA4_MXFP4: return run_nt_main<FMT_MXFP4>(p, grid, st);
-    case LORA4_NVFP4: return run_nt_main<FMT_NVFP4>(p, grid, st);
+  NtParams q = p;
+  const bool split = pl.lds_splits > 1 && p.R > 0 && partx && p.out.C && p.out.ldc == p.Nc;
+  if (split) {
+    q.Rsplit = lds_split_len(pl.lds_splits, p.R);
+    q.out.part = partx;
+    q.out.part_stride = p.M * p.Nc;
+    grid.z = (unsigned)pl.lds_splits;
   }
-  return LORA4_ERR_FORMAT;
+  lora4_status r = LORA4_ERR_FORMAT;
+  switch (fmt) {
+    case LORA4_NF4: r = run_nt_main<FMT_NF4>(q, grid, st); break;
+    case LORA4_NF4_DQ: r = run_nt_main<FMT_NF4_DQ>(q, grid, st); break;
+    case LORA4_MXFP4: r = run_nt_main<FMT_MXFP4>(q, grid, st); break;
+    case LORA4_NVFP4: r = run_nt_main<FMT_NVFP4>(q, grid, st); break;
+  }
+  TRY(r);
+  if (split)
+    TRY(reduce_bf16("reduce_y", partx, pl.lds_splits, p.M * p.Nc, p.M * p.Nc, p.out.C, p.out.alpha, nullptr, 0.0f,
+                    st));
+  return LORA4_OK;
 }
 
 template <int FMT>
@@ -656,7 +709,8 @@ lora4_status run_nn_main(const NnParams &p, dim3 grid, hipStream_t st) {
   return launch("gemm_nn_dgrad", k_gemm_nn<FMT, BM_MAIN, BN_MAIN, 2>, grid, dim3(THREADS), p, st);
 }
 
-lora4_status run_nn_main_fmt(int fmt, const NnParams &p, dim3 grid, const TailParts *tp, hipStream_t st) {
+lora4_status run_nn_main_fmt(int fmt, const NnParams &p, dim3 grid, const Plan &pl, float *partx,
+                             const TailParts *tp, hipStream_t st) {
   if (dgrad_taken(p.R, p.A.ld, p.M, p.W, p.Nc, p.groups)) {
     big::Params q = big_params(p.A, p.W, p.R, p.A2, p.B2, p.r2, p.M, p.Nc, p.offsets, p.groups, p.out.C,
                                p.out.ldc);
@@ -664,13 +718,26 @@ lora4_status run_nn_main_fmt(int fmt, const NnParams &p, dim3 grid, const TailPa
     return run_dgrad_fmt(fmt, q, st);
   }
   if (tp) return LORA4_ERR_UNIMPLEMENTED;   // (callers check the same predicates)
-  switch (fmt) {
-    case LORA4_NF4: return run_nn_main<FMT_NF4>(p, grid, st);
-    case LORA4_NF4_DQ: return run_nn_main<FMT_NF4_DQ>(p, grid, st);
-    case LORA4_MXFP4: return run_nn_main<FMT_MXFP4>(p, grid, st);
-    case LORA4_NVFP4: return run_nn_main<FMT_NVFP4>(p, grid, st);
+  NnParams q = p;
+  const bool split = pl.lds_splits > 1 && p.R > 0 && partx && p.out.C && p.out.ldc == p.Nc;
+  if (split) {
+    q.Rsplit = lds_split_len(pl.lds_splits, p.R);
+    q.out.part = partx;
+    q.out.part_stride = p.M * p.Nc;
+    grid.z = (unsigned)pl.lds_splits;
   }
-  return LORA4_ERR_FORMAT;
+  lora4_status r = LORA4_ERR_FORMAT;
+  switch (fmt) {
+    case LORA4_NF4: r = run_nn_main<FMT_NF4>(q, grid, st); break;
+    case LORA4_NF4_DQ: r = run_nn_main<FMT_NF4_DQ>(q, grid, st); break;
+    case LORA4_MXFP4: r = run_nn_main<FMT_MXFP4>(q, grid, st); break;
+    case LORA4_NVFP4: r = run_nn_main<FMT_NVFP4>(q, grid, st); break;
+  }
+  TRY(r);
+  if (split)
+    TRY(reduce_bf16("reduce_dx", partx, pl.lds_splits, p.M * p.Nc, p.M * p.Nc, p.out.C, p.out.alpha, nullptr, 0.0f,
+                    st));
+  return LORA4_OK;
 }
 
 // Both jobs share P (the rank) and so the P tiling; grid sizes of the two are
@@ -717,6 +784,9 @@ struct SkSched {
 };
 constexpr int64_t SK_TARGET_WG = 512;   // workgroups wanted per pass
 constexpr int64_t SK_MAX_RANGES = 4;    // (8 measured 0.5% slower on the 8B layer set)
+// below this many bytes of activations one range: the pass is short, and its
+// partials would cost a reduction launch of its own on the small grids
+constexpr int64_t SK_SPLIT_MIN_BYTES = (int64_t)4 << 20;
 SkSched sk_sched(int64_t M, int64_t R, int r, int64_t E) {
   SkSched f{};
   f.tj = r <= 16 ? 1 : r <= 32 ? 2 : r <= 64 ? 4 : 8;
@@ -728,6 +798,7 @@ SkSched sk_sched(int64_t M, int64_t R, int r, int64_t E) {
   const int64_t chunks = std::max<int64_t>(1, ceil_div(R, 32));
   int64_t want = ceil_div(SK_TARGET_WG, blocks);
   want = std::max<int64_t>(1, std::min<int64_t>({want, chunks / 8, SK_MAX_RANGES}));
+  if (M * R * 2 < SK_SPLIT_MIN_BYTES) want = 1;
   f.klen = ceil_div(chunks, want) * 32;
   f.ranges = (int)ceil_div(chunks * 32, f.klen);
   return f;
@@ -1183,19 +1254,20 @@ static lora4_status forward_impl(const Base &bs, const uint16_t *X, int64_t M, c
   p.tab = nf4_table();
   dim3 grid((unsigned)ceil_div(pl.N, BN_MAIN), (unsigned)pl.row_slots, 1);
   float *party = ws_at<float>(workspace, pl.off_party);
-  TRY(run_nt_main_fmt(W->format, p, grid, pl, party, z_tail ? &ztp : nullptr, st));
+  float *partx = ws_at<float>(workspace, pl.off_partx);
+  TRY(run_nt_main_fmt(W->format, p, grid, pl, party, partx, z_tail ? &ztp : nullptr, st));
   if (Y_base) {
     NtParams q = p;
     q.r2 = 0;
     q.out.C = Y_base;
-    TRY(run_nt_main_fmt(W->format, q, grid, pl, party, nullptr, st));
+    TRY(run_nt_main_fmt(W->format, q, grid, pl, party, partx, nullptr, st));
   }
   if (Y_lora) {
     NtParams q = p;
     q.R = 0;
     q.Rsplit = 64;
     q.out.C = Y_lora;
-    TRY(run_nt_main_fmt(W->format, q, grid, pl, party, nullptr, st));
+    TRY(run_nt_main_fmt(W->format, q, grid, pl, party, partx, nullptr, st));
   }
   return LORA4_OK;
 }
@@ -1261,7 +1333,8 @@ static lora4_status backward_impl(const Base &bs, const uint16_t *X, const uint1
     p.out = GemmOut{dX, pl.K, nullptr, 0, 1.0f};
     p.tab = nf4_table();
     dim3 grid((unsigned)ceil_div(pl.K, BN_MAIN), (unsigned)pl.row_slots, 1);
-    TRY(run_nn_main_fmt(W->format, p, grid, dz_tail ? &dztp : nullptr, st));
+    TRY(run_nn_main_fmt(W->format, p, grid, pl, ws_at<float>(workspace, pl.off_partx), dz_tail ? &dztp : nullptr,
+                        st));
   }
 
   // dA = dZ^T X and dB^T = Z^T dY, split over rows, in one launch; one launch
