@@ -225,6 +225,46 @@ def test_forward_split_grouped(monkeypatch):
     assert rel(got["Y"], fo["Y"]) <= TOL
 
 
+@pytest.mark.parametrize("grouped", [False, True])
+def test_small_grid_splits_the_reduction(grouped, monkeypatch):
+    """A 128 x 128 grid that fills less than half the GPU (256 tokens x 1024:
+    16 workgroups, 40 with three groups) splits the base GEMMs' reduction into
+    ranges of fp32 partials that one launch sums in range order (reduce_y,
+    reduce_dx), the rank-r term added in the last range. Checked against the
+    oracle, with an empty group, and bitwise against a second identical call."""
+    monkeypatch.setenv("LORA4_BIG", "0")
+    M, K, N, r = 256, 1024, 1024, 16
+    offs = [0, 100, 100, 256] if grouped else None
+    lay = synth.small_layer(M, K, N, r, fmt=synth.NF4, index=61, experts=3 if grouped else 1, offsets=offs)
+    print_case("small grid split", offs)
+    t = synth.inputs(lay)
+    L.timing_enable(True)
+    try:
+        L.timing_collect()
+        got = _run(lay, t, offsets=offs)
+        names = set(L.timing_collect())
+    finally:
+        L.timing_enable(False)
+    assert "reduce_y" in names and "reduce_dx" in names, names
+    again = _run(lay, t, offsets=offs)
+    for k in ("Y", "Z", "dX", "dA", "dB"):
+        assert np.array_equal(got[k], again[k]), k
+    if not grouped:
+        _check_all(got, _oracle(lay, t))
+        return
+    Ws = [dequant_rows(t["W"][e], np.arange(N), synth.NF4) for e in range(3)]
+    As = [f64(a) for a in t["A"]]
+    Bs = [f64(b) for b in t["B"]]
+    fo = lora.grouped_forward(f64(t["X"]), Ws, As, Bs, lay.s, offs)
+    bo = lora.grouped_backward(f64(t["X"]), Ws, As, Bs, lay.s, f64(t["dY"]), offs)
+    for k in ("Y", "Z"):
+        assert rel(got[k], fo[k]) <= TOL, k
+    assert rel(got["dX"], bo["dX"]) <= TOL
+    for e in (0, 2):
+        assert rel(got["dA"][e], bo["dA"][e]) <= TOL and rel(got["dB"][e], bo["dB"][e]) <= TOL, e
+    assert not (got["dA"][1] & 0x7FFF).any() and not (got["dB"][1] & 0x7FFF).any()   # (±0)
+
+
 def test_forward_two_rounds_of_tiles(monkeypatch):
     """320 output tiles (more than one per CU): the XCD-aware block order over
     a partial second round. Checked on sampled columns of the first 96 column
