@@ -302,7 +302,7 @@ struct FwdSched {
 constexpr FwdSched FWD_LDS_KERNEL{false, 0, 0, 1, 1 << 30, 0, false};
 FwdSched fwd_sched(int64_t M, int64_t N, int64_t K, int64_t E, const PackedW &W);
 struct SkSched;
-size_t sk_part_bytes_for(int64_t M, int64_t R, int r, int64_t E);
+size_t sk_part_bytes_for(int64_t M, int64_t R, int r, int64_t E, int transb);
 lora4_status reduce_bf16(const char *name, const float *part, int splits, int64_t stride, int64_t n,
                          uint16_t *out1, float a1, uint16_t *out2, float a2, hipStream_t st);
 
@@ -390,8 +390,8 @@ Plan make_plan(int which, const Base &b, int64_t M, int r, size_t cap = SIZE_MAX
   p.off_dz = p.off_sz;
   p.off_skpart = off;  // fp32 partials of the rank-r passes (Z, then dZ)
   {
-    size_t b = sk_part_bytes_for(M, p.K, r, p.E);
-    if (which == 1) b = std::max(b, sk_part_bytes_for(M, p.N, r, p.E));
+    size_t b = sk_part_bytes_for(M, p.K, r, p.E, 0);
+    if (which == 1) b = std::max(b, sk_part_bytes_for(M, p.N, r, p.E, 1));
     off += b;
   }
   p.off_party = off;  // forward: fp32 partials of the split base GEMM
@@ -773,28 +773,68 @@ lora4_status run_rows_tj(int transb, const skinny::Params &p, dim3 grid, hipStre
   return launch("rows_skinny_z", skinny::k_rows_skinny<TM, TJ, 0>, grid, dim3(skinny::THREADS), p, st);
 }
 
-// Rank-r row-block pass schedule: rows per workgroup 16 tm, columns 16 tj, and
-// the reduction split into at most 4 `ranges` of klen elements so that the
-// grid has about two workgroups per CU (each range at least 8 chunks of 32).
-// Rank 16 takes 32-row blocks (512 workgroups on 4096 rows; 64-row blocks
-// and 256 workgroups measured 0.3% slower on the 8B layer set).
+// Rank-r row-block pass schedule. Two kernels:
+// * k_rows_lds (whole 16-byte pieces: R % 8 == 0, and r % 8 == 0 for dZ, whose
+//   small operand B is r-contiguous): 64 tm rows per workgroup, ns stages of
+//   64 deep; the reduction split into at most 4 `ranges` so that about one
+//   round of workgroups (as many as fit the CUs' LDS) covers the GPU, one range
+//   at rank 128 (the GEMM tails then read bf16 Z instead of four fp32 partials
+//   of 128 columns);
+// * k_rows_skinny otherwise: 16 tm rows, the four waves taking the range's
+//   32-wide chunks in turn, ranges so that the grid has about two workgroups
+//   per CU. Rank 16 takes 32-row blocks (512 workgroups on 4096 rows; 64-row
+//   blocks and 256 workgroups measured 0.3% slower on the 8B layer set).
+// Columns: 16 tj per workgroup (grid.y covers larger r).
 struct SkSched {
   int tm, tj, ranges;
   int64_t klen;
+  bool lds;
+  int ns;
 };
 constexpr int64_t SK_TARGET_WG = 512;   // workgroups wanted per pass
 constexpr int64_t SK_MAX_RANGES = 4;    // (8 measured 0.5% slower on the 8B layer set)
 // below this many bytes of activations one range: the pass is short, and its
 // partials would cost a reduction launch of its own on the small grids
 constexpr int64_t SK_SPLIT_MIN_BYTES = (int64_t)4 << 20;
-SkSched sk_sched(int64_t M, int64_t R, int r, int64_t E) {
+constexpr int64_t LDS_PER_CU = 160 * 1024;
+
+bool sk_lds_fits(int64_t R, int r, int transb) {
+  const int64_t lim = (int64_t)1 << 31;
+  return R % 8 == 0 && (!transb || r % 8 == 0) && R * 2 * 128 < lim && (int64_t)r * R * 2 < lim;
+}
+
+size_t sk_lds_bytes(int tm, int tj, int ns) {
+  switch (tj) {
+    case 1: return skinny::LdsRing<1, 1, 0, 6>::bytes();
+    case 2: return skinny::LdsRing<1, 2, 0, 6>::bytes();
+    case 4: return skinny::LdsRing<2, 4, 0, 4>::bytes();
+    default: return skinny::LdsRing<2, 8, 0, 4>::bytes();
+  }
+}
+
+SkSched sk_sched(int64_t M, int64_t R, int r, int64_t E, int transb) {
   SkSched f{};
   f.tj = r <= 16 ? 1 : r <= 32 ? 2 : r <= 64 ? 4 : 8;
+  f.lds = sk_lds_fits(R, r, transb);
+  const int64_t jt = ceil_div(r, 16 * f.tj);
+  if (f.lds) {
+    f.tm = f.tj >= 4 ? 2 : 1;
+    f.ns = f.tj >= 4 ? 4 : 6;
+    const int64_t blocks = (ceil_div(std::max<int64_t>(M, 1), 64 * f.tm) + (E > 1 ? E : 0)) * jt;
+    const int64_t steps = std::max<int64_t>(1, ceil_div(R, 64));
+    const int64_t round = cu_count() * std::max<int64_t>(1, LDS_PER_CU / (int64_t)sk_lds_bytes(f.tm, f.tj, f.ns));
+    int64_t want = std::max<int64_t>(1, round / blocks);
+    want = std::max<int64_t>(1, std::min<int64_t>({want, steps / 4, SK_MAX_RANGES}));
+    if (f.tj >= 8 || M * R * 2 < SK_SPLIT_MIN_BYTES) want = 1;
+    f.klen = ceil_div(steps, want) * 64;
+    f.ranges = (int)ceil_div(steps * 64, f.klen);
+    return f;
+  }
   // 64-row blocks from rank 17 on: every block re-reads the small operand
   // (A or B) over its range, so taller blocks cut that traffic (at rank 128,
   // 16-row blocks read A from L2 eight times as often as X itself)
   f.tm = f.tj == 1 ? 2 : 4;
-  const int64_t blocks = (ceil_div(std::max<int64_t>(M, 1), 16 * f.tm) + (E > 1 ? E : 0)) * ceil_div(r, 16 * f.tj);
+  const int64_t blocks = (ceil_div(std::max<int64_t>(M, 1), 16 * f.tm) + (E > 1 ? E : 0)) * jt;
   const int64_t chunks = std::max<int64_t>(1, ceil_div(R, 32));
   int64_t want = ceil_div(SK_TARGET_WG, blocks);
   want = std::max<int64_t>(1, std::min<int64_t>({want, chunks / 8, SK_MAX_RANGES}));
@@ -804,15 +844,23 @@ SkSched sk_sched(int64_t M, int64_t R, int r, int64_t E) {
   return f;
 }
 
-size_t sk_part_bytes_for(int64_t M, int64_t R, int r, int64_t E) {
-  const SkSched f = sk_sched(M, R, r, E);
+size_t sk_part_bytes_for(int64_t M, int64_t R, int r, int64_t E, int transb) {
+  const SkSched f = sk_sched(M, R, r, E, transb);
   return f.ranges > 1 ? align256((size_t)f.ranges * M * r * 4) : 0;
+}
+
+template <int TM, int TJ, int NS>
+lora4_status run_rows_lds(int transb, const skinny::Params &p, dim3 grid, hipStream_t st) {
+  const size_t lds = skinny::LdsRing<TM, TJ, 0, NS>::bytes();
+  if (transb)
+    return launch_lds("rows_skinny_dz", skinny::k_rows_lds<TM, TJ, 1, NS>, grid, dim3(skinny::THREADS), lds, p, st);
+  return launch_lds("rows_skinny_z", skinny::k_rows_lds<TM, TJ, 0, NS>, grid, dim3(skinny::THREADS), lds, p, st);
 }
 
 lora4_status rows_skinny(int transb, const uint16_t *act, int64_t ld_act, const uint16_t *w, int64_t ld_w,
                          int64_t g_w, int64_t R, int64_t M, int r, const int64_t *offs, int64_t E, uint16_t *o1,
                          float a1, uint16_t *o2, float a2, float *part, bool defer_reduce, hipStream_t st) {
-  const SkSched f = sk_sched(M, R, r, E);
+  const SkSched f = sk_sched(M, R, r, E, transb);
   skinny::Params p{};
   p.act = act;
   p.ld_act = ld_act;
@@ -830,10 +878,17 @@ lora4_status rows_skinny(int transb, const uint16_t *act, int64_t ld_act, const 
   p.alpha2 = a2;
   p.klen = f.klen;
   p.part = part;
-  const int64_t slots = ceil_div(std::max<int64_t>(M, 1), 16 * f.tm) + (E > 1 ? E : 0);
+  const int64_t slots = ceil_div(std::max<int64_t>(M, 1), (f.lds ? 64 : 16) * f.tm) + (E > 1 ? E : 0);
   dim3 grid((unsigned)slots, (unsigned)ceil_div(r, 16 * f.tj), (unsigned)f.ranges);
   lora4_status st1 = LORA4_ERR_UNIMPLEMENTED;
-  switch (f.tj) {
+  if (f.lds) {
+    switch (f.tj) {
+      case 1: st1 = run_rows_lds<1, 1, 6>(transb, p, grid, st); break;
+      case 2: st1 = run_rows_lds<1, 2, 6>(transb, p, grid, st); break;
+      case 4: st1 = run_rows_lds<2, 4, 4>(transb, p, grid, st); break;
+      default: st1 = run_rows_lds<2, 8, 4>(transb, p, grid, st); break;
+    }
+  } else switch (f.tj) {
     case 1:
       st1 = f.tm == 2 ? run_rows_tj<2, 1>(transb, p, grid, st) : run_rows_tj<4, 1>(transb, p, grid, st);
       break;
@@ -1233,7 +1288,7 @@ static lora4_status forward_impl(const Base &bs, const uint16_t *X, int64_t M, c
   // the partials are reduced into Z and s Z here.
   uint16_t *sZ = ws_at<uint16_t>(workspace, pl.off_sz);
   float *skpart = ws_at<float>(workspace, pl.off_skpart);
-  const SkSched zs = sk_sched(M, pl.K, r, pl.E);
+  const SkSched zs = sk_sched(M, pl.K, r, pl.E, 0);
   const bool z_tail = zs.ranges > 1 && zs.ranges <= big::A2_MAX_PARTS && fwd_regs_taken(pl.K, pl);
   const TailParts ztp{skpart, zs.ranges, s, Z, 1.0f, Y_lora ? sZ : nullptr, s};
   TRY(z_pass(pl, W, X, A, group_offsets, Z, 1.0f, sZ, s, skpart, z_tail, st));
@@ -1309,7 +1364,7 @@ static lora4_status backward_impl(const Base &bs, const uint16_t *X, const uint1
   // into ranges and the 256 x 256 dgrad kernel, that kernel's tail adds the
   // fp32 range partials (its column-tile-0 blocks store dZ for the dA pass).
   float *skpart = ws_at<float>(workspace, pl.off_skpart);
-  const SkSched dzs = sk_sched(M, pl.N, r, pl.E);
+  const SkSched dzs = sk_sched(M, pl.N, r, pl.E, 1);
   const bool dz_tail = dzs.ranges > 1 && dzs.ranges <= big::A2_MAX_PARTS &&
                        dgrad_taken(pl.N, pl.N, M, packed_of(bs), pl.K, pl.E);
   const TailParts dztp{skpart, dzs.ranges, s, dZ, s, nullptr, 0.0f};
@@ -1541,7 +1596,7 @@ lora4_status lora4_forward_mx(const lora4_W *W, const uint16_t *X, int64_t M, co
   // where there are several (and its column-tile-0 blocks store Z)
   uint16_t *sZ = ws_at<uint16_t>(workspace, pl.off_sz);
   float *skpart = ws_at<float>(workspace, pl.off_skpart);
-  const SkSched zs = sk_sched(M, pl.K, r, 1);
+  const SkSched zs = sk_sched(M, pl.K, r, 1, 0);
   const bool z_tail = zs.ranges > 1 && zs.ranges <= big::A2_MAX_PARTS;
   const TailParts ztp{skpart, zs.ranges, s, Z, 1.0f, nullptr, 0.0f};
   TRY(z_pass(pl, W, X, A, nullptr, Z, 1.0f, sZ, s, skpart, z_tail, st));

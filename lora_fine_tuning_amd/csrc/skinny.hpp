@@ -20,6 +20,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "gemm_big.hpp"
 
 namespace lora4 {
 namespace skinny {
@@ -209,6 +210,186 @@ __global__ __launch_bounds__(THREADS) void k_rows_skinny(Params p) {
       }
     }
   }
+}
+
+// The same products through an LDS ring, for whole 16-byte pieces (the
+// reduction length, both leading dimensions and, for dZ, the rank multiples of
+// 8). Every load is a direct-to-LDS load of one 16-byte piece per lane, eight
+// lanes per 128-byte row segment, so each load instruction reads whole cache
+// lines (the register path above reads 64 bytes of each of 16 rows, half
+// lines, and measured 2-3 TB/s at ranks 64 and 128). A step is 64 deep: the
+// activation tile [BM rows][64] in the conflict-free tile64 layout and the
+// small operand's tile (A [BN rows][64] in the same layout, or B [64 rows][BN]
+// with its 16-byte pieces XOR-swizzled per row for the transposing reads).
+// The four waves split the rows (wave w: rows 16 TM w ..) and share the small
+// operand's tile, so it is read once per workgroup and no partial sums cross
+// waves. NS stages, loads issued NS - 1 steps ahead; the loads past the range
+// are issued as out-of-range loads (zeros), so every wave has the same number
+// of loads in flight per step.
+template <int TM, int TJ, int TRANSB, int NS>
+struct LdsRing {
+  static constexpr int BM = 64 * TM, BN = 16 * TJ;
+  static constexpr int XT = BM * 64;                      // activation stage, bf16 elements
+  static constexpr int WB = BN / 8;                       // 1 KB blocks of the small operand's stage
+  static constexpr int WPW = (WB + 3) / 4;                // of them per wave (padded with empty loads)
+  static constexpr int ST = XT + WPW * 4 * 512;           // stage size, bf16 elements
+  static constexpr int LPS = BM / 32 + WPW;               // loads per wave per step
+  static constexpr int bytes() { return NS * ST * 2; }
+};
+
+// B stage [64][BN] (TRANSB 1): 16-byte piece q of row n stored at q ^ bsw(n),
+// which spreads the four rows of a transposing read over different banks.
+template <int BN>
+__device__ __forceinline__ int bsw(int n) {
+  return BN >= 64 ? (n & 3) << 1 : 0;
+}
+
+template <int TM, int TJ, int TRANSB, int NS>
+__global__ __launch_bounds__(THREADS) void k_rows_lds(Params p) {
+  using Ring = LdsRing<TM, TJ, TRANSB, NS>;
+  constexpr int BM = Ring::BM, BN = Ring::BN, XT = Ring::XT, WB = Ring::WB, WPW = Ring::WPW, ST = Ring::ST;
+  constexpr int PPR = BN / 8;   // 16-byte pieces per row of the B stage
+  extern __shared__ __attribute__((aligned(16))) uint16_t ring[];
+
+  const RowTile rt = map_row_tile(blockIdx.x, BM, p.offsets, p.groups, p.M);
+  if (rt.group < 0) return;
+  const int g = rt.group;
+  const int64_t row0 = rt.row0, row_end = rt.row_end;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+
+  // this workgroup's range of 64-deep steps, and where its loads stop
+  const int64_t nsteps_all = (p.R + 63) / 64;
+  const int64_t s_begin = (int64_t)blockIdx.z * (p.klen / 64);
+  const int64_t s_end = s_begin + p.klen / 64 < nsteps_all ? s_begin + p.klen / 64 : nsteps_all;
+  const int nsteps = s_end > s_begin ? (int)(s_end - s_begin) : 0;
+  const int64_t k_lim = s_end * 64 < p.R ? s_end * 64 : p.R;
+
+  // activations: rows of this tile, 8 (4 c + wave) + lane / 8 (c < BM / 32)
+  const big::rsrc_t x_rsrc =
+      big::make_rsrc(p.act + row0 * p.ld_act, big::clamp_bytes((row_end - row0) * p.ld_act * 2));
+  const int x_kq = tile64_dma_chunk(lane, wave) * 8;
+  const uint32_t x_voff0 = (uint32_t)(((wave * 8 + (lane >> 3)) * p.ld_act + x_kq) * 2);
+  const uint32_t x_cstep = (uint32_t)(32 * p.ld_act * 2);
+
+  // the small operand of this group: A [r][R] (TRANSB 0) or B [R][r] (TRANSB 1)
+  const uint16_t *w = p.w + g * p.g_w;
+  const big::rsrc_t w_rsrc = big::make_rsrc(
+      w, big::clamp_bytes((TRANSB ? p.R * p.ld_w : (int64_t)p.r * p.ld_w) * 2));
+  // per load i < WPW of this wave: the piece's offset at step 0 (or OOB) and
+  // the element it covers along the reduction (to cut at k_lim)
+  uint32_t w_voff[WPW];
+  int w_k[WPW];
+#pragma unroll
+  for (int i = 0; i < WPW; ++i) {
+    const int b = wave + 4 * i;   // 1 KB block of the stage
+    w_voff[i] = big::OOB;
+    w_k[i] = 0;
+    if (b < WB) {
+      if constexpr (TRANSB == 0) {
+        const int j = 8 * b + (lane >> 3);                       // A row (rank index)
+        const int kq = tile64_dma_chunk(lane, b) * 8;
+        w_k[i] = kq;
+        if (j < p.r) w_voff[i] = (uint32_t)((j * p.ld_w + kq) * 2);
+      } else {
+        const int P = b * 64 + lane;                             // flat piece of the [64][BN] stage
+        const int n = P / PPR, q = (P % PPR) ^ bsw<BN>(n);
+        w_k[i] = n;
+        if (q * 8 < p.r) w_voff[i] = (uint32_t)((n * p.ld_w + q * 8) * 2);
+      }
+    }
+  }
+
+  auto issue = [&](int s) {
+    uint16_t *st = ring + (s % NS) * ST;
+    const int64_t k0 = (s_begin + s) * 64;
+    const bool x_edge = k0 + x_kq >= k_lim;
+#pragma unroll
+    for (int c = 0; c < BM / 32; ++c)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc, (__attribute__((address_space(3))) void *)(st + (c * 4 + wave) * 512),
+                                               16, x_edge ? big::OOB : x_voff0 + c * x_cstep, (int)(k0 * 2), 0, 0);
+#pragma unroll
+    for (int i = 0; i < WPW; ++i) {
+      const uint32_t vo = w_voff[i];   // (the builtin's offset taken straight from the array
+                                       // leaves the kernel without its host-side launch stub)
+      const uint32_t off = vo == big::OOB || k0 + w_k[i] >= k_lim ? big::OOB : vo;
+      const int so = TRANSB ? (int)(k0 * p.ld_w * 2) : (int)(k0 * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (__attribute__((address_space(3))) void *)(st + XT + (wave + 4 * i) * 512),
+                                               16, off, so, 0, 0);
+    }
+  };
+
+  f32x4_t acc[TM][TJ];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int s) {
+    const uint16_t *xs = ring + (s % NS) * ST;
+    const uint16_t *ws = xs + XT;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4_t af[TM], bf[TJ];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = lds_read_b128(xs + tile64_swz(16 * (TM * wave + i) + lr, ks * 4 + lg));
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        if constexpr (TRANSB == 0) {
+          bf[j] = lds_read_b128(ws + tile64_swz(16 * j + lr, ks * 4 + lg));
+        } else {
+          // lane (column 16 j + lr, group lg): reduction rows 32 ks + 8 lg .. +7
+          const int n = 32 * ks + 8 * lg + (lr >> 2), c = 16 * j + (lr & 3) * 4;
+          const u32x2_t lo = lds_read_tr16(ws + n * BN + (((c >> 3) ^ bsw<BN>(n)) << 3) + (c & 7));
+          const u32x2_t hi = lds_read_tr16(ws + (n + 4) * BN + (((c >> 3) ^ bsw<BN>(n + 4)) << 3) + (c & 7));
+          bf[j] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_16x16x32(af[i], bf[j], acc[i][j]);
+    }
+  };
+
+  // every step, each wave waits for its own loads of that step (those of the
+  // NS - 2 later steps may stay in flight), then meets the others: the step's
+  // stage is complete and the stage read one step earlier is free again
+  constexpr int VM = (NS - 2) * Ring::LPS;
+  static_assert(VM < 64, "vmcnt field");
+  constexpr int VMCNT = (VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14);
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) issue(s);
+  for (int s = 0; s < nsteps; ++s) {
+    __builtin_amdgcn_s_waitcnt(VMCNT);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(s + NS - 1);
+    compute(s);
+  }
+  // the loads past the range still land (zeros): drain them before the
+  // workgroup's LDS can be handed to another
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // lane holds rows 4 lg + e of each 16-row block, column lr of each 16-column block
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t row = row0 + 16 * (TM * wave + i) + 4 * lg + e;
+        const int col = 16 * j + lr;
+        if (row >= row_end || col >= p.r) continue;
+        const float v = acc[i][j][e];
+        if (gridDim.z > 1) {
+          p.part[((int64_t)blockIdx.z * p.M + row) * p.r + col] = v;
+        } else {
+          p.out1[row * p.r + col] = to_bf16(v * p.alpha1);
+          if (p.out2) p.out2[row * p.r + col] = to_bf16(v * p.alpha2);
+        }
+      }
 }
 
 }  // namespace skinny
