@@ -789,7 +789,6 @@ struct SkSched {
   int tm, tj, ranges;
   int64_t klen;
   bool lds;
-  int ns;
 };
 constexpr int64_t SK_TARGET_WG = 512;   // workgroups wanted per pass
 constexpr int64_t SK_MAX_RANGES = 4;    // (8 measured 0.5% slower on the 8B layer set)
@@ -803,7 +802,8 @@ bool sk_lds_fits(int64_t R, int r, int transb) {
   return R % 8 == 0 && (!transb || r % 8 == 0) && R * 2 * 128 < lim && (int64_t)r * R * 2 < lim;
 }
 
-size_t sk_lds_bytes(int tm, int tj, int ns) {
+// LDS of the k_rows_lds instantiation for tj (the tm and ns go with it)
+size_t sk_lds_bytes(int tj) {
   switch (tj) {
     case 1: return skinny::LdsRing<1, 1, 0, 6>::bytes();
     case 2: return skinny::LdsRing<1, 2, 0, 6>::bytes();
@@ -818,11 +818,10 @@ SkSched sk_sched(int64_t M, int64_t R, int r, int64_t E, int transb) {
   f.lds = sk_lds_fits(R, r, transb);
   const int64_t jt = ceil_div(r, 16 * f.tj);
   if (f.lds) {
-    f.tm = f.tj >= 4 ? 2 : 1;
-    f.ns = f.tj >= 4 ? 4 : 6;
+    f.tm = f.tj >= 4 ? 2 : 1;   // (stages: 6 up to rank 32, 4 above, as rows_skinny instantiates them)
     const int64_t blocks = (ceil_div(std::max<int64_t>(M, 1), 64 * f.tm) + (E > 1 ? E : 0)) * jt;
     const int64_t steps = std::max<int64_t>(1, ceil_div(R, 64));
-    const int64_t round = cu_count() * std::max<int64_t>(1, LDS_PER_CU / (int64_t)sk_lds_bytes(f.tm, f.tj, f.ns));
+    const int64_t round = cu_count() * std::max<int64_t>(1, LDS_PER_CU / (int64_t)sk_lds_bytes(f.tj));
     int64_t want = std::max<int64_t>(1, round / blocks);
     want = std::max<int64_t>(1, std::min<int64_t>({want, steps / 4, SK_MAX_RANGES}));
     if (f.tj >= 8 || M * R * 2 < SK_SPLIT_MIN_BYTES) want = 1;
