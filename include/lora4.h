@@ -100,9 +100,13 @@ typedef enum {
  * ceil(N/64) row blocks, KB = ceil(K/64) k blocks, tile (rb, kb) is tile
  * number t = rb*KB + kb; row i of a tile is row 64*rb + i of W, element j of
  * it is element 64*kb + j. Rows past N and elements past K are zero padding.
- *  codes         : uint8, 2048 bytes per tile at 2048*t; row i at 32*i; byte
- *                  j of a row holds element 2j in its low nibble and element
- *                  2j+1 in its high nibble.
+ *  codes         : uint8, 2048 bytes per tile at 2048*t; row i at 32*i.
+ *                  MXFP4, NVFP4: byte j of a row holds element 2j in its low
+ *                  nibble and element 2j+1 in its high nibble. NF4, NF4_DQ:
+ *                  in each 4-byte word (elements 8w .. 8w+7 of the row),
+ *                  byte j holds element 8w+j in its low nibble and 8w+j+4 in
+ *                  its high nibble (the decoder reads each half's indices
+ *                  straight from the word).
  *  scales        : NF4    : float, 64 per tile at 64*t; entry i = the scale of
  *                           row i's 64 elements
  *                  NF4_DQ : uint8 E4M3 codes, 64 per tile at 64*t, as NF4

@@ -17,8 +17,14 @@
 // values; it agrees bit for bit with the exact product rounded to bf16 for
 // all 16 x 16 code pairs and all finite scales (checked on the device).
 //
-// Packing (all formats): byte j of a row holds element 2j in its low nibble
-// and element 2j+1 in its high nibble.
+// Packing: row-major (the oracle's bytes, lora4_import_rowmajor's input):
+// byte j of a row holds element 2j in its low nibble and element 2j+1 in its
+// high nibble. The tiled storage keeps that order for MXFP4 and NVFP4 (the
+// hardware FP4 convert takes element pairs from one byte); for NF4 and
+// NF4-DQ, byte j of each 32-bit word of codes (elements 8w .. 8w+7 of the
+// row) holds element 8w + j in its low nibble and 8w + j + 4 in its high
+// nibble, so the table lookups take both halves' indices straight from the
+// word (nf4_nibble).
 #pragma once
 
 #include "common.hpp"
@@ -58,8 +64,12 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t E) {
   return __builtin_bit_cast(float, bits);
 }
 
-// Dequantize 32 consecutive NF4 elements (16 code bytes) sharing one scale
-// into 16 words of bf16 pairs (element 2j in the low half of word j).
+// Bit offset of element i (0..7) within an NF4 code word of the tiled storage.
+__host__ __device__ constexpr int nf4_nibble(int i) { return i < 4 ? 8 * i : 8 * (i - 4) + 4; }
+
+// Dequantize 32 consecutive NF4 elements (16 code bytes, tiled storage)
+// sharing one scale into 16 words of bf16 pairs (element 2j in the low half
+// of word j).
 // qlds: the 16 fp32 levels in LDS (each lane reads its own level; the 16
 // entries sit in 16 different banks, so the reads never conflict).
 __device__ __forceinline__ void dequant32_nf4(u32x4_t codes, float scale, const float *qlds,
@@ -69,8 +79,8 @@ __device__ __forceinline__ void dequant32_nf4(u32x4_t codes, float scale, const 
     uint32_t w = codes[d];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      uint32_t lo = (w >> (8 * p)) & 15u;
-      uint32_t hi = (w >> (8 * p + 4)) & 15u;
+      uint32_t lo = (w >> nf4_nibble(2 * p)) & 15u;
+      uint32_t hi = (w >> nf4_nibble(2 * p + 1)) & 15u;
       float a = qlds[lo] * scale;
       float b = qlds[hi] * scale;
       out[4 * d + p] = pack_bf16x2(a, b);
@@ -120,8 +130,7 @@ __device__ __forceinline__ void dequant32_mxfp4(u32x4_t codes, float scale, uint
 // Storage of a packed base: each group's [N, K] is cut into tiles of 64 rows
 // by 64 elements (RB = ceil(N / 64) row blocks, KB = ceil(K / 64) k blocks;
 // tile (rb, kb) is number rb KB + kb). A tile's codes are 2048 contiguous
-// bytes, 32 per row (byte j: elements 2j, 2j+1 of the block in its low and
-// high nibble); its scales are 64 contiguous entries (one per row, NF4 and
+// bytes, 32 per row (nibble order above); its scales are 64 contiguous entries (one per row, NF4 and
 // NF4-DQ) or 128 (two per row, MXFP4). Rows past N and elements past K are
 // zero. One step of either GEMM reads one tile per wave, so every global load
 // of codes covers whole contiguous rows of a tile.

@@ -361,10 +361,17 @@ __device__ __forceinline__ RunTable make_table_pair(float c, const float qh[8], 
   return table_pair_from(t, sel);
 }
 
-// 4 indices (bytes 0..15) -> low and high bytes of T[idx].
-__device__ __forceinline__ void lookup4(const RunTable &T, uint32_t idx, uint32_t &L, uint32_t &H) {
-  const uint32_t i7 = idx & 0x07070707u;
-  const uint32_t s3 = ((idx >> 1) & 0x04040404u) | T.sel;   // byte j: j + 4 * bit3
+// Lookup indices of the four elements in the low (HI = 0) or high nibbles of
+// an NF4 code word (elements 0..3 or 4..7, nf4_nibble): i7 = the code's low
+// three bits per byte, s3 = byte j: j + 4 * bit 3 (selects the table half).
+template <int HI>
+__device__ __forceinline__ void nf4_idx(const RunTable &T, uint32_t c, uint32_t &i7, uint32_t &s3) {
+  i7 = (c >> (4 * HI)) & 0x07070707u;
+  s3 = ((c >> (4 * HI + 1)) & 0x04040404u) | T.sel;
+}
+
+// Low and high bytes of T[index] for the four indices (i7, s3).
+__device__ __forceinline__ void lookup4(const RunTable &T, uint32_t i7, uint32_t s3, uint32_t &L, uint32_t &H) {
   const uint32_t la = perm(T.lo[1], T.lo[0], i7);
   const uint32_t lb = perm(T.lo[3], T.lo[2], i7);
   const uint32_t ha = perm(T.hi[1], T.hi[0], i7);
@@ -373,17 +380,19 @@ __device__ __forceinline__ void lookup4(const RunTable &T, uint32_t idx, uint32_
   H = perm(hb, ha, s3);
 }
 
-// 8 codes (element i in bits 4i..4i+3) -> 4 words of bf16 pairs.
+// Elements 0..3 (low and high bytes L, H) -> 2 words of bf16 pairs.
+__device__ __forceinline__ uint32_t pair_lo(uint32_t L, uint32_t H) { return perm(H, L, 0x05010400u); }
+__device__ __forceinline__ uint32_t pair_hi(uint32_t L, uint32_t H) { return perm(H, L, 0x07030602u); }
+
+// 8 codes (one word of the tiled NF4 storage) -> 4 words of bf16 pairs:
+// 23 VALU instructions.
 __device__ __forceinline__ u32x4_t decode8_nf4(const RunTable &T, uint32_t c) {
-  const uint32_t ev = c & 0x0F0F0F0Fu;            // n0 n2 n4 n6
-  const uint32_t od = (c >> 4) & 0x0F0F0F0Fu;     // n1 n3 n5 n7
-  const uint32_t i0 = perm(od, ev, 0x05010400u);  // n0 n1 n2 n3
-  const uint32_t i1 = perm(od, ev, 0x07030602u);  // n4 n5 n6 n7
-  uint32_t L0, H0, L1, H1;
-  lookup4(T, i0, L0, H0);
-  lookup4(T, i1, L1, H1);
-  return u32x4_t{perm(H0, L0, 0x05010400u), perm(H0, L0, 0x07030602u), perm(H1, L1, 0x05010400u),
-                 perm(H1, L1, 0x07030602u)};
+  uint32_t i7, s3, L0, H0, L1, H1;
+  nf4_idx<0>(T, c, i7, s3);
+  lookup4(T, i7, s3, L0, H0);
+  nf4_idx<1>(T, c, i7, s3);
+  lookup4(T, i7, s3, L1, H1);
+  return u32x4_t{pair_lo(L0, H0), pair_hi(L0, H0), pair_lo(L1, H1), pair_hi(L1, H1)};
 }
 
 __device__ __forceinline__ u32x4_t decode8_mxfp4(uint32_t c, float s) {

@@ -261,7 +261,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
   // and meets the others; the next step's first fragments are then read
   // behind the last MFMAs of this one.
   struct WordDec {
-    uint32_t i0, i1, L0, H0, L1, H1;
+    uint32_t i0, i1, L0, H0, L1, H1;   // i0, i1: lookup indices of elements 0..3 (big::nf4_idx)
     float sc;   // NVFP4: the word's E4M3 block scale
   };
   struct TabBuild {
@@ -352,21 +352,22 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_dgrad(Params p) {
         lds_write_b128(Bs + wt_off(lane, wave * 64 + 8 * q), u32x4_t{o.L0, o.H0, o.L1, o.H1});
       }
     } else {
+      // indices of elements 0..3; their lookup; indices and lookup of
+      // elements 4..7 (from the code word); interleave + LDS write
       if (st == 0) {
-        const uint32_t ev = code & 0x0F0F0F0Fu;          // n0 n2 n4 n6
-        const uint32_t od = (code >> 4) & 0x0F0F0F0Fu;   // n1 n3 n5 n7
-        o.i0 = big::perm(od, ev, 0x05010400u);           // n0 n1 n2 n3
-        o.i1 = big::perm(od, ev, 0x07030602u);           // n4 n5 n6 n7
+        big::nf4_idx<0>(T, code, o.i0, o.i1);
         pin(o.i0);
         pin(o.i1);
       } else if (st == 1) {
-        big::lookup4(T, o.i0, o.L0, o.H0);
+        big::lookup4(T, o.i0, o.i1, o.L0, o.H0);
       } else if (st == 2) {
-        big::lookup4(T, o.i1, o.L1, o.H1);
+        uint32_t i7, s3;
+        big::nf4_idx<1>(T, code, i7, s3);
+        big::lookup4(T, i7, s3, o.L1, o.H1);
       } else {
         lds_write_b128(Bs + wt_off(lane, wave * 64 + 8 * q),
-                       u32x4_t{big::perm(o.H0, o.L0, 0x05010400u), big::perm(o.H0, o.L0, 0x07030602u),
-                               big::perm(o.H1, o.L1, 0x05010400u), big::perm(o.H1, o.L1, 0x07030602u)});
+                       u32x4_t{big::pair_lo(o.L0, o.H0), big::pair_hi(o.L0, o.H0), big::pair_lo(o.L1, o.H1),
+                               big::pair_hi(o.L1, o.H1)});
       }
     }
   };

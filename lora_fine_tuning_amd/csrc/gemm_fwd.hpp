@@ -271,7 +271,7 @@ __device__ __forceinline__ void fwd_tile(const Params &p, uint16_t *smem, const 
   // of a table build, or one global load), fenced so that nothing moves
   // between pairs.
   struct WordDec {
-    uint32_t i0, i1, L0, H0, L1, H1;
+    uint32_t i0, i1, L0, H0, L1, H1;   // i0, i1: lookup indices of elements 0..3 (big::nf4_idx)
   };
   struct RunBuild {
     float c;
@@ -332,26 +332,27 @@ __device__ __forceinline__ void fwd_tile(const Params &p, uint16_t *smem, const 
       }
       f.w[j][q][i & 3] = v;
     } else {
-      auto unpack = [](uint32_t c, WordDec &o) {
-        const uint32_t ev = c & 0x0F0F0F0Fu;          // n0 n2 n4 n6
-        const uint32_t od = (c >> 4) & 0x0F0F0F0Fu;   // n1 n3 n5 n7
-        o.i0 = big::perm(od, ev, 0x05010400u);        // n0 n1 n2 n3
-        o.i1 = big::perm(od, ev, 0x07030602u);        // n4 n5 n6 n7
+      // stages of a word: indices of elements 0..3; their lookup; indices
+      // and lookup of elements 4..7 (from the code word); the interleave
+      auto hi_half = [&](uint32_t c, WordDec &o) {
+        uint32_t i7, s3;
+        big::nf4_idx<1>(d.T, c, i7, s3);
+        big::lookup4(d.T, i7, s3, o.L1, o.H1);
       };
       auto fin = [](const WordDec &o) -> u32x4_t {
-        return u32x4_t{big::perm(o.H0, o.L0, 0x05010400u), big::perm(o.H0, o.L0, 0x07030602u),
-                       big::perm(o.H1, o.L1, 0x05010400u), big::perm(o.H1, o.L1, 0x07030602u)};
+        return u32x4_t{big::pair_lo(o.L0, o.H0), big::pair_hi(o.L0, o.H0), big::pair_lo(o.L1, o.H1),
+                       big::pair_hi(o.L1, o.H1)};
       };
       switch (i) {
-        case 0: unpack(w.c[j][q0], wd[0]); break;
-        case 1: big::lookup4(d.T, wd[0].i0, wd[0].L0, wd[0].H0); break;
-        case 2: big::lookup4(d.T, wd[0].i1, wd[0].L1, wd[0].H1); break;
+        case 0: big::nf4_idx<0>(d.T, w.c[j][q0], wd[0].i0, wd[0].i1); break;
+        case 1: big::lookup4(d.T, wd[0].i0, wd[0].i1, wd[0].L0, wd[0].H0); break;
+        case 2: hi_half(w.c[j][q0], wd[0]); break;
         case 3:
           f.w[j][q0] = fin(wd[0]);
-          unpack(w.c[j][q0 + 1], wd[1]);
+          big::nf4_idx<0>(d.T, w.c[j][q0 + 1], wd[1].i0, wd[1].i1);
           break;
-        case 4: big::lookup4(d.T, wd[1].i0, wd[1].L0, wd[1].H0); break;
-        case 5: big::lookup4(d.T, wd[1].i1, wd[1].L1, wd[1].H1); break;
+        case 4: big::lookup4(d.T, wd[1].i0, wd[1].i1, wd[1].L0, wd[1].H0); break;
+        case 5: hi_half(w.c[j][q0 + 1], wd[1]); break;
         case 6: f.w[j][q0 + 1] = fin(wd[1]); break;
         default: break;
       }

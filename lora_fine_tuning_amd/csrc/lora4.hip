@@ -1545,8 +1545,9 @@ lora4_status lora4_import_rowmajor(int32_t format, int64_t N, int64_t K, int64_t
     return LORA4_ERR_ALIGN;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int64_t nc = groups * w_blocks(N) * w_blocks(K) * 128;   // 16-byte pieces of codes
+  const int nf4 = format == LORA4_NF4 || format == LORA4_NF4_DQ ? 1 : 0;   // (nibble order of the storage)
   TRY(launch_args("import_codes", k_retile_codes, dim3((unsigned)ceil_div(nc, 256)), dim3(256), st, codes_rm, N,
-                  K, groups, codes));
+                  K, groups, nf4, codes));
   const int epr = format == LORA4_MXFP4 ? 2 : format == LORA4_NVFP4 ? 4 : 1;
   const int64_t ns = groups * w_blocks(N) * w_blocks(K) * 64 * epr;
   const dim3 grid((unsigned)ceil_div(ns, 256));

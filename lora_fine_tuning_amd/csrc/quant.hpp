@@ -86,7 +86,8 @@ __device__ __forceinline__ float absmax8(const u32x4_t v) {
   return m;
 }
 
-// NF4 codes of 8 elements with block scale c (byte h: elements 2h, 2h + 1).
+// NF4 codes of 8 elements with block scale c, as one word of the tiled
+// storage (element i at bit nf4_nibble(i)).
 __device__ __forceinline__ uint32_t nf4_encode8(const u32x4_t v, float c, const Nf4Table &tab) {
   uint32_t word = 0;
 #pragma unroll
@@ -95,7 +96,7 @@ __device__ __forceinline__ uint32_t nf4_encode8(const u32x4_t v, float c, const 
     const float b = bf16_bits_to_f32(v[h] >> 16);
     const float xa = (c == 0.0f) ? 0.0f : a / c;
     const float xb = (c == 0.0f) ? 0.0f : b / c;
-    word |= (nf4_encode(xa, tab) | (nf4_encode(xb, tab) << 4)) << (8 * h);
+    word |= (nf4_encode(xa, tab) << nf4_nibble(2 * h)) | (nf4_encode(xb, tab) << nf4_nibble(2 * h + 1));
   }
   return word;
 }
@@ -241,9 +242,18 @@ __global__ __launch_bounds__(PACK_THREADS) void k_quant_nvfp4(const uint16_t *W,
 // piece of a row's codes is either whole inside the row or past its end.
 // ---------------------------------------------------------------------------
 
+// A row-major NF4 code word (element i at bits 4i) in the tiled storage's
+// nibble order (element i at nf4_nibble(i)).
+__device__ __forceinline__ uint32_t nf4_word_to_tiled(uint32_t w) {
+  uint32_t t = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) t |= ((w >> (4 * i)) & 15u) << nf4_nibble(i);
+  return t;
+}
+
 // One thread per 16-byte piece c of the output: tile c / 128, row (c / 2) % 64,
-// half c % 2.
-__global__ void k_retile_codes(const uint8_t *src, int64_t N, int64_t K, int64_t groups, uint8_t *dst) {
+// half c % 2. nf4: reorder the nibbles of each word (NF4, NF4-DQ).
+__global__ void k_retile_codes(const uint8_t *src, int64_t N, int64_t K, int64_t groups, int nf4, uint8_t *dst) {
   const int64_t KB = w_blocks(K);
   const int64_t per_group = w_blocks(N) * KB * 128;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -257,6 +267,7 @@ __global__ void k_retile_codes(const uint8_t *src, int64_t N, int64_t K, int64_t
   const int64_t row_bytes = K >> 1;
   u32x4_t v = {0u, 0u, 0u, 0u};
   if (n < N && byte0 < row_bytes) v = *reinterpret_cast<const u32x4_t *>(src + (g * N + n) * row_bytes + byte0);
+  if (nf4) v = u32x4_t{nf4_word_to_tiled(v[0]), nf4_word_to_tiled(v[1]), nf4_word_to_tiled(v[2]), nf4_word_to_tiled(v[3])};
   *reinterpret_cast<u32x4_t *>(dst + idx * 16) = v;
 }
 

@@ -44,13 +44,39 @@ def _blocks(x):
     return -(-x // 64)
 
 
-def tile_codes(codes, N, K):
-    """Row-major codes [N, K/2] -> the library's storage: 64 x 64-element tiles
-    (2048 bytes, 32 per row), tile (rb, kb) at rb * KB + kb, zero padding."""
+# NF4 code words in the library's storage: element i of each 8-element word
+# (row-major: nibble i) sits at nibble NF4_NIBBLE[i] (include/lora4.h: byte j
+# holds elements j and j + 4).
+NF4_NIBBLE = [0, 2, 4, 6, 1, 3, 5, 7]
+
+
+def _nf4_words(codes, inverse=False):
+    """Row-major NF4 code bytes (rows of whole 4-byte words) <-> the storage's
+    nibble order, word by word."""
+    w = np.ascontiguousarray(codes).view(np.uint32)
+    out = np.zeros_like(w)
+    for i, pos in enumerate(NF4_NIBBLE):
+        src, dst = (pos, i) if inverse else (i, pos)
+        out |= ((w >> np.uint32(4 * src)) & np.uint32(15)) << np.uint32(4 * dst)
+    return out.view(np.uint8).reshape(codes.shape)
+
+
+def tile_codes(codes, N, K, fmt):
+    """Row-major codes [N, K/2] of format fmt -> the library's storage: 64 x
+    64-element tiles (2048 bytes, 32 per row), tile (rb, kb) at rb * KB + kb,
+    zero padding; NF4 and NF4-DQ words in the storage's nibble order."""
     RB, KB = _blocks(N), _blocks(K)
     buf = np.zeros((RB * 64, KB * 32), dtype=np.uint8)
     buf[:N, :codes.shape[1]] = codes
+    if fmt in (synth.NF4, synth.NF4_DQ):
+        buf = _nf4_words(buf)
     return np.ascontiguousarray(buf.reshape(RB, 64, KB, 32).transpose(0, 2, 1, 3)).reshape(-1)
+
+
+def untile_codes(flat, N, K, rows, fmt):
+    """Rows of the stored codes back as row-major bytes (K/2 per row)."""
+    c = np.ascontiguousarray(untile_rows(flat, N, K, rows, 32))
+    return _nf4_words(c, inverse=True) if fmt in (synth.NF4, synth.NF4_DQ) else c
 
 
 def tile_scales(sc, N, K):

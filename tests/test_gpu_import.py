@@ -49,7 +49,7 @@ def test_import_matches_packer_and_permutation(fmt, N, K, E):
     assert np.array_equal(got_c, ref.codes.cpu().numpy())
     assert np.array_equal(got_s.view(np.uint8), ref.scales.cpu().numpy().view(np.uint8))
     for e in range(E):
-        assert np.array_equal(got_c[e], tile_codes(codes_rm[e], N, K))
+        assert np.array_equal(got_c[e], tile_codes(codes_rm[e], N, K, fmt))
         assert np.array_equal(got_s[e].view(np.uint8), tile_scales(scales_rm[e], N, K).view(np.uint8))
 
 

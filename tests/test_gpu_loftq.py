@@ -15,6 +15,7 @@ import torch
 import lora_fine_tuning_amd as L
 from oracle import loftq, nf4
 from oracle.codecs import bf16_to_f32
+import synth
 from gpu_util import DEV, f64, print_case, tile_codes, tile_scales, to_dev, to_host
 from synth import to_bf16
 
@@ -36,7 +37,7 @@ def test_one_iteration_is_nf4_plus_best_rank_r(N, K, r):
     base, A, B = L.loftq_init(to_dev(Wb), r, iters=1, s=1.0)
     torch.cuda.synchronize()
     codes, sc = nf4.quantize(Wb)
-    assert np.array_equal(base.codes[0].cpu().numpy(), tile_codes(codes, N, K))
+    assert np.array_equal(base.codes[0].cpu().numpy(), tile_codes(codes, N, K, synth.NF4))
     assert np.array_equal(base.scales[0].cpu().numpy().view(np.uint32), tile_scales(sc, N, K).view(np.uint32))
     W = f64(Wb)
     R = W - bf16_to_f32(nf4.dequantize(codes, sc)).astype(np.float64)
@@ -64,9 +65,9 @@ def test_five_iterations_match_the_oracle_error(dq):
              None if base.scales2 is None else base.scales2[0].cpu().numpy())
     # the GPU's Q through the library's one-hot-checked dequant: compare via the
     # oracle dequant of the untiled packing
-    from gpu_util import untile_rows
+    from gpu_util import untile_codes, untile_rows
     rows = np.arange(N)
-    codes = untile_rows(parts[0], N, K, rows, 32)
+    codes = untile_codes(parts[0], N, K, rows, synth.NF4_DQ if dq else synth.NF4)
     if dq:
         c8 = untile_rows(parts[1], N, K, rows, 1)
         Q = bf16_to_f32(nf4.dequantize_dq(codes, c8, parts[2])).astype(np.float64)
@@ -87,7 +88,6 @@ def test_llama8b_base_shapes():
     (1024 x 4096) through the five-iteration loop against the oracle's error,
     and the q projection (4096 x 4096) through one iteration against the
     Eckart-Young optimum of its NF4 residual."""
-    import synth
     lay_k = synth.layers(2)[1]
     Wk = synth.inputs(lay_k, names=("W",))["W"]
     print_case("loftq 8b k", Wk.shape)
@@ -95,8 +95,8 @@ def test_llama8b_base_shapes():
     torch.cuda.synchronize()
     N, K = Wk.shape
     rows = np.arange(N)
-    from gpu_util import untile_rows
-    codes = untile_rows(base.codes[0].cpu().numpy(), N, K, rows, 32)
+    from gpu_util import untile_codes, untile_rows
+    codes = untile_codes(base.codes[0].cpu().numpy(), N, K, rows, synth.NF4)
     scv = untile_rows(base.scales[0].cpu().numpy().view(np.float32), N, K, rows, 1)
     Q = bf16_to_f32(nf4.dequantize(codes, scv)).astype(np.float64)
     W = f64(Wk)
@@ -112,7 +112,7 @@ def test_llama8b_base_shapes():
     torch.cuda.synchronize()
     c, sc = nf4.quantize(Wq)
     N, K = Wq.shape
-    assert np.array_equal(base.codes[0].cpu().numpy(), tile_codes(c, N, K))
+    assert np.array_equal(base.codes[0].cpu().numpy(), tile_codes(c, N, K, synth.NF4))
     R = f64(Wq) - bf16_to_f32(nf4.dequantize(c, sc)).astype(np.float64)
     S = np.linalg.svd(R, compute_uv=False)
     e_opt = np.sqrt(np.sum(S[lay_q.r:] ** 2))

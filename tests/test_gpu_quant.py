@@ -49,7 +49,7 @@ def test_quant_pack_bit_exact(fmt, N, K):
     ref = oracle_pack(W, fmt)
     # the library stores the oracle's row-major codes and scales in 64 x 64
     # tiles (include/lora4.h); padding is zero
-    assert np.array_equal(pk.codes[0].cpu().numpy(), tile_codes(ref[0], N, K))
+    assert np.array_equal(pk.codes[0].cpu().numpy(), tile_codes(ref[0], N, K, fmt))
     if fmt == synth.NF4:
         assert np.array_equal(pk.scales[0].cpu().numpy().view(np.uint32), tile_scales(ref[1], N, K).view(np.uint32))
     elif fmt == synth.NF4_DQ:
@@ -99,7 +99,7 @@ def _custom_base(fmt, N, K, seed):
 
 def _to_packed(parts, fmt, N, K):
     """Row-major codes and scales, stored in the library's tiles on the GPU."""
-    codes = torch.from_numpy(tile_codes(parts[0], N, K)).to(DEV)[None]
+    codes = torch.from_numpy(tile_codes(parts[0], N, K, fmt)).to(DEV)[None]
     sc = torch.from_numpy(tile_scales(parts[1], N, K)).to(DEV)[None]
     if fmt == synth.NF4:
         return L.PackedBase(L.LORA4_NF4, N, K, 1, codes, sc)

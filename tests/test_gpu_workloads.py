@@ -90,7 +90,7 @@ def run_layer_gpu(lay, t):
 def check_packing(lay, got, packs):
     """The whole packed base against the oracle's packing, bit for bit."""
     for q, pk in enumerate(packs):
-        assert np.array_equal(got["codes"][q], tile_codes(pk[0], lay.N, lay.K)), f"codes of group {q}"
+        assert np.array_equal(got["codes"][q], tile_codes(pk[0], lay.N, lay.K, lay.fmt)), f"codes of group {q}"
         assert np.array_equal(got["scales"][q].view(np.uint8), tile_scales(pk[1], lay.N, lay.K).view(np.uint8)), \
             f"scales of group {q}"
         if lay.fmt == synth.NF4_DQ:
