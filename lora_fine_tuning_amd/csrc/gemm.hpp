@@ -91,6 +91,14 @@ struct TnParams {
   int groups;
   int splits;         // row splits per group (gridDim.z == splits)
   float *part;        // [splits][groups][P][Q]
+  // In-launch reduction (cnt != nullptr): one arrival counter per output
+  // tile, zero on entry and left zero. The block that arrives last at a tile
+  // sums the tile's partials in split order and writes
+  // out[g][p][q] = bf16(alpha sum) (transpose_out: out[g][q][p]).
+  unsigned *cnt;
+  uint16_t *out;
+  float alpha;
+  int transpose_out;
 };
 
 // --------------------------------------------------------------------------
@@ -550,8 +558,72 @@ __global__ __launch_bounds__(THREADS) void k_gemm_nn(NnParams p) {
 // TN kernel: partial[split][g][P][Q] = sum over the split's rows of U^T V
 // --------------------------------------------------------------------------
 
+// In-launch reduction of a TN tile's split partials (TnParams::cnt): every
+// block's partials are written through to memory (system-scope stores, so no
+// cache of any XCD holds them dirty) and acknowledged before the block
+// counts itself in; the block that arrives last reads them back past the
+// caches, sums them in split order from +0 (so the result does not depend on
+// which block is last) and writes the bf16 tile, then resets the counter for
+// the next launch. No block waits for another.
+template <int BP, int BQ>
+__device__ __forceinline__ void tn_reduce_last(const TnParams &p, int64_t p0, int64_t q0, int g, int64_t cnt_idx) {
+  __shared__ int last;
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's partial stores are acknowledged
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned arrived =
+        __hip_atomic_fetch_add(&p.cnt[cnt_idx], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    last = arrived + 1 == (unsigned)p.splits;
+    if (last) __hip_atomic_store(&p.cnt[cnt_idx], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+  __syncthreads();
+  if (!last) return;
+  const int64_t PQ = p.P * p.Q;
+  const int64_t gstride = (int64_t)p.groups * PQ;   // one split's partials
+  // the job's partials through a buffer descriptor, read with sc0 sc1 (past
+  // every cache) 16 bytes per lane, the loads of up to 16 splits in flight
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      p.part, (short)0, (int)std::min<int64_t>((int64_t)p.splits * gstride * 4, 0x7FFFFFFF), 0x00020000);
+  constexpr int SYS = 17;   // cache policy: sc0 | sc1
+  const bool vec = (p.Q % 4) == 0 && (int64_t)p.splits * gstride * 4 <= 0x7FFFFFFF;
+  // 4 consecutive q per thread and pass
+  for (int idx = threadIdx.x * 4; idx < BP * BQ; idx += THREADS * 4) {
+    const int64_t pp = p0 + idx / BQ, q = q0 + idx % BQ;
+    if (pp >= p.P || q >= p.Q) continue;
+    float sum[4] = {0.f, 0.f, 0.f, 0.f};
+    const int64_t e0 = (int64_t)g * PQ + pp * p.Q + q;   // element offset in split 0
+    if (vec) {
+      for (int k0 = 0; k0 < p.splits; k0 += 16) {
+        f32x4_t v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          if (k0 + u < p.splits)
+            v[u] = __builtin_bit_cast(
+                f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)((e0 + (k0 + u) * gstride) * 4), 0, SYS));
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          if (k0 + u < p.splits)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sum[e] += v[u][e];
+      }
+    } else {
+      for (int k = 0; k < p.splits; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (q + e < p.Q)
+            sum[e] += __hip_atomic_load(p.part + e0 + k * gstride + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (q + e >= p.Q) break;
+      const int64_t o = p.transpose_out ? (q + e) * p.P + pp : pp * p.Q + q + e;
+      p.out[(int64_t)g * PQ + o] = to_bf16(sum[e] * p.alpha);
+    }
+  }
+}
+
 template <int BP, int BQ, int WAVES_P>
-__device__ __forceinline__ void tn_tile(const TnParams &p, int bx, int by, int bz) {
+__device__ __forceinline__ void tn_tile(const TnParams &p, int bx, int by, int bz, int64_t cnt_idx) {
   constexpr int WAVES_Q = 4 / WAVES_P;
   constexpr int WTP = BP / WAVES_P, WTQ = BQ / WAVES_Q;
   constexpr int FM = WTP / 16, FN = WTQ / 16;
@@ -626,10 +698,16 @@ __device__ __forceinline__ void tn_tile(const TnParams &p, int bx, int by, int b
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int64_t pp = p0 + wp0 + i * 16 + (lane >> 4) * 4 + e;
-        if (pp < p.P && q < p.Q) out[pp * p.Q + q] = acc[i][j][e];
+        if (pp < p.P && q < p.Q) {
+          if (p.cnt)   // written through to memory: read by another block below
+            __hip_atomic_store(&out[pp * p.Q + q], acc[i][j][e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          else
+            out[pp * p.Q + q] = acc[i][j][e];
+        }
       }
     }
   }
+  if (p.cnt) tn_reduce_last<BP, BQ>(p, p0, q0, g, cnt_idx);
 }
 
 // Two independent TN products with the same P tiling in one launch (the
@@ -644,7 +722,10 @@ __global__ __launch_bounds__(THREADS) void k_gemm_tn2(TnParams a, TnParams b, in
   if (second) id -= na;
   const TnParams p = second ? b : a;
   const int64_t qt = second ? qb : qa;
-  tn_tile<BP, BQ, WAVES_P>(p, (int)(id % ptiles), (int)((id / ptiles) % qt), (int)(id / (ptiles * qt)));
+  const int bx = (int)(id % ptiles), by = (int)((id / ptiles) % qt), bz = (int)(id / (ptiles * qt));
+  // arrival counter of the output tile (group bz / splits, Q tile by, P tile bx)
+  const int64_t cnt_idx = ((int64_t)(bz / p.splits) * qt + by) * ptiles + bx;
+  tn_tile<BP, BQ, WAVES_P>(p, bx, by, bz, cnt_idx);
 }
 
 // --------------------------------------------------------------------------
@@ -694,28 +775,6 @@ __global__ void k_reduce_bf16(const float *part, int splits, int64_t stride, int
     const u32x2_t w = {pack_bf16x2(s[0] * alpha2, s[1] * alpha2), pack_bf16x2(s[2] * alpha2, s[3] * alpha2)};
     *reinterpret_cast<u32x2_t *>(out2 + i) = w;
   }
-}
-
-// dA[i] = bf16(sum_s partA[s][i]) for i < na, then
-// dB[g][n][j] = bf16(alpha sum_s partB[s][g][j][n]) (partials hold dB^T).
-__global__ void k_reduce_dadb(const float *part_a, int splits_a, int64_t na, uint16_t *dA, const float *part_b,
-                              int splits_b, int groups, int64_t P, int64_t Q, uint16_t *dB, float alpha) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < na) {
-    float s = 0.f;
-    for (int k = 0; k < splits_a; ++k) s += part_a[k * na + i];
-    dA[i] = to_bf16(s);
-    return;
-  }
-  const int64_t ib = i - na;
-  const int64_t total = (int64_t)groups * P * Q;
-  if (ib >= total) return;
-  const int64_t g = ib / (P * Q);
-  const int64_t rem = ib - g * P * Q;
-  const int64_t q = rem / P, pp = rem - q * P;
-  float s = 0.f;
-  for (int k = 0; k < splits_b; ++k) s += part_b[((int64_t)k * groups + g) * P * Q + pp * Q + q];
-  dB[ib] = to_bf16(s * alpha);
 }
 
 __global__ void k_fill_u16(uint16_t *p, int64_t n, uint16_t v) {

@@ -316,7 +316,8 @@ struct Plan {
   FwdSched fs;                // forward base GEMM schedule
   int lds_splits;             // reduction splits of the 128 x 128 base GEMM (forward or dgrad), 1: none
   // workspace offsets
-  size_t off_sz, off_zw, off_dz, off_part, off_part_b, off_party, off_skpart, off_partx, bytes;
+  size_t off_sz, off_zw, off_dz, off_part, off_part_b, off_cnt, off_party, off_skpart, off_partx, bytes;
+  int64_t ncnt;       // backward: arrival counters of the dA / dB tiles (TnParams::cnt)
 };
 
 constexpr int BM_MAIN = 128, BN_MAIN = 128;
@@ -397,10 +398,14 @@ Plan make_plan(int which, const Base &b, int64_t M, int r, size_t cap = SIZE_MAX
   p.off_party = off;  // forward: fp32 partials of the split base GEMM
   if (which == 0 && p.fs.use && p.fs.split_tiles > 0)
     off += align256((size_t)p.fs.split_tiles * p.fs.ksplit * fwd::BM * fwd::BN * 4);
-  p.off_part = off;  // backward: dA partials, then dB^T partials
+  p.off_part = off;  // backward: dA partials, then dB^T partials, then their tiles' counters
+  p.ncnt = 0;
   if (which == 1) {
     p.off_part_b = off + align256((size_t)p.msplit_a * p.E * r * p.K * 4);
     off = p.off_part_b + align256((size_t)p.msplit_b * p.E * r * p.N * 4);
+    p.off_cnt = off;
+    p.ncnt = rtiles * (p.tq_a + p.tq_b) * p.E;
+    off += align256((size_t)p.ncnt * 4);
   }
   p.off_partx = off;  // fp32 partials of the split 128 x 128 base GEMM
   if (p.lds_splits > 1) off += align256((size_t)p.lds_splits * M * (which == 0 ? p.N : p.K) * 4);
@@ -858,7 +863,8 @@ lora4_status run_rows_lds(int transb, const skinny::Params &p, dim3 grid, hipStr
 
 lora4_status rows_skinny(int transb, const uint16_t *act, int64_t ld_act, const uint16_t *w, int64_t ld_w,
                          int64_t g_w, int64_t R, int64_t M, int r, const int64_t *offs, int64_t E, uint16_t *o1,
-                         float a1, uint16_t *o2, float a2, float *part, bool defer_reduce, hipStream_t st) {
+                         float a1, uint16_t *o2, float a2, float *part, bool defer_reduce, hipStream_t st,
+                         unsigned *zero = nullptr, int64_t zero_n = 0) {
   const SkSched f = sk_sched(M, R, r, E, transb);
   skinny::Params p{};
   p.act = act;
@@ -877,6 +883,8 @@ lora4_status rows_skinny(int transb, const uint16_t *act, int64_t ld_act, const 
   p.alpha2 = a2;
   p.klen = f.klen;
   p.part = part;
+  p.zero = zero;
+  p.zero_n = zero_n;
   const int64_t slots = ceil_div(std::max<int64_t>(M, 1), (f.lds ? 64 : 16) * f.tm) + (E > 1 ? E : 0);
   dim3 grid((unsigned)slots, (unsigned)ceil_div(r, 16 * f.tj), (unsigned)f.ranges);
   lora4_status st1 = LORA4_ERR_UNIMPLEMENTED;
@@ -1367,8 +1375,10 @@ static lora4_status backward_impl(const Base &bs, const uint16_t *X, const uint1
   const bool dz_tail = dzs.ranges > 1 && dzs.ranges <= big::A2_MAX_PARTS &&
                        dgrad_taken(pl.N, pl.N, M, packed_of(bs), pl.K, pl.E);
   const TailParts dztp{skpart, dzs.ranges, s, dZ, s, nullptr, 0.0f};
+  // (its first block also zeroes the dA / dB tiles' arrival counters)
+  unsigned *cnt = ws_at<unsigned>(workspace, pl.off_cnt);
   TRY(rows_skinny(1, dY, pl.N, B, r, pl.N * r, pl.N, M, r, group_offsets, pl.E, dZ, s, nullptr, 0.0f, skpart,
-                  dz_tail, st));
+                  dz_tail, st, cnt, pl.ncnt));
 
   // dX = dY deq(W) + dZ A
   {
@@ -1391,8 +1401,8 @@ static lora4_status backward_impl(const Base &bs, const uint16_t *X, const uint1
                         st));
   }
 
-  // dA = dZ^T X and dB^T = Z^T dY, split over rows, in one launch; one launch
-  // reduces both
+  // dA = dZ^T X and dB^T = Z^T dY, split over rows, in one launch; the last
+  // block to finish each output tile reduces its splits (TnParams::cnt)
   float *part_b = ws_at<float>(workspace, pl.off_part_b);
   {
     TnParams pa{};
@@ -1405,20 +1415,22 @@ static lora4_status backward_impl(const Base &bs, const uint16_t *X, const uint1
     pa.groups = (int)pl.E;
     pa.splits = pl.msplit_a;
     pa.part = part;
+    pa.cnt = cnt;
+    pa.out = dA;
+    pa.alpha = 1.0f;
+    pa.transpose_out = 0;
     TnParams pb = pa;
     pb.U = mat(Zu, r);
     pb.V = mat(dY, pl.N);
     pb.Q = pl.N;
     pb.splits = pl.msplit_b;
     pb.part = part_b;
+    pb.cnt = cnt + ceil_div(r, pl.rt) * pl.tq_a * pl.E;
+    pb.out = dB;
+    pb.alpha = s;
+    pb.transpose_out = 1;
     TRY(run_tn2("gemm_tn_dA_dB", pl.rt, pa, pb, pl.tq_a, (int)(pl.msplit_a * pl.E), pl.tq_b,
                 (int)(pl.msplit_b * pl.E), st));
-  }
-  {
-    const int64_t na = pl.E * r * pl.K, nb = pl.E * r * pl.N;
-    TRY(launch_args("reduce_dA_dB", k_reduce_dadb, dim3((unsigned)ceil_div(na + nb, 256)), dim3(256), st,
-                    (const float *)part, pl.msplit_a, na, dA, (const float *)part_b, pl.msplit_b, (int)pl.E,
-                    (int64_t)r, pl.N, dB, s));
   }
   return LORA4_OK;
 }

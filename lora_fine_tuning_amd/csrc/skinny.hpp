@@ -41,9 +41,20 @@ struct Params {
   float alpha2;
   int64_t klen;          // reduction elements per range (multiple of 32)
   float *part;           // [ranges][M][r] fp32 when gridDim.z > 1
+  // side job of block (0, 0, 0): zero_n words at `zero` set to 0 (the
+  // arrival counters of a later launch of the same backward), or none
+  unsigned *zero;
+  int64_t zero_n;
 };
 
 constexpr int THREADS = 256;
+
+// The side job (Params::zero), written through to memory.
+__device__ __forceinline__ void zero_side_job(const Params &p) {
+  if (p.zero && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+    for (int64_t i = threadIdx.x; i < p.zero_n; i += THREADS)
+      __hip_atomic_store(&p.zero[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
 
 // 16 bytes of row `row` of a bf16 matrix at column k (zero past `kend`,
 // element-wise when the 16-byte load would be misaligned or cross kend).
@@ -76,6 +87,7 @@ __global__ __launch_bounds__(THREADS) void k_rows_skinny(Params p) {
   constexpr int RS = SLOTS < 32 ? SLOTS : 32;
   __shared__ __attribute__((aligned(16))) float red[4][RS][64];
 
+  zero_side_job(p);
   const RowTile rt = map_row_tile(blockIdx.x, BM, p.offsets, p.groups, p.M);
   if (rt.group < 0) return;
   const int g = rt.group;
@@ -251,6 +263,7 @@ __global__ __launch_bounds__(THREADS) void k_rows_lds(Params p) {
   constexpr int PPR = BN / 8;   // 16-byte pieces per row of the B stage
   extern __shared__ __attribute__((aligned(16))) uint16_t ring[];
 
+  zero_side_job(p);
   const RowTile rt = map_row_tile(blockIdx.x, BM, p.offsets, p.groups, p.M);
   if (rt.group < 0) return;
   const int g = rt.group;
