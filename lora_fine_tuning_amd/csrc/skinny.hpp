@@ -270,6 +270,9 @@ __global__ __launch_bounds__(THREADS) void k_rows_lds(Params p) {
   const int64_t row0 = rt.row0, row_end = rt.row_end;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
+  // this workgroup's rank columns: j0 .. j0 + BN - 1 (grid.y covers ranks
+  // above BN)
+  const int j0 = blockIdx.y * BN;
 
   // this workgroup's range of 64-deep steps, and where its loads stop
   const int64_t nsteps_all = (p.R + 63) / 64;
@@ -300,7 +303,7 @@ __global__ __launch_bounds__(THREADS) void k_rows_lds(Params p) {
     w_k[i] = 0;
     if (b < WB) {
       if constexpr (TRANSB == 0) {
-        const int j = 8 * b + (lane >> 3);                       // A row (rank index)
+        const int j = j0 + 8 * b + (lane >> 3);                  // A row (rank index)
         const int kq = tile64_dma_chunk(lane, b) * 8;
         w_k[i] = kq;
         if (j < p.r) w_voff[i] = (uint32_t)((j * p.ld_w + kq) * 2);
@@ -308,7 +311,7 @@ __global__ __launch_bounds__(THREADS) void k_rows_lds(Params p) {
         const int P = b * 64 + lane;                             // flat piece of the [64][BN] stage
         const int n = P / PPR, q = (P % PPR) ^ bsw<BN>(n);
         w_k[i] = n;
-        if (q * 8 < p.r) w_voff[i] = (uint32_t)((n * p.ld_w + q * 8) * 2);
+        if (j0 + q * 8 < p.r) w_voff[i] = (uint32_t)((n * p.ld_w + j0 + q * 8) * 2);
       }
     }
   }
@@ -393,7 +396,7 @@ __global__ __launch_bounds__(THREADS) void k_rows_lds(Params p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int64_t row = row0 + 16 * (TM * wave + i) + 4 * lg + e;
-        const int col = 16 * j + lr;
+        const int col = j0 + 16 * j + lr;
         if (row >= row_end || col >= p.r) continue;
         const float v = acc[i][j][e];
         if (gridDim.z > 1) {

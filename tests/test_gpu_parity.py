@@ -330,3 +330,18 @@ def test_tails_add_rank_r_partials(r, grouped, monkeypatch):
     o = None if offs is None else torch.tensor(offs, dtype=torch.int64, device=DEV)
     fw = L.forward(base, to_dev(t["X"]), to_dev(t["A"]), to_dev(t["B"]), lay.s, group_offsets=o, want_z=False)
     assert np.array_equal(to_host(fw["Y"]), got["Y"])
+
+
+@pytest.mark.parametrize("fmt", [synth.NF4, synth.MXFP4])
+@pytest.mark.parametrize("M,K,N,r", [(300, 512, 384, 256), (130, 256, 200, 200), (77, 192, 136, 136),
+                                     (64, 128, 96, 130)])
+def test_ranks_above_128(fmt, M, K, N, r, tiles):
+    """Ranks above 128, up to the largest the library accepts (256): the
+    rank-r passes then run more than one 128-wide block of rank columns (the
+    grid's second dimension), the dA/dB pass more than one rank tile, and the
+    GEMM heads and tails more than two 64-deep rank steps. r = 130 is not a
+    multiple of 8 (the dZ pass takes the register kernel)."""
+    lay = synth.small_layer(M, K, N, r, fmt=fmt, index=(M + r) % 89)
+    print_case("rank above 128", fmt, M, K, N, r)
+    t = synth.inputs(lay)
+    _check_all(_run(lay, t, Z_from_forward=(M % 2 == 0)), _oracle(lay, t))
