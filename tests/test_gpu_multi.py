@@ -78,11 +78,12 @@ def test_adapters_over_one_base(fmt, cut, tiles):
     assert rel(got["Y_base"], Xf @ Wd.T) <= TOL
 
 
-@pytest.mark.parametrize("r", [12, 40, 72])
+@pytest.mark.parametrize("r", [12, 40, 72, 136, 256])
 def test_ranks_off_the_8_grid(r, tiles):
     """Ranks that are not multiples of 8 (one adapter's rank columns padded to
-    the next multiple of 8 where a tile's adapters run as one product) and a
-    rank above 64."""
+    the next multiple of 8 where a tile's adapters run as one product), a rank
+    above 64, and ranks above 128 up to the largest accepted (more than one
+    128-wide rank block in the rank-r passes)."""
     offs = OFFSETS["twelve"]
     lay, t, W, got = _case(synth.NF4, 300, 512, 384, r, offs, index=53)
     print_case("multi r", r, offs)

@@ -98,6 +98,8 @@ CASES = [
     (128, 4096, 512, 64),      # few tiles: split reduction
     (1024, 8192, 768, 16),     # long reduction: rank-r range partials summed in the GEMM
     (64, 96, 40, 128),         # tiny, r = 128
+    (300, 512, 384, 256),      # the largest rank accepted: two 128-wide rank blocks in the Z pass
+    (200, 1024, 264, 136),     # rank above 128, not a multiple of 64
 ]
 
 

@@ -65,7 +65,8 @@ def test_single_linear_workload_parity(tiles):
 
 @pytest.mark.parametrize("fmt", [synth.NF4, synth.NF4_DQ, synth.MXFP4, synth.NVFP4])
 @pytest.mark.parametrize("M,K,N,r", [(200, 192, 200, 8), (64, 320, 96, 24), (300, 256, 100, 4),
-                                     (129, 1024, 264, 64), (17, 512, 136, 128), (1, 64, 8, 1)])
+                                     (129, 1024, 264, 64), (17, 512, 136, 128), (1, 64, 8, 1),
+                                     (33, 64, 3, 5), (5, 128, 1, 2)])
 def test_ragged_shapes(fmt, M, K, N, r, tiles):
     if fmt in (synth.MXFP4, synth.NVFP4):
         K = K - 32 if K % 64 == 0 and K > 64 else K     # exercise K % 64 == 32

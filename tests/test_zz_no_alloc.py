@@ -41,6 +41,7 @@ def _oracle_Y(lay, t):
     ((1024, 1024, 1024, 16, synth.NF4, 1), (256, 1024, 1024, 16, synth.NF4, 2)),
     ((4096, 4096, 1024, 16, synth.NF4, 3), (700, 512, 320, 8, synth.MXFP4, 4)),
     ((600, 640, 384, 24, synth.NF4_DQ, 5), (130, 640, 384, 24, synth.NF4_DQ, 6)),
+    ((520, 512, 384, 256, synth.NF4, 7), (130, 512, 384, 136, synth.MXFP4, 8)),   # ranks above 128
 ])
 def test_noalloc_matches_forward_two_calls(first, second):
     for spec in (first, second):
