@@ -346,3 +346,33 @@ def test_ranks_above_128(fmt, M, K, N, r, tiles):
     print_case("rank above 128", fmt, M, K, N, r)
     t = synth.inputs(lay)
     _check_all(_run(lay, t, Z_from_forward=(M % 2 == 0)), _oracle(lay, t))
+
+
+@pytest.mark.parametrize("fmt", [synth.NF4, synth.MXFP4])
+def test_many_small_experts(fmt, tiles):
+    """200 experts, each with its own base and adapter, of 0 to 9 rows (79 of
+    them empty), 550 rows in all: every row tile is an expert's short last
+    tile, and the grids hold more row slots for the experts than rows. Every
+    expert's dA and dB against the oracle; the empty ones zero."""
+    E, K, N, r = 200, 128, 96, 8
+    rng = np.random.default_rng(2024)
+    counts = rng.integers(0, 10, size=E)
+    counts[rng.choice(E, E // 3, replace=False)] = 0
+    offs = [0] + np.cumsum(counts).tolist()
+    lay = synth.small_layer(offs[-1], K, N, r, fmt=fmt, index=29, experts=E, offsets=offs)
+    print_case("many small experts", fmt, E, offs[-1])
+    t = synth.inputs(lay)
+    got = _run(lay, t, offsets=offs)
+    Ws = [dequant_rows(t["W"][e], np.arange(N), fmt) for e in range(E)]
+    As = [f64(a) for a in t["A"]]
+    Bs = [f64(b) for b in t["B"]]
+    fo = lora.grouped_forward(f64(t["X"]), Ws, As, Bs, lay.s, offs)
+    bo = lora.grouped_backward(f64(t["X"]), Ws, As, Bs, lay.s, f64(t["dY"]), offs)
+    for k in ("Y", "Z"):
+        assert rel(got[k], fo[k]) <= TOL, k
+    assert rel(got["dX"], bo["dX"]) <= TOL
+    for e in range(E):
+        if counts[e]:
+            assert rel(got["dA"][e], bo["dA"][e]) <= TOL and rel(got["dB"][e], bo["dB"][e]) <= TOL, e
+        else:
+            assert not (got["dA"][e] & 0x7FFF).any() and not (got["dB"][e] & 0x7FFF).any(), e
