@@ -29,8 +29,9 @@ def _W(N, K, seed):
     return to_bf16(w)
 
 
-# r + 16 <= 64 factors CholeskyQR on the device, r = 56 (72 columns) on the host
-@pytest.mark.parametrize("N,K,r", [(256, 512, 16), (520, 1024, 8), (256, 512, 56)])
+# r + 16 <= 64 factors CholeskyQR on the device, r = 56 (72 columns) and the
+# largest rank accepted, 128 (144 columns), on the host
+@pytest.mark.parametrize("N,K,r", [(256, 512, 16), (520, 1024, 8), (256, 512, 56), (320, 512, 128)])
 def test_one_iteration_is_nf4_plus_best_rank_r(N, K, r):
     print_case("loftq 1", N, K, r)
     Wb = _W(N, K, N + K)
