@@ -14,8 +14,8 @@ import torch
 import lora_fine_tuning_amd as L
 import synth
 from oracle import lora
-from gpu_util import (DEV, TILE_PATHS, TOL, dequant_rows, f64, pack_gpu, print_case, rel, set_tiles, to_dev,
-                      to_host)
+from gpu_util import (DEV, TILE_PATHS, TOL, dequant_rows, f64, guarded, pack_gpu, print_case, rel, set_tiles,
+                      to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -27,13 +27,31 @@ def tiles(request, monkeypatch):
 
 
 def _run(lay, t, s=None, Z_from_forward=True, offsets=None):
+    """Forward and backward of one layer; every output and both workspaces sit
+    inside guard bands that must come back untouched."""
     s = lay.s if s is None else s
     base = pack_gpu(t["W"], lay.fmt)
     X, A, B, dY = (to_dev(t[k]) for k in ("X", "A", "B", "dY"))
     offs = None if offsets is None else torch.tensor(offsets, dtype=torch.int64, device=DEV)
-    fw = L.forward(base, X, A, B, s, group_offsets=offs, want_parts=True)
-    bw = L.backward(base, X, dY, A, B, s, Z=fw["Z"] if Z_from_forward else None, group_offsets=offs)
+    M, r = X.shape[0], A.shape[-2]
+    checks = []
+
+    def g(name, shape, dtype=torch.bfloat16):
+        v, c = guarded(shape, dtype)
+        checks.append((name, c))
+        return v
+
+    ws0 = g("forward workspace", (L.lora4_workspace_bytes(0, base.abi(), M, r),), torch.uint8)
+    ws1 = g("backward workspace", (L.lora4_workspace_bytes(1, base.abi(), M, r),), torch.uint8)
+    fo = {"Y": g("Y", (M, base.N)), "Z": g("Z", (M, r)), "Y_base": g("Y_base", (M, base.N)),
+          "Y_lora": g("Y_lora", (M, base.N))}
+    bo = {"dX": g("dX", (M, base.K)), "dA": g("dA", tuple(A.shape)), "dB": g("dB", tuple(B.shape))}
+    fw = L.forward(base, X, A, B, s, group_offsets=offs, want_parts=True, workspace=ws0, out=fo)
+    bw = L.backward(base, X, dY, A, B, s, Z=fw["Z"] if Z_from_forward else None, group_offsets=offs,
+                    workspace=ws1, out=bo)
     torch.cuda.synchronize()
+    for name, c in checks:
+        c(name)
     out = {k: to_host(v) for k, v in fw.items()}
     out.update({k: to_host(v) for k, v in bw.items()})
     return out
