@@ -158,8 +158,8 @@ def print_case(*args):
 # Full-size parity: the oracle over whole matrices, guard bands, element bounds
 # ---------------------------------------------------------------------------
 
-# Host threads for the row chunks of the oracle's packing and dequant (the
-# GPU machine grants 16 CPUs per GPU). numpy releases the GIL inside its array
+# Host threads for the row chunks of the oracle's packing and dequant (at
+# most 16: the host share of one GPU). numpy releases the GIL inside its array
 # loops, so threads run the chunks in parallel; the oracle functions are the
 # same, called on row ranges (every format packs rows independently, except
 # the double quantization of NF4-DQ's scales, applied to the whole matrix).
