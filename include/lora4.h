@@ -25,7 +25,9 @@
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller. Tensors are
  *    dense, row-major and contiguous. bf16 values are passed as uint16_t bit
- *    patterns. 16-byte alignment is required for every tensor pointer.
+ *    patterns. 16-byte alignment is required for every tensor pointer except
+ *    the NF4-DQ second-level scales (scales2), which need 4 bytes: a group's
+ *    slice of a stacked [groups][...] array starts at a multiple of 4 bytes.
  *  - stream is a hipStream_t passed as void* (NULL = the null stream). Every
  *    call is asynchronous on that stream; nothing synchronizes the device.
  *    Pointers are borrowed until the stream work completes.
@@ -80,7 +82,7 @@ typedef enum {
   LORA4_OK = 0,
   LORA4_ERR_NULL = -1,          /* a required pointer is NULL                    */
   LORA4_ERR_SHAPE = -2,         /* a size is out of range or inconsistent        */
-  LORA4_ERR_ALIGN = -3,         /* a tensor pointer is not 16-byte aligned       */
+  LORA4_ERR_ALIGN = -3,         /* a tensor pointer is not 16-byte aligned (scales2: 4) */
   LORA4_ERR_FORMAT = -4,        /* unknown format, or block does not match it    */
   LORA4_ERR_WORKSPACE = -5,     /* workspace NULL or smaller than required       */
   LORA4_ERR_HIP = -6,           /* a HIP call or kernel launch failed            */

@@ -232,6 +232,10 @@ lora4_status launch_lds(const char *name, Kern kernel, dim3 grid, dim3 block, si
 // ---------------------------------------------------------------------------
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+// NF4-DQ second-level scales are read and written one float at a time; a
+// group's slice of a stacked [groups][...] array starts at a multiple of 4
+// bytes only (lora4_packed_bytes part 2 is 4 * ceil(N*K/64/256))
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -249,7 +253,7 @@ lora4_status check_W(const lora4_W *W) {
   if (!W->codes || !W->scales) return LORA4_ERR_NULL;
   if (W->format == LORA4_NF4_DQ && !W->scales2) return LORA4_ERR_NULL;
   if (!aligned16(W->codes) || !aligned16(W->scales)) return LORA4_ERR_ALIGN;
-  if (W->format == LORA4_NF4_DQ && !aligned16(W->scales2)) return LORA4_ERR_ALIGN;
+  if (W->format == LORA4_NF4_DQ && !aligned4(W->scales2)) return LORA4_ERR_ALIGN;
   return LORA4_OK;
 }
 
@@ -1519,7 +1523,7 @@ lora4_status quant_pack_nf4(const uint16_t *W_bf16, int64_t N, int64_t K, int32_
   if (!W_bf16 || !codes || !scales) return LORA4_ERR_NULL;
   if (double_quant && !scales2) return LORA4_ERR_NULL;
   if (N < 1 || K < 64 || K % 64 != 0 || N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return LORA4_ERR_SHAPE;
-  if (!aligned16(W_bf16) || !aligned16(codes) || !aligned16(scales) || (double_quant && !aligned16(scales2)))
+  if (!aligned16(W_bf16) || !aligned16(codes) || !aligned16(scales) || (double_quant && !aligned4(scales2)))
     return LORA4_ERR_ALIGN;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   TRY(clear_padding(N, K, double_quant ? LORA4_NF4_DQ : LORA4_NF4, codes, scales, st));
@@ -1659,8 +1663,9 @@ lora4_status lora4_loftq_init(const uint16_t *W, int64_t N, int64_t K, int32_t r
   if (r < 1 || r > 128 || r + LOFTQ_OVERSAMPLE > N || r + LOFTQ_OVERSAMPLE > K) return LORA4_ERR_SHAPE;
   if (iters < 1 || iters > 64 || !std::isfinite(s) || s == 0.0f) return LORA4_ERR_SHAPE;
   for (const void *q : {(const void *)W, (const void *)codes, (const void *)scales, (const void *)A,
-                        (const void *)B, (const void *)scales2})
-    if (q && !aligned16(q)) return LORA4_ERR_ALIGN;
+                        (const void *)B})
+    if (!aligned16(q)) return LORA4_ERR_ALIGN;
+  if (scales2 && !aligned4(scales2)) return LORA4_ERR_ALIGN;
   const LoftqPlan lp = make_loftq_plan(N, K, r);
   if (!workspace) return LORA4_ERR_WORKSPACE;
   if (!aligned16(workspace)) return LORA4_ERR_ALIGN;

@@ -70,6 +70,7 @@ def test_format_and_block_validation(lib):
     assert fwd(_W(fmt=2)) == ENULL                        # DQ needs scales2
     assert fwd(_W(codes=None)) == ENULL
     assert fwd(_W(codes=250)) == EALIGN
+    assert fwd(_W(fmt=2, scales2=4098)) == EALIGN          # DQ scales2: 4-byte alignment
     assert fwd(_W(), r=0) == ESHAPE
     assert fwd(_W(), r=257) == ESHAPE
     assert fwd(_W(), s=float("nan")) == ESHAPE
@@ -106,6 +107,7 @@ def test_quant_pack_validation(lib):
     assert L.quant_pack_nf4(4096, 16, 96, 0, 4096, 4096, None, None) == ESHAPE
     assert L.quant_pack_nf4(4096, 16, 64, 1, 4096, 4096, None, None) == ENULL
     assert L.quant_pack_nf4(4100, 16, 64, 0, 4096, 4096, None, None) == EALIGN
+    assert L.quant_pack_nf4(4096, 16, 64, 1, 4096, 4096, 4098, None) == EALIGN   # scales2: 4-byte alignment
     assert L.quant_pack_mxfp4(4096, 16, 48, 4096, 4096, None) == ESHAPE
     assert L.quant_pack_mxfp4(4096, 0, 64, 4096, 4096, None) == ESHAPE
 

@@ -129,7 +129,7 @@ def test_zero_base_isolates_the_lora_path(tiles):
 def test_grouped_small_with_empty_group(tiles):
     K, N, r, E = 256, 96, 16, 5
     offs = [0, 70, 70, 200, 201, 333]
-    for fmt in (synth.MXFP4, synth.NF4):
+    for fmt in (synth.MXFP4, synth.NF4, synth.NF4_DQ, synth.NVFP4):
         lay = synth.small_layer(offs[-1], K, N, r, fmt=fmt, index=21, experts=E, offsets=offs)
         print_case("grouped", fmt, offs)
         t = synth.inputs(lay)
@@ -366,7 +366,7 @@ def test_ranks_above_128(fmt, M, K, N, r, tiles):
     _check_all(_run(lay, t, Z_from_forward=(M % 2 == 0)), _oracle(lay, t))
 
 
-@pytest.mark.parametrize("fmt", [synth.NF4, synth.MXFP4])
+@pytest.mark.parametrize("fmt", [synth.NF4, synth.MXFP4, synth.NF4_DQ, synth.NVFP4])
 def test_many_small_experts(fmt, tiles):
     """200 experts, each with its own base and adapter, of 0 to 9 rows (79 of
     them empty), 550 rows in all: every row tile is an expert's short last
