@@ -22,7 +22,7 @@ def tiles(request, monkeypatch):
     return set_tiles(monkeypatch, request.param)
 
 
-def _case(fmt, M, K, N, r, offs, index):
+def _case(fmt, M, K, N, r, offs, index, z_from_forward=True):
     G = len(offs) - 1
     lay = synth.small_layer(M, K, N, r, fmt=fmt, index=index, experts=G, offsets=offs)
     t = synth.inputs(lay)
@@ -44,7 +44,8 @@ def _case(fmt, M, K, N, r, offs, index):
     fo = {"Y": g("Y", (M, N)), "Z": g("Z", (M, r)), "Y_base": g("Y_base", (M, N)), "Y_lora": g("Y_lora", (M, N))}
     bo = {"dX": g("dX", (M, K)), "dA": g("dA", tuple(A.shape)), "dB": g("dB", tuple(B.shape))}
     fw = L.forward_multi(base, X, A, B, lay.s, adapter_offsets=o, want_parts=True, workspace=ws0, out=fo)
-    bw = L.backward_multi(base, X, dY, A, B, lay.s, Z=fw["Z"], adapter_offsets=o, workspace=ws1, out=bo)
+    bw = L.backward_multi(base, X, dY, A, B, lay.s, Z=fw["Z"] if z_from_forward else None, adapter_offsets=o,
+                          workspace=ws1, out=bo)
     torch.cuda.synchronize()
     for name, c in checks:
         c(name)
@@ -175,3 +176,22 @@ def test_many_adapters_large_tiles():
         dz = lay.s * (dYe @ f64(B_u[e]))
         assert rel(dA[e], dz.T @ Xe) <= TOL, e
         assert rel(dB[e], lay.s * (dYe.T @ (Xe @ f64(A_u[e]).T))) <= TOL, e
+
+
+@pytest.mark.parametrize("fmt", [synth.NF4, synth.MXFP4])
+def test_backward_recomputes_z(fmt, tiles):
+    """The backward with no Z from the forward recomputes it per adapter
+    (twelve adapters, several in one row tile) before the dZ pass and the
+    dA / dB pass; against the grouped oracle."""
+    offs = OFFSETS["twelve"]
+    lay, t, W, got = _case(fmt, 300, 512, 384, 16, offs, index=57, z_from_forward=False)
+    print_case("multi recompute Z", fmt, offs)
+    G = len(offs) - 1
+    Wd = dequant_rows(W, np.arange(lay.N), fmt)
+    bo = lora.grouped_backward(f64(t["X"]), [Wd] * G, [f64(a) for a in t["A"]], [f64(b) for b in t["B"]], lay.s,
+                               f64(t["dY"]), offs)
+    assert rel(got["dX"], bo["dX"]) <= TOL
+    for e in range(G):
+        if offs[e + 1] > offs[e]:
+            assert rel(got["dA"][e], bo["dA"][e]) <= TOL, e
+            assert rel(got["dB"][e], bo["dB"][e]) <= TOL, e
